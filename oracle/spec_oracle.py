@@ -1,0 +1,362 @@
+"""Plain fp64 CPU oracle for batched speculative-decoding verification.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module. The product path (the HIP
+library and its Python binding) never calls it and shares no code with it.
+
+It states, slowly and literally, what one verification step computes for each
+sequence: temperature softmax of every needed logit row, the ordered acceptance
+walk, the residual or bonus draw, the emitted tokens, the accepted-length
+histogram and a per-slot acceptance EMA. Everything is float64 numpy; nothing is
+blocked, fused or reordered.
+
+Sources (the five pages this method is described on), abbreviated below:
+
+  [DVC]   "Speculative Decoding: Draft, Verify, and Correct"
+  [SMB]   "Speculative Decoding: How a Small Model Speeds Up a Big One Without
+           Changing Its Output"
+  [RNR]   "Speculative decoding: why correcting a rejection is not resampling
+           from the target"
+  [MNW]   "Margins, Not Windows: Training-Free Per-Step Lossy Speculative
+           Decoding" (AdaptiveSpec summary)
+
+Conventions the pages leave open, and the reading taken here (each one is also
+listed with its reason in the design notes):
+
+  * Acceptance: a draft d is kept with probability min(1, p(d)/q(d)); with one
+    supplied uniform u it is kept iff p(d) >= q(d) or u < p(d)/q(d) (strict).
+    q(d) = 0 therefore always keeps the draft ([SMB] "Seeing It in Code",
+    [RNR] s.2).
+  * Uniform consumption: u[b, i] decides position i; u[b, K] drives the single
+    correction or bonus draw. Greedy and margin modes use no uniforms.
+  * Inverse CDF: weights in index order 0..V-1, C_v the inclusive prefix sum,
+    draw = smallest v with C_v > u * C_{V-1}; if rounding leaves no such v, the
+    largest v with positive weight. Zero-weight tokens are never drawn.
+  * Residual normaliser Z = sum_v max(0, p_v - q_v), summed as a prefix sum in
+    index order (never as 1 - sum min(p, q)). Z = 0 after a rejection can only
+    come from rounding; the draw then falls back to p_j (counted).
+  * Bonus token: always emitted when all K drafts are kept (stochastic: drawn
+    from p_K; greedy/margin: argmax of target row K).
+  * argmax: lowest index among equal maxima of the raw logits.
+  * Margin rule: every position is tested in order; a draft is kept iff it is
+    the target argmax or p(d)/p(argmax) > tau (strict), with p at the call's
+    temperature. The first failing position is the rejection and its
+    correction is the target argmax.
+  * Invalid input: a sequence with a drafted token outside [0, V), or with a
+    needed logit row holding NaN or +inf or no finite maximum (all -inf), is
+    marked invalid: accept_len -1, tokens all -1, not counted in the histogram,
+    EMA untouched. Needed rows: all K+1 target rows, plus all K draft rows in
+    stochastic mode.
+  * EMA: per call and slot, x = accept_len / K; the first observation of a slot
+    sets it, later ones do ema = decay * ema + (1 - decay) * x.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+MODE_STOCHASTIC = 0
+MODE_GREEDY = 1
+MODE_MARGIN = 2
+
+
+# --------------------------------------------------------------------------
+# Distributions
+# --------------------------------------------------------------------------
+
+def row_is_valid(x) -> bool:
+    """A logit row is usable iff it has no NaN, no +inf and a finite maximum."""
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return False
+    if np.isnan(x).any() or np.isposinf(x).any():
+        return False
+    return bool(np.isfinite(x.max()))
+
+
+def softmax_t(x, T: float) -> np.ndarray:
+    """Sampling distribution of one logit row at temperature T.
+
+    p(v) = exp((x_v - M) / T) / sum_w exp((x_w - M) / T), M = max_w x_w.
+    The distribution that acceptance and correction use must be the one the
+    sampler really draws from, i.e. after temperature ([DVC] "Preserve the
+    distribution you actually intend"; [RNR] s.1). -inf logits get exactly 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    M = x.max()
+    e = np.exp((x - M) / float(T))
+    return e / e.sum()
+
+
+def argmax_lowest(x) -> int:
+    """Index of the largest raw logit; the lowest index wins a tie."""
+    x = np.asarray(x, dtype=np.float64)
+    M = x.max()
+    return int(np.flatnonzero(x == M)[0])
+
+
+# --------------------------------------------------------------------------
+# One-position building blocks ([DVC] "Name the two distributions at one
+# prefix", "Why the correction recovers the target"; [RNR] s.2)
+# --------------------------------------------------------------------------
+
+def acceptance_probability(p, q) -> np.ndarray:
+    """a(v) = min(1, p(v) / q(v)); a(v) = 1 where q(v) = 0 (p >= q there)."""
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    a = np.ones_like(p)
+    lo = p < q
+    a[lo] = p[lo] / q[lo]
+    return a
+
+
+def accepted_mass(p, q) -> np.ndarray:
+    """Mass that reaches each token through an accepted proposal: q(v) a(v)."""
+    q = np.asarray(q, dtype=np.float64)
+    return q * acceptance_probability(p, q)
+
+
+def positive_residual(p, q):
+    """Unnormalised residual [p - q]_+ and its index-order total Z.
+
+    Z is the rejection probability: it equals 1 - sum min(p, q) when both sum
+    to one, but is computed from the positive parts so that p = q gives
+    exactly 0 ([DVC] "Why the correction recovers the target"; [RNR] s.2).
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    r = np.maximum(p - q, 0.0)
+    Z = float(np.cumsum(r)[-1]) if r.size else 0.0
+    return r, Z
+
+
+def residual_distribution(p, q) -> np.ndarray:
+    """Normalised residual r = [p - q]_+ / Z (undefined when Z = 0)."""
+    r, Z = positive_residual(p, q)
+    if Z <= 0.0:
+        raise ZeroDivisionError("residual undefined: Z = 0 (p == q)")
+    return r / Z
+
+
+def inverse_cdf(w, u: float):
+    """Draw from the weights w with one uniform u in [0, 1).
+
+    Returns (token, boundary_distance). token = smallest v with C_v > u * C_end
+    where C is the inclusive prefix sum in index order; when rounding leaves no
+    such v, the largest v with w_v > 0. The distance is how far u lies from the
+    nearest edge of the chosen token's interval, in u units.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    C = np.cumsum(w)
+    total = C[-1]
+    t = float(u) * total
+    v = int(np.searchsorted(C, t, side="right"))
+    if v >= w.size:
+        v = int(np.flatnonzero(w > 0.0)[-1])
+    lo = C[v - 1] / total if v > 0 else 0.0
+    hi = C[v] / total
+    dist = min(abs(float(u) - lo), abs(float(u) - hi))
+    return v, dist
+
+
+# --------------------------------------------------------------------------
+# One sequence ([DVC] "Verify several proposed tokens in one target pass";
+# [SMB] "The Guarantee Behind Rejection Sampling"; [RNR] s.5; [MNW] s.3)
+# --------------------------------------------------------------------------
+
+@dataclass
+class SequenceResult:
+    tokens: np.ndarray            # [K+1] int64, -1 after the last emitted token
+    accept_len: int               # accepted drafts j (emitted = j + 1); -1 if invalid
+    p_d: np.ndarray               # [K] p_i(d_i) (stochastic); margin ratio (margin); NaN (greedy)
+    q_d: np.ndarray               # [K] q_i(d_i) (stochastic); NaN otherwise
+    z: float                      # residual Z at j (stochastic, j < K); -1 otherwise
+    argmax: np.ndarray            # [K+1] lowest-index argmax of each target row (all modes)
+    min_dist: float               # smallest boundary distance among decisions taken
+    zero_q_accepts: int = 0
+    z0_fallback: int = 0
+    valid: bool = True
+    dists: list = field(default_factory=list)
+
+
+def verify_sequence(target, draft, tokens, u, T: float, mode: int,
+                    tau: float = 0.0) -> SequenceResult:
+    """Verify one sequence.
+
+    target: [K+1, V] logits, draft: [K, V] logits (stochastic only),
+    tokens: [K] drafted tokens, u: [K+1] uniforms (stochastic only).
+    """
+    target = np.asarray(target, dtype=np.float64)
+    K = target.shape[0] - 1
+    V = target.shape[1]
+    toks = np.asarray(tokens, dtype=np.int64).reshape(K)
+    nan_k = np.full(K, np.nan)
+    out = np.full(K + 1, -1, dtype=np.int64)
+
+    valid = bool(np.all((toks >= 0) & (toks < V)))
+    valid = valid and all(row_is_valid(target[i]) for i in range(K + 1))
+    if mode == MODE_STOCHASTIC:
+        draft = np.asarray(draft, dtype=np.float64)
+        valid = valid and all(row_is_valid(draft[i]) for i in range(K))
+    argmax = np.array([argmax_lowest(target[i]) if row_is_valid(target[i]) else -1
+                       for i in range(K + 1)], dtype=np.int64)
+    if not valid:
+        return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
+                              math.inf, valid=False)
+
+    dists = []
+    zero_q = 0
+    z0 = 0
+    z = -1.0
+    p_d = nan_k.copy()
+    q_d = nan_k.copy()
+
+    if mode == MODE_STOCHASTIC:
+        u = np.asarray(u, dtype=np.float64).reshape(K + 1)
+        p_rows = [softmax_t(target[i], T) for i in range(K + 1)]
+        q_rows = [softmax_t(draft[i], T) for i in range(K)]
+        for i in range(K):
+            p_d[i] = p_rows[i][toks[i]]
+            q_d[i] = q_rows[i][toks[i]]
+        j = K
+        for i in range(K):
+            P, Q = p_d[i], q_d[i]
+            if P >= Q:
+                keep = True
+                if Q == 0.0:
+                    zero_q += 1
+                if Q > 0.0:
+                    dists.append(abs(u[i] - P / Q))
+            else:
+                ratio = P / Q
+                keep = bool(u[i] < ratio)
+                dists.append(abs(u[i] - ratio))
+            if not keep:
+                j = i
+                break
+        if j < K:
+            r, Z = positive_residual(p_rows[j], q_rows[j])
+            z = Z
+            if Z > 0.0:
+                c, dist = inverse_cdf(r, u[K])
+            else:
+                z0 += 1
+                c, dist = inverse_cdf(p_rows[j], u[K])
+        else:
+            c, dist = inverse_cdf(p_rows[K], u[K])
+        dists.append(dist)
+    elif mode == MODE_GREEDY:
+        j = K
+        for i in range(K):
+            if toks[i] != argmax[i]:
+                j = i
+                break
+        c = int(argmax[j])
+    elif mode == MODE_MARGIN:
+        for i in range(K):
+            p = softmax_t(target[i], T)
+            p_d[i] = p[toks[i]] / p[argmax[i]]
+        j = K
+        for i in range(K):
+            if toks[i] == argmax[i]:
+                continue
+            dists.append(abs(p_d[i] - tau))
+            if not (p_d[i] > tau):
+                j = i
+                break
+        c = int(argmax[j])
+    else:
+        raise ValueError(f"unknown mode {mode}")
+
+    out[:j] = toks[:j]
+    out[j] = c
+    return SequenceResult(out, j, p_d, q_d, z, argmax,
+                          min(dists) if dists else math.inf,
+                          zero_q_accepts=zero_q, z0_fallback=z0, valid=True,
+                          dists=dists)
+
+
+# --------------------------------------------------------------------------
+# Batch, histogram and EMA ([RNR] s.7 on recording the accepted-length
+# distribution; [MNW] s.3 on a rolling acceptance history)
+# --------------------------------------------------------------------------
+
+class EmaState:
+    """Per-slot acceptance EMA: float64 value and observation count."""
+
+    def __init__(self, n_slots: int, decay: float):
+        self.decay = float(decay)
+        self.ema = np.zeros(n_slots, dtype=np.float64)
+        self.steps = np.zeros(n_slots, dtype=np.int64)
+
+    def observe(self, slot: int, x: float) -> None:
+        if self.steps[slot] == 0:
+            self.ema[slot] = x
+        else:
+            self.ema[slot] = self.decay * self.ema[slot] + (1.0 - self.decay) * x
+        self.steps[slot] += 1
+
+
+@dataclass
+class BatchResult:
+    tokens: np.ndarray        # [B, K+1] int64
+    accept_len: np.ndarray    # [B] int64
+    hist: np.ndarray          # [K+1] int64
+    p_d: np.ndarray           # [B, K]
+    q_d: np.ndarray           # [B, K]
+    z: np.ndarray             # [B]
+    argmax: np.ndarray        # [B, K+1]
+    min_dist: np.ndarray      # [B]
+    zero_q_accepts: int
+    z0_fallbacks: int
+    invalid: int
+
+
+def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
+                 tau: float = 0.0, ema: EmaState | None = None,
+                 rows=None) -> BatchResult:
+    """Verify every sequence b (or only those listed in `rows`).
+
+    target [B, K+1, V], draft [B, K, V] (stochastic), tokens [B, K],
+    uniforms [B, K+1]. Arrays may be any float dtype; they are widened to
+    float64 one sequence at a time. When `ema` is given, slot b is updated
+    for every valid verified sequence b.
+    """
+    B = target.shape[0]
+    K = target.shape[1] - 1
+    idx = list(range(B)) if rows is None else [int(b) for b in rows]
+    n = len(idx)
+    out = BatchResult(
+        tokens=np.full((n, K + 1), -1, dtype=np.int64),
+        accept_len=np.full(n, -1, dtype=np.int64),
+        hist=np.zeros(K + 1, dtype=np.int64),
+        p_d=np.full((n, K), np.nan), q_d=np.full((n, K), np.nan),
+        z=np.full(n, -1.0), argmax=np.full((n, K + 1), -1, dtype=np.int64),
+        min_dist=np.full(n, math.inf), zero_q_accepts=0, z0_fallbacks=0,
+        invalid=0)
+    for k, b in enumerate(idx):
+        res = verify_sequence(
+            target[b],
+            draft[b] if (draft is not None and mode == MODE_STOCHASTIC) else None,
+            tokens[b],
+            uniforms[b] if (uniforms is not None and mode == MODE_STOCHASTIC) else None,
+            T, mode, tau)
+        out.tokens[k] = res.tokens
+        out.accept_len[k] = res.accept_len
+        out.p_d[k] = res.p_d
+        out.q_d[k] = res.q_d
+        out.z[k] = res.z
+        out.argmax[k] = res.argmax
+        out.min_dist[k] = res.min_dist
+        out.zero_q_accepts += res.zero_q_accepts
+        out.z0_fallbacks += res.z0_fallback
+        if res.valid:
+            out.hist[res.accept_len] += 1
+            if ema is not None and K > 0:
+                ema.observe(b, res.accept_len / K)
+        else:
+            out.invalid += 1
+    return out
