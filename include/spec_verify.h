@@ -1,0 +1,181 @@
+/*
+ * spec_verify.h -- batched speculative-decoding verification on one AMD
+ * MI355X (gfx950) GPU, behind a plain C ABI.
+ *
+ * What one call computes, per sequence b of a batch of B (sources are cited
+ * by page title and section):
+ *
+ *   - target logits at K+1 positions and draft logits at K positions over a
+ *     vocabulary of V tokens are turned into sampling laws p_i and q_i by a
+ *     temperature softmax ("Speculative Decoding: Draft, Verify, and Correct",
+ *     section "Preserve the distribution you actually intend"; "Speculative
+ *     decoding: why correcting a rejection is not resampling from the target",
+ *     section 1);
+ *   - drafted tokens d_0..d_{K-1} are tested in order, each kept with
+ *     probability min(1, p_i(d_i)/q_i(d_i)), until the first rejection j
+ *     ("Draft, Verify, and Correct", sections "Name the two distributions at
+ *     one prefix" and "Verify several proposed tokens in one target pass");
+ *   - at j < K a correction is drawn from the normalised positive residual
+ *     [p_j - q_j]_+ ("Draft, Verify, and Correct", section "Why the correction
+ *     recovers the target"; "... not resampling from the target", sections 2
+ *     and 3); at j = K a bonus token is drawn from p_K ("... not resampling
+ *     from the target", section 5);
+ *   - greedy mode keeps a draft iff it is the target argmax and emits the
+ *     argmax otherwise ("Speculative Decoding: How a Small Model Speeds Up a
+ *     Big One Without Changing Its Output", section "The Guarantee Behind
+ *     Rejection Sampling"); margin mode also keeps a mismatched draft when
+ *     p(d)/p(argmax) exceeds tau ("Margins, Not Windows: Training-Free
+ *     Per-Step Lossy Speculative Decoding", section 3, margin-based lossy
+ *     verification);
+ *   - the accepted-length histogram of the call and a per-slot rolling
+ *     acceptance EMA are maintained ("... not resampling from the target",
+ *     section 7; "Margins, Not Windows", section 3, dynamic tree shaping).
+ *
+ * Conventions fixed by this library where the pages leave a choice:
+ *   - u[b][i] decides position i (keep iff p >= q or u < p/q, strict);
+ *     u[b][K] drives the one correction/bonus draw (inverse CDF in index
+ *     order: smallest v whose inclusive prefix weight exceeds u times the
+ *     total; clamped to the last positive-weight token). Greedy and margin
+ *     modes read no uniforms.
+ *   - argmax ties go to the lowest index, on raw logit values.
+ *   - q(d) = 0 keeps the draft (counted); Z = 0 after a rejection (rounding
+ *     only) draws from p_j instead (counted).
+ *   - a sequence whose drafted token is outside [0, V), or whose needed logit
+ *     row holds NaN or +inf or only -inf, is reported invalid: accept_len -1,
+ *     all tokens -1, not counted in the histogram, EMA untouched. Needed rows:
+ *     all K+1 target rows, plus all K draft rows in stochastic mode.
+ *   - logits times log2(e)/T must be finite in fp32; rows that overflow are
+ *     reported invalid.
+ *
+ * Threading and streams: every call is asynchronous on the stream it is
+ * given, never allocates, never synchronises and never touches the default
+ * stream, so it may be captured into a HIP graph. Calls on one handle must be
+ * ordered (one stream, or explicit events); the handle's workspace and EMA
+ * state are shared by all of them.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify_handle spec_verify_handle;
+
+enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 };
+enum { SV_MODE_STOCHASTIC = 0, SV_MODE_GREEDY = 1, SV_MODE_MARGIN = 2 };
+enum {
+    SV_OK = 0,
+    SV_EINVAL = -1,        /* bad argument; nothing was enqueued */
+    SV_EUNSUPPORTED = -2,  /* unknown dtype */
+    SV_ENOMEM = -3,        /* device allocation failed in init */
+    SV_EHIP = -4           /* a HIP call or launch failed; see spec_verify_last_error */
+};
+
+/* Device-side counters, cumulative since init or the last reset. */
+typedef struct spec_verify_stats {
+    uint64_t sequences;        /* valid sequences verified */
+    uint64_t invalid;          /* sequences reported invalid (bad token or row) */
+    uint64_t zero_q_accepts;   /* kept drafts whose draft probability was 0 */
+    uint64_t z0_fallbacks;     /* rejections whose residual summed to 0 */
+    uint64_t calls;            /* successful spec_verify calls (host counter) */
+} spec_verify_stats;
+
+/*
+ * Create a handle for batches of up to max_batch sequences with K drafts over
+ * a vocabulary of V tokens stored as logits_dtype (SV_DTYPE_F32 or
+ * SV_DTYPE_BF16). 1 <= K <= 63, 1 <= V < 2^31 / (K+1), 1 <= max_batch.
+ * ema_decay in [0, 1] weights the previous EMA value. Uses the current HIP
+ * device; the handle owns its device workspace (about 64 * max_batch * K
+ * bytes plus a few KB per sequence), the EMA state (float64 value and int32
+ * count per slot) and the counters, and frees them in spec_verify_destroy.
+ * Synchronises the device once (initialisation only).
+ */
+int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
+                     int logits_dtype, double ema_decay);
+
+/*
+ * Verify B sequences (1 <= B <= max_batch). All pointers are device pointers
+ * to contiguous row-major arrays, owned by the caller, aligned to their
+ * element size; 16-byte alignment of the logit arrays (with V a multiple of 8
+ * for bf16, 4 for fp32) selects the 128-bit load path.
+ *
+ *   target_logits   [B][K+1][V] logits_dtype
+ *   draft_logits    [B][K][V]   logits_dtype; stochastic mode only (may be NULL otherwise)
+ *   draft_tokens    [B][K]      int32
+ *   uniforms        [B][K+1]    float32 in [0, 1); stochastic mode only (may be NULL otherwise)
+ *   temperature     T > 0, finite (stochastic and margin modes; ignored by greedy)
+ *   mode            SV_MODE_*
+ *   tau             margin threshold (margin mode; finite), ignored otherwise
+ *   out_tokens      [B][K+1]    int32: kept drafts, then the correction/bonus, then -1
+ *   out_accept_len  [B]         int32: kept drafts j in 0..K (emitted = j+1); -1 if invalid
+ *   out_accept_hist [K+1]       uint32: zeroed, then hist[j] counts this call's valid sequences
+ *   stream          HIP stream the work is ordered on
+ *
+ * EMA slot b is updated with x = accept_len/K for every valid sequence b.
+ * Returns SV_OK once the work is enqueued, or an error code with nothing
+ * enqueued (SV_EINVAL for a NULL handle or required pointer, B out of range,
+ * an unknown mode, T not finite or T <= 0 in stochastic/margin mode, tau not
+ * finite in margin mode; SV_EHIP for a failed launch).
+ */
+int spec_verify(spec_verify_handle *h, int B,
+                const void *target_logits, const void *draft_logits,
+                const int32_t *draft_tokens, const float *uniforms,
+                float temperature, int mode, float tau,
+                int32_t *out_tokens, int32_t *out_accept_len,
+                uint32_t *out_accept_hist, hipStream_t stream);
+
+/* Free everything the handle owns (synchronises the device). NULL-safe. */
+int spec_verify_destroy(spec_verify_handle *h);
+
+/*
+ * Optional per-call side outputs written by later spec_verify calls (device
+ * pointers sized for max_batch; NULL disables each one):
+ *   p_d    [B][K] float64: stochastic p_i(d_i); margin p_i(d_i)/p_i(argmax_i); greedy NaN
+ *   q_d    [B][K] float64: stochastic q_i(d_i); NaN otherwise
+ *   z      [B]    float64: residual total Z at the rejection (stochastic, j < K), else -1
+ *   argmax [B][K+1] int32: lowest-index argmax of each target row (greedy and margin)
+ * Values at positions after the first rejection are still filled. Invalid
+ * sequences get NaN / -1.
+ */
+int spec_verify_set_aux(spec_verify_handle *h, double *p_d, double *q_d,
+                        double *z, int32_t *argmax);
+
+/* EMA state accessors, ordered on `stream`. Device pointers of max_batch entries. */
+int spec_verify_get_ema(spec_verify_handle *h, double *ema_dev, int32_t *steps_dev,
+                        hipStream_t stream);
+int spec_verify_set_ema(spec_verify_handle *h, const double *ema_dev,
+                        const int32_t *steps_dev, hipStream_t stream);
+int spec_verify_reset_ema(spec_verify_handle *h, hipStream_t stream);
+
+/* Copy the counters to host memory; synchronises `stream`. reset != 0 clears them. */
+int spec_verify_get_stats(spec_verify_handle *h, spec_verify_stats *out, int reset,
+                          hipStream_t stream);
+
+/*
+ * Profiling. With enable != 0, each later spec_verify call records HIP events
+ * on its stream just before and just after its streaming pass over the logits
+ * and after its last kernel (up to 4096 calls between reads; later calls are
+ * not recorded). The events are created here, never in spec_verify.
+ * spec_verify_profile_read waits for the recorded calls to finish and returns
+ * the summed milliseconds of the streaming pass and of whole calls, and how
+ * many calls were recorded, then starts a new window. enable = 0 frees them.
+ */
+int spec_verify_profile(spec_verify_handle *h, int enable);
+int spec_verify_profile_read(spec_verify_handle *h, double *stream_pass_ms, double *call_ms,
+                             int *n_calls);
+
+/* Text of the last error on this handle ("" if none). Valid until the next call. */
+const char *spec_verify_last_error(const spec_verify_handle *h);
+
+/* Library version string. */
+const char *spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,240 @@
+"""Python binding of libspecverify (batched speculative-decoding verification
+on MI355X).
+
+Argument marshalling only: every step of verification runs in the HIP
+kernels of the shared library. torch provides device memory and the stream
+the work is ordered on. torch is imported before the library is loaded so
+that the library binds to the same HIP runtime instance as torch.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB as LIB_PATH
+
+SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
+MODES = {"stochastic": 0, "greedy": 1, "margin": 2}
+SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_ENOMEM, SV_EHIP = 0, -1, -2, -3, -4
+_ERRNAMES = {-1: "SV_EINVAL", -2: "SV_EUNSUPPORTED", -3: "SV_ENOMEM", -4: "SV_EHIP"}
+
+EXPORTED = (
+    "spec_verify_init", "spec_verify", "spec_verify_destroy", "spec_verify_set_aux",
+    "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
+    "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
+    "spec_verify_last_error", "spec_verify_version",
+)
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERRNAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("sequences", ctypes.c_uint64), ("invalid", ctypes.c_uint64),
+                ("zero_q_accepts", ctypes.c_uint64), ("z0_fallbacks", ctypes.c_uint64),
+                ("calls", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing; build it first (python -m "
+            "speculative_decoding_verification_temp_amd.build)")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    L.spec_verify_init.argtypes = [ctypes.POINTER(vp), i32, i32, i32, i32, f64]
+    L.spec_verify.argtypes = [vp, i32, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp]
+    L.spec_verify_destroy.argtypes = [vp]
+    L.spec_verify_set_aux.argtypes = [vp, vp, vp, vp, vp]
+    L.spec_verify_get_ema.argtypes = [vp, vp, vp, vp]
+    L.spec_verify_set_ema.argtypes = [vp, vp, vp, vp]
+    L.spec_verify_reset_ema.argtypes = [vp, vp]
+    L.spec_verify_get_stats.argtypes = [vp, ctypes.POINTER(Stats), i32, vp]
+    L.spec_verify_profile.argtypes = [vp, i32]
+    L.spec_verify_profile_read.argtypes = [vp, ctypes.POINTER(f64), ctypes.POINTER(f64),
+                                           ctypes.POINTER(i32)]
+    L.spec_verify_last_error.argtypes = [vp]
+    L.spec_verify_last_error.restype = ctypes.c_char_p
+    L.spec_verify_version.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name not in ("spec_verify_last_error", "spec_verify_version"):
+            getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class SpecVerifier:
+    """One verification handle: fixed K, V and logit dtype, batches up to
+    max_batch, with its own workspace and per-slot acceptance EMA."""
+
+    def __init__(self, max_batch: int, K: int, V: int, dtype=torch.bfloat16,
+                 ema_decay: float = 0.99, device=None):
+        self.lib = load_library()
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        if dtype not in (torch.float32, torch.bfloat16):
+            raise SpecVerifyError(SV_EUNSUPPORTED, f"logit dtype {dtype}")
+        self.max_batch, self.K, self.V, self.dtype = int(max_batch), int(K), int(V), dtype
+        self.ema_decay = float(ema_decay)
+        h = ctypes.c_void_p()
+        code = SV_DTYPE_F32 if dtype == torch.float32 else SV_DTYPE_BF16
+        with torch.cuda.device(self.device):
+            rc = self.lib.spec_verify_init(ctypes.byref(h), self.max_batch, self.K, self.V,
+                                           code, self.ema_decay)
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_verify_init failed")
+        self._h = h
+        self._aux = None
+
+    # -- lifetime --
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            with torch.cuda.device(self.device):
+                self.lib.spec_verify_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, rc: int, what: str):
+        if rc != SV_OK:
+            msg = self.lib.spec_verify_last_error(self._h)
+            raise SpecVerifyError(rc, f"{what}: {msg.decode() if msg else ''}")
+
+    # -- side outputs --
+    def enable_aux(self) -> dict:
+        """Allocate and register the per-call side outputs (p(d), q(d), Z, argmax)."""
+        B, K = self.max_batch, self.K
+        dev = self.device
+        self._aux = dict(
+            p_d=torch.empty((B, K), dtype=torch.float64, device=dev),
+            q_d=torch.empty((B, K), dtype=torch.float64, device=dev),
+            z=torch.empty((B,), dtype=torch.float64, device=dev),
+            argmax=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+        a = self._aux
+        self._check(self.lib.spec_verify_set_aux(self._h, _ptr(a["p_d"]), _ptr(a["q_d"]),
+                                                 _ptr(a["z"]), _ptr(a["argmax"])), "set_aux")
+        return a
+
+    def disable_aux(self):
+        self._check(self.lib.spec_verify_set_aux(self._h, None, None, None, None), "set_aux")
+        self._aux = None
+
+    @property
+    def aux(self):
+        return self._aux
+
+    # -- verification --
+    def _check_logits(self, t, rows, name):
+        B = t.shape[0]
+        if t.device != self.device or t.dtype != self.dtype:
+            raise SpecVerifyError(SV_EINVAL, f"{name}: expected {self.dtype} on {self.device}")
+        if tuple(t.shape) != (B, rows, self.V) or not t.is_contiguous():
+            raise SpecVerifyError(SV_EINVAL, f"{name}: expected contiguous [B, {rows}, {self.V}]")
+
+    def verify(self, target, draft, tokens, uniforms=None, temperature: float = 1.0,
+               mode: str = "stochastic", tau: float = 0.0, out=None):
+        """Verify a batch. Returns (tokens [B, K+1] int32, accept_len [B] int32,
+        hist [K+1] int32 holding uint32 counts), ordered on the current stream."""
+        if mode not in MODES:
+            raise SpecVerifyError(SV_EINVAL, f"unknown mode {mode!r}")
+        K = self.K
+        B = int(target.shape[0])
+        self._check_logits(target, K + 1, "target")
+        if mode == "stochastic":
+            if draft is None or uniforms is None:
+                raise SpecVerifyError(SV_EINVAL, "stochastic mode needs draft and uniforms")
+            self._check_logits(draft, K, "draft")
+            if draft.shape[0] != B:
+                raise SpecVerifyError(SV_EINVAL, "draft batch differs from target")
+            if (uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1)
+                    or not uniforms.is_contiguous() or uniforms.device != self.device):
+                raise SpecVerifyError(SV_EINVAL, "uniforms: expected contiguous float32 [B, K+1]")
+        else:
+            draft = None
+            uniforms = None
+        if (tokens.dtype != torch.int32 or tuple(tokens.shape) != (B, K)
+                or not tokens.is_contiguous() or tokens.device != self.device):
+            raise SpecVerifyError(SV_EINVAL, "tokens: expected contiguous int32 [B, K]")
+        if out is None:
+            out = (torch.empty((B, K + 1), dtype=torch.int32, device=self.device),
+                   torch.empty((B,), dtype=torch.int32, device=self.device),
+                   torch.empty((K + 1,), dtype=torch.int32, device=self.device))
+        ot, ol, oh = out
+        with torch.cuda.device(self.device):
+            rc = self.lib.spec_verify(self._h, B, _ptr(target), _ptr(draft), _ptr(tokens),
+                                      _ptr(uniforms), float(temperature), MODES[mode],
+                                      float(tau), _ptr(ot), _ptr(ol), _ptr(oh),
+                                      _stream(self.device))
+        self._check(rc, "spec_verify")
+        return ot, ol, oh
+
+    # -- EMA and counters --
+    def ema(self):
+        e = torch.empty((self.max_batch,), dtype=torch.float64, device=self.device)
+        s = torch.empty((self.max_batch,), dtype=torch.int32, device=self.device)
+        self._check(self.lib.spec_verify_get_ema(self._h, _ptr(e), _ptr(s),
+                                                 _stream(self.device)), "get_ema")
+        return e, s
+
+    def set_ema(self, ema, steps):
+        ema = ema.to(device=self.device, dtype=torch.float64).contiguous()
+        steps = steps.to(device=self.device, dtype=torch.int32).contiguous()
+        if ema.numel() != self.max_batch or steps.numel() != self.max_batch:
+            raise SpecVerifyError(SV_EINVAL, "set_ema: need max_batch entries")
+        self._check(self.lib.spec_verify_set_ema(self._h, _ptr(ema), _ptr(steps),
+                                                 _stream(self.device)), "set_ema")
+        torch.cuda.current_stream(self.device).synchronize()
+
+    def reset_ema(self):
+        self._check(self.lib.spec_verify_reset_ema(self._h, _stream(self.device)), "reset_ema")
+
+    def stats(self, reset: bool = False) -> dict:
+        s = Stats()
+        self._check(self.lib.spec_verify_get_stats(self._h, ctypes.byref(s), int(reset),
+                                                   _stream(self.device)), "get_stats")
+        return {k: int(getattr(s, k)) for k, _ in Stats._fields_}
+
+
+    # -- profiling --
+    def profile(self, enable: bool = True):
+        """Record HIP events around the streaming pass of later calls."""
+        self._check(self.lib.spec_verify_profile(self._h, int(enable)), "profile")
+
+    def profile_read(self):
+        """(streaming-pass ms, whole-call ms, calls) summed since the last read."""
+        a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+        self._check(self.lib.spec_verify_profile_read(self._h, ctypes.byref(a), ctypes.byref(b),
+                                                      ctypes.byref(n)), "profile_read")
+        return a.value, b.value, n.value
+
+
+def version() -> str:
+    return load_library().spec_verify_version().decode()
+
+
+__all__ = ["SpecVerifier", "SpecVerifyError", "load_library", "version", "MODES", "EXPORTED"]

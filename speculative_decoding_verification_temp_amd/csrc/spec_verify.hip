@@ -1,0 +1,453 @@
+// Host side of the verification library: handle, workspace, argument
+// checks and stream-ordered launches of the kernels in sv_kernels.hpp.
+#include "spec_verify.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "sv_kernels.hpp"
+
+#ifndef SV_U_BF16
+#define SV_U_BF16 2
+#endif
+#ifndef SV_U_F32
+#define SV_U_F32 4
+#endif
+#ifndef SV_U_MAX
+#define SV_U_MAX 4
+#endif
+
+namespace {
+
+constexpr int kMaxSeg = 16;
+constexpr int kTilesPerWave = 4;
+constexpr int kProfCalls = 4096;
+constexpr double kLog2e = 1.4426950408889634073599246810018921;
+
+struct Launch {
+  int vec;          // elements per chunk: 8 (bf16) / 4 (fp32) vector path, 1 scalar path
+  int nseg;         // segments per row in the streaming pass
+  int seg_chunks;   // chunks per segment
+  int ntiles;       // draw tiles per row
+};
+
+}  // namespace
+
+struct spec_verify_handle {
+  int device = 0;
+  int max_batch = 0, K = 0, V = 0, dtype = 0;
+  double decay = 0.99;
+  sv::RowPart* parts = nullptr;
+  sv::DrawRow* draw = nullptr;
+  double* tsum_w = nullptr;
+  double* tsum_p = nullptr;
+  double* ema = nullptr;
+  int32_t* steps = nullptr;
+  sv::DevStats* stats = nullptr;
+  int ntiles_max = 0;
+  unsigned long long calls = 0;
+  double* aux_p = nullptr;
+  double* aux_q = nullptr;
+  double* aux_z = nullptr;
+  int32_t* aux_argmax = nullptr;
+  hipEvent_t* prof_ev = nullptr;   // 3 events per recorded call
+  int prof_cap = 0, prof_n = 0;
+  int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
+  int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
+  char err[256] = {0};
+};
+
+namespace {
+
+int fail(spec_verify_handle* h, int code, const char* fmt, ...) {
+  if (h != nullptr) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(h->err, sizeof(h->err), fmt, ap);
+    va_end(ap);
+  }
+  return code;
+}
+
+int check_launch(spec_verify_handle* h, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(h, SV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return SV_OK;
+}
+
+inline int div_up(long long a, long long b) { return int((a + b - 1) / b); }
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return (s != nullptr && *s) ? atoi(s) : dflt;
+}
+
+Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
+  Launch L;
+  L.vec = vec;
+  const long long nchunks = h->V / vec;
+  const long long min_seg = (long long)sv::kBlock * U;
+  int max_nseg = int(nchunks / min_seg);
+  if (max_nseg < 1) max_nseg = 1;
+  if (max_nseg > kMaxSeg) max_nseg = kMaxSeg;
+  int nseg = h->nseg_force > 0 ? h->nseg_force : div_up(h->target_wgs, (long long)B * rows);
+  if (nseg > max_nseg) nseg = max_nseg;
+  if (nseg < 1) nseg = 1;
+  L.seg_chunks = div_up(nchunks, nseg);
+  L.nseg = div_up(nchunks, L.seg_chunks);
+  if (L.nseg < 1) L.nseg = 1;
+  L.ntiles = div_up(nchunks, sv::kTileChunks);
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Event k (0: before the streaming pass, 1: after it, 2: after the call) of
+// the current recorded call.
+void prof_mark(spec_verify_handle* h, int k, hipStream_t s) {
+  if (h->prof_ev != nullptr && h->prof_n < h->prof_cap)
+    (void)hipEventRecord(h->prof_ev[3 * h->prof_n + k], s);
+}
+
+template <int DT, int VEC, int U>
+int run_stochastic(spec_verify_handle* h, const Launch& L, int B, const void* target,
+                   const void* draft, const int32_t* tokens, const float* uniforms, float c,
+                   int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
+  const int K = h->K, V = h->V;
+  const int rows = 2 * K + 1;
+  const long long grid1 = (long long)B * rows * L.nseg;
+  prof_mark(h, 0, s);
+  hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(grid1)), dim3(sv::kBlock), 0,
+                     s, target, draft, K, V, L.nseg, L.seg_chunks, c, h->parts, hist);
+  int rc = check_launch(h, "rowstats_sum");
+  prof_mark(h, 1, s);
+  if (rc) return rc;
+  const int grid2 = div_up(B, sv::kWavesPerBlock);
+  hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
+                     L.nseg, h->parts, target, draft, tokens, uniforms, c, out_tokens, out_len,
+                     hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
+                     h->aux_z);
+  rc = check_launch(h, "scan_stochastic");
+  if (rc) return rc;
+  const int wps = div_up(L.ntiles, kTilesPerWave);
+  const int grid3 = div_up((long long)B * wps, sv::kWavesPerBlock);
+  hipLaunchKernelGGL((sv::draw_tiles<DT, VEC>), dim3(grid3), dim3(sv::kBlock), 0, s, B, K, V,
+                     L.ntiles, kTilesPerWave, wps, target, draft, h->draw, c, h->tsum_w,
+                     h->tsum_p);
+  rc = check_launch(h, "draw_tiles");
+  if (rc) return rc;
+  hipLaunchKernelGGL((sv::draw_pick<DT, VEC>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
+                     L.ntiles, target, draft, h->draw, uniforms, c, h->tsum_w, h->tsum_p,
+                     out_tokens, h->stats, h->aux_z);
+  return check_launch(h, "draw_pick");
+}
+
+template <int DT, int VEC, int U>
+int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target,
+               const int32_t* tokens, bool margin, double invT, double tau,
+               int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
+  const int K = h->K, V = h->V;
+  const int rows = K + 1;
+  const long long grid1 = (long long)B * rows * L.nseg;
+  prof_mark(h, 0, s);
+  hipLaunchKernelGGL((sv::rowstats_max<DT, VEC, U>), dim3(unsigned(grid1)), dim3(sv::kBlock), 0,
+                     s, target, K, V, L.nseg, L.seg_chunks, h->parts, hist);
+  int rc = check_launch(h, "rowstats_max");
+  prof_mark(h, 1, s);
+  if (rc) return rc;
+  const int grid2 = div_up(B, sv::kWavesPerBlock);
+  if (margin)
+    hipLaunchKernelGGL((sv::scan_argmax<DT, true>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
+                       L.nseg, h->parts, target, tokens, invT, tau, out_tokens, out_len, hist,
+                       h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
+                       h->aux_argmax);
+  else
+    hipLaunchKernelGGL((sv::scan_argmax<DT, false>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K,
+                       V, L.nseg, h->parts, target, tokens, invT, tau, out_tokens, out_len, hist,
+                       h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
+                       h->aux_argmax);
+  return check_launch(h, "scan_argmax");
+}
+
+void free_all(spec_verify_handle* h) {
+  void* ptrs[] = {h->parts, h->draw, h->tsum_w, h->tsum_p, h->ema, h->steps, h->stats};
+  for (void* p : ptrs)
+    if (p != nullptr) (void)hipFree(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_verify_version(void) { return "specverify 0.1 (gfx950)"; }
+
+int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int logits_dtype,
+                     double ema_decay) {
+  if (out == nullptr) return SV_EINVAL;
+  *out = nullptr;
+  if (logits_dtype != SV_DTYPE_F32 && logits_dtype != SV_DTYPE_BF16) return SV_EUNSUPPORTED;
+  if (max_batch < 1 || K < 1 || K > 63 || V < 1) return SV_EINVAL;
+  if ((long long)V * (K + 1) >= (1ll << 31)) return SV_EINVAL;
+  if (!(ema_decay >= 0.0 && ema_decay <= 1.0)) return SV_EINVAL;
+
+  spec_verify_handle* h = new (std::nothrow) spec_verify_handle();
+  if (h == nullptr) return SV_ENOMEM;
+  h->max_batch = max_batch;
+  h->K = K;
+  h->V = V;
+  h->dtype = logits_dtype;
+  h->decay = ema_decay;
+  h->target_wgs = env_int("SPEC_VERIFY_TARGET_WGS", 2048);
+  h->nseg_force = env_int("SPEC_VERIFY_NSEG", 0);
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return SV_EHIP;
+  }
+  h->ntiles_max = div_up(V, sv::kTileChunks);   // scalar path has the most tiles
+  const size_t n_parts = (size_t)max_batch * (2 * K + 1) * kMaxSeg;
+  const size_t n_tiles = (size_t)max_batch * h->ntiles_max;
+  bool ok = hipMalloc(&h->parts, n_parts * sizeof(sv::RowPart)) == hipSuccess &&
+            hipMalloc(&h->draw, (size_t)max_batch * sizeof(sv::DrawRow)) == hipSuccess &&
+            hipMalloc(&h->tsum_w, n_tiles * sizeof(double)) == hipSuccess &&
+            hipMalloc(&h->tsum_p, n_tiles * sizeof(double)) == hipSuccess &&
+            hipMalloc(&h->ema, (size_t)max_batch * sizeof(double)) == hipSuccess &&
+            hipMalloc(&h->steps, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
+            hipMalloc(&h->stats, sizeof(sv::DevStats)) == hipSuccess;
+  if (!ok) {
+    free_all(h);
+    delete h;
+    return SV_ENOMEM;
+  }
+  hipLaunchKernelGGL(sv::fill_f64_i32, dim3(div_up(max_batch, 256)), dim3(256), 0, nullptr,
+                     h->ema, h->steps, max_batch, 0.0, 0);
+  hipLaunchKernelGGL(sv::fill_u64, dim3(1), dim3(64), 0, nullptr,
+                     reinterpret_cast<unsigned long long*>(h->stats),
+                     int(sizeof(sv::DevStats) / 8));
+  if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    free_all(h);
+    delete h;
+    return SV_EHIP;
+  }
+  *out = h;
+  return SV_OK;
+}
+
+int spec_verify_destroy(spec_verify_handle* h) {
+  if (h == nullptr) return SV_OK;
+  (void)spec_verify_profile(h, 0);
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+  return SV_OK;
+}
+
+int spec_verify_set_aux(spec_verify_handle* h, double* p_d, double* q_d, double* z,
+                        int32_t* argmax) {
+  if (h == nullptr) return SV_EINVAL;
+  h->aux_p = p_d;
+  h->aux_q = q_d;
+  h->aux_z = z;
+  h->aux_argmax = argmax;
+  return SV_OK;
+}
+
+int spec_verify(spec_verify_handle* h, int B, const void* target, const void* draft,
+                const int32_t* tokens, const float* uniforms, float temperature, int mode,
+                float tau, int32_t* out_tokens, int32_t* out_len, uint32_t* out_hist,
+                hipStream_t stream) {
+  if (h == nullptr) return SV_EINVAL;
+  h->err[0] = 0;
+  if (B < 1 || B > h->max_batch) return fail(h, SV_EINVAL, "B=%d outside [1, %d]", B, h->max_batch);
+  if (target == nullptr || tokens == nullptr || out_tokens == nullptr || out_len == nullptr ||
+      out_hist == nullptr)
+    return fail(h, SV_EINVAL, "required pointer is NULL");
+  if (mode != SV_MODE_STOCHASTIC && mode != SV_MODE_GREEDY && mode != SV_MODE_MARGIN)
+    return fail(h, SV_EINVAL, "unknown mode %d", mode);
+  const size_t es = h->dtype == SV_DTYPE_BF16 ? 2 : 4;
+  if (mode == SV_MODE_STOCHASTIC) {
+    if (draft == nullptr || uniforms == nullptr)
+      return fail(h, SV_EINVAL, "stochastic mode needs draft logits and uniforms");
+    if (!(std::isfinite(temperature) && temperature > 0.0f))
+      return fail(h, SV_EINVAL, "temperature must be finite and > 0");
+    if (!aligned(draft, es) || !aligned(uniforms, 4))
+      return fail(h, SV_EINVAL, "misaligned draft logits or uniforms");
+  }
+  if (mode == SV_MODE_MARGIN) {
+    if (!(std::isfinite(temperature) && temperature > 0.0f))
+      return fail(h, SV_EINVAL, "temperature must be finite and > 0");
+    if (!std::isfinite(tau)) return fail(h, SV_EINVAL, "tau must be finite");
+  }
+  if (!aligned(target, es) || !aligned(tokens, 4) || !aligned(out_tokens, 4) ||
+      !aligned(out_len, 4) || !aligned(out_hist, 4))
+    return fail(h, SV_EINVAL, "misaligned pointer");
+
+  const int full_vec = h->dtype == SV_DTYPE_BF16 ? 8 : 4;
+  bool vec = (h->V % full_vec) == 0 && aligned(target, 16);
+  if (mode == SV_MODE_STOCHASTIC) vec = vec && aligned(draft, 16);
+
+  int rc = SV_OK;
+  const float c = float(kLog2e / double(temperature));
+  if (mode == SV_MODE_STOCHASTIC) {
+    const int rows = 2 * h->K + 1;
+    if (h->dtype == SV_DTYPE_BF16) {
+      if (vec)
+        rc = run_stochastic<sv::DT_BF16, 8, SV_U_BF16>(
+            h, plan(h, B, rows, 8, SV_U_BF16), B, target, draft, tokens, uniforms, c,
+            out_tokens, out_len, out_hist, stream);
+      else
+        rc = run_stochastic<sv::DT_BF16, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, draft,
+                                                tokens, uniforms, c, out_tokens, out_len,
+                                                out_hist, stream);
+    } else {
+      if (vec)
+        rc = run_stochastic<sv::DT_F32, 4, SV_U_F32>(
+            h, plan(h, B, rows, 4, SV_U_F32), B, target, draft, tokens, uniforms, c,
+            out_tokens, out_len, out_hist, stream);
+      else
+        rc = run_stochastic<sv::DT_F32, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, draft,
+                                               tokens, uniforms, c, out_tokens, out_len,
+                                               out_hist, stream);
+    }
+  } else {
+    const bool margin = mode == SV_MODE_MARGIN;
+    const double invT = margin ? 1.0 / double(temperature) : 1.0;
+    const int rows = h->K + 1;
+    if (h->dtype == SV_DTYPE_BF16) {
+      if (vec)
+        rc = run_argmax<sv::DT_BF16, 8, SV_U_MAX>(h, plan(h, B, rows, 8, SV_U_MAX), B, target,
+                                                  tokens, margin, invT, double(tau), out_tokens,
+                                                  out_len, out_hist, stream);
+      else
+        rc = run_argmax<sv::DT_BF16, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, tokens, margin,
+                                           invT, double(tau), out_tokens, out_len, out_hist,
+                                           stream);
+    } else {
+      if (vec)
+        rc = run_argmax<sv::DT_F32, 4, SV_U_MAX>(h, plan(h, B, rows, 4, SV_U_MAX), B, target,
+                                                 tokens, margin, invT, double(tau), out_tokens,
+                                                 out_len, out_hist, stream);
+      else
+        rc = run_argmax<sv::DT_F32, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, tokens, margin,
+                                          invT, double(tau), out_tokens, out_len, out_hist,
+                                          stream);
+    }
+  }
+  if (rc == SV_OK) {
+    ++h->calls;
+    if (h->prof_ev != nullptr && h->prof_n < h->prof_cap) {
+      prof_mark(h, 2, stream);
+      ++h->prof_n;
+    }
+  }
+  return rc;
+}
+
+int spec_verify_profile(spec_verify_handle* h, int enable) {
+  if (h == nullptr) return SV_EINVAL;
+  if (h->prof_ev != nullptr) {
+    (void)hipDeviceSynchronize();
+    for (int i = 0; i < 3 * h->prof_cap; ++i) (void)hipEventDestroy(h->prof_ev[i]);
+    delete[] h->prof_ev;
+    h->prof_ev = nullptr;
+    h->prof_cap = h->prof_n = 0;
+  }
+  if (!enable) return SV_OK;
+  h->prof_ev = new (std::nothrow) hipEvent_t[3 * kProfCalls];
+  if (h->prof_ev == nullptr) return SV_ENOMEM;
+  for (int i = 0; i < 3 * kProfCalls; ++i) {
+    if (hipEventCreate(&h->prof_ev[i]) != hipSuccess) {
+      for (int k = 0; k < i; ++k) (void)hipEventDestroy(h->prof_ev[k]);
+      delete[] h->prof_ev;
+      h->prof_ev = nullptr;
+      return fail(h, SV_EHIP, "hipEventCreate failed");
+    }
+  }
+  h->prof_cap = kProfCalls;
+  h->prof_n = 0;
+  return SV_OK;
+}
+
+int spec_verify_profile_read(spec_verify_handle* h, double* stream_pass_ms, double* call_ms,
+                             int* n_calls) {
+  if (h == nullptr || h->prof_ev == nullptr) return SV_EINVAL;
+  double a = 0.0, b = 0.0;
+  for (int i = 0; i < h->prof_n; ++i) {
+    float t1 = 0.f, t2 = 0.f;
+    if (hipEventSynchronize(h->prof_ev[3 * i + 2]) != hipSuccess ||
+        hipEventElapsedTime(&t1, h->prof_ev[3 * i], h->prof_ev[3 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t2, h->prof_ev[3 * i], h->prof_ev[3 * i + 2]) != hipSuccess)
+      return fail(h, SV_EHIP, "event timing failed");
+    a += t1;
+    b += t2;
+  }
+  if (stream_pass_ms != nullptr) *stream_pass_ms = a;
+  if (call_ms != nullptr) *call_ms = b;
+  if (n_calls != nullptr) *n_calls = h->prof_n;
+  h->prof_n = 0;
+  return SV_OK;
+}
+
+int spec_verify_get_ema(spec_verify_handle* h, double* ema_dev, int32_t* steps_dev,
+                        hipStream_t stream) {
+  if (h == nullptr) return SV_EINVAL;
+  if (ema_dev != nullptr &&
+      hipMemcpyAsync(ema_dev, h->ema, (size_t)h->max_batch * sizeof(double),
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return fail(h, SV_EHIP, "get_ema copy failed");
+  if (steps_dev != nullptr &&
+      hipMemcpyAsync(steps_dev, h->steps, (size_t)h->max_batch * sizeof(int32_t),
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return fail(h, SV_EHIP, "get_ema copy failed");
+  return SV_OK;
+}
+
+int spec_verify_set_ema(spec_verify_handle* h, const double* ema_dev, const int32_t* steps_dev,
+                        hipStream_t stream) {
+  if (h == nullptr || ema_dev == nullptr || steps_dev == nullptr) return SV_EINVAL;
+  if (hipMemcpyAsync(h->ema, ema_dev, (size_t)h->max_batch * sizeof(double),
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(h->steps, steps_dev, (size_t)h->max_batch * sizeof(int32_t),
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return fail(h, SV_EHIP, "set_ema copy failed");
+  return SV_OK;
+}
+
+int spec_verify_reset_ema(spec_verify_handle* h, hipStream_t stream) {
+  if (h == nullptr) return SV_EINVAL;
+  hipLaunchKernelGGL(sv::fill_f64_i32, dim3(div_up(h->max_batch, 256)), dim3(256), 0, stream,
+                     h->ema, h->steps, h->max_batch, 0.0, 0);
+  return check_launch(h, "reset_ema");
+}
+
+int spec_verify_get_stats(spec_verify_handle* h, spec_verify_stats* out, int reset,
+                          hipStream_t stream) {
+  if (h == nullptr || out == nullptr) return SV_EINVAL;
+  sv::DevStats d;
+  if (hipMemcpyAsync(&d, h->stats, sizeof(d), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(h, SV_EHIP, "get_stats copy failed");
+  out->sequences = d.sequences;
+  out->invalid = d.invalid;
+  out->zero_q_accepts = d.zero_q_accepts;
+  out->z0_fallbacks = d.z0_fallbacks;
+  out->calls = h->calls;
+  if (reset) {
+    hipLaunchKernelGGL(sv::fill_u64, dim3(1), dim3(64), 0, stream,
+                       reinterpret_cast<unsigned long long*>(h->stats),
+                       int(sizeof(sv::DevStats) / 8));
+    h->calls = 0;
+    return check_launch(h, "reset_stats");
+  }
+  return SV_OK;
+}
+
+const char* spec_verify_last_error(const spec_verify_handle* h) {
+  return h == nullptr ? "null handle" : h->err;
+}
+
+}  // extern "C"

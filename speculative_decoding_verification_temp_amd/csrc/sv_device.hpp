@@ -1,0 +1,188 @@
+// Device helpers for the verification kernels: logit chunk loads and
+// unpacking, exact power-of-two rescaling of running sums, and fixed-order
+// wavefront / workgroup reductions (results never depend on timing).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;                 // threads per workgroup (4 wavefronts)
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kTileChunksPerLane = 4;       // draw tile: 4 chunks per lane of one wavefront
+constexpr int kTileChunks = kWave * kTileChunksPerLane;
+constexpr float kRefInit = -1.0e30f;        // reference exponent before any finite logit
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// A chunk is the unit one lane loads at once: 16 bytes on the vector path
+// (8 bf16 or 4 fp32 logits), one element on the scalar path.
+template <int DT, int VEC> struct Chunk;
+
+template <> struct Chunk<DT_BF16, 8> {
+  static constexpr int N = 8;
+  using raw_t = u32x4;
+  __device__ static inline raw_t load(const void* row, long long c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + c);
+  }
+  __device__ static inline void unpack(const raw_t& r, float (&x)[N]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(r[k] << 16);
+      x[2 * k + 1] = __uint_as_float(r[k] & 0xffff0000u);
+    }
+  }
+  // true iff any element is NaN (exponent all ones, mantissa non-zero)
+  __device__ static inline uint32_t nan_bits(const raw_t& r) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t lo = r[k] & 0x7fffu, hi = (r[k] >> 16) & 0x7fffu;
+      m |= (lo > 0x7f80u) | (hi > 0x7f80u);
+    }
+    return m;
+  }
+};
+
+template <> struct Chunk<DT_F32, 4> {
+  static constexpr int N = 4;
+  using raw_t = u32x4;
+  __device__ static inline raw_t load(const void* row, long long c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + c);
+  }
+  __device__ static inline void unpack(const raw_t& r, float (&x)[N]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(r[k]);
+  }
+  __device__ static inline uint32_t nan_bits(const raw_t& r) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m |= ((r[k] & 0x7fffffffu) > 0x7f800000u);
+    return m;
+  }
+};
+
+template <> struct Chunk<DT_BF16, 1> {
+  static constexpr int N = 1;
+  using raw_t = uint32_t;
+  __device__ static inline raw_t load(const void* row, long long c) {
+    return reinterpret_cast<const uint16_t*>(row)[c];
+  }
+  __device__ static inline void unpack(const raw_t& r, float (&x)[N]) {
+    x[0] = __uint_as_float(r << 16);
+  }
+  __device__ static inline uint32_t nan_bits(const raw_t& r) { return (r & 0x7fffu) > 0x7f80u; }
+};
+
+template <> struct Chunk<DT_F32, 1> {
+  static constexpr int N = 1;
+  using raw_t = uint32_t;
+  __device__ static inline raw_t load(const void* row, long long c) {
+    return reinterpret_cast<const uint32_t*>(row)[c];
+  }
+  __device__ static inline void unpack(const raw_t& r, float (&x)[N]) { x[0] = __uint_as_float(r); }
+  __device__ static inline uint32_t nan_bits(const raw_t& r) {
+    return (r & 0x7fffffffu) > 0x7f800000u;
+  }
+};
+
+template <int DT> __device__ inline float load_logit(const void* row, long long v) {
+  if constexpr (DT == DT_BF16)
+    return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[v]) << 16);
+  else
+    return reinterpret_cast<const float*>(row)[v];
+}
+
+template <int DT> constexpr int elem_bytes() { return DT == DT_BF16 ? 2 : 4; }
+
+// One softmax term relative to an integer reference exponent R:
+// 2^(x * c - R), where c = log2(e) / T. The same expression (one fma, one
+// hardware exp2) is used wherever a term is formed, so a row and its gathered
+// element, and two bitwise-equal rows, give bitwise-equal results.
+__device__ inline float term(float x, float c, float R) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -R));
+}
+
+// Scale a float64 sum by 2^(from - to) exactly (from <= to, both integers or
+// the initial reference). Saturating conversion keeps the empty state at 0.
+__device__ inline double rescale(double s, float from, float to) {
+  float d = fmaxf(from - to, -2000.0f);   // also maps NaN (inf - inf) to -2000
+  return __builtin_ldexp(s, int(d));
+}
+
+// ---- wavefront reductions (fixed butterfly order) ----
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ inline uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// (value, index) max; equal values keep the lower index. Index -1 = empty.
+__device__ inline void argmax_combine(float& m, int& i, float m2, int i2) {
+  bool take = (i2 >= 0) && (i < 0 || m2 > m || (m2 == m && i2 < i));
+  m = take ? m2 : m;
+  i = take ? i2 : i;
+}
+
+__device__ inline void wave_argmax(float& m, int& i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, kWave);
+    int i2 = __shfl_xor(i, o, kWave);
+    argmax_combine(m, i, m2, i2);
+  }
+}
+
+// Inclusive prefix sum over the lanes of a wavefront (Hillis-Steele).
+__device__ inline double wave_incl_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Per-row partial produced by the streaming pass, one per (row, segment).
+struct RowPart {
+  double S;      // sum of 2^(x*c - R) over the segment (stochastic rows)
+  float R;       // integer reference exponent of S
+  float m;       // max raw logit (greedy/margin rows)
+  int idx;       // lowest index attaining m (greedy/margin rows), -1 if none
+  int flags;     // bit 0: NaN seen (greedy/margin rows)
+};
+
+// Final statistics of the row a sequence draws from, left by the scan for the
+// draw kernels.
+struct DrawRow {
+  double S_t, S_d;
+  float R_t, R_d;
+  int j;         // rejection index (K = bonus), -1 = nothing to draw
+  int pad;
+};
+
+struct DevStats {
+  unsigned long long sequences;
+  unsigned long long invalid;
+  unsigned long long zero_q_accepts;
+  unsigned long long z0_fallbacks;
+};
+
+}  // namespace sv

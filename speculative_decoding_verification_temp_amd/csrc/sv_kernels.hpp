@@ -1,0 +1,645 @@
+// Verification kernels for gfx950.
+//
+//   rowstats_sum   streaming pass over every (row, segment) of the target and
+//                  draft logits: running sum of softmax terms relative to an
+//                  integer reference exponent (stochastic mode).
+//   rowstats_max   streaming pass over target rows: max, lowest-index argmax
+//                  and a NaN flag (greedy and margin modes).
+//   scan_*         one wavefront per sequence: combine segment partials, form
+//                  p(d), q(d) (or argmax matches / margin ratios), find the
+//                  first rejection with a ballot, emit tokens, histogram, EMA.
+//   draw_tiles     per-tile sums of the residual [p_j - q_j]_+ (or of p_K for
+//                  the bonus, or of p_j for the Z = 0 fallback).
+//   draw_pick      one wavefront per sequence: prefix over tile sums, then a
+//                  re-read of the crossing tile with a wavefront prefix scan
+//                  to find the drawn token.
+//
+// None of the kernels use floating-point atomics; every reduction has a fixed
+// order, so reruns are bitwise identical.
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+// --------------------------------------------------------------------------
+// Row addressing. Stochastic rows of sequence b: r = 0..K are target rows,
+// r = K+1..2K are draft rows 0..K-1. Greedy/margin rows: r = 0..K target.
+// --------------------------------------------------------------------------
+template <int DT>
+__device__ inline const void* row_ptr(const void* target, const void* draft, int b, int r,
+                                      int K, int V) {
+  constexpr int s = elem_bytes<DT>();
+  if (r <= K)
+    return static_cast<const char*>(target) + ((long long)b * (K + 1) + r) * (long long)V * s;
+  return static_cast<const char*>(draft) + ((long long)b * K + (r - K - 1)) * (long long)V * s;
+}
+
+// --------------------------------------------------------------------------
+// Streaming softmax normaliser. Each lane keeps a float64 sum S of
+// 2^(x*c - R) with an integer reference R >= max(x)*c; when a new chunk group
+// raises the maximum, S is rescaled by an exact power of two. Within a group
+// the terms are added pairwise in fp32 and the group total is added to S in
+// fp64.
+// --------------------------------------------------------------------------
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_sum(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, int nseg,
+    int seg_chunks, float c, RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+  using C = Chunk<DT, VEC>;
+  const int tid = threadIdx.x;
+  const long long wg = blockIdx.x;
+  const int rows = 2 * K + 1;
+  const int seg = int(wg % nseg);
+  const long long grow = wg / nseg;
+  const int b = int(grow / rows), r = int(grow % rows);
+  if (wg == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+
+  const void* row = row_ptr<DT>(target, draft, b, r, K, V);
+  const long long nchunks = V / VEC;
+  const long long c0 = (long long)seg * seg_chunks;
+  const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
+
+  float R = kRefInit;
+  double S = 0.0;
+  long long ci = c0 + tid;
+  // full groups of U chunks per lane
+  for (; ci + (long long)(U - 1) * kBlock < c1; ci += (long long)U * kBlock) {
+    typename C::raw_t raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = C::load(row, ci + (long long)u * kBlock);
+    float x[U][C::N];
+#pragma unroll
+    for (int u = 0; u < U; ++u) C::unpack(raw[u], x[u]);
+    float gm = x[0][0];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < C::N; ++k) gm = fmaxf(gm, x[u][k]);
+    const float Rn = fmaxf(R, ceilf(gm * c));
+    S = rescale(S, R, Rn);
+    R = Rn;
+    float t[U * C::N];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < C::N; ++k) t[u * C::N + k] = term(x[u][k], c, R);
+#pragma unroll
+    for (int w = 1; w < U * C::N; w <<= 1)
+#pragma unroll
+      for (int k = 0; k + w < U * C::N; k += 2 * w) t[k] += t[k + w];
+    S += (double)t[0];
+  }
+  // remainder, one chunk at a time
+  for (; ci < c1; ci += kBlock) {
+    typename C::raw_t raw = C::load(row, ci);
+    float x[C::N];
+    C::unpack(raw, x);
+    float gm = x[0];
+#pragma unroll
+    for (int k = 1; k < C::N; ++k) gm = fmaxf(gm, x[k]);
+    const float Rn = fmaxf(R, ceilf(gm * c));
+    S = rescale(S, R, Rn);
+    R = Rn;
+    float t[C::N];
+#pragma unroll
+    for (int k = 0; k < C::N; ++k) t[k] = term(x[k], c, R);
+#pragma unroll
+    for (int w = 1; w < C::N; w <<= 1)
+#pragma unroll
+      for (int k = 0; k + w < C::N; k += 2 * w) t[k] += t[k + w];
+    S += (double)t[0];
+  }
+
+  // workgroup combine: common reference, exact rescale, fixed-order sums
+  __shared__ float sR[kWavesPerBlock];
+  __shared__ double sS[kWavesPerBlock];
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  float Rw = wave_max(R);
+  double Sw = wave_sum(rescale(S, R, Rw));
+  if (lane == 0) {
+    sR[wid] = Rw;
+    sS[wid] = Sw;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Rb = sR[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) Rb = fmaxf(Rb, sR[w]);
+    double Sb = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) Sb += rescale(sS[w], sR[w], Rb);
+    RowPart p;
+    p.S = Sb;
+    p.R = Rb;
+    p.m = 0.0f;
+    p.idx = -1;
+    p.flags = 0;
+    parts[wg] = p;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Streaming max / argmax / NaN flag over target rows (greedy, margin).
+// A lane remembers the first chunk in which its running maximum was reached
+// and finds the lowest matching element in it at the end.
+// --------------------------------------------------------------------------
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ target, int K,
+                                                       int V, int nseg, int seg_chunks,
+                                                       RowPart* __restrict__ parts,
+                                                       uint32_t* __restrict__ hist) {
+  using C = Chunk<DT, VEC>;
+  const int tid = threadIdx.x;
+  const long long wg = blockIdx.x;
+  const int rows = K + 1;
+  const int seg = int(wg % nseg);
+  const long long grow = wg / nseg;
+  const int b = int(grow / rows), r = int(grow % rows);
+  if (wg == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+
+  const void* row = row_ptr<DT>(target, nullptr, b, r, K, V);
+  const long long nchunks = V / VEC;
+  const long long c0 = (long long)seg * seg_chunks;
+  const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
+
+  float best = -__builtin_inff();
+  long long best_c = -1;
+  typename C::raw_t best_raw{};
+  uint32_t nan = 0;
+  long long ci = c0 + tid;
+  for (; ci + (long long)(U - 1) * kBlock < c1; ci += (long long)U * kBlock) {
+    typename C::raw_t raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = C::load(row, ci + (long long)u * kBlock);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[C::N];
+      C::unpack(raw[u], x);
+      float cm = x[0];
+#pragma unroll
+      for (int k = 1; k < C::N; ++k) cm = fmaxf(cm, x[k]);
+      nan |= C::nan_bits(raw[u]);
+      const bool up = cm > best;
+      best = up ? cm : best;
+      best_c = up ? ci + (long long)u * kBlock : best_c;
+      best_raw = up ? raw[u] : best_raw;
+    }
+  }
+  for (; ci < c1; ci += kBlock) {
+    typename C::raw_t raw = C::load(row, ci);
+    float x[C::N];
+    C::unpack(raw, x);
+    float cm = x[0];
+#pragma unroll
+    for (int k = 1; k < C::N; ++k) cm = fmaxf(cm, x[k]);
+    nan |= C::nan_bits(raw);
+    const bool up = cm > best;
+    best = up ? cm : best;
+    best_c = up ? ci : best_c;
+    best_raw = up ? raw : best_raw;
+  }
+  int idx = -1;
+  if (best_c >= 0) {
+    float x[C::N];
+    C::unpack(best_raw, x);
+    int e = C::N - 1;
+#pragma unroll
+    for (int k = C::N - 1; k >= 0; --k) e = (x[k] == best) ? k : e;
+    idx = int(best_c * VEC + e);
+  }
+
+  __shared__ float sm[kWavesPerBlock];
+  __shared__ int si[kWavesPerBlock];
+  __shared__ uint32_t sn[kWavesPerBlock];
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  wave_argmax(best, idx);
+  nan = wave_or(nan);
+  if (lane == 0) {
+    sm[wid] = best;
+    si[wid] = idx;
+    sn[wid] = nan;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m = sm[0];
+    int i = si[0];
+    uint32_t f = sn[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) {
+      argmax_combine(m, i, sm[w], si[w]);
+      f |= sn[w];
+    }
+    RowPart p;
+    p.S = 0.0;
+    p.R = 0.0f;
+    p.m = m;
+    p.idx = i;
+    p.flags = f ? 1 : 0;
+    parts[wg] = p;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Scan helpers
+// --------------------------------------------------------------------------
+__device__ inline void combine_sum_parts(const RowPart* p, int nseg, float& R, double& S) {
+  R = p[0].R;
+  for (int s = 1; s < nseg; ++s) R = fmaxf(R, p[s].R);
+  S = 0.0;
+  for (int s = 0; s < nseg; ++s) S += rescale(p[s].S, p[s].R, R);
+}
+
+__device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, int& idx,
+                                         int& nan) {
+  m = p[0].m;
+  idx = p[0].idx;
+  nan = p[0].flags;
+  for (int s = 1; s < nseg; ++s) {
+    argmax_combine(m, idx, p[s].m, p[s].idx);
+    nan |= p[s].flags;
+  }
+}
+
+__device__ inline bool finite_pos(double S) { return S > 0.0 && S < __builtin_inf(); }
+
+__device__ inline void emit_and_update(int lane, int b, int K, int j, bool bad,
+                                       const int32_t* __restrict__ tokens,
+                                       int32_t* __restrict__ out_tokens,
+                                       int32_t* __restrict__ out_len,
+                                       uint32_t* __restrict__ hist, double* __restrict__ ema,
+                                       int32_t* __restrict__ steps, double decay,
+                                       DevStats* __restrict__ st, int fill_at_j, int d) {
+  if (lane <= K) {
+    int v;
+    if (bad)
+      v = -1;
+    else if (lane < j)
+      v = d;
+    else if (lane == j)
+      v = fill_at_j;
+    else
+      v = -1;
+    out_tokens[(long long)b * (K + 1) + lane] = v;
+  }
+  if (lane == 0) {
+    out_len[b] = bad ? -1 : j;
+    if (bad) {
+      atomicAdd(&st->invalid, 1ull);
+    } else {
+      atomicAdd(&hist[j], 1u);
+      atomicAdd(&st->sequences, 1ull);
+      const double x = double(j) / double(K);
+      const int n = steps[b];
+      ema[b] = (n == 0) ? x : decay * ema[b] + (1.0 - decay) * x;
+      steps[b] = n + 1;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Stochastic scan: lane i tests position i.
+// --------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kBlock) void scan_stochastic(
+    int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
+    const void* __restrict__ target, const void* __restrict__ draft,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+    uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
+    double decay, DevStats* __restrict__ st, DrawRow* __restrict__ draw, double* aux_p,
+    double* aux_q, double* aux_z) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (b >= B) return;
+  const int rows = 2 * K + 1;
+  const RowPart* pb = parts + (long long)b * rows * nseg;
+
+  float Rt = 0.0f, Rd = 0.0f;
+  double St = 1.0, Sd = 1.0;
+  bool lane_bad = false;
+  if (lane <= K) {
+    combine_sum_parts(pb + (long long)lane * nseg, nseg, Rt, St);
+    lane_bad |= !finite_pos(St);
+  }
+  int d = 0;
+  double P = 0.0, Q = 1.0;
+  bool keep = true, zq = false;
+  if (lane < K) {
+    combine_sum_parts(pb + (long long)(K + 1 + lane) * nseg, nseg, Rd, Sd);
+    lane_bad |= !finite_pos(Sd);
+    d = tokens[(long long)b * K + lane];
+    const bool dok = d >= 0 && d < V;
+    lane_bad |= !dok;
+    if (!lane_bad) {
+      const float xt = load_logit<DT>(row_ptr<DT>(target, draft, b, lane, K, V), d);
+      const float xd = load_logit<DT>(row_ptr<DT>(target, draft, b, K + 1 + lane, K, V), d);
+      P = double(term(xt, c, Rt)) / St;
+      Q = double(term(xd, c, Rd)) / Sd;
+      const double u = uniforms[(long long)b * (K + 1) + lane];
+      keep = (P >= Q) || (u < P / Q);
+      zq = keep && Q == 0.0;
+    }
+  }
+  const bool bad = __any(lane_bad);
+  const unsigned long long rej = __ballot(lane < K && !keep);
+  const int j = rej ? __ffsll((long long)rej) - 1 : K;
+
+  if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = bad ? __builtin_nan("") : P;
+  if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = bad ? __builtin_nan("") : Q;
+
+  // statistics of row j for the draw
+  const float Rtj = __shfl(Rt, j, kWave), Rdj = __shfl(Rd, j, kWave);
+  const double Stj = __shfl(St, j, kWave), Sdj = __shfl(Sd, j, kWave);
+  if (lane == 0) {
+    DrawRow dr;
+    dr.S_t = Stj;
+    dr.S_d = Sdj;
+    dr.R_t = Rtj;
+    dr.R_d = Rdj;
+    dr.j = bad ? -1 : j;
+    dr.pad = 0;
+    draw[b] = dr;
+    if (bad && aux_z != nullptr) aux_z[b] = -1.0;
+  }
+  const unsigned long long zqm = __ballot(zq && lane < j);
+  if (lane == 0 && !bad && zqm) atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
+  emit_and_update(lane, b, K, j, bad, tokens, out_tokens, out_len, hist, ema, steps, decay, st,
+                  -1, d);
+}
+
+// --------------------------------------------------------------------------
+// Greedy / margin scan over the argmax partials.
+// --------------------------------------------------------------------------
+template <int DT, bool MARGIN>
+__global__ __launch_bounds__(kBlock) void scan_argmax(
+    int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
+    const void* __restrict__ target, const int32_t* __restrict__ tokens, double invT,
+    double tau, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+    uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
+    double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
+    int32_t* aux_argmax) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (b >= B) return;
+  const RowPart* pb = parts + (long long)b * (K + 1) * nseg;
+
+  float m = 0.0f;
+  int A = -1, nan = 0;
+  bool lane_bad = false;
+  if (lane <= K) {
+    combine_max_parts(pb + (long long)lane * nseg, nseg, m, A, nan);
+    lane_bad |= nan != 0 || !(m > -__builtin_inff() && m < __builtin_inff()) || A < 0;
+  }
+  int d = 0;
+  bool keep = true;
+  double ratio = __builtin_nan("");
+  if (lane < K) {
+    d = tokens[(long long)b * K + lane];
+    lane_bad |= !(d >= 0 && d < V);
+    if (!lane_bad) {
+      if constexpr (MARGIN) {
+        const float xd = load_logit<DT>(row_ptr<DT>(target, nullptr, b, lane, K, V), d);
+        ratio = exp((double(xd) - double(m)) * invT);
+        keep = (d == A) || (ratio > tau);
+      } else {
+        keep = (d == A);
+      }
+    }
+  }
+  const bool bad = __any(lane_bad);
+  const unsigned long long rej = __ballot(lane < K && !keep);
+  const int j = rej ? __ffsll((long long)rej) - 1 : K;
+  const int Aj = __shfl(A, j, kWave);
+
+  if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = bad ? __builtin_nan("") : ratio;
+  if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = __builtin_nan("");
+  if (aux_z != nullptr && lane == 0) aux_z[b] = -1.0;
+  if (aux_argmax != nullptr && lane <= K) aux_argmax[(long long)b * (K + 1) + lane] = A;
+  emit_and_update(lane, b, K, j, bad, tokens, out_tokens, out_len, hist, ema, steps, decay, st,
+                  Aj, d);
+}
+
+// --------------------------------------------------------------------------
+// Draw, phase 1: tile sums of the draw weights. Weight of token v:
+//   j < K : max(0, p_j(v) - q_j(v))       (residual)
+//   j = K : p_K(v)                        (bonus)
+// plus, for j < K, the tile sums of p_j(v) for the Z = 0 fallback.
+// A tile is kTileChunks consecutive chunks; one wavefront sums one tile.
+// --------------------------------------------------------------------------
+template <int DT, int VEC> struct DrawWeights {
+  using C = Chunk<DT, VEC>;
+  const void* trow;
+  const void* drow;
+  float c, Rt, Rd;
+  double invSt, invSd;
+  bool residual;
+
+  __device__ inline void init(const void* target, const void* draft, const DrawRow& dr, int b,
+                              int K, int V, float c_) {
+    c = c_;
+    residual = dr.j < K;
+    trow = row_ptr<DT>(target, draft, b, dr.j, K, V);
+    drow = residual ? row_ptr<DT>(target, draft, b, K + 1 + dr.j, K, V) : nullptr;
+    Rt = dr.R_t;
+    Rd = dr.R_d;
+    invSt = 1.0 / dr.S_t;
+    invSd = 1.0 / dr.S_d;
+  }
+  // weights of one chunk: w = draw weight, pw = p_j weight (fallback)
+  __device__ inline void chunk(long long ci, double (&w)[C::N], double (&pw)[C::N]) const {
+    float xt[C::N];
+    C::unpack(C::load(trow, ci), xt);
+    if (residual) {
+      float xd[C::N];
+      C::unpack(C::load(drow, ci), xd);
+#pragma unroll
+      for (int k = 0; k < C::N; ++k) {
+        const double p = double(term(xt[k], c, Rt)) * invSt;
+        const double q = double(term(xd[k], c, Rd)) * invSd;
+        w[k] = fmax(p - q, 0.0);
+        pw[k] = p;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < C::N; ++k) {
+        const double p = double(term(xt[k], c, Rt)) * invSt;
+        w[k] = p;
+        pw[k] = p;
+      }
+    }
+  }
+};
+
+template <int DT, int VEC>
+__global__ __launch_bounds__(kBlock) void draw_tiles(
+    int B, int K, int V, int ntiles, int tiles_per_wave, int waves_per_seq,
+    const void* __restrict__ target, const void* __restrict__ draft,
+    const DrawRow* __restrict__ draw, float c, double* __restrict__ tsum_w,
+    double* __restrict__ tsum_p) {
+  using C = Chunk<DT, VEC>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const long long gw = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int b = int(gw / waves_per_seq);
+  if (b >= B) return;
+  const int w = int(gw % waves_per_seq);
+  const DrawRow dr = draw[b];
+  if (dr.j < 0) return;
+  DrawWeights<DT, VEC> W;
+  W.init(target, draft, dr, b, K, V, c);
+  const long long nchunks = V / VEC;
+  const int t0 = w * tiles_per_wave, t1 = min(ntiles, t0 + tiles_per_wave);
+  for (int t = t0; t < t1; ++t) {
+    double aw = 0.0, ap = 0.0;
+#pragma unroll
+    for (int k = 0; k < kTileChunksPerLane; ++k) {
+      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
+      if (ci < nchunks) {
+        double wv[C::N], pv[C::N];
+        W.chunk(ci, wv, pv);
+#pragma unroll
+        for (int e = 0; e < C::N; ++e) {
+          aw += wv[e];
+          ap += pv[e];
+        }
+      }
+    }
+    aw = wave_sum(aw);
+    if (lane == 0) tsum_w[(long long)b * ntiles + t] = aw;
+    if (W.residual) {
+      ap = wave_sum(ap);
+      if (lane == 0) tsum_p[(long long)b * ntiles + t] = ap;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Draw, phase 2: one wavefront per sequence.
+// --------------------------------------------------------------------------
+template <int DT, int VEC>
+__global__ __launch_bounds__(kBlock) void draw_pick(
+    int B, int K, int V, int ntiles, const void* __restrict__ target,
+    const void* __restrict__ draft, const DrawRow* __restrict__ draw,
+    const float* __restrict__ uniforms, float c, const double* __restrict__ tsum_w,
+    const double* __restrict__ tsum_p, int32_t* __restrict__ out_tokens,
+    DevStats* __restrict__ st, double* aux_z) {
+  using C = Chunk<DT, VEC>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (b >= B) return;
+  const DrawRow dr = draw[b];
+  if (dr.j < 0) return;
+  DrawWeights<DT, VEC> W;
+  W.init(target, draft, dr, b, K, V, c);
+
+  // total of the draw weights, as the end of an in-order prefix over tiles
+  const double* ts = tsum_w + (long long)b * ntiles;
+  double carry = 0.0;
+  for (int t0 = 0; t0 < ntiles; t0 += kWave) {
+    const double v = (t0 + lane < ntiles) ? ts[t0 + lane] : 0.0;
+    carry += __shfl(wave_incl_scan(v, lane), kWave - 1, kWave);
+  }
+  const double Zr = carry;
+  const bool fallback = W.residual && !(Zr > 0.0);
+  if (fallback) {
+    ts = tsum_p + (long long)b * ntiles;
+    carry = 0.0;
+    for (int t0 = 0; t0 < ntiles; t0 += kWave) {
+      const double v = (t0 + lane < ntiles) ? ts[t0 + lane] : 0.0;
+      carry += __shfl(wave_incl_scan(v, lane), kWave - 1, kWave);
+    }
+  }
+  const double total = carry;
+  const double tgt = double(uniforms[(long long)b * (K + 1) + K]) * total;
+
+  // crossing tile: first tile whose inclusive prefix exceeds tgt; if none
+  // (rounding), the last tile with positive weight
+  int tile = -1, last_pos = -1;
+  double base = 0.0;
+  carry = 0.0;
+  for (int t0 = 0; t0 < ntiles && tile < 0; t0 += kWave) {
+    const double v = (t0 + lane < ntiles) ? ts[t0 + lane] : 0.0;
+    const double incl = carry + wave_incl_scan(v, lane);
+    const unsigned long long hit = __ballot(t0 + lane < ntiles && incl > tgt);
+    const unsigned long long pos = __ballot(t0 + lane < ntiles && v > 0.0);
+    if (pos) last_pos = t0 + 63 - __clzll((long long)pos);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      tile = t0 + l;
+      base = __shfl(incl - v, l, kWave);
+    }
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  const bool clamp = tile < 0;
+  if (clamp) tile = last_pos;
+
+  // re-read the crossing tile; in-order prefix over its chunks. If rounding
+  // leaves no crossing inside the tile, take its last positive-weight token.
+  const long long nchunks = V / VEC;
+  int token = -1, last_elem = -1;
+  for (int k = 0; k < kTileChunksPerLane && token < 0; ++k) {
+    const long long ci = (long long)tile * kTileChunks + (long long)k * kWave + lane;
+    double wv[C::N], pv[C::N];
+    double cs = 0.0;
+    const bool valid = tile >= 0 && ci < nchunks;
+    int lp = -1;
+    if (valid) {
+      W.chunk(ci, wv, pv);
+      if (fallback) {
+#pragma unroll
+        for (int e = 0; e < C::N; ++e) wv[e] = pv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < C::N; ++e) {
+        cs += wv[e];
+        lp = (wv[e] > 0.0) ? int(ci * VEC + e) : lp;
+      }
+    }
+    int lpw = lp;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) lpw = max(lpw, __shfl_xor(lpw, o, kWave));
+    last_elem = max(last_elem, lpw);
+    if (clamp) continue;
+    const double incl = base + wave_incl_scan(cs, lane);
+    const unsigned long long hit = __ballot(valid && incl > tgt);
+    if (hit) {
+      const int l = __ffsll((long long)hit) - 1;
+      int tok = -1;
+      if (lane == l) {
+        double run = incl - cs;
+#pragma unroll
+        for (int e = 0; e < C::N; ++e) {
+          run += wv[e];
+          if (tok < 0 && run > tgt) tok = int(ci * VEC + e);
+        }
+        if (tok < 0) tok = lp;   // the chunk holds positive weight (cs > 0)
+      }
+      token = __shfl(tok, l, kWave);
+    }
+    base = __shfl(incl, kWave - 1, kWave);
+  }
+  if (token < 0) token = last_elem;
+  if (lane == 0) {
+    out_tokens[(long long)b * (K + 1) + dr.j] = token;
+    if (aux_z != nullptr) aux_z[b] = W.residual ? Zr : -1.0;
+    if (fallback) atomicAdd(&st->z0_fallbacks, 1ull);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Small utilities
+// --------------------------------------------------------------------------
+__global__ void fill_f64_i32(double* a, int32_t* b, int n, double va, int32_t vb) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    a[i] = va;
+    b[i] = vb;
+  }
+}
+
+__global__ void fill_u64(unsigned long long* a, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] = 0ull;
+}
+
+}  // namespace sv

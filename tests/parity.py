@@ -1,0 +1,99 @@
+"""GPU-vs-oracle comparison helpers for the parity tests.
+
+The rule: emitted tokens, accept lengths and argmaxes must be identical for
+every sequence whose decisions all lie at least 1e-6 (in uniform units) from a
+decision boundary, as measured by the fp64 oracle; sequences closer than that
+are counted and excused, and must be rare. p(d), q(d), margin ratios and Z
+must agree within 1e-5 absolute.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import spec_oracle as O
+from workloads import to_host_f64
+
+BOUNDARY = 1e-6
+PROB_TOL = 1e-5
+
+
+def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None):
+    """Run the oracle on the listed sequences of a generated input dict."""
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = torch.as_tensor(rows, device=x["target"].device)
+    tgt = to_host_f64(x["target"].index_select(0, idx))
+    drf = to_host_f64(x["draft"].index_select(0, idx)) if mode == "stochastic" else None
+    tok = x["tokens"].index_select(0, idx).cpu().numpy()
+    uni = x["uniforms"].index_select(0, idx).cpu().double().numpy()
+    m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
+    if ema is not None:
+        # EMA slots are batch rows: feed the oracle a state indexed by row
+        sub = O.EmaState(len(rows), ema.decay)
+        sub.ema[:] = ema.ema[rows]
+        sub.steps[:] = ema.steps[rows]
+        res = O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau, ema=sub)
+        ema.ema[rows] = sub.ema
+        ema.steps[rows] = sub.steps
+        return res
+    return O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau)
+
+
+def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
+    """Compare GPU outputs (full-batch tensors) on `rows` against oracle
+    results for the same rows. Returns a small report dict."""
+    rows = np.asarray(rows, dtype=np.int64)
+    g_tok = tokens.cpu().numpy()[rows].astype(np.int64)
+    g_len = accept_len.cpu().numpy()[rows].astype(np.int64)
+    strict = ref.min_dist >= BOUNDARY
+    bad_len = np.flatnonzero(strict & (g_len != ref.accept_len))
+    bad_tok = np.flatnonzero(strict & np.any(g_tok != ref.tokens, axis=1))
+    assert len(bad_len) == 0 and len(bad_tok) == 0, (
+        f"{label}: {len(bad_len)} accept_len and {len(bad_tok)} token mismatches; "
+        f"first rows {rows[bad_tok[:5]] if len(bad_tok) else rows[bad_len[:5]]}; "
+        f"gpu {g_tok[bad_tok[:2]] if len(bad_tok) else g_len[bad_len[:5]]} "
+        f"oracle {ref.tokens[bad_tok[:2]] if len(bad_tok) else ref.accept_len[bad_len[:5]]}")
+    report = dict(rows=len(rows), excused=int((~strict).sum()))
+    if aux is not None:
+        valid = ref.accept_len >= 0
+        if mode in ("stochastic", "margin"):
+            gp = aux["p_d"].cpu().numpy()[rows]
+            err = np.abs(gp[valid] - ref.p_d[valid])
+            assert np.nanmax(err, initial=0.0) <= PROB_TOL, f"{label}: p_d err {np.nanmax(err)}"
+            report["p_err"] = float(np.nanmax(err, initial=0.0))
+        if mode == "stochastic":
+            gq = aux["q_d"].cpu().numpy()[rows]
+            err = np.abs(gq[valid] - ref.q_d[valid])
+            assert np.nanmax(err, initial=0.0) <= PROB_TOL, f"{label}: q_d err {np.nanmax(err)}"
+            report["q_err"] = float(np.nanmax(err, initial=0.0))
+            gz = aux["z"].cpu().numpy()[rows]
+            sel = valid & strict
+            zerr = np.abs(gz[sel] - ref.z[sel])
+            assert np.max(zerr, initial=0.0) <= PROB_TOL, f"{label}: Z err {np.max(zerr)}"
+            report["z_err"] = float(np.max(zerr, initial=0.0))
+        if mode in ("greedy", "margin"):
+            ga = aux["argmax"].cpu().numpy()[rows]
+            assert np.array_equal(ga[valid], ref.argmax[valid]), f"{label}: argmax mismatch"
+    return report
+
+
+def check_invariants(tokens, accept_len, hist, drafts, V: int, K: int):
+    """Properties that hold at any size for the GPU outputs."""
+    t = tokens.cpu().numpy().astype(np.int64)
+    j = accept_len.cpu().numpy().astype(np.int64)
+    h = hist.cpu().numpy().astype(np.int64)
+    d = drafts.cpu().numpy().astype(np.int64)
+    valid = j >= 0
+    assert h.sum() == valid.sum()
+    assert (np.arange(K + 1) * h).sum() == j[valid].sum()
+    assert np.array_equal(np.bincount(j[valid], minlength=K + 1), h)
+    pos = np.arange(K + 1)[None, :]
+    jj = np.where(valid, j, 0)[:, None]
+    dpad = np.concatenate([d, np.full((d.shape[0], 1), -7)], axis=1)
+    tv, dv, jv = t[valid], dpad[valid], jj[valid]
+    assert np.all((pos >= jv) | (tv == dv))
+    at_j = np.take_along_axis(tv, jv, axis=1)[:, 0]
+    assert np.all((at_j >= 0) & (at_j < V))
+    assert np.all((pos <= jv) | (tv == -1))
+    assert np.all(t[~valid] == -1)
