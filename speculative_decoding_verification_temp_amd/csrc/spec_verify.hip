@@ -44,8 +44,7 @@ struct spec_verify_handle {
   double decay = 0.99;
   sv::RowPart* parts = nullptr;
   sv::DrawRow* draw = nullptr;
-  double* tsum_w = nullptr;
-  double* tsum_p = nullptr;
+  sv::TileSums* tsum = nullptr;
   double* ema = nullptr;
   int32_t* steps = nullptr;
   sv::DevStats* stats = nullptr;
@@ -117,7 +116,8 @@ void prof_mark(spec_verify_handle* h, int k, hipStream_t s) {
 template <int DT, int VEC, int U>
 int run_stochastic(spec_verify_handle* h, const Launch& L, int B, const void* target,
                    const void* draft, const int32_t* tokens, const float* uniforms, float c,
-                   int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
+                   double c64, int32_t* out_tokens, int32_t* out_len, uint32_t* hist,
+                   hipStream_t s) {
   const int K = h->K, V = h->V;
   const int rows = 2 * K + 1;
   const long long grid1 = (long long)B * rows * L.nseg;
@@ -137,13 +137,12 @@ int run_stochastic(spec_verify_handle* h, const Launch& L, int B, const void* ta
   const int wps = div_up(L.ntiles, kTilesPerWave);
   const int grid3 = div_up((long long)B * wps, sv::kWavesPerBlock);
   hipLaunchKernelGGL((sv::draw_tiles<DT, VEC>), dim3(grid3), dim3(sv::kBlock), 0, s, B, K, V,
-                     L.ntiles, kTilesPerWave, wps, target, draft, h->draw, c, h->tsum_w,
-                     h->tsum_p);
+                     L.ntiles, kTilesPerWave, wps, target, draft, h->draw, c64, h->tsum);
   rc = check_launch(h, "draw_tiles");
   if (rc) return rc;
   hipLaunchKernelGGL((sv::draw_pick<DT, VEC>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
-                     L.ntiles, target, draft, h->draw, uniforms, c, h->tsum_w, h->tsum_p,
-                     out_tokens, h->stats, h->aux_z);
+                     L.ntiles, target, draft, h->draw, uniforms, c64, h->tsum, out_tokens,
+                     h->stats, h->aux_z);
   return check_launch(h, "draw_pick");
 }
 
@@ -175,7 +174,7 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
 }
 
 void free_all(spec_verify_handle* h) {
-  void* ptrs[] = {h->parts, h->draw, h->tsum_w, h->tsum_p, h->ema, h->steps, h->stats};
+  void* ptrs[] = {h->parts, h->draw, h->tsum, h->ema, h->steps, h->stats};
   for (void* p : ptrs)
     if (p != nullptr) (void)hipFree(p);
 }
@@ -213,8 +212,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   const size_t n_tiles = (size_t)max_batch * h->ntiles_max;
   bool ok = hipMalloc(&h->parts, n_parts * sizeof(sv::RowPart)) == hipSuccess &&
             hipMalloc(&h->draw, (size_t)max_batch * sizeof(sv::DrawRow)) == hipSuccess &&
-            hipMalloc(&h->tsum_w, n_tiles * sizeof(double)) == hipSuccess &&
-            hipMalloc(&h->tsum_p, n_tiles * sizeof(double)) == hipSuccess &&
+            hipMalloc(&h->tsum, n_tiles * sizeof(sv::TileSums)) == hipSuccess &&
             hipMalloc(&h->ema, (size_t)max_batch * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->steps, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
             hipMalloc(&h->stats, sizeof(sv::DevStats)) == hipSuccess;
@@ -291,26 +289,27 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   if (mode == SV_MODE_STOCHASTIC) vec = vec && aligned(draft, 16);
 
   int rc = SV_OK;
-  const float c = float(kLog2e / double(temperature));
+  const double c64 = kLog2e / double(temperature);
+  const float c = float(c64);
   if (mode == SV_MODE_STOCHASTIC) {
     const int rows = 2 * h->K + 1;
     if (h->dtype == SV_DTYPE_BF16) {
       if (vec)
         rc = run_stochastic<sv::DT_BF16, 8, SV_U_BF16>(
             h, plan(h, B, rows, 8, SV_U_BF16), B, target, draft, tokens, uniforms, c,
-            out_tokens, out_len, out_hist, stream);
+            c64, out_tokens, out_len, out_hist, stream);
       else
         rc = run_stochastic<sv::DT_BF16, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, draft,
-                                                tokens, uniforms, c, out_tokens, out_len,
+                                                tokens, uniforms, c, c64, out_tokens, out_len,
                                                 out_hist, stream);
     } else {
       if (vec)
         rc = run_stochastic<sv::DT_F32, 4, SV_U_F32>(
             h, plan(h, B, rows, 4, SV_U_F32), B, target, draft, tokens, uniforms, c,
-            out_tokens, out_len, out_hist, stream);
+            c64, out_tokens, out_len, out_hist, stream);
       else
         rc = run_stochastic<sv::DT_F32, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, draft,
-                                               tokens, uniforms, c, out_tokens, out_len,
+                                               tokens, uniforms, c, c64, out_tokens, out_len,
                                                out_hist, stream);
     }
   } else {

@@ -107,6 +107,32 @@ __device__ inline float term(float x, float c, float R) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -R));
 }
 
+// 2^a in float64 to about 1e-11 relative: a = n + f with n = rint(a),
+// |f| <= 1/2, 2^f by its Taylor series of degree 9 (Horner), then an exact
+// scaling by 2^n. Arguments below -1100 (including -inf) give 0. Used where
+// single-precision exponentials are not accurate enough: the per-token
+// weights of the correction/bonus draw, whose prefix sums are compared with
+// a uniform at the resolution of one token's share of a large vocabulary.
+__device__ inline double exp2_acc(double a) {
+  constexpr double L = 0.6931471805599453094172321214581766;   // ln 2
+  constexpr double c1 = L, c2 = c1 * L / 2, c3 = c2 * L / 3, c4 = c3 * L / 4, c5 = c4 * L / 5,
+                   c6 = c5 * L / 6, c7 = c6 * L / 7, c8 = c7 * L / 8, c9 = c8 * L / 9;
+  a = fmax(a, -1100.0);
+  const double n = __builtin_rint(a);
+  const double f = a - n;
+  double p = c9;
+  p = __builtin_fma(p, f, c8);
+  p = __builtin_fma(p, f, c7);
+  p = __builtin_fma(p, f, c6);
+  p = __builtin_fma(p, f, c5);
+  p = __builtin_fma(p, f, c4);
+  p = __builtin_fma(p, f, c3);
+  p = __builtin_fma(p, f, c2);
+  p = __builtin_fma(p, f, c1);
+  p = __builtin_fma(p, f, 1.0);
+  return __builtin_ldexp(p, int(n));
+}
+
 // Scale a float64 sum by 2^(from - to) exactly (from <= to, both integers or
 // the initial reference). Saturating conversion keeps the empty state at 0.
 __device__ inline double rescale(double s, float from, float to) {
@@ -172,10 +198,17 @@ struct RowPart {
 // Final statistics of the row a sequence draws from, left by the scan for the
 // draw kernels.
 struct DrawRow {
-  double S_t, S_d;
+  double rho;    // S_t / S_d from the streaming pass: sign test of p - q
   float R_t, R_d;
   int j;         // rejection index (K = bonus), -1 = nothing to draw
   int pad;
+};
+
+// Per-tile sums left by the draw's first phase, all relative to the row
+// references R_t, R_d: E = sum e_t(v), Ed = sum e_d(v), and over the tokens
+// with e_t(v) > rho * e_d(v): A = sum e_t(v), Bd = sum e_d(v).
+struct TileSums {
+  double E, Ed, A, Bd;
 };
 
 struct DevStats {

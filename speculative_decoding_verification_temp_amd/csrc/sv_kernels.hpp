@@ -353,8 +353,7 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
   const double Stj = __shfl(St, j, kWave), Sdj = __shfl(Sd, j, kWave);
   if (lane == 0) {
     DrawRow dr;
-    dr.S_t = Stj;
-    dr.S_d = Sdj;
+    dr.rho = Stj / Sdj;
     dr.R_t = Rtj;
     dr.R_d = Rdj;
     dr.j = bad ? -1 : j;
@@ -421,52 +420,56 @@ __global__ __launch_bounds__(kBlock) void scan_argmax(
 }
 
 // --------------------------------------------------------------------------
-// Draw, phase 1: tile sums of the draw weights. Weight of token v:
-//   j < K : max(0, p_j(v) - q_j(v))       (residual)
-//   j = K : p_K(v)                        (bonus)
-// plus, for j < K, the tile sums of p_j(v) for the Z = 0 fallback.
-// A tile is kTileChunks consecutive chunks; one wavefront sums one tile.
+// The draw. Its weights are formed in float64 with exp2_acc from the raw
+// logits of the rows it draws from, relative to the streaming pass's integer
+// references:
+//   e_t(v) = 2^(x_t(v) * c - R_t),  e_d(v) = 2^(x_d(v) * c - R_d),
+// so p_j(v) = e_t(v) / S_t and q_j(v) = e_d(v) / S_d with S = sum of e.
+//   j < K : weight max(0, e_t(v) - rho * e_d(v)), rho = S_t / S_d  (residual)
+//   j = K : weight e_t(v)                                           (bonus)
+// Phase 1 (draw_tiles) sums each tile of kTileChunks chunks: E, Ed, and A, Bd
+// over the tokens where the streaming pass's rho says p > q. Phase 2
+// (draw_pick) forms exact S_t, S_d and rho from the E sums, the tile weights
+// max(0, A - rho * Bd), finds the tile where the prefix crosses u * total and
+// re-reads that tile to find the token. A token whose sign of p - q differs
+// between the two rho values has |p - q| at the rounding level of rho, so its
+// weight is negligible either way.
 // --------------------------------------------------------------------------
-template <int DT, int VEC> struct DrawWeights {
+template <int DT, int VEC> struct DrawRows {
   using C = Chunk<DT, VEC>;
   const void* trow;
   const void* drow;
-  float c, Rt, Rd;
-  double invSt, invSd;
+  double c, Rt, Rd;
   bool residual;
 
   __device__ inline void init(const void* target, const void* draft, const DrawRow& dr, int b,
-                              int K, int V, float c_) {
+                              int K, int V, double c_) {
     c = c_;
     residual = dr.j < K;
     trow = row_ptr<DT>(target, draft, b, dr.j, K, V);
     drow = residual ? row_ptr<DT>(target, draft, b, K + 1 + dr.j, K, V) : nullptr;
     Rt = dr.R_t;
     Rd = dr.R_d;
-    invSt = 1.0 / dr.S_t;
-    invSd = 1.0 / dr.S_d;
   }
-  // weights of one chunk: w = draw weight, pw = p_j weight (fallback)
-  __device__ inline void chunk(long long ci, double (&w)[C::N], double (&pw)[C::N]) const {
+  __device__ inline void load(long long ci, typename C::raw_t& rt, typename C::raw_t& rd) const {
+    rt = C::load(trow, ci);
+    if (residual) rd = C::load(drow, ci);
+  }
+  // exact terms of one chunk (et, and ed when drawing from a residual)
+  __device__ inline void terms(const typename C::raw_t& rt, const typename C::raw_t& rd,
+                               double (&et)[C::N], double (&ed)[C::N]) const {
     float xt[C::N];
-    C::unpack(C::load(trow, ci), xt);
+    C::unpack(rt, xt);
+#pragma unroll
+    for (int k = 0; k < C::N; ++k) et[k] = exp2_acc(__builtin_fma(double(xt[k]), c, -Rt));
     if (residual) {
       float xd[C::N];
-      C::unpack(C::load(drow, ci), xd);
+      C::unpack(rd, xd);
 #pragma unroll
-      for (int k = 0; k < C::N; ++k) {
-        const double p = double(term(xt[k], c, Rt)) * invSt;
-        const double q = double(term(xd[k], c, Rd)) * invSd;
-        w[k] = fmax(p - q, 0.0);
-        pw[k] = p;
-      }
+      for (int k = 0; k < C::N; ++k) ed[k] = exp2_acc(__builtin_fma(double(xd[k]), c, -Rd));
     } else {
 #pragma unroll
-      for (int k = 0; k < C::N; ++k) {
-        const double p = double(term(xt[k], c, Rt)) * invSt;
-        w[k] = p;
-        pw[k] = p;
-      }
+      for (int k = 0; k < C::N; ++k) ed[k] = 0.0;
     }
   }
 };
@@ -475,8 +478,7 @@ template <int DT, int VEC>
 __global__ __launch_bounds__(kBlock) void draw_tiles(
     int B, int K, int V, int ntiles, int tiles_per_wave, int waves_per_seq,
     const void* __restrict__ target, const void* __restrict__ draft,
-    const DrawRow* __restrict__ draw, float c, double* __restrict__ tsum_w,
-    double* __restrict__ tsum_p) {
+    const DrawRow* __restrict__ draw, double c, TileSums* __restrict__ tsum) {
   using C = Chunk<DT, VEC>;
   const int lane = threadIdx.x & (kWave - 1);
   const long long gw = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
@@ -485,80 +487,114 @@ __global__ __launch_bounds__(kBlock) void draw_tiles(
   const int w = int(gw % waves_per_seq);
   const DrawRow dr = draw[b];
   if (dr.j < 0) return;
-  DrawWeights<DT, VEC> W;
+  DrawRows<DT, VEC> W;
   W.init(target, draft, dr, b, K, V, c);
+  const double rho = dr.rho;
   const long long nchunks = V / VEC;
   const int t0 = w * tiles_per_wave, t1 = min(ntiles, t0 + tiles_per_wave);
   for (int t = t0; t < t1; ++t) {
-    double aw = 0.0, ap = 0.0;
+    typename C::raw_t rt[kTileChunksPerLane], rd[kTileChunksPerLane];
+#pragma unroll
+    for (int k = 0; k < kTileChunksPerLane; ++k) {
+      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
+      if (ci < nchunks) W.load(ci, rt[k], rd[k]);
+    }
+    double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
 #pragma unroll
     for (int k = 0; k < kTileChunksPerLane; ++k) {
       const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
       if (ci < nchunks) {
-        double wv[C::N], pv[C::N];
-        W.chunk(ci, wv, pv);
+        double et[C::N], ed[C::N];
+        W.terms(rt[k], rd[k], et, ed);
 #pragma unroll
         for (int e = 0; e < C::N; ++e) {
-          aw += wv[e];
-          ap += pv[e];
+          E += et[e];
+          Ed += ed[e];
+          const bool pos = et[e] > rho * ed[e];
+          A += pos ? et[e] : 0.0;
+          Bd += pos ? ed[e] : 0.0;
         }
       }
     }
-    aw = wave_sum(aw);
-    if (lane == 0) tsum_w[(long long)b * ntiles + t] = aw;
+    E = wave_sum(E);
     if (W.residual) {
-      ap = wave_sum(ap);
-      if (lane == 0) tsum_p[(long long)b * ntiles + t] = ap;
+      Ed = wave_sum(Ed);
+      A = wave_sum(A);
+      Bd = wave_sum(Bd);
+    }
+    if (lane == 0) {
+      TileSums ts;
+      ts.E = E;
+      ts.Ed = Ed;
+      ts.A = A;
+      ts.Bd = Bd;
+      tsum[(long long)b * ntiles + t] = ts;
     }
   }
 }
 
-// --------------------------------------------------------------------------
-// Draw, phase 2: one wavefront per sequence.
-// --------------------------------------------------------------------------
+// In-order inclusive prefix over the tile weights of one sequence; returns
+// the total (same value on every lane).
+__device__ inline double tiles_total(const TileSums* ts, int ntiles, int lane, int which,
+                                     double rho) {
+  double carry = 0.0;
+  for (int t0 = 0; t0 < ntiles; t0 += kWave) {
+    double v = 0.0;
+    if (t0 + lane < ntiles) {
+      const TileSums s = ts[t0 + lane];
+      v = which ? fmax(s.A - rho * s.Bd, 0.0) : s.E;
+    }
+    carry += __shfl(wave_incl_scan(v, lane), kWave - 1, kWave);
+  }
+  return carry;
+}
+
 template <int DT, int VEC>
 __global__ __launch_bounds__(kBlock) void draw_pick(
     int B, int K, int V, int ntiles, const void* __restrict__ target,
     const void* __restrict__ draft, const DrawRow* __restrict__ draw,
-    const float* __restrict__ uniforms, float c, const double* __restrict__ tsum_w,
-    const double* __restrict__ tsum_p, int32_t* __restrict__ out_tokens,
-    DevStats* __restrict__ st, double* aux_z) {
+    const float* __restrict__ uniforms, double c, const TileSums* __restrict__ tsum,
+    int32_t* __restrict__ out_tokens, DevStats* __restrict__ st, double* aux_z) {
   using C = Chunk<DT, VEC>;
   const int lane = threadIdx.x & (kWave - 1);
   const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (b >= B) return;
   const DrawRow dr = draw[b];
   if (dr.j < 0) return;
-  DrawWeights<DT, VEC> W;
+  DrawRows<DT, VEC> W;
   W.init(target, draft, dr, b, K, V, c);
+  const TileSums* ts = tsum + (long long)b * ntiles;
 
-  // total of the draw weights, as the end of an in-order prefix over tiles
-  const double* ts = tsum_w + (long long)b * ntiles;
-  double carry = 0.0;
-  for (int t0 = 0; t0 < ntiles; t0 += kWave) {
-    const double v = (t0 + lane < ntiles) ? ts[t0 + lane] : 0.0;
-    carry += __shfl(wave_incl_scan(v, lane), kWave - 1, kWave);
+  // exact normalisers (fixed order, broadcast from lane 0)
+  double St = 0.0, Sd = 0.0;
+  for (int t = lane; t < ntiles; t += kWave) {
+    St += ts[t].E;
+    Sd += ts[t].Ed;
   }
-  const double Zr = carry;
-  const bool fallback = W.residual && !(Zr > 0.0);
+  St = __shfl(wave_sum(St), 0, kWave);
+  Sd = __shfl(wave_sum(Sd), 0, kWave);
+  const double rho = W.residual ? St / Sd : 0.0;
+
+  int which = W.residual ? 1 : 0;
+  double total = tiles_total(ts, ntiles, lane, which, rho);
+  const double zres = which ? total : -1.0;
+  const bool fallback = W.residual && !(total > 0.0);
   if (fallback) {
-    ts = tsum_p + (long long)b * ntiles;
-    carry = 0.0;
-    for (int t0 = 0; t0 < ntiles; t0 += kWave) {
-      const double v = (t0 + lane < ntiles) ? ts[t0 + lane] : 0.0;
-      carry += __shfl(wave_incl_scan(v, lane), kWave - 1, kWave);
-    }
+    which = 0;
+    total = tiles_total(ts, ntiles, lane, 0, rho);
   }
-  const double total = carry;
   const double tgt = double(uniforms[(long long)b * (K + 1) + K]) * total;
 
   // crossing tile: first tile whose inclusive prefix exceeds tgt; if none
   // (rounding), the last tile with positive weight
   int tile = -1, last_pos = -1;
-  double base = 0.0;
-  carry = 0.0;
+  double base = 0.0, carry = 0.0;
   for (int t0 = 0; t0 < ntiles && tile < 0; t0 += kWave) {
-    const double v = (t0 + lane < ntiles) ? ts[t0 + lane] : 0.0;
+    double v = 0.0;
+    if (t0 + lane < ntiles) {
+      const TileSums s = ts[t0 + lane];
+      v = which ? fmax(s.A - rho * s.Bd, 0.0) : s.E;
+    }
     const double incl = carry + wave_incl_scan(v, lane);
     const unsigned long long hit = __ballot(t0 + lane < ntiles && incl > tgt);
     const unsigned long long pos = __ballot(t0 + lane < ntiles && v > 0.0);
@@ -573,46 +609,58 @@ __global__ __launch_bounds__(kBlock) void draw_pick(
   const bool clamp = tile < 0;
   if (clamp) tile = last_pos;
 
-  // re-read the crossing tile; in-order prefix over its chunks. If rounding
-  // leaves no crossing inside the tile, take its last positive-weight token.
+  // re-read the crossing tile: all of this lane's chunks at once, then an
+  // in-order prefix over chunks (k-major, then lanes) and elements
   const long long nchunks = V / VEC;
-  int token = -1, last_elem = -1;
-  for (int k = 0; k < kTileChunksPerLane && token < 0; ++k) {
-    const long long ci = (long long)tile * kTileChunks + (long long)k * kWave + lane;
-    double wv[C::N], pv[C::N];
-    double cs = 0.0;
-    const bool valid = tile >= 0 && ci < nchunks;
-    int lp = -1;
-    if (valid) {
-      W.chunk(ci, wv, pv);
-      if (fallback) {
+  typename C::raw_t rt[kTileChunksPerLane], rd[kTileChunksPerLane];
+  double cs[kTileChunksPerLane];
+  int lp[kTileChunksPerLane];
 #pragma unroll
-        for (int e = 0; e < C::N; ++e) wv[e] = pv[e];
-      }
+  for (int k = 0; k < kTileChunksPerLane; ++k) {
+    const long long ci = (long long)tile * kTileChunks + (long long)k * kWave + lane;
+    if (tile >= 0 && ci < nchunks) W.load(ci, rt[k], rd[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < kTileChunksPerLane; ++k) {
+    const long long ci = (long long)tile * kTileChunks + (long long)k * kWave + lane;
+    cs[k] = 0.0;
+    lp[k] = -1;
+    if (tile >= 0 && ci < nchunks) {
+      double et[C::N], ed[C::N];
+      W.terms(rt[k], rd[k], et, ed);
 #pragma unroll
       for (int e = 0; e < C::N; ++e) {
-        cs += wv[e];
-        lp = (wv[e] > 0.0) ? int(ci * VEC + e) : lp;
+        const double wv = which ? fmax(et[e] - rho * ed[e], 0.0) : et[e];
+        cs[k] += wv;
+        lp[k] = wv > 0.0 ? int(ci * VEC + e) : lp[k];
       }
     }
-    int lpw = lp;
+  }
+  int token = -1, last_elem = -1;
+#pragma unroll
+  for (int k = 0; k < kTileChunksPerLane; ++k) {
+    int lpw = lp[k];
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) lpw = max(lpw, __shfl_xor(lpw, o, kWave));
     last_elem = max(last_elem, lpw);
-    if (clamp) continue;
-    const double incl = base + wave_incl_scan(cs, lane);
+    if (clamp || token >= 0) continue;
+    const long long ci = (long long)tile * kTileChunks + (long long)k * kWave + lane;
+    const bool valid = tile >= 0 && ci < nchunks;
+    const double incl = base + wave_incl_scan(cs[k], lane);
     const unsigned long long hit = __ballot(valid && incl > tgt);
     if (hit) {
       const int l = __ffsll((long long)hit) - 1;
       int tok = -1;
       if (lane == l) {
-        double run = incl - cs;
+        double et[C::N], ed[C::N];
+        W.terms(rt[k], rd[k], et, ed);
+        double run = incl - cs[k];
 #pragma unroll
         for (int e = 0; e < C::N; ++e) {
-          run += wv[e];
+          run += which ? fmax(et[e] - rho * ed[e], 0.0) : et[e];
           if (tok < 0 && run > tgt) tok = int(ci * VEC + e);
         }
-        if (tok < 0) tok = lp;   // the chunk holds positive weight (cs > 0)
+        if (tok < 0) tok = lp[k];   // the chunk holds positive weight
       }
       token = __shfl(tok, l, kWave);
     }
@@ -621,7 +669,7 @@ __global__ __launch_bounds__(kBlock) void draw_pick(
   if (token < 0) token = last_elem;
   if (lane == 0) {
     out_tokens[(long long)b * (K + 1) + dr.j] = token;
-    if (aux_z != nullptr) aux_z[b] = W.residual ? Zr : -1.0;
+    if (aux_z != nullptr) aux_z[b] = W.residual ? fmax(zres, 0.0) / St : -1.0;
     if (fallback) atomicAdd(&st->z0_fallbacks, 1ull);
   }
 }

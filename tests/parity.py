@@ -19,25 +19,42 @@ BOUNDARY = 1e-6
 PROB_TOL = 1e-5
 
 
-def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None):
-    """Run the oracle on the listed sequences of a generated input dict."""
+def _merge(parts):
+    out = parts[0]
+    for p in parts[1:]:
+        for k in ("tokens", "accept_len", "p_d", "q_d", "z", "argmax", "min_dist"):
+            setattr(out, k, np.concatenate([getattr(out, k), getattr(p, k)]))
+        out.hist = out.hist + p.hist
+        out.zero_q_accepts += p.zero_q_accepts
+        out.z0_fallbacks += p.z0_fallbacks
+        out.invalid += p.invalid
+    return out
+
+
+def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int = 256):
+    """Run the oracle on the listed sequences of a generated input dict
+    (host copies are made a chunk of sequences at a time)."""
     rows = np.asarray(rows, dtype=np.int64)
-    idx = torch.as_tensor(rows, device=x["target"].device)
-    tgt = to_host_f64(x["target"].index_select(0, idx))
-    drf = to_host_f64(x["draft"].index_select(0, idx)) if mode == "stochastic" else None
-    tok = x["tokens"].index_select(0, idx).cpu().numpy()
-    uni = x["uniforms"].index_select(0, idx).cpu().double().numpy()
     m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
-    if ema is not None:
-        # EMA slots are batch rows: feed the oracle a state indexed by row
-        sub = O.EmaState(len(rows), ema.decay)
-        sub.ema[:] = ema.ema[rows]
-        sub.steps[:] = ema.steps[rows]
-        res = O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau, ema=sub)
-        ema.ema[rows] = sub.ema
-        ema.steps[rows] = sub.steps
-        return res
-    return O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau)
+    parts = []
+    for c0 in range(0, len(rows), chunk):
+        sub_rows = rows[c0:c0 + chunk]
+        idx = torch.as_tensor(sub_rows, device=x["target"].device)
+        tgt = to_host_f64(x["target"].index_select(0, idx))
+        drf = to_host_f64(x["draft"].index_select(0, idx)) if mode == "stochastic" else None
+        tok = x["tokens"].index_select(0, idx).cpu().numpy()
+        uni = x["uniforms"].index_select(0, idx).cpu().double().numpy()
+        if ema is not None:
+            # EMA slots are batch rows: feed the oracle a state indexed by row
+            sub = O.EmaState(len(sub_rows), ema.decay)
+            sub.ema[:] = ema.ema[sub_rows]
+            sub.steps[:] = ema.steps[sub_rows]
+            parts.append(O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau, ema=sub))
+            ema.ema[sub_rows] = sub.ema
+            ema.steps[sub_rows] = sub.steps
+        else:
+            parts.append(O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau))
+    return _merge(parts)
 
 
 def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
@@ -54,7 +71,10 @@ def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
         f"first rows {rows[bad_tok[:5]] if len(bad_tok) else rows[bad_len[:5]]}; "
         f"gpu {g_tok[bad_tok[:2]] if len(bad_tok) else g_len[bad_len[:5]]} "
         f"oracle {ref.tokens[bad_tok[:2]] if len(bad_tok) else ref.accept_len[bad_len[:5]]}")
-    report = dict(rows=len(rows), excused=int((~strict).sum()))
+    # near-boundary sequences are excused; count how many actually differ
+    diff = (g_len != ref.accept_len) | np.any(g_tok != ref.tokens, axis=1)
+    report = dict(rows=len(rows), near_boundary=int((~strict).sum()),
+                  mismatches=int(diff.sum()))
     if aux is not None:
         valid = ref.accept_len >= 0
         if mode in ("stochastic", "margin"):
