@@ -10,7 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "sv_kernels.hpp"
+#include "sv_fused.hpp"
 
 #ifndef SV_U_BF16
 #define SV_U_BF16 2
@@ -25,7 +25,6 @@
 namespace {
 
 constexpr int kMaxSeg = 16;
-constexpr int kTilesPerWave = 4;
 constexpr int kProfCalls = 4096;
 constexpr double kLog2e = 1.4426950408889634073599246810018921;
 
@@ -45,6 +44,9 @@ struct spec_verify_handle {
   sv::RowPart* parts = nullptr;
   sv::DrawRow* draw = nullptr;
   sv::TileSums* tsum = nullptr;
+  double* table = nullptr;            // bf16 exponential table of the current call
+  int tiles_per_group = 16;           // draw tiles per workgroup (tuning)
+  int fused_min_batch = 0;            // smallest batch for one workgroup per sequence, 0 = off
   double* ema = nullptr;
   int32_t* steps = nullptr;
   sv::DevStats* stats = nullptr;
@@ -104,6 +106,14 @@ Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
   return L;
 }
 
+// entries per sign of the bf16 exponential table: exponent fields from 2^-16
+// up, as many as keep |x * c| < 1000
+int tab_half(double c) {
+  int n = sv::kTabMaxExp;
+  while (n > 1 && std::ldexp(1.0, n - 16) * c > 1000.0) --n;
+  return n * 128;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Event k (0: before the streaming pass, 1: after it, 2: after the call) of
@@ -113,37 +123,65 @@ void prof_mark(spec_verify_handle* h, int k, hipStream_t s) {
     (void)hipEventRecord(h->prof_ev[3 * h->prof_n + k], s);
 }
 
+// Stochastic mode, multi-kernel pipeline: streaming pass over every
+// (row, segment), acceptance scan, draw tile sums, pick.
 template <int DT, int VEC, int U>
-int run_stochastic(spec_verify_handle* h, const Launch& L, int B, const void* target,
-                   const void* draft, const int32_t* tokens, const float* uniforms, float c,
-                   double c64, int32_t* out_tokens, int32_t* out_len, uint32_t* hist,
-                   hipStream_t s) {
+int run_stochastic(spec_verify_handle* h, int B, const void* target, const void* draft,
+                   const int32_t* tokens, const float* uniforms, float c, double c64,
+                   int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
   const int K = h->K, V = h->V;
   const int rows = 2 * K + 1;
-  const long long grid1 = (long long)B * rows * L.nseg;
+  const Launch L = plan(h, B, rows, VEC, U);
+  const bool tab = (DT == sv::DT_BF16 && VEC == 8);
+  const int n_half = tab_half(c64);
+  const int groups = div_up(L.ntiles, h->tiles_per_group);
+  const int grid_seq = div_up(B, sv::kWavesPerBlock);
   prof_mark(h, 0, s);
-  hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(grid1)), dim3(sv::kBlock), 0,
-                     s, target, draft, K, V, L.nseg, L.seg_chunks, c, h->parts, hist);
+  hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
+                     dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
+                     h->parts, hist);
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
-  const int grid2 = div_up(B, sv::kWavesPerBlock);
-  hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
-                     L.nseg, h->parts, target, draft, tokens, uniforms, c, out_tokens, out_len,
+  hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
+                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, out_tokens, out_len,
                      hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
-                     h->aux_z);
-  rc = check_launch(h, "scan_stochastic");
-  if (rc) return rc;
-  const int wps = div_up(L.ntiles, kTilesPerWave);
-  const int grid3 = div_up((long long)B * wps, sv::kWavesPerBlock);
-  hipLaunchKernelGGL((sv::draw_tiles<DT, VEC>), dim3(grid3), dim3(sv::kBlock), 0, s, B, K, V,
-                     L.ntiles, kTilesPerWave, wps, target, draft, h->draw, c64, h->tsum);
-  rc = check_launch(h, "draw_tiles");
-  if (rc) return rc;
-  hipLaunchKernelGGL((sv::draw_pick<DT, VEC>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
-                     L.ntiles, target, draft, h->draw, uniforms, c64, h->tsum, out_tokens,
+                     h->aux_z, tab ? h->table : nullptr, n_half, c64);
+  if ((rc = check_launch(h, "scan_stochastic"))) return rc;
+  hipLaunchKernelGGL((sv::draw<DT, VEC>), dim3(B * groups), dim3(sv::kBlock), 0, s, 0, B, K, V,
+                     L.ntiles, h->tiles_per_group, groups, target, draft, h->draw, c64, n_half,
+                     h->table, h->tsum);
+  if ((rc = check_launch(h, "draw"))) return rc;
+  hipLaunchKernelGGL((sv::draw_pick<DT, VEC>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
+                     V, L.ntiles, target, draft, h->draw, uniforms, c64, h->tsum, out_tokens,
                      h->stats, h->aux_z);
   return check_launch(h, "draw_pick");
+}
+
+// Stochastic mode, one workgroup per sequence (large batches).
+template <int DT, int VEC, int U>
+int run_fused(spec_verify_handle* h, int B, const void* target, const void* draft,
+              const int32_t* tokens, const float* uniforms, float c, double c64,
+              int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
+  const int K = h->K, V = h->V;
+  prof_mark(h, 0, s);
+  hipLaunchKernelGGL(sv::zero_hist, dim3(1), dim3(64), 0, s, hist, K + 1);
+  int rc = check_launch(h, "zero_hist");
+  if (rc) return rc;
+  hipLaunchKernelGGL((sv::verify_fused<DT, VEC, U>), dim3(B), dim3(sv::kFBlock), 0, s, K, V,
+                     target, draft, tokens, uniforms, c, c64, tab_half(c64), out_tokens,
+                     out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q,
+                     h->aux_z);
+  rc = check_launch(h, "verify_fused");
+  prof_mark(h, 1, s);
+  return rc;
+}
+
+// whether the one-workgroup-per-sequence kernel serves this call
+bool use_fused(const spec_verify_handle* h, int B, int vec) {
+  if (h->fused_min_batch <= 0 || B < h->fused_min_batch || vec == 1) return false;
+  const long long ntiles = ((long long)h->V / vec + sv::kTileChunks - 1) / sv::kTileChunks;
+  return ntiles <= sv::kFMaxTiles && 2 * h->K + 1 <= sv::kFMaxRows;
 }
 
 template <int DT, int VEC, int U>
@@ -174,7 +212,7 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
 }
 
 void free_all(spec_verify_handle* h) {
-  void* ptrs[] = {h->parts, h->draw, h->tsum, h->ema, h->steps, h->stats};
+  void* ptrs[] = {h->parts, h->draw, h->tsum, h->table, h->ema, h->steps, h->stats};
   for (void* p : ptrs)
     if (p != nullptr) (void)hipFree(p);
 }
@@ -203,6 +241,9 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   h->decay = ema_decay;
   h->target_wgs = env_int("SPEC_VERIFY_TARGET_WGS", 2048);
   h->nseg_force = env_int("SPEC_VERIFY_NSEG", 0);
+  h->tiles_per_group = env_int("SPEC_VERIFY_TILES_PER_GROUP", 16);
+  if (h->tiles_per_group < 1) h->tiles_per_group = 1;
+  h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return SV_EHIP;
@@ -213,6 +254,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   bool ok = hipMalloc(&h->parts, n_parts * sizeof(sv::RowPart)) == hipSuccess &&
             hipMalloc(&h->draw, (size_t)max_batch * sizeof(sv::DrawRow)) == hipSuccess &&
             hipMalloc(&h->tsum, n_tiles * sizeof(sv::TileSums)) == hipSuccess &&
+            hipMalloc(&h->table, (size_t)sv::kTabMax * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->ema, (size_t)max_batch * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->steps, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
             hipMalloc(&h->stats, sizeof(sv::DevStats)) == hipSuccess;
@@ -292,25 +334,26 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   const double c64 = kLog2e / double(temperature);
   const float c = float(c64);
   if (mode == SV_MODE_STOCHASTIC) {
-    const int rows = 2 * h->K + 1;
-    if (h->dtype == SV_DTYPE_BF16) {
+    if (h->dtype == SV_DTYPE_BF16 && vec && use_fused(h, B, 8))
+      rc = run_fused<sv::DT_BF16, 8, 8>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens,
+                                        out_len, out_hist, stream);
+    else if (h->dtype == SV_DTYPE_F32 && vec && use_fused(h, B, 4))
+      rc = run_fused<sv::DT_F32, 4, 8>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens,
+                                       out_len, out_hist, stream);
+    else if (h->dtype == SV_DTYPE_BF16) {
       if (vec)
-        rc = run_stochastic<sv::DT_BF16, 8, SV_U_BF16>(
-            h, plan(h, B, rows, 8, SV_U_BF16), B, target, draft, tokens, uniforms, c,
-            c64, out_tokens, out_len, out_hist, stream);
+        rc = run_stochastic<sv::DT_BF16, 8, SV_U_BF16>(h, B, target, draft, tokens, uniforms, c,
+                                                       c64, out_tokens, out_len, out_hist, stream);
       else
-        rc = run_stochastic<sv::DT_BF16, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, draft,
-                                                tokens, uniforms, c, c64, out_tokens, out_len,
-                                                out_hist, stream);
+        rc = run_stochastic<sv::DT_BF16, 1, 8>(h, B, target, draft, tokens, uniforms, c, c64,
+                                                out_tokens, out_len, out_hist, stream);
     } else {
       if (vec)
-        rc = run_stochastic<sv::DT_F32, 4, SV_U_F32>(
-            h, plan(h, B, rows, 4, SV_U_F32), B, target, draft, tokens, uniforms, c,
-            c64, out_tokens, out_len, out_hist, stream);
+        rc = run_stochastic<sv::DT_F32, 4, SV_U_F32>(h, B, target, draft, tokens, uniforms, c,
+                                                     c64, out_tokens, out_len, out_hist, stream);
       else
-        rc = run_stochastic<sv::DT_F32, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, draft,
-                                               tokens, uniforms, c, c64, out_tokens, out_len,
-                                               out_hist, stream);
+        rc = run_stochastic<sv::DT_F32, 1, 8>(h, B, target, draft, tokens, uniforms, c, c64,
+                                               out_tokens, out_len, out_hist, stream);
     }
   } else {
     const bool margin = mode == SV_MODE_MARGIN;

@@ -8,11 +8,10 @@
 //   scan_*         one wavefront per sequence: combine segment partials, form
 //                  p(d), q(d) (or argmax matches / margin ratios), find the
 //                  first rejection with a ballot, emit tokens, histogram, EMA.
-//   draw_tiles     per-tile sums of the residual [p_j - q_j]_+ (or of p_K for
-//                  the bonus, or of p_j for the Z = 0 fallback).
-//   draw_pick      one wavefront per sequence: prefix over tile sums, then a
-//                  re-read of the crossing tile with a wavefront prefix scan
-//                  to find the drawn token.
+//   draw           correction/bonus draw: per-tile float64 sums of the draw
+//                  weights (exact normalisers, residual split by sign), then
+//                  the last workgroup of each sequence prefix-scans the tile
+//                  sums and re-reads the crossing tile to find the token.
 //
 // None of the kernels use floating-point atomics; every reduction has a fixed
 // order, so reruns are bitwise identical.
@@ -44,16 +43,16 @@ __device__ inline const void* row_ptr(const void* target, const void* draft, int
 // --------------------------------------------------------------------------
 template <int DT, int VEC, int U>
 __global__ __launch_bounds__(kBlock) void rowstats_sum(
-    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, int nseg,
-    int seg_chunks, float c, RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+    const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
+    int nseg, int seg_chunks, float c, RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
-  const long long wg = blockIdx.x;
   const int rows = 2 * K + 1;
+  const long long wg = (long long)b0 * rows * nseg + blockIdx.x;   // global (row, segment)
   const int seg = int(wg % nseg);
   const long long grow = wg / nseg;
   const int b = int(grow / rows), r = int(grow % rows);
-  if (wg == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
 
   const void* row = row_ptr<DT>(target, draft, b, r, K, V);
   const long long nchunks = V / VEC;
@@ -297,20 +296,73 @@ __device__ inline void emit_and_update(int lane, int b, int K, int j, bool bad,
   }
 }
 
+// Table of 2^(x * c) in float64 for every bf16 value x with 2^-16 <= |x| <
+// 2^(n_exp - 16): n_exp exponent fields of 128 mantissas, positive values
+// first. n_exp is chosen on the host so that |x * c| < 1000 over the table,
+// which keeps every entry a normal float64. Other values (0, tiny, huge,
+// infinities) take the direct exp2_acc path.
+constexpr int kTabELo = 127 - 16;
+constexpr int kTabMaxExp = 23;
+constexpr int kTabMax = 2 * kTabMaxExp * 128;
+
+// entry i of the table (value index order as above)
+__device__ inline double exp_table_entry(int i, int n_half, double c) {
+  const int neg = i >= n_half;
+  const uint32_t bits = uint32_t((neg ? i - n_half : i) + (kTabELo << 7)) | (neg ? 0x8000u : 0u);
+  return exp2_acc(double(__uint_as_float(bits << 16)) * c);
+}
+
+// table offset of a bf16 value, or -1 when it is outside the table
+__device__ inline int tab_index(uint32_t bits, int n_half) {
+  const uint32_t off = (bits & 0x7fffu) - uint32_t(kTabELo << 7);
+  return off < uint32_t(n_half) ? int(off) + ((bits & 0x8000u) ? n_half : 0) : -1;
+}
+
+// 2^(x*c - R) for the bf16 values of one chunk: table loads for all of them
+// first, then the direct path for the (rare) values outside the table
+__device__ inline void tab_terms8(const double* T, const u32x4& raw, int n_half, double c,
+                                  double R, double (&out)[8]) {
+  int idx[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    idx[2 * k] = tab_index(raw[k] & 0xffffu, n_half);
+    idx[2 * k + 1] = tab_index(raw[k] >> 16, n_half);
+  }
+  const int sh = -int(R);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out[k] = __builtin_ldexp(T[idx[k] < 0 ? 0 : idx[k]], sh);
+  bool rare = false;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rare |= idx[k] < 0;
+  if (rare) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (idx[k] < 0) {
+        const uint32_t bits = (k & 1) ? (raw[k >> 1] >> 16) : (raw[k >> 1] & 0xffffu);
+        out[k] = exp2_acc(__builtin_fma(double(__uint_as_float(bits << 16)), c, -R));
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------------------
 // Stochastic scan: lane i tests position i.
 // --------------------------------------------------------------------------
 template <int DT>
 __global__ __launch_bounds__(kBlock) void scan_stochastic(
-    int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
+    int b0, int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
     const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, DrawRow* __restrict__ draw, double* aux_p,
-    double* aux_q, double* aux_z) {
+    double* aux_q, double* aux_z, double* __restrict__ table, int n_half, double c64) {
+  // the draw's bf16 exponential table, spread over this grid's threads
+  if (table != nullptr)
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < 2 * n_half; i += gridDim.x * kBlock)
+      table[i] = exp_table_entry(i, n_half, c64);
   const int lane = threadIdx.x & (kWave - 1);
-  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  const int b = b0 + blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (b >= B) return;
   const int rows = 2 * K + 1;
   const RowPart* pb = parts + (long long)b * rows * nseg;
@@ -475,61 +527,21 @@ template <int DT, int VEC> struct DrawRows {
 };
 
 template <int DT, int VEC>
-__global__ __launch_bounds__(kBlock) void draw_tiles(
-    int B, int K, int V, int ntiles, int tiles_per_wave, int waves_per_seq,
-    const void* __restrict__ target, const void* __restrict__ draft,
-    const DrawRow* __restrict__ draw, double c, TileSums* __restrict__ tsum) {
-  using C = Chunk<DT, VEC>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const long long gw = (long long)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  const int b = int(gw / waves_per_seq);
-  if (b >= B) return;
-  const int w = int(gw % waves_per_seq);
-  const DrawRow dr = draw[b];
-  if (dr.j < 0) return;
-  DrawRows<DT, VEC> W;
-  W.init(target, draft, dr, b, K, V, c);
-  const double rho = dr.rho;
-  const long long nchunks = V / VEC;
-  const int t0 = w * tiles_per_wave, t1 = min(ntiles, t0 + tiles_per_wave);
-  for (int t = t0; t < t1; ++t) {
-    typename C::raw_t rt[kTileChunksPerLane], rd[kTileChunksPerLane];
-#pragma unroll
-    for (int k = 0; k < kTileChunksPerLane; ++k) {
-      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
-      if (ci < nchunks) W.load(ci, rt[k], rd[k]);
-    }
-    double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
-#pragma unroll
-    for (int k = 0; k < kTileChunksPerLane; ++k) {
-      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
-      if (ci < nchunks) {
-        double et[C::N], ed[C::N];
-        W.terms(rt[k], rd[k], et, ed);
-#pragma unroll
-        for (int e = 0; e < C::N; ++e) {
-          E += et[e];
-          Ed += ed[e];
-          const bool pos = et[e] > rho * ed[e];
-          A += pos ? et[e] : 0.0;
-          Bd += pos ? ed[e] : 0.0;
-        }
-      }
-    }
-    E = wave_sum(E);
+__device__ inline void chunk_terms_tab(const double* T, int n_half, const DrawRows<DT, VEC>& W,
+                                       const typename Chunk<DT, VEC>::raw_t& rt,
+                                       const typename Chunk<DT, VEC>::raw_t& rd,
+                                       double (&et)[Chunk<DT, VEC>::N],
+                                       double (&ed)[Chunk<DT, VEC>::N]) {
+  if constexpr (DT == DT_BF16 && VEC == 8) {
+    tab_terms8(T, rt, n_half, W.c, W.Rt, et);
     if (W.residual) {
-      Ed = wave_sum(Ed);
-      A = wave_sum(A);
-      Bd = wave_sum(Bd);
+      tab_terms8(T, rd, n_half, W.c, W.Rd, ed);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ed[k] = 0.0;
     }
-    if (lane == 0) {
-      TileSums ts;
-      ts.E = E;
-      ts.Ed = Ed;
-      ts.A = A;
-      ts.Bd = Bd;
-      tsum[(long long)b * ntiles + t] = ts;
-    }
+  } else {
+    W.terms(rt, rd, et, ed);
   }
 }
 
@@ -549,23 +561,15 @@ __device__ inline double tiles_total(const TileSums* ts, int ntiles, int lane, i
   return carry;
 }
 
+// Phase 2 for one sequence, run by one wavefront: exact normalisers and
+// residual total from the tile sums, the crossing tile, then an in-order
+// prefix over the re-read tile.
 template <int DT, int VEC>
-__global__ __launch_bounds__(kBlock) void draw_pick(
-    int B, int K, int V, int ntiles, const void* __restrict__ target,
-    const void* __restrict__ draft, const DrawRow* __restrict__ draw,
-    const float* __restrict__ uniforms, double c, const TileSums* __restrict__ tsum,
-    int32_t* __restrict__ out_tokens, DevStats* __restrict__ st, double* aux_z) {
+__device__ void pick_token(int b, int K, int V, int ntiles, const DrawRow& dr,
+                           const DrawRows<DT, VEC>& W, const TileSums* __restrict__ ts,
+                           const float* __restrict__ uniforms, int32_t* __restrict__ out_tokens,
+                           DevStats* __restrict__ st, double* aux_z, int lane) {
   using C = Chunk<DT, VEC>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (b >= B) return;
-  const DrawRow dr = draw[b];
-  if (dr.j < 0) return;
-  DrawRows<DT, VEC> W;
-  W.init(target, draft, dr, b, K, V, c);
-  const TileSums* ts = tsum + (long long)b * ntiles;
-
-  // exact normalisers (fixed order, broadcast from lane 0)
   double St = 0.0, Sd = 0.0;
   for (int t = lane; t < ntiles; t += kWave) {
     St += ts[t].E;
@@ -672,6 +676,92 @@ __global__ __launch_bounds__(kBlock) void draw_pick(
     if (aux_z != nullptr) aux_z[b] = W.residual ? fmax(zres, 0.0) / St : -1.0;
     if (fallback) atomicAdd(&st->z0_fallbacks, 1ull);
   }
+}
+
+// Phase 1 of the draw: workgroup (b, g) sums tiles [g * tiles_per_group,
+// (g + 1) * tiles_per_group) of sequence b, one tile per wavefront at a time.
+// For bf16 rows every term comes from a float64 table of 2^(x*c) staged in
+// LDS, scaled exactly by 2^-R.
+template <int DT, int VEC>
+__global__ __launch_bounds__(kBlock) void draw(
+    int b0, int B, int K, int V, int ntiles, int tiles_per_group, int groups,
+    const void* __restrict__ target, const void* __restrict__ draft,
+    const DrawRow* __restrict__ draws, double c, int n_half, const double* __restrict__ table,
+    TileSums* __restrict__ tsum) {
+  using C = Chunk<DT, VEC>;
+  constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
+  __shared__ double T[kTab ? kTabMax : 1];
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int b = b0 + int(blockIdx.x) / groups, g = int(blockIdx.x) % groups;
+  const DrawRow dr = draws[b];
+  if (dr.j < 0) return;                       // uniform over the workgroup
+  DrawRows<DT, VEC> W;
+  W.init(target, draft, dr, b, K, V, c);
+  if constexpr (kTab) {
+    for (int i = threadIdx.x; i < n_half; i += kBlock)   // n_half pairs of doubles
+      reinterpret_cast<u32x4*>(T)[i] = reinterpret_cast<const u32x4*>(table)[i];
+    __syncthreads();
+  }
+  const double rho = dr.rho;
+  const long long nchunks = V / VEC;
+  const int t_end = min(ntiles, (g + 1) * tiles_per_group);
+  for (int t = g * tiles_per_group + wid; t < t_end; t += kWavesPerBlock) {
+    typename C::raw_t rt[kTileChunksPerLane], rd[kTileChunksPerLane];
+#pragma unroll
+    for (int k = 0; k < kTileChunksPerLane; ++k) {
+      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
+      if (ci < nchunks) W.load(ci, rt[k], rd[k]);
+    }
+    double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
+#pragma unroll
+    for (int k = 0; k < kTileChunksPerLane; ++k) {
+      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
+      if (ci < nchunks) {
+        double et[C::N], ed[C::N];
+        chunk_terms_tab<DT, VEC>(T, n_half, W, rt[k], rd[k], et, ed);
+#pragma unroll
+        for (int e = 0; e < C::N; ++e) {
+          E += et[e];
+          Ed += ed[e];
+          const bool pos = et[e] > rho * ed[e];
+          A += pos ? et[e] : 0.0;
+          Bd += pos ? ed[e] : 0.0;
+        }
+      }
+    }
+    E = wave_sum(E);
+    if (W.residual) {
+      Ed = wave_sum(Ed);
+      A = wave_sum(A);
+      Bd = wave_sum(Bd);
+    }
+    if (lane == 0) {
+      TileSums s;
+      s.E = E;
+      s.Ed = Ed;
+      s.A = A;
+      s.Bd = Bd;
+      tsum[(long long)b * ntiles + t] = s;
+    }
+  }
+}
+
+// Phase 2 as its own kernel: one wavefront per sequence.
+template <int DT, int VEC>
+__global__ __launch_bounds__(kBlock) void draw_pick(
+    int b0, int B, int K, int V, int ntiles, const void* __restrict__ target,
+    const void* __restrict__ draft, const DrawRow* __restrict__ draws,
+    const float* __restrict__ uniforms, double c, const TileSums* __restrict__ tsum,
+    int32_t* __restrict__ out_tokens, DevStats* __restrict__ st, double* aux_z) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = b0 + blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (b >= B) return;
+  const DrawRow dr = draws[b];
+  if (dr.j < 0) return;
+  DrawRows<DT, VEC> W;
+  W.init(target, draft, dr, b, K, V, c);
+  pick_token<DT, VEC>(b, K, V, ntiles, dr, W, tsum + (long long)b * ntiles, uniforms, out_tokens,
+                      st, aux_z, lane);
 }
 
 // --------------------------------------------------------------------------

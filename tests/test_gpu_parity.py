@@ -100,6 +100,45 @@ def test_c2_forced_segments_agree(sv, monkeypatch):
     assert torch.allclose(outs[0][2], outs[1][2], rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_fused_and_pipeline_paths_agree(sv, monkeypatch, name):
+    """The one-workgroup-per-sequence kernel (forced on for a small batch) and
+    the multi-kernel pipeline both match the oracle and each other."""
+    cfg = CONFIGS[name]
+    x = make_inputs(cfg, 5, DEV)
+    outs = {}
+    for path, min_b in (("pipeline", "0"), ("fused", "1")):
+        monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", min_b)
+        v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
+        outs[path] = (tok.clone(), alen.clone(), hist.clone(),
+                      {k: t.clone() for k, t in aux.items()})
+        v.close()
+    rows = np.arange(cfg.B)
+    ref = oracle_for(x, rows, "stochastic")
+    for path, (tok, alen, hist, aux) in outs.items():
+        rep = compare(rows, ref, tok, alen, "stochastic", aux, f"{name}/{path}")
+        check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
+        _log(f"{name}/{path}: {rep}")
+    a, b = outs["pipeline"], outs["fused"]
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert torch.allclose(a[3]["p_d"], b[3]["p_d"], rtol=1e-6, atol=0)
+    assert torch.allclose(a[3]["z"], b[3]["z"], rtol=1e-9, atol=1e-15)
+
+
+def test_c3_pipeline_path_sampled(sv, monkeypatch):
+    """The multi-kernel pipeline at the full c3 shape (the fused kernel is
+    the default there)."""
+    monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "0")
+    cfg = CONFIGS["c3"]
+    x = make_inputs(cfg, 1, DEV, "stochastic")
+    v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
+    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
+    rows = _sample(cfg.B, 16, 37)
+    rep = compare(rows, oracle_for(x, rows, "stochastic"), tok, alen, "stochastic", aux,
+                  "c3/pipeline")
+    _log(f"c3/pipeline: {rep}")
+
+
 # --------------------------------------------------------------------------
 # full-size configurations, sampled sequences
 # --------------------------------------------------------------------------
