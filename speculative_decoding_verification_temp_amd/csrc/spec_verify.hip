@@ -13,7 +13,7 @@
 #include "sv_fused.hpp"
 
 #ifndef SV_U_BF16
-#define SV_U_BF16 2
+#define SV_U_BF16 4
 #endif
 #ifndef SV_U_F32
 #define SV_U_F32 4
@@ -47,6 +47,7 @@ struct spec_verify_handle {
   double* table = nullptr;            // bf16 exponential table of the current call
   int tiles_per_group = 16;           // draw tiles per workgroup (tuning)
   int fused_min_batch = 0;            // smallest batch for one workgroup per sequence, 0 = off
+  int finish_seq = 1;                 // scan + draw + pick in one kernel after the streaming pass
   double* ema = nullptr;
   int32_t* steps = nullptr;
   sv::DevStats* stats = nullptr;
@@ -143,6 +144,14 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
+  if (h->finish_seq && L.ntiles <= sv::kFMaxTiles && rows <= sv::kFMaxRows) {
+    hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock>), dim3(B),
+                       dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
+                       h->parts, target, draft, tokens, uniforms, c, c64, n_half, out_tokens,
+                       out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q,
+                       h->aux_z);
+    return check_launch(h, "finish_seq");
+  }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
                      V, L.nseg, h->parts, target, draft, tokens, uniforms, c, out_tokens, out_len,
                      hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
@@ -244,6 +253,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   h->tiles_per_group = env_int("SPEC_VERIFY_TILES_PER_GROUP", 16);
   if (h->tiles_per_group < 1) h->tiles_per_group = 1;
   h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);
+  h->finish_seq = env_int("SPEC_VERIFY_FINISH_SEQ", 1);
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return SV_EHIP;

@@ -205,8 +205,10 @@ struct DrawRow {
 };
 
 // Per-tile sums left by the draw's first phase, all relative to the row
-// references R_t, R_d: E = sum e_t(v), Ed = sum e_d(v), and over the tokens
-// with e_t(v) > rho * e_d(v): A = sum e_t(v), Bd = sum e_d(v).
+// references R_t, R_d, with rho the streaming pass's S_t / S_d: E = sum e_t(v),
+// Ed = sum e_d(v), and over the tokens with e_t(v) > rho * e_d(v):
+// A = sum (e_t(v) - rho * e_d(v)), Bd = sum e_d(v). For the exact ratio rho',
+// the tile's residual weight is A + (rho - rho') * Bd.
 struct TileSums {
   double E, Ed, A, Bd;
 };

@@ -507,6 +507,19 @@ template <int DT, int VEC> struct DrawRows {
     rt = C::load(trow, ci);
     if (residual) rd = C::load(drow, ci);
   }
+  // exact draw weight of element e of a chunk: the residual max(0, e_t - rho e_d)
+  // (which = 1) or the target term e_t (which = 0)
+  __device__ inline double weight(const typename C::raw_t& rt, const typename C::raw_t& rd, int e,
+                                  int which, double rho) const {
+    float xt[C::N];
+    C::unpack(rt, xt);
+    const double et = exp2_acc(__builtin_fma(double(xt[e]), c, -Rt));
+    if (!which) return et;
+    float xd[C::N];
+    C::unpack(rd, xd);
+    const double ed = exp2_acc(__builtin_fma(double(xd[e]), c, -Rd));
+    return fmax(et - rho * ed, 0.0);
+  }
   // exact terms of one chunk (et, and ed when drawing from a residual)
   __device__ inline void terms(const typename C::raw_t& rt, const typename C::raw_t& rd,
                                double (&et)[C::N], double (&ed)[C::N]) const {
@@ -545,17 +558,84 @@ __device__ inline void chunk_terms_tab(const double* T, int n_half, const DrawRo
   }
 }
 
+// Tile-sum accumulation for one chunk of a bf16 row pair, a 32-bit word (two
+// tokens) at a time: table terms for both rows, the direct path only for
+// values outside the table, then E += e_t, Ed += e_d, and over p > q (judged
+// with the streaming pass's rho) A += e_t - rho e_d, Bd += e_d.
+__device__ inline void accum_pair(double et, double ed, double rho, double& E, double& Ed,
+                                  double& A, double& Bd) {
+  E += et;
+  Ed += ed;
+  const double dv = __builtin_fma(-rho, ed, et);
+  A += fmax(dv, 0.0);
+  Bd = __builtin_fma(dv > 0.0 ? 1.0 : 0.0, ed, Bd);
+}
+
+__device__ inline double tab_fix(double v, int idx, uint32_t bits, double c, double R) {
+  return idx < 0 ? exp2_acc(__builtin_fma(double(__uint_as_float(bits << 16)), c, -R)) : v;
+}
+
+template <int DT, int VEC>
+__device__ __forceinline__ void accum_chunk(const double* T, int n_half, const DrawRows<DT, VEC>& W,
+                                   const typename Chunk<DT, VEC>::raw_t& rt,
+                                   const typename Chunk<DT, VEC>::raw_t& rd, double rho,
+                                   double& E, double& Ed, double& A, double& Bd) {
+  using C = Chunk<DT, VEC>;
+  if constexpr (DT == DT_BF16 && VEC == 8) {
+    const int sht = -int(W.Rt), shd = -int(W.Rd);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t t0 = rt[k] & 0xffffu, t1 = rt[k] >> 16;
+      const int i0 = tab_index(t0, n_half), i1 = tab_index(t1, n_half);
+      double e0 = __builtin_ldexp(T[i0 < 0 ? 0 : i0], sht);
+      double e1 = __builtin_ldexp(T[i1 < 0 ? 0 : i1], sht);
+      if (W.residual) {
+        const uint32_t d0 = rd[k] & 0xffffu, d1 = rd[k] >> 16;
+        const int j0 = tab_index(d0, n_half), j1 = tab_index(d1, n_half);
+        double f0 = __builtin_ldexp(T[j0 < 0 ? 0 : j0], shd);
+        double f1 = __builtin_ldexp(T[j1 < 0 ? 0 : j1], shd);
+        if ((i0 | i1 | j0 | j1) < 0) {
+          e0 = tab_fix(e0, i0, t0, W.c, W.Rt);
+          e1 = tab_fix(e1, i1, t1, W.c, W.Rt);
+          f0 = tab_fix(f0, j0, d0, W.c, W.Rd);
+          f1 = tab_fix(f1, j1, d1, W.c, W.Rd);
+        }
+        accum_pair(e0, f0, rho, E, Ed, A, Bd);
+        accum_pair(e1, f1, rho, E, Ed, A, Bd);
+      } else {
+        if ((i0 | i1) < 0) {
+          e0 = tab_fix(e0, i0, t0, W.c, W.Rt);
+          e1 = tab_fix(e1, i1, t1, W.c, W.Rt);
+        }
+        E += e0;
+        E += e1;
+      }
+    }
+  } else {
+    double et[C::N], ed[C::N];
+    W.terms(rt, rd, et, ed);
+#pragma unroll
+    for (int e = 0; e < C::N; ++e) {
+      if (W.residual)
+        accum_pair(et[e], ed[e], rho, E, Ed, A, Bd);
+      else
+        E += et[e];
+    }
+  }
+}
+
 // In-order inclusive prefix over the tile weights of one sequence; returns
 // the total (same value on every lane).
+__device__ inline double tile_weight(const TileSums& s, int which, double drho) {
+  return which ? fmax(__builtin_fma(drho, s.Bd, s.A), 0.0) : s.E;
+}
+
 __device__ inline double tiles_total(const TileSums* ts, int ntiles, int lane, int which,
-                                     double rho) {
+                                     double drho) {
   double carry = 0.0;
   for (int t0 = 0; t0 < ntiles; t0 += kWave) {
     double v = 0.0;
-    if (t0 + lane < ntiles) {
-      const TileSums s = ts[t0 + lane];
-      v = which ? fmax(s.A - rho * s.Bd, 0.0) : s.E;
-    }
+    if (t0 + lane < ntiles) v = tile_weight(ts[t0 + lane], which, drho);
     carry += __shfl(wave_incl_scan(v, lane), kWave - 1, kWave);
   }
   return carry;
@@ -565,7 +645,7 @@ __device__ inline double tiles_total(const TileSums* ts, int ntiles, int lane, i
 // residual total from the tile sums, the crossing tile, then an in-order
 // prefix over the re-read tile.
 template <int DT, int VEC>
-__device__ void pick_token(int b, int K, int V, int ntiles, const DrawRow& dr,
+__device__ __forceinline__ void pick_token(int b, int K, int V, int ntiles, const DrawRow& dr,
                            const DrawRows<DT, VEC>& W, const TileSums* __restrict__ ts,
                            const float* __restrict__ uniforms, int32_t* __restrict__ out_tokens,
                            DevStats* __restrict__ st, double* aux_z, int lane) {
@@ -578,14 +658,15 @@ __device__ void pick_token(int b, int K, int V, int ntiles, const DrawRow& dr,
   St = __shfl(wave_sum(St), 0, kWave);
   Sd = __shfl(wave_sum(Sd), 0, kWave);
   const double rho = W.residual ? St / Sd : 0.0;
+  const double drho = dr.rho - rho;          // tile sums used the streaming pass's ratio
 
   int which = W.residual ? 1 : 0;
-  double total = tiles_total(ts, ntiles, lane, which, rho);
+  double total = tiles_total(ts, ntiles, lane, which, drho);
   const double zres = which ? total : -1.0;
   const bool fallback = W.residual && !(total > 0.0);
   if (fallback) {
     which = 0;
-    total = tiles_total(ts, ntiles, lane, 0, rho);
+    total = tiles_total(ts, ntiles, lane, 0, drho);
   }
   const double tgt = double(uniforms[(long long)b * (K + 1) + K]) * total;
 
@@ -595,10 +676,7 @@ __device__ void pick_token(int b, int K, int V, int ntiles, const DrawRow& dr,
   double base = 0.0, carry = 0.0;
   for (int t0 = 0; t0 < ntiles && tile < 0; t0 += kWave) {
     double v = 0.0;
-    if (t0 + lane < ntiles) {
-      const TileSums s = ts[t0 + lane];
-      v = which ? fmax(s.A - rho * s.Bd, 0.0) : s.E;
-    }
+    if (t0 + lane < ntiles) v = tile_weight(ts[t0 + lane], which, drho);
     const double incl = carry + wave_incl_scan(v, lane);
     const unsigned long long hit = __ballot(t0 + lane < ntiles && incl > tgt);
     const unsigned long long pos = __ballot(t0 + lane < ntiles && v > 0.0);
@@ -716,18 +794,7 @@ __global__ __launch_bounds__(kBlock) void draw(
 #pragma unroll
     for (int k = 0; k < kTileChunksPerLane; ++k) {
       const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
-      if (ci < nchunks) {
-        double et[C::N], ed[C::N];
-        chunk_terms_tab<DT, VEC>(T, n_half, W, rt[k], rd[k], et, ed);
-#pragma unroll
-        for (int e = 0; e < C::N; ++e) {
-          E += et[e];
-          Ed += ed[e];
-          const bool pos = et[e] > rho * ed[e];
-          A += pos ? et[e] : 0.0;
-          Bd += pos ? ed[e] : 0.0;
-        }
-      }
+      if (ci < nchunks) accum_chunk<DT, VEC>(T, n_half, W, rt[k], rd[k], rho, E, Ed, A, Bd);
     }
     E = wave_sum(E);
     if (W.residual) {
