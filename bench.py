@@ -198,12 +198,21 @@ def main():
         "roofline": roofline,
     }
     if args.copy_probe:
+        # a plain 1 GiB device copy: counter calibration and a bandwidth reference
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
         for _ in range(3):
             dst.copy_(src)
+        c1.record()
         torch.cuda.synchronize()
-        res["copy_probe_bytes"] = 1 << 30
+        ms = c0.elapsed_time(c1) / 3
+        res["copy_probe"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                             "ms": round(ms, 4), "gbs": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)}
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         # the output buffers hold the last timed step's results

@@ -376,3 +376,34 @@ def test_ema_tracks_oracle_and_accessors(sv):
     e, s = v.ema()
     torch.cuda.synchronize()
     assert torch.all(e == 0) and torch.all(s == 0)
+
+
+def test_c3_ema_600_steps(sv):
+    """The 600-step run at the full c3 shape with fresh logits each step and
+    EMA decay 0.99: four seeded slots are verified by the oracle at every
+    step (tokens, accept lengths) and their EMA compared at the end; every
+    step's outputs satisfy the invariants on the whole batch."""
+    cfg = CONFIGS["c3"]
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, cfg.torch_dtype, ema_decay=cfg.ema_decay)
+    ema = O.EmaState(cfg.B, cfg.ema_decay)
+    rows = _sample(cfg.B, 4, 38)
+    near = 0
+    for step in range(cfg.steps):
+        x = make_inputs(cfg, step, DEV, "stochastic")
+        tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T)
+        torch.cuda.synchronize()
+        ref = oracle_for(x, rows, "stochastic", ema=ema)
+        rep = compare(rows, ref, tok, alen, "stochastic", None, f"ema step {step}")
+        assert rep["mismatches"] == 0, rep
+        near += rep["near_boundary"]
+        check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
+        if step % 100 == 0:
+            _log(f"ema step {step}: mean accept {alen.float().mean().item():.3f}")
+    e, s = v.ema()
+    torch.cuda.synchronize()
+    e = e.cpu().numpy()
+    assert np.all(s.cpu().numpy()[: cfg.B] == cfg.steps)
+    err = np.abs(e[rows] - ema.ema[rows]).max()
+    _log(f"ema 600 steps: slots {rows.tolist()} gpu {np.round(e[rows], 6).tolist()} "
+         f"oracle {np.round(ema.ema[rows], 6).tolist()} max err {err:.2e} near-boundary {near}")
+    assert err <= 1e-5
