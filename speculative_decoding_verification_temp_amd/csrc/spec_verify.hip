@@ -107,11 +107,11 @@ Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
   return L;
 }
 
-// entries per sign of the bf16 exponential table: exponent fields from 2^-16
-// up, as many as keep |x * c| < 1000
+// entries per sign of the bf16 exponential table that the scaled lookups use:
+// exponent fields from 2^-25 up, as many as keep |x * c| < 1000
 int tab_half(double c) {
   int n = sv::kTabMaxExp;
-  while (n > 1 && std::ldexp(1.0, n - 16) * c > 1000.0) --n;
+  while (n > 1 && std::ldexp(1.0, n - 25) * c > 1000.0) --n;
   return n * 128;
 }
 

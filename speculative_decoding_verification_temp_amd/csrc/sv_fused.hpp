@@ -155,6 +155,328 @@ __device__ __forceinline__ void pick_token_block(int b, int K, int V, int ntiles
   }
 }
 
+// Draw tile sums of bf16 rows straight from the table entries 2^(x * c),
+// scaled by 2^-R once per tile instead of once per term. When both rows'
+// references satisfy |R| <= kUnscaledMaxR, every term of the rows is a normal
+// float64 number no larger than about 2^R (x * c <= R over a row), so
+//   E  = 2^-Rt sum Tt,   Ed = 2^-Rd sum Td,
+//   A  = 2^-Rt sum over {Tt > rho2 Td} of (Tt - rho2 Td),
+//   Bd = 2^-Rd sum over the same set of Td,   rho2 = rho 2^(Rt - Rd),
+// are the sums of the scaled terms, formed with one exact scaling per tile.
+// A table lookup costs a few packed 16-bit operations per word of two values:
+// offset = bits - base per half (the sign stays in bit 15 for in-window
+// values), byte offset = (offset << 3) with the sign put back in bit 15.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+constexpr float kUnscaledMaxR = 500.0f;
+constexpr uint32_t kTabOutBits = 0x70007000u;   // offset >= 4096 in either half
+
+// byte offsets into the table of the two bf16 values of word w (16 bits
+// each); ORs the raw offsets into acc, whose kTabOutBits then flag a value
+// outside the table window (its byte offset is then in range but meaningless)
+__device__ __forceinline__ uint32_t tab_offsets2(uint32_t w, uint32_t& acc) {
+  constexpr unsigned short kB = (unsigned short)(kTabELo << 7);
+  const u16x2 o = __builtin_bit_cast(u16x2, w) - (u16x2){kB, kB};
+  acc |= __builtin_bit_cast(uint32_t, o);
+  const u16x2 sh = o << (u16x2){3, 3};
+  return (w & 0x80008000u) | (__builtin_bit_cast(uint32_t, sh) & 0x7fff7fffu);
+}
+
+__device__ __forceinline__ double tab_at(const double* T, uint32_t byte_off) {
+  return *reinterpret_cast<const double*>(reinterpret_cast<const char*>(T) + byte_off);
+}
+
+// 2^(x * c) of one bf16 value: its table entry, or exp2_acc outside the window
+__device__ __forceinline__ double term_unscaled(const double* T, uint32_t bits, double c) {
+  const uint32_t off = (bits & 0x7fffu) - uint32_t(kTabELo << 7);
+  if (off < uint32_t(kTabStride)) return T[off + ((bits & 0x8000u) ? kTabStride : 0)];
+  return exp2_acc(double(__uint_as_float(bits << 16)) * c);
+}
+
+__device__ __forceinline__ void accum_pair_u(double et, double ed, double rho2, double& E,
+                                             double& Ed, double& A, double& Bd) {
+  E += et;
+  Ed += ed;
+  const double dv = __builtin_fma(-rho2, ed, et);
+  const double s = dv > 0.0 ? 1.0 : 0.0;
+  A = __builtin_fma(s, dv, A);
+  Bd = __builtin_fma(s, ed, Bd);
+}
+
+// A unit is kUnitChunks chunks of 8 bf16 values per lane and row; a tile is
+// kUnits units.
+constexpr int kUnitChunks = 1;
+constexpr int kUnits = kTileChunksPerLane / kUnitChunks;
+struct UnitBuf {
+  u32x4 a[kUnitChunks], d[kUnitChunks];
+};
+
+// word i of chunk k of a unit, by selects (no indexing of the register arrays)
+__device__ __forceinline__ uint32_t word_at(const u32x4 (&a)[kUnitChunks], int k, int i) {
+  static_assert(kUnitChunks <= 2, "select chain covers two chunks");
+  u32x4 x = a[0];
+  if constexpr (kUnitChunks == 2) x = k == 0 ? a[0] : a[1];
+  return i == 0 ? x[0] : i == 1 ? x[1] : i == 2 ? x[2] : x[3];
+}
+
+// one lane's sums over one unit (chunks c0 + k * kWave; RAGGED: chunks at or
+// past nchunks are skipped)
+template <bool RESID, bool RAGGED>
+__device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, long long c0,
+                                          long long nchunks, double rho2, double c, double& E,
+                                          double& Ed, double& A, double& Bd) {
+  uint32_t acc = 0;
+  E = Ed = A = Bd = 0.0;
+#pragma unroll
+  for (int k = 0; k < kUnitChunks; ++k) {
+    if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t pt = tab_offsets2(u.a[k][q], acc);
+      const double t0 = tab_at(T, pt & 0xffffu), t1 = tab_at(T, pt >> 16);
+      if constexpr (RESID) {
+        const uint32_t pd = tab_offsets2(u.d[k][q], acc);
+        const double f0 = tab_at(T, pd & 0xffffu), f1 = tab_at(T, pd >> 16);
+        accum_pair_u(t0, f0, rho2, E, Ed, A, Bd);
+        accum_pair_u(t1, f1, rho2, E, Ed, A, Bd);
+      } else {
+        E += t0;
+        E += t1;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // one chunk's lookups in flight at a time
+  }
+  if (acc & kTabOutBits) {     // a value outside the window: this lane again, term by term
+    E = Ed = A = Bd = 0.0;
+#pragma unroll 1
+    for (int v = 0; v < kUnitChunks * 8; ++v) {
+      const int k = v >> 3, q = v & 7;
+      if (RAGGED && c0 + (long long)k * kWave >= nchunks) break;
+      const uint32_t wt = word_at(u.a, k, q >> 1);
+      const double et = term_unscaled(T, (q & 1) ? wt >> 16 : wt & 0xffffu, c);
+      if constexpr (RESID) {
+        const uint32_t wd = word_at(u.d, k, q >> 1);
+        const double ed = term_unscaled(T, (q & 1) ? wd >> 16 : wd & 0xffffu, c);
+        accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
+      } else {
+        E += et;
+      }
+    }
+  }
+}
+
+// Tile sums of the draw rows. Wavefront w takes tiles w, w + NW, ... as a
+// stream of units, with the units of one tile in flight: the loads of unit
+// i + kUnits are issued right after unit i has been summed, so a wavefront
+// keeps kUnits - 1 units of loads outstanding while it computes. Chunks past
+// the row end are clamped to the last chunk for loading and skipped in the
+// sums.
+template <bool RESID, int NW>
+__device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow, const void* drow,
+                                               const DrawRow& dr, double c, int ntiles,
+                                               long long nchunks, TileSums* tiles, int wid,
+                                               int lane) {
+  using C = Chunk<DT_BF16, 8>;
+  const double rho2 = RESID ? __builtin_ldexp(dr.rho, int(dr.R_t) - int(dr.R_d)) : 0.0;
+  const int st = -int(dr.R_t), sd = -int(dr.R_d);
+  const int my_tiles = wid < ntiles ? (ntiles - 1 - wid) / NW + 1 : 0;
+  auto unit_c0 = [&](int ti, int u) -> long long {
+    return (long long)(wid + ti * NW) * kTileChunks + (long long)u * kUnitChunks * kWave + lane;
+  };
+  auto load_unit = [&](int ti, int u, UnitBuf& b) {
+    const long long c0 = unit_c0(ti, u);
+#pragma unroll
+    for (int k = 0; k < kUnitChunks; ++k) {
+      const long long ci = min(c0 + (long long)k * kWave, nchunks - 1);
+      b.a[k] = C::load(trow, ci);
+      if constexpr (RESID) b.d[k] = C::load(drow, ci);
+    }
+  };
+  auto finish_tile = [&](int ti, double E, double Ed, double A, double Bd) {
+    E = wave_sum(E);
+    if constexpr (RESID) {
+      Ed = wave_sum(Ed);
+      A = wave_sum(A);
+      Bd = wave_sum(Bd);
+    }
+    if (lane == 0) {
+      TileSums ts;
+      ts.E = __builtin_ldexp(E, st);
+      ts.Ed = RESID ? __builtin_ldexp(Ed, sd) : 0.0;
+      ts.A = RESID ? __builtin_ldexp(A, st) : 0.0;
+      ts.Bd = RESID ? __builtin_ldexp(Bd, sd) : 0.0;
+      tiles[wid + ti * NW] = ts;
+    }
+  };
+  if (my_tiles == 0) return;
+  UnitBuf b[kUnits];
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) load_unit(0, u, b[u]);
+  // every tile but this wavefront's last is whole (only the row's last tile
+  // can be ragged), and its loop body issues its loads unconditionally
+  int ti = 0;
+  for (; ti + 1 < my_tiles; ++ti) {
+    double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      double e, ed, a, bd;
+      unit_sums<RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      load_unit(ti + 1, u, b[u]);
+      E += e;
+      Ed += ed;
+      A += a;
+      Bd += bd;
+    }
+    finish_tile(ti, E, Ed, A, Bd);
+  }
+  double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
+  const bool whole = (long long)(wid + ti * NW + 1) * kTileChunks <= nchunks;
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) {
+    double e, ed, a, bd;
+    if (whole)
+      unit_sums<RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+    else
+      unit_sums<RESID, true>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+    E += e;
+    Ed += ed;
+    A += a;
+    Bd += bd;
+  }
+  finish_tile(ti, E, Ed, A, Bd);
+}
+
+// Phase 4 when the tile sums came from tiles_unscaled. Wavefronts 0-3 each
+// find the crossing tile from the tile sums (the same arithmetic in each, so
+// the same tile); thread t < kTileChunks then re-reads chunk t of that tile,
+// forms its 8 exact weights from the table relative to 2^Rt,
+//   residual: max(0, Tt - rho2 Td) with the exact rho2 = (St / Sd) 2^(Rt - Rd),
+//   bonus or Z = 0 fallback: Tt,
+// and a prefix over the chunk sums in token order finds the token, compared
+// against u * total scaled by 2^Rt (exact).
+template <int NT>
+__device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long long nchunks,
+                                              const DrawRow& dr, const void* trow,
+                                              const void* drow, bool residual, const double* T,
+                                              double c, const TileSums* ts,
+                                              const float* __restrict__ uniforms,
+                                              int32_t* __restrict__ out_tokens,
+                                              DevStats* __restrict__ st, double* aux_z,
+                                              PickShared& sh) {
+  using C = Chunk<DT_BF16, 8>;
+  static_assert(NT >= kTileChunks, "pick needs one thread per tile chunk");
+  constexpr int kPW = kTileChunks / kWave;      // wavefronts in the pick
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  int tile = -1, which = 0;
+  bool clamp = false, fallback = false;
+  double tgt = 0.0, base = 0.0, rho2 = 0.0, zres = -1.0, St = 0.0;
+  double wv[8];
+  double cs = 0.0;
+  int lp = -1;
+  long long ci = 0;
+  bool valid = false;
+  if (wid < kPW) {
+    double Sd = 0.0;
+    for (int t = lane; t < ntiles; t += kWave) {
+      St += ts[t].E;
+      Sd += ts[t].Ed;
+    }
+    St = __shfl(wave_sum(St), 0, kWave);
+    Sd = __shfl(wave_sum(Sd), 0, kWave);
+    const double rho = residual ? St / Sd : 0.0;
+    const double drho = dr.rho - rho;
+    which = residual ? 1 : 0;
+    double total = tiles_total(ts, ntiles, lane, which, drho);
+    zres = which ? total : -1.0;
+    fallback = residual && !(total > 0.0);
+    if (fallback) {
+      which = 0;
+      total = tiles_total(ts, ntiles, lane, 0, drho);
+    }
+    tgt = double(uniforms[(long long)b * (K + 1) + K]) * total;
+    int last_pos = -1;
+    double carry = 0.0;
+    for (int t0 = 0; t0 < ntiles && tile < 0; t0 += kWave) {
+      double v = 0.0;
+      if (t0 + lane < ntiles) v = tile_weight(ts[t0 + lane], which, drho);
+      const double incl = carry + wave_incl_scan(v, lane);
+      const unsigned long long hit = __ballot(t0 + lane < ntiles && incl > tgt);
+      const unsigned long long pos = __ballot(t0 + lane < ntiles && v > 0.0);
+      if (pos) last_pos = t0 + 63 - __clzll((long long)pos);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        tile = t0 + l;
+        base = __shfl(incl - v, l, kWave);
+      }
+      carry = __shfl(incl, kWave - 1, kWave);
+    }
+    clamp = tile < 0;
+    if (clamp) tile = last_pos;
+    rho2 = which ? __builtin_ldexp(rho, int(dr.R_t) - int(dr.R_d)) : 0.0;
+    // this thread's chunk of the crossing tile
+    ci = (long long)tile * kTileChunks + tid;
+    valid = tile >= 0 && ci < nchunks;
+    const long long cl = valid ? ci : 0;
+    const u32x4 wt = C::load(trow, cl);
+    const u32x4 wd = which ? C::load(drow, cl) : wt;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bt = (e & 1) ? wt[e >> 1] >> 16 : wt[e >> 1] & 0xffffu;
+      const double et = term_unscaled(T, bt, c);
+      if (which) {
+        const uint32_t bd = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
+        wv[e] = fmax(__builtin_fma(-rho2, term_unscaled(T, bd, c), et), 0.0);
+      } else {
+        wv[e] = et;
+      }
+      if (!valid) wv[e] = 0.0;
+      cs += wv[e];
+      lp = wv[e] > 0.0 ? int(ci * 8 + e) : lp;
+    }
+    // compare in units of 2^-Rt
+    tgt = __builtin_ldexp(tgt, int(dr.R_t));
+    base = __builtin_ldexp(base, int(dr.R_t));
+  }
+  const double wincl = wave_incl_scan(cs, lane);
+  int wlp = lp;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) wlp = max(wlp, __shfl_xor(wlp, o, kWave));
+  if (wid < kPW && lane == kWave - 1) sh.wsum[wid] = wincl;
+  if (wid < kPW && lane == 0) sh.wlp[wid] = wlp;
+  __syncthreads();
+  if (wid < kPW) {
+    double before = base;
+#pragma unroll
+    for (int w = 0; w < kPW; ++w) before += w < wid ? sh.wsum[w] : 0.0;
+    const double incl = before + wincl;
+    const unsigned long long hit = __ballot(valid && !clamp && incl > tgt);
+    int tok = -1;
+    if (hit && lane == __ffsll((long long)hit) - 1) {
+      double run = incl - cs;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        run += wv[e];
+        if (tok < 0 && run > tgt) tok = int(ci * 8 + e);
+      }
+      if (tok < 0) tok = lp;            // the chunk holds positive weight
+    }
+    tok = __shfl(tok, hit ? __ffsll((long long)hit) - 1 : 0, kWave);
+    if (lane == 0) sh.whit[wid] = hit ? tok : -1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int token = -1, last_elem = -1;
+#pragma unroll
+    for (int w = 0; w < kPW; ++w) {
+      if (token < 0) token = sh.whit[w];
+      last_elem = max(last_elem, sh.wlp[w]);
+    }
+    if (token < 0) token = last_elem;
+    out_tokens[(long long)b * (K + 1) + dr.j] = token;
+    if (aux_z != nullptr) aux_z[b] = residual ? fmax(zres, 0.0) / St : -1.0;
+    if (fallback) atomicAdd(&st->z0_fallbacks, 1ull);
+  }
+}
+
 // Phases 2-4 for one sequence, given its row statistics in LDS (fR, fS):
 // the acceptance scan on wavefront 0, the draw's float64 tile sums of row
 // pair j over all wavefronts of the workgroup, then the pick.
@@ -229,40 +551,60 @@ __device__ __forceinline__ void finish_sequence(
   if (dr.j < 0) return;
 
   // ---- 3. draw tile sums of row pair j (or target row K) ----
-  // wavefront w takes tiles w, w + kW, ...; the next tile's chunks are loaded
-  // while the current one is summed
+  // wavefront w takes tiles w, w + kW, ...
   DrawRows<DT, VEC> W;
   W.init(target, draft, dr, b, K, V, c64);
   const int ntiles = int((nchunks + kTileChunks - 1) / kTileChunks);
-  for (int t = wid; t < ntiles; t += kW) {
-    double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
+  // bf16 rows with moderate references: table terms without per-term scaling
+  // (tiles_unscaled); otherwise every term scaled by 2^-R as it is formed
+  bool unscaled = false;
+  if constexpr (DT == DT_BF16 && VEC == 8)
+    unscaled = fabsf(dr.R_t) <= kUnscaledMaxR && (!W.residual || fabsf(dr.R_d) <= kUnscaledMaxR);
+  if (unscaled) {
+    if constexpr (DT == DT_BF16 && VEC == 8) {
+      if (W.residual)
+        tiles_unscaled<true, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid, lane);
+      else
+        tiles_unscaled<false, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid, lane);
+    }
+  } else {
+    for (int t = wid; t < ntiles; t += kW) {
+      double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
 #pragma unroll
-    for (int k = 0; k < kTileChunksPerLane; ++k) {
-      const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
-      if (ci < nchunks) {
-        typename C::raw_t a, d;
-        W.load(ci, a, d);
-        accum_chunk<DT, VEC>(T, n_half, W, a, d, dr.rho, E, Ed, A, Bd);
+      for (int k = 0; k < kTileChunksPerLane; ++k) {
+        const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
+        if (ci < nchunks) {
+          typename C::raw_t a, d;
+          W.load(ci, a, d);
+          accum_chunk<DT, VEC>(T, n_half, W, a, d, dr.rho, E, Ed, A, Bd);
+        }
       }
-    }
-    E = wave_sum(E);
-    if (W.residual) {
-      Ed = wave_sum(Ed);
-      A = wave_sum(A);
-      Bd = wave_sum(Bd);
-    }
-    if (lane == 0) {
-      TileSums ts;
-      ts.E = E;
-      ts.Ed = Ed;
-      ts.A = A;
-      ts.Bd = Bd;
-      tiles[t] = ts;
+      E = wave_sum(E);
+      if (W.residual) {
+        Ed = wave_sum(Ed);
+        A = wave_sum(A);
+        Bd = wave_sum(Bd);
+      }
+      if (lane == 0) {
+        TileSums ts;
+        ts.E = E;
+        ts.Ed = Ed;
+        ts.A = A;
+        ts.Bd = Bd;
+        tiles[t] = ts;
+      }
     }
   }
   __syncthreads();
 
   // ---- 4. pick ----
+  if constexpr (DT == DT_BF16 && VEC == 8) {
+    if (unscaled) {
+      pick_unscaled<NT>(b, K, ntiles, nchunks, dr, W.trow, W.drow, W.residual, T, c64, tiles,
+                        uniforms, out_tokens, st, aux_z, psh);
+      return;
+    }
+  }
   pick_token_block<DT, VEC, NT>(b, K, V, ntiles, dr, W, tiles, uniforms, out_tokens, st, aux_z,
                                 psh);
 }
@@ -333,7 +675,7 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
   if (ngroups > 0) issue(0, buf[0]);
   if (ngroups > 1) issue(1, buf[1]);
   if constexpr (kTab) {
-    for (int i = tid; i < 2 * n_half; i += kFBlock) T[i] = exp_table_entry(i, n_half, c64);
+    for (int i = tid; i < kTabMax; i += kFBlock) T[i] = exp_table_entry(i, c64);
   }
 
   float Ra[2] = {kRefInit, kRefInit};
@@ -431,7 +773,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
   if constexpr (kTab) {
-    for (int i = tid; i < 2 * n_half; i += NT) T[i] = exp_table_entry(i, n_half, c64);
+    for (int i = tid; i < kTabMax; i += NT) T[i] = exp_table_entry(i, c64);
   }
   for (int r = tid; r < rows; r += NT) {
     float R;

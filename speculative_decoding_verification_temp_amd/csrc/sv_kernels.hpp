@@ -296,26 +296,32 @@ __device__ inline void emit_and_update(int lane, int b, int K, int j, bool bad,
   }
 }
 
-// Table of 2^(x * c) in float64 for every bf16 value x with 2^-16 <= |x| <
-// 2^(n_exp - 16): n_exp exponent fields of 128 mantissas, positive values
-// first. n_exp is chosen on the host so that |x * c| < 1000 over the table,
-// which keeps every entry a normal float64. Other values (0, tiny, huge,
-// infinities) take the direct exp2_acc path.
-constexpr int kTabELo = 127 - 16;
-constexpr int kTabMaxExp = 23;
-constexpr int kTabMax = 2 * kTabMaxExp * 128;
+// Table of 2^(x * c) in float64 for the bf16 values x with 2^-25 <= |x| <
+// 2^7: 32 exponent fields of 128 mantissas per sign. Entry (off, sign), off =
+// (bits & 0x7fff) - (kTabELo << 7), sits at index off + 4096 * sign, so that
+// its byte offset is (off << 3) | (sign << 15): the whole table is exactly
+// 64 KiB and any 16-bit byte offset stays inside it. Entries where |x * c|
+// exceeds about 1000 are not normal float64 numbers; the scaled lookups below
+// use only the first n_half offsets of each sign (n_half chosen on the host so
+// that |x * c| <= 1000 there) and take every other value (0, tiny, huge,
+// infinities) through the direct exp2_acc path.
+constexpr int kTabELo = 127 - 25;
+constexpr int kTabMaxExp = 32;
+constexpr int kTabStride = kTabMaxExp * 128;   // 4096 entries per sign
+constexpr int kTabMax = 2 * kTabStride;        // 8192 entries, 64 KiB
 
-// entry i of the table (value index order as above)
-__device__ inline double exp_table_entry(int i, int n_half, double c) {
-  const int neg = i >= n_half;
-  const uint32_t bits = uint32_t((neg ? i - n_half : i) + (kTabELo << 7)) | (neg ? 0x8000u : 0u);
+// entry i of the table (layout as above)
+__device__ inline double exp_table_entry(int i, double c) {
+  const uint32_t bits = uint32_t((i & (kTabStride - 1)) + (kTabELo << 7)) |
+                        (i >= kTabStride ? 0x8000u : 0u);
   return exp2_acc(double(__uint_as_float(bits << 16)) * c);
 }
 
-// table offset of a bf16 value, or -1 when it is outside the table
+// table index of a bf16 value, or -1 when it is outside the first n_half
+// offsets of its sign
 __device__ inline int tab_index(uint32_t bits, int n_half) {
   const uint32_t off = (bits & 0x7fffu) - uint32_t(kTabELo << 7);
-  return off < uint32_t(n_half) ? int(off) + ((bits & 0x8000u) ? n_half : 0) : -1;
+  return off < uint32_t(n_half) ? int(off) + ((bits & 0x8000u) ? kTabStride : 0) : -1;
 }
 
 // 2^(x*c - R) for the bf16 values of one chunk: table loads for all of them
@@ -359,8 +365,8 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
     double* aux_q, double* aux_z, double* __restrict__ table, int n_half, double c64) {
   // the draw's bf16 exponential table, spread over this grid's threads
   if (table != nullptr)
-    for (int i = blockIdx.x * kBlock + threadIdx.x; i < 2 * n_half; i += gridDim.x * kBlock)
-      table[i] = exp_table_entry(i, n_half, c64);
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < kTabMax; i += gridDim.x * kBlock)
+      table[i] = exp_table_entry(i, c64);
   const int lane = threadIdx.x & (kWave - 1);
   const int b = b0 + blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (b >= B) return;
@@ -776,7 +782,7 @@ __global__ __launch_bounds__(kBlock) void draw(
   DrawRows<DT, VEC> W;
   W.init(target, draft, dr, b, K, V, c);
   if constexpr (kTab) {
-    for (int i = threadIdx.x; i < n_half; i += kBlock)   // n_half pairs of doubles
+    for (int i = threadIdx.x; i < kTabMax / 2; i += kBlock)   // pairs of doubles
       reinterpret_cast<u32x4*>(T)[i] = reinterpret_cast<const u32x4*>(table)[i];
     __syncthreads();
   }
