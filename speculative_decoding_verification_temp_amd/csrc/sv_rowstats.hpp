@@ -1,0 +1,235 @@
+// Streaming passes over the logit rows (gfx950).
+//
+//   rowstats_sum   every (row, segment) of the target and draft logits:
+//                  running sum of softmax terms relative to an integer
+//                  reference exponent (stochastic mode).
+//   rowstats_max   every (row, segment) of the target logits: max,
+//                  lowest-index argmax and a NaN flag (greedy and margin).
+//
+// Both keep their per-segment partials in a fixed order; reruns are bitwise
+// identical.
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+// --------------------------------------------------------------------------
+// Row addressing. Stochastic rows of sequence b: r = 0..K are target rows,
+// r = K+1..2K are draft rows 0..K-1. Greedy/margin rows: r = 0..K target.
+// --------------------------------------------------------------------------
+template <int DT>
+__device__ inline const void* row_ptr(const void* target, const void* draft, int b, int r,
+                                      int K, int V) {
+  constexpr int s = elem_bytes<DT>();
+  if (r <= K)
+    return static_cast<const char*>(target) + ((long long)b * (K + 1) + r) * (long long)V * s;
+  return static_cast<const char*>(draft) + ((long long)b * K + (r - K - 1)) * (long long)V * s;
+}
+
+// --------------------------------------------------------------------------
+// Streaming softmax normaliser. Each lane keeps a float64 sum S of
+// 2^(x*c - R) with an integer reference R >= max(x)*c; when a new chunk group
+// raises the maximum, S is rescaled by an exact power of two. Within a group
+// the terms are added pairwise in fp32 and the group total is added to S in
+// fp64.
+// --------------------------------------------------------------------------
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_sum(
+    const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
+    int nseg, int seg_chunks, float c, RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+  using C = Chunk<DT, VEC>;
+  const int tid = threadIdx.x;
+  const int rows = 2 * K + 1;
+  const long long wg = (long long)b0 * rows * nseg + blockIdx.x;   // global (row, segment)
+  const int seg = int(wg % nseg);
+  const long long grow = wg / nseg;
+  const int b = int(grow / rows), r = int(grow % rows);
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+
+  const void* row = row_ptr<DT>(target, draft, b, r, K, V);
+  const long long nchunks = V / VEC;
+  const long long c0 = (long long)seg * seg_chunks;
+  const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
+
+  float R = kRefInit;
+  double S = 0.0;
+  long long ci = c0 + tid;
+  // full groups of U chunks per lane
+  for (; ci + (long long)(U - 1) * kBlock < c1; ci += (long long)U * kBlock) {
+    typename C::raw_t raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = C::load(row, ci + (long long)u * kBlock);
+    float x[U][C::N];
+#pragma unroll
+    for (int u = 0; u < U; ++u) C::unpack(raw[u], x[u]);
+    float gm = x[0][0];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < C::N; ++k) gm = fmaxf(gm, x[u][k]);
+    const float Rn = fmaxf(R, ceilf(gm * c));
+    S = rescale(S, R, Rn);
+    R = Rn;
+    float t[U * C::N];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < C::N; ++k) t[u * C::N + k] = term(x[u][k], c, R);
+#pragma unroll
+    for (int w = 1; w < U * C::N; w <<= 1)
+#pragma unroll
+      for (int k = 0; k + w < U * C::N; k += 2 * w) t[k] += t[k + w];
+    S += (double)t[0];
+  }
+  // remainder, one chunk at a time
+  for (; ci < c1; ci += kBlock) {
+    typename C::raw_t raw = C::load(row, ci);
+    float x[C::N];
+    C::unpack(raw, x);
+    float gm = x[0];
+#pragma unroll
+    for (int k = 1; k < C::N; ++k) gm = fmaxf(gm, x[k]);
+    const float Rn = fmaxf(R, ceilf(gm * c));
+    S = rescale(S, R, Rn);
+    R = Rn;
+    float t[C::N];
+#pragma unroll
+    for (int k = 0; k < C::N; ++k) t[k] = term(x[k], c, R);
+#pragma unroll
+    for (int w = 1; w < C::N; w <<= 1)
+#pragma unroll
+      for (int k = 0; k + w < C::N; k += 2 * w) t[k] += t[k + w];
+    S += (double)t[0];
+  }
+
+  // workgroup combine: common reference, exact rescale, fixed-order sums
+  __shared__ float sR[kWavesPerBlock];
+  __shared__ double sS[kWavesPerBlock];
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  float Rw = wave_max(R);
+  double Sw = wave_sum(rescale(S, R, Rw));
+  if (lane == 0) {
+    sR[wid] = Rw;
+    sS[wid] = Sw;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float Rb = sR[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) Rb = fmaxf(Rb, sR[w]);
+    double Sb = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) Sb += rescale(sS[w], sR[w], Rb);
+    RowPart p;
+    p.S = Sb;
+    p.R = Rb;
+    p.m = 0.0f;
+    p.idx = -1;
+    p.flags = 0;
+    parts[wg] = p;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Streaming max / argmax / NaN flag over target rows (greedy, margin).
+// A lane remembers the first chunk in which its running maximum was reached
+// and finds the lowest matching element in it at the end.
+// --------------------------------------------------------------------------
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ target, int K,
+                                                       int V, int nseg, int seg_chunks,
+                                                       RowPart* __restrict__ parts,
+                                                       uint32_t* __restrict__ hist) {
+  using C = Chunk<DT, VEC>;
+  const int tid = threadIdx.x;
+  const long long wg = blockIdx.x;
+  const int rows = K + 1;
+  const int seg = int(wg % nseg);
+  const long long grow = wg / nseg;
+  const int b = int(grow / rows), r = int(grow % rows);
+  if (wg == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+
+  const void* row = row_ptr<DT>(target, nullptr, b, r, K, V);
+  const long long nchunks = V / VEC;
+  const long long c0 = (long long)seg * seg_chunks;
+  const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
+
+  float best = -__builtin_inff();
+  long long best_c = -1;
+  typename C::raw_t best_raw{};
+  uint32_t nan = 0;
+  long long ci = c0 + tid;
+  for (; ci + (long long)(U - 1) * kBlock < c1; ci += (long long)U * kBlock) {
+    typename C::raw_t raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = C::load(row, ci + (long long)u * kBlock);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[C::N];
+      C::unpack(raw[u], x);
+      float cm = x[0];
+#pragma unroll
+      for (int k = 1; k < C::N; ++k) cm = fmaxf(cm, x[k]);
+      nan |= C::nan_bits(raw[u]);
+      const bool up = cm > best;
+      best = up ? cm : best;
+      best_c = up ? ci + (long long)u * kBlock : best_c;
+      best_raw = up ? raw[u] : best_raw;
+    }
+  }
+  for (; ci < c1; ci += kBlock) {
+    typename C::raw_t raw = C::load(row, ci);
+    float x[C::N];
+    C::unpack(raw, x);
+    float cm = x[0];
+#pragma unroll
+    for (int k = 1; k < C::N; ++k) cm = fmaxf(cm, x[k]);
+    nan |= C::nan_bits(raw);
+    const bool up = cm > best;
+    best = up ? cm : best;
+    best_c = up ? ci : best_c;
+    best_raw = up ? raw : best_raw;
+  }
+  int idx = -1;
+  if (best_c >= 0) {
+    float x[C::N];
+    C::unpack(best_raw, x);
+    int e = C::N - 1;
+#pragma unroll
+    for (int k = C::N - 1; k >= 0; --k) e = (x[k] == best) ? k : e;
+    idx = int(best_c * VEC + e);
+  }
+
+  __shared__ float sm[kWavesPerBlock];
+  __shared__ int si[kWavesPerBlock];
+  __shared__ uint32_t sn[kWavesPerBlock];
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  wave_argmax(best, idx);
+  nan = wave_or(nan);
+  if (lane == 0) {
+    sm[wid] = best;
+    si[wid] = idx;
+    sn[wid] = nan;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m = sm[0];
+    int i = si[0];
+    uint32_t f = sn[0];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) {
+      argmax_combine(m, i, sm[w], si[w]);
+      f |= sn[w];
+    }
+    RowPart p;
+    p.S = 0.0;
+    p.R = 0.0f;
+    p.m = m;
+    p.idx = i;
+    p.flags = f ? 1 : 0;
+    parts[wg] = p;
+  }
+}
+
+}  // namespace sv
