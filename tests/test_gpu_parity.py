@@ -14,7 +14,8 @@ import torch
 
 from oracle import spec_oracle as O
 from tests.parity import check_invariants, compare, oracle_for
-from workloads import CONFIGS, const_alpha_inputs, make_inputs, mc_inputs, to_host_f64
+from workloads import (CONFIGS, const_alpha_inputs, make_inputs, mc_inputs, to_host_f64,
+                       window_edge_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -272,6 +273,45 @@ def test_scalar_path_odd_vocab_bf16(sv):
         ref = oracle_for(x, rows, mode, tau=0.3)
         compare(rows, ref, tok, alen, mode, aux, f"V1001/{mode}")
         check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
+
+
+def test_bf16_values_outside_table_window(sv):
+    """bf16 rows holding +-0, magnitudes below 2^-25, magnitudes of 128 and
+    more, -inf, and dominant +150 entries: the draw's table lookups flag these
+    values and recompute those lanes term by term. Full batch against the
+    oracle, ragged last tile (V = 32000)."""
+    cfg = CONFIGS["c2"].scaled(B=64, K=4, T=1.0)
+    x = window_edge_inputs(cfg, 0, DEV)
+    v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
+    rows = np.arange(cfg.B)
+    ref = oracle_for(x, rows, "stochastic")
+    rep = compare(rows, ref, tok, alen, "stochastic", aux, "window edges")
+    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
+    assert np.array_equal(hist.cpu().numpy(), ref.hist)
+    assert np.all(alen.cpu().numpy() >= 0)
+    _log(f"window edges: {rep}")
+
+
+@pytest.mark.parametrize("case", ["low_temperature", "shifted_logits"])
+def test_bf16_large_reference_scaled_draw(sv, case):
+    """Rows whose integer reference |R| = |ceil(max(x) log2(e) / T)| exceeds 500
+    (T = 0.02, or logits shifted to about -900) take the draw path that scales
+    every term by 2^-R as it is formed. Full batch against the oracle."""
+    if case == "low_temperature":
+        cfg = CONFIGS["c2"].scaled(B=48, K=3, T=0.02)
+        x = make_inputs(cfg, 1, DEV)
+    else:
+        cfg = CONFIGS["c2"].scaled(B=48, K=3, T=1.0)
+        x = make_inputs(cfg, 2, DEV)
+        for key in ("target", "draft"):
+            x[key] = (x[key].to(torch.float32) - 900.0).to(torch.bfloat16).contiguous()
+    v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
+    rows = np.arange(cfg.B)
+    ref = oracle_for(x, rows, "stochastic")
+    rep = compare(rows, ref, tok, alen, "stochastic", aux, case)
+    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
+    assert np.array_equal(hist.cpu().numpy(), ref.hist)
+    _log(f"{case}: {rep}")
 
 
 # --------------------------------------------------------------------------

@@ -5,4 +5,5 @@ of the verification arithmetic; both the HIP library and the CPU oracle consume
 what it produces.
 """
 
-from .gen import CONFIGS, Config, make_inputs, mc_inputs, const_alpha_inputs, to_host_f64  # noqa: F401
+from .gen import (CONFIGS, Config, make_inputs, mc_inputs, const_alpha_inputs,  # noqa: F401
+                  to_host_f64, window_edge_inputs)

@@ -167,6 +167,33 @@ def make_inputs(cfg: Config, step: int = 0, device="cpu", mode: str | None = Non
                 pq_idx=pq_idx, z_idx=z_idx)
 
 
+def window_edge_inputs(cfg: Config, step: int = 0, device="cpu") -> dict:
+    """bf16-style logits that reach every special value a float64 exponential
+    table over 2^-25 <= |x| < 2^7 does not cover. In a seeded ~2.2% of the
+    entries of every target and draft row: +-0.0 (1%), +-2^-30 (0.5%), -inf
+    (0.5%) and values in (-228, -128] (0.2%); in the target rows of even
+    sequences also +150 at ~0.02% of the entries, which then dominate p.
+    Drafted tokens are sampled from the modified draft rows at T."""
+    x = make_inputs(cfg, step, device, "stochastic")
+    g = _gen(device, seed_for(cfg.index, step, 4))
+    for key in ("target", "draft"):
+        t = x[key].to(torch.float32)
+        u = torch.rand(t.shape, generator=g, device=device)
+        sgn = torch.where(torch.rand(t.shape, generator=g, device=device) < 0.5, -1.0, 1.0)
+        big = -128.0 - 100.0 * torch.rand(t.shape, generator=g, device=device)
+        t = torch.where(u < 0.010, 0.0 * sgn, t)
+        t = torch.where((u >= 0.010) & (u < 0.015), sgn * 2.0 ** -30, t)
+        t = torch.where((u >= 0.015) & (u < 0.020), torch.full_like(t, float("-inf")), t)
+        t = torch.where((u >= 0.020) & (u < 0.022), big, t)
+        if key == "target":
+            even = (torch.arange(cfg.B, device=device) % 2 == 0).view(-1, 1, 1)
+            t = torch.where(even & (u >= 0.9998), torch.full_like(t, 150.0), t)
+        x[key] = t.to(cfg.torch_dtype).contiguous()
+    g1 = _gen(device, seed_for(cfg.index, step, 5))
+    x["tokens"] = _gumbel_max(x["draft"], cfg.T, g1).to(torch.int32).contiguous()
+    return x
+
+
 def _log(p) -> np.ndarray:
     with np.errstate(divide="ignore"):
         return np.log(np.asarray(p, dtype=np.float64))
