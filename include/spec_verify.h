@@ -158,11 +158,13 @@ int spec_verify_get_stats(spec_verify_handle *h, spec_verify_stats *out, int res
 /*
  * Profiling. With enable != 0, each later spec_verify call records HIP events
  * on its stream just before and just after its streaming pass over the logits
- * and after its last kernel (up to 4096 calls between reads; later calls are
- * not recorded). The events are created here, never in spec_verify.
- * spec_verify_profile_read waits for the recorded calls to finish and returns
- * the summed milliseconds of the streaming pass and of whole calls, and how
- * many calls were recorded, then starts a new window. enable = 0 frees them.
+ * (up to 4096 calls between reads; later calls are not recorded), and with
+ * bit 1 of enable set (enable = 2 or 3) also after its last kernel. The events
+ * are timing-only (no system-scope fence) and created here, never in
+ * spec_verify. spec_verify_profile_read waits for the recorded calls to finish
+ * and returns the summed milliseconds of the streaming pass and of whole calls
+ * (0 unless call ends are recorded), and how many calls were recorded, then
+ * starts a new window. enable = 0 frees them.
  */
 int spec_verify_profile(spec_verify_handle *h, int enable);
 int spec_verify_profile_read(spec_verify_handle *h, double *stream_pass_ms, double *call_ms,

@@ -221,9 +221,11 @@ class SpecVerifier:
 
 
     # -- profiling --
-    def profile(self, enable: bool = True):
-        """Record HIP events around the streaming pass of later calls."""
-        self._check(self.lib.spec_verify_profile(self._h, int(enable)), "profile")
+    def profile(self, enable: bool = True, call_end: bool = False):
+        """Record HIP events around the streaming pass of later calls (and after
+        each call when call_end is set)."""
+        flag = (1 | (2 if call_end else 0)) if enable else 0
+        self._check(self.lib.spec_verify_profile(self._h, flag), "profile")
 
     def profile_read(self):
         """(streaming-pass ms, whole-call ms, calls) summed since the last read."""

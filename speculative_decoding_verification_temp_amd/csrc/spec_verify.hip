@@ -58,6 +58,7 @@ struct spec_verify_handle {
   double* aux_z = nullptr;
   int32_t* aux_argmax = nullptr;
   hipEvent_t* prof_ev = nullptr;   // 3 events per recorded call
+  bool prof_call_end = false;      // also record the end of each call
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
@@ -392,7 +393,7 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   if (rc == SV_OK) {
     ++h->calls;
     if (h->prof_ev != nullptr && h->prof_n < h->prof_cap) {
-      prof_mark(h, 2, stream);
+      if (h->prof_call_end) prof_mark(h, 2, stream);
       ++h->prof_n;
     }
   }
@@ -411,8 +412,10 @@ int spec_verify_profile(spec_verify_handle* h, int enable) {
   if (!enable) return SV_OK;
   h->prof_ev = new (std::nothrow) hipEvent_t[3 * kProfCalls];
   if (h->prof_ev == nullptr) return SV_ENOMEM;
+  // timing-only events: no system-scope fence when they complete, so that
+  // recording them perturbs the calls they bracket as little as possible
   for (int i = 0; i < 3 * kProfCalls; ++i) {
-    if (hipEventCreate(&h->prof_ev[i]) != hipSuccess) {
+    if (hipEventCreateWithFlags(&h->prof_ev[i], hipEventDisableSystemFence) != hipSuccess) {
       for (int k = 0; k < i; ++k) (void)hipEventDestroy(h->prof_ev[k]);
       delete[] h->prof_ev;
       h->prof_ev = nullptr;
@@ -421,6 +424,7 @@ int spec_verify_profile(spec_verify_handle* h, int enable) {
   }
   h->prof_cap = kProfCalls;
   h->prof_n = 0;
+  h->prof_call_end = (enable & 2) != 0;
   return SV_OK;
 }
 
@@ -430,9 +434,11 @@ int spec_verify_profile_read(spec_verify_handle* h, double* stream_pass_ms, doub
   double a = 0.0, b = 0.0;
   for (int i = 0; i < h->prof_n; ++i) {
     float t1 = 0.f, t2 = 0.f;
-    if (hipEventSynchronize(h->prof_ev[3 * i + 2]) != hipSuccess ||
+    const int last = h->prof_call_end ? 2 : 1;
+    if (hipEventSynchronize(h->prof_ev[3 * i + last]) != hipSuccess ||
         hipEventElapsedTime(&t1, h->prof_ev[3 * i], h->prof_ev[3 * i + 1]) != hipSuccess ||
-        hipEventElapsedTime(&t2, h->prof_ev[3 * i], h->prof_ev[3 * i + 2]) != hipSuccess)
+        (h->prof_call_end &&
+         hipEventElapsedTime(&t2, h->prof_ev[3 * i], h->prof_ev[3 * i + 2]) != hipSuccess))
       return fail(h, SV_EHIP, "event timing failed");
     a += t1;
     b += t2;

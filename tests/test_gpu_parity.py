@@ -447,3 +447,23 @@ def test_c3_ema_600_steps(sv):
     _log(f"ema 600 steps: slots {rows.tolist()} gpu {np.round(e[rows], 6).tolist()} "
          f"oracle {np.round(ema.ema[rows], 6).tolist()} max err {err:.2e} near-boundary {near}")
     assert err <= 1e-5
+
+
+def test_profiling_events(sv):
+    """The profiling window counts the recorded calls; the streaming-pass time
+    is positive and, when call ends are recorded, no longer than the call."""
+    cfg = CONFIGS["c2"].scaled(B=16)
+    x = make_inputs(cfg, 0, DEV)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    for call_end in (False, True):
+        v.profile(True, call_end=call_end)
+        for _ in range(3):
+            v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+        pass_ms, call_ms, n = v.profile_read()
+        assert n == 3 and pass_ms > 0.0
+        if call_end:
+            assert call_ms >= pass_ms
+        else:
+            assert call_ms == 0.0
+        v.profile(False)
+
