@@ -170,15 +170,22 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr float kUnscaledMaxR = 500.0f;
 constexpr uint32_t kTabOutBits = 0x70007000u;   // offset >= 4096 in either half
 
-// byte offsets into the table of the two bf16 values of word w (16 bits
-// each); ORs the raw offsets into acc, whose kTabOutBits then flag a value
-// outside the table window (its byte offset is then in range but meaningless)
+// Table byte offsets of the two bf16 values of word w: the low 16 bits of
+// the result for the low value, the high 16 bits for the high one, each
+// ((bits - base) << 3) with the value's sign in bit 15 (one bit insert). For a
+// value inside the window bit 15 of the shifted offset is already 0; for any
+// other value the offset is meaningless but still a 16-bit offset, i.e.
+// inside the table. ORs the raw offsets into acc, whose kTabOutBits then flag
+// such values. The empty asm keeps the packed offsets as one value, so that
+// each half costs one extract.
 __device__ __forceinline__ uint32_t tab_offsets2(uint32_t w, uint32_t& acc) {
   constexpr unsigned short kB = (unsigned short)(kTabELo << 7);
   const u16x2 o = __builtin_bit_cast(u16x2, w) - (u16x2){kB, kB};
   acc |= __builtin_bit_cast(uint32_t, o);
-  const u16x2 sh = o << (u16x2){3, 3};
-  return (w & 0x80008000u) | (__builtin_bit_cast(uint32_t, sh) & 0x7fff7fffu);
+  const uint32_t sh = __builtin_bit_cast(uint32_t, (u16x2)(o << (u16x2){3, 3}));
+  uint32_t p = (w & 0x80008000u) | sh;
+  asm volatile("" : "+v"(p));
+  return p;
 }
 
 __device__ __forceinline__ double tab_at(const double* T, uint32_t byte_off) {
