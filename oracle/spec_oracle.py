@@ -49,6 +49,20 @@ listed with its reason in the design notes):
     stochastic mode.
   * EMA: per call and slot, x = accept_len / K; the first observation of a slot
     sets it, later ones do ema = decay * ema + (1 - decay) * x.
+  * Stopping rules ([DVC] "Verify several proposed tokens in one target pass"
+    and "Speculation needs cache rollback": end-of-sequence and length limits
+    may end a cycle before the draft block is used up, and the returned tokens
+    must agree with them). Optional per call: an end-of-sequence token id eos
+    (-1 = none), and per sequence a draft count k_b in [0, K] and an emission
+    budget m_b >= 1. The walk tests positions 0..k_b-1 only (j <= k_b, the
+    bonus comes from target row k_b); the candidate emission d_0..d_{j-1}, c is
+    cut after its first eos and to its first m_b tokens; accept_len is the
+    number of drafts emitted; the correction or bonus c is drawn only when it
+    is emitted (still with u[b, K]). Needed rows become target rows 0..k_b and
+    draft rows 0..k_b-1; k_b outside [0, K] or m_b < 1 makes the sequence
+    invalid. The EMA observes accept_len / k_b and skips sequences with
+    k_b = 0. With eos = -1, k_b = K and m_b >= K + 1 every rule above reduces
+    to the plain cycle.
 """
 
 from __future__ import annotations
@@ -170,113 +184,143 @@ def inverse_cdf(w, u: float):
 @dataclass
 class SequenceResult:
     tokens: np.ndarray            # [K+1] int64, -1 after the last emitted token
-    accept_len: int               # accepted drafts j (emitted = j + 1); -1 if invalid
+    accept_len: int               # drafts emitted (plain cycle: j, emitted = j + 1); -1 if invalid
     p_d: np.ndarray               # [K] p_i(d_i) (stochastic); margin ratio (margin); NaN (greedy)
     q_d: np.ndarray               # [K] q_i(d_i) (stochastic); NaN otherwise
-    z: float                      # residual Z at j (stochastic, j < K); -1 otherwise
+    z: float                      # residual Z at j (stochastic, j < k_b, correction emitted); -1 otherwise
     argmax: np.ndarray            # [K+1] lowest-index argmax of each target row (all modes)
     min_dist: float               # smallest boundary distance among decisions taken
     zero_q_accepts: int = 0
     z0_fallback: int = 0
     valid: bool = True
     dists: list = field(default_factory=list)
+    draft_len: int = -1           # k_b used by the walk
 
 
 def verify_sequence(target, draft, tokens, u, T: float, mode: int,
-                    tau: float = 0.0) -> SequenceResult:
+                    tau: float = 0.0, eos: int = -1, draft_len: int | None = None,
+                    max_emit: int | None = None) -> SequenceResult:
     """Verify one sequence.
 
     target: [K+1, V] logits, draft: [K, V] logits (stochastic only),
     tokens: [K] drafted tokens, u: [K+1] uniforms (stochastic only).
+    eos, draft_len (k_b) and max_emit (m_b) are the optional stopping rules of
+    the module docstring; the defaults give the plain cycle.
     """
     target = np.asarray(target, dtype=np.float64)
     K = target.shape[0] - 1
     V = target.shape[1]
+    kb = K if draft_len is None else int(draft_len)
+    m = K + 1 if max_emit is None else int(max_emit)
     toks = np.asarray(tokens, dtype=np.int64).reshape(K)
     nan_k = np.full(K, np.nan)
     out = np.full(K + 1, -1, dtype=np.int64)
 
-    valid = bool(np.all((toks >= 0) & (toks < V)))
-    valid = valid and all(row_is_valid(target[i]) for i in range(K + 1))
+    valid = 0 <= kb <= K and m >= 1
+    valid = valid and bool(np.all((toks[:kb] >= 0) & (toks[:kb] < V)))
+    valid = valid and all(row_is_valid(target[i]) for i in range(kb + 1))
     if mode == MODE_STOCHASTIC:
         draft = np.asarray(draft, dtype=np.float64)
-        valid = valid and all(row_is_valid(draft[i]) for i in range(K))
+        valid = valid and all(row_is_valid(draft[i]) for i in range(kb))
     argmax = np.array([argmax_lowest(target[i]) if row_is_valid(target[i]) else -1
                        for i in range(K + 1)], dtype=np.int64)
     if not valid:
         return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
                               math.inf, valid=False)
 
-    dists = []
+    acc_dists = []       # (position, distance of that position's decision)
     zero_q = 0
-    z0 = 0
-    z = -1.0
     p_d = nan_k.copy()
     q_d = nan_k.copy()
 
+    # 1. the ordered walk over positions 0..kb-1: j = first rejection, else kb
     if mode == MODE_STOCHASTIC:
         u = np.asarray(u, dtype=np.float64).reshape(K + 1)
-        p_rows = [softmax_t(target[i], T) for i in range(K + 1)]
-        q_rows = [softmax_t(draft[i], T) for i in range(K)]
-        for i in range(K):
+        p_rows = [softmax_t(target[i], T) for i in range(kb + 1)]
+        q_rows = [softmax_t(draft[i], T) for i in range(kb)]
+        for i in range(kb):
             p_d[i] = p_rows[i][toks[i]]
             q_d[i] = q_rows[i][toks[i]]
-        j = K
-        for i in range(K):
+        j = kb
+        for i in range(kb):
             P, Q = p_d[i], q_d[i]
             if P >= Q:
                 keep = True
                 if Q == 0.0:
                     zero_q += 1
                 if Q > 0.0:
-                    dists.append(abs(u[i] - P / Q))
+                    acc_dists.append((i, abs(u[i] - P / Q)))
             else:
                 ratio = P / Q
                 keep = bool(u[i] < ratio)
-                dists.append(abs(u[i] - ratio))
+                acc_dists.append((i, abs(u[i] - ratio)))
             if not keep:
                 j = i
                 break
-        if j < K:
-            r, Z = positive_residual(p_rows[j], q_rows[j])
-            z = Z
-            if Z > 0.0:
-                c, dist = inverse_cdf(r, u[K])
-            else:
-                z0 += 1
-                c, dist = inverse_cdf(p_rows[j], u[K])
-        else:
-            c, dist = inverse_cdf(p_rows[K], u[K])
-        dists.append(dist)
     elif mode == MODE_GREEDY:
-        j = K
-        for i in range(K):
+        j = kb
+        for i in range(kb):
             if toks[i] != argmax[i]:
                 j = i
                 break
-        c = int(argmax[j])
     elif mode == MODE_MARGIN:
-        for i in range(K):
+        for i in range(kb):
             p = softmax_t(target[i], T)
             p_d[i] = p[toks[i]] / p[argmax[i]]
-        j = K
-        for i in range(K):
+        j = kb
+        for i in range(kb):
             if toks[i] == argmax[i]:
                 continue
-            dists.append(abs(p_d[i] - tau))
+            acc_dists.append((i, abs(p_d[i] - tau)))
             if not (p_d[i] > tau):
                 j = i
                 break
-        c = int(argmax[j])
     else:
         raise ValueError(f"unknown mode {mode}")
 
-    out[:j] = toks[:j]
-    out[j] = c
-    return SequenceResult(out, j, p_d, q_d, z, argmax,
+    # 2. stopping rules: emission d_0..d_{j-1}, c, cut after the first eos
+    #    among the kept drafts and to m tokens
+    L = j + 1
+    for i in range(j):
+        if toks[i] == eos:
+            L = i + 1
+            break
+    L = min(L, m)
+    n_drafts = min(j, L)
+    emit_c = L > j
+
+    # 3. the correction (j < kb) or bonus (j = kb), only when it is emitted
+    z = -1.0
+    z0 = 0
+    c = -1
+    draw_dist = None
+    if emit_c:
+        if mode == MODE_STOCHASTIC:
+            if j < kb:
+                r, Z = positive_residual(p_rows[j], q_rows[j])
+                z = Z
+                if Z > 0.0:
+                    c, draw_dist = inverse_cdf(r, u[K])
+                else:
+                    z0 += 1
+                    c, draw_dist = inverse_cdf(p_rows[j], u[K])
+            else:
+                c, draw_dist = inverse_cdf(p_rows[kb], u[K])
+        else:
+            c = int(argmax[j])
+
+    # decisions at positions the emission reaches are the ones that matter
+    dists = [d for (i, d) in acc_dists if i < L]
+    if draw_dist is not None:
+        dists.append(draw_dist)
+
+    out[:n_drafts] = toks[:n_drafts]
+    if emit_c:
+        out[j] = c
+    return SequenceResult(out, n_drafts, p_d, q_d, z, argmax,
                           min(dists) if dists else math.inf,
                           zero_q_accepts=zero_q, z0_fallback=z0, valid=True,
-                          dists=dists)
+                          dists=dists, draft_len=kb)
 
 
 # --------------------------------------------------------------------------
@@ -317,13 +361,14 @@ class BatchResult:
 
 def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
                  tau: float = 0.0, ema: EmaState | None = None,
-                 rows=None) -> BatchResult:
+                 rows=None, eos: int = -1, draft_len=None, max_emit=None) -> BatchResult:
     """Verify every sequence b (or only those listed in `rows`).
 
     target [B, K+1, V], draft [B, K, V] (stochastic), tokens [B, K],
     uniforms [B, K+1]. Arrays may be any float dtype; they are widened to
     float64 one sequence at a time. When `ema` is given, slot b is updated
-    for every valid verified sequence b.
+    for every valid verified sequence b with k_b > 0. eos, draft_len [B] and
+    max_emit [B] (indexed by b) are the optional stopping rules.
     """
     B = target.shape[0]
     K = target.shape[1] - 1
@@ -343,7 +388,9 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
             draft[b] if (draft is not None and mode == MODE_STOCHASTIC) else None,
             tokens[b],
             uniforms[b] if (uniforms is not None and mode == MODE_STOCHASTIC) else None,
-            T, mode, tau)
+            T, mode, tau, eos=eos,
+            draft_len=None if draft_len is None else int(draft_len[b]),
+            max_emit=None if max_emit is None else int(max_emit[b]))
         out.tokens[k] = res.tokens
         out.accept_len[k] = res.accept_len
         out.p_d[k] = res.p_d
@@ -355,8 +402,8 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
         out.z0_fallbacks += res.z0_fallback
         if res.valid:
             out.hist[res.accept_len] += 1
-            if ema is not None and K > 0:
-                ema.observe(b, res.accept_len / K)
+            if ema is not None and res.draft_len > 0:
+                ema.observe(b, res.accept_len / res.draft_len)
         else:
             out.invalid += 1
     return out
