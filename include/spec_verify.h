@@ -115,7 +115,8 @@ int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
  *   out_accept_hist [K+1]       uint32: zeroed, then hist[j] counts this call's valid sequences
  *   stream          HIP stream the work is ordered on
  *
- * EMA slot b is updated with x = accept_len/K for every valid sequence b.
+ * EMA slot b is updated with x = accept_len/K for every valid sequence b
+ * (accept_len/k_b under the stopping rules of spec_verify_set_stops).
  * Returns SV_OK once the work is enqueued, or an error code with nothing
  * enqueued (SV_EINVAL for a NULL handle or required pointer, B out of range,
  * an unknown mode, T not finite or T <= 0 in stochastic/margin mode, tau not
@@ -143,6 +144,32 @@ int spec_verify_destroy(spec_verify_handle *h);
  */
 int spec_verify_set_aux(spec_verify_handle *h, double *p_d, double *q_d,
                         double *z, int32_t *argmax);
+
+/*
+ * Stopping rules for later spec_verify calls on this handle ([DVC] "Verify
+ * several proposed tokens in one target pass" and "Speculation needs cache
+ * rollback": end-of-sequence and length limits can end a cycle before its
+ * draft block is used up, and the returned tokens must agree with them).
+ *
+ *   eos_token  end-of-sequence token id, or -1 for none (< -1: SV_EINVAL)
+ *   draft_len  [max_batch] int32 device array, k_b in [0, K]: drafts tested
+ *              for sequence b; NULL = K for every sequence
+ *   max_emit   [max_batch] int32 device array, m_b >= 1: tokens sequence b
+ *              may emit in this cycle; NULL = no limit
+ *
+ * Per sequence the walk tests positions 0..k_b-1 (j = first rejection, else
+ * k_b; the bonus comes from target row k_b); the emission d_0..d_{j-1}, c is
+ * cut after its first end-of-sequence token and to its first m_b tokens;
+ * out_accept_len and the histogram count the drafts emitted; the correction
+ * or bonus is drawn (with uniforms[b][K]) only when it is emitted, and z is
+ * then -1. Only target rows 0..k_b and draft rows 0..k_b-1 are needed. A k_b
+ * outside [0, K] or an m_b < 1 makes the sequence invalid. The arrays are
+ * read by the device during later calls and stay owned by the caller; they
+ * must outlive those calls. spec_verify_set_stops(h, -1, NULL, NULL) restores
+ * the plain cycle.
+ */
+int spec_verify_set_stops(spec_verify_handle *h, int eos_token, const int32_t *draft_len,
+                          const int32_t *max_emit);
 
 /* EMA state accessors, ordered on `stream`. Device pointers of max_batch entries. */
 int spec_verify_get_ema(spec_verify_handle *h, double *ema_dev, int32_t *steps_dev,

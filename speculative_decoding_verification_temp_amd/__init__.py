@@ -23,6 +23,7 @@ _ERRNAMES = {-1: "SV_EINVAL", -2: "SV_EUNSUPPORTED", -3: "SV_ENOMEM", -4: "SV_EH
 
 EXPORTED = (
     "spec_verify_init", "spec_verify", "spec_verify_destroy", "spec_verify_set_aux",
+    "spec_verify_set_stops",
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
     "spec_verify_last_error", "spec_verify_version",
@@ -59,6 +60,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify.argtypes = [vp, i32, vp, vp, vp, vp, f32, i32, f32, vp, vp, vp, vp]
     L.spec_verify_destroy.argtypes = [vp]
     L.spec_verify_set_aux.argtypes = [vp, vp, vp, vp, vp]
+    L.spec_verify_set_stops.argtypes = [vp, i32, vp, vp]
     L.spec_verify_get_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_set_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_reset_ema.argtypes = [vp, vp]
@@ -106,6 +108,7 @@ class SpecVerifier:
             raise SpecVerifyError(rc, "spec_verify_init failed")
         self._h = h
         self._aux = None
+        self._stops = (None, None)
 
     # -- lifetime --
     def close(self):
@@ -147,6 +150,24 @@ class SpecVerifier:
     @property
     def aux(self):
         return self._aux
+
+    # -- stopping rules --
+    def set_stops(self, eos: int = -1, draft_len=None, max_emit=None):
+        """End-of-sequence token, per-sequence draft counts [max_batch] and
+        emission budgets [max_batch] (int32 device tensors, or None) for later
+        calls. The tensors are kept referenced here while they are in use."""
+        for t in (draft_len, max_emit):
+            if t is not None and (t.dtype != torch.int32 or t.device != self.device
+                                  or t.numel() < self.max_batch or not t.is_contiguous()):
+                raise ValueError("stop arrays must be contiguous int32 device tensors "
+                                 "of at least max_batch entries")
+        self._check(self.lib.spec_verify_set_stops(
+            self._h, int(eos), None if draft_len is None else _ptr(draft_len),
+            None if max_emit is None else _ptr(max_emit)), "set_stops")
+        self._stops = (draft_len, max_emit)
+
+    def clear_stops(self):
+        self.set_stops(-1, None, None)
 
     # -- verification --
     def _check_logits(self, t, rows, name):

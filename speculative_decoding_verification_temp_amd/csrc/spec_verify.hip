@@ -59,6 +59,7 @@ struct spec_verify_handle {
   int32_t* aux_argmax = nullptr;
   hipEvent_t* prof_ev = nullptr;   // 3 events per recorded call
   bool prof_call_end = false;      // also record the end of each call
+  sv::Stops stops{nullptr, nullptr, -1};   // stopping rules for later calls
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
@@ -148,14 +149,14 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   if (h->finish_seq && L.ntiles <= sv::kFMaxTiles && rows <= sv::kFMaxRows) {
     hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
-                       h->parts, target, draft, tokens, uniforms, c, c64, n_half, out_tokens,
-                       out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q,
-                       h->aux_z);
+                       h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->stops,
+                       out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p,
+                       h->aux_q, h->aux_z);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
-                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, out_tokens, out_len,
-                     hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
+                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, h->stops, out_tokens,
+                     out_len, hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
                      h->aux_z, tab ? h->table : nullptr, n_half, c64);
   if ((rc = check_launch(h, "scan_stochastic"))) return rc;
   hipLaunchKernelGGL((sv::draw<DT, VEC>), dim3(B * groups), dim3(sv::kBlock), 0, s, 0, B, K, V,
@@ -179,7 +180,7 @@ int run_fused(spec_verify_handle* h, int B, const void* target, const void* draf
   int rc = check_launch(h, "zero_hist");
   if (rc) return rc;
   hipLaunchKernelGGL((sv::verify_fused<DT, VEC, U>), dim3(B), dim3(sv::kFBlock), 0, s, K, V,
-                     target, draft, tokens, uniforms, c, c64, tab_half(c64), out_tokens,
+                     target, draft, tokens, uniforms, c, c64, tab_half(c64), h->stops, out_tokens,
                      out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q,
                      h->aux_z);
   rc = check_launch(h, "verify_fused");
@@ -210,12 +211,14 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
   const int grid2 = div_up(B, sv::kWavesPerBlock);
   if (margin)
     hipLaunchKernelGGL((sv::scan_argmax<DT, true>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
-                       L.nseg, h->parts, target, tokens, invT, tau, out_tokens, out_len, hist,
+                       L.nseg, h->parts, target, tokens, invT, tau, h->stops, out_tokens, out_len,
+                       hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);
   else
     hipLaunchKernelGGL((sv::scan_argmax<DT, false>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K,
-                       V, L.nseg, h->parts, target, tokens, invT, tau, out_tokens, out_len, hist,
+                       V, L.nseg, h->parts, target, tokens, invT, tau, h->stops, out_tokens, out_len,
+                       hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);
   return check_launch(h, "scan_argmax");
@@ -304,6 +307,15 @@ int spec_verify_set_aux(spec_verify_handle* h, double* p_d, double* q_d, double*
   h->aux_q = q_d;
   h->aux_z = z;
   h->aux_argmax = argmax;
+  return SV_OK;
+}
+
+int spec_verify_set_stops(spec_verify_handle* h, int eos_token, const int32_t* draft_len,
+                          const int32_t* max_emit) {
+  if (h == nullptr || eos_token < -1) return SV_EINVAL;
+  h->stops.eos = eos_token;
+  h->stops.k = draft_len;
+  h->stops.m = max_emit;
   return SV_OK;
 }
 

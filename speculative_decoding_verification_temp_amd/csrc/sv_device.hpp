@@ -200,8 +200,8 @@ struct RowPart {
 struct DrawRow {
   double rho;    // S_t / S_d from the streaming pass: sign test of p - q
   float R_t, R_d;
-  int j;         // rejection index (K = bonus), -1 = nothing to draw
-  int pad;
+  int j;         // rejection index (kb = bonus), -1 = nothing to draw
+  int kb;        // drafts tested in this sequence
 };
 
 // Per-tile sums left by the draw's first phase, all relative to the row

@@ -491,7 +491,7 @@ template <int DT, int VEC, int NT>
 __device__ __forceinline__ void finish_sequence(
     int b, int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
-    int n_half, const double* T, const float* fR, const double* fS, TileSums* tiles,
+    Stops sp, int n_half, const double* T, const float* fR, const double* fS, TileSums* tiles,
     DrawRow& s_dr, PickShared& psh, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
@@ -503,10 +503,12 @@ __device__ __forceinline__ void finish_sequence(
   auto row_base = [&](int r) -> const void* { return row_ptr<DT>(target, draft, b, r, K, V); };
   // ---- 2. acceptance scan on wavefront 0 ----
   if (wid == 0) {
+    int kb, m;
+    bool lane_bad;
+    stops_of(sp, b, K, kb, m, lane_bad);
     float Rt = 0.0f, Rd = 0.0f;
     double St = 1.0, Sd = 1.0;
-    bool lane_bad = false;
-    if (lane <= K) {
+    if (lane <= kb) {
       Rt = fR[lane];
       St = fS[lane];
       lane_bad |= !finite_pos(St);
@@ -514,7 +516,7 @@ __device__ __forceinline__ void finish_sequence(
     int d = 0;
     double P = 0.0, Q = 1.0;
     bool keep = true, zq = false;
-    if (lane < K) {
+    if (lane < kb) {
       Rd = fR[K + 1 + lane];
       Sd = fS[K + 1 + lane];
       lane_bad |= !finite_pos(Sd);
@@ -531,10 +533,12 @@ __device__ __forceinline__ void finish_sequence(
       }
     }
     const bool bad = __any(lane_bad);
-    const unsigned long long rej = __ballot(lane < K && !keep);
-    const int j = rej ? __ffsll((long long)rej) - 1 : K;
-    if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = bad ? __builtin_nan("") : P;
-    if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = bad ? __builtin_nan("") : Q;
+    const Walk w = walk_outcome(lane, kb, m, sp.eos, keep, d);
+    const int j = w.j;
+    if (aux_p != nullptr && lane < K)
+      aux_p[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : P;
+    if (aux_q != nullptr && lane < K)
+      aux_q[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : Q;
     const float Rtj = __shfl(Rt, j, kWave), Rdj = __shfl(Rd, j, kWave);
     const double Stj = __shfl(St, j, kWave), Sdj = __shfl(Sd, j, kWave);
     if (lane == 0) {
@@ -542,16 +546,16 @@ __device__ __forceinline__ void finish_sequence(
       dr.rho = Stj / Sdj;
       dr.R_t = Rtj;
       dr.R_d = Rdj;
-      dr.j = bad ? -1 : j;
-      dr.pad = 0;
+      dr.j = (bad || w.cpos < 0) ? -1 : j;     // -1: invalid, or no correction emitted
+      dr.kb = kb;
       s_dr = dr;
-      if (bad && aux_z != nullptr) aux_z[b] = -1.0;
+      if (dr.j < 0 && aux_z != nullptr) aux_z[b] = -1.0;
     }
     const unsigned long long zqm = __ballot(zq && lane < j);
     if (lane == 0 && !bad && zqm)
       atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
-    emit_and_update(lane, b, K, j, bad, tokens, out_tokens, out_len, hist, ema, steps, decay, st,
-                    -1, d);
+    emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
+                    decay, st, d);
   }
   __syncthreads();
   const DrawRow dr = s_dr;
@@ -620,7 +624,7 @@ template <int DT, int VEC, int U>
 __global__ __launch_bounds__(kFBlock) void verify_fused(
     int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
-    int n_half, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+    int n_half, Stops sp, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
   using C = Chunk<DT, VEC>;
@@ -642,10 +646,14 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
   const int kmax = int((nchunks + kFBlock - 1) / kFBlock);   // chunk slots per thread per row
   const int total = rows * kmax;
 
-  // drafted tokens outside [0, V) make the sequence invalid: skip the rows
+  // drafted tokens outside [0, V) at tested positions make the sequence
+  // invalid: skip the rows (bad stopping rules are flagged by the scan)
   if (wid == 0) {
-    const int d = lane < K ? tokens[(long long)b * K + lane] : 0;
-    const bool bad = __any(lane < K && !(d >= 0 && d < V));
+    int kb, m;
+    bool sbad;
+    stops_of(sp, b, K, kb, m, sbad);
+    const int d = lane < kb ? tokens[(long long)b * K + lane] : 0;
+    const bool bad = __any(lane < kb && !(d >= 0 && d < V));
     if (lane == 0) s_bad_token = bad ? 1 : 0;
   }
   __syncthreads();
@@ -654,8 +662,8 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
       if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = __builtin_nan("");
       if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = __builtin_nan("");
       if (aux_z != nullptr && lane == 0) aux_z[b] = -1.0;
-      emit_and_update(lane, b, K, 0, true, tokens, out_tokens, out_len, hist, ema, steps, decay,
-                      st, -1, 0);
+      emit_and_update(lane, b, K, 0, 0, -1, -1, true, out_tokens, out_len, hist, ema, steps,
+                      decay, st, 0);
     }
     return;
   }
@@ -754,7 +762,7 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
   }
   __syncthreads();
 
-  finish_sequence<DT, VEC, kFBlock>(b, K, V, target, draft, tokens, uniforms, c, c64, n_half, T,
+  finish_sequence<DT, VEC, kFBlock>(b, K, V, target, draft, tokens, uniforms, c, c64, sp, n_half, T,
                                     fR, fS, tiles, s_dr, psh, out_tokens, out_len, hist, ema,
                                     steps,
                                     decay, st, aux_p, aux_q, aux_z);
@@ -766,7 +774,7 @@ template <int DT, int VEC, int NT>
 __global__ __launch_bounds__(NT) void finish_seq(
     int K, int V, int nseg, const RowPart* __restrict__ parts, const void* __restrict__ target,
     const void* __restrict__ draft, const int32_t* __restrict__ tokens,
-    const float* __restrict__ uniforms, float c, double c64, int n_half,
+    const float* __restrict__ uniforms, float c, double c64, int n_half, Stops sp,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len, uint32_t* __restrict__ hist,
     double* __restrict__ ema, int32_t* __restrict__ steps, double decay,
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
@@ -790,7 +798,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
     fS[r] = S;
   }
   __syncthreads();
-  finish_sequence<DT, VEC, NT>(b, K, V, target, draft, tokens, uniforms, c, c64, n_half, T,
+  finish_sequence<DT, VEC, NT>(b, K, V, target, draft, tokens, uniforms, c, c64, sp, n_half, T,
                                     fR, fS, tiles, s_dr, psh, out_tokens, out_len, hist, ema,
                                     steps,
                                     decay, st, aux_p, aux_q, aux_z);

@@ -40,36 +40,77 @@ __device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, i
 
 __device__ inline bool finite_pos(double S) { return S > 0.0 && S < __builtin_inf(); }
 
-__device__ inline void emit_and_update(int lane, int b, int K, int j, bool bad,
-                                       const int32_t* __restrict__ tokens,
-                                       int32_t* __restrict__ out_tokens,
+// Stopping rules of one call: an end-of-sequence token (-1 = none) and,
+// per sequence, a draft count k_b in [0, K] and an emission budget m_b >= 1
+// (null arrays: k_b = K, m_b = K + 1). See [DVC] "Verify several proposed
+// tokens in one target pass" and "Speculation needs cache rollback".
+struct Stops {
+  const int32_t* k;
+  const int32_t* m;
+  int eos;
+};
+
+__device__ inline void stops_of(const Stops& sp, int b, int K, int& kb, int& m, bool& bad) {
+  kb = sp.k != nullptr ? sp.k[b] : K;
+  m = sp.m != nullptr ? sp.m[b] : K + 1;
+  bad = !(kb >= 0 && kb <= K && m >= 1);
+  if (bad) kb = 0;
+}
+
+// The walk's outcome under the stopping rules, on one wavefront (lane i holds
+// position i): j = first rejection among positions < kb (else kb); the
+// emission d_0..d_{j-1}, c is cut after its first end-of-sequence draft and
+// to m tokens. n = drafts emitted; cpos = j when the correction or bonus is
+// emitted, else -1.
+struct Walk {
+  int j, n, cpos;
+};
+__device__ inline Walk walk_outcome(int lane, int kb, int m, int eos, bool keep, int d) {
+  Walk w;
+  const unsigned long long rej = __ballot(lane < kb && !keep);
+  w.j = rej ? __ffsll((long long)rej) - 1 : kb;
+  const unsigned long long em = __ballot(lane < w.j && d == eos);
+  int L = em ? __ffsll((long long)em) : w.j + 1;     // cut after the first eos
+  L = min(L, m);
+  w.n = min(w.j, L);
+  w.cpos = L > w.j ? w.j : -1;
+  return w;
+}
+
+// Emit (tokens, accept length), histogram and EMA for one sequence: positions
+// < n hold the drafts, position cpos the value cval (or -1, to be filled by
+// the draw), the rest -1. The EMA observes n / kb (skipped when kb = 0).
+__device__ inline void emit_and_update(int lane, int b, int K, int kb, int n, int cpos, int cval,
+                                       bool bad, int32_t* __restrict__ out_tokens,
                                        int32_t* __restrict__ out_len,
                                        uint32_t* __restrict__ hist, double* __restrict__ ema,
                                        int32_t* __restrict__ steps, double decay,
-                                       DevStats* __restrict__ st, int fill_at_j, int d) {
+                                       DevStats* __restrict__ st, int d) {
   if (lane <= K) {
     int v;
     if (bad)
       v = -1;
-    else if (lane < j)
+    else if (lane < n)
       v = d;
-    else if (lane == j)
-      v = fill_at_j;
+    else if (lane == cpos)
+      v = cval;
     else
       v = -1;
     out_tokens[(long long)b * (K + 1) + lane] = v;
   }
   if (lane == 0) {
-    out_len[b] = bad ? -1 : j;
+    out_len[b] = bad ? -1 : n;
     if (bad) {
       atomicAdd(&st->invalid, 1ull);
     } else {
-      atomicAdd(&hist[j], 1u);
+      atomicAdd(&hist[n], 1u);
       atomicAdd(&st->sequences, 1ull);
-      const double x = double(j) / double(K);
-      const int n = steps[b];
-      ema[b] = (n == 0) ? x : decay * ema[b] + (1.0 - decay) * x;
-      steps[b] = n + 1;
+      if (kb > 0) {
+        const double x = double(n) / double(kb);
+        const int c = steps[b];
+        ema[b] = (c == 0) ? x : decay * ema[b] + (1.0 - decay) * x;
+        steps[b] = c + 1;
+      }
     }
   }
 }
@@ -136,7 +177,7 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void scan_stochastic(
     int b0, int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
     const void* __restrict__ target, const void* __restrict__ draft,
-    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, Stops sp,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, DrawRow* __restrict__ draw, double* aux_p,
@@ -151,17 +192,19 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
   const int rows = 2 * K + 1;
   const RowPart* pb = parts + (long long)b * rows * nseg;
 
+  int kb, m;
+  bool lane_bad;
+  stops_of(sp, b, K, kb, m, lane_bad);
   float Rt = 0.0f, Rd = 0.0f;
   double St = 1.0, Sd = 1.0;
-  bool lane_bad = false;
-  if (lane <= K) {
+  if (lane <= kb) {
     combine_sum_parts(pb + (long long)lane * nseg, nseg, Rt, St);
     lane_bad |= !finite_pos(St);
   }
   int d = 0;
   double P = 0.0, Q = 1.0;
   bool keep = true, zq = false;
-  if (lane < K) {
+  if (lane < kb) {
     combine_sum_parts(pb + (long long)(K + 1 + lane) * nseg, nseg, Rd, Sd);
     lane_bad |= !finite_pos(Sd);
     d = tokens[(long long)b * K + lane];
@@ -178,13 +221,15 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
     }
   }
   const bool bad = __any(lane_bad);
-  const unsigned long long rej = __ballot(lane < K && !keep);
-  const int j = rej ? __ffsll((long long)rej) - 1 : K;
+  const Walk w = walk_outcome(lane, kb, m, sp.eos, keep, d);
 
-  if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = bad ? __builtin_nan("") : P;
-  if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = bad ? __builtin_nan("") : Q;
+  if (aux_p != nullptr && lane < K)
+    aux_p[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : P;
+  if (aux_q != nullptr && lane < K)
+    aux_q[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : Q;
 
-  // statistics of row j for the draw
+  // statistics of row j for the draw (j = kb: the bonus from target row kb)
+  const int j = w.j;
   const float Rtj = __shfl(Rt, j, kWave), Rdj = __shfl(Rd, j, kWave);
   const double Stj = __shfl(St, j, kWave), Sdj = __shfl(Sd, j, kWave);
   if (lane == 0) {
@@ -192,15 +237,15 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
     dr.rho = Stj / Sdj;
     dr.R_t = Rtj;
     dr.R_d = Rdj;
-    dr.j = bad ? -1 : j;
-    dr.pad = 0;
+    dr.j = (bad || w.cpos < 0) ? -1 : j;
+    dr.kb = kb;
     draw[b] = dr;
-    if (bad && aux_z != nullptr) aux_z[b] = -1.0;
+    if (dr.j < 0 && aux_z != nullptr) aux_z[b] = -1.0;
   }
-  const unsigned long long zqm = __ballot(zq && lane < j);
+  const unsigned long long zqm = __ballot(zq && lane < w.j);
   if (lane == 0 && !bad && zqm) atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
-  emit_and_update(lane, b, K, j, bad, tokens, out_tokens, out_len, hist, ema, steps, decay, st,
-                  -1, d);
+  emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
+                  decay, st, d);
 }
 
 // --------------------------------------------------------------------------
@@ -210,7 +255,7 @@ template <int DT, bool MARGIN>
 __global__ __launch_bounds__(kBlock) void scan_argmax(
     int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
     const void* __restrict__ target, const int32_t* __restrict__ tokens, double invT,
-    double tau, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+    double tau, Stops sp, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
     int32_t* aux_argmax) {
@@ -219,17 +264,18 @@ __global__ __launch_bounds__(kBlock) void scan_argmax(
   if (b >= B) return;
   const RowPart* pb = parts + (long long)b * (K + 1) * nseg;
 
+  int kb, mm;
+  bool lane_bad;
+  stops_of(sp, b, K, kb, mm, lane_bad);
   float m = 0.0f;
   int A = -1, nan = 0;
-  bool lane_bad = false;
-  if (lane <= K) {
-    combine_max_parts(pb + (long long)lane * nseg, nseg, m, A, nan);
+  if (lane <= K) combine_max_parts(pb + (long long)lane * nseg, nseg, m, A, nan);
+  if (lane <= kb)
     lane_bad |= nan != 0 || !(m > -__builtin_inff() && m < __builtin_inff()) || A < 0;
-  }
   int d = 0;
   bool keep = true;
   double ratio = __builtin_nan("");
-  if (lane < K) {
+  if (lane < kb) {
     d = tokens[(long long)b * K + lane];
     lane_bad |= !(d >= 0 && d < V);
     if (!lane_bad) {
@@ -243,16 +289,17 @@ __global__ __launch_bounds__(kBlock) void scan_argmax(
     }
   }
   const bool bad = __any(lane_bad);
-  const unsigned long long rej = __ballot(lane < K && !keep);
-  const int j = rej ? __ffsll((long long)rej) - 1 : K;
-  const int Aj = __shfl(A, j, kWave);
+  const Walk w = walk_outcome(lane, kb, mm, sp.eos, keep, d);
+  const int Aj = __shfl(A, w.j, kWave);
 
-  if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = bad ? __builtin_nan("") : ratio;
+  if (aux_p != nullptr && lane < K)
+    aux_p[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : ratio;
   if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = __builtin_nan("");
   if (aux_z != nullptr && lane == 0) aux_z[b] = -1.0;
-  if (aux_argmax != nullptr && lane <= K) aux_argmax[(long long)b * (K + 1) + lane] = A;
-  emit_and_update(lane, b, K, j, bad, tokens, out_tokens, out_len, hist, ema, steps, decay, st,
-                  Aj, d);
+  if (aux_argmax != nullptr && lane <= K)
+    aux_argmax[(long long)b * (K + 1) + lane] = A;
+  emit_and_update(lane, b, K, kb, w.n, w.cpos, Aj, bad, out_tokens, out_len, hist, ema, steps,
+                  decay, st, d);
 }
 
 // --------------------------------------------------------------------------
@@ -281,7 +328,7 @@ template <int DT, int VEC> struct DrawRows {
   __device__ inline void init(const void* target, const void* draft, const DrawRow& dr, int b,
                               int K, int V, double c_) {
     c = c_;
-    residual = dr.j < K;
+    residual = dr.j < dr.kb;
     trow = row_ptr<DT>(target, draft, b, dr.j, K, V);
     drow = residual ? row_ptr<DT>(target, draft, b, K + 1 + dr.j, K, V) : nullptr;
     Rt = dr.R_t;

@@ -31,9 +31,12 @@ def _merge(parts):
     return out
 
 
-def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int = 256):
+def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int = 256,
+               stops=None):
     """Run the oracle on the listed sequences of a generated input dict
-    (host copies are made a chunk of sequences at a time)."""
+    (host copies are made a chunk of sequences at a time). stops: optional
+    (eos, draft_len [B] or None, max_emit [B] or None) with host arrays indexed
+    by batch row."""
     rows = np.asarray(rows, dtype=np.int64)
     m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
     parts = []
@@ -44,16 +47,21 @@ def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int 
         drf = to_host_f64(x["draft"].index_select(0, idx)) if mode == "stochastic" else None
         tok = x["tokens"].index_select(0, idx).cpu().numpy()
         uni = x["uniforms"].index_select(0, idx).cpu().double().numpy()
+        kw = {}
+        if stops is not None:
+            eos, kb, mx = stops
+            kw = dict(eos=eos, draft_len=None if kb is None else np.asarray(kb)[sub_rows],
+                      max_emit=None if mx is None else np.asarray(mx)[sub_rows])
         if ema is not None:
             # EMA slots are batch rows: feed the oracle a state indexed by row
             sub = O.EmaState(len(sub_rows), ema.decay)
             sub.ema[:] = ema.ema[sub_rows]
             sub.steps[:] = ema.steps[sub_rows]
-            parts.append(O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau, ema=sub))
+            parts.append(O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau, ema=sub, **kw))
             ema.ema[sub_rows] = sub.ema
             ema.steps[sub_rows] = sub.steps
         else:
-            parts.append(O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau))
+            parts.append(O.verify_batch(tgt, drf, tok, uni, x["T"], m, tau, **kw))
     return _merge(parts)
 
 

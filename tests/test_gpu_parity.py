@@ -103,13 +103,17 @@ def test_c2_forced_segments_agree(sv, monkeypatch):
 
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_fused_and_pipeline_paths_agree(sv, monkeypatch, name):
-    """The one-workgroup-per-sequence kernel (forced on for a small batch) and
-    the multi-kernel pipeline both match the oracle and each other."""
+    """The three stochastic paths match the oracle and each other: the
+    streaming pass then one workgroup per sequence (default), the streaming
+    pass then separate scan, tile-sum and pick kernels (the path for V >
+    524288), and one workgroup per sequence for everything (forced on)."""
     cfg = CONFIGS[name]
     x = make_inputs(cfg, 5, DEV)
     outs = {}
-    for path, min_b in (("pipeline", "0"), ("fused", "1")):
+    for path, min_b, fin in (("pipeline", "0", "1"), ("multikernel", "0", "0"),
+                             ("fused", "1", "1")):
         monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", min_b)
+        monkeypatch.setenv("SPEC_VERIFY_FINISH_SEQ", fin)
         v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
         outs[path] = (tok.clone(), alen.clone(), hist.clone(),
                       {k: t.clone() for k, t in aux.items()})
@@ -120,16 +124,20 @@ def test_fused_and_pipeline_paths_agree(sv, monkeypatch, name):
         rep = compare(rows, ref, tok, alen, "stochastic", aux, f"{name}/{path}")
         check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
         _log(f"{name}/{path}: {rep}")
-    a, b = outs["pipeline"], outs["fused"]
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    assert torch.allclose(a[3]["p_d"], b[3]["p_d"], rtol=1e-6, atol=0)
-    assert torch.allclose(a[3]["z"], b[3]["z"], rtol=1e-9, atol=1e-15)
+    a = outs["pipeline"]
+    for other in ("multikernel", "fused"):
+        b = outs[other]
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+        assert torch.allclose(a[3]["p_d"], b[3]["p_d"], rtol=1e-6, atol=0)
+        assert torch.allclose(a[3]["z"], b[3]["z"], rtol=1e-9, atol=1e-15)
 
 
 def test_c3_pipeline_path_sampled(sv, monkeypatch):
-    """The multi-kernel pipeline at the full c3 shape (the fused kernel is
-    the default there)."""
+    """The multi-kernel path (separate scan, tile-sum and pick kernels) at the
+    full c3 shape; the default there is one workgroup per sequence after the
+    streaming pass."""
     monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "0")
+    monkeypatch.setenv("SPEC_VERIFY_FINISH_SEQ", "0")
     cfg = CONFIGS["c3"]
     x = make_inputs(cfg, 1, DEV, "stochastic")
     v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
