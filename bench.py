@@ -64,7 +64,7 @@ def traffic_for(workload: str, kernel: str):
     return fetch + write
 
 
-def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float):
+def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None):
     """Time the fp64 CPU oracle on a bounded sample of the same workload, one
     sequence at a time on one core, cycling over the input sets until about
     `seconds` of oracle time, and compare its outputs with the GPU's for those
@@ -84,7 +84,8 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float):
         tok = x["tokens"][b:b + 1].cpu().numpy()
         uni = x["uniforms"][b:b + 1].cpu().double().numpy()
         t0 = time.perf_counter()
-        r = O.verify_batch(tgt, drf, tok, uni, cfg.T, m, cfg.tau)
+        r = O.verify_batch(tgt, drf, tok, uni, cfg.T, m, cfg.tau,
+                           draft_len=None if kb is None else kb[b:b + 1])
         t_cpu += time.perf_counter() - t0
         if r.min_dist[0] >= 1e-6 and (r.accept_len[0] != len_g[b]
                                       or not np.array_equal(r.tokens[0], tok_g[b])):
@@ -107,6 +108,9 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--stops", default="none", choices=["none", "varlen"],
+                    help="varlen: per-sequence draft counts k_b drawn uniformly from 1..K "
+                         "(seeded), no end-of-sequence token, no budget")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -116,6 +120,7 @@ def main():
               "shard over GPUs with no exchange, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import speculative_decoding_verification_temp_amd as sv
     from workloads import CONFIGS, make_inputs
@@ -134,6 +139,11 @@ def main():
     torch.cuda.synchronize()
 
     v = sv.SpecVerifier(B, K, V, cfg.torch_dtype, ema_decay=cfg.ema_decay)
+    kb = np.full(B, K, dtype=np.int64)
+    if args.stops == "varlen":
+        kb = np.random.default_rng([20260923, cfg.index, 7]).integers(1, K + 1, B)
+        kb_dev = torch.as_tensor(kb.astype(np.int32), device=dev).contiguous()
+        v.set_stops(-1, kb_dev, None)
     out = (torch.empty((B, K + 1), dtype=torch.int32, device=dev),
            torch.empty((B,), dtype=torch.int32, device=dev),
            torch.empty((K + 1,), dtype=torch.int32, device=dev))
@@ -150,8 +160,9 @@ def main():
         torch.cuda.synchronize()
         a = out[1].cpu()
         valid = a >= 0
+        kbt = torch.as_tensor(kb)
         if mode == "stochastic":
-            rows = int(((a < K) & valid).sum()) * 2 + int((a == K).sum())
+            rows = int(((a < kbt) & valid).sum()) * 2 + int((a == kbt).sum())
         else:
             rows = 0
         draw_bytes.append(rows * V * s)
@@ -175,13 +186,13 @@ def main():
     ms_step = ms_total / args.steps
     pass_avg = pass_ms / max(1, ncalls)
 
-    rows_per_seq = 2 * K + 1 if mode == "stochastic" else K + 1
-    pass_bytes = B * rows_per_seq * V * s
+    rows_total = int((2 * kb + 1).sum()) if mode == "stochastic" else int((kb + 1).sum())
+    pass_bytes = rows_total * V * s
     io_bytes = B * (K * 4 + (K + 1) * 4 + (K + 1) * 4 + 4) + 2 * B * K * s
     call_bytes = pass_bytes + sum(draw_bytes) / len(draw_bytes) + io_bytes
     kernel = "rowstats_sum" if mode == "stochastic" else "rowstats_max"
     achieved = pass_bytes / (pass_avg * 1e-3) / 1e9
-    traffic = traffic_for(f"{cfg.name}/{mode}", kernel)
+    traffic = traffic_for(f"{cfg.name}/{mode}", kernel) if args.stops == "none" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "kernel": kernel,
@@ -196,7 +207,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name} {mode}: B={B} K={K} V={V} {cfg.dtype} logits, "
-                               f"T={cfg.T}" + (f", tau={cfg.tau}" if mode == "margin" else ""),
+                               f"T={cfg.T}" + (f", tau={cfg.tau}" if mode == "margin" else "")
+                               + (", per-sequence draft counts 1..K" if args.stops == "varlen"
+                                  else ""),
                    "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU"},
         "achieved_hbm_gbs": round(call_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_of_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -226,7 +239,8 @@ def main():
             step(i)
             torch.cuda.synchronize()
             gpu_outs.append((out[0].cpu().numpy(), out[1].cpu().numpy()))
-        res["cpu_baseline"] = cpu_baseline(sets, gpu_outs, cfg, mode, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(sets, gpu_outs, cfg, mode, args.cpu_seconds,
+                                           kb if args.stops == "varlen" else None)
     print(json.dumps(res), flush=True)
 
 

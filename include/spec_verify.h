@@ -138,7 +138,8 @@ int spec_verify_destroy(spec_verify_handle *h);
  *   p_d    [B][K] float64: stochastic p_i(d_i); margin p_i(d_i)/p_i(argmax_i); greedy NaN
  *   q_d    [B][K] float64: stochastic q_i(d_i); NaN otherwise
  *   z      [B]    float64: residual total Z at the rejection (stochastic, j < K), else -1
- *   argmax [B][K+1] int32: lowest-index argmax of each target row (greedy and margin)
+ *   argmax [B][K+1] int32: lowest-index argmax of each target row (greedy and margin;
+ *          -1 for rows past the draft count k_b of spec_verify_set_stops)
  * Values at positions after the first rejection are still filled. Invalid
  * sequences get NaN / -1.
  */

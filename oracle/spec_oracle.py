@@ -188,7 +188,7 @@ class SequenceResult:
     p_d: np.ndarray               # [K] p_i(d_i) (stochastic); margin ratio (margin); NaN (greedy)
     q_d: np.ndarray               # [K] q_i(d_i) (stochastic); NaN otherwise
     z: float                      # residual Z at j (stochastic, j < k_b, correction emitted); -1 otherwise
-    argmax: np.ndarray            # [K+1] lowest-index argmax of each target row (all modes)
+    argmax: np.ndarray            # [K+1] lowest-index argmax of target rows 0..k_b, else -1
     min_dist: float               # smallest boundary distance among decisions taken
     zero_q_accepts: int = 0
     z0_fallback: int = 0
@@ -222,7 +222,8 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     if mode == MODE_STOCHASTIC:
         draft = np.asarray(draft, dtype=np.float64)
         valid = valid and all(row_is_valid(draft[i]) for i in range(kb))
-    argmax = np.array([argmax_lowest(target[i]) if row_is_valid(target[i]) else -1
+    # per-row argmax side output: rows 0..k_b (rows past k_b are not read)
+    argmax = np.array([argmax_lowest(target[i]) if i <= kb and row_is_valid(target[i]) else -1
                        for i in range(K + 1)], dtype=np.int64)
     if not valid:
         return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,

@@ -99,7 +99,10 @@ Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
   int max_nseg = int(nchunks / min_seg);
   if (max_nseg < 1) max_nseg = 1;
   if (max_nseg > kMaxSeg) max_nseg = kMaxSeg;
-  int nseg = h->nseg_force > 0 ? h->nseg_force : div_up(h->target_wgs, (long long)B * rows);
+  // with per-sequence draft counts some (row, segment) workgroups exit at
+  // once; four times as many, shorter ones keep the other rows evenly spread
+  const long long target = (long long)h->target_wgs * (h->stops.k != nullptr ? 4 : 1);
+  int nseg = h->nseg_force > 0 ? h->nseg_force : div_up(target, (long long)B * rows);
   if (nseg > max_nseg) nseg = max_nseg;
   if (nseg < 1) nseg = 1;
   L.seg_chunks = div_up(nchunks, nseg);
@@ -142,7 +145,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   prof_mark(h, 0, s);
   hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
                      dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                     h->parts, hist);
+                     h->stops.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
@@ -204,7 +207,7 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
   const long long grid1 = (long long)B * rows * L.nseg;
   prof_mark(h, 0, s);
   hipLaunchKernelGGL((sv::rowstats_max<DT, VEC, U>), dim3(unsigned(grid1)), dim3(sv::kBlock), 0,
-                     s, target, K, V, L.nseg, L.seg_chunks, h->parts, hist);
+                     s, target, K, V, L.nseg, L.seg_chunks, h->stops.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_max");
   prof_mark(h, 1, s);
   if (rc) return rc;

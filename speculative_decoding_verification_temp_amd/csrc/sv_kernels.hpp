@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void scan_argmax(
   if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = __builtin_nan("");
   if (aux_z != nullptr && lane == 0) aux_z[b] = -1.0;
   if (aux_argmax != nullptr && lane <= K)
-    aux_argmax[(long long)b * (K + 1) + lane] = A;
+    aux_argmax[(long long)b * (K + 1) + lane] = lane <= kb ? A : -1;   // rows past k_b unread
   emit_and_update(lane, b, K, kb, w.n, w.cpos, Aj, bad, out_tokens, out_len, hist, ema, steps,
                   decay, st, d);
 }

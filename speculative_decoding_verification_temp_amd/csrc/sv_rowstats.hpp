@@ -37,7 +37,8 @@ __device__ inline const void* row_ptr(const void* target, const void* draft, int
 template <int DT, int VEC, int U>
 __global__ __launch_bounds__(kBlock) void rowstats_sum(
     const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
-    int nseg, int seg_chunks, float c, RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+    int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
@@ -46,6 +47,12 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
   const long long grow = wg / nseg;
   const int b = int(grow / rows), r = int(grow % rows);
   if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  // with per-sequence draft counts k_b, target rows past k_b and draft rows
+  // k_b.. are never read again: skip them (uniform over the workgroup)
+  if (kdraft != nullptr) {
+    const int kb = kdraft[b];
+    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  }
 
   const void* row = row_ptr<DT>(target, draft, b, r, K, V);
   const long long nchunks = V / VEC;
@@ -139,6 +146,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
 template <int DT, int VEC, int U>
 __global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ target, int K,
                                                        int V, int nseg, int seg_chunks,
+                                                       const int32_t* __restrict__ kdraft,
                                                        RowPart* __restrict__ parts,
                                                        uint32_t* __restrict__ hist) {
   using C = Chunk<DT, VEC>;
@@ -149,6 +157,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ 
   const long long grow = wg / nseg;
   const int b = int(grow / rows), r = int(grow % rows);
   if (wg == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (kdraft != nullptr && r > kdraft[b]) return;   // target row past k_b: not needed
 
   const void* row = row_ptr<DT>(target, nullptr, b, r, K, V);
   const long long nchunks = V / VEC;
