@@ -93,6 +93,18 @@ typedef struct spec_verify_stats {
  * bytes plus a few KB per sequence), the EMA state (float64 value and int32
  * count per slot) and the counters, and frees them in spec_verify_destroy.
  * Synchronises the device once (initialisation only).
+ *
+ * Path selection and tuning are read from the environment here (for tests and
+ * measurement; the defaults are the tuned ones):
+ *   SPEC_VERIFY_TARGET_WGS       streaming-pass workgroups to aim for (2048)
+ *   SPEC_VERIFY_NSEG             fixed segments per row (0 = from the target)
+ *   SPEC_VERIFY_FINISH_SEQ       0: stochastic draw as separate scan, tile-sum
+ *                                and pick kernels instead of one workgroup per
+ *                                sequence (that path is always used when a row
+ *                                has more than 256 draw tiles)
+ *   SPEC_VERIFY_TILES_PER_GROUP  draw tiles per workgroup on that path (16)
+ *   SPEC_VERIFY_FUSED_MIN_B      smallest batch that streams and finishes each
+ *                                sequence in one kernel (0 = never)
  */
 int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
                      int logits_dtype, double ema_decay);

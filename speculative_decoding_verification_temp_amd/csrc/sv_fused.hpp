@@ -1,18 +1,21 @@
-// Stochastic verification with one workgroup per sequence.
+// Stochastic verification with one 1024-thread workgroup per sequence after
+// the streaming pass (finish_seq, the default for up to 256 draw tiles per
+// row, i.e. V <= 524288), or for the whole path (verify_fused).
 //
-// One launch does the whole path for each sequence, with all communication
-// inside the workgroup (LDS and barriers), none across workgroups:
-//   1. stream the sequence's 2K+1 logit rows once (128-bit non-temporal
-//      loads, a rolling prefetch buffer that runs across row boundaries) and
-//      keep per-wavefront softmax partials of every row in LDS;
+// Per sequence, with all communication inside the workgroup (LDS and
+// barriers), none across workgroups:
+//   1. (verify_fused only) stream the sequence's 2K+1 logit rows once and keep
+//      per-wavefront softmax partials of every row in LDS; finish_seq instead
+//      combines the streaming pass's per-segment partials;
 //   2. combine the partials in a fixed order and run the acceptance scan on
-//      one wavefront (first rejection j, emitted tokens, histogram, EMA);
-//   3. re-read row pair j (or target row K for the bonus) and form the draw's
-//      float64 tile sums in LDS;
+//      one wavefront (first rejection j, stopping rules, emitted tokens,
+//      histogram, EMA);
+//   3. re-read row pair j (or target row k_b for the bonus) and form the
+//      draw's float64 tile sums in LDS;
 //   4. pick the token from the tile sums and the re-read crossing tile.
-// A whole grid of sequences streams at full HBM bandwidth as long as every
-// compute unit holds at least one sequence, so the host uses this kernel for
-// large batches and the multi-kernel pipeline otherwise.
+// verify_fused is off unless SPEC_VERIFY_FUSED_MIN_B is set: at 4 waves per
+// SIMD its streaming part is slower than the separate streaming pass, and its
+// finish gains no overlap.
 #pragma once
 
 #include "sv_kernels.hpp"

@@ -4,10 +4,14 @@
 //   scan_*         one wavefront per sequence: combine segment partials, form
 //                  p(d), q(d) (or argmax matches / margin ratios), find the
 //                  first rejection with a ballot, emit tokens, histogram, EMA.
-//   draw           correction/bonus draw: per-tile float64 sums of the draw
-//                  weights (exact normalisers, residual split by sign), then
-//                  the last workgroup of each sequence prefix-scans the tile
-//                  sums and re-reads the crossing tile to find the token.
+//   draw           correction/bonus draw, first phase: per-tile float64 sums
+//                  of the draw weights (exact normalisers, residual split by
+//                  sign), several workgroups per sequence.
+//   draw_pick      second phase, one wavefront per sequence: exact
+//                  normalisers from the tile sums, the crossing tile, and a
+//                  re-read of that tile to find the token.
+// These serve vocabularies beyond the per-sequence kernel's tile limit; the
+// per-sequence kernel (sv_fused.hpp) shares the helpers below.
 //
 // None of the kernels use floating-point atomics; every reduction has a fixed
 // order, so reruns are bitwise identical.
@@ -141,33 +145,6 @@ __device__ inline double exp_table_entry(int i, double c) {
 __device__ inline int tab_index(uint32_t bits, int n_half) {
   const uint32_t off = (bits & 0x7fffu) - uint32_t(kTabELo << 7);
   return off < uint32_t(n_half) ? int(off) + ((bits & 0x8000u) ? kTabStride : 0) : -1;
-}
-
-// 2^(x*c - R) for the bf16 values of one chunk: table loads for all of them
-// first, then the direct path for the (rare) values outside the table
-__device__ inline void tab_terms8(const double* T, const u32x4& raw, int n_half, double c,
-                                  double R, double (&out)[8]) {
-  int idx[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    idx[2 * k] = tab_index(raw[k] & 0xffffu, n_half);
-    idx[2 * k + 1] = tab_index(raw[k] >> 16, n_half);
-  }
-  const int sh = -int(R);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) out[k] = __builtin_ldexp(T[idx[k] < 0 ? 0 : idx[k]], sh);
-  bool rare = false;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) rare |= idx[k] < 0;
-  if (rare) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (idx[k] < 0) {
-        const uint32_t bits = (k & 1) ? (raw[k >> 1] >> 16) : (raw[k >> 1] & 0xffffu);
-        out[k] = exp2_acc(__builtin_fma(double(__uint_as_float(bits << 16)), c, -R));
-      }
-    }
-  }
 }
 
 // --------------------------------------------------------------------------
@@ -369,25 +346,6 @@ template <int DT, int VEC> struct DrawRows {
     }
   }
 };
-
-template <int DT, int VEC>
-__device__ inline void chunk_terms_tab(const double* T, int n_half, const DrawRows<DT, VEC>& W,
-                                       const typename Chunk<DT, VEC>::raw_t& rt,
-                                       const typename Chunk<DT, VEC>::raw_t& rd,
-                                       double (&et)[Chunk<DT, VEC>::N],
-                                       double (&ed)[Chunk<DT, VEC>::N]) {
-  if constexpr (DT == DT_BF16 && VEC == 8) {
-    tab_terms8(T, rt, n_half, W.c, W.Rt, et);
-    if (W.residual) {
-      tab_terms8(T, rd, n_half, W.c, W.Rd, ed);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ed[k] = 0.0;
-    }
-  } else {
-    W.terms(rt, rd, et, ed);
-  }
-}
 
 // Tile-sum accumulation for one chunk of a bf16 row pair, a 32-bit word (two
 // tokens) at a time: table terms for both rows, the direct path only for
