@@ -64,37 +64,121 @@ def traffic_for(workload: str, kernel: str):
     return fetch + write
 
 
-def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None):
-    """Time the fp64 CPU oracle on a bounded sample of the same workload, one
-    sequence at a time on one core, cycling over the input sets until about
-    `seconds` of oracle time, and compare its outputs with the GPU's for those
-    sequences (gpu_outs[i] holds the GPU's tokens and accept lengths for set i)."""
+# ---- CPU baseline: the oracle on host cores --------------------------------
+# Worker processes are spawned (fresh interpreters that import numpy and the
+# oracle only, never the GPU runtime) and read the sampled inputs from shared
+# memory, so a task is just a sequence index.
+_W = {}
+
+
+def _worker_init(specs, T, mode, tau):
+    from multiprocessing import shared_memory
     import numpy as np
     from oracle import spec_oracle as O
-    from workloads import to_host_f64
+    _W["shm"] = []
+    for name, (shm_name, shape, dtype) in specs.items():
+        if shm_name is None:
+            _W[name] = None
+            continue
+        shm = shared_memory.SharedMemory(name=shm_name)
+        _W["shm"].append(shm)
+        _W[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
+    _W["args"] = (T, mode, tau)
+    _W["O"] = O
+
+
+def _worker_task(k):
+    O = _W["O"]
+    T, mode, tau = _W["args"]
+    n = _W["tgt"].shape[0]
+    q = k % n
+    kb = _W["kb"]
+    r = O.verify_batch(_W["tgt"][q:q + 1], None if _W["drf"] is None else _W["drf"][q:q + 1],
+                       _W["tok"][q:q + 1], _W["uni"][q:q + 1], T, mode, tau,
+                       draft_len=None if kb is None else kb[q:q + 1])
+    return q, int(r.accept_len[0]), r.tokens[0].tolist(), float(r.min_dist[0])
+
+
+def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None):
+    """Time the fp64 CPU oracle on a bounded sample of the same workload, one
+    sequence per task: first in this process on one core, then on a pool of
+    worker processes (one per usable core, at most 16), about seconds/2 each,
+    cycling over up to 64 sequences of the timed input sets. Every verified
+    sequence is compared with the GPU's output for it (gpu_outs[i] holds the
+    GPU's tokens and accept lengths for set i)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    import numpy as np
+    import torch
+    from oracle import spec_oracle as O
 
     m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
-    n, mism, t_cpu, k = 0, 0, 0.0, 0
-    while t_cpu < seconds and k < 64 * cfg.B:
-        i, b = (k // cfg.B) % len(sets), k % cfg.B
-        x = sets[i]
+    n = min(64, len(sets) * cfg.B)
+    where = [(k % len(sets), (k // len(sets)) % cfg.B) for k in range(n)]
+    arrays = {
+        "tgt": np.stack([sets[i]["target"][b].to(torch.float32).cpu().numpy() for i, b in where]),
+        "drf": (np.stack([sets[i]["draft"][b].to(torch.float32).cpu().numpy() for i, b in where])
+                if mode == "stochastic" else None),
+        "tok": np.stack([sets[i]["tokens"][b].cpu().numpy() for i, b in where]),
+        "uni": np.stack([sets[i]["uniforms"][b].cpu().double().numpy() for i, b in where]),
+        "kb": None if kb is None else np.asarray([kb[b] for _, b in where]),
+    }
+
+    def check(q, alen, toks, dist):
+        i, b = where[q]
         tok_g, len_g = gpu_outs[i]
-        tgt = to_host_f64(x["target"][b:b + 1])
-        drf = to_host_f64(x["draft"][b:b + 1]) if mode == "stochastic" else None
-        tok = x["tokens"][b:b + 1].cpu().numpy()
-        uni = x["uniforms"][b:b + 1].cpu().double().numpy()
-        t0 = time.perf_counter()
-        r = O.verify_batch(tgt, drf, tok, uni, cfg.T, m, cfg.tau,
-                           draft_len=None if kb is None else kb[b:b + 1])
-        t_cpu += time.perf_counter() - t0
-        if r.min_dist[0] >= 1e-6 and (r.accept_len[0] != len_g[b]
-                                      or not np.array_equal(r.tokens[0], tok_g[b])):
-            mism += 1
-        n += 1
-        k += 1
-    return dict(value=n / t_cpu, unit="seqs/s", cores=1, kind="oracle",
-                sample=f"{n} sequence verifications cycling over the {len(sets)} input set(s) of "
-                       f"the timed batch, fp64 numpy, one thread ({t_cpu:.1f} s of oracle time)",
+        return int(dist >= 1e-6 and (alen != len_g[b] or not np.array_equal(toks, tok_g[b])))
+
+    # one core, in this process
+    mism, n1 = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds / 2 or n1 == 0:
+        q = n1 % n
+        r = O.verify_batch(arrays["tgt"][q:q + 1],
+                           None if arrays["drf"] is None else arrays["drf"][q:q + 1],
+                           arrays["tok"][q:q + 1], arrays["uni"][q:q + 1], cfg.T, m, cfg.tau,
+                           draft_len=None if kb is None else arrays["kb"][q:q + 1])
+        mism += check(q, int(r.accept_len[0]), r.tokens[0], float(r.min_dist[0]))
+        n1 += 1
+    t1 = time.perf_counter() - t0
+
+    # all usable cores (at most 16), worker processes over shared memory
+    try:
+        nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        nproc = max(1, min(16, os.cpu_count() or 1))
+    shms, specs = [], {}
+    try:
+        for name, a in arrays.items():
+            if a is None:
+                specs[name] = (None, None, None)
+                continue
+            shm = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            shms.append(shm)
+            np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf)[...] = a
+            specs[name] = (shm.name, a.shape, a.dtype.str)
+        ctx = mp.get_context("spawn")
+        with cf.ProcessPoolExecutor(nproc, mp_context=ctx, initializer=_worker_init,
+                                    initargs=(specs, cfg.T, m, cfg.tau)) as ex:
+            list(ex.map(_worker_task, range(nproc)))          # start-up, not timed
+            nn, k = 0, 0
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < seconds / 2 or nn == 0:
+                for q, alen, toks, dist in ex.map(_worker_task, range(k, k + 2 * nproc)):
+                    mism += check(q, alen, np.asarray(toks), dist)
+                k += 2 * nproc
+                nn += 2 * nproc
+            tn = time.perf_counter() - t0
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    return dict(value=nn / tn, unit="seqs/s", cores=nproc, kind="oracle",
+                single_core_value=n1 / t1,
+                sample=f"{n1} sequence verifications on one core ({t1:.1f} s), then {nn} on "
+                       f"{nproc} worker processes ({tn:.1f} s), cycling over {n} sequences of "
+                       f"the timed input sets; fp64 numpy",
                 parity_mismatches=mism)
 
 
@@ -111,6 +195,9 @@ def main():
     ap.add_argument("--stops", default="none", choices=["none", "varlen"],
                     help="varlen: per-sequence draft counts k_b drawn uniformly from 1..K "
                          "(seeded), no end-of-sequence token, no budget")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="also time a plain 2 GiB streaming read with the streaming pass's "
+                         "access pattern (achievable-bandwidth reference)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -216,6 +303,25 @@ def main():
         "algorithmic_bytes_per_step": int(call_bytes),
         "roofline": roofline,
     }
+    if args.read_probe:
+        buf = torch.zeros(2 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            sv.read_probe(buf, sink)
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r0.record()
+        for _ in range(20):
+            sv.read_probe(buf, sink)
+        r1.record()
+        torch.cuda.synchronize()
+        ms = r0.elapsed_time(r1) / 20
+        gbs = buf.numel() / (ms * 1e-3) / 1e9
+        res["read_probe"] = {"bytes": buf.numel(), "ms": round(ms, 4), "gbs": round(gbs, 1),
+                             "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "streaming_pass_vs_probe": round(achieved / gbs, 4)}
+        del buf
     if args.copy_probe:
         # a plain 1 GiB device copy: counter calibration and a bandwidth reference
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

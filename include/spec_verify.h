@@ -216,6 +216,17 @@ const char *spec_verify_last_error(const spec_verify_handle *h);
 /* Library version string. */
 const char *spec_verify_version(void);
 
+/*
+ * Measurement aid (no handle): one plain streaming read of `bytes` bytes at
+ * device pointer `buf`, with the streaming pass's access pattern (256-thread
+ * workgroups over 256.5 KB spans, 128-bit non-temporal loads), enqueued on
+ * `stream`. It gives the achievable read bandwidth that the streaming pass is
+ * compared with. buf must be 16-byte aligned and bytes a positive multiple of
+ * 16 (else SV_EINVAL); sink is a device uint32 the kernel may write. SV_EHIP
+ * if the launch fails.
+ */
+int spec_verify_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

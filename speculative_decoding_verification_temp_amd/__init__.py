@@ -26,7 +26,7 @@ EXPORTED = (
     "spec_verify_set_stops",
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
-    "spec_verify_last_error", "spec_verify_version",
+    "spec_verify_last_error", "spec_verify_version", "spec_verify_read_probe",
 )
 
 
@@ -71,6 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify_last_error.argtypes = [vp]
     L.spec_verify_last_error.restype = ctypes.c_char_p
     L.spec_verify_version.restype = ctypes.c_char_p
+    L.spec_verify_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
     for name in EXPORTED:
         if name not in ("spec_verify_last_error", "spec_verify_version"):
             getattr(L, name).restype = i32
@@ -84,6 +85,17 @@ def _ptr(t):
 
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def read_probe(buf: "torch.Tensor", sink: "torch.Tensor") -> None:
+    """One plain streaming read of `buf` (a contiguous device tensor, 16-byte
+    aligned, size a multiple of 16 bytes) on the current stream: the
+    achievable-bandwidth reference for the streaming pass."""
+    L = load_library()
+    rc = L.spec_verify_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                  _stream(buf.device))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "read_probe")
 
 
 class SpecVerifier:

@@ -239,6 +239,16 @@ extern "C" {
 
 const char* spec_verify_version(void) { return "specverify 0.1 (gfx950)"; }
 
+int spec_verify_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (buf == nullptr || sink == nullptr || bytes < 16 || bytes % 16 != 0 || !aligned(buf, 16))
+    return SV_EINVAL;
+  const long long chunks = (long long)(bytes / 16);
+  const long long span = 16032;   // one 128256-token bf16 row
+  hipLaunchKernelGGL(sv::read_probe, dim3(unsigned(div_up(chunks, span))), dim3(sv::kBlock), 0,
+                     stream, static_cast<const sv::u32x4*>(buf), chunks, span, sink);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int logits_dtype,
                      double ema_decay) {
   if (out == nullptr) return SV_EINVAL;

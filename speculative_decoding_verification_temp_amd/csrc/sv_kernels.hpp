@@ -636,4 +636,30 @@ __global__ void fill_u64(unsigned long long* a, int n) {
   if (i < n) a[i] = 0ull;
 }
 
+// Plain streaming read at the streaming pass's access pattern (one 256-thread
+// workgroup per span of span_chunks 16-byte chunks, four non-temporal loads
+// in flight per lane): the achievable-bandwidth reference for the roofline.
+// The loaded words are folded with XOR so the loads cannot be removed; sink
+// is written only if the fold hits a fixed value.
+__global__ __launch_bounds__(kBlock) void read_probe(const u32x4* __restrict__ buf,
+                                                     long long chunks, long long span_chunks,
+                                                     uint32_t* __restrict__ sink) {
+  const long long c0 = (long long)blockIdx.x * span_chunks;
+  const long long c1 = min(c0 + span_chunks, chunks);
+  uint32_t x = 0;
+  long long ci = c0 + threadIdx.x;
+  for (; ci + 3 * kBlock < c1; ci += 4 * kBlock) {
+    u32x4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = __builtin_nontemporal_load(buf + ci + u * kBlock);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= r[u][0] ^ r[u][1] ^ r[u][2] ^ r[u][3];
+  }
+  for (; ci < c1; ci += kBlock) {
+    const u32x4 r = __builtin_nontemporal_load(buf + ci);
+    x ^= r[0] ^ r[1] ^ r[2] ^ r[3];
+  }
+  if (x == 0x9e3779b9u) sink[0] = x;
+}
+
 }  // namespace sv

@@ -475,3 +475,19 @@ def test_profiling_events(sv):
             assert call_ms == 0.0
         v.profile(False)
 
+
+
+def test_read_probe_entry_point(sv):
+    """The streaming-read measurement aid runs on a device buffer and rejects
+    misaligned or ragged sizes before enqueueing anything."""
+    L = sv.load_library()
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(4, dtype=torch.int32, device=DEV)
+    sv.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream(DEV).cuda_stream
+    ptr = buf.data_ptr()
+    assert L.spec_verify_read_probe(ptr + 4, 1024, sink.data_ptr(), s) == sv.SV_EINVAL
+    assert L.spec_verify_read_probe(ptr, 1000, sink.data_ptr(), s) == sv.SV_EINVAL
+    assert L.spec_verify_read_probe(None, 1024, sink.data_ptr(), s) == sv.SV_EINVAL
+    assert L.spec_verify_read_probe(ptr, 1024, None, s) == sv.SV_EINVAL
