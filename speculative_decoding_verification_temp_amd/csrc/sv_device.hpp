@@ -107,31 +107,31 @@ __device__ inline float term(float x, float c, float R) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -R));
 }
 
-// 2^a in float64 to about 1e-11 relative: a = n + f with n = rint(a),
-// |f| <= 1/2, 2^f by its Taylor series of degree 9 (Horner), then an exact
-// scaling by 2^n. Arguments below -1100 (including -inf) give 0. Used where
-// single-precision exponentials are not accurate enough: the per-token
-// weights of the correction/bonus draw, whose prefix sums are compared with
-// a uniform at the resolution of one token's share of a large vocabulary.
-__device__ inline double exp2_acc(double a) {
+// 2^a in float64: a = n + f with n = rint(a), |f| <= 1/2, 2^f by its Taylor
+// series (Horner), then an exact scaling by 2^n. Arguments below -1100
+// (including -inf) give 0. Used where single-precision exponentials are not
+// accurate enough: the per-token weights of the correction/bonus draw, whose
+// prefix sums are compared with a uniform at the resolution of one token's
+// share of a large vocabulary. DEG = 9 (about 1e-11 relative at |f| = 1/2,
+// far less near f = 0) for per-token use; DEG = 12 (below 2e-16) for the
+// tables built once per workgroup.
+template <int DEG>
+__device__ inline double exp2_taylor(double a) {
   constexpr double L = 0.6931471805599453094172321214581766;   // ln 2
-  constexpr double c1 = L, c2 = c1 * L / 2, c3 = c2 * L / 3, c4 = c3 * L / 4, c5 = c4 * L / 5,
-                   c6 = c5 * L / 6, c7 = c6 * L / 7, c8 = c7 * L / 8, c9 = c8 * L / 9;
+  double cf[DEG + 1];
+  cf[0] = 1.0;
+#pragma unroll
+  for (int k = 1; k <= DEG; ++k) cf[k] = cf[k - 1] * L / k;
   a = fmax(a, -1100.0);
   const double n = __builtin_rint(a);
   const double f = a - n;
-  double p = c9;
-  p = __builtin_fma(p, f, c8);
-  p = __builtin_fma(p, f, c7);
-  p = __builtin_fma(p, f, c6);
-  p = __builtin_fma(p, f, c5);
-  p = __builtin_fma(p, f, c4);
-  p = __builtin_fma(p, f, c3);
-  p = __builtin_fma(p, f, c2);
-  p = __builtin_fma(p, f, c1);
-  p = __builtin_fma(p, f, 1.0);
+  double p = cf[DEG];
+#pragma unroll
+  for (int k = DEG - 1; k >= 0; --k) p = __builtin_fma(p, f, cf[k]);
   return __builtin_ldexp(p, int(n));
 }
+__device__ inline double exp2_acc(double a) { return exp2_taylor<9>(a); }
+__device__ inline double exp2_acc_hi(double a) { return exp2_taylor<12>(a); }
 
 // Scale a float64 sum by 2^(from - to) exactly (from <= to, both integers or
 // the initial reference). Saturating conversion keeps the empty state at 0.

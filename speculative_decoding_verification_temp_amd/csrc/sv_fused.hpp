@@ -202,6 +202,25 @@ __device__ __forceinline__ double term_unscaled(const double* T, uint32_t bits, 
   return exp2_acc(double(__uint_as_float(bits << 16)) * c);
 }
 
+// fp32 rows: 2^y = 2^floor(y) * 2^(i/256) * 2^r in float64, with i the
+// nearest integer to 256 (y - floor(y)) (all steps exact), |r| <= 1/512, a
+// 257-entry LDS table T2[i] = 2^(i/256) and a degree-4 polynomial for 2^r
+// (truncation error below 4e-17 relative). y <= -1100 (including -inf) gives 0.
+constexpr int kTab2 = 257;
+__device__ inline double exp2_frac_entry(int i) { return exp2_acc_hi(double(i) * (1.0 / 256.0)); }
+__device__ __forceinline__ double exp2_tab(double y, const double* T2) {
+  constexpr double L = 0.6931471805599453094172321214581766;   // ln 2
+  constexpr double a1 = L, a2 = a1 * L / 2, a3 = a2 * L / 3, a4 = a3 * L / 4;
+  y = fmax(y, -1100.0);
+  const double n = __builtin_floor(y);
+  const double t = (y - n) * 256.0;
+  const double ti = __builtin_rint(t);
+  const double r = (t - ti) * (1.0 / 256.0);
+  const double p =
+      __builtin_fma(__builtin_fma(__builtin_fma(__builtin_fma(a4, r, a3), r, a2), r, a1), r, 1.0);
+  return __builtin_ldexp(T2[int(ti)] * p, int(n));
+}
+
 __device__ __forceinline__ void accum_pair_u(double et, double ed, double rho2, double& E,
                                              double& Ed, double& A, double& Bd) {
   E += et;
@@ -230,12 +249,29 @@ __device__ __forceinline__ uint32_t word_at(const u32x4 (&a)[kUnitChunks], int k
 
 // one lane's sums over one unit (chunks c0 + k * kWave; RAGGED: chunks at or
 // past nchunks are skipped)
-template <bool RESID, bool RAGGED>
+template <int DT, bool RESID, bool RAGGED>
 __device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, long long c0,
                                           long long nchunks, double rho2, double c, double& E,
                                           double& Ed, double& A, double& Bd) {
-  uint32_t acc = 0;
   E = Ed = A = Bd = 0.0;
+  if constexpr (DT == DT_F32) {      // 4 fp32 values per chunk, terms from exp2_tab
+#pragma unroll
+    for (int k = 0; k < kUnitChunks; ++k) {
+      if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, T);
+        if constexpr (RESID) {
+          const double ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, T);
+          accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
+        } else {
+          E += et;
+        }
+      }
+    }
+    return;
+  }
+  uint32_t acc = 0;
 #pragma unroll
   for (int k = 0; k < kUnitChunks; ++k) {
     if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
@@ -280,12 +316,12 @@ __device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, lon
 // keeps kUnits - 1 units of loads outstanding while it computes. Chunks past
 // the row end are clamped to the last chunk for loading and skipped in the
 // sums.
-template <bool RESID, int NW>
+template <int DT, int VEC, bool RESID, int NW>
 __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow, const void* drow,
                                                const DrawRow& dr, double c, int ntiles,
                                                long long nchunks, TileSums* tiles, int wid,
                                                int lane) {
-  using C = Chunk<DT_BF16, 8>;
+  using C = Chunk<DT, VEC>;
   const double rho2 = RESID ? __builtin_ldexp(dr.rho, int(dr.R_t) - int(dr.R_d)) : 0.0;
   const int st = -int(dr.R_t), sd = -int(dr.R_d);
   const int my_tiles = wid < ntiles ? (ntiles - 1 - wid) / NW + 1 : 0;
@@ -329,7 +365,7 @@ __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       double e, ed, a, bd;
-      unit_sums<RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
       load_unit(ti + 1, u, b[u]);
       E += e;
       Ed += ed;
@@ -344,9 +380,9 @@ __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow
   for (int u = 0; u < kUnits; ++u) {
     double e, ed, a, bd;
     if (whole)
-      unit_sums<RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
     else
-      unit_sums<RESID, true>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, true>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
     E += e;
     Ed += ed;
     A += a;
@@ -363,7 +399,7 @@ __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow
 //   bonus or Z = 0 fallback: Tt,
 // and a prefix over the chunk sums in token order finds the token, compared
 // against u * total scaled by 2^Rt (exact).
-template <int NT>
+template <int DT, int VEC, int NT>
 __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long long nchunks,
                                               const DrawRow& dr, const void* trow,
                                               const void* drow, bool residual, const double* T,
@@ -372,14 +408,14 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
                                               int32_t* __restrict__ out_tokens,
                                               DevStats* __restrict__ st, double* aux_z,
                                               PickShared& sh) {
-  using C = Chunk<DT_BF16, 8>;
+  using C = Chunk<DT, VEC>;
   static_assert(NT >= kTileChunks, "pick needs one thread per tile chunk");
   constexpr int kPW = kTileChunks / kWave;      // wavefronts in the pick
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   int tile = -1, which = 0;
   bool clamp = false, fallback = false;
   double tgt = 0.0, base = 0.0, rho2 = 0.0, zres = -1.0, St = 0.0;
-  double wv[8];
+  double wv[C::N];
   double cs = 0.0;
   int lp = -1;
   long long ci = 0;
@@ -429,18 +465,19 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
     const u32x4 wt = C::load(trow, cl);
     const u32x4 wd = which ? C::load(drow, cl) : wt;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t bt = (e & 1) ? wt[e >> 1] >> 16 : wt[e >> 1] & 0xffffu;
-      const double et = term_unscaled(T, bt, c);
-      if (which) {
-        const uint32_t bd = (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu;
-        wv[e] = fmax(__builtin_fma(-rho2, term_unscaled(T, bd, c), et), 0.0);
+    for (int e = 0; e < C::N; ++e) {
+      double et, ed = 0.0;
+      if constexpr (DT == DT_BF16) {
+        et = term_unscaled(T, (e & 1) ? wt[e >> 1] >> 16 : wt[e >> 1] & 0xffffu, c);
+        if (which) ed = term_unscaled(T, (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu, c);
       } else {
-        wv[e] = et;
+        et = exp2_tab(double(__uint_as_float(wt[e])) * c, T);
+        if (which) ed = exp2_tab(double(__uint_as_float(wd[e])) * c, T);
       }
+      wv[e] = which ? fmax(__builtin_fma(-rho2, ed, et), 0.0) : et;
       if (!valid) wv[e] = 0.0;
       cs += wv[e];
-      lp = wv[e] > 0.0 ? int(ci * 8 + e) : lp;
+      lp = wv[e] > 0.0 ? int(ci * VEC + e) : lp;
     }
     // compare in units of 2^-Rt
     tgt = __builtin_ldexp(tgt, int(dr.R_t));
@@ -463,9 +500,9 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
     if (hit && lane == __ffsll((long long)hit) - 1) {
       double run = incl - cs;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < C::N; ++e) {
         run += wv[e];
-        if (tok < 0 && run > tgt) tok = int(ci * 8 + e);
+        if (tok < 0 && run > tgt) tok = int(ci * VEC + e);
       }
       if (tok < 0) tok = lp;            // the chunk holds positive weight
     }
@@ -572,14 +609,17 @@ __device__ __forceinline__ void finish_sequence(
   // bf16 rows with moderate references: table terms without per-term scaling
   // (tiles_unscaled); otherwise every term scaled by 2^-R as it is formed
   bool unscaled = false;
-  if constexpr (DT == DT_BF16 && VEC == 8)
+  constexpr bool kFast = (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4);
+  if constexpr (kFast)
     unscaled = fabsf(dr.R_t) <= kUnscaledMaxR && (!W.residual || fabsf(dr.R_d) <= kUnscaledMaxR);
   if (unscaled) {
-    if constexpr (DT == DT_BF16 && VEC == 8) {
+    if constexpr (kFast) {
       if (W.residual)
-        tiles_unscaled<true, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid, lane);
+        tiles_unscaled<DT, VEC, true, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
+                                          lane);
       else
-        tiles_unscaled<false, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid, lane);
+        tiles_unscaled<DT, VEC, false, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
+                                           lane);
     }
   } else {
     for (int t = wid; t < ntiles; t += kW) {
@@ -612,9 +652,9 @@ __device__ __forceinline__ void finish_sequence(
   __syncthreads();
 
   // ---- 4. pick ----
-  if constexpr (DT == DT_BF16 && VEC == 8) {
+  if constexpr (kFast) {
     if (unscaled) {
-      pick_unscaled<NT>(b, K, ntiles, nchunks, dr, W.trow, W.drow, W.residual, T, c64, tiles,
+      pick_unscaled<DT, VEC, NT>(b, K, ntiles, nchunks, dr, W.trow, W.drow, W.residual, T, c64, tiles,
                         uniforms, out_tokens, st, aux_z, psh);
       return;
     }
@@ -632,7 +672,8 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
   using C = Chunk<DT, VEC>;
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
-  __shared__ double T[kTab ? kTabMax : 1];
+  constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
+  __shared__ double T[kTab ? kTabMax : kTab2F ? kTab2 : 1];
   __shared__ float pR[kFMaxRows][kFWaves];
   __shared__ double pS[kFMaxRows][kFWaves];
   __shared__ float fR[kFMaxRows];
@@ -694,6 +735,9 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
   if (ngroups > 1) issue(1, buf[1]);
   if constexpr (kTab) {
     for (int i = tid; i < kTabMax; i += kFBlock) T[i] = exp_table_entry(i, c64);
+  }
+  if constexpr (kTab2F) {
+    for (int i = tid; i < kTab2; i += kFBlock) T[i] = exp2_frac_entry(i);
   }
 
   float Ra[2] = {kRefInit, kRefInit};
@@ -782,7 +826,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
     double* __restrict__ ema, int32_t* __restrict__ steps, double decay,
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
-  __shared__ double T[kTab ? kTabMax : 1];
+  constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
+  __shared__ double T[kTab ? kTabMax : kTab2F ? kTab2 : 1];
   __shared__ float fR[kFMaxRows];
   __shared__ double fS[kFMaxRows];
   __shared__ TileSums tiles[kFMaxTiles];
@@ -792,6 +837,9 @@ __global__ __launch_bounds__(NT) void finish_seq(
   const int rows = 2 * K + 1;
   if constexpr (kTab) {
     for (int i = tid; i < kTabMax; i += NT) T[i] = exp_table_entry(i, c64);
+  }
+  if constexpr (kTab2F) {
+    for (int i = tid; i < kTab2; i += NT) T[i] = exp2_frac_entry(i);
   }
   for (int r = tid; r < rows; r += NT) {
     float R;

@@ -137,7 +137,7 @@ constexpr int kTabMax = 2 * kTabStride;        // 8192 entries, 64 KiB
 __device__ inline double exp_table_entry(int i, double c) {
   const uint32_t bits = uint32_t((i & (kTabStride - 1)) + (kTabELo << 7)) |
                         (i >= kTabStride ? 0x8000u : 0u);
-  return exp2_acc(double(__uint_as_float(bits << 16)) * c);
+  return exp2_acc_hi(double(__uint_as_float(bits << 16)) * c);
 }
 
 // table index of a bf16 value, or -1 when it is outside the first n_half
