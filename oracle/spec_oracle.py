@@ -63,6 +63,22 @@ listed with its reason in the design notes):
     invalid. The EMA observes accept_len / k_b and skips sequences with
     k_b = 0. With eos = -1, k_b = K and m_b >= K + 1 every rule above reduces
     to the plain cycle.
+  * Truncation ([RNR] s.1: p and q are the distributions the samplers really
+    use, after temperature, masks and truncation; s.2: a mask applied only
+    after the correction breaks the guarantee). Optional per sequence: top_k
+    and top_p, applied in that order to every target and draft row of a
+    stochastic sequence before anything else uses p or q (greedy and margin
+    modes do not sample and ignore them). top-k (1 <= top_k < V) keeps the
+    tokens whose logit is at least the top_k-th largest logit counted with
+    multiplicity, so a tie at the cut keeps every tied token. top-p
+    (top_p < 1) then keeps, on the renormalised top-k distribution, each
+    token whose kept tokens with strictly larger logits hold less than top_p
+    of the mass: whole value levels from the top, up to and including the
+    first level at which the mass reaches top_p. The kept tokens are
+    renormalised; dropped tokens get probability exactly 0 in the acceptance
+    ratio, the residual and the bonus draw. top_k <= 0 or >= V and
+    top_p >= 1 mean no truncation; top_p <= 0 or NaN makes the sequence
+    invalid.
 """
 
 from __future__ import annotations
@@ -103,6 +119,50 @@ def softmax_t(x, T: float) -> np.ndarray:
     M = x.max()
     e = np.exp((x - M) / float(T))
     return e / e.sum()
+
+
+def truncation_keep(x, T: float, top_k: int = 0, top_p: float = 1.0):
+    """Tokens kept by top-k and then top-p truncation of one logit row.
+
+    Returns (keep mask, top-p boundary distance). The distance is the
+    smallest |mass above a level - top_p| over the value levels of the top-k
+    set (mass in units of the renormalised top-k distribution): how close
+    the top-p cut came to moving. inf when top-p is off.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    V = x.size
+    keep = np.ones(V, dtype=bool)
+    if 1 <= top_k < V:
+        kth = np.sort(x)[::-1][top_k - 1]      # k-th largest, with multiplicity
+        keep &= x >= kth
+    dist = math.inf
+    if top_p < 1.0:
+        p = softmax_t(x, T)
+        w = np.where(keep, p, 0.0)
+        w = w / w.sum()
+        # the kept tokens by value, largest first, grouped into value levels
+        vals, ws = x[keep], w[keep]
+        order = np.argsort(-vals, kind="stable")
+        vals, ws = vals[order], ws[order]
+        starts = np.flatnonzero(np.concatenate([[True], vals[1:] != vals[:-1]]))
+        level_mass = np.add.reduceat(ws, starts)
+        above = 0.0                    # mass of the levels above the current one
+        lowest_kept = vals[0]
+        for s0, m in zip(starts, level_mass):
+            dist = min(dist, abs(above - top_p))
+            if above < top_p:
+                lowest_kept = vals[s0]
+            above += m
+        keep &= x >= lowest_kept
+    return keep, dist
+
+
+def truncated_softmax(x, T: float, top_k: int = 0, top_p: float = 1.0):
+    """p after temperature and truncation: softmax_t restricted to the kept
+    tokens and renormalised. Returns (p, top-p boundary distance)."""
+    keep, dist = truncation_keep(x, T, top_k, top_p)
+    p = np.where(keep, softmax_t(x, T), 0.0)
+    return p / p.sum(), dist
 
 
 def argmax_lowest(x) -> int:
@@ -199,13 +259,15 @@ class SequenceResult:
 
 def verify_sequence(target, draft, tokens, u, T: float, mode: int,
                     tau: float = 0.0, eos: int = -1, draft_len: int | None = None,
-                    max_emit: int | None = None) -> SequenceResult:
+                    max_emit: int | None = None, top_k: int = 0,
+                    top_p: float = 1.0) -> SequenceResult:
     """Verify one sequence.
 
     target: [K+1, V] logits, draft: [K, V] logits (stochastic only),
     tokens: [K] drafted tokens, u: [K+1] uniforms (stochastic only).
-    eos, draft_len (k_b) and max_emit (m_b) are the optional stopping rules of
-    the module docstring; the defaults give the plain cycle.
+    eos, draft_len (k_b) and max_emit (m_b) are the optional stopping rules,
+    top_k and top_p the optional truncation of the module docstring; the
+    defaults give the plain cycle.
     """
     target = np.asarray(target, dtype=np.float64)
     K = target.shape[0] - 1
@@ -222,6 +284,7 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     if mode == MODE_STOCHASTIC:
         draft = np.asarray(draft, dtype=np.float64)
         valid = valid and all(row_is_valid(draft[i]) for i in range(kb))
+        valid = valid and float(top_p) > 0.0      # NaN compares false
     # per-row argmax side output: rows 0..k_b (rows past k_b are not read)
     argmax = np.array([argmax_lowest(target[i]) if i <= kb and row_is_valid(target[i]) else -1
                        for i in range(K + 1)], dtype=np.int64)
@@ -237,8 +300,12 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     # 1. the ordered walk over positions 0..kb-1: j = first rejection, else kb
     if mode == MODE_STOCHASTIC:
         u = np.asarray(u, dtype=np.float64).reshape(K + 1)
-        p_rows = [softmax_t(target[i], T) for i in range(kb + 1)]
-        q_rows = [softmax_t(draft[i], T) for i in range(kb)]
+        tp = [truncated_softmax(target[i], T, top_k, top_p) for i in range(kb + 1)]
+        tq = [truncated_softmax(draft[i], T, top_k, top_p) for i in range(kb)]
+        p_rows = [p for p, _ in tp]
+        q_rows = [q for q, _ in tq]
+        # a top-p cut close to moving is a decision too (every needed row)
+        acc_dists += [(-1, d) for _, d in tp + tq if d < math.inf]
         for i in range(kb):
             p_d[i] = p_rows[i][toks[i]]
             q_d[i] = q_rows[i][toks[i]]
@@ -362,14 +429,16 @@ class BatchResult:
 
 def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
                  tau: float = 0.0, ema: EmaState | None = None,
-                 rows=None, eos: int = -1, draft_len=None, max_emit=None) -> BatchResult:
+                 rows=None, eos: int = -1, draft_len=None, max_emit=None,
+                 top_k=None, top_p=None) -> BatchResult:
     """Verify every sequence b (or only those listed in `rows`).
 
     target [B, K+1, V], draft [B, K, V] (stochastic), tokens [B, K],
     uniforms [B, K+1]. Arrays may be any float dtype; they are widened to
     float64 one sequence at a time. When `ema` is given, slot b is updated
     for every valid verified sequence b with k_b > 0. eos, draft_len [B] and
-    max_emit [B] (indexed by b) are the optional stopping rules.
+    max_emit [B] (indexed by b) are the optional stopping rules, top_k [B]
+    and top_p [B] the optional truncation.
     """
     B = target.shape[0]
     K = target.shape[1] - 1
@@ -391,7 +460,9 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
             uniforms[b] if (uniforms is not None and mode == MODE_STOCHASTIC) else None,
             T, mode, tau, eos=eos,
             draft_len=None if draft_len is None else int(draft_len[b]),
-            max_emit=None if max_emit is None else int(max_emit[b]))
+            max_emit=None if max_emit is None else int(max_emit[b]),
+            top_k=0 if top_k is None else int(top_k[b]),
+            top_p=1.0 if top_p is None else float(top_p[b]))
         out.tokens[k] = res.tokens
         out.accept_len[k] = res.accept_len
         out.p_d[k] = res.p_d
