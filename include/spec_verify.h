@@ -184,6 +184,33 @@ int spec_verify_set_aux(spec_verify_handle *h, double *p_d, double *q_d,
 int spec_verify_set_stops(spec_verify_handle *h, int eos_token, const int32_t *draft_len,
                           const int32_t *max_emit);
 
+/*
+ * Top-k / top-p truncation for later stochastic spec_verify calls on this
+ * handle ([RNR] s.1: p and q are the distributions the samplers really use,
+ * after temperature and truncation; s.2: a mask that only the correction
+ * sees breaks the guarantee). Every needed target and draft row of sequence
+ * b is truncated with the same rules before the acceptance ratio, the
+ * residual and the bonus draw use it:
+ *
+ *   top_k  [max_batch] int32 device array: keep the values at or above the
+ *          top_k-th largest logit of the row, counted with multiplicity (all
+ *          values tied with it stay); <= 0 or >= V: no top-k; NULL: off
+ *   top_p  [max_batch] float32 device array: then keep, from the top, whole
+ *          value levels up to and including the first level at which the
+ *          kept mass reaches top_p of the top-k mass; >= 1: no top-p; not
+ *          > 0 (or NaN): the sequence is invalid; NULL: off
+ *
+ * Kept tokens are renormalised, dropped ones have probability exactly 0.
+ * Greedy and margin calls ignore the settings. Only bf16 logits are
+ * supported (SV_EUNSUPPORTED for a float32 handle) with V up to 524288
+ * (larger V: spec_verify returns SV_EUNSUPPORTED). The arrays are read by
+ * the device during later calls and stay owned by the caller; they must
+ * outlive those calls. spec_verify_set_truncation(h, NULL, NULL) turns
+ * truncation off. Returns SV_EINVAL for a NULL handle or a misaligned array.
+ */
+int spec_verify_set_truncation(spec_verify_handle *h, const int32_t *top_k,
+                               const float *top_p);
+
 /* EMA state accessors, ordered on `stream`. Device pointers of max_batch entries. */
 int spec_verify_get_ema(spec_verify_handle *h, double *ema_dev, int32_t *steps_dev,
                         hipStream_t stream);

@@ -23,7 +23,7 @@ _ERRNAMES = {-1: "SV_EINVAL", -2: "SV_EUNSUPPORTED", -3: "SV_ENOMEM", -4: "SV_EH
 
 EXPORTED = (
     "spec_verify_init", "spec_verify", "spec_verify_destroy", "spec_verify_set_aux",
-    "spec_verify_set_stops",
+    "spec_verify_set_stops", "spec_verify_set_truncation",
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
     "spec_verify_last_error", "spec_verify_version", "spec_verify_read_probe",
@@ -61,6 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify_destroy.argtypes = [vp]
     L.spec_verify_set_aux.argtypes = [vp, vp, vp, vp, vp]
     L.spec_verify_set_stops.argtypes = [vp, i32, vp, vp]
+    L.spec_verify_set_truncation.argtypes = [vp, vp, vp]
     L.spec_verify_get_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_set_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_reset_ema.argtypes = [vp, vp]
@@ -180,6 +181,23 @@ class SpecVerifier:
 
     def clear_stops(self):
         self.set_stops(-1, None, None)
+
+    def set_truncation(self, top_k=None, top_p=None):
+        """Per-sequence top-k [max_batch] (int32) and top-p [max_batch]
+        (float32) device tensors, or None, for later stochastic calls (bf16
+        logits). The tensors are kept referenced here while they are in use."""
+        for t, dt, name in ((top_k, torch.int32, "top_k"), (top_p, torch.float32, "top_p")):
+            if t is not None and (t.dtype != dt or t.device != self.device or not t.is_contiguous()
+                                  or t.numel() < self.max_batch):
+                raise ValueError(f"{name} must be a contiguous {dt} device tensor of "
+                                 f"at least max_batch entries")
+        self._check(self.lib.spec_verify_set_truncation(
+            self._h, None if top_k is None else _ptr(top_k),
+            None if top_p is None else _ptr(top_p)), "set_truncation")
+        self._trunc = (top_k, top_p)
+
+    def clear_truncation(self):
+        self.set_truncation(None, None)
 
     # -- verification --
     def _check_logits(self, t, rows, name):

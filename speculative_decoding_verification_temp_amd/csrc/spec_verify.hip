@@ -10,7 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "sv_fused.hpp"
+#include "sv_trunc.hpp"
 
 #ifndef SV_U_BF16
 #define SV_U_BF16 4
@@ -60,6 +60,7 @@ struct spec_verify_handle {
   hipEvent_t* prof_ev = nullptr;   // 3 events per recorded call
   bool prof_call_end = false;      // also record the end of each call
   sv::Stops stops{nullptr, nullptr, -1};   // stopping rules for later calls
+  sv::Trunc trunc{nullptr, nullptr};       // top-k / top-p truncation for later calls
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
@@ -150,7 +151,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   prof_mark(h, 1, s);
   if (rc) return rc;
   if (h->finish_seq && L.ntiles <= sv::kFMaxTiles && rows <= sv::kFMaxRows) {
-    hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock>), dim3(B),
+    hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock, false>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
                        h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->stops,
                        out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p,
@@ -170,6 +171,32 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
                      V, L.ntiles, target, draft, h->draw, uniforms, c64, h->tsum, out_tokens,
                      h->stats, h->aux_z);
   return check_launch(h, "draw_pick");
+}
+
+// Stochastic mode with top-k / top-p truncation (bf16 rows): the truncation
+// pass (one workgroup per needed row, exact value histogram) instead of the
+// streaming pass, then the per-sequence finish with masked tables.
+template <int VEC>
+int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draft,
+              const int32_t* tokens, const float* uniforms, float c, double c64,
+              int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
+  const int K = h->K, V = h->V;
+  const int rows = 2 * K + 1;
+  const int ntiles = div_up(V / VEC, sv::kTileChunks);
+  if (ntiles > sv::kFMaxTiles || rows > sv::kFMaxRows)
+    return fail(h, SV_EUNSUPPORTED, "truncation needs V <= %d (bf16)",
+                sv::kFMaxTiles * sv::kTileChunks * VEC);
+  prof_mark(h, 0, s);
+  hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(B * rows)), dim3(sv::kTrBlock), 0,
+                     s, target, draft, K, V, c, c64, h->trunc, h->stops.k, h->parts, hist);
+  int rc = check_launch(h, "rowstats_trunc");
+  prof_mark(h, 1, s);
+  if (rc) return rc;
+  hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
+                     dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
+                     uniforms, c, c64, tab_half(c64), h->stops, out_tokens, out_len, hist, h->ema,
+                     h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z);
+  return check_launch(h, "finish_seq (truncated)");
 }
 
 // Stochastic mode, one workgroup per sequence (large batches).
@@ -332,6 +359,17 @@ int spec_verify_set_stops(spec_verify_handle* h, int eos_token, const int32_t* d
   return SV_OK;
 }
 
+int spec_verify_set_truncation(spec_verify_handle* h, const int32_t* top_k, const float* top_p) {
+  if (h == nullptr) return SV_EINVAL;
+  if ((top_k != nullptr || top_p != nullptr) && h->dtype != SV_DTYPE_BF16)
+    return fail(h, SV_EUNSUPPORTED, "truncation is implemented for bf16 logits");
+  if (top_k != nullptr && !aligned(top_k, 4)) return fail(h, SV_EINVAL, "misaligned top_k");
+  if (top_p != nullptr && !aligned(top_p, 4)) return fail(h, SV_EINVAL, "misaligned top_p");
+  h->trunc.k = top_k;
+  h->trunc.p = top_p;
+  return SV_OK;
+}
+
 int spec_verify(spec_verify_handle* h, int B, const void* target, const void* draft,
                 const int32_t* tokens, const float* uniforms, float temperature, int mode,
                 float tau, int32_t* out_tokens, int32_t* out_len, uint32_t* out_hist,
@@ -369,7 +407,15 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   int rc = SV_OK;
   const double c64 = kLog2e / double(temperature);
   const float c = float(c64);
-  if (mode == SV_MODE_STOCHASTIC) {
+  const bool trunc = h->trunc.k != nullptr || h->trunc.p != nullptr;
+  if (mode == SV_MODE_STOCHASTIC && trunc) {
+    if (vec)
+      rc = run_trunc<8>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens, out_len,
+                        out_hist, stream);
+    else
+      rc = run_trunc<1>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens, out_len,
+                        out_hist, stream);
+  } else if (mode == SV_MODE_STOCHASTIC) {
     if (h->dtype == SV_DTYPE_BF16 && vec && use_fused(h, B, 8))
       rc = run_fused<sv::DT_BF16, 8, 8>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens,
                                         out_len, out_hist, stream);

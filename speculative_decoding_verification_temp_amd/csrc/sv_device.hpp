@@ -202,6 +202,7 @@ struct DrawRow {
   float R_t, R_d;
   int j;         // rejection index (kb = bonus), -1 = nothing to draw
   int kb;        // drafts tested in this sequence
+  uint32_t thr_t, thr_d;   // truncation: smallest kept value key of each row (0 = all)
 };
 
 // Per-tile sums left by the draw's first phase, all relative to the row

@@ -195,11 +195,14 @@ __device__ __forceinline__ double tab_at(const double* T, uint32_t byte_off) {
   return *reinterpret_cast<const double*>(reinterpret_cast<const char*>(T) + byte_off);
 }
 
-// 2^(x * c) of one bf16 value: its table entry, or exp2_acc outside the window
-__device__ __forceinline__ double term_unscaled(const double* T, uint32_t bits, double c) {
+// 2^(x * c) of one bf16 value: its table entry, or exp2_acc outside the
+// window (0 there when the row's truncation drops the value; inside the
+// window the table itself holds 0 for dropped values)
+__device__ __forceinline__ double term_unscaled(const double* T, uint32_t bits, double c,
+                                                uint32_t thr) {
   const uint32_t off = (bits & 0x7fffu) - uint32_t(kTabELo << 7);
   if (off < uint32_t(kTabStride)) return T[off + ((bits & 0x8000u) ? kTabStride : 0)];
-  return exp2_acc(double(__uint_as_float(bits << 16)) * c);
+  return bf16_key(bits) >= thr ? exp2_acc(double(__uint_as_float(bits << 16)) * c) : 0.0;
 }
 
 // fp32 rows: 2^y = 2^floor(y) * 2^(i/256) * 2^r in float64, with i the
@@ -248,9 +251,11 @@ __device__ __forceinline__ uint32_t word_at(const u32x4 (&a)[kUnitChunks], int k
 }
 
 // one lane's sums over one unit (chunks c0 + k * kWave; RAGGED: chunks at or
-// past nchunks are skipped)
+// past nchunks are skipped). Tt, Td: the target and draft rows' tables (one
+// table unless the rows are truncated), thr_t, thr_d their threshold keys.
 template <int DT, bool RESID, bool RAGGED>
-__device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, long long c0,
+__device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, uint32_t thr_t,
+                                          uint32_t thr_d, const UnitBuf& u, long long c0,
                                           long long nchunks, double rho2, double c, double& E,
                                           double& Ed, double& A, double& Bd) {
   E = Ed = A = Bd = 0.0;
@@ -260,9 +265,9 @@ __device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, lon
       if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const double et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, T);
+        const double et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, Tt);
         if constexpr (RESID) {
-          const double ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, T);
+          const double ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, Tt);
           accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
         } else {
           E += et;
@@ -278,10 +283,10 @@ __device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, lon
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t pt = tab_offsets2(u.a[k][q], acc);
-      const double t0 = tab_at(T, pt & 0xffffu), t1 = tab_at(T, pt >> 16);
+      const double t0 = tab_at(Tt, pt & 0xffffu), t1 = tab_at(Tt, pt >> 16);
       if constexpr (RESID) {
         const uint32_t pd = tab_offsets2(u.d[k][q], acc);
-        const double f0 = tab_at(T, pd & 0xffffu), f1 = tab_at(T, pd >> 16);
+        const double f0 = tab_at(Td, pd & 0xffffu), f1 = tab_at(Td, pd >> 16);
         accum_pair_u(t0, f0, rho2, E, Ed, A, Bd);
         accum_pair_u(t1, f1, rho2, E, Ed, A, Bd);
       } else {
@@ -298,10 +303,10 @@ __device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, lon
       const int k = v >> 3, q = v & 7;
       if (RAGGED && c0 + (long long)k * kWave >= nchunks) break;
       const uint32_t wt = word_at(u.a, k, q >> 1);
-      const double et = term_unscaled(T, (q & 1) ? wt >> 16 : wt & 0xffffu, c);
+      const double et = term_unscaled(Tt, (q & 1) ? wt >> 16 : wt & 0xffffu, c, thr_t);
       if constexpr (RESID) {
         const uint32_t wd = word_at(u.d, k, q >> 1);
-        const double ed = term_unscaled(T, (q & 1) ? wd >> 16 : wd & 0xffffu, c);
+        const double ed = term_unscaled(Td, (q & 1) ? wd >> 16 : wd & 0xffffu, c, thr_d);
         accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
       } else {
         E += et;
@@ -317,7 +322,8 @@ __device__ __forceinline__ void unit_sums(const double* T, const UnitBuf& u, lon
 // the row end are clamped to the last chunk for loading and skipped in the
 // sums.
 template <int DT, int VEC, bool RESID, int NW>
-__device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow, const void* drow,
+__device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* Td,
+                                               const void* trow, const void* drow,
                                                const DrawRow& dr, double c, int ntiles,
                                                long long nchunks, TileSums* tiles, int wid,
                                                int lane) {
@@ -365,7 +371,8 @@ __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       double e, ed, a, bd;
-      unit_sums<DT, RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, false>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u), nchunks,
+                                  rho2, c, e, ed, a, bd);
       load_unit(ti + 1, u, b[u]);
       E += e;
       Ed += ed;
@@ -380,9 +387,11 @@ __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow
   for (int u = 0; u < kUnits; ++u) {
     double e, ed, a, bd;
     if (whole)
-      unit_sums<DT, RESID, false>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, false>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u), nchunks,
+                                  rho2, c, e, ed, a, bd);
     else
-      unit_sums<DT, RESID, true>(T, b[u], unit_c0(ti, u), nchunks, rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, true>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u), nchunks,
+                                 rho2, c, e, ed, a, bd);
     E += e;
     Ed += ed;
     A += a;
@@ -402,8 +411,8 @@ __device__ __forceinline__ void tiles_unscaled(const double* T, const void* trow
 template <int DT, int VEC, int NT>
 __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long long nchunks,
                                               const DrawRow& dr, const void* trow,
-                                              const void* drow, bool residual, const double* T,
-                                              double c, const TileSums* ts,
+                                              const void* drow, bool residual, const double* Tt,
+                                              const double* Td, double c, const TileSums* ts,
                                               const float* __restrict__ uniforms,
                                               int32_t* __restrict__ out_tokens,
                                               DevStats* __restrict__ st, double* aux_z,
@@ -468,11 +477,12 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
     for (int e = 0; e < C::N; ++e) {
       double et, ed = 0.0;
       if constexpr (DT == DT_BF16) {
-        et = term_unscaled(T, (e & 1) ? wt[e >> 1] >> 16 : wt[e >> 1] & 0xffffu, c);
-        if (which) ed = term_unscaled(T, (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu, c);
+        et = term_unscaled(Tt, (e & 1) ? wt[e >> 1] >> 16 : wt[e >> 1] & 0xffffu, c, dr.thr_t);
+        if (which)
+          ed = term_unscaled(Td, (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu, c, dr.thr_d);
       } else {
-        et = exp2_tab(double(__uint_as_float(wt[e])) * c, T);
-        if (which) ed = exp2_tab(double(__uint_as_float(wd[e])) * c, T);
+        et = exp2_tab(double(__uint_as_float(wt[e])) * c, Tt);
+        if (which) ed = exp2_tab(double(__uint_as_float(wd[e])) * c, Tt);
       }
       wv[e] = which ? fmax(__builtin_fma(-rho2, ed, et), 0.0) : et;
       if (!valid) wv[e] = 0.0;
@@ -527,11 +537,18 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
 // Phases 2-4 for one sequence, given its row statistics in LDS (fR, fS):
 // the acceptance scan on wavefront 0, the draw's float64 tile sums of row
 // pair j over all wavefronts of the workgroup, then the pick.
-template <int DT, int VEC, int NT>
+// TRUNC (bf16 rows): fK holds each row's truncation threshold key and fS its
+// truncated normaliser, a sum of level_term values; p(d) and q(d) are formed
+// with level_term too and are 0 for dropped values, and once j is
+// known T is filled with two tables, the target row's and the draft row's,
+// each 0 at the values its row drops (without TRUNC, T is one table built by
+// the caller).
+template <int DT, int VEC, int NT, bool TRUNC>
 __device__ __forceinline__ void finish_sequence(
     int b, int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
-    Stops sp, int n_half, const double* T, const float* fR, const double* fS, TileSums* tiles,
+    Stops sp, int n_half, double* T, const float* fR, const double* fS, const uint32_t* fK,
+    TileSums* tiles,
     DrawRow& s_dr, PickShared& psh, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
@@ -548,9 +565,11 @@ __device__ __forceinline__ void finish_sequence(
     stops_of(sp, b, K, kb, m, lane_bad);
     float Rt = 0.0f, Rd = 0.0f;
     double St = 1.0, Sd = 1.0;
+    uint32_t kt = 0u, kd = 0u;
     if (lane <= kb) {
       Rt = fR[lane];
       St = fS[lane];
+      if constexpr (TRUNC) kt = fK[lane];
       lane_bad |= !finite_pos(St);
     }
     int d = 0;
@@ -559,14 +578,23 @@ __device__ __forceinline__ void finish_sequence(
     if (lane < kb) {
       Rd = fR[K + 1 + lane];
       Sd = fS[K + 1 + lane];
+      if constexpr (TRUNC) kd = fK[K + 1 + lane];
       lane_bad |= !finite_pos(Sd);
       d = tokens[(long long)b * K + lane];
       lane_bad |= !(d >= 0 && d < V);   // checked before the gather below
       if (!lane_bad) {
         const float xt = load_logit<DT>(row_base(lane), d);
         const float xd = load_logit<DT>(row_base(K + 1 + lane), d);
-        P = double(term(xt, c, Rt)) / St;
-        Q = double(term(xd, c, Rd)) / Sd;
+        if constexpr (TRUNC) {
+          // the same level terms as the truncated normalisers; 0 when dropped
+          const uint32_t at = bf16_key(__float_as_uint(xt) >> 16);
+          const uint32_t ad = bf16_key(__float_as_uint(xd) >> 16);
+          P = (at >= kt && key_finite(at)) ? level_term(at, c64, Rt) / St : 0.0;
+          Q = (ad >= kd && key_finite(ad)) ? level_term(ad, c64, Rd) / Sd : 0.0;
+        } else {
+          P = double(term(xt, c, Rt)) / St;
+          Q = double(term(xd, c, Rd)) / Sd;
+        }
         const double u = uniforms[(long long)b * (K + 1) + lane];
         keep = (P >= Q) || (u < P / Q);
         zq = keep && Q == 0.0;
@@ -581,6 +609,7 @@ __device__ __forceinline__ void finish_sequence(
       aux_q[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : Q;
     const float Rtj = __shfl(Rt, j, kWave), Rdj = __shfl(Rd, j, kWave);
     const double Stj = __shfl(St, j, kWave), Sdj = __shfl(Sd, j, kWave);
+    const uint32_t ktj = __shfl(kt, j, kWave), kdj = __shfl(kd, j, kWave);
     if (lane == 0) {
       DrawRow dr;
       dr.rho = Stj / Sdj;
@@ -588,6 +617,8 @@ __device__ __forceinline__ void finish_sequence(
       dr.R_d = Rdj;
       dr.j = (bad || w.cpos < 0) ? -1 : j;     // -1: invalid, or no correction emitted
       dr.kb = kb;
+      dr.thr_t = ktj;
+      dr.thr_d = kdj;
       s_dr = dr;
       if (dr.j < 0 && aux_z != nullptr) aux_z[b] = -1.0;
     }
@@ -600,6 +631,18 @@ __device__ __forceinline__ void finish_sequence(
   __syncthreads();
   const DrawRow dr = s_dr;
   if (dr.j < 0) return;
+  constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
+  if constexpr (TRUNC && kTab) {
+    for (int i = tid; i < kTabMax; i += NT) {
+      const double e = exp_table_entry(i, c64);
+      const uint32_t kx = bf16_key(tab_bits(i));
+      T[i] = kx >= dr.thr_t ? e : 0.0;
+      T[kTabMax + i] = kx >= dr.thr_d ? e : 0.0;
+    }
+    __syncthreads();
+  }
+  const double* Tt = T;
+  const double* Td = (TRUNC && kTab) ? T + kTabMax : T;
 
   // ---- 3. draw tile sums of row pair j (or target row K) ----
   // wavefront w takes tiles w, w + kW, ...
@@ -615,11 +658,11 @@ __device__ __forceinline__ void finish_sequence(
   if (unscaled) {
     if constexpr (kFast) {
       if (W.residual)
-        tiles_unscaled<DT, VEC, true, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
-                                          lane);
+        tiles_unscaled<DT, VEC, true, kW>(Tt, Td, W.trow, W.drow, dr, c64, ntiles, nchunks,
+                                          tiles, wid, lane);
       else
-        tiles_unscaled<DT, VEC, false, kW>(T, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
-                                           lane);
+        tiles_unscaled<DT, VEC, false, kW>(Tt, Td, W.trow, W.drow, dr, c64, ntiles, nchunks,
+                                           tiles, wid, lane);
     }
   } else {
     for (int t = wid; t < ntiles; t += kW) {
@@ -630,7 +673,7 @@ __device__ __forceinline__ void finish_sequence(
         if (ci < nchunks) {
           typename C::raw_t a, d;
           W.load(ci, a, d);
-          accum_chunk<DT, VEC>(T, n_half, W, a, d, dr.rho, E, Ed, A, Bd);
+          accum_chunk<DT, VEC>(Tt, Td, n_half, W, a, d, dr.rho, E, Ed, A, Bd);
         }
       }
       E = wave_sum(E);
@@ -654,7 +697,8 @@ __device__ __forceinline__ void finish_sequence(
   // ---- 4. pick ----
   if constexpr (kFast) {
     if (unscaled) {
-      pick_unscaled<DT, VEC, NT>(b, K, ntiles, nchunks, dr, W.trow, W.drow, W.residual, T, c64, tiles,
+      pick_unscaled<DT, VEC, NT>(b, K, ntiles, nchunks, dr, W.trow, W.drow, W.residual, Tt, Td,
+                                 c64, tiles,
                         uniforms, out_tokens, st, aux_z, psh);
       return;
     }
@@ -809,15 +853,18 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
   }
   __syncthreads();
 
-  finish_sequence<DT, VEC, kFBlock>(b, K, V, target, draft, tokens, uniforms, c, c64, sp, n_half, T,
-                                    fR, fS, tiles, s_dr, psh, out_tokens, out_len, hist, ema,
+  finish_sequence<DT, VEC, kFBlock, false>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
+                                           n_half, T, fR, fS, nullptr, tiles, s_dr, psh,
+                                           out_tokens, out_len, hist, ema,
                                     steps,
                                     decay, st, aux_p, aux_q, aux_z);
 }
 
 // After the multi-workgroup streaming pass: one workgroup per sequence
-// combines the row partials (fixed order) and runs phases 2-4.
-template <int DT, int VEC, int NT>
+// combines the row partials (fixed order) and runs phases 2-4. TRUNC: after
+// the truncation pass instead, with one partial per row whose idx holds the
+// row's threshold key.
+template <int DT, int VEC, int NT, bool TRUNC>
 __global__ __launch_bounds__(NT) void finish_seq(
     int K, int V, int nseg, const RowPart* __restrict__ parts, const void* __restrict__ target,
     const void* __restrict__ draft, const int32_t* __restrict__ tokens,
@@ -827,15 +874,17 @@ __global__ __launch_bounds__(NT) void finish_seq(
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
   constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
-  __shared__ double T[kTab ? kTabMax : kTab2F ? kTab2 : 1];
+  static_assert(!TRUNC || DT == DT_BF16, "truncation is implemented for bf16 rows");
+  __shared__ double T[kTab ? (TRUNC ? 2 * kTabMax : kTabMax) : kTab2F ? kTab2 : 1];
   __shared__ float fR[kFMaxRows];
   __shared__ double fS[kFMaxRows];
+  __shared__ uint32_t fK[TRUNC ? kFMaxRows : 1];
   __shared__ TileSums tiles[kFMaxTiles];
   __shared__ DrawRow s_dr;
   __shared__ PickShared psh;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
-  if constexpr (kTab) {
+  if constexpr (kTab && !TRUNC) {
     for (int i = tid; i < kTabMax; i += NT) T[i] = exp_table_entry(i, c64);
   }
   if constexpr (kTab2F) {
@@ -844,13 +893,16 @@ __global__ __launch_bounds__(NT) void finish_seq(
   for (int r = tid; r < rows; r += NT) {
     float R;
     double S;
-    combine_sum_parts(parts + ((long long)b * rows + r) * nseg, nseg, R, S);
+    const RowPart* pr = parts + ((long long)b * rows + r) * nseg;
+    combine_sum_parts(pr, nseg, R, S);
     fR[r] = R;
     fS[r] = S;
+    if constexpr (TRUNC) fK[r] = uint32_t(pr->idx);
   }
   __syncthreads();
-  finish_sequence<DT, VEC, NT>(b, K, V, target, draft, tokens, uniforms, c, c64, sp, n_half, T,
-                                    fR, fS, tiles, s_dr, psh, out_tokens, out_len, hist, ema,
+  finish_sequence<DT, VEC, NT, TRUNC>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
+                                      n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
+                                      out_len, hist, ema,
                                     steps,
                                     decay, st, aux_p, aux_q, aux_z);
 }

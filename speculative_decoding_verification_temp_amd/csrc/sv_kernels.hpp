@@ -133,11 +133,14 @@ constexpr int kTabMaxExp = 32;
 constexpr int kTabStride = kTabMaxExp * 128;   // 4096 entries per sign
 constexpr int kTabMax = 2 * kTabStride;        // 8192 entries, 64 KiB
 
-// entry i of the table (layout as above)
+// bf16 bit pattern of table entry i (layout as above)
+__device__ inline uint32_t tab_bits(int i) {
+  return uint32_t((i & (kTabStride - 1)) + (kTabELo << 7)) | (i >= kTabStride ? 0x8000u : 0u);
+}
+
+// entry i of the table
 __device__ inline double exp_table_entry(int i, double c) {
-  const uint32_t bits = uint32_t((i & (kTabStride - 1)) + (kTabELo << 7)) |
-                        (i >= kTabStride ? 0x8000u : 0u);
-  return exp2_acc_hi(double(__uint_as_float(bits << 16)) * c);
+  return exp2_acc_hi(double(__uint_as_float(tab_bits(i) << 16)) * c);
 }
 
 // table index of a bf16 value, or -1 when it is outside the first n_half
@@ -145,6 +148,37 @@ __device__ inline double exp_table_entry(int i, double c) {
 __device__ inline int tab_index(uint32_t bits, int n_half) {
   const uint32_t off = (bits & 0x7fffu) - uint32_t(kTabELo << 7);
   return off < uint32_t(n_half) ? int(off) + ((bits & 0x8000u) ? kTabStride : 0) : -1;
+}
+
+// Order-preserving 16-bit key of a bf16 value (bits = its 16-bit pattern):
+// 0x8000 + |x| for x >= 0, 0x8000 - |x| for x < 0 (|x| as the 15-bit pattern),
+// so larger values have larger keys and -0 shares the key of +0. Keys run
+// from 1 (the largest negative NaN) to 0xffff; finite values lie in
+// [0x81, 0xff7f], -inf is 0x80 and +inf 0xff80. A truncated row keeps the
+// values whose key is at least its threshold key; threshold 0 keeps all.
+__device__ inline uint32_t bf16_key(uint32_t bits) {
+  const uint32_t mag = bits & 0x7fffu;
+  return (bits & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+}
+constexpr uint32_t kKeyNegInf = 0x80u, kKeyPosInf = 0xff80u;
+
+// the bf16 value of a key
+__device__ inline float key_value(uint32_t key) {
+  const uint32_t bits = key >= 0x8000u ? key - 0x8000u : (0x8000u | (0x8000u - key));
+  return __uint_as_float(bits << 16);
+}
+
+__device__ inline bool key_finite(uint32_t key) { return key > kKeyNegInf && key < kKeyPosInf; }
+
+// 2^(x c - R) of a finite bf16 value (by key) in float64 for the truncated
+// path's normalisers and p(d), q(d): the exponent x c - R, formed with the
+// float64 c, is split exactly into an integer and a part in [-1/2, 1/2],
+// whose power of two is taken in single precision (relative error below
+// 2e-7 whatever the size of x c)
+__device__ inline double level_term(uint32_t key, double c64, float R) {
+  const double a = fmax(__builtin_fma(double(key_value(key)), c64, -double(R)), -2000.0);
+  const double n = __builtin_rint(a);
+  return __builtin_ldexp(double(__builtin_amdgcn_exp2f(float(a - n))), int(n));
 }
 
 // --------------------------------------------------------------------------
@@ -216,6 +250,7 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
     dr.R_d = Rdj;
     dr.j = (bad || w.cpos < 0) ? -1 : j;
     dr.kb = kb;
+    dr.thr_t = dr.thr_d = 0u;
     draw[b] = dr;
     if (dr.j < 0 && aux_z != nullptr) aux_z[b] = -1.0;
   }
@@ -300,6 +335,7 @@ template <int DT, int VEC> struct DrawRows {
   const void* trow;
   const void* drow;
   double c, Rt, Rd;
+  uint32_t thr_t, thr_d;
   bool residual;
 
   __device__ inline void init(const void* target, const void* draft, const DrawRow& dr, int b,
@@ -310,6 +346,13 @@ template <int DT, int VEC> struct DrawRows {
     drow = residual ? row_ptr<DT>(target, draft, b, K + 1 + dr.j, K, V) : nullptr;
     Rt = dr.R_t;
     Rd = dr.R_d;
+    thr_t = dr.thr_t;
+    thr_d = dr.thr_d;
+  }
+  // whether a value survives its row's truncation (bf16 rows only)
+  __device__ static inline bool kept(float x, uint32_t thr) {
+    if constexpr (DT == DT_BF16) return bf16_key(__float_as_uint(x) >> 16) >= thr;
+    return true;
   }
   __device__ inline void load(long long ci, typename C::raw_t& rt, typename C::raw_t& rd) const {
     rt = C::load(trow, ci);
@@ -321,11 +364,11 @@ template <int DT, int VEC> struct DrawRows {
                                   int which, double rho) const {
     float xt[C::N];
     C::unpack(rt, xt);
-    const double et = exp2_acc(__builtin_fma(double(xt[e]), c, -Rt));
+    const double et = kept(xt[e], thr_t) ? exp2_acc(__builtin_fma(double(xt[e]), c, -Rt)) : 0.0;
     if (!which) return et;
     float xd[C::N];
     C::unpack(rd, xd);
-    const double ed = exp2_acc(__builtin_fma(double(xd[e]), c, -Rd));
+    const double ed = kept(xd[e], thr_d) ? exp2_acc(__builtin_fma(double(xd[e]), c, -Rd)) : 0.0;
     return fmax(et - rho * ed, 0.0);
   }
   // exact terms of one chunk (et, and ed when drawing from a residual)
@@ -334,12 +377,14 @@ template <int DT, int VEC> struct DrawRows {
     float xt[C::N];
     C::unpack(rt, xt);
 #pragma unroll
-    for (int k = 0; k < C::N; ++k) et[k] = exp2_acc(__builtin_fma(double(xt[k]), c, -Rt));
+    for (int k = 0; k < C::N; ++k)
+      et[k] = kept(xt[k], thr_t) ? exp2_acc(__builtin_fma(double(xt[k]), c, -Rt)) : 0.0;
     if (residual) {
       float xd[C::N];
       C::unpack(rd, xd);
 #pragma unroll
-      for (int k = 0; k < C::N; ++k) ed[k] = exp2_acc(__builtin_fma(double(xd[k]), c, -Rd));
+      for (int k = 0; k < C::N; ++k)
+        ed[k] = kept(xd[k], thr_d) ? exp2_acc(__builtin_fma(double(xd[k]), c, -Rd)) : 0.0;
     } else {
 #pragma unroll
       for (int k = 0; k < C::N; ++k) ed[k] = 0.0;
@@ -360,12 +405,19 @@ __device__ inline void accum_pair(double et, double ed, double rho, double& E, d
   Bd = __builtin_fma(dv > 0.0 ? 1.0 : 0.0, ed, Bd);
 }
 
-__device__ inline double tab_fix(double v, int idx, uint32_t bits, double c, double R) {
-  return idx < 0 ? exp2_acc(__builtin_fma(double(__uint_as_float(bits << 16)), c, -R)) : v;
+// a term the table did not give (idx < 0): formed directly, 0 when truncated
+__device__ inline double tab_fix(double v, int idx, uint32_t bits, double c, double R,
+                                 uint32_t thr) {
+  if (idx >= 0) return v;
+  return bf16_key(bits) >= thr ? exp2_acc(__builtin_fma(double(__uint_as_float(bits << 16)), c, -R))
+                               : 0.0;
 }
 
+// Tt, Td: the tables for the target and the draft row (the same table unless
+// the rows are truncated, when each holds 0 at the values its row drops)
 template <int DT, int VEC>
-__device__ __forceinline__ void accum_chunk(const double* T, int n_half, const DrawRows<DT, VEC>& W,
+__device__ __forceinline__ void accum_chunk(const double* Tt, const double* Td, int n_half,
+                                   const DrawRows<DT, VEC>& W,
                                    const typename Chunk<DT, VEC>::raw_t& rt,
                                    const typename Chunk<DT, VEC>::raw_t& rd, double rho,
                                    double& E, double& Ed, double& A, double& Bd) {
@@ -376,25 +428,25 @@ __device__ __forceinline__ void accum_chunk(const double* T, int n_half, const D
     for (int k = 0; k < 4; ++k) {
       const uint32_t t0 = rt[k] & 0xffffu, t1 = rt[k] >> 16;
       const int i0 = tab_index(t0, n_half), i1 = tab_index(t1, n_half);
-      double e0 = __builtin_ldexp(T[i0 < 0 ? 0 : i0], sht);
-      double e1 = __builtin_ldexp(T[i1 < 0 ? 0 : i1], sht);
+      double e0 = __builtin_ldexp(Tt[i0 < 0 ? 0 : i0], sht);
+      double e1 = __builtin_ldexp(Tt[i1 < 0 ? 0 : i1], sht);
       if (W.residual) {
         const uint32_t d0 = rd[k] & 0xffffu, d1 = rd[k] >> 16;
         const int j0 = tab_index(d0, n_half), j1 = tab_index(d1, n_half);
-        double f0 = __builtin_ldexp(T[j0 < 0 ? 0 : j0], shd);
-        double f1 = __builtin_ldexp(T[j1 < 0 ? 0 : j1], shd);
+        double f0 = __builtin_ldexp(Td[j0 < 0 ? 0 : j0], shd);
+        double f1 = __builtin_ldexp(Td[j1 < 0 ? 0 : j1], shd);
         if ((i0 | i1 | j0 | j1) < 0) {
-          e0 = tab_fix(e0, i0, t0, W.c, W.Rt);
-          e1 = tab_fix(e1, i1, t1, W.c, W.Rt);
-          f0 = tab_fix(f0, j0, d0, W.c, W.Rd);
-          f1 = tab_fix(f1, j1, d1, W.c, W.Rd);
+          e0 = tab_fix(e0, i0, t0, W.c, W.Rt, W.thr_t);
+          e1 = tab_fix(e1, i1, t1, W.c, W.Rt, W.thr_t);
+          f0 = tab_fix(f0, j0, d0, W.c, W.Rd, W.thr_d);
+          f1 = tab_fix(f1, j1, d1, W.c, W.Rd, W.thr_d);
         }
         accum_pair(e0, f0, rho, E, Ed, A, Bd);
         accum_pair(e1, f1, rho, E, Ed, A, Bd);
       } else {
         if ((i0 | i1) < 0) {
-          e0 = tab_fix(e0, i0, t0, W.c, W.Rt);
-          e1 = tab_fix(e1, i1, t1, W.c, W.Rt);
+          e0 = tab_fix(e0, i0, t0, W.c, W.Rt, W.thr_t);
+          e1 = tab_fix(e1, i1, t1, W.c, W.Rt, W.thr_t);
         }
         E += e0;
         E += e1;
@@ -583,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void draw(
 #pragma unroll
     for (int k = 0; k < kTileChunksPerLane; ++k) {
       const long long ci = (long long)t * kTileChunks + (long long)k * kWave + lane;
-      if (ci < nchunks) accum_chunk<DT, VEC>(T, n_half, W, rt[k], rd[k], rho, E, Ed, A, Bd);
+      if (ci < nchunks) accum_chunk<DT, VEC>(T, T, n_half, W, rt[k], rd[k], rho, E, Ed, A, Bd);
     }
     E = wave_sum(E);
     if (W.residual) {

@@ -32,11 +32,11 @@ def _merge(parts):
 
 
 def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int = 256,
-               stops=None):
+               stops=None, trunc=None):
     """Run the oracle on the listed sequences of a generated input dict
     (host copies are made a chunk of sequences at a time). stops: optional
     (eos, draft_len [B] or None, max_emit [B] or None) with host arrays indexed
-    by batch row."""
+    by batch row; trunc: optional (top_k [B] or None, top_p [B] or None)."""
     rows = np.asarray(rows, dtype=np.int64)
     m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
     parts = []
@@ -52,6 +52,10 @@ def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int 
             eos, kb, mx = stops
             kw = dict(eos=eos, draft_len=None if kb is None else np.asarray(kb)[sub_rows],
                       max_emit=None if mx is None else np.asarray(mx)[sub_rows])
+        if trunc is not None:
+            tk, tp = trunc
+            kw.update(top_k=None if tk is None else np.asarray(tk)[sub_rows],
+                      top_p=None if tp is None else np.asarray(tp)[sub_rows])
         if ema is not None:
             # EMA slots are batch rows: feed the oracle a state indexed by row
             sub = O.EmaState(len(sub_rows), ema.decay)

@@ -1,0 +1,241 @@
+"""GPU parity of top-k / top-p truncation (bf16 rows) against the oracle.
+
+The truncated path is its own pass over the rows (an exact per-row value
+histogram) followed by the per-sequence finish with masked tables, so these
+tests cover: per-sequence mixes of settings (including settings that are off
+and invalid ones), values outside the finish's exponential table window,
+rows whose 16-bit histogram counters wrap, low temperatures (the scaled draw
+path), the stopping rules together with truncation, top_k = 1 against the
+greedy mode, and the headline shape on sampled sequences.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spec_oracle as O
+from tests.parity import compare, oracle_for
+from workloads import CONFIGS, make_inputs, to_host_f64, window_edge_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import speculative_decoding_verification_temp_amd as pkg
+    pkg.load_library()
+    torch.cuda.set_device(DEV)
+    return pkg
+
+
+def _settings(B, V, seed, invalid=False):
+    rng = np.random.default_rng(seed)
+    tk = rng.choice([0, 1, 2, 20, 50, 1000, V, V + 7, -3], B).astype(np.int32)
+    tp = rng.choice([1.0, 0.5, 0.8, 0.9, 0.95, 0.99, 1.5], B).astype(np.float32)
+    if invalid:
+        tp[1], tp[2] = 0.0, np.nan
+    return tk, tp
+
+
+def _resample_drafts(x, T, tk, tp, seed):
+    """Drafted tokens from each sequence's truncated draft distribution (the
+    draft sampler's law), drawn on the host."""
+    rng = np.random.default_rng(seed)
+    d = to_host_f64(x["draft"])
+    B, K, _ = d.shape
+    toks = np.zeros((B, K), dtype=np.int32)
+    for b in range(B):
+        p = float(tp[b]) if np.isfinite(tp[b]) and tp[b] > 0 else 1.0
+        for i in range(K):
+            q, _ = O.truncated_softmax(d[b, i], T, int(tk[b]), p)
+            toks[b, i] = rng.choice(q.size, p=q)
+    x["tokens"] = torch.as_tensor(toks, device=DEV).contiguous()
+
+
+def _run(sv, x, cfg, tk, tp, stops=None, decay=0.9, T=None):
+    T = cfg.T if T is None else T
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype, ema_decay=decay)
+    aux = v.enable_aux()
+    tk_d = None if tk is None else torch.as_tensor(tk, device=DEV).contiguous()
+    tp_d = None if tp is None else torch.as_tensor(tp, device=DEV).contiguous()
+    v.set_truncation(tk_d, tp_d)
+    if stops is not None:
+        eos, kb, mx = stops
+        v.set_stops(eos, None if kb is None else torch.as_tensor(kb, device=DEV).contiguous(),
+                    None if mx is None else torch.as_tensor(mx, device=DEV).contiguous())
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], T,
+                               "stochastic")
+    torch.cuda.synchronize()
+    return v, aux, tok, alen, hist
+
+
+def _check(sv, x, cfg, tk, tp, label, stops=None, T=None, rows=None):
+    v, aux, tok, alen, hist = _run(sv, x, cfg, tk, tp, stops=stops, T=T)
+    xT = dict(x)
+    if T is not None:
+        xT["T"] = T
+    rows = np.arange(cfg.B) if rows is None else np.asarray(rows)
+    ema = O.EmaState(cfg.B, 0.9)
+    ref = oracle_for(xT, rows, "stochastic", ema=ema, stops=stops, trunc=(tk, tp))
+    rep = compare(rows, ref, tok, alen, "stochastic", aux, label)
+    if len(rows) == cfg.B:
+        assert np.array_equal(hist.cpu().numpy(), ref.hist)
+        e, s = v.ema()
+        torch.cuda.synchronize()
+        assert np.array_equal(s.cpu().numpy(), ema.steps)
+        assert np.max(np.abs(e.cpu().numpy() - ema.ema)) <= 1e-12
+    print(f"{label}: {rep}", flush=True)
+    return tok, alen, ref
+
+
+def test_trunc_c2_per_sequence_settings(sv):
+    cfg = CONFIGS["c2"]
+    x = make_inputs(cfg, 1, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 1, invalid=True)
+    _resample_drafts(x, cfg.T, tk, tp, 2)
+    tok, alen, ref = _check(sv, x, cfg, tk, tp, "trunc/c2/mixed")
+    a = alen.cpu().numpy()
+    assert a[1] == -1 and a[2] == -1          # top_p = 0 and NaN
+    assert (a >= 0).sum() == cfg.B - 2
+
+
+@pytest.mark.parametrize("which", ["top_k", "top_p"])
+def test_trunc_c2_one_rule(sv, which):
+    cfg = CONFIGS["c2"].scaled(B=48)
+    x = make_inputs(cfg, 2, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 3)
+    if which == "top_k":
+        tp = None
+    else:
+        tk = None
+    _resample_drafts(x, cfg.T, tk if tk is not None else np.zeros(cfg.B, np.int32),
+                     tp if tp is not None else np.ones(cfg.B, np.float32), 4)
+    _check(sv, x, cfg, tk, tp, f"trunc/c2/{which}")
+
+
+def test_trunc_untruncated_drafts(sv):
+    """Drafts sampled from the untruncated draft: many fall outside the
+    draft's kept set (q(d) = 0, kept by the acceptance rule, counted)."""
+    cfg = CONFIGS["c2"].scaled(B=32)
+    x = make_inputs(cfg, 3, DEV)
+    tk = np.full(cfg.B, 30, np.int32)
+    tp = np.full(cfg.B, 0.9, np.float32)
+    _check(sv, x, cfg, tk, tp, "trunc/c2/raw drafts")
+
+
+def test_trunc_window_edges(sv):
+    cfg = CONFIGS["c2"].scaled(B=32)
+    x = window_edge_inputs(cfg, 4, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 5)
+    _resample_drafts(x, cfg.T, tk, tp, 6)
+    _check(sv, x, cfg, tk, tp, "trunc/window edges")
+
+
+def test_trunc_wrapped_counters(sv):
+    """More than 65535 equal values in a row: at the maximum (sequence 0,
+    a tie of 70000 kept tokens), below it (sequence 1), as -inf (sequence 2),
+    and next to a busy neighbour sharing its 32-bit counter word (sequence 3:
+    66000 at -2, 61256 at the next bf16 value up)."""
+    cfg = CONFIGS["c3"].scaled(B=4, K=3)
+    x = make_inputs(cfg, 5, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    V = cfg.V
+    for key in ("target", "draft"):
+        t = x[key]
+        for b in range(cfg.B):
+            for i in range(t.shape[1]):
+                perm = torch.randperm(V, generator=g, device=DEV)
+                if b == 0:
+                    t[b, i] = torch.minimum(t[b, i], torch.tensor(-1.0, device=DEV,
+                                                                  dtype=t.dtype))
+                    t[b, i, perm[:70000]] = 0.0
+                elif b == 1:
+                    t[b, i, perm[:70000]] = -4.0
+                elif b == 2:
+                    t[b, i, perm[:66000]] = float("-inf")
+                else:
+                    t[b, i, perm[:66000]] = -2.0
+                    t[b, i, perm[66000:V - 1000]] = -1.9921875   # next bf16 value up
+    tk = np.array([100, 50, 0, 70000], np.int32)
+    tp = np.array([0.9, 0.95, 0.9, 1.0], np.float32)
+    _resample_drafts(x, cfg.T, tk, tp, 7)
+    _check(sv, x, cfg, tk, tp, "trunc/wrapped counters")
+
+
+def test_trunc_low_temperature_scaled_path(sv):
+    cfg = CONFIGS["c2"].scaled(B=24)
+    x = make_inputs(cfg, 6, DEV)
+    T = 0.02                       # |x c| far above the unscaled range
+    tk, tp = _settings(cfg.B, cfg.V, 8)
+    _resample_drafts(x, T, tk, tp, 9)
+    _check(sv, x, cfg, tk, tp, "trunc/low temperature", T=T)
+
+
+def test_trunc_with_stops(sv):
+    cfg = CONFIGS["c2"].scaled(B=48)
+    x = make_inputs(cfg, 7, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 10)
+    _resample_drafts(x, cfg.T, tk, tp, 11)
+    rng = np.random.default_rng(12)
+    toks = x["tokens"].cpu().numpy()
+    eos = int(np.bincount(toks.ravel()).argmax())
+    kb = rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    mx = rng.integers(1, cfg.K + 3, cfg.B).astype(np.int32)
+    _check(sv, x, cfg, tk, tp, "trunc/stops", stops=(eos, kb, mx))
+
+
+def test_trunc_top_k_one_is_greedy(sv):
+    """top_k = 1 for every sequence, drafts at the draft argmax: the
+    stochastic path must give the greedy path's tokens on every sequence
+    whose needed rows have a unique maximum."""
+    cfg = CONFIGS["c2"].scaled(B=64)
+    x = make_inputs(cfg, 8, DEV, "greedy")
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    g_tok, g_len, _ = [t.clone() for t in v.verify(x["target"], x["draft"], x["tokens"],
+                                                   x["uniforms"], cfg.T, "greedy")]
+    v.set_truncation(torch.ones(cfg.B, dtype=torch.int32, device=DEV), None)
+    s_tok, s_len, _ = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T,
+                               "stochastic")
+    torch.cuda.synchronize()
+    t = x["target"].float()
+    d = x["draft"].float()
+    uniq = ((t == t.max(-1, keepdim=True).values).sum(-1) == 1).all(-1) & \
+           ((d == d.max(-1, keepdim=True).values).sum(-1) == 1).all(-1)
+    u = uniq.cpu().numpy()
+    assert u.sum() > cfg.B // 2
+    assert np.array_equal(s_tok.cpu().numpy()[u], g_tok.cpu().numpy()[u])
+    assert np.array_equal(s_len.cpu().numpy()[u], g_len.cpu().numpy()[u])
+
+
+def test_set_truncation_arguments(sv):
+    cfg = CONFIGS["c1"]
+    v32 = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32)
+    one = torch.ones(cfg.B, dtype=torch.int32, device=DEV)
+    assert v32.lib.spec_verify_set_truncation(v32._h, sv._ptr(one), None) == sv.SV_EUNSUPPORTED
+    assert v32.lib.spec_verify_set_truncation(v32._h, None, None) == sv.SV_OK
+    assert v32.lib.spec_verify_set_truncation(None, None, None) == sv.SV_EINVAL
+    cfg2 = CONFIGS["c2"].scaled(B=16)
+    x = make_inputs(cfg2, 9, DEV)
+    v = sv.SpecVerifier(cfg2.B, cfg2.K, cfg2.V, x["target"].dtype)
+    plain = [t.clone() for t in v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"],
+                                         cfg2.T)]
+    v.set_truncation(torch.full((cfg2.B,), 5, dtype=torch.int32, device=DEV), None)
+    v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg2.T)
+    v.clear_truncation()
+    again = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg2.T)
+    torch.cuda.synchronize()
+    assert torch.equal(plain[0], again[0]) and torch.equal(plain[1], again[1])
+
+
+def test_trunc_c3_sampled(sv):
+    """The headline shape (B = 256, K = 7, V = 128256) with top_k = 50 and
+    top_p = 0.9 on every sequence; the oracle checks 24 sampled sequences."""
+    cfg = CONFIGS["c3"]
+    x = make_inputs(cfg, 0, DEV)
+    tk = np.full(cfg.B, 50, np.int32)
+    tp = np.full(cfg.B, 0.9, np.float32)
+    rows = np.random.default_rng(13).choice(cfg.B, 24, replace=False)
+    _check(sv, x, cfg, tk, tp, "trunc/c3 sampled", rows=np.sort(rows))
