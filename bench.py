@@ -71,7 +71,7 @@ def traffic_for(workload: str, kernel: str):
 _W = {}
 
 
-def _worker_init(specs, T, mode, tau):
+def _worker_init(specs, T, mode, tau, trunc=(0, 1.0)):
     from multiprocessing import shared_memory
     import numpy as np
     from oracle import spec_oracle as O
@@ -84,6 +84,7 @@ def _worker_init(specs, T, mode, tau):
         _W["shm"].append(shm)
         _W[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
     _W["args"] = (T, mode, tau)
+    _W["trunc"] = trunc
     _W["O"] = O
 
 
@@ -93,13 +94,15 @@ def _worker_task(k):
     n = _W["tgt"].shape[0]
     q = k % n
     kb = _W["kb"]
+    tk, tp = _W["trunc"]
     r = O.verify_batch(_W["tgt"][q:q + 1], None if _W["drf"] is None else _W["drf"][q:q + 1],
                        _W["tok"][q:q + 1], _W["uni"][q:q + 1], T, mode, tau,
-                       draft_len=None if kb is None else kb[q:q + 1])
+                       draft_len=None if kb is None else kb[q:q + 1],
+                       top_k=[tk], top_p=[tp])
     return q, int(r.accept_len[0]), r.tokens[0].tolist(), float(r.min_dist[0])
 
 
-def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None):
+def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1.0)):
     """Time the fp64 CPU oracle on a bounded sample of the same workload, one
     sequence per task: first in this process on one core, then on a pool of
     worker processes (one per usable core, at most 16), about seconds/2 each,
@@ -138,7 +141,8 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None):
         r = O.verify_batch(arrays["tgt"][q:q + 1],
                            None if arrays["drf"] is None else arrays["drf"][q:q + 1],
                            arrays["tok"][q:q + 1], arrays["uni"][q:q + 1], cfg.T, m, cfg.tau,
-                           draft_len=None if kb is None else arrays["kb"][q:q + 1])
+                           draft_len=None if kb is None else arrays["kb"][q:q + 1],
+                           top_k=[trunc[0]], top_p=[trunc[1]])
         mism += check(q, int(r.accept_len[0]), r.tokens[0], float(r.min_dist[0]))
         n1 += 1
     t1 = time.perf_counter() - t0
@@ -160,7 +164,7 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None):
             specs[name] = (shm.name, a.shape, a.dtype.str)
         ctx = mp.get_context("spawn")
         with cf.ProcessPoolExecutor(nproc, mp_context=ctx, initializer=_worker_init,
-                                    initargs=(specs, cfg.T, m, cfg.tau)) as ex:
+                                    initargs=(specs, cfg.T, m, cfg.tau, trunc)) as ex:
             list(ex.map(_worker_task, range(nproc)))          # start-up, not timed
             nn, k = 0, 0
             t0 = time.perf_counter()
@@ -195,6 +199,11 @@ def main():
     ap.add_argument("--stops", default="none", choices=["none", "varlen"],
                     help="varlen: per-sequence draft counts k_b drawn uniformly from 1..K "
                          "(seeded), no end-of-sequence token, no budget")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="stochastic mode: top-k truncation of every target and draft row "
+                         "(every sequence); 0 = off")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="stochastic mode: top-p truncation after top-k; 1 = off")
     ap.add_argument("--read-probe", action="store_true",
                     help="also time a plain 2 GiB streaming read with the streaming pass's "
                          "access pattern (achievable-bandwidth reference)")
@@ -231,6 +240,10 @@ def main():
         kb = np.random.default_rng([20260923, cfg.index, 7]).integers(1, K + 1, B)
         kb_dev = torch.as_tensor(kb.astype(np.int32), device=dev).contiguous()
         v.set_stops(-1, kb_dev, None)
+    trunc = mode == "stochastic" and (0 < args.top_k < V or args.top_p < 1.0)
+    if trunc:
+        v.set_truncation(torch.full((B,), args.top_k, dtype=torch.int32, device=dev),
+                         torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
     out = (torch.empty((B, K + 1), dtype=torch.int32, device=dev),
            torch.empty((B,), dtype=torch.int32, device=dev),
            torch.empty((K + 1,), dtype=torch.int32, device=dev))
@@ -277,7 +290,8 @@ def main():
     pass_bytes = rows_total * V * s
     io_bytes = B * (K * 4 + (K + 1) * 4 + (K + 1) * 4 + 4) + 2 * B * K * s
     call_bytes = pass_bytes + sum(draw_bytes) / len(draw_bytes) + io_bytes
-    kernel = "rowstats_sum" if mode == "stochastic" else "rowstats_max"
+    kernel = ("rowstats_trunc" if trunc else "rowstats_sum") if mode == "stochastic" \
+        else "rowstats_max"
     achieved = pass_bytes / (pass_avg * 1e-3) / 1e9
     traffic = traffic_for(f"{cfg.name}/{mode}", kernel) if args.stops == "none" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -296,7 +310,8 @@ def main():
         "config": {"workload": f"{cfg.name} {mode}: B={B} K={K} V={V} {cfg.dtype} logits, "
                                f"T={cfg.T}" + (f", tau={cfg.tau}" if mode == "margin" else "")
                                + (", per-sequence draft counts 1..K" if args.stops == "varlen"
-                                  else ""),
+                                  else "")
+                               + (f", top-k {args.top_k}, top-p {args.top_p}" if trunc else ""),
                    "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU"},
         "achieved_hbm_gbs": round(call_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_of_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -345,8 +360,9 @@ def main():
             step(i)
             torch.cuda.synchronize()
             gpu_outs.append((out[0].cpu().numpy(), out[1].cpu().numpy()))
-        res["cpu_baseline"] = cpu_baseline(sets, gpu_outs, cfg, mode, args.cpu_seconds,
-                                           kb if args.stops == "varlen" else None)
+        res["cpu_baseline"] = cpu_baseline(
+            sets, gpu_outs, cfg, mode, args.cpu_seconds, kb if args.stops == "varlen" else None,
+            (args.top_k, float(np.float32(args.top_p))) if trunc else (0, 1.0))
     print(json.dumps(res), flush=True)
 
 

@@ -63,6 +63,13 @@ __device__ __forceinline__ uint32_t bf16_keys2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w ^ m) - neg);
 }
 
+// LDS word of histogram word w = key >> 1. Thread t of the scan owns words
+// 32t .. 32t + 31 (keys 64t .. 64t + 63), read as eight 16-byte chunks; the
+// chunks of each segment are permuted by the low 3 bits of t, so that when
+// every thread reads chunk q of its own segment the wavefront's reads spread
+// over all banks instead of landing on one.
+__device__ __forceinline__ uint32_t hist_word(uint32_t w) { return w ^ ((w >> 3) & 0x1cu); }
+
 // Counting modes: every key without looking, or (careful) only the even or
 // only the odd keys, recording wraps.
 enum { kCountFast = 0, kCountEven = 1, kCountOdd = 2 };
@@ -70,7 +77,7 @@ enum { kCountFast = 0, kCountEven = 1, kCountOdd = 2 };
 template <int MODE>
 __device__ __forceinline__ void count_key(uint32_t* H, uint32_t key, uint32_t* nwrap,
                                           uint32_t* wraps) {
-  const uint32_t w = key >> 1, sh = (key & 1u) << 4;
+  const uint32_t w = hist_word(key >> 1), sh = (key & 1u) << 4;
   if constexpr (MODE == kCountFast) {
     atomicAdd(&H[w], 1u << sh);
   } else {
@@ -205,24 +212,35 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
   const void* row = row_ptr<DT_BF16>(target, draft, b, r, K, V);
   const uint32_t k0 = uint32_t(tid) * kKeysPerThread;
 
-  // count of this thread's key k0 + i (i < 64): its 16-bit counter plus
-  // 65536 per wrap the careful count recorded for it
+  // The scan phase walks this thread's keys k0 .. k0 + 63 one 16-byte chunk
+  // (8 keys) at a time: chunk q holds the counts of keys k0 + 8q + e, e < 8,
+  // key k0 + 8q + 2i in the low and k0 + 8q + 2i + 1 in the high half of word
+  // i. A key that wrapped in the careful count has 65536 more per recorded
+  // wrap.
   uint32_t nwrap = 0;
-  auto cnt = [&](int i) -> uint32_t {
-    const uint32_t key = k0 + uint32_t(i);
-    uint32_t n = (H[key >> 1] >> ((key & 1u) << 4)) & 0xffffu;
-    if (nwrap != 0u) {
-      const int nw = min(int(nwrap), kMaxWraps);
+  auto chunk = [&](int q) -> u32x4 {
+    return reinterpret_cast<const u32x4*>(H)[tid * (kKeysPerThread / 8) + (q ^ (tid & 7))];
+  };
+  auto wrap_extra = [&](uint32_t key) -> uint32_t {
+    uint32_t n = 0;
+    const int nw = min(int(nwrap), kMaxWraps);
 #pragma unroll 1
-      for (int e = 0; e < nw; ++e) n += s_wraps[e] == key ? 65536u : 0u;
-    }
+    for (int e = 0; e < nw; ++e) n += s_wraps[e] == key ? 65536u : 0u;
     return n;
   };
   auto thread_total = [&]() -> uint32_t {
     nwrap = s_nwrap;
     uint32_t t = 0;
-#pragma unroll 4
-    for (int i = 0; i < kKeysPerThread; ++i) t += cnt(i);
+#pragma unroll 2
+    for (int q = 0; q < kKeysPerThread / 8; ++q) {
+      const u32x4 v = chunk(q);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t += (v[i] & 0xffffu) + (v[i] >> 16);
+    }
+    if (nwrap != 0u)
+#pragma unroll 1
+      for (int e = 0; e < min(int(nwrap), kMaxWraps); ++e)
+        t += (s_wraps[e] >> 6) == uint32_t(tid) ? 65536u : 0u;
     return t;
   };
 
@@ -236,17 +254,42 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
     n_t = thread_total();
     bad = tr_sum(n_t, s_u) != uint32_t(V) || nwrap > uint32_t(kMaxWraps);
   }
-  int top_t = 0;
-  bool nonfinite = false;
-#pragma unroll 4
-  for (int i = 0; i < kKeysPerThread; ++i) {
-    const uint32_t key = k0 + uint32_t(i), n = cnt(i);
-    if (n != 0u && key_finite(key)) top_t = int(key);
-    if (n != 0u && (key < kKeyNegInf || key >= kKeyPosInf)) nonfinite = true;
+  // bit i of nz: key k0 + i occurs in the row
+  uint64_t nz = 0;
+#pragma unroll 1
+  for (int q = 0; q < kKeysPerThread / 8; ++q) {
+    const u32x4 v = chunk(q);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bits |= ((v[i] & 0xffffu) ? 1u : 0u) << (2 * i) | ((v[i] >> 16) ? 2u : 0u) << (2 * i);
+    nz |= uint64_t(bits) << (8 * q);
   }
+  if (nwrap != 0u)
+#pragma unroll 1
+    for (int e = 0; e < min(int(nwrap), kMaxWraps); ++e)
+      if ((s_wraps[e] >> 6) == uint32_t(tid)) nz |= 1ull << (s_wraps[e] & 63u);
+  // finite keys of this thread (only the first and last few threads hold others)
+  uint64_t fin = ~0ull, nonfin = 0;
+  if (k0 <= kKeyNegInf || k0 + uint32_t(kKeysPerThread - 1) >= kKeyPosInf) {
+    fin = 0;
+#pragma unroll 1
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const uint32_t key = k0 + uint32_t(i);
+      if (key_finite(key)) fin |= 1ull << i;
+      if (key < kKeyNegInf || key >= kKeyPosInf) nonfin |= 1ull << i;
+    }
+  }
+  const int top_t = (nz & fin) ? int(k0) + 63 - __builtin_clzll(nz & fin) : 0;
   const int top = tr_max(top_t, s_i);
-  bad = bad || tr_max(nonfinite ? 1 : 0, s_i) != 0 || top == 0;
+  bad = bad || tr_max((nz & nonfin) ? 1 : 0, s_i) != 0 || top == 0;
   const float R = top > 0 ? ceilf(key_value(uint32_t(top)) * c) : 0.0f;
+  // count of key k0 + i from LDS
+  auto count_of = [&](int i) -> uint32_t {
+    const uint32_t key = k0 + uint32_t(i);
+    const uint32_t n = (H[hist_word(key >> 1)] >> ((key & 1u) << 4)) & 0xffffu;
+    return nwrap != 0u ? n + wrap_extra(key) : n;
+  };
 
   // ---- 2. top-k threshold from the counts ----
   const int kk = tr.k != nullptr ? tr.k[b] : 0;
@@ -257,9 +300,10 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
     const int cut = tr_max(above + n_t >= uint32_t(kk) ? tid : -1, s_i);
     if (tid == cut) {
       uint32_t acc = above;
-#pragma unroll 1
-      for (int i = kKeysPerThread - 1; i >= 0; --i) {
-        acc += cnt(i);
+      for (uint64_t m = nz; m != 0;) {
+        const int i = 63 - __builtin_clzll(m);
+        m &= ~(1ull << i);
+        acc += count_of(i);
         if (acc >= uint32_t(kk)) {
           s_key = k0 + uint32_t(i);
           break;
@@ -272,12 +316,16 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
   }
 
   // ---- 3. level masses at or above the top-k threshold, S_k ----
+  // The occurring finite keys at or above tk, largest first; the top-p walk
+  // below repeats the same operations in the same order.
+  const uint64_t ge = tk <= k0 ? ~0ull
+                      : tk > k0 + uint32_t(kKeysPerThread - 1) ? 0ull : (~0ull << (tk - k0));
+  const uint64_t live = nz & fin & ge;
   double M_t = 0.0;
-#pragma unroll 2
-  for (int i = kKeysPerThread - 1; i >= 0; --i) {
-    const uint32_t key = k0 + uint32_t(i), n = cnt(i);
-    if (n != 0u && key >= tk && key_finite(key))
-      M_t = __builtin_fma(double(n), level_term(key, c64, R), M_t);
+  for (uint64_t m = live; m != 0;) {
+    const int i = 63 - __builtin_clzll(m);
+    m &= ~(1ull << i);
+    M_t = __builtin_fma(double(count_of(i)), level_term(k0 + uint32_t(i), c64, R), M_t);
   }
   double S_k;
   const double above_m = tr_above(M_t, s_d, S_k);
@@ -293,16 +341,14 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
     if (cut >= 0) {
       if (tid == cut) {
         double part = 0.0;
-#pragma unroll 1
-        for (int i = kKeysPerThread - 1; i >= 0; --i) {
-          const uint32_t key = k0 + uint32_t(i), n = cnt(i);
-          if (n != 0u && key >= tk && key_finite(key)) {
-            part = __builtin_fma(double(n), level_term(key, c64, R), part);
-            if (above_m + part >= goal) {
-              s_key = key;
-              s_S = above_m + part;
-              break;
-            }
+        for (uint64_t m = live; m != 0;) {
+          const int i = 63 - __builtin_clzll(m);
+          m &= ~(1ull << i);
+          part = __builtin_fma(double(count_of(i)), level_term(k0 + uint32_t(i), c64, R), part);
+          if (above_m + part >= goal) {
+            s_key = k0 + uint32_t(i);
+            s_S = above_m + part;
+            break;
           }
         }
       }
