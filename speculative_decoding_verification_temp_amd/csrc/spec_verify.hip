@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -63,6 +64,7 @@ struct spec_verify_handle {
   sv::Trunc trunc{nullptr, nullptr};       // top-k / top-p truncation for later calls
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
+  int n_cu = 256;          // compute units of the device
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
   char err[256] = {0};
 };
@@ -174,8 +176,9 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
 }
 
 // Stochastic mode with top-k / top-p truncation (bf16 rows): the truncation
-// pass (one workgroup per needed row, exact value histogram) instead of the
-// streaming pass, then the per-sequence finish with masked tables.
+// passes instead of the streaming pass (the window pass over every needed
+// row, then the full-histogram pass over the rows it handed over, if any),
+// then the per-sequence finish with masked tables.
 template <int VEC>
 int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draft,
               const int32_t* tokens, const float* uniforms, float c, double c64,
@@ -187,9 +190,14 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
     return fail(h, SV_EUNSUPPORTED, "truncation needs V <= %d (bf16)",
                 sv::kFMaxTiles * sv::kTileChunks * VEC);
   prof_mark(h, 0, s);
-  hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(B * rows)), dim3(sv::kTrBlock), 0,
-                     s, target, draft, K, V, c, c64, h->trunc, h->stops.k, h->parts, hist);
-  int rc = check_launch(h, "rowstats_trunc");
+  hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>), dim3(unsigned(B * rows)), dim3(sv::kTwBlock),
+                     0, s, target, draft, K, V, c, c64, h->trunc, h->stops.k, h->parts, hist);
+  int rc = check_launch(h, "rowstats_trunc_win");
+  if (rc) return rc;
+  hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(std::min(B * rows, h->n_cu))),
+                     dim3(sv::kTrBlock), 0, s, target, draft, K, V, c, c64, h->trunc, h->stops.k,
+                     h->parts, (long long)B * rows);
+  rc = check_launch(h, "rowstats_trunc");
   prof_mark(h, 1, s);
   if (rc) return rc;
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
@@ -302,6 +310,10 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
     delete h;
     return SV_EHIP;
   }
+  int n_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device) ==
+          hipSuccess && n_cu > 0)
+    h->n_cu = n_cu;
   h->ntiles_max = div_up(V, sv::kTileChunks);   // scalar path has the most tiles
   const size_t n_parts = (size_t)max_batch * (2 * K + 1) * kMaxSeg;
   const size_t n_tiles = (size_t)max_batch * h->ntiles_max;

@@ -1,4 +1,4 @@
-// Top-k / top-p truncation pass over bf16 logit rows (gfx950).
+// Top-k / top-p truncation passes over bf16 logit rows (gfx950).
 //
 // p and q are the distributions the samplers really use, after temperature
 // and truncation, and the same truncation has to hold in the acceptance ratio,
@@ -8,11 +8,10 @@
 // and including the first level at which the kept mass reaches top_p of the
 // top-k mass.
 //
-// One 1024-thread workgroup per needed row (target rows 0..k_b, draft rows
-// 0..k_b-1) reads the row once and counts its values into an exact histogram
-// over the 65536 order-preserving 16-bit keys (bf16_key), held in LDS as
-// 16-bit counters, two to a 32-bit word (128 KiB). Every value of one level
-// has the same softmax term, so the histogram gives all the truncation needs:
+// Each needed row (target rows 0..k_b, draft rows 0..k_b-1) is read once and
+// its values counted into an exact histogram by value. Every value of one
+// level has the same softmax term, so the histogram gives all the truncation
+// needs:
 //   * the row maximum and the integer reference R = ceil(max * c);
 //   * top-k: the threshold is the level at which the count of values at or
 //     above it, from the top, first reaches k;
@@ -21,19 +20,28 @@
 //     top, first reaches top_p * S_k;
 //   * the truncated normaliser: the mass at or above the final threshold.
 // Output: one RowPart per row with S = truncated normaliser (relative to
-// 2^R), R, idx = threshold key. A row holding NaN or +inf, or without a
-// finite maximum, or a sequence whose top_p is not > 0, gets S = NaN, which
-// makes the sequence invalid in the scan.
+// 2^R), R, idx = threshold key (bf16_key order). A row holding NaN or +inf,
+// or without a finite maximum, or a sequence whose top_p is not > 0, gets
+// S = NaN, which makes the sequence invalid in the scan.
 //
-// A 16-bit counter wraps only when one value occurs more than 65535 times in
-// the row. The first count adds without looking; the counts are then summed
-// and compared with V. On a mismatch the row is counted again, in two passes
-// with returning atomics: first only the even keys (low halves), where a
-// wrap's carry into the still-empty high half is taken back at once, then
-// only the odd keys (high halves), whose carries leave the word. Each wrap is
-// recorded in a short list (65536 more for that key); as the halves are never
-// counted at the same time, no count sees another half's carry. A row that
-// still does not add up (more wraps than the list holds) is marked invalid.
+// Two passes share the work. The window pass (rowstats_trunc_win, at the end
+// of this file) takes every row whose values are all zeros, -inf or inside
+// the finish's table window 2^-25 <= |x| < 2^7: 8192 bins with 32-bit
+// counters in 32 KiB of LDS, so that several rows share a compute unit. It
+// marks any other row, and the full pass (rowstats_trunc) then counts those
+// rows over all 65536 16-bit keys: one 1024-thread workgroup per row, 16-bit
+// counters two to a 32-bit word (128 KiB).
+//
+// In the full pass a counter wraps only when one value occurs more than
+// 65535 times in the row. The first count adds without looking; the counts
+// are then summed and compared with V. On a mismatch the row is counted
+// again, in two passes with returning atomics: first only the even keys (low
+// halves), where a wrap's carry into the still-empty high half is taken back
+// at once, then only the odd keys (high halves), whose carries leave the
+// word. Each wrap is recorded in a short list (65536 more for that key); as
+// the halves are never counted at the same time, no count sees another
+// half's carry. A row that still does not add up (more wraps than the list
+// holds) is marked invalid.
 #pragma once
 
 #include "sv_fused.hpp"
@@ -45,6 +53,8 @@ constexpr int kTrWaves = kTrBlock / kWave;
 constexpr int kHistWords = 32768;                    // 65536 16-bit counters
 constexpr int kKeysPerThread = 65536 / kTrBlock;     // 64 consecutive keys per thread
 constexpr int kMaxWraps = 32;
+
+constexpr int kTruncRedo = 2;   // RowPart flag: the row needs the full-histogram pass
 
 // Truncation settings of one call, per sequence (null: that rule is off).
 struct Trunc {
@@ -133,8 +143,8 @@ __device__ __forceinline__ void count_row(const void* row, int V, uint32_t* H, u
   __syncthreads();
 }
 
-// ---- workgroup reductions over the 16 wavefronts (fixed order) ----
-template <typename T_>
+// ---- workgroup reductions over the NW wavefronts (fixed order) ----
+template <typename T_, int NW = kTrWaves>
 __device__ inline T_ tr_sum(T_ v, T_* s) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
 #pragma unroll
@@ -143,11 +153,12 @@ __device__ inline T_ tr_sum(T_ v, T_* s) {
   __syncthreads();
   T_ t = 0;
 #pragma unroll
-  for (int w = 0; w < kTrWaves; ++w) t += s[w];
+  for (int w = 0; w < NW; ++w) t += s[w];
   __syncthreads();
   return t;
 }
 
+template <int NW = kTrWaves>
 __device__ inline int tr_max(int v, int* s) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
 #pragma unroll
@@ -156,14 +167,14 @@ __device__ inline int tr_max(int v, int* s) {
   __syncthreads();
   int t = s[0];
 #pragma unroll
-  for (int w = 1; w < kTrWaves; ++w) t = max(t, s[w]);
+  for (int w = 1; w < NW; ++w) t = max(t, s[w]);
   __syncthreads();
   return t;
 }
 
 // Sum of v over the threads with a larger index (= the higher keys), and the
 // total over all threads.
-template <typename T_>
+template <typename T_, int NW = kTrWaves>
 __device__ inline T_ tr_above(T_ v, T_* s, T_& total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   T_ incl = v;      // sum over lanes lane..63 of this wavefront
@@ -178,7 +189,7 @@ __device__ inline T_ tr_above(T_ v, T_* s, T_& total) {
   __syncthreads();
   T_ hi = 0, tot = 0;
 #pragma unroll
-  for (int w = kTrWaves - 1; w >= 0; --w) {
+  for (int w = NW - 1; w >= 0; --w) {
     if (w > wid) hi += s[w];
     tot += s[w];
   }
@@ -188,10 +199,14 @@ __device__ inline T_ tr_above(T_ v, T_* s, T_& total) {
 }
 
 template <int VEC>
+// One workgroup per compute unit takes rows blockIdx.x, blockIdx.x +
+// gridDim.x, ... (nrows = B (2K + 1)): its threads first check up to 1024 of
+// them at once and list the ones the window pass handed over, then the
+// workgroup counts the listed rows one after another.
 __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
     double c64, Trunc tr, const int32_t* __restrict__ kdraft, RowPart* __restrict__ parts,
-    uint32_t* __restrict__ hist) {
+    long long nrows) {
   __shared__ uint32_t H[kHistWords];
   __shared__ uint32_t s_wraps[kMaxWraps];
   __shared__ uint32_t s_nwrap;
@@ -200,15 +215,31 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
   __shared__ double s_d[kTrWaves];
   __shared__ uint32_t s_key;
   __shared__ double s_S;
+  __shared__ long long s_rows[kTrBlock];
+  __shared__ int s_nrows;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
-  const long long grow = blockIdx.x;
-  const int b = int(grow / rows), r = int(grow % rows);
-  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
-  if (kdraft != nullptr) {           // rows past the draft count are not needed
-    const int kb = kdraft[b];
-    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  for (long long g0 = blockIdx.x; g0 < nrows; g0 += (long long)gridDim.x * kTrBlock) {
+  if (tid == 0) s_nrows = 0;
+  __syncthreads();
+  {
+    const long long cand = g0 + (long long)tid * gridDim.x;
+    if (cand < nrows) {
+      const int cb = int(cand / rows), cr = int(cand % rows);
+      bool need = true;              // rows past the draft count are not needed
+      if (kdraft != nullptr) {
+        const int kb = kdraft[cb];
+        need = !(cr <= K ? cr > kb : cr - K - 1 >= kb);
+      }
+      if (need && parts[cand].flags == kTruncRedo) s_rows[atomicAdd(&s_nrows, 1)] = cand;
+    }
   }
+  __syncthreads();
+  const int n_listed = s_nrows;
+  for (int li = 0; li < n_listed; ++li) {
+  const long long grow = s_rows[li];
+  const int b = int(grow / rows), r = int(grow % rows);
+  __syncthreads();                   // the previous row's scan is over
   const void* row = row_ptr<DT_BF16>(target, draft, b, r, K, V);
   const uint32_t k0 = uint32_t(tid) * kKeysPerThread;
 
@@ -363,6 +394,317 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
     p.R = R;
     p.m = 0.0f;
     p.idx = int(thr);
+    p.flags = 0;
+    parts[grow] = p;
+  }
+  }
+  __syncthreads();                   // the list is read before it is reset
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Window pass (the common case): one 512-thread workgroup per needed row
+// counts the row into 8192 bins with 32-bit counters (32 KiB of LDS, so that
+// several rows share a compute unit and one row's scan overlaps another's
+// reads). The bins ascend with the value: bin 0 holds -inf, bins 1 .. 3968
+// the negative values with 2^-24 <= |x| < 2^7 (one bin per value), bin 3969
+// the negative values with |x| < 2^-24, bin 3970 zero, bin 3971 the positive
+// values below 2^-24, bins 3972 .. 7939 the positive window values; bin 8191
+// counts every other value (|x| >= 2^7, +inf, NaN). The two bins of tiny
+// values hold several values each: their masses are summed value by value
+// in a second read of the row (only rows that have such values), and a row
+// whose maximum or threshold falls in one of them is handed over. A row with
+// a value in bin 8191 is handed over too: marked kTruncRedo and left to the
+// full-histogram pass above.
+// ---------------------------------------------------------------------------
+constexpr int kTwBlock = 512;
+constexpr int kTwWaves = kTwBlock / kWave;
+constexpr int kWinBins = 8192;
+constexpr int kBinsPerThread = kWinBins / kTwBlock;      // 16
+constexpr int kWinELo = 127 - 24;                        // smallest window exponent field
+constexpr int kWinHalf = 31 * 128;                       // 3968 window values per sign
+constexpr int kWinZero = kWinHalf + 2;                   // 3970
+constexpr int kTinyNeg = kWinZero - 1, kTinyPos = kWinZero + 1;
+constexpr int kWinOther = kWinBins - 1;
+constexpr uint32_t kTinyKey = 0xffffffffu;               // a cut inside a tiny-value bin
+
+// key (bf16_key order) of bin i < kWinOther outside the tiny-value bins
+__device__ inline uint32_t win_key(int i) {
+  if (i == 0) return kKeyNegInf;
+  if (i == kWinZero) return 0x8000u;
+  const uint32_t mag = uint32_t(i > kWinZero ? i - kTinyPos - 1 : kTinyNeg - 1 - i) +
+                       uint32_t(kWinELo << 7);
+  return i > kWinZero ? 0x8000u + mag : 0x8000u - mag;
+}
+
+// bin of one bf16 value, without branches
+__device__ __forceinline__ uint32_t win_bin(uint32_t bits) {
+  const uint32_t mag = bits & 0x7fffu;
+  const uint32_t off2 = mag - uint32_t((kWinELo << 7) - 2);          // window: 2 .. 3969
+  const int neg = int(bits << 16) >> 31;                              // 0 or -1
+  const uint32_t wb = uint32_t(kWinZero) + ((off2 ^ uint32_t(neg)) - uint32_t(neg));
+  const uint32_t tiny = uint32_t(kWinZero) + ((1u ^ uint32_t(neg)) - uint32_t(neg));
+  const uint32_t sp = mag == 0u ? uint32_t(kWinZero)
+                      : mag < uint32_t(kWinELo << 7) ? tiny
+                      : bits == 0xff80u ? 0u : uint32_t(kWinOther);
+  return off2 - 2u < uint32_t(kWinHalf) ? wb : sp;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
+    double c64, Trunc tr, const int32_t* __restrict__ kdraft, RowPart* __restrict__ parts,
+    uint32_t* __restrict__ hist) {
+  using C = Chunk<DT_BF16, VEC>;
+  __shared__ uint32_t H[kWinBins];
+  __shared__ uint32_t s_u[kTwWaves];
+  __shared__ int s_i[kTwWaves];
+  __shared__ double s_d[kTwWaves];
+  __shared__ uint32_t s_key;
+  __shared__ double s_S;
+  const int tid = threadIdx.x;
+  const int rows = 2 * K + 1;
+  const long long grow = blockIdx.x;
+  const int b = int(grow / rows), r = int(grow % rows);
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (kdraft != nullptr) {           // rows past the draft count are not needed
+    const int kb = kdraft[b];
+    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  }
+  const void* row = row_ptr<DT_BF16>(target, draft, b, r, K, V);
+
+  // ---- 1. count: groups of U chunks per thread, the next group's loads
+  // issued before the current group is counted ----
+  for (int i = tid; i < kWinBins / 4; i += kTwBlock)
+    reinterpret_cast<u32x4*>(H)[i] = (u32x4){0u, 0u, 0u, 0u};
+  __syncthreads();
+  {
+    constexpr int U = 4;
+    using raw_t = typename C::raw_t;
+    const long long nchunks = V / VEC;
+    const long long span = (long long)U * kTwBlock;
+    const long long first = nchunks - tid - (long long)(U - 1) * kTwBlock;
+    const long long G = first > 0 ? (first + span - 1) / span : 0;   // whole groups
+    auto load_group = [&](long long g, raw_t (&a)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = C::load(row, tid + g * span + (long long)u * kTwBlock);
+    };
+    // a chunk whose 8 values all lie in the window takes the short bin
+    // formula; any other chunk classifies each value
+    auto count_chunk = [&](const raw_t& raw) {
+      if constexpr (VEC == 8) {
+        uint32_t o2[8], worst = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu;
+          o2[e] = (bits & 0x7fffu) - uint32_t((kWinELo << 7) - 2);
+          worst = max(worst, o2[e] - 2u);
+        }
+        if (worst < uint32_t(kWinHalf)) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t neg = uint32_t(int(raw[e >> 1] << ((e & 1) ? 0 : 16)) >> 31);
+            atomicAdd(&H[uint32_t(kWinZero) + ((o2[e] ^ neg) - neg)], 1u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            atomicAdd(&H[win_bin((e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu)], 1u);
+        }
+      } else {
+        atomicAdd(&H[win_bin(raw)], 1u);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one chunk's bins at a time
+    };
+    if (G > 0) {
+      raw_t a[U];
+      load_group(0, a);
+      for (long long g = 0; g + 1 < G; ++g) {
+        raw_t n[U];
+        load_group(g + 1, n);
+#pragma unroll
+        for (int u = 0; u < U; ++u) count_chunk(a[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = n[u];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) count_chunk(a[u]);
+    }
+    for (long long ci = tid + G * span; ci < nchunks; ci += kTwBlock) count_chunk(C::load(row, ci));
+  }
+  __syncthreads();
+  // rows this pass does not finish go to the full pass (uniform decisions)
+  auto hand_over = [&]() {
+    if (tid == 0) {
+      RowPart p;
+      p.S = __builtin_nan("");
+      p.R = 0.0f;
+      p.m = 0.0f;
+      p.idx = 0;
+      p.flags = kTruncRedo;
+      parts[grow] = p;
+    }
+  };
+  if (H[kWinOther] != 0u) {          // values outside the window
+    hand_over();
+    return;
+  }
+  const bool tiny_vals = H[kTinyNeg] + H[kTinyPos] != 0u;
+
+  // ---- 2. this thread's levels: bins 16t + 15 down to 16t ----
+  const int bin0 = tid * kBinsPerThread;
+  uint32_t cnt[kBinsPerThread];
+#pragma unroll
+  for (int q = 0; q < kBinsPerThread / 4; ++q) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(H)[tid * (kBinsPerThread / 4) + q];
+    cnt[4 * q] = v[0];
+    cnt[4 * q + 1] = v[1];
+    cnt[4 * q + 2] = v[2];
+    cnt[4 * q + 3] = v[3];
+  }
+  uint32_t n_t = 0;
+  int top_t = -1;                    // highest occupied bin above -inf
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) {
+    n_t += cnt[j];
+    if (cnt[j] != 0u && bin0 + j > 0) top_t = bin0 + j;
+  }
+  const int top_bin = tr_max<kTwWaves>(top_t, s_i);
+  if (top_bin == kTinyNeg || top_bin == kTinyPos) {   // the maximum is a tiny value
+    hand_over();
+    return;
+  }
+  bool bad = top_bin < 0;            // no finite value
+  const float R = bad ? 0.0f : ceilf(key_value(win_key(top_bin)) * c);
+
+  // Masses of the tiny-value bins. Each such value's term is 2^(x c - R)
+  // with |x c| < 2^-24 c: for c <= 4 (temperatures above about 0.36) it is
+  // 2^-R to within 1.7e-7 relative, the level terms' own accuracy, and the
+  // bin mass is its count times 2^-R; otherwise every value's term is summed
+  // in a second read of the row.
+  double tmass[2] = {0.0, 0.0};      // [negative, positive]
+  if (tiny_vals && !bad && c64 <= 4.0) {
+    const double z = level_term(0x8000u, c64, R);
+    tmass[0] = __dmul_rn(double(H[kTinyNeg]), z);
+    tmass[1] = __dmul_rn(double(H[kTinyPos]), z);
+  } else if (tiny_vals && !bad) {
+    const long long nchunks = V / VEC;
+    double mn = 0.0, mp = 0.0;
+    for (long long ci = tid; ci < nchunks; ci += kTwBlock) {
+      const typename C::raw_t raw = C::load(row, ci);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        uint32_t bits;
+        if constexpr (VEC == 8)
+          bits = (e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu;
+        else
+          bits = raw;
+        const uint32_t mag = bits & 0x7fffu;
+        if (mag != 0u && mag < uint32_t(kWinELo << 7)) {
+          const double t = level_term(bf16_key(bits), c64, R);
+          if (bits & 0x8000u)
+            mn += t;
+          else
+            mp += t;
+        }
+      }
+    }
+    tmass[0] = tr_sum<double, kTwWaves>(mn, s_d);
+    tmass[1] = tr_sum<double, kTwWaves>(mp, s_d);
+  }
+  // mass of bin i at the reference R (rounded products and sums, so that
+  // the mass loop and the top-p walk give bitwise-equal partial sums)
+  auto bin_mass = [&](int i, uint32_t n) -> double {
+    if (i == kTinyNeg) return tmass[0];
+    if (i == kTinyPos) return tmass[1];
+    return __dmul_rn(double(n), level_term(win_key(i), c64, R));
+  };
+
+  // ---- 3. top-k threshold bin from the counts (one thread holds the cut) ----
+  const int kk = tr.k != nullptr ? tr.k[b] : 0;
+  int tk = 0;                        // smallest kept bin
+  if (kk >= 1 && kk < V) {
+    uint32_t n_all;
+    const uint32_t above = tr_above<uint32_t, kTwWaves>(n_t, s_u, n_all);
+    if (above < uint32_t(kk) && above + n_t >= uint32_t(kk)) {
+      uint32_t acc = above;
+      int cut = bin0;
+      bool found = false;
+#pragma unroll
+      for (int j = kBinsPerThread - 1; j >= 0; --j) {
+        acc += cnt[j];
+        if (!found && acc >= uint32_t(kk)) {
+          cut = bin0 + j;
+          found = true;
+        }
+      }
+      s_key = uint32_t(cut);
+    }
+    __syncthreads();
+    tk = int(s_key);
+    __syncthreads();
+    if (tk == kTinyNeg || tk == kTinyPos) {   // the k-th value is a tiny one
+      hand_over();
+      return;
+    }
+  }
+
+  // ---- 4. level masses at or above the top-k threshold, S_k (the top-p
+  // walk repeats these operations in the same order) ----
+  double M_t = 0.0;
+#pragma unroll
+  for (int j = kBinsPerThread - 1; j >= 0; --j) {
+    if (cnt[j] != 0u && bin0 + j > 0 && bin0 + j >= tk)
+      M_t = __dadd_rn(M_t, bin_mass(bin0 + j, cnt[j]));
+  }
+  double S_k;
+  const double above_m = tr_above<double, kTwWaves>(M_t, s_d, S_k);
+
+  // ---- 5. top-p threshold bin from the masses ----
+  const float pp = tr.p != nullptr ? tr.p[b] : 1.0f;
+  bad = bad || !(pp > 0.0f);
+  int thr = tk;
+  double S_tr = S_k;
+  if (pp < 1.0f && !bad) {
+    const double goal = double(pp) * S_k;
+    const int cut = tr_max<kTwWaves>(above_m + M_t >= goal ? tid : -1, s_i);
+    if (cut >= 0) {
+      if (tid == cut) {
+        double part = 0.0;
+        bool found = false;
+        int last = bin0;
+#pragma unroll
+        for (int j = kBinsPerThread - 1; j >= 0; --j) {
+          if (cnt[j] != 0u && bin0 + j > 0 && bin0 + j >= tk) {
+            part = __dadd_rn(part, bin_mass(bin0 + j, cnt[j]));
+            last = bin0 + j;
+            if (!found && above_m + part >= goal) {
+              s_key = uint32_t(bin0 + j);
+              s_S = above_m + part;
+              found = true;
+            }
+          }
+        }
+        if (!found) {                // equal partial sums make this unreachable
+          s_key = uint32_t(last);
+          s_S = above_m + part;
+        }
+      }
+      __syncthreads();
+      thr = int(s_key);
+      S_tr = s_S;
+      if (thr == kTinyNeg || thr == kTinyPos) {   // the top-p cut is inside a tiny bin
+        hand_over();
+        return;
+      }
+    }
+  }
+  if (tid == 0) {
+    RowPart p;
+    p.S = bad ? __builtin_nan("") : S_tr;
+    p.R = R;
+    p.m = 0.0f;
+    p.idx = int(win_key(thr));
     p.flags = 0;
     parts[grow] = p;
   }

@@ -133,11 +133,15 @@ def test_trunc_window_edges(sv):
     _check(sv, x, cfg, tk, tp, "trunc/window edges")
 
 
-def test_trunc_wrapped_counters(sv):
+@pytest.mark.parametrize("which_pass", ["window", "full"])
+def test_trunc_wrapped_counters(sv, which_pass):
     """More than 65535 equal values in a row: at the maximum (sequence 0,
     a tie of 70000 kept tokens), below it (sequence 1), as -inf (sequence 2),
-    and next to a busy neighbour sharing its 32-bit counter word (sequence 3:
-    66000 at -2, 61256 at the next bf16 value up)."""
+    and next to a busy neighbour sharing its 32-bit counter word in the full
+    pass (sequence 3: 66000 at -2, 61256 at the next bf16 value up). With
+    which_pass = "full" every row also holds one value of magnitude 2^-30
+    (outside the window pass's bins), so the rows go through the full
+    pass's 16-bit counters and their careful recount."""
     cfg = CONFIGS["c3"].scaled(B=4, K=3)
     x = make_inputs(cfg, 5, DEV)
     g = torch.Generator(device=DEV)
@@ -159,10 +163,71 @@ def test_trunc_wrapped_counters(sv):
                 else:
                     t[b, i, perm[:66000]] = -2.0
                     t[b, i, perm[66000:V - 1000]] = -1.9921875   # next bf16 value up
+                if which_pass == "full":
+                    t[b, i, perm[V - 1]] = 2.0 ** -30
     tk = np.array([100, 50, 0, 70000], np.int32)
     tp = np.array([0.9, 0.95, 0.9, 1.0], np.float32)
     _resample_drafts(x, cfg.T, tk, tp, 7)
-    _check(sv, x, cfg, tk, tp, "trunc/wrapped counters")
+    _check(sv, x, cfg, tk, tp, f"trunc/wrapped counters/{which_pass}")
+
+
+@pytest.mark.parametrize("T", [0.8, 0.1])
+def test_trunc_tiny_values(sv, T):
+    """Values with 0 < |x| < 2^-24 share two bins of the window pass, whose
+    masses are then summed value by value; a row whose maximum, top-k cut or
+    top-p cut falls among them is handed to the full pass. Sequences 0-7:
+    a few tiny values per row (thresholds elsewhere); 8-15: rows of tiny
+    values and zeros only (maximum tiny); 16-23: 50 values in [0.5, 3], the
+    tiny ones, the rest <= -1, and a top-k cut inside the tiny values;
+    24-31: plain rows. At T = 0.8 the tiny bins' masses are count * 2^-R,
+    at T = 0.1 they are summed value by value in a second read."""
+    cfg = CONFIGS["c2"].scaled(B=32)
+    x = make_inputs(cfg, 11, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    tk = np.zeros(cfg.B, np.int32)
+    tp = np.ones(cfg.B, np.float32)
+    for key in ("target", "draft"):
+        t = x[key]
+        for b in range(24):
+            for i in range(t.shape[1]):
+                perm = torch.randperm(cfg.V, generator=g, device=DEV)
+                sgn = torch.where(torch.rand(200, generator=g, device=DEV) < 0.5, -1.0, 1.0)
+                tiny = sgn * 2.0 ** (-30.0 - 20.0 * torch.rand(200, generator=g, device=DEV))
+                if b < 8:
+                    t[b, i, perm[:200]] = tiny.to(t.dtype)
+                elif b < 16:
+                    t[b, i] = 0.0
+                    t[b, i, perm[:200]] = tiny.to(t.dtype)
+                else:
+                    t[b, i] = torch.minimum(t[b, i], torch.tensor(-1.0, device=DEV, dtype=t.dtype))
+                    t[b, i, perm[:200]] = tiny.to(t.dtype)
+                    t[b, i, perm[200:250]] = (0.5 + 2.5 * torch.rand(50, generator=g, device=DEV)
+                                              ).to(t.dtype)
+    tk[:8], tp[:8] = 40, 0.9
+    tk[8:16], tp[8:16] = 0, 0.5
+    tk[16:24] = 150                  # inside the 200 tiny values
+    tk[24:], tp[24:] = 30, 0.8
+    _resample_drafts(x, T, tk, tp, 18)
+    _check(sv, x, cfg, tk, tp, f"trunc/tiny values/T={T}", T=T)
+
+
+def test_trunc_mixed_passes(sv):
+    """One batch whose rows split between the two passes: in half of the
+    sequences a single row holds one value outside the window (a tiny
+    magnitude, a huge one, +150 dominating the row, or -3e38)."""
+    cfg = CONFIGS["c2"].scaled(B=32)
+    x = make_inputs(cfg, 10, DEV)
+    specials = [2.0 ** -30, -2.0 ** -40, -200.0, 150.0, -3.0e38]
+    rng = np.random.default_rng(14)
+    for b in range(0, cfg.B, 2):
+        key = "target" if rng.random() < 0.5 else "draft"
+        i = int(rng.integers(0, x[key].shape[1]))
+        v = int(rng.integers(0, cfg.V))
+        x[key][b, i, v] = specials[(b // 2) % len(specials)]
+    tk, tp = _settings(cfg.B, cfg.V, 15)
+    _resample_drafts(x, cfg.T, tk, tp, 16)
+    _check(sv, x, cfg, tk, tp, "trunc/mixed passes")
 
 
 def test_trunc_low_temperature_scaled_path(sv):
