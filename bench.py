@@ -27,7 +27,7 @@ if ROOT not in sys.path:
 
 METRIC = "verified seqs/sec + achieved HBM GB/s (% of MI355X peak), V=128256 B=256 K=7"
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rowstats_sum_c3.json")
+PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "speculative_decoding_verification_temp_amd", "csrc")
 
 
@@ -35,13 +35,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-# the sources that define the streaming kernels whose traffic is recorded
-STREAM_SOURCES = ("sv_device.hpp", "sv_rowstats.hpp")
+# the sources that define each streaming kernel whose traffic is recorded
+STREAM_SOURCES = {
+    "rowstats_sum": ("sv_device.hpp", "sv_rowstats.hpp"),
+    "rowstats_max": ("sv_device.hpp", "sv_rowstats.hpp"),
+    "rowstats_trunc_win": ("sv_device.hpp", "sv_rowstats.hpp", "sv_kernels.hpp", "sv_fused.hpp",
+                           "sv_trunc.hpp"),
+}
 
 
-def source_digest() -> str:
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{kernel}_{workload.replace('/', '_')}.json")
+
+
+def source_digest(kernel: str = "rowstats_sum") -> str:
     h = hashlib.sha256()
-    for name in STREAM_SOURCES:
+    for name in STREAM_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -52,11 +61,11 @@ def traffic_for(workload: str, kernel: str):
     """HBM bytes per dispatch from committed rocprofv3 counter runs, or None
     when they were taken on other kernel source or another workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel, workload)) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_digest") != source_digest() or t.get("workload") != workload \
+    if t.get("source_digest") != source_digest(kernel) or t.get("workload") != workload \
             or t.get("kernel") != kernel:
         return None
     fetch = t["fetch_kib_per_dispatch"] * 1024.0 * t["copy_factor_fetch"]
@@ -290,10 +299,11 @@ def main():
     pass_bytes = rows_total * V * s
     io_bytes = B * (K * 4 + (K + 1) * 4 + (K + 1) * 4 + 4) + 2 * B * K * s
     call_bytes = pass_bytes + sum(draw_bytes) / len(draw_bytes) + io_bytes
-    kernel = ("rowstats_trunc" if trunc else "rowstats_sum") if mode == "stochastic" \
+    kernel = ("rowstats_trunc_win" if trunc else "rowstats_sum") if mode == "stochastic" \
         else "rowstats_max"
     achieved = pass_bytes / (pass_avg * 1e-3) / 1e9
-    traffic = traffic_for(f"{cfg.name}/{mode}", kernel) if args.stops == "none" else None
+    workload = f"{cfg.name}/{mode}" + (f"/top-k{args.top_k}-top-p{args.top_p}" if trunc else "")
+    traffic = traffic_for(workload, kernel) if args.stops == "none" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "kernel": kernel,

@@ -225,7 +225,8 @@ int spec_verify_get_stats(spec_verify_handle *h, spec_verify_stats *out, int res
 /*
  * Profiling. With enable != 0, each later spec_verify call records HIP events
  * on its stream just before and just after its streaming pass over the logits
- * (up to 4096 calls between reads; later calls are not recorded), and with
+ * (with truncation: the window pass of the truncation passes) (up to 4096
+ * calls between reads; later calls are not recorded), and with
  * bit 1 of enable set (enable = 2 or 3) also after its last kernel. The events
  * are timing-only (no system-scope fence) and created here, never in
  * spec_verify. spec_verify_profile_read waits for the recorded calls to finish

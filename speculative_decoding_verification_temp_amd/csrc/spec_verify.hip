@@ -193,13 +193,12 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
   hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>), dim3(unsigned(B * rows)), dim3(sv::kTwBlock),
                      0, s, target, draft, K, V, c, c64, h->trunc, h->stops.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_trunc_win");
+  prof_mark(h, 1, s);
   if (rc) return rc;
   hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(std::min(B * rows, h->n_cu))),
                      dim3(sv::kTrBlock), 0, s, target, draft, K, V, c, c64, h->trunc, h->stops.k,
                      h->parts, (long long)B * rows);
-  rc = check_launch(h, "rowstats_trunc");
-  prof_mark(h, 1, s);
-  if (rc) return rc;
+  if ((rc = check_launch(h, "rowstats_trunc"))) return rc;
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                      uniforms, c, c64, tab_half(c64), h->stops, out_tokens, out_len, hist, h->ema,
