@@ -79,6 +79,18 @@ listed with its reason in the design notes):
     ratio, the residual and the bonus draw. top_k <= 0 or >= V and
     top_p >= 1 mean no truncation; top_p <= 0 or NaN makes the sequence
     invalid.
+  * Tree-shape policy ([MNW] s.3, dynamic draft tree-shaping), optional,
+    after the EMA update of each sequence: a draft confidence score
+    DCS = min(1, conf * acc / d) from the draft's top-1 probability conf
+    (supplied by the caller, in [0, 1]), the slot's rolling acceptance acc
+    (the EMA; [MNW]'s alpha = 0.3 is decay 0.7) and a saturation divisor d > 0
+    (the pages give neither the combination nor d: this product is a reading,
+    and the part of the policy that is parity-unpinned). The next shape
+    (nsteps, top-k, ndt) interpolates linearly from (3, 4, 4) at DCS = 0 to
+    (7, 1, 8) at DCS = 1, each rounded half up. Five consecutive zero-accept
+    steps (accept_len = 0 with k_b > 0) restore the starting shape (3, 4, 4)
+    and restart the slot's EMA. Invalid sequences and conf outside [0, 1]
+    give shape (-1, -1, -1) and leave the policy state alone.
 """
 
 from __future__ import annotations
@@ -412,6 +424,43 @@ class EmaState:
         self.steps[slot] += 1
 
 
+START_SHAPE = (3, 4, 4)      # (nsteps, top-k, ndt): wide and shallow
+DEEP_SHAPE = (7, 1, 8)       # deep and narrow
+BREAKER_STEPS = 5
+
+
+def shape_for(dcs: float):
+    """(nsteps, top-k, ndt) at confidence dcs in [0, 1]: each component moves
+    linearly from START_SHAPE to DEEP_SHAPE, rounded half up."""
+    return tuple(int(math.floor(a + (b - a) * dcs + 0.5)) for a, b in zip(START_SHAPE, DEEP_SHAPE))
+
+
+class TreePolicy:
+    """Per-slot tree-shape policy state (the zero-accept streak) and step."""
+
+    def __init__(self, n_slots: int, d: float):
+        self.d = float(d)
+        self.streak = np.zeros(n_slots, dtype=np.int64)
+
+    def step(self, ema: EmaState, slot: int, valid: bool, accept_len: int, draft_len: int,
+             conf: float):
+        """Shape for the next step of `slot`, after its EMA update; returns
+        (shape, dcs)."""
+        conf = float(conf)
+        if not valid or not (0.0 <= conf <= 1.0):
+            return (-1, -1, -1), math.nan
+        if draft_len > 0:
+            self.streak[slot] = self.streak[slot] + 1 if accept_len == 0 else 0
+        if self.streak[slot] >= BREAKER_STEPS:
+            self.streak[slot] = 0
+            ema.ema[slot] = 0.0
+            ema.steps[slot] = 0
+            return START_SHAPE, 0.0
+        acc = ema.ema[slot] if ema.steps[slot] > 0 else 0.0
+        dcs = min(1.0, conf * acc / self.d)
+        return shape_for(dcs), dcs
+
+
 @dataclass
 class BatchResult:
     tokens: np.ndarray        # [B, K+1] int64
@@ -425,12 +474,15 @@ class BatchResult:
     zero_q_accepts: int
     z0_fallbacks: int
     invalid: int
+    shape: np.ndarray = None  # [B, 3] next tree shape (policy only)
+    dcs: np.ndarray = None    # [B] draft confidence score (policy only)
 
 
 def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
                  tau: float = 0.0, ema: EmaState | None = None,
                  rows=None, eos: int = -1, draft_len=None, max_emit=None,
-                 top_k=None, top_p=None) -> BatchResult:
+                 top_k=None, top_p=None, policy: TreePolicy | None = None,
+                 conf=None) -> BatchResult:
     """Verify every sequence b (or only those listed in `rows`).
 
     target [B, K+1, V], draft [B, K, V] (stochastic), tokens [B, K],
@@ -438,7 +490,9 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
     float64 one sequence at a time. When `ema` is given, slot b is updated
     for every valid verified sequence b with k_b > 0. eos, draft_len [B] and
     max_emit [B] (indexed by b) are the optional stopping rules, top_k [B]
-    and top_p [B] the optional truncation.
+    and top_p [B] the optional truncation. With `policy` (which needs `ema`)
+    and conf [B] (the draft's top-1 probabilities), each sequence's next
+    tree shape is computed after its EMA update.
     """
     B = target.shape[0]
     K = target.shape[1] - 1
@@ -452,6 +506,9 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
         z=np.full(n, -1.0), argmax=np.full((n, K + 1), -1, dtype=np.int64),
         min_dist=np.full(n, math.inf), zero_q_accepts=0, z0_fallbacks=0,
         invalid=0)
+    if policy is not None:
+        out.shape = np.full((n, 3), -1, dtype=np.int64)
+        out.dcs = np.full(n, math.nan)
     for k, b in enumerate(idx):
         res = verify_sequence(
             target[b],
@@ -478,4 +535,8 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
                 ema.observe(b, res.accept_len / res.draft_len)
         else:
             out.invalid += 1
+        if policy is not None:
+            shape, dcs = policy.step(ema, b, res.valid, res.accept_len, res.draft_len, conf[b])
+            out.shape[k] = shape
+            out.dcs[k] = dcs
     return out
