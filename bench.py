@@ -213,6 +213,8 @@ def main():
                          "(every sequence); 0 = off")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="stochastic mode: top-p truncation after top-k; 1 = off")
+    ap.add_argument("--policy", action="store_true",
+                    help="run the tree-shape policy epilogue (seeded draft confidences, d = 0.5)")
     ap.add_argument("--read-probe", action="store_true",
                     help="also time a plain 2 GiB streaming read with the streaming pass's "
                          "access pattern (achievable-bandwidth reference)")
@@ -253,6 +255,9 @@ def main():
     if trunc:
         v.set_truncation(torch.full((B,), args.top_k, dtype=torch.int32, device=dev),
                          torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
+    if args.policy:
+        conf = np.random.default_rng([20260923, cfg.index, 8]).uniform(0.0, 1.0, B)
+        v.set_policy(torch.as_tensor(conf.astype(np.float32), device=dev), 0.5)
     out = (torch.empty((B, K + 1), dtype=torch.int32, device=dev),
            torch.empty((B,), dtype=torch.int32, device=dev),
            torch.empty((K + 1,), dtype=torch.int32, device=dev))
@@ -321,7 +326,8 @@ def main():
                                f"T={cfg.T}" + (f", tau={cfg.tau}" if mode == "margin" else "")
                                + (", per-sequence draft counts 1..K" if args.stops == "varlen"
                                   else "")
-                               + (f", top-k {args.top_k}, top-p {args.top_p}" if trunc else ""),
+                               + (f", top-k {args.top_k}, top-p {args.top_p}" if trunc else "")
+                               + (", tree-shape policy" if args.policy else ""),
                    "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU"},
         "achieved_hbm_gbs": round(call_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_of_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -211,6 +211,38 @@ int spec_verify_set_stops(spec_verify_handle *h, int eos_token, const int32_t *d
 int spec_verify_set_truncation(spec_verify_handle *h, const int32_t *top_k,
                                const float *top_p);
 
+/*
+ * Tree-shape policy epilogue for later spec_verify calls on this handle
+ * ([MNW] s.3, dynamic draft tree-shaping: a draft confidence score combines
+ * the draft's top-1 probability with the rolling acceptance history and picks
+ * the next step's (nsteps, top-k, ndt) between (3, 4, 4) and (7, 1, 8); five
+ * consecutive zero-accept steps restore the starting configuration). After
+ * each sequence's EMA update (the rolling acceptance; [MNW]'s alpha = 0.3 is
+ * ema_decay = 0.7 at spec_verify_init):
+ *
+ *   DCS_b = min(1, draft_conf[b] * ema_b / d)   (ema_b = 0 before the first
+ *                                                observation of slot b)
+ *   shape = (3 + 4 DCS, 4 - 3 DCS, 4 + 4 DCS), each rounded half up;
+ *   after five consecutive calls with accept_len = 0 (and k_b > 0) the slot's
+ *   EMA restarts and the shape is (3, 4, 4).
+ *
+ * The pages give neither the combination nor d; this product is the reading
+ * taken. Arguments (device pointers sized for max_batch, caller-owned, read
+ * or written during later calls):
+ *   draft_conf  [max_batch] float32: the draft's top-1 probability for this
+ *               cycle, in [0, 1]; NULL turns the policy off
+ *   d           saturation divisor, finite and > 0
+ *   out_shape   [max_batch][3] int32: nsteps, top-k, ndt for the next step;
+ *               (-1, -1, -1) for invalid sequences or draft_conf outside
+ *               [0, 1], whose state is left alone
+ *   out_dcs     [max_batch] float64 score, or NULL
+ * The zero-accept streaks live in the handle; spec_verify_reset_ema clears
+ * them with the EMA. Returns SV_EINVAL for a NULL handle, a NULL out_shape
+ * with draft_conf set, a bad d or a misaligned array.
+ */
+int spec_verify_set_policy(spec_verify_handle *h, const float *draft_conf, double d,
+                           int32_t *out_shape, double *out_dcs);
+
 /* EMA state accessors, ordered on `stream`. Device pointers of max_batch entries. */
 int spec_verify_get_ema(spec_verify_handle *h, double *ema_dev, int32_t *steps_dev,
                         hipStream_t stream);

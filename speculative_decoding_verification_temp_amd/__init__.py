@@ -23,7 +23,7 @@ _ERRNAMES = {-1: "SV_EINVAL", -2: "SV_EUNSUPPORTED", -3: "SV_ENOMEM", -4: "SV_EH
 
 EXPORTED = (
     "spec_verify_init", "spec_verify", "spec_verify_destroy", "spec_verify_set_aux",
-    "spec_verify_set_stops", "spec_verify_set_truncation",
+    "spec_verify_set_stops", "spec_verify_set_truncation", "spec_verify_set_policy",
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
     "spec_verify_last_error", "spec_verify_version", "spec_verify_read_probe",
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify_set_aux.argtypes = [vp, vp, vp, vp, vp]
     L.spec_verify_set_stops.argtypes = [vp, i32, vp, vp]
     L.spec_verify_set_truncation.argtypes = [vp, vp, vp]
+    L.spec_verify_set_policy.argtypes = [vp, vp, ctypes.c_double, vp, vp]
     L.spec_verify_get_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_set_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_reset_ema.argtypes = [vp, vp]
@@ -198,6 +199,30 @@ class SpecVerifier:
 
     def clear_truncation(self):
         self.set_truncation(None, None)
+
+    def set_policy(self, draft_conf, d: float = 0.5, want_dcs: bool = False):
+        """Tree-shape policy for later calls: draft_conf is a float32 device
+        tensor of at least max_batch draft top-1 probabilities (or None to
+        turn the policy off). Returns (shape [max_batch, 3] int32, dcs
+        [max_batch] float64 or None), device tensors the calls write."""
+        if draft_conf is None:
+            self._check(self.lib.spec_verify_set_policy(self._h, None, 1.0, None, None),
+                        "set_policy")
+            self._policy = None
+            return None
+        if (draft_conf.dtype != torch.float32 or draft_conf.device != self.device
+                or not draft_conf.is_contiguous() or draft_conf.numel() < self.max_batch):
+            raise ValueError("draft_conf must be a contiguous float32 device tensor of at least "
+                             "max_batch entries")
+        shape = torch.full((self.max_batch, 3), -1, dtype=torch.int32, device=self.device)
+        dcs = (torch.full((self.max_batch,), float("nan"), dtype=torch.float64,
+                          device=self.device) if want_dcs else None)
+        self._check(self.lib.spec_verify_set_policy(self._h, _ptr(draft_conf), float(d),
+                                                    _ptr(shape),
+                                                    None if dcs is None else _ptr(dcs)),
+                    "set_policy")
+        self._policy = (draft_conf, shape, dcs)
+        return shape, dcs
 
     # -- verification --
     def _check_logits(self, t, rows, name):

@@ -51,6 +51,7 @@ struct spec_verify_handle {
   int finish_seq = 1;                 // scan + draw + pick in one kernel after the streaming pass
   double* ema = nullptr;
   int32_t* steps = nullptr;
+  int32_t* streak = nullptr;          // tree-shape policy state, per slot
   sv::DevStats* stats = nullptr;
   int ntiles_max = 0;
   unsigned long long calls = 0;
@@ -60,7 +61,7 @@ struct spec_verify_handle {
   int32_t* aux_argmax = nullptr;
   hipEvent_t* prof_ev = nullptr;   // 3 events per recorded call
   bool prof_call_end = false;      // also record the end of each call
-  sv::Stops stops{nullptr, nullptr, -1};   // stopping rules for later calls
+  sv::Rules rules{};   // stopping rules and tree-shape policy for later calls
   sv::Trunc trunc{nullptr, nullptr};       // top-k / top-p truncation for later calls
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
@@ -104,7 +105,7 @@ Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
   if (max_nseg > kMaxSeg) max_nseg = kMaxSeg;
   // with per-sequence draft counts some (row, segment) workgroups exit at
   // once; four times as many, shorter ones keep the other rows evenly spread
-  const long long target = (long long)h->target_wgs * (h->stops.k != nullptr ? 4 : 1);
+  const long long target = (long long)h->target_wgs * (h->rules.k != nullptr ? 4 : 1);
   int nseg = h->nseg_force > 0 ? h->nseg_force : div_up(target, (long long)B * rows);
   if (nseg > max_nseg) nseg = max_nseg;
   if (nseg < 1) nseg = 1;
@@ -148,20 +149,20 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   prof_mark(h, 0, s);
   hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
                      dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                     h->stops.k, h->parts, hist);
+                     h->rules.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
   if (h->finish_seq && L.ntiles <= sv::kFMaxTiles && rows <= sv::kFMaxRows) {
     hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock, false>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
-                       h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->stops,
+                       h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
                        out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p,
                        h->aux_q, h->aux_z);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
-                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, h->stops, out_tokens,
+                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, h->rules, out_tokens,
                      out_len, hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
                      h->aux_z, tab ? h->table : nullptr, n_half, c64);
   if ((rc = check_launch(h, "scan_stochastic"))) return rc;
@@ -191,17 +192,17 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
                 sv::kFMaxTiles * sv::kTileChunks * VEC);
   prof_mark(h, 0, s);
   hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>), dim3(unsigned(B * rows)), dim3(sv::kTwBlock),
-                     0, s, target, draft, K, V, c, c64, h->trunc, h->stops.k, h->parts, hist);
+                     0, s, target, draft, K, V, c, c64, h->trunc, h->rules.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_trunc_win");
   prof_mark(h, 1, s);
   if (rc) return rc;
   hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(std::min(B * rows, h->n_cu))),
-                     dim3(sv::kTrBlock), 0, s, target, draft, K, V, c, c64, h->trunc, h->stops.k,
+                     dim3(sv::kTrBlock), 0, s, target, draft, K, V, c, c64, h->trunc, h->rules.k,
                      h->parts, (long long)B * rows);
   if ((rc = check_launch(h, "rowstats_trunc"))) return rc;
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
-                     uniforms, c, c64, tab_half(c64), h->stops, out_tokens, out_len, hist, h->ema,
+                     uniforms, c, c64, tab_half(c64), h->rules, out_tokens, out_len, hist, h->ema,
                      h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z);
   return check_launch(h, "finish_seq (truncated)");
 }
@@ -217,7 +218,7 @@ int run_fused(spec_verify_handle* h, int B, const void* target, const void* draf
   int rc = check_launch(h, "zero_hist");
   if (rc) return rc;
   hipLaunchKernelGGL((sv::verify_fused<DT, VEC, U>), dim3(B), dim3(sv::kFBlock), 0, s, K, V,
-                     target, draft, tokens, uniforms, c, c64, tab_half(c64), h->stops, out_tokens,
+                     target, draft, tokens, uniforms, c, c64, tab_half(c64), h->rules, out_tokens,
                      out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q,
                      h->aux_z);
   rc = check_launch(h, "verify_fused");
@@ -241,20 +242,20 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
   const long long grid1 = (long long)B * rows * L.nseg;
   prof_mark(h, 0, s);
   hipLaunchKernelGGL((sv::rowstats_max<DT, VEC, U>), dim3(unsigned(grid1)), dim3(sv::kBlock), 0,
-                     s, target, K, V, L.nseg, L.seg_chunks, h->stops.k, h->parts, hist);
+                     s, target, K, V, L.nseg, L.seg_chunks, h->rules.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_max");
   prof_mark(h, 1, s);
   if (rc) return rc;
   const int grid2 = div_up(B, sv::kWavesPerBlock);
   if (margin)
     hipLaunchKernelGGL((sv::scan_argmax<DT, true>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
-                       L.nseg, h->parts, target, tokens, invT, tau, h->stops, out_tokens, out_len,
+                       L.nseg, h->parts, target, tokens, invT, tau, h->rules, out_tokens, out_len,
                        hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);
   else
     hipLaunchKernelGGL((sv::scan_argmax<DT, false>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K,
-                       V, L.nseg, h->parts, target, tokens, invT, tau, h->stops, out_tokens, out_len,
+                       V, L.nseg, h->parts, target, tokens, invT, tau, h->rules, out_tokens, out_len,
                        hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);
@@ -262,7 +263,7 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
 }
 
 void free_all(spec_verify_handle* h) {
-  void* ptrs[] = {h->parts, h->draw, h->tsum, h->table, h->ema, h->steps, h->stats};
+  void* ptrs[] = {h->parts, h->draw, h->tsum, h->table, h->ema, h->steps, h->streak, h->stats};
   for (void* p : ptrs)
     if (p != nullptr) (void)hipFree(p);
 }
@@ -322,6 +323,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
             hipMalloc(&h->table, (size_t)sv::kTabMax * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->ema, (size_t)max_batch * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->steps, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
+            hipMalloc(&h->streak, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
             hipMalloc(&h->stats, sizeof(sv::DevStats)) == hipSuccess;
   if (!ok) {
     free_all(h);
@@ -330,6 +332,9 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   }
   hipLaunchKernelGGL(sv::fill_f64_i32, dim3(div_up(max_batch, 256)), dim3(256), 0, nullptr,
                      h->ema, h->steps, max_batch, 0.0, 0);
+  hipLaunchKernelGGL(sv::fill_i32, dim3(div_up(max_batch, 256)), dim3(256), 0, nullptr, h->streak,
+                     max_batch, 0);
+  h->rules.pol.streak = h->streak;
   hipLaunchKernelGGL(sv::fill_u64, dim3(1), dim3(64), 0, nullptr,
                      reinterpret_cast<unsigned long long*>(h->stats),
                      int(sizeof(sv::DevStats) / 8));
@@ -364,9 +369,9 @@ int spec_verify_set_aux(spec_verify_handle* h, double* p_d, double* q_d, double*
 int spec_verify_set_stops(spec_verify_handle* h, int eos_token, const int32_t* draft_len,
                           const int32_t* max_emit) {
   if (h == nullptr || eos_token < -1) return SV_EINVAL;
-  h->stops.eos = eos_token;
-  h->stops.k = draft_len;
-  h->stops.m = max_emit;
+  h->rules.eos = eos_token;
+  h->rules.k = draft_len;
+  h->rules.m = max_emit;
   return SV_OK;
 }
 
@@ -561,7 +566,29 @@ int spec_verify_reset_ema(spec_verify_handle* h, hipStream_t stream) {
   if (h == nullptr) return SV_EINVAL;
   hipLaunchKernelGGL(sv::fill_f64_i32, dim3(div_up(h->max_batch, 256)), dim3(256), 0, stream,
                      h->ema, h->steps, h->max_batch, 0.0, 0);
+  hipLaunchKernelGGL(sv::fill_i32, dim3(div_up(h->max_batch, 256)), dim3(256), 0, stream,
+                     h->streak, h->max_batch, 0);
   return check_launch(h, "reset_ema");
+}
+
+int spec_verify_set_policy(spec_verify_handle* h, const float* draft_conf, double d,
+                           int32_t* out_shape, double* out_dcs) {
+  if (h == nullptr) return SV_EINVAL;
+  if (draft_conf == nullptr) {
+    h->rules.pol.conf = nullptr;
+    h->rules.pol.shape = nullptr;
+    h->rules.pol.dcs = nullptr;
+    return SV_OK;
+  }
+  if (out_shape == nullptr || !(std::isfinite(d) && d > 0.0))
+    return fail(h, SV_EINVAL, "policy needs out_shape and a finite divisor d > 0");
+  if (!aligned(draft_conf, 4) || !aligned(out_shape, 4) || !aligned(out_dcs, 8))
+    return fail(h, SV_EINVAL, "misaligned policy array");
+  h->rules.pol.conf = draft_conf;
+  h->rules.pol.shape = out_shape;
+  h->rules.pol.dcs = out_dcs;
+  h->rules.pol.d = d;
+  return SV_OK;
 }
 
 int spec_verify_get_stats(spec_verify_handle* h, spec_verify_stats* out, int reset,

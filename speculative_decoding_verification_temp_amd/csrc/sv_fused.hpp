@@ -547,7 +547,7 @@ template <int DT, int VEC, int NT, bool TRUNC>
 __device__ __forceinline__ void finish_sequence(
     int b, int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
-    Stops sp, int n_half, double* T, const float* fR, const double* fS, const uint32_t* fK,
+    Rules sp, int n_half, double* T, const float* fR, const double* fS, const uint32_t* fK,
     TileSums* tiles,
     DrawRow& s_dr, PickShared& psh, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_len,
@@ -626,7 +626,7 @@ __device__ __forceinline__ void finish_sequence(
     if (lane == 0 && !bad && zqm)
       atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
     emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
-                    decay, st, d);
+                    decay, st, d, sp.pol);
   }
   __syncthreads();
   const DrawRow dr = s_dr;
@@ -711,7 +711,7 @@ template <int DT, int VEC, int U>
 __global__ __launch_bounds__(kFBlock) void verify_fused(
     int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
-    int n_half, Stops sp, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+    int n_half, Rules sp, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
   using C = Chunk<DT, VEC>;
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
       if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = __builtin_nan("");
       if (aux_z != nullptr && lane == 0) aux_z[b] = -1.0;
       emit_and_update(lane, b, K, 0, 0, -1, -1, true, out_tokens, out_len, hist, ema, steps,
-                      decay, st, 0);
+                      decay, st, 0, sp.pol);
     }
     return;
   }
@@ -868,7 +868,7 @@ template <int DT, int VEC, int NT, bool TRUNC>
 __global__ __launch_bounds__(NT) void finish_seq(
     int K, int V, int nseg, const RowPart* __restrict__ parts, const void* __restrict__ target,
     const void* __restrict__ draft, const int32_t* __restrict__ tokens,
-    const float* __restrict__ uniforms, float c, double c64, int n_half, Stops sp,
+    const float* __restrict__ uniforms, float c, double c64, int n_half, Rules sp,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len, uint32_t* __restrict__ hist,
     double* __restrict__ ema, int32_t* __restrict__ steps, double decay,
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {

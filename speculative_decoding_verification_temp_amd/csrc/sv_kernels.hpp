@@ -44,17 +44,36 @@ __device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, i
 
 __device__ inline bool finite_pos(double S) { return S > 0.0 && S < __builtin_inf(); }
 
-// Stopping rules of one call: an end-of-sequence token (-1 = none) and,
-// per sequence, a draft count k_b in [0, K] and an emission budget m_b >= 1
-// (null arrays: k_b = K, m_b = K + 1). See [DVC] "Verify several proposed
-// tokens in one target pass" and "Speculation needs cache rollback".
-struct Stops {
-  const int32_t* k;
-  const int32_t* m;
-  int eos;
+// Tree-shape policy epilogue ([MNW] s.3, dynamic draft tree-shaping), run
+// after each sequence's EMA update when conf is set: the draft confidence
+// score DCS = min(1, conf_b * acc_b / d) from the caller's draft top-1
+// probability conf_b in [0, 1] and the slot's acceptance EMA acc_b, and the
+// next shape (nsteps, top-k, ndt) interpolated from (3, 4, 4) at DCS = 0 to
+// (7, 1, 8) at DCS = 1, rounded half up; five consecutive zero-accept steps
+// (k_b > 0) restore (3, 4, 4) and restart the slot's EMA. Invalid sequences
+// and conf outside [0, 1] give (-1, -1, -1) and leave the state alone.
+struct Policy {
+  const float* conf;   // [B] draft top-1 probabilities; null = policy off
+  int32_t* shape;      // [B][3] out: nsteps, top-k, ndt
+  double* dcs;         // [B] out (may be null)
+  int32_t* streak;     // [max_batch] consecutive zero-accept steps (state)
+  double d;            // saturation divisor > 0
+};
+constexpr int kBreakerSteps = 5;
+
+// Per-call rules: stopping rules (an end-of-sequence token, -1 = none, and
+// per sequence a draft count k_b in [0, K] and an emission budget m_b >= 1;
+// null arrays: k_b = K, m_b = K + 1; see [DVC] "Verify several proposed
+// tokens in one target pass" and "Speculation needs cache rollback") and the
+// tree-shape policy.
+struct Rules {
+  const int32_t* k = nullptr;
+  const int32_t* m = nullptr;
+  int eos = -1;
+  Policy pol{nullptr, nullptr, nullptr, nullptr, 1.0};
 };
 
-__device__ inline void stops_of(const Stops& sp, int b, int K, int& kb, int& m, bool& bad) {
+__device__ inline void stops_of(const Rules& sp, int b, int K, int& kb, int& m, bool& bad) {
   kb = sp.k != nullptr ? sp.k[b] : K;
   m = sp.m != nullptr ? sp.m[b] : K + 1;
   bad = !(kb >= 0 && kb <= K && m >= 1);
@@ -81,15 +100,53 @@ __device__ inline Walk walk_outcome(int lane, int kb, int m, int eos, bool keep,
   return w;
 }
 
+// (nsteps, top-k, ndt) component at score dcs, rounded half up (the same
+// rounded operations as the oracle, never fused, so the same integers)
+__device__ inline int32_t shape_at(double a, double b, double dcs) {
+#pragma clang fp contract(off)
+  return int32_t(__builtin_floor(a + (b - a) * dcs + 0.5));
+}
+
+// The policy step of sequence b (lane 0, after the EMA update).
+__device__ inline void policy_step(const Policy& pol, int b, int kb, int n, bool bad,
+                                   double* __restrict__ ema, int32_t* __restrict__ steps) {
+#pragma clang fp contract(off)
+  const double conf = double(pol.conf[b]);
+  int32_t s0 = -1, s1 = -1, s2 = -1;
+  double dcs = __builtin_nan("");
+  if (!bad && conf >= 0.0 && conf <= 1.0) {
+    int st = pol.streak[b];
+    if (kb > 0) st = (n == 0) ? st + 1 : 0;
+    if (st >= kBreakerSteps) {
+      st = 0;
+      ema[b] = 0.0;
+      steps[b] = 0;
+      dcs = 0.0;
+    } else {
+      const double acc = steps[b] > 0 ? ema[b] : 0.0;
+      dcs = fmin(1.0, conf * acc / pol.d);
+    }
+    pol.streak[b] = st;
+    s0 = shape_at(3.0, 7.0, dcs);
+    s1 = shape_at(4.0, 1.0, dcs);
+    s2 = shape_at(4.0, 8.0, dcs);
+  }
+  pol.shape[3 * b] = s0;
+  pol.shape[3 * b + 1] = s1;
+  pol.shape[3 * b + 2] = s2;
+  if (pol.dcs != nullptr) pol.dcs[b] = dcs;
+}
+
 // Emit (tokens, accept length), histogram and EMA for one sequence: positions
 // < n hold the drafts, position cpos the value cval (or -1, to be filled by
-// the draw), the rest -1. The EMA observes n / kb (skipped when kb = 0).
+// the draw), the rest -1. The EMA observes n / kb (skipped when kb = 0), with
+// the same rounded operations as the oracle; then the policy step, if set.
 __device__ inline void emit_and_update(int lane, int b, int K, int kb, int n, int cpos, int cval,
                                        bool bad, int32_t* __restrict__ out_tokens,
                                        int32_t* __restrict__ out_len,
                                        uint32_t* __restrict__ hist, double* __restrict__ ema,
                                        int32_t* __restrict__ steps, double decay,
-                                       DevStats* __restrict__ st, int d) {
+                                       DevStats* __restrict__ st, int d, const Policy& pol) {
   if (lane <= K) {
     int v;
     if (bad)
@@ -110,12 +167,14 @@ __device__ inline void emit_and_update(int lane, int b, int K, int kb, int n, in
       atomicAdd(&hist[n], 1u);
       atomicAdd(&st->sequences, 1ull);
       if (kb > 0) {
+#pragma clang fp contract(off)
         const double x = double(n) / double(kb);
         const int c = steps[b];
         ema[b] = (c == 0) ? x : decay * ema[b] + (1.0 - decay) * x;
         steps[b] = c + 1;
       }
     }
+    if (pol.conf != nullptr) policy_step(pol, b, kb, n, bad, ema, steps);
   }
 }
 
@@ -188,7 +247,7 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void scan_stochastic(
     int b0, int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
     const void* __restrict__ target, const void* __restrict__ draft,
-    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, Stops sp,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, Rules sp,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, DrawRow* __restrict__ draw, double* aux_p,
@@ -257,7 +316,7 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
   const unsigned long long zqm = __ballot(zq && lane < w.j);
   if (lane == 0 && !bad && zqm) atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
   emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
-                  decay, st, d);
+                  decay, st, d, sp.pol);
 }
 
 // --------------------------------------------------------------------------
@@ -267,7 +326,7 @@ template <int DT, bool MARGIN>
 __global__ __launch_bounds__(kBlock) void scan_argmax(
     int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
     const void* __restrict__ target, const int32_t* __restrict__ tokens, double invT,
-    double tau, Stops sp, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
+    double tau, Rules sp, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
     int32_t* aux_argmax) {
@@ -311,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void scan_argmax(
   if (aux_argmax != nullptr && lane <= K)
     aux_argmax[(long long)b * (K + 1) + lane] = lane <= kb ? A : -1;   // rows past k_b unread
   emit_and_update(lane, b, K, kb, w.n, w.cpos, Aj, bad, out_tokens, out_len, hist, ema, steps,
-                  decay, st, d);
+                  decay, st, d, sp.pol);
 }
 
 // --------------------------------------------------------------------------
@@ -681,6 +740,11 @@ __global__ void fill_f64_i32(double* a, int32_t* b, int n, double va, int32_t vb
     a[i] = va;
     b[i] = vb;
   }
+}
+
+__global__ void fill_i32(int32_t* a, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] = v;
 }
 
 __global__ void fill_u64(unsigned long long* a, int n) {

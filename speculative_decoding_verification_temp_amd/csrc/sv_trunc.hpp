@@ -585,8 +585,8 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
   double tmass[2] = {0.0, 0.0};      // [negative, positive]
   if (tiny_vals && !bad && c64 <= 4.0) {
     const double z = level_term(0x8000u, c64, R);
-    tmass[0] = __dmul_rn(double(H[kTinyNeg]), z);
-    tmass[1] = __dmul_rn(double(H[kTinyPos]), z);
+    tmass[0] = double(H[kTinyNeg]) * z;
+    tmass[1] = double(H[kTinyPos]) * z;
   } else if (tiny_vals && !bad) {
     const long long nchunks = V / VEC;
     double mn = 0.0, mp = 0.0;
@@ -612,12 +612,14 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
     tmass[0] = tr_sum<double, kTwWaves>(mn, s_d);
     tmass[1] = tr_sum<double, kTwWaves>(mp, s_d);
   }
-  // mass of bin i at the reference R (rounded products and sums, so that
-  // the mass loop and the top-p walk give bitwise-equal partial sums)
+  // mass of bin i at the reference R; it and the sums below are never
+  // fused, so the mass loop and the top-p walk give bitwise-equal partial
+  // sums
   auto bin_mass = [&](int i, uint32_t n) -> double {
+#pragma clang fp contract(off)
     if (i == kTinyNeg) return tmass[0];
     if (i == kTinyPos) return tmass[1];
-    return __dmul_rn(double(n), level_term(win_key(i), c64, R));
+    return double(n) * level_term(win_key(i), c64, R);
   };
 
   // ---- 3. top-k threshold bin from the counts (one thread holds the cut) ----
@@ -654,8 +656,10 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
   double M_t = 0.0;
 #pragma unroll
   for (int j = kBinsPerThread - 1; j >= 0; --j) {
-    if (cnt[j] != 0u && bin0 + j > 0 && bin0 + j >= tk)
-      M_t = __dadd_rn(M_t, bin_mass(bin0 + j, cnt[j]));
+    if (cnt[j] != 0u && bin0 + j > 0 && bin0 + j >= tk) {
+#pragma clang fp contract(off)
+      M_t = M_t + bin_mass(bin0 + j, cnt[j]);
+    }
   }
   double S_k;
   const double above_m = tr_above<double, kTwWaves>(M_t, s_d, S_k);
@@ -676,7 +680,10 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
 #pragma unroll
         for (int j = kBinsPerThread - 1; j >= 0; --j) {
           if (cnt[j] != 0u && bin0 + j > 0 && bin0 + j >= tk) {
-            part = __dadd_rn(part, bin_mass(bin0 + j, cnt[j]));
+            {
+#pragma clang fp contract(off)
+              part = part + bin_mass(bin0 + j, cnt[j]);
+            }
             last = bin0 + j;
             if (!found && above_m + part >= goal) {
               s_key = uint32_t(bin0 + j);

@@ -1,0 +1,163 @@
+"""GPU parity of the tree-shape policy epilogue against the oracle.
+
+The epilogue runs in every scan path right after the EMA update, so the tests
+cover a 12-step greedy and margin run whose first sequences keep missing
+(the five-step breaker fires twice), one stochastic step on each stochastic
+path (per-sequence finish, multi-kernel, one kernel per sequence, truncated),
+invalid confidences, turning the policy off, and the reset of its state.
+Shapes and scores are compared exactly: both sides take the same rounded
+float64 operations.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spec_oracle as O
+from workloads import CONFIGS, make_inputs, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+D = 0.45
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import speculative_decoding_verification_temp_amd as pkg
+    pkg.load_library()
+    torch.cuda.set_device(DEV)
+    return pkg
+
+
+def _conf(B, step, bad=False):
+    rng = np.random.default_rng(100 + step)
+    c = rng.uniform(0.0, 1.0, B).astype(np.float32)
+    c[rng.random(B) < 0.1] = 1.0
+    if bad:
+        c[1], c[2], c[3] = -0.1, 2.0, np.nan
+    return c
+
+
+def _compare(shape, dcs, ref, rows=None):
+    g_shape = shape.cpu().numpy()
+    g_dcs = dcs.cpu().numpy()
+    rows = np.arange(len(ref.shape)) if rows is None else rows
+    assert np.array_equal(g_shape[rows], ref.shape[rows]), (g_shape[rows], ref.shape[rows])
+    both_nan = np.isnan(g_dcs[rows]) & np.isnan(ref.dcs[rows])
+    assert np.all(both_nan | (g_dcs[rows] == ref.dcs[rows]))
+
+
+@pytest.mark.parametrize("mode", ["greedy", "margin"])
+def test_policy_multistep_with_breaker(sv, mode):
+    cfg = CONFIGS["c1"].scaled(B=16)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32, ema_decay=0.7)
+    conf_d = torch.zeros(cfg.B, dtype=torch.float32, device=DEV)
+    shape, dcs = v.set_policy(conf_d, D, want_dcs=True)
+    ema = O.EmaState(cfg.B, 0.7)
+    pol = O.TreePolicy(cfg.B, D)
+    fired = 0
+    for step in range(12):
+        x = make_inputs(cfg, step, DEV, "greedy")
+        toks = x["tokens"].clone()
+        # sequences 0-2 always miss at once: the first draft is row 0's minimum
+        toks[:3, 0] = x["target"][:3, 0].argmin(-1).to(torch.int32)
+        conf = _conf(cfg.B, step, bad=(step == 4))
+        conf_d.copy_(torch.as_tensor(conf, device=DEV))
+        tok, alen, hist = v.verify(x["target"], None, toks, None, cfg.T, mode, tau=0.3)
+        torch.cuda.synchronize()
+        ref = O.verify_batch(to_host_f64(x["target"]), None, toks.cpu().numpy(), None, cfg.T,
+                             O.MODE_GREEDY if mode == "greedy" else O.MODE_MARGIN, 0.3,
+                             ema=ema, policy=pol, conf=conf)
+        assert np.array_equal(alen.cpu().numpy(), ref.accept_len)
+        _compare(shape, dcs, ref)
+        fired += int(np.sum(np.all(ref.shape[:3] == (3, 4, 4), axis=1) & (pol.streak[:3] == 0)))
+        e, s = v.ema()
+        torch.cuda.synchronize()
+        assert np.array_equal(s.cpu().numpy(), ema.steps)
+        assert np.array_equal(e.cpu().numpy(), ema.ema)
+    assert fired >= 6                      # sequences 0-2 reset at steps 5 and 10
+
+
+@pytest.mark.parametrize("path", ["finish", "multikernel", "fused", "trunc"])
+def test_policy_stochastic_paths(sv, monkeypatch, path):
+    monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "1" if path == "fused" else "0")
+    monkeypatch.setenv("SPEC_VERIFY_FINISH_SEQ", "0" if path == "multikernel" else "1")
+    cfg = CONFIGS["c2"].scaled(B=48)
+    x = make_inputs(cfg, 5, DEV)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype, ema_decay=0.7)
+    # seed the EMA (some slots without observations)
+    ema = O.EmaState(cfg.B, 0.7)
+    rng = np.random.default_rng(7)
+    ema.ema[:] = rng.uniform(0, 1, cfg.B)
+    ema.steps[:] = rng.integers(0, 3, cfg.B)
+    v.set_ema(torch.as_tensor(ema.ema, device=DEV), torch.as_tensor(ema.steps.astype(np.int32),
+                                                                     device=DEV))
+    pol = O.TreePolicy(cfg.B, D)
+    conf = _conf(cfg.B, 9, bad=True)
+    conf_d = torch.as_tensor(conf, device=DEV)
+    shape, dcs = v.set_policy(conf_d, D, want_dcs=True)
+    trunc = None
+    if path == "trunc":
+        tk = np.full(cfg.B, 40, np.int32)
+        tp = np.full(cfg.B, 0.9, np.float32)
+        v.set_truncation(torch.as_tensor(tk, device=DEV), torch.as_tensor(tp, device=DEV))
+        trunc = dict(top_k=tk, top_p=tp)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T)
+    torch.cuda.synchronize()
+    ref = O.verify_batch(to_host_f64(x["target"]), to_host_f64(x["draft"]),
+                         x["tokens"].cpu().numpy(), x["uniforms"].cpu().double().numpy(), cfg.T,
+                         O.MODE_STOCHASTIC, ema=ema, policy=pol, conf=conf, **(trunc or {}))
+    strict = ref.min_dist >= 1e-6
+    assert np.array_equal(alen.cpu().numpy()[strict], ref.accept_len[strict])
+    _compare(shape, dcs, ref, np.flatnonzero(strict))
+    g = shape.cpu().numpy()
+    assert np.all(g[[1, 2, 3]] == -1)      # confidences outside [0, 1]
+
+
+def test_policy_streaks_fire_and_reset(sv):
+    cfg = CONFIGS["c1"].scaled(B=8)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32, ema_decay=0.7)
+    conf_d = torch.full((cfg.B,), 0.9, dtype=torch.float32, device=DEV)
+    shape, _ = v.set_policy(conf_d, D)
+    x = make_inputs(cfg, 0, DEV, "greedy")
+    toks = (x["tokens"] + 1) % cfg.V       # every first draft misses
+    # a target row whose argmax is the drafted token would spoil the test
+    argm = x["target"][:, :cfg.K].argmax(-1).to(torch.int32)
+    toks = torch.where(toks == argm, (toks + 1) % cfg.V, toks).contiguous()
+    for step in range(4):
+        v.verify(x["target"], None, toks, None, cfg.T, "greedy")
+    torch.cuda.synchronize()
+    assert np.all(shape.cpu().numpy() == (3, 4, 4))
+    v.reset_ema()                          # clears the streaks with the EMA
+    for step in range(4):
+        v.verify(x["target"], None, toks, None, cfg.T, "greedy")
+    _, s = v.ema()
+    torch.cuda.synchronize()
+    assert np.all(s.cpu().numpy() == 4)    # no breaker fired: the streaks restarted
+    v.verify(x["target"], None, toks, None, cfg.T, "greedy")
+    _, s = v.ema()
+    torch.cuda.synchronize()
+    assert np.all(s.cpu().numpy() == 0)    # the fifth miss fires it
+    v.set_policy(None)
+    shape.fill_(7)
+    v.verify(x["target"], None, toks, None, cfg.T, "greedy")
+    torch.cuda.synchronize()
+    assert np.all(shape.cpu().numpy() == 7)   # off: nothing written
+
+
+def test_set_policy_arguments(sv):
+    cfg = CONFIGS["c1"]
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32)
+    conf = torch.zeros(cfg.B, dtype=torch.float32, device=DEV)
+    out = torch.zeros((cfg.B, 3), dtype=torch.int32, device=DEV)
+    lib = v.lib
+    assert lib.spec_verify_set_policy(None, None, 1.0, None, None) == sv.SV_EINVAL
+    assert lib.spec_verify_set_policy(v._h, sv._ptr(conf), 1.0, None, None) == sv.SV_EINVAL
+    for d in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.spec_verify_set_policy(v._h, sv._ptr(conf), d, sv._ptr(out), None) == \
+            sv.SV_EINVAL
+    assert lib.spec_verify_set_policy(v._h, sv._ptr(conf), 0.5, sv._ptr(out), None) == sv.SV_OK
+    assert lib.spec_verify_set_policy(v._h, None, 0.0, None, None) == sv.SV_OK
