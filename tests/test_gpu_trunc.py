@@ -304,3 +304,21 @@ def test_trunc_c3_sampled(sv):
     tp = np.full(cfg.B, 0.9, np.float32)
     rows = np.random.default_rng(13).choice(cfg.B, 24, replace=False)
     _check(sv, x, cfg, tk, tp, "trunc/c3 sampled", rows=np.sort(rows))
+
+
+@pytest.mark.parametrize("V,K,B", [(1001, 3, 8), (3, 1, 4), (16, 2, 1), (8191, 1, 5)])
+def test_trunc_scalar_and_small_shapes(sv, V, K, B):
+    """Vocabularies that are not a multiple of 8 take the scalar-load
+    instances of both truncation passes; K = 1, B = 1 and V = 3 are the
+    smallest shapes. Even sequences also hold one value outside the window
+    (so both passes run in one batch)."""
+    cfg = CONFIGS["c2"].scaled(B=B, K=K, V=V)
+    x = make_inputs(cfg, 12, DEV)
+    for b in range(0, B, 2):
+        x["target"][b, 0, (7 * b) % V] = 2.0 ** -30
+        x["draft"][b, 0, (3 * b + 1) % V] = -200.0
+    rng = np.random.default_rng(19)
+    tk = rng.integers(0, V + 1, B).astype(np.int32)
+    tp = rng.choice([1.0, 0.3, 0.7, 0.95], B).astype(np.float32)
+    _resample_drafts(x, cfg.T, tk, tp, 20)
+    _check(sv, x, cfg, tk, tp, f"trunc/V={V} K={K} B={B}")
