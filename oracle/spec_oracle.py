@@ -91,6 +91,19 @@ listed with its reason in the design notes):
     steps (accept_len = 0 with k_b > 0) restore the starting shape (3, 4, 4)
     and restart the slot's EMA. Invalid sequences and conf outside [0, 1]
     give shape (-1, -1, -1) and leave the policy state alone.
+  * Draft residual side output ([DRIFT] "The update rule and its objective":
+    at every drafted position both distributions are restricted to a shared
+    top-m support and the residual is the target log-probability minus the
+    draft log-probability there; m = 32 in "Ablations"). Optional, stochastic
+    mode: for each valid sequence and position i < k_b, the support S is the
+    m tokens with the largest draft logits (ties to the lower index; all V
+    tokens when V <= m), listed by descending draft logit then index; both
+    temperature softmaxes are restricted to S and renormalised, and
+    r(v) = log p_S(v) - log q_S(v) = (x_t(v) - x_d(v)) / T
+           - log sum_S exp(x_t / T) + log sum_S exp(x_d / T).
+    "Shared top m" is read as the draft's top m (the candidates the draft's
+    bias adjusts). Other positions and invalid sequences: support -1,
+    residual NaN.
 """
 
 from __future__ import annotations
@@ -422,6 +435,46 @@ class EmaState:
         else:
             self.ema[slot] = self.decay * self.ema[slot] + (1.0 - self.decay) * x
         self.steps[slot] += 1
+
+
+def draft_topm_support(draft_row, m: int) -> np.ndarray:
+    """The m tokens with the largest draft logits, ties to the lower index,
+    in that order (all tokens when V <= m)."""
+    x = np.asarray(draft_row, dtype=np.float64)
+    order = np.lexsort((np.arange(x.size), -x))
+    return order[:min(m, x.size)]
+
+
+def drift_residual(target_row, draft_row, T: float, m: int):
+    """(support, residual) of one drafted position: log p_S - log q_S on the
+    draft's top-m support S, both laws restricted to S and renormalised."""
+    S = draft_topm_support(draft_row, m)
+    xt = np.asarray(target_row, dtype=np.float64)[S] / float(T)
+    xd = np.asarray(draft_row, dtype=np.float64)[S] / float(T)
+
+    def lse(v):
+        mx = v.max()
+        return mx + math.log(np.exp(v - mx).sum())
+
+    return S, (xt - lse(xt)) - (xd - lse(xd))
+
+
+def drift_batch(target, draft, T: float, m: int, accept_len, draft_len=None):
+    """Side output for a batch: support [B, K, m] (-1 where not defined) and
+    residual [B, K, m] (NaN there), for valid sequences (accept_len >= 0)
+    and positions i < k_b. Slots past V (V < m) stay -1 / NaN."""
+    B, K = draft.shape[0], draft.shape[1]
+    sup = np.full((B, K, m), -1, dtype=np.int64)
+    res = np.full((B, K, m), np.nan)
+    for b in range(B):
+        if accept_len[b] < 0:
+            continue
+        kb = K if draft_len is None else int(draft_len[b])
+        for i in range(kb):
+            S, r = drift_residual(target[b, i], draft[b, i], T, m)
+            sup[b, i, :S.size] = S
+            res[b, i, :S.size] = r
+    return sup, res
 
 
 START_SHAPE = (3, 4, 4)      # (nsteps, top-k, ndt): wide and shallow
