@@ -213,6 +213,9 @@ def main():
                          "(every sequence); 0 = off")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="stochastic mode: top-p truncation after top-k; 1 = off")
+    ap.add_argument("--residual", type=int, default=0,
+                    help="stochastic mode: draft residual side output on the draft's top-m "
+                         "support (m = this value, 0 = off)")
     ap.add_argument("--policy", action="store_true",
                     help="run the tree-shape policy epilogue (seeded draft confidences, d = 0.5)")
     ap.add_argument("--read-probe", action="store_true",
@@ -255,6 +258,8 @@ def main():
     if trunc:
         v.set_truncation(torch.full((B,), args.top_k, dtype=torch.int32, device=dev),
                          torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
+    if args.residual and mode == "stochastic":
+        v.set_residual(args.residual)
     if args.policy:
         conf = np.random.default_rng([20260923, cfg.index, 8]).uniform(0.0, 1.0, B)
         v.set_policy(torch.as_tensor(conf.astype(np.float32), device=dev), 0.5)
@@ -327,7 +332,9 @@ def main():
                                + (", per-sequence draft counts 1..K" if args.stops == "varlen"
                                   else "")
                                + (f", top-k {args.top_k}, top-p {args.top_p}" if trunc else "")
-                               + (", tree-shape policy" if args.policy else ""),
+                               + (", tree-shape policy" if args.policy else "")
+                               + (f", draft residual m={args.residual}"
+                                  if args.residual and mode == "stochastic" else ""),
                    "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU"},
         "achieved_hbm_gbs": round(call_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_of_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

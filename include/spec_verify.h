@@ -243,6 +243,32 @@ int spec_verify_set_truncation(spec_verify_handle *h, const int32_t *top_k,
 int spec_verify_set_policy(spec_verify_handle *h, const float *draft_conf, double d,
                            int32_t *out_shape, double *out_dcs);
 
+/*
+ * Draft residual side output for later stochastic spec_verify calls
+ * ([DRIFT] "The update rule and its objective": at every drafted position
+ * both distributions are restricted to a shared top-m support, and the
+ * target log-probability minus the draft log-probability there is the
+ * supervision a draft recalibration memory learns from; m = 32 in its
+ * ablations). For each valid sequence b and drafted position i < k_b:
+ *
+ *   S = the m tokens with the largest draft logits at position i (ties to
+ *       the lower token index; all V tokens when V < m), listed by
+ *       descending draft logit, then ascending index;
+ *   out_support[b][i][s] = the s-th token of S;
+ *   out_residual[b][i][s] = (x_t(v) - x_d(v)) / T - LSE_S(x_t / T) + LSE_S(x_d / T)
+ *                         = log p_S(v) - log q_S(v), both laws renormalised on S.
+ *
+ * "Shared top m" is read as the draft's top m. Positions i >= k_b, invalid
+ * sequences and slots s >= V hold -1 and NaN. Arrays are device pointers of
+ * [max_batch][K][m] entries (int32 and float64), caller-owned, written by
+ * later calls on their stream after the verification itself; each position
+ * reads its draft row twice more (one extra kernel, one workgroup per
+ * position). bf16 logits only (SV_EUNSUPPORTED otherwise); 1 <= m <= 64
+ * (else SV_EINVAL). out_support = NULL turns it off.
+ */
+int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
+                             double *out_residual);
+
 /* EMA state accessors, ordered on `stream`. Device pointers of max_batch entries. */
 int spec_verify_get_ema(spec_verify_handle *h, double *ema_dev, int32_t *steps_dev,
                         hipStream_t stream);

@@ -24,6 +24,7 @@ _ERRNAMES = {-1: "SV_EINVAL", -2: "SV_EUNSUPPORTED", -3: "SV_ENOMEM", -4: "SV_EH
 EXPORTED = (
     "spec_verify_init", "spec_verify", "spec_verify_destroy", "spec_verify_set_aux",
     "spec_verify_set_stops", "spec_verify_set_truncation", "spec_verify_set_policy",
+    "spec_verify_set_residual",
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
     "spec_verify_last_error", "spec_verify_version", "spec_verify_read_probe",
@@ -63,6 +64,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify_set_stops.argtypes = [vp, i32, vp, vp]
     L.spec_verify_set_truncation.argtypes = [vp, vp, vp]
     L.spec_verify_set_policy.argtypes = [vp, vp, ctypes.c_double, vp, vp]
+    L.spec_verify_set_residual.argtypes = [vp, i32, vp, vp]
     L.spec_verify_get_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_set_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_reset_ema.argtypes = [vp, vp]
@@ -199,6 +201,23 @@ class SpecVerifier:
 
     def clear_truncation(self):
         self.set_truncation(None, None)
+
+    def set_residual(self, m: int = 32):
+        """Draft residual side output for later stochastic calls (bf16). m = 0
+        turns it off. Returns (support [max_batch, K, m] int32, residual
+        [max_batch, K, m] float64), device tensors the calls write."""
+        if m == 0:
+            self._check(self.lib.spec_verify_set_residual(self._h, 0, None, None),
+                        "set_residual")
+            self._residual = None
+            return None
+        sup = torch.full((self.max_batch, self.K, m), -1, dtype=torch.int32, device=self.device)
+        res = torch.full((self.max_batch, self.K, m), float("nan"), dtype=torch.float64,
+                         device=self.device)
+        self._check(self.lib.spec_verify_set_residual(self._h, int(m), _ptr(sup), _ptr(res)),
+                    "set_residual")
+        self._residual = (sup, res)
+        return sup, res
 
     def set_policy(self, draft_conf, d: float = 0.5, want_dcs: bool = False):
         """Tree-shape policy for later calls: draft_conf is a float32 device

@@ -11,7 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "sv_trunc.hpp"
+#include "sv_drift.hpp"
 
 #ifndef SV_U_BF16
 #define SV_U_BF16 4
@@ -63,6 +63,9 @@ struct spec_verify_handle {
   bool prof_call_end = false;      // also record the end of each call
   sv::Rules rules{};   // stopping rules and tree-shape policy for later calls
   sv::Trunc trunc{nullptr, nullptr};       // top-k / top-p truncation for later calls
+  int drift_m = 0;                         // draft residual side output: support width
+  int32_t* drift_sup = nullptr;            //   [max_batch][K][m] support, null = off
+  double* drift_res = nullptr;             //   [max_batch][K][m] residuals
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int n_cu = 256;          // compute units of the device
@@ -386,6 +389,28 @@ int spec_verify_set_truncation(spec_verify_handle* h, const int32_t* top_k, cons
   return SV_OK;
 }
 
+int spec_verify_set_residual(spec_verify_handle* h, int m, int32_t* out_support,
+                             double* out_residual) {
+  if (h == nullptr) return SV_EINVAL;
+  if (out_support == nullptr) {
+    h->drift_sup = nullptr;
+    h->drift_res = nullptr;
+    h->drift_m = 0;
+    return SV_OK;
+  }
+  if (h->dtype != SV_DTYPE_BF16)
+    return fail(h, SV_EUNSUPPORTED, "the residual side output is implemented for bf16 logits");
+  if (m < 1 || m > sv::kDriftMaxM || out_residual == nullptr)
+    return fail(h, SV_EINVAL, "residual side output needs 1 <= m <= %d and both arrays",
+                sv::kDriftMaxM);
+  if (!aligned(out_support, 4) || !aligned(out_residual, 8))
+    return fail(h, SV_EINVAL, "misaligned residual arrays");
+  h->drift_m = m;
+  h->drift_sup = out_support;
+  h->drift_res = out_residual;
+  return SV_OK;
+}
+
 int spec_verify(spec_verify_handle* h, int B, const void* target, const void* draft,
                 const int32_t* tokens, const float* uniforms, float temperature, int mode,
                 float tau, int32_t* out_tokens, int32_t* out_len, uint32_t* out_hist,
@@ -476,6 +501,18 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
                                           invT, double(tau), out_tokens, out_len, out_hist,
                                           stream);
     }
+  }
+  if (rc == SV_OK && mode == SV_MODE_STOCHASTIC && h->drift_sup != nullptr) {
+    const double invT = 1.0 / double(temperature);
+    if (vec)
+      hipLaunchKernelGGL((sv::drift_residual<8>), dim3(unsigned(B * h->K)), dim3(sv::kTrBlock), 0,
+                         stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
+                         h->drift_sup, h->drift_res);
+    else
+      hipLaunchKernelGGL((sv::drift_residual<1>), dim3(unsigned(B * h->K)), dim3(sv::kTrBlock), 0,
+                         stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
+                         h->drift_sup, h->drift_res);
+    rc = check_launch(h, "drift_residual");
   }
   if (rc == SV_OK) {
     ++h->calls;

@@ -542,8 +542,9 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
 // with level_term too and are 0 for dropped values, and once j is
 // known T is filled with two tables, the target row's and the draft row's,
 // each 0 at the values its row drops (without TRUNC, T is one table built by
-// the caller).
-template <int DT, int VEC, int NT, bool TRUNC>
+// the caller, or, with TABLE_IN_SCAN, by wavefronts 1.. while wavefront 0
+// runs the scan).
+template <int DT, int VEC, int NT, bool TRUNC, bool TABLE_IN_SCAN>
 __device__ __forceinline__ void finish_sequence(
     int b, int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
@@ -627,6 +628,13 @@ __device__ __forceinline__ void finish_sequence(
       atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
     emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
                     decay, st, d, sp.pol);
+  } else {
+    if constexpr (TABLE_IN_SCAN && DT == DT_BF16 && VEC == 8) {
+      for (int i = tid - kWave; i < kTabMax; i += NT - kWave) T[i] = exp_table_entry(i, c64);
+    }
+    if constexpr (TABLE_IN_SCAN && DT == DT_F32 && VEC == 4) {
+      for (int i = tid - kWave; i < kTab2; i += NT - kWave) T[i] = exp2_frac_entry(i);
+    }
   }
   __syncthreads();
   const DrawRow dr = s_dr;
@@ -853,7 +861,7 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
   }
   __syncthreads();
 
-  finish_sequence<DT, VEC, kFBlock, false>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
+  finish_sequence<DT, VEC, kFBlock, false, false>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
                                            n_half, T, fR, fS, nullptr, tiles, s_dr, psh,
                                            out_tokens, out_len, hist, ema,
                                     steps,
@@ -884,12 +892,6 @@ __global__ __launch_bounds__(NT) void finish_seq(
   __shared__ PickShared psh;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
-  if constexpr (kTab && !TRUNC) {
-    for (int i = tid; i < kTabMax; i += NT) T[i] = exp_table_entry(i, c64);
-  }
-  if constexpr (kTab2F) {
-    for (int i = tid; i < kTab2; i += NT) T[i] = exp2_frac_entry(i);
-  }
   for (int r = tid; r < rows; r += NT) {
     float R;
     double S;
@@ -900,7 +902,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
     if constexpr (TRUNC) fK[r] = uint32_t(pr->idx);
   }
   __syncthreads();
-  finish_sequence<DT, VEC, NT, TRUNC>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
+  finish_sequence<DT, VEC, NT, TRUNC, !TRUNC>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
                                       n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
                                       out_len, hist, ema,
                                     steps,

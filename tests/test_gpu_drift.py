@@ -1,0 +1,112 @@
+"""GPU parity of the draft residual side output against the oracle.
+
+Supports must match exactly (token ids in order); residuals within 1e-9
+(both sides sum the same 32 float64 exponentials in different orders).
+Cases: a full c2 batch with per-sequence draft counts and invalid sequences,
+rows with many ties, V below m, -inf logits inside the support, draft rows
+with more than 65535 equal values (the histogram's careful recount), and
+argument errors.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spec_oracle as O
+from workloads import CONFIGS, make_inputs, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+TOL = 1e-9
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import speculative_decoding_verification_temp_amd as pkg
+    pkg.load_library()
+    torch.cuda.set_device(DEV)
+    return pkg
+
+
+def _run(sv, x, cfg, m, kb=None):
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    sup, res = v.set_residual(m)
+    if kb is not None:
+        v.set_stops(-1, torch.as_tensor(kb, device=DEV).contiguous(), None)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+    torch.cuda.synchronize()
+    return sup.cpu().numpy(), res.cpu().numpy(), alen.cpu().numpy()
+
+
+def _check(x, cfg, m, sup, res, alen, kb=None, label=""):
+    # the call takes the temperature as float32: the oracle uses that value
+    T32 = float(np.float32(x["T"]))
+    ref_sup, ref_res = O.drift_batch(to_host_f64(x["target"]), to_host_f64(x["draft"]), T32, m,
+                                     alen, kb)
+    assert np.array_equal(sup, ref_sup), f"{label}: support differs at " \
+        f"{np.argwhere(sup != ref_sup)[:5]}"
+    both_nan = np.isnan(res) & np.isnan(ref_res)
+    same_inf = np.isinf(res) & (res == ref_res)
+    close = np.abs(res - ref_res) <= TOL
+    assert np.all(both_nan | same_inf | close), f"{label}: residual err " \
+        f"{np.nanmax(np.abs(res - ref_res)[~(both_nan | same_inf)])}"
+    print(f"{label}: {int((sup >= 0).sum())} support entries checked", flush=True)
+
+
+def test_residual_c2_with_draft_counts(sv):
+    cfg = CONFIGS["c2"].scaled(B=32)
+    x = make_inputs(cfg, 3, DEV)
+    x["tokens"][5, 0] = cfg.V + 3              # an invalid sequence
+    kb = np.random.default_rng(4).integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    sup, res, alen = _run(sv, x, cfg, 32, kb)
+    assert alen[5] == -1
+    _check(x, cfg, 32, sup, res, alen, kb, "residual/c2")
+
+
+def test_residual_many_ties_and_small_m(sv):
+    cfg = CONFIGS["c2"].scaled(B=16, V=4000)
+    x = make_inputs(cfg, 6, DEV)
+    for key in ("target", "draft"):
+        x[key] = (torch.round(x[key].float() * 2) / 2).to(x[key].dtype).contiguous()
+    for m in (1, 7, 64):
+        sup, res, alen = _run(sv, x, cfg, m)
+        _check(x, cfg, m, sup, res, alen, label=f"residual/ties m={m}")
+
+
+def test_residual_v_below_m_and_neg_inf(sv):
+    cfg = CONFIGS["c2"].scaled(B=8, V=24, K=3)
+    x = make_inputs(cfg, 7, DEV)
+    x["draft"][2, :, 10:] = float("-inf")      # only 10 finite draft values: -inf in the support
+    x["target"][3, 0, :5] = float("-inf")
+    sup, res, alen = _run(sv, x, cfg, 32)
+    assert np.all(sup[:, :, 24:] == -1)
+    _check(x, cfg, 32, sup, res, alen, label="residual/V<m")
+
+
+def test_residual_wrapped_counters(sv):
+    cfg = CONFIGS["c3"].scaled(B=2, K=2)
+    x = make_inputs(cfg, 8, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    for b in range(cfg.B):
+        for i in range(cfg.K):
+            perm = torch.randperm(cfg.V, generator=g, device=DEV)
+            x["draft"][b, i, perm[:70000]] = 5.0 if b == 0 else -5.0   # a 70000-way tie
+    sup, res, alen = _run(sv, x, cfg, 32)
+    _check(x, cfg, 32, sup, res, alen, label="residual/wrapped counters")
+
+
+def test_set_residual_arguments(sv):
+    cfg = CONFIGS["c1"]
+    v32 = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32)
+    buf = torch.zeros(cfg.B * cfg.K * 64, dtype=torch.int32, device=DEV)
+    dbl = torch.zeros(cfg.B * cfg.K * 64, dtype=torch.float64, device=DEV)
+    assert v32.lib.spec_verify_set_residual(v32._h, 32, sv._ptr(buf), sv._ptr(dbl)) == \
+        sv.SV_EUNSUPPORTED
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.bfloat16)
+    for m in (0, 65, -1):
+        assert v.lib.spec_verify_set_residual(v._h, m, sv._ptr(buf), sv._ptr(dbl)) == sv.SV_EINVAL
+    assert v.lib.spec_verify_set_residual(v._h, 8, sv._ptr(buf), None) == sv.SV_EINVAL
+    assert v.lib.spec_verify_set_residual(v._h, 8, None, None) == sv.SV_OK
+    assert v.lib.spec_verify_set_residual(None, 8, None, None) == sv.SV_EINVAL
