@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "sv_drift.hpp"
+#include "sv_trunc.hpp"
 
 #ifndef SV_U_BF16
 #define SV_U_BF16 4
@@ -505,11 +506,11 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   if (rc == SV_OK && mode == SV_MODE_STOCHASTIC && h->drift_sup != nullptr) {
     const double invT = 1.0 / double(temperature);
     if (vec)
-      hipLaunchKernelGGL((sv::drift_residual<8>), dim3(unsigned(B * h->K)), dim3(sv::kTrBlock), 0,
+      hipLaunchKernelGGL((sv::drift_residual<8>), dim3(unsigned(B * h->K)), dim3(sv::kDriftBlock), 0,
                          stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
                          h->drift_sup, h->drift_res);
     else
-      hipLaunchKernelGGL((sv::drift_residual<1>), dim3(unsigned(B * h->K)), dim3(sv::kTrBlock), 0,
+      hipLaunchKernelGGL((sv::drift_residual<1>), dim3(unsigned(B * h->K)), dim3(sv::kDriftBlock), 0,
                          stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
                          h->drift_sup, h->drift_res);
     rc = check_launch(h, "drift_residual");

@@ -9,62 +9,135 @@
 // renormalised on it:
 //   r(v) = (x_t(v) - x_d(v)) / T - LSE_S(x_t / T) + LSE_S(x_d / T).
 //
-// One 1024-thread workgroup per (sequence, drafted position i < k_b) of a
-// valid sequence (the scan's accept length is read to tell): the draft row is
-// counted into the full pass's exact 65536-key histogram (with its careful
-// recount when a 16-bit counter wraps), the m-th largest value follows from
-// the counts, a second read of the row collects the tokens above it into one
-// LDS list and the tokens tied with it into another (slots by atomics, the
-// loads pipelined as in the count), the lowest-index ties are picked by
-// ranking the tie list (with more ties than the list holds, a third read
-// walks the row in index order), and wavefront 0 ranks the m tokens and forms
-// the two float64 log-sum-exps over them.
+// One 256-thread workgroup per (sequence, drafted position i < k_b) of a
+// valid sequence (the scan's accept length is read to tell) reads the draft
+// row once. Token v is ranked by the 48-bit key
+//   (order-preserving bf16 key << 32) | (2^32 - 1 - v),
+// so a larger logit comes first, equal logits fall to the lower index, and no
+// two tokens share a key: the support is the m largest keys. Each wavefront
+// appends the keys that reach its threshold to an LDS list; before the list
+// could overflow it finds the m-th largest key in it (byte-wise radix select)
+// and keeps only the keys at or above it, which becomes its new threshold.
+// The m-th largest key of any part of the row is at most the row's m-th
+// largest, so no support token is ever dropped, and the wavefronts may share
+// their thresholds through one LDS word. The common case, a chunk with no key
+// at the threshold, costs a float compare per value: a bf16 key reaches the
+// threshold's upper 16 bits exactly when the value, widened to float, is at
+// least the value those bits encode. At the end wavefront 0 merges the
+// four lists, keeps the m largest keys, ranks them and forms the two float64
+// log-sum-exps over them.
 #pragma once
 
-#include "sv_trunc.hpp"
+#include "sv_kernels.hpp"
 
 namespace sv {
 
 constexpr int kDriftMaxM = 64;
-constexpr int kTieCap = kTrBlock;   // ties at the threshold kept unordered
+constexpr int kDriftBlock = 256;
+constexpr int kDriftWaves = kDriftBlock / kWave;
+constexpr int kDriftCap = 1024;      // keys per wavefront list
+constexpr int kDriftUnroll = 4;      // chunks per thread per group (two groups in flight)
 
-// inclusive prefix of v over the threads of the workgroup in index order, and
-// the workgroup total
-__device__ inline uint32_t tr_prefix(uint32_t v, uint32_t* s, uint32_t& total) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  uint32_t incl = v;
+// LDS written by some lanes of a wavefront, then read by others
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// the float a bf16 key stands for (-inf for keys at or below -inf's)
+__device__ inline float key_float(uint32_t key) {
+  const uint32_t bits = key >= 0x8000u ? key - 0x8000u : 0x8000u | min(0x8000u - key, 0x7f80u);
+  return __uint_as_float(bits << 16);
+}
+
+// active lanes of `mask` below this lane
+__device__ inline uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+// The want-th largest (1 <= want <= n) of the n distinct keys buf[0..n), all
+// below 2^48, by byte-wise radix select from the top byte down: each round
+// counts the keys that match the bytes chosen so far into 256 bins private to
+// the wavefront and walks the bins from the top; it stops as soon as a single
+// key is left. Called by all lanes of one wavefront.
+__device__ inline uint64_t wave_kth_largest(const uint64_t* buf, int n, uint32_t want,
+                                            uint32_t* bins) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t prefix = 0, pmask = 0;
+#pragma unroll 1
+  for (int shift = 40; shift >= 0; shift -= 8) {
+    for (int q = lane; q < 256; q += kWave) bins[q] = 0u;
+    wave_sync();
+    for (int e = lane; e < n; e += kWave) {
+      const uint64_t v = buf[e];
+      if ((v & pmask) == prefix) atomicAdd(&bins[uint32_t(v >> shift) & 255u], 1u);
+    }
+    wave_sync();
+    // lane L walks bins 255 - 4L down to 252 - 4L; lanes in order cover 255..0
+    uint32_t c[4], s = 0;
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t u = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += u;
-  }
-  if (lane == kWave - 1) s[wid] = incl;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
+    for (int j = 0; j < 4; ++j) {
+      c[j] = bins[255 - 4 * lane - j];
+      s += c[j];
+    }
+    uint32_t incl = s;
 #pragma unroll
-  for (int w = 0; w < kTrWaves; ++w) {
-    if (w < wid) before += s[w];
-    tot += s[w];
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    const uint32_t excl = incl - s;
+    const bool mine = excl < want && incl >= want;   // exactly one lane
+    uint32_t byte = 0, above = 0, at = 0;
+    if (mine) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (at == 0u && acc + c[j] >= want) {
+          byte = uint32_t(255 - 4 * lane - j);
+          above = acc;
+          at = c[j];
+        }
+        acc += c[j];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    byte = __shfl(byte, src, kWave);
+    above = __shfl(above, src, kWave);
+    at = __shfl(at, src, kWave);
+    want -= above;
+    prefix |= uint64_t(byte) << shift;
+    pmask |= uint64_t(255) << shift;
+    wave_sync();                                     // bins are cleared next round
+    if (at == 1u) {
+      uint64_t r = 0;
+      for (int e = lane; e < n; e += kWave) {
+        const uint64_t v = buf[e];
+        if ((v & pmask) == prefix) r = v;
+      }
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(r, o, kWave);
+        r = u > r ? u : r;
+      }
+      return r;
+    }
   }
-  __syncthreads();
-  total = tot;
-  return before + incl;
+  return prefix;
 }
 
 template <int VEC>
-__global__ __launch_bounds__(kTrBlock) void drift_residual(
+__global__ __launch_bounds__(kDriftBlock) void drift_residual(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, double invT,
     int m, const int32_t* __restrict__ kdraft, const int32_t* __restrict__ accept_len,
     int32_t* __restrict__ out_support, double* __restrict__ out_res) {
   using C = Chunk<DT_BF16, VEC>;
-  __shared__ uint32_t H[kHistWords];
-  __shared__ uint32_t s_wraps[kMaxWraps];
-  __shared__ uint32_t s_nwrap;
-  __shared__ uint32_t s_u[kTrWaves];
-  __shared__ int s_i[kTrWaves];
-  __shared__ uint32_t s_key, s_above, s_fill, s_ties, s_ntie;
-  __shared__ int s_sel[kDriftMaxM];
-  __shared__ int s_tie[kTieCap];
+  __shared__ uint64_t s_keys[kDriftWaves][kDriftCap];
+  __shared__ uint32_t s_bins[kDriftWaves][256];
+  __shared__ uint32_t s_count[kDriftWaves];
+  __shared__ unsigned long long s_thr;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = int(blockIdx.x) / K, i = int(blockIdx.x) % K;
   const long long o0 = ((long long)b * K + i) * m;
@@ -78,184 +151,152 @@ __global__ __launch_bounds__(kTrBlock) void drift_residual(
   }
   const void* drow = row_ptr<DT_BF16>(target, draft, b, K + 1 + i, K, V);
   const void* trow = row_ptr<DT_BF16>(target, draft, b, i, K, V);
-  const int mm = min(m, V);
-  const uint32_t k0 = uint32_t(tid) * kKeysPerThread;
-
-  // ---- 1. exact histogram of the draft row ----
-  uint32_t nwrap = 0;
-  auto count_of = [&](int ii) -> uint32_t {
-    const uint32_t key = k0 + uint32_t(ii);
-    uint32_t n = (H[hist_word(key >> 1)] >> ((key & 1u) << 4)) & 0xffffu;
-    if (nwrap != 0u) {
-      const int nw = min(int(nwrap), kMaxWraps);
-#pragma unroll 1
-      for (int e = 0; e < nw; ++e) n += s_wraps[e] == key ? 65536u : 0u;
-    }
-    return n;
-  };
-  auto thread_total = [&]() -> uint32_t {
-    nwrap = s_nwrap;
-    uint32_t t = 0;
-#pragma unroll 2
-    for (int q = 0; q < kKeysPerThread / 8; ++q) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(H)[tid * (kKeysPerThread / 8) + (q ^ (tid & 7))];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) t += (v[w] & 0xffffu) + (v[w] >> 16);
-    }
-    if (nwrap != 0u)
-#pragma unroll 1
-      for (int e = 0; e < min(int(nwrap), kMaxWraps); ++e)
-        t += (s_wraps[e] >> 6) == uint32_t(tid) ? 65536u : 0u;
-    return t;
-  };
-  count_row<VEC, kCountFast>(drow, V, H, &s_nwrap, s_wraps);
-  uint32_t n_t = thread_total();
-  if (tr_sum(n_t, s_u) != uint32_t(V)) {
-    count_row<VEC, kCountEven>(drow, V, H, &s_nwrap, s_wraps);
-    count_row<VEC, kCountOdd>(drow, V, H, &s_nwrap, s_wraps);
-    n_t = thread_total();
-  }
-
-  // ---- 2. the mm-th largest key and the count strictly above it ----
-  {
-    uint32_t n_all;
-    const uint32_t above = tr_above(n_t, s_u, n_all);
-    if (above < uint32_t(mm) && above + n_t >= uint32_t(mm)) {
-      uint32_t acc = above;
-#pragma unroll 1
-      for (int ii = kKeysPerThread - 1; ii >= 0; --ii) {
-        const uint32_t n = count_of(ii);
-        if (acc + n >= uint32_t(mm)) {
-          s_key = k0 + uint32_t(ii);
-          s_above = acc;
-          break;
-        }
-        acc += n;
-      }
-    }
-    if (tid == 0) {
-      s_fill = 0u;
-      s_ties = 0u;
-      s_ntie = 0u;
-    }
-    __syncthreads();
-  }
-  const uint32_t kth = s_key, n_above = s_above;
-  const uint32_t need = uint32_t(mm) - n_above;   // ties at kth to take, lowest indices first
-
-  // ---- 3. collect: every token above kth (fewer than mm), and the ties at
-  // kth, in one pipelined read ----
-  const long long nchunks = V / VEC;
-  auto collect_chunk = [&](const typename C::raw_t& raw, long long ci) {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      uint32_t bits;
-      if constexpr (VEC == 8)
-        bits = (e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu;
-      else
-        bits = raw;
-      const uint32_t key = bf16_key(bits);
-      if (key > kth) {
-        const uint32_t slot = atomicAdd(&s_fill, 1u);
-        if (slot < uint32_t(kDriftMaxM)) s_sel[slot] = int(ci * VEC + e);
-      } else if (key == kth) {
-        const uint32_t slot = atomicAdd(&s_ntie, 1u);
-        if (slot < uint32_t(kTieCap)) s_tie[slot] = int(ci * VEC + e);
-      }
-    }
-  };
-  {
-    constexpr int U = 4;
-    long long ci = tid;
-    for (; ci + (long long)(U - 1) * kTrBlock < nchunks; ci += (long long)U * kTrBlock) {
-      typename C::raw_t raw[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) raw[u] = C::load(drow, ci + (long long)u * kTrBlock);
-#pragma unroll
-      for (int u = 0; u < U; ++u) collect_chunk(raw[u], ci + (long long)u * kTrBlock);
-    }
-    for (; ci < nchunks; ci += kTrBlock) collect_chunk(C::load(drow, ci), ci);
-  }
+  const uint32_t mm = uint32_t(min(m, V));
+  if (tid == 0) s_thr = 0ull;
   __syncthreads();
-  const uint32_t ntie = s_ntie;
-  if (ntie <= uint32_t(kTieCap)) {
-    // the `need` lowest indices among the ties: rank each by index
-    if (tid < int(ntie)) {
-      const int v = s_tie[tid];
-      uint32_t rank = 0;
-#pragma unroll 4
-      for (uint32_t o = 0; o < ntie; ++o) rank += s_tie[o] < v ? 1u : 0u;
-      if (rank < need) s_sel[n_above + rank] = v;
+
+  uint64_t* keys = s_keys[wid];
+  uint32_t* bins = s_bins[wid];
+  uint32_t fill = 0;           // wavefront-uniform
+  uint64_t thr = 0;            // keys below it cannot be in the support
+  float thr_f = key_float(0u); // the value of thr's bf16 key
+  // keep the keys at or above max(the want-th largest key, the shared threshold)
+  auto compact = [&](uint32_t want) {
+    uint64_t t = thr;
+    if (fill > want) {
+      const uint64_t kth = wave_kth_largest(keys, int(fill), want, bins);
+      t = kth > t ? kth : t;
+      if (lane == 0) atomicMax(&s_thr, (unsigned long long)t);
     }
-  } else {
-    // more ties than the list holds: walk the row in index order (blocks of
-    // kTrBlock chunks, thread order = index order) and take the first `need`
-    for (long long c0 = 0; c0 < nchunks && s_ties < need; c0 += kTrBlock) {
-      const long long ci = c0 + tid;
-      uint32_t bits[VEC];
-      if (ci < nchunks) {
-        const typename C::raw_t raw = C::load(drow, ci);
+    const uint64_t shared =
+        __hip_atomic_load(&s_thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    t = shared > t ? shared : t;
+    uint32_t out = 0;          // in place: a key moves only to a lower slot
+    for (uint32_t base = 0; base < fill; base += kWave) {
+      const uint32_t e = base + uint32_t(lane);
+      const uint64_t v = e < fill ? keys[e] : 0ull;
+      const bool keep = e < fill && v >= t;
+      const uint64_t mask = __ballot(keep);
+      if (keep) keys[out + lanes_below(mask)] = v;
+      out += uint32_t(__popcll(mask));
+    }
+    wave_sync();
+    fill = out;
+    thr = t;
+    thr_f = key_float(uint32_t(t >> 32));
+  };
+
+  // ---- one read of the draft row; the next group's loads are in flight
+  // while a group is filtered (indexes past the row are clamped to its last
+  // chunk and ignored) ----
+  const long long nchunks = V / VEC;
+  constexpr long long kPerIt = (long long)kDriftBlock * kDriftUnroll;
+  constexpr uint32_t kPerChunk = uint32_t(kWave * VEC);   // keys one chunk step can add
+  const long long nit = (nchunks + kPerIt - 1) / kPerIt;
+  using raw_t = typename C::raw_t;
+  auto load_group = [&](long long it, raw_t (&raw)[kDriftUnroll]) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          if constexpr (VEC == 8)
-            bits[e] = (e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu;
-          else
-            bits[e] = raw;
-        }
-      }
-      uint32_t ties = 0;
+    for (int u = 0; u < kDriftUnroll; ++u) {
+      const long long ci = (it * kDriftUnroll + u) * kDriftBlock + tid;
+      raw[u] = C::load(drow, ci < nchunks ? ci : nchunks - 1);
+    }
+  };
+  // bits of value e of a chunk (e may differ between lanes)
+  auto value_bits = [&](const raw_t& r, int e) -> uint32_t {
+    if constexpr (VEC == 8) {
+      const uint32_t w = (e & 4) ? ((e & 2) ? r[3] : r[2]) : ((e & 2) ? r[1] : r[0]);
+      return (e & 1) ? w >> 16 : w & 0xffffu;
+    } else {
+      return r;
+    }
+  };
+  auto filter_group = [&](long long it, const raw_t (&raw)[kDriftUnroll]) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) ties += (ci < nchunks && bf16_key(bits[e]) == kth) ? 1u : 0u;
-      uint32_t blk_ties;
-      const uint32_t incl = tr_prefix(ties, s_u, blk_ties);
-      const uint32_t base = s_ties;
-      uint32_t t = base + incl - ties;             // ties before this thread's
+    for (int u = 0; u < kDriftUnroll; ++u) {
+      const long long ci = (it * kDriftUnroll + u) * kDriftBlock + tid;
+      // the values of this lane's chunk that may reach the threshold
+      uint32_t pend = 0;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        if (ci < nchunks && bf16_key(bits[e]) == kth) {
-          if (t < need) s_sel[n_above + t] = int(ci * VEC + e);
-          ++t;
-        }
+        uint32_t hi;                           // the value's bits in a float's upper half
+        if constexpr (VEC == 8)
+          hi = (e & 1) ? raw[u][e >> 1] & 0xffff0000u : raw[u][e >> 1] << 16;
+        else
+          hi = raw[u] << 16;
+        pend |= __uint_as_float(hi) >= thr_f ? 1u << e : 0u;
       }
-      __syncthreads();
-      if (tid == 0) s_ties = base + blk_ties;
-      __syncthreads();
+      if (ci >= nchunks) pend = 0u;
+      if (__ballot(pend != 0u) == 0ull) continue;   // uniform: the common case
+      if (fill > uint32_t(kDriftCap) - kPerChunk) compact(mm);
+      // one value per lane and round, as many rounds as the busiest lane needs
+      while (__ballot(pend != 0u) != 0ull) {
+        const bool act = pend != 0u;
+        const int e = act ? __builtin_ctz(pend) : 0;
+        pend &= pend - 1u;
+        const uint64_t k = (uint64_t(bf16_key(value_bits(raw[u], e))) << 32) |
+                           uint64_t(~uint32_t(ci * VEC + e));
+        const bool put = act && k >= thr;
+        const uint64_t mask = __ballot(put);
+        if (put) keys[fill + lanes_below(mask)] = k;
+        fill += uint32_t(__popcll(mask));
+      }
+    }
+  };
+  {
+    // two register sets in turn; loads are unconditional, so the compiler's
+    // wait counts stay exact, and groups past the row filter nothing
+    raw_t ga[kDriftUnroll], gb[kDriftUnroll];
+    load_group(0, ga);
+#pragma unroll 1
+    for (long long it = 0; it < nit; it += 2) {
+      load_group(it + 1, gb);
+      filter_group(it, ga);
+      load_group(it + 2, ga);
+      filter_group(it + 1, gb);
     }
   }
+  compact(mm);                                  // at most mm keys per wavefront
+  if (lane == 0) s_count[wid] = fill;
   __syncthreads();
 
-  // ---- 4. rank the mm tokens, residuals on wavefront 0 ----
-  if (wid == 0) {
-    int v = -1;
-    float xd = 0.0f;
-    if (lane < mm) {
-      v = s_sel[lane];
-      xd = load_logit<DT_BF16>(drow, v);
-    }
-    // rank: descending draft logit, then ascending index
-    int rank = 0;
-    for (int o = 0; o < mm; ++o) {
-      const int vo = __shfl(v, o, kWave);
-      const float xo = __shfl(xd, o, kWave);
-      rank += (lane < mm && (xo > xd || (xo == xd && vo < v))) ? 1 : 0;
-    }
-    const double at = lane < mm ? double(load_logit<DT_BF16>(trow, v)) * invT : -__builtin_inf();
-    const double ad = lane < mm ? double(xd) * invT : -__builtin_inf();
-    double mt = at, md = ad;
+  // ---- merge, keep the mm largest keys, rank, residuals on wavefront 0 ----
+  if (wid != 0) return;
+  {
+    uint32_t n = fill;
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      mt = fmax(mt, __shfl_xor(mt, o, kWave));
-      md = fmax(md, __shfl_xor(md, o, kWave));
+    for (int w = 1; w < kDriftWaves; ++w) {
+      const uint32_t cw = s_count[w];
+      for (uint32_t e = uint32_t(lane); e < cw; e += kWave) keys[n + e] = s_keys[w][e];
+      n += cw;
     }
-    const double lse_t = mt + log(wave_sum(lane < mm ? exp(at - mt) : 0.0));
-    const double lse_d = md + log(wave_sum(lane < mm ? exp(ad - md) : 0.0));
-    if (lane < mm) {
-      out_support[o0 + rank] = v;
-      out_res[o0 + rank] = (at - lse_t) - (ad - lse_d);
-    } else if (lane < m) {
-      out_support[o0 + lane] = -1;
-      out_res[o0 + lane] = __builtin_nan("");
-    }
+    wave_sync();
+    fill = n;
+  }
+  compact(mm);                                  // exactly mm keys remain
+  const bool has = uint32_t(lane) < mm;
+  const uint64_t key = has ? keys[lane] : 0ull;
+  int rank = 0;
+  for (int o = 0; o < int(mm); ++o) {
+    const uint64_t ko = __shfl(key, o, kWave);
+    rank += (has && ko > key) ? 1 : 0;
+  }
+  const int v = has ? int(~uint32_t(key)) : -1;
+  const double ad = has ? double(load_logit<DT_BF16>(drow, v)) * invT : -__builtin_inf();
+  const double at = has ? double(load_logit<DT_BF16>(trow, v)) * invT : -__builtin_inf();
+  double mt = at, md = ad;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    mt = fmax(mt, __shfl_xor(mt, o, kWave));
+    md = fmax(md, __shfl_xor(md, o, kWave));
+  }
+  const double lse_t = mt + log(wave_sum(has ? exp(at - mt) : 0.0));
+  const double lse_d = md + log(wave_sum(has ? exp(ad - md) : 0.0));
+  if (has) {
+    out_support[o0 + rank] = v;
+    out_res[o0 + rank] = (at - lse_t) - (ad - lse_d);
+  } else if (lane < m) {
+    out_support[o0 + lane] = -1;
+    out_res[o0 + lane] = __builtin_nan("");
   }
 }
 
