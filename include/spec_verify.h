@@ -71,7 +71,7 @@ enum {
     SV_OK = 0,
     SV_EINVAL = -1,        /* bad argument; nothing was enqueued */
     SV_EUNSUPPORTED = -2,  /* unknown dtype */
-    SV_ENOMEM = -3,        /* device allocation failed in init */
+    SV_ENOMEM = -3,        /* device allocation failed (init, set_residual) */
     SV_EHIP = -4           /* a HIP call or launch failed; see spec_verify_last_error */
 };
 
@@ -261,10 +261,16 @@ int spec_verify_set_policy(spec_verify_handle *h, const float *draft_conf, doubl
  * "Shared top m" is read as the draft's top m. Positions i >= k_b, invalid
  * sequences and slots s >= V hold -1 and NaN. Arrays are device pointers of
  * [max_batch][K][m] entries (int32 and float64), caller-owned, written by
- * later calls on their stream after the verification itself; each position
- * reads its draft row twice more (one extra kernel, one workgroup per
- * position). bf16 logits only (SV_EUNSUPPORTED otherwise); 1 <= m <= 64
- * (else SV_EINVAL). out_support = NULL turns it off.
+ * later calls on their stream after the verification itself. Where the
+ * call's streaming pass reads 16-byte chunks of bf16 rows, that pass also
+ * keeps the draft rows' top-m candidates and one small kernel per call
+ * finishes the output; otherwise (truncation, one kernel per sequence, rows
+ * not in 16-byte chunks) one extra kernel reads each draft row once more.
+ * The first call with out_support set allocates the candidate lists,
+ * max_batch * K * 32 KiB on the handle's device, kept until
+ * spec_verify_destroy (SV_ENOMEM if that fails); spec_verify itself still
+ * allocates nothing. bf16 logits only (SV_EUNSUPPORTED otherwise);
+ * 1 <= m <= 64 (else SV_EINVAL). out_support = NULL turns it off.
  */
 int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
                              double *out_residual);

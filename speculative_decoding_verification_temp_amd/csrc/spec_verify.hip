@@ -27,6 +27,7 @@
 namespace {
 
 constexpr int kMaxSeg = 16;
+static_assert(kMaxSeg <= sv::kTopmMaxSeg, "top-m lists are laid out for kTopmMaxSeg segments");
 constexpr int kProfCalls = 4096;
 constexpr double kLog2e = 1.4426950408889634073599246810018921;
 
@@ -67,6 +68,8 @@ struct spec_verify_handle {
   int drift_m = 0;                         // draft residual side output: support width
   int32_t* drift_sup = nullptr;            //   [max_batch][K][m] support, null = off
   double* drift_res = nullptr;             //   [max_batch][K][m] residuals
+  uint64_t* topm_lists = nullptr;          // streaming-pass top-m lists (allocated by set_residual)
+  int topm_nseg = 0;                       // segments per row of this call's lists, 0 = none
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int n_cu = 256;          // compute units of the device
@@ -151,9 +154,21 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   const int groups = div_up(L.ntiles, h->tiles_per_group);
   const int grid_seq = div_up(B, sv::kWavesPerBlock);
   prof_mark(h, 0, s);
-  hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
-                     dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                     h->rules.k, h->parts, hist);
+  bool topm = false;
+  if constexpr (DT == sv::DT_BF16 && VEC == 8) {
+    // the residual side output takes its draft-row candidates from this pass
+    if (h->drift_sup != nullptr && h->topm_lists != nullptr) {
+      hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U, true>), dim3(unsigned(B * rows * L.nseg)),
+                         dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
+                         h->rules.k, h->parts, hist, h->drift_m, h->topm_lists);
+      h->topm_nseg = L.nseg;
+      topm = true;
+    }
+  }
+  if (!topm)
+    hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
+                       dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
+                       h->rules.k, h->parts, hist, 0, nullptr);
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
@@ -267,7 +282,8 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
 }
 
 void free_all(spec_verify_handle* h) {
-  void* ptrs[] = {h->parts, h->draw, h->tsum, h->table, h->ema, h->steps, h->streak, h->stats};
+  void* ptrs[] = {h->parts, h->draw,  h->tsum,  h->table,     h->ema,
+                  h->steps, h->streak, h->stats, h->topm_lists};
   for (void* p : ptrs)
     if (p != nullptr) (void)hipFree(p);
 }
@@ -406,6 +422,20 @@ int spec_verify_set_residual(spec_verify_handle* h, int m, int32_t* out_support,
                 sv::kDriftMaxM);
   if (!aligned(out_support, 4) || !aligned(out_residual, 8))
     return fail(h, SV_EINVAL, "misaligned residual arrays");
+  if (h->topm_lists == nullptr) {
+    // the streaming pass's top-m lists: every (draft row, segment, wavefront)
+    const size_t bytes = (size_t)h->max_batch * h->K * kMaxSeg * sv::kTopmRowSlots * 8;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    if (hipSetDevice(h->device) != hipSuccess)
+      return fail(h, SV_EHIP, "cannot select device %d", h->device);
+    const hipError_t e = hipMalloc((void**)&h->topm_lists, bytes);
+    (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+      h->topm_lists = nullptr;
+      return fail(h, SV_ENOMEM, "top-m lists (%zu bytes): %s", bytes, hipGetErrorString(e));
+    }
+  }
   h->drift_m = m;
   h->drift_sup = out_support;
   h->drift_res = out_residual;
@@ -418,6 +448,7 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
                 hipStream_t stream) {
   if (h == nullptr) return SV_EINVAL;
   h->err[0] = 0;
+  h->topm_nseg = 0;
   if (B < 1 || B > h->max_batch) return fail(h, SV_EINVAL, "B=%d outside [1, %d]", B, h->max_batch);
   if (target == nullptr || tokens == nullptr || out_tokens == nullptr || out_len == nullptr ||
       out_hist == nullptr)
@@ -505,7 +536,11 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   }
   if (rc == SV_OK && mode == SV_MODE_STOCHASTIC && h->drift_sup != nullptr) {
     const double invT = 1.0 / double(temperature);
-    if (vec)
+    if (h->topm_nseg > 0)
+      hipLaunchKernelGGL(sv::drift_merge, dim3(unsigned(B * h->K)), dim3(sv::kWave), 0, stream,
+                         target, draft, h->K, h->V, invT, h->drift_m, h->topm_nseg,
+                         h->topm_lists, h->rules.k, out_len, h->drift_sup, h->drift_res);
+    else if (vec)
       hipLaunchKernelGGL((sv::drift_residual<8>), dim3(unsigned(B * h->K)), dim3(sv::kDriftBlock), 0,
                          stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
                          h->drift_sup, h->drift_res);

@@ -209,25 +209,8 @@ __device__ inline int tab_index(uint32_t bits, int n_half) {
   return off < uint32_t(n_half) ? int(off) + ((bits & 0x8000u) ? kTabStride : 0) : -1;
 }
 
-// Order-preserving 16-bit key of a bf16 value (bits = its 16-bit pattern):
-// 0x8000 + |x| for x >= 0, 0x8000 - |x| for x < 0 (|x| as the 15-bit pattern),
-// so larger values have larger keys and -0 shares the key of +0. Keys run
-// from 1 (the largest negative NaN) to 0xffff; finite values lie in
-// [0x81, 0xff7f], -inf is 0x80 and +inf 0xff80. A truncated row keeps the
-// values whose key is at least its threshold key; threshold 0 keeps all.
-__device__ inline uint32_t bf16_key(uint32_t bits) {
-  const uint32_t mag = bits & 0x7fffu;
-  return (bits & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
-}
-constexpr uint32_t kKeyNegInf = 0x80u, kKeyPosInf = 0xff80u;
-
-// the bf16 value of a key
-__device__ inline float key_value(uint32_t key) {
-  const uint32_t bits = key >= 0x8000u ? key - 0x8000u : (0x8000u | (0x8000u - key));
-  return __uint_as_float(bits << 16);
-}
-
-__device__ inline bool key_finite(uint32_t key) { return key > kKeyNegInf && key < kKeyPosInf; }
+// bf16_key, key_value and key_finite (order keys of bf16 values) are in
+// sv_topm.hpp.
 
 // 2^(x c - R) of a finite bf16 value (by key) in float64 for the truncated
 // path's normalisers and p(d), q(d): the exponent x c - R, formed with the

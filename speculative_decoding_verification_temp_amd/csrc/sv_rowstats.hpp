@@ -11,6 +11,7 @@
 #pragma once
 
 #include "sv_device.hpp"
+#include "sv_topm.hpp"
 
 namespace sv {
 
@@ -34,11 +35,24 @@ __device__ inline const void* row_ptr(const void* target, const void* draft, int
 // the terms are added pairwise in fp32 and the group total is added to S in
 // fp64.
 // --------------------------------------------------------------------------
-template <int DT, int VEC, int U>
+//
+// With TOPM (bf16 chunks of 8 only), the workgroups of draft rows also keep a
+// top-m candidate list per wavefront (sv_topm.hpp) for the draft residual
+// side output and store it, as at most m keys followed by zeros, at
+//   topm_lists[((b K + i) nseg + seg) 4 + wavefront][0..m)
+// (64 slots per list). The list is fed from each full group of chunks the
+// wavefront reads with all 64 lanes together; the few chunks a lane reads
+// after its wavefront's lanes part (at most 2U - 1) are read again and fed
+// at the end. The normaliser is computed exactly as without TOPM.
+constexpr int kTopmCapFused = 448;   // keys per wavefront list in the streaming pass
+
+template <int DT, int VEC, int U, bool TOPM = false>
 __global__ __launch_bounds__(kBlock) void rowstats_sum(
     const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
     int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
-    RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
+    uint64_t* __restrict__ topm_lists) {
+  static_assert(!TOPM || (DT == DT_BF16 && VEC == 8), "top-m lists need bf16 chunks of 8");
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
@@ -58,6 +72,19 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
   const long long nchunks = V / VEC;
   const long long c0 = (long long)seg * seg_chunks;
   const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
+
+  [[maybe_unused]] TopM tm;
+  [[maybe_unused]] const bool topm_row = TOPM && r > K;   // uniform
+  [[maybe_unused]] long long topm_next = c0 + tid;        // first chunk not yet fed
+  if constexpr (TOPM) {
+    __shared__ uint64_t s_tk[kWavesPerBlock][kTopmCapFused];
+    __shared__ uint32_t s_tb[kWavesPerBlock][256];
+    __shared__ unsigned long long s_tt;
+    if (tid == 0) s_tt = 0ull;
+    __syncthreads();
+    tm.init(s_tk[tid / kWave], s_tb[tid / kWave], &s_tt, kTopmCapFused,
+            uint32_t(min(topm_m, V)));
+  }
 
   float R = kRefInit;
   double S = 0.0;
@@ -88,6 +115,12 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
 #pragma unroll
       for (int k = 0; k + w < U * C::N; k += 2 * w) t[k] += t[k + w];
     S += (double)t[0];
+    if constexpr (TOPM) {
+      if (topm_row && __builtin_amdgcn_read_exec() == ~0ull) {   // all 64 lanes here
+        if (__ballot(gm >= tm.thr_f) != 0ull) tm.offer_group<U>(raw, ci, kBlock, (1u << U) - 1u);
+        topm_next = ci + (long long)U * kBlock;
+      }
+    }
   }
   // remainder, one chunk at a time
   for (; ci < c1; ci += kBlock) {
@@ -108,6 +141,27 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
 #pragma unroll
       for (int k = 0; k + w < C::N; k += 2 * w) t[k] += t[k + w];
     S += (double)t[0];
+  }
+
+  if constexpr (TOPM) {
+    if (topm_row) {   // the lanes are together again: feed the chunks read apart
+      typename C::raw_t raw[2 * U - 1];
+      uint32_t valid = 0;
+#pragma unroll
+      for (int j = 0; j < 2 * U - 1; ++j) {
+        const long long cc = topm_next + (long long)j * kBlock;
+        raw[j] = C::load(row, cc < c1 ? cc : c0);
+        valid |= cc < c1 ? 1u << j : 0u;
+      }
+      tm.offer_group<2 * U - 1>(raw, topm_next, kBlock, valid);
+      tm.compact();
+      const int lane = tid & (kWave - 1);
+      uint64_t* out = topm_lists +
+                      ((((long long)b * K + (r - K - 1)) * nseg + seg) * kWavesPerBlock +
+                       tid / kWave) * 64;
+      for (uint32_t e = uint32_t(lane); e < tm.want; e += kWave)
+        out[e] = e < tm.fill ? tm.keys[e] : 0ull;
+    }
   }
 
   // workgroup combine: common reference, exact rescale, fixed-order sums

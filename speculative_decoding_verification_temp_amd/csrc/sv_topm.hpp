@@ -1,0 +1,303 @@
+// Order keys of bf16 values and top-m selection over bf16 rows by
+// wavefront-private candidate lists (gfx950).
+//
+// Token v of a row is ranked by the 48-bit key
+//   (order-preserving bf16 key << 32) | (2^32 - 1 - v),
+// so a larger logit comes first, equal logits fall to the lower index, and no
+// two tokens share a key: the row's top m tokens are its m largest keys. A
+// wavefront appends the keys that reach its threshold to a list in LDS; when
+// the list is nearly full it finds the m-th largest key in it (byte-wise
+// radix select) and keeps only the keys at or above it, which becomes its
+// threshold. The m-th largest key of any part of a row is at most the row's
+// m-th largest, so no top-m token is ever dropped, and the wavefronts of a
+// workgroup may share their thresholds through one LDS word. Filtering costs
+// a float compare per value: a bf16 key reaches the threshold's upper 16 bits
+// exactly when the value, widened to float, is at least the value those bits
+// encode.
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+// Order-preserving 16-bit key of a bf16 value (bits = its 16-bit pattern):
+// 0x8000 + |x| for x >= 0, 0x8000 - |x| for x < 0 (|x| as the 15-bit pattern),
+// so larger values have larger keys and -0 shares the key of +0. Keys run
+// from 1 (the largest negative NaN) to 0xffff; finite values lie in
+// [0x81, 0xff7f], -inf is 0x80 and +inf 0xff80. A truncated row keeps the
+// values whose key is at least its threshold key; threshold 0 keeps all.
+__device__ inline uint32_t bf16_key(uint32_t bits) {
+  const uint32_t mag = bits & 0x7fffu;
+  return (bits & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+}
+constexpr uint32_t kKeyNegInf = 0x80u, kKeyPosInf = 0xff80u;
+
+// the bf16 value of a key
+__device__ inline float key_value(uint32_t key) {
+  const uint32_t bits = key >= 0x8000u ? key - 0x8000u : (0x8000u | (0x8000u - key));
+  return __uint_as_float(bits << 16);
+}
+
+__device__ inline bool key_finite(uint32_t key) { return key > kKeyNegInf && key < kKeyPosInf; }
+
+// the least float whose bf16 key reaches `key` (-inf for keys up to -inf's)
+__device__ inline float key_floor(uint32_t key) {
+  return key <= kKeyNegInf ? -__builtin_inff() : key_value(key);
+}
+
+// LDS written by some lanes of a wavefront, then read by others
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// active lanes of `mask` below this lane
+__device__ inline uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+// The want-th largest (1 <= want <= n) of the n distinct keys buf[0..n), all
+// below 2^48, by byte-wise radix select from the top byte down: each round
+// counts the keys that match the bytes chosen so far into 256 bins private to
+// the wavefront and walks the bins from the top; it stops as soon as a single
+// key is left. Called by all 64 lanes of one wavefront.
+__device__ inline uint64_t wave_kth_largest(const uint64_t* buf, int n, uint32_t want,
+                                            uint32_t* bins) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t prefix = 0, pmask = 0;
+#pragma unroll 1
+  for (int shift = 40; shift >= 0; shift -= 8) {
+    for (int q = lane; q < 256; q += kWave) bins[q] = 0u;
+    wave_sync();
+    for (int e = lane; e < n; e += kWave) {
+      const uint64_t v = buf[e];
+      if ((v & pmask) == prefix) atomicAdd(&bins[uint32_t(v >> shift) & 255u], 1u);
+    }
+    wave_sync();
+    // lane L walks bins 255 - 4L down to 252 - 4L; lanes in order cover 255..0
+    uint32_t c[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = bins[255 - 4 * lane - j];
+      s += c[j];
+    }
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    const uint32_t excl = incl - s;
+    const bool mine = excl < want && incl >= want;   // exactly one lane
+    uint32_t byte = 0, above = 0, at = 0;
+    if (mine) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (at == 0u && acc + c[j] >= want) {
+          byte = uint32_t(255 - 4 * lane - j);
+          above = acc;
+          at = c[j];
+        }
+        acc += c[j];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    byte = __shfl(byte, src, kWave);
+    above = __shfl(above, src, kWave);
+    at = __shfl(at, src, kWave);
+    want -= above;
+    prefix |= uint64_t(byte) << shift;
+    pmask |= uint64_t(255) << shift;
+    wave_sync();                                     // bins are cleared next round
+    if (at == 1u) {
+      uint64_t r = 0;
+      for (int e = lane; e < n; e += kWave) {
+        const uint64_t v = buf[e];
+        if ((v & pmask) == prefix) r = v;
+      }
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(r, o, kWave);
+        r = u > r ? u : r;
+      }
+      return r;
+    }
+  }
+  return prefix;
+}
+
+// bits of value e of a bf16 chunk of 8 (four words, low half first); e may
+// differ between lanes
+__device__ inline uint32_t chunk8_bits(const u32x4& r, int e) {
+  const uint32_t w = (e & 4) ? ((e & 2) ? r[3] : r[2]) : ((e & 2) ? r[1] : r[0]);
+  return (e & 1) ? w >> 16 : w & 0xffffu;
+}
+
+// values of a bf16 chunk of 8 at or above thr_f, as bits 0..7
+__device__ inline uint32_t chunk8_pend(const u32x4& r, float thr_f) {
+  uint32_t pend = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t hi = (e & 1) ? r[e >> 1] & 0xffff0000u : r[e >> 1] << 16;
+    pend |= __uint_as_float(hi) >= thr_f ? 1u << e : 0u;
+  }
+  return pend;
+}
+
+// the largest value of a bf16 chunk of 8 as a float (NaN values ignored)
+__device__ inline float chunk8_max(const u32x4& r) {
+  float mx = __uint_as_float(r[0] << 16);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    const uint32_t hi = (e & 1) ? r[e >> 1] & 0xffff0000u : r[e >> 1] << 16;
+    mx = fmaxf(mx, __uint_as_float(hi));
+  }
+  return mx;
+}
+
+// The candidate list of one wavefront. Every member function is called by all
+// 64 lanes of the wavefront together; fill, thr and thr_f are the same in
+// every lane.
+struct TopM {
+  uint64_t* keys;              // cap entries of LDS
+  uint32_t* bins;              // 256 words of LDS
+  unsigned long long* shared;  // the workgroup's threshold (LDS)
+  uint32_t cap, want;          // list size (>= want + 64); m
+  uint32_t fill;
+  uint64_t thr;                // keys below it cannot be among the m largest
+  float thr_f;                 // key_floor of thr's bf16 key
+
+  __device__ void init(uint64_t* k, uint32_t* b, unsigned long long* s, uint32_t c, uint32_t w) {
+    keys = k;
+    bins = b;
+    shared = s;
+    cap = c;
+    want = w;
+    fill = 0;
+    thr = 0;
+    thr_f = -__builtin_inff();
+  }
+
+  // keep the keys at or above max(the want-th largest key, the shared threshold)
+  __device__ void compact() {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t t = thr;
+    if (fill > want) {
+      const uint64_t kth = wave_kth_largest(keys, int(fill), want, bins);
+      t = kth > t ? kth : t;
+      if (lane == 0) atomicMax(shared, (unsigned long long)t);
+    }
+    const uint64_t sh = __hip_atomic_load(shared, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    t = sh > t ? sh : t;
+    uint32_t out = 0;          // in place: a key moves only to a lower slot
+    for (uint32_t base = 0; base < fill; base += kWave) {
+      const uint32_t e = base + uint32_t(lane);
+      const uint64_t v = e < fill ? keys[e] : 0ull;
+      const bool keep = e < fill && v >= t;
+      const uint64_t mask = __ballot(keep);
+      if (keep) keys[out + lanes_below(mask)] = v;
+      out += uint32_t(__popcll(mask));
+    }
+    wave_sync();
+    fill = out;
+    thr = t;
+    thr_f = key_floor(uint32_t(t >> 32));
+  }
+
+  // Offer the values of one bf16 chunk whose bits in `pend` are set (value e
+  // has index idx0 + e, bits bits_of(e)); one value per lane and round, as
+  // many rounds as the busiest lane needs.
+  template <class BitsOf>
+  __device__ void offer(uint32_t pend, BitsOf bits_of, long long idx0) {
+    while (__ballot(pend != 0u) != 0ull) {
+      if (fill > cap - uint32_t(kWave)) compact();
+      const bool act = pend != 0u;
+      const int e = act ? __builtin_ctz(pend) : 0;
+      pend &= pend - 1u;
+      const uint64_t k =
+          (uint64_t(bf16_key(bits_of(e))) << 32) | uint64_t(~uint32_t(idx0 + e));
+      const bool put = act && k >= thr;
+      const uint64_t mask = __ballot(put);
+      if (put) keys[fill + lanes_below(mask)] = k;
+      fill += uint32_t(__popcll(mask));
+    }
+  }
+
+  // Offer a lane's N bf16 chunks of 8: chunk u holds the values of indexes
+  // 8 c_u .. 8 c_u + 7 with c_u = c0 + u * stride, and is skipped unless bit
+  // u of `valid` is set. Each round takes one chunk per lane among those
+  // whose largest value reaches the threshold, so a lane with one candidate
+  // chunk costs one round.
+  template <int N>
+  __device__ void offer_group(const u32x4 (&raw)[N], long long c0, long long stride,
+                              uint32_t valid) {
+    uint32_t cand = 0;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      cand |= ((valid >> u) & 1u) != 0u && chunk8_max(raw[u]) >= thr_f ? 1u << u : 0u;
+    while (__ballot(cand != 0u) != 0ull) {
+      const bool act = cand != 0u;
+      const int u = act ? __builtin_ctz(cand) : 0;
+      cand &= cand - 1u;
+      // the chunk of this lane's round, by selects on register copies (the
+      // empty asm keeps the compiler from indexing the array in memory)
+      u32x4 ch;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t x = raw[0][w];
+        asm volatile("" : "+v"(x));
+#pragma unroll
+        for (int j = 1; j < N; ++j) {
+          uint32_t y = raw[j][w];
+          asm volatile("" : "+v"(y));
+          x = u == j ? y : x;
+        }
+        ch[w] = x;
+      }
+      const uint32_t pend = act ? chunk8_pend(ch, thr_f) : 0u;
+      offer(pend, [&](int e) { return chunk8_bits(ch, e); }, (c0 + (long long)u * stride) * 8);
+    }
+  }
+};
+
+// The residual side output of one drafted position from its support: the
+// `mm` keys keys[0..mm) (the draft row's top mm tokens, any order) are ranked
+// by key, and at rank r the token and
+//   (x_t(v)/T - LSE_S(x_t/T)) - (x_d(v)/T - LSE_S(x_d/T))
+// are written; slots mm..m-1 get -1 and NaN. One whole wavefront; mm <= 64.
+__device__ inline void support_residual(const uint64_t* keys, uint32_t mm, const void* drow,
+                                        const void* trow, double invT, int m,
+                                        int32_t* __restrict__ out_support,
+                                        double* __restrict__ out_res) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool has = uint32_t(lane) < mm;
+  const uint64_t key = has ? keys[lane] : 0ull;
+  int rank = 0;
+  for (int o = 0; o < int(mm); ++o) {
+    const uint64_t ko = __shfl(key, o, kWave);
+    rank += (has && ko > key) ? 1 : 0;
+  }
+  const int v = has ? int(~uint32_t(key)) : -1;
+  const double ad = has ? double(load_logit<DT_BF16>(drow, v)) * invT : -__builtin_inf();
+  const double at = has ? double(load_logit<DT_BF16>(trow, v)) * invT : -__builtin_inf();
+  double mt = at, md = ad;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    mt = fmax(mt, __shfl_xor(mt, o, kWave));
+    md = fmax(md, __shfl_xor(md, o, kWave));
+  }
+  const double lse_t = mt + log(wave_sum(has ? exp(at - mt) : 0.0));
+  const double lse_d = md + log(wave_sum(has ? exp(ad - md) : 0.0));
+  if (has) {
+    out_support[rank] = v;
+    out_res[rank] = (at - lse_t) - (ad - lse_d);
+  } else if (lane < m) {
+    out_support[lane] = -1;
+    out_res[lane] = __builtin_nan("");
+  }
+}
+
+}  // namespace sv

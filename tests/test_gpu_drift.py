@@ -4,7 +4,10 @@ Supports must match exactly (token ids in order); residuals within 1e-9
 (both sides sum the same 32 float64 exponentials in different orders).
 Cases: a full c2 batch with per-sequence draft counts and invalid sequences,
 rows with many ties, V below m, -inf logits inside the support, draft rows
-with more than 65535 equal values (the histogram's careful recount), and
+with 70000 equal values, every route to the support (the streaming pass's
+candidate lists with one and three segments per row, the kernel that reads
+the rows itself after truncation, on rows not in 16-byte chunks and after the
+one-kernel path), verification outputs unchanged by the side output, and
 argument errors.
 """
 
@@ -84,7 +87,7 @@ def test_residual_v_below_m_and_neg_inf(sv):
     _check(x, cfg, 32, sup, res, alen, label="residual/V<m")
 
 
-def test_residual_wrapped_counters(sv):
+def test_residual_70000_way_tie(sv):
     cfg = CONFIGS["c3"].scaled(B=2, K=2)
     x = make_inputs(cfg, 8, DEV)
     g = torch.Generator(device=DEV)
@@ -94,7 +97,7 @@ def test_residual_wrapped_counters(sv):
             perm = torch.randperm(cfg.V, generator=g, device=DEV)
             x["draft"][b, i, perm[:70000]] = 5.0 if b == 0 else -5.0   # a 70000-way tie
     sup, res, alen = _run(sv, x, cfg, 32)
-    _check(x, cfg, 32, sup, res, alen, label="residual/wrapped counters")
+    _check(x, cfg, 32, sup, res, alen, label="residual/70000-way tie")
 
 
 def test_set_residual_arguments(sv):
@@ -110,3 +113,45 @@ def test_set_residual_arguments(sv):
     assert v.lib.spec_verify_set_residual(v._h, 8, sv._ptr(buf), None) == sv.SV_EINVAL
     assert v.lib.spec_verify_set_residual(v._h, 8, None, None) == sv.SV_OK
     assert v.lib.spec_verify_set_residual(None, 8, None, None) == sv.SV_EINVAL
+
+
+@pytest.mark.parametrize("route", ["streaming", "streaming-3seg", "own-truncated", "own-scalar",
+                                   "own-one-kernel"])
+def test_residual_routes(sv, monkeypatch, route):
+    """Every route to the support: the streaming pass's lists (one and three
+    segments per row) and the kernel that reads the draft rows itself (with
+    truncation, on rows not in 16-byte chunks, after the one-kernel path)."""
+    monkeypatch.setenv("SPEC_VERIFY_NSEG", "3" if route == "streaming-3seg" else "0")
+    monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "1" if route == "own-one-kernel" else "0")
+    V = {"own-scalar": 4001, "streaming-3seg": 40000}.get(route, 8000)   # 3 segments need V/8 >= 3072
+    cfg = CONFIGS["c2"].scaled(B=24, V=V)
+    x = make_inputs(cfg, 11, DEV)
+    x["draft"][1] = torch.round(x["draft"][1].float() * 2).to(x["draft"].dtype) / 2   # ties
+    x["draft"][2, 0, ::3] = float("-inf")
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    if route == "own-truncated":
+        v.set_truncation(torch.full((cfg.B,), 50, dtype=torch.int32, device=DEV),
+                         torch.full((cfg.B,), 0.9, dtype=torch.float32, device=DEV))
+    sup, res = v.set_residual(16)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+    torch.cuda.synchronize()
+    _check(x, cfg, 16, sup.cpu().numpy(), res.cpu().numpy(), alen.cpu().numpy(),
+           label=f"residual/{route}")
+
+
+def test_residual_leaves_verification_unchanged(sv):
+    """The streaming pass computes its normalisers the same way with the
+    top-m lists on: tokens, accept lengths and the histogram are bitwise
+    those of a call without the side output."""
+    cfg = CONFIGS["c3"].scaled(B=64)
+    x = make_inputs(cfg, 12, DEV)
+    outs = []
+    for m in (0, 32):
+        v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+        if m:
+            v.set_residual(m)
+        tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+        torch.cuda.synchronize()
+        outs.append((tok.cpu().numpy(), alen.cpu().numpy(), hist.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
