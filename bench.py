@@ -37,10 +37,10 @@ def log(msg):
 
 # the sources that define each streaming kernel whose traffic is recorded
 STREAM_SOURCES = {
-    "rowstats_sum": ("sv_device.hpp", "sv_rowstats.hpp"),
-    "rowstats_max": ("sv_device.hpp", "sv_rowstats.hpp"),
-    "rowstats_trunc_win": ("sv_device.hpp", "sv_rowstats.hpp", "sv_kernels.hpp", "sv_fused.hpp",
-                           "sv_trunc.hpp"),
+    "rowstats_sum": ("sv_device.hpp", "sv_topm.hpp", "sv_rowstats.hpp"),
+    "rowstats_max": ("sv_device.hpp", "sv_topm.hpp", "sv_rowstats.hpp"),
+    "rowstats_trunc_win": ("sv_device.hpp", "sv_topm.hpp", "sv_rowstats.hpp", "sv_kernels.hpp",
+                           "sv_fused.hpp", "sv_trunc.hpp"),
 }
 
 
@@ -312,7 +312,8 @@ def main():
     kernel = ("rowstats_trunc_win" if trunc else "rowstats_sum") if mode == "stochastic" \
         else "rowstats_max"
     achieved = pass_bytes / (pass_avg * 1e-3) / 1e9
-    workload = f"{cfg.name}/{mode}" + (f"/top-k{args.top_k}-top-p{args.top_p}" if trunc else "")
+    workload = f"{cfg.name}/{mode}" + (f"/top-k{args.top_k}-top-p{args.top_p}" if trunc else "") \
+        + (f"/residual{args.residual}" if args.residual and mode == "stochastic" else "")
     traffic = traffic_for(workload, kernel) if args.stops == "none" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

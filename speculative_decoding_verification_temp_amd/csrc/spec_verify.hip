@@ -537,7 +537,9 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   if (rc == SV_OK && mode == SV_MODE_STOCHASTIC && h->drift_sup != nullptr) {
     const double invT = 1.0 / double(temperature);
     if (h->topm_nseg > 0)
-      hipLaunchKernelGGL(sv::drift_merge, dim3(unsigned(B * h->K)), dim3(sv::kWave), 0, stream,
+      hipLaunchKernelGGL(sv::drift_merge, dim3(unsigned(B * h->K)), dim3(sv::kWave),
+                         size_t(h->topm_nseg) * sv::kWavesPerBlock * std::min(h->drift_m, h->V) * 8,
+                         stream,
                          target, draft, h->K, h->V, invT, h->drift_m, h->topm_nseg,
                          h->topm_lists, h->rules.k, out_len, h->drift_sup, h->drift_res);
     else if (vec)

@@ -146,13 +146,14 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
 
 // Per drafted position: the m largest keys of the lists the streaming pass
 // stored for its draft row (nseg segments x 4 wavefronts, mm slots each,
-// empty slots 0), then the residuals. One wavefront per drafted position.
+// empty slots 0), then the residuals. One wavefront per drafted position;
+// dynamic LDS of nseg * 4 * min(m, V) keys.
 __global__ __launch_bounds__(kWave) void drift_merge(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, double invT,
     int m, int nseg, const uint64_t* __restrict__ lists, const int32_t* __restrict__ kdraft,
     const int32_t* __restrict__ accept_len, int32_t* __restrict__ out_support,
     double* __restrict__ out_res) {
-  __shared__ uint64_t s_keys[kMergeCap];
+  extern __shared__ uint64_t s_keys[];
   __shared__ uint32_t s_bins[256];
   __shared__ unsigned long long s_thr;
   const int lane = threadIdx.x;
@@ -162,18 +163,29 @@ __global__ __launch_bounds__(kWave) void drift_merge(
   if (accept_len[b] < 0 || i >= kb) return no_support(m, out_support + o0, out_res + o0);
   const uint32_t mm = uint32_t(min(m, V));
   const uint64_t* L = lists + ((long long)b * K + i) * nseg * kTopmRowSlots;
+  // slot e of the nseg * 4 lists of mm slots: list e / mm, slot e % mm; eight
+  // loads per lane are issued before any is used
+  const uint32_t n_slots = uint32_t(nseg * kWavesPerBlock) * mm;
   uint32_t fill = 0;
-  for (int l = 0; l < nseg * kWavesPerBlock; ++l) {
-    const uint64_t k = uint32_t(lane) < mm ? L[l * kTopmListSlots + lane] : 0ull;
-    const bool put = k != 0ull;                 // keys are never 0
-    const uint64_t mask = __ballot(put);
-    if (put) s_keys[fill + lanes_below(mask)] = k;
-    fill += uint32_t(__popcll(mask));
+  for (uint32_t base = 0; base < n_slots; base += 8u * kWave) {
+    uint64_t k[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t e = base + uint32_t(q * kWave + lane);
+      k[q] = e < n_slots ? L[(e / mm) * kTopmListSlots + e % mm] : 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool put = k[q] != 0ull;                   // keys are never 0
+      const uint64_t mask = __ballot(put);
+      if (put) s_keys[fill + lanes_below(mask)] = k[q];
+      fill += uint32_t(__popcll(mask));
+    }
   }
   if (lane == 0) s_thr = 0ull;
   wave_sync();
   TopM tm;
-  tm.init(s_keys, s_bins, &s_thr, kMergeCap, mm);
+  tm.init(s_keys, s_bins, &s_thr, n_slots, mm);
   tm.fill = fill;
   tm.compact();                                 // exactly mm keys remain
   support_residual(s_keys, mm, row_ptr<DT_BF16>(target, draft, b, K + 1 + i, K, V),
