@@ -155,3 +155,34 @@ def test_residual_leaves_verification_unchanged(sv):
         outs.append((tok.cpu().numpy(), alen.cpu().numpy(), hist.cpu().numpy()))
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_residual_c3_sampled(sv):
+    """The full c3 batch with m = 32 as bench.py runs it (the streaming pass's
+    lists): at every drafted position the support's draft logits, in order,
+    are the 32 largest of the row (torch's topk as the checker) and the
+    residual is finite; sampled positions match the oracle exactly."""
+    cfg = CONFIGS["c3"]
+    x = make_inputs(cfg, 13, DEV)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    sup, res = v.set_residual(32)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+    torch.cuda.synchronize()
+    valid = alen >= 0
+    assert bool(valid.all())
+    top = torch.topk(x["draft"].float(), 32, dim=-1).values          # [B, K, 32], descending
+    got = torch.gather(x["draft"].float(), 2, sup.long())
+    assert torch.equal(got, top)
+    assert bool(torch.isfinite(res).all())
+    rng = np.random.default_rng(14)
+    picks = rng.choice(cfg.B * cfg.K, 48, replace=False)
+    T32 = float(np.float32(x["T"]))
+    s_np, r_np = sup.cpu().numpy(), res.cpu().numpy()
+    for p in picks:
+        b, i = divmod(int(p), cfg.K)
+        S, r = O.drift_residual(to_host_f64(x["target"][b, i]), to_host_f64(x["draft"][b, i]),
+                                T32, 32)
+        assert np.array_equal(s_np[b, i], S), (b, i)
+        assert np.max(np.abs(r_np[b, i] - r)) <= TOL, (b, i)
+    print(f"residual/c3: {cfg.B * cfg.K} positions against topk, {len(picks)} against the oracle",
+          flush=True)
