@@ -269,8 +269,8 @@ int spec_verify_set_policy(spec_verify_handle *h, const float *draft_conf, doubl
  * The first call with out_support set allocates the candidate lists,
  * max_batch * K * 32 KiB on the handle's device, kept until
  * spec_verify_destroy (SV_ENOMEM if that fails); spec_verify itself still
- * allocates nothing. bf16 logits only (SV_EUNSUPPORTED otherwise);
- * 1 <= m <= 64 (else SV_EINVAL). out_support = NULL turns it off.
+ * allocates nothing. bf16 and fp32 logits; 1 <= m <= 64 (else
+ * SV_EINVAL). out_support = NULL turns it off.
  */
 int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
                              double *out_residual);

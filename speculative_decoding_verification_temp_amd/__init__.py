@@ -203,7 +203,7 @@ class SpecVerifier:
         self.set_truncation(None, None)
 
     def set_residual(self, m: int = 32):
-        """Draft residual side output for later stochastic calls (bf16). m = 0
+        """Draft residual side output for later stochastic calls. m = 0
         turns it off. Returns (support [max_batch, K, m] int32, residual
         [max_batch, K, m] float64), device tensors the calls write."""
         if m == 0:

@@ -155,7 +155,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   const int grid_seq = div_up(B, sv::kWavesPerBlock);
   prof_mark(h, 0, s);
   bool topm = false;
-  if constexpr (DT == sv::DT_BF16 && VEC == 8) {
+  if constexpr ((DT == sv::DT_BF16 && VEC == 8) || (DT == sv::DT_F32 && VEC == 4)) {
     // the residual side output takes its draft-row candidates from this pass
     if (h->drift_sup != nullptr && h->topm_lists != nullptr) {
       hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U, true>), dim3(unsigned(B * rows * L.nseg)),
@@ -279,6 +279,27 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);
   return check_launch(h, "scan_argmax");
+}
+
+// The residual side output after a stochastic call: from the streaming pass's
+// lists when this call's pass kept them, else reading the draft rows.
+template <int DT, int VEC>
+void launch_residual(spec_verify_handle* h, int B, bool vec, const void* target,
+                     const void* draft, double invT, const int32_t* out_len, hipStream_t s) {
+  const dim3 grid(unsigned(B * h->K));
+  if (h->topm_nseg > 0)
+    hipLaunchKernelGGL(sv::drift_merge<DT>, grid, dim3(sv::kWave),
+                       size_t(h->topm_nseg) * sv::kWavesPerBlock * std::min(h->drift_m, h->V) * 8,
+                       s, target, draft, h->K, h->V, invT, h->drift_m, h->topm_nseg,
+                       h->topm_lists, h->rules.k, out_len, h->drift_sup, h->drift_res);
+  else if (vec)
+    hipLaunchKernelGGL((sv::drift_residual<DT, VEC>), grid, dim3(sv::kDriftBlock), 0, s, target,
+                       draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len, h->drift_sup,
+                       h->drift_res);
+  else
+    hipLaunchKernelGGL((sv::drift_residual<DT, 1>), grid, dim3(sv::kDriftBlock), 0, s, target,
+                       draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len, h->drift_sup,
+                       h->drift_res);
 }
 
 void free_all(spec_verify_handle* h) {
@@ -415,8 +436,6 @@ int spec_verify_set_residual(spec_verify_handle* h, int m, int32_t* out_support,
     h->drift_m = 0;
     return SV_OK;
   }
-  if (h->dtype != SV_DTYPE_BF16)
-    return fail(h, SV_EUNSUPPORTED, "the residual side output is implemented for bf16 logits");
   if (m < 1 || m > sv::kDriftMaxM || out_residual == nullptr)
     return fail(h, SV_EINVAL, "residual side output needs 1 <= m <= %d and both arrays",
                 sv::kDriftMaxM);
@@ -536,20 +555,10 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   }
   if (rc == SV_OK && mode == SV_MODE_STOCHASTIC && h->drift_sup != nullptr) {
     const double invT = 1.0 / double(temperature);
-    if (h->topm_nseg > 0)
-      hipLaunchKernelGGL(sv::drift_merge, dim3(unsigned(B * h->K)), dim3(sv::kWave),
-                         size_t(h->topm_nseg) * sv::kWavesPerBlock * std::min(h->drift_m, h->V) * 8,
-                         stream,
-                         target, draft, h->K, h->V, invT, h->drift_m, h->topm_nseg,
-                         h->topm_lists, h->rules.k, out_len, h->drift_sup, h->drift_res);
-    else if (vec)
-      hipLaunchKernelGGL((sv::drift_residual<8>), dim3(unsigned(B * h->K)), dim3(sv::kDriftBlock), 0,
-                         stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
-                         h->drift_sup, h->drift_res);
+    if (h->dtype == SV_DTYPE_BF16)
+      launch_residual<sv::DT_BF16, 8>(h, B, vec, target, draft, invT, out_len, stream);
     else
-      hipLaunchKernelGGL((sv::drift_residual<1>), dim3(unsigned(B * h->K)), dim3(sv::kDriftBlock), 0,
-                         stream, target, draft, h->K, h->V, invT, h->drift_m, h->rules.k, out_len,
-                         h->drift_sup, h->drift_res);
+      launch_residual<sv::DT_F32, 4>(h, B, vec, target, draft, invT, out_len, stream);
     rc = check_launch(h, "drift_residual");
   }
   if (rc == SV_OK) {

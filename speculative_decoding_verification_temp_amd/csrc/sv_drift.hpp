@@ -18,6 +18,7 @@
 //   - drift_residual, one 256-thread workgroup per drafted position that
 //     reads the draft row once, for calls whose rows are read by another pass
 //     (truncation, one kernel per sequence) or are not in 16-byte chunks.
+// Logits are bf16 or fp32 (DT).
 // Only valid sequences (the scan's accept length is read to tell) and drafted
 // positions i < k_b get a support; both routes end in support_residual.
 #pragma once
@@ -44,13 +45,14 @@ __device__ inline void no_support(int m, int32_t* out_support, double* out_res) 
   }
 }
 
-template <int VEC>
+template <int DT, int VEC>
 __global__ __launch_bounds__(kDriftBlock) void drift_residual(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, double invT,
     int m, const int32_t* __restrict__ kdraft, const int32_t* __restrict__ accept_len,
     int32_t* __restrict__ out_support, double* __restrict__ out_res) {
-  using C = Chunk<DT_BF16, VEC>;
+  using C = Chunk<DT, VEC>;
   using raw_t = typename C::raw_t;
+  constexpr bool kVector = VEC > 1;         // 16-byte chunks (8 bf16 or 4 fp32)
   __shared__ uint64_t s_keys[kDriftWaves][kDriftCap];
   __shared__ uint32_t s_bins[kDriftWaves][256];
   __shared__ uint32_t s_count[kDriftWaves];
@@ -60,12 +62,12 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   const long long o0 = ((long long)b * K + i) * m;
   const int kb = kdraft != nullptr ? kdraft[b] : K;
   if (accept_len[b] < 0 || i >= kb) return no_support(m, out_support + o0, out_res + o0);
-  const void* drow = row_ptr<DT_BF16>(target, draft, b, K + 1 + i, K, V);
-  const void* trow = row_ptr<DT_BF16>(target, draft, b, i, K, V);
+  const void* drow = row_ptr<DT>(target, draft, b, K + 1 + i, K, V);
+  const void* trow = row_ptr<DT>(target, draft, b, i, K, V);
   const uint32_t mm = uint32_t(min(m, V));
   if (tid == 0) s_thr = 0ull;
   __syncthreads();
-  TopM tm;
+  TopM<DT> tm;
   tm.init(s_keys[wid], s_bins[wid], &s_thr, kDriftCap, mm);
 
   // ---- one read of the draft row; one group's loads are in flight while
@@ -82,34 +84,23 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
     }
   };
   auto filter_group = [&](long long it, const raw_t (&raw)[kDriftUnroll]) {
-    if constexpr (VEC == 8) {
+    if constexpr (kVector) {
       const long long c0 = it * kDriftUnroll * kDriftBlock + tid;
       uint32_t valid = 0;
 #pragma unroll
       for (int u = 0; u < kDriftUnroll; ++u)
         valid |= c0 + (long long)u * kDriftBlock < nchunks ? 1u << u : 0u;
-      tm.offer_group<kDriftUnroll>(raw, c0, kDriftBlock, valid);
-      return;
-    }
+      tm.template offer_group<kDriftUnroll>(raw, c0, kDriftBlock, valid);
+    } else {
 #pragma unroll
-    for (int u = 0; u < kDriftUnroll; ++u) {
-      const long long ci = (it * kDriftUnroll + u) * kDriftBlock + tid;
-      uint32_t pend;
-      if constexpr (VEC == 8)
-        pend = chunk8_pend(raw[u], tm.thr_f);
-      else
-        pend = __uint_as_float(raw[u] << 16) >= tm.thr_f ? 1u : 0u;
-      if (ci >= nchunks) pend = 0u;
-      if (__ballot(pend != 0u) == 0ull) continue;   // uniform: the common case
-      tm.offer(
-          pend,
-          [&](int e) -> uint32_t {
-            if constexpr (VEC == 8)
-              return chunk8_bits(raw[u], e);
-            else
-              return raw[u];
-          },
-          ci * VEC);
+      for (int u = 0; u < kDriftUnroll; ++u) {
+        const long long ci = (it * kDriftUnroll + u) * kDriftBlock + tid;
+        // one value per chunk: its bits in raw[u]
+        const float x = __uint_as_float(DT == DT_BF16 ? raw[u] << 16 : raw[u]);
+        const uint32_t pend = ci < nchunks && x >= tm.thr_f ? 1u : 0u;
+        if (__ballot(pend != 0u) == 0ull) continue;   // uniform: the common case
+        tm.offer(pend, [&](int) -> uint32_t { return raw[u]; }, ci);
+      }
     }
   };
   {
@@ -141,13 +132,14 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   wave_sync();
   tm.fill = n;
   tm.compact();                                 // exactly mm keys remain
-  support_residual(s_keys[0], mm, drow, trow, invT, m, out_support + o0, out_res + o0);
+  support_residual<DT>(s_keys[0], mm, drow, trow, invT, m, out_support + o0, out_res + o0);
 }
 
 // Per drafted position: the m largest keys of the lists the streaming pass
 // stored for its draft row (nseg segments x 4 wavefronts, mm slots each,
 // empty slots 0), then the residuals. One wavefront per drafted position;
 // dynamic LDS of nseg * 4 * min(m, V) keys.
+template <int DT>
 __global__ __launch_bounds__(kWave) void drift_merge(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, double invT,
     int m, int nseg, const uint64_t* __restrict__ lists, const int32_t* __restrict__ kdraft,
@@ -184,13 +176,13 @@ __global__ __launch_bounds__(kWave) void drift_merge(
   }
   if (lane == 0) s_thr = 0ull;
   wave_sync();
-  TopM tm;
+  TopM<DT> tm;
   tm.init(s_keys, s_bins, &s_thr, n_slots, mm);
   tm.fill = fill;
   tm.compact();                                 // exactly mm keys remain
-  support_residual(s_keys, mm, row_ptr<DT_BF16>(target, draft, b, K + 1 + i, K, V),
-                   row_ptr<DT_BF16>(target, draft, b, i, K, V), invT, m, out_support + o0,
-                   out_res + o0);
+  support_residual<DT>(s_keys, mm, row_ptr<DT>(target, draft, b, K + 1 + i, K, V),
+                       row_ptr<DT>(target, draft, b, i, K, V), invT, m, out_support + o0,
+                       out_res + o0);
 }
 
 }  // namespace sv

@@ -36,7 +36,7 @@ __device__ inline const void* row_ptr(const void* target, const void* draft, int
 // fp64.
 // --------------------------------------------------------------------------
 //
-// With TOPM (bf16 chunks of 8 only), the workgroups of draft rows also keep a
+// With TOPM (16-byte chunks only), the workgroups of draft rows also keep a
 // top-m candidate list per wavefront (sv_topm.hpp) for the draft residual
 // side output and store it, as at most m keys followed by zeros, at
 //   topm_lists[((b K + i) nseg + seg) 4 + wavefront][0..m)
@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
     int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
     uint64_t* __restrict__ topm_lists) {
-  static_assert(!TOPM || (DT == DT_BF16 && VEC == 8), "top-m lists need bf16 chunks of 8");
+  static_assert(!TOPM || (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4),
+                "top-m lists need 16-byte chunks");
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
   const long long c0 = (long long)seg * seg_chunks;
   const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
 
-  [[maybe_unused]] TopM tm;
+  [[maybe_unused]] TopM<DT> tm;
   [[maybe_unused]] const bool topm_row = TOPM && r > K;   // uniform
   [[maybe_unused]] long long topm_next = c0 + tid;        // first chunk not yet fed
   if constexpr (TOPM) {
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
     S += (double)t[0];
     if constexpr (TOPM) {
       if (topm_row && __builtin_amdgcn_read_exec() == ~0ull) {   // all 64 lanes here
-        if (__ballot(gm >= tm.thr_f) != 0ull) tm.offer_group<U>(raw, ci, kBlock, (1u << U) - 1u);
+        if (__ballot(gm >= tm.thr_f) != 0ull) tm.template offer_group<U>(raw, ci, kBlock, (1u << U) - 1u);
         topm_next = ci + (long long)U * kBlock;
       }
     }
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
         raw[j] = C::load(row, cc < c1 ? cc : c0);
         valid |= cc < c1 ? 1u << j : 0u;
       }
-      tm.offer_group<2 * U - 1>(raw, topm_next, kBlock, valid);
+      tm.template offer_group<2 * U - 1>(raw, topm_next, kBlock, valid);
       tm.compact();
       const int lane = tid & (kWave - 1);
       uint64_t* out = topm_lists +

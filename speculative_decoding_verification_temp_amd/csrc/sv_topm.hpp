@@ -1,8 +1,9 @@
-// Order keys of bf16 values and top-m selection over bf16 rows by
+// Order keys of logits and top-m selection over logit rows by
 // wavefront-private candidate lists (gfx950).
 //
-// Token v of a row is ranked by the 48-bit key
-//   (order-preserving bf16 key << 32) | (2^32 - 1 - v),
+// Token v of a row is ranked by the key
+//   (order-preserving key of its logit << 32) | (2^32 - 1 - v),
+// 48 bits for bf16 logits (16-bit order key), 64 for fp32 (32-bit),
 // so a larger logit comes first, equal logits fall to the lower index, and no
 // two tokens share a key: the row's top m tokens are its m largest keys. A
 // wavefront appends the keys that reach its threshold to a list in LDS; when
@@ -11,9 +12,9 @@
 // threshold. The m-th largest key of any part of a row is at most the row's
 // m-th largest, so no top-m token is ever dropped, and the wavefronts of a
 // workgroup may share their thresholds through one LDS word. Filtering costs
-// a float compare per value: a bf16 key reaches the threshold's upper 16 bits
-// exactly when the value, widened to float, is at least the value those bits
-// encode.
+// a float compare per value: a logit's order key reaches the threshold's
+// upper 32 bits exactly when the logit, as a float, is at least the value
+// those bits encode.
 #pragma once
 
 #include "sv_device.hpp"
@@ -45,6 +46,37 @@ __device__ inline float key_floor(uint32_t key) {
   return key <= kKeyNegInf ? -__builtin_inff() : key_value(key);
 }
 
+// Order key of a logit of type DT from its bits, the bf16 construction on 32
+// bits for fp32 (-0 and +0 alike); keys are never 0 for non-NaN values.
+template <int DT>
+__device__ inline uint32_t order_key(uint32_t bits) {
+  if constexpr (DT == DT_BF16) {
+    return bf16_key(bits);
+  } else {
+    const uint32_t mag = bits & 0x7fffffffu;
+    return (bits & 0x80000000u) ? 0x80000000u - mag : 0x80000000u + mag;
+  }
+}
+
+// the least float whose order key reaches `key` (-inf for keys up to -inf's)
+template <int DT>
+__device__ inline float order_floor(uint32_t key) {
+  if constexpr (DT == DT_BF16) {
+    return key_floor(key);
+  } else {
+    constexpr uint32_t kNegInfKey = 0x80000000u - 0x7f800000u;
+    if (key <= kNegInfKey) return -__builtin_inff();
+    const uint32_t bits = key >= 0x80000000u ? key - 0x80000000u : 0x80000000u | (0x80000000u - key);
+    return __uint_as_float(bits);
+  }
+}
+
+// the shift of the top byte of a token key
+template <int DT>
+constexpr int key_top_shift() {
+  return DT == DT_BF16 ? 40 : 56;
+}
+
 // LDS written by some lanes of a wavefront, then read by others
 __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -59,16 +91,16 @@ __device__ inline uint32_t lanes_below(uint64_t mask) {
 }
 
 // The want-th largest (1 <= want <= n) of the n distinct keys buf[0..n), all
-// below 2^48, by byte-wise radix select from the top byte down: each round
+// below 2^(top_shift + 8), by byte-wise radix select from the top byte down: each round
 // counts the keys that match the bytes chosen so far into 256 bins private to
 // the wavefront and walks the bins from the top; it stops as soon as a single
 // key is left. Called by all 64 lanes of one wavefront.
 __device__ inline uint64_t wave_kth_largest(const uint64_t* buf, int n, uint32_t want,
-                                            uint32_t* bins) {
+                                            uint32_t* bins, int top_shift) {
   const int lane = threadIdx.x & (kWave - 1);
   uint64_t prefix = 0, pmask = 0;
 #pragma unroll 1
-  for (int shift = 40; shift >= 0; shift -= 8) {
+  for (int shift = top_shift; shift >= 0; shift -= 8) {
     for (int q = lane; q < 256; q += kWave) bins[q] = 0u;
     wave_sync();
     for (int e = lane; e < n; e += kWave) {
@@ -129,38 +161,52 @@ __device__ inline uint64_t wave_kth_largest(const uint64_t* buf, int n, uint32_t
   return prefix;
 }
 
-// bits of value e of a bf16 chunk of 8 (four words, low half first); e may
-// differ between lanes
-__device__ inline uint32_t chunk8_bits(const u32x4& r, int e) {
-  const uint32_t w = (e & 4) ? ((e & 2) ? r[3] : r[2]) : ((e & 2) ? r[1] : r[0]);
-  return (e & 1) ? w >> 16 : w & 0xffffu;
-}
+// Values of a 16-byte chunk of logits: 8 bf16 (low half of each word first)
+// or 4 fp32.
+template <int DT> struct ChunkVals;
+template <> struct ChunkVals<DT_BF16> {
+  static constexpr int N = 8;
+  // value e as a float (e known at compile time)
+  __device__ static float value(const u32x4& r, int e) {
+    return __uint_as_float((e & 1) ? r[e >> 1] & 0xffff0000u : r[e >> 1] << 16);
+  }
+  // bits of value e (e may differ between lanes)
+  __device__ static uint32_t bits(const u32x4& r, int e) {
+    const uint32_t w = (e & 4) ? ((e & 2) ? r[3] : r[2]) : ((e & 2) ? r[1] : r[0]);
+    return (e & 1) ? w >> 16 : w & 0xffffu;
+  }
+};
+template <> struct ChunkVals<DT_F32> {
+  static constexpr int N = 4;
+  __device__ static float value(const u32x4& r, int e) { return __uint_as_float(r[e]); }
+  __device__ static uint32_t bits(const u32x4& r, int e) {
+    return (e & 2) ? ((e & 1) ? r[3] : r[2]) : ((e & 1) ? r[1] : r[0]);
+  }
+};
 
-// values of a bf16 chunk of 8 at or above thr_f, as bits 0..7
-__device__ inline uint32_t chunk8_pend(const u32x4& r, float thr_f) {
+// the values of a chunk at or above thr_f, as bits 0..N-1
+template <int DT>
+__device__ inline uint32_t chunk_pend(const u32x4& r, float thr_f) {
   uint32_t pend = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t hi = (e & 1) ? r[e >> 1] & 0xffff0000u : r[e >> 1] << 16;
-    pend |= __uint_as_float(hi) >= thr_f ? 1u << e : 0u;
-  }
+  for (int e = 0; e < ChunkVals<DT>::N; ++e)
+    pend |= ChunkVals<DT>::value(r, e) >= thr_f ? 1u << e : 0u;
   return pend;
 }
 
-// the largest value of a bf16 chunk of 8 as a float (NaN values ignored)
-__device__ inline float chunk8_max(const u32x4& r) {
-  float mx = __uint_as_float(r[0] << 16);
+// the largest value of a chunk (NaN values ignored)
+template <int DT>
+__device__ inline float chunk_max(const u32x4& r) {
+  float mx = ChunkVals<DT>::value(r, 0);
 #pragma unroll
-  for (int e = 1; e < 8; ++e) {
-    const uint32_t hi = (e & 1) ? r[e >> 1] & 0xffff0000u : r[e >> 1] << 16;
-    mx = fmaxf(mx, __uint_as_float(hi));
-  }
+  for (int e = 1; e < ChunkVals<DT>::N; ++e) mx = fmaxf(mx, ChunkVals<DT>::value(r, e));
   return mx;
 }
 
-// The candidate list of one wavefront. Every member function is called by all
-// 64 lanes of the wavefront together; fill, thr and thr_f are the same in
-// every lane.
+// The candidate list of one wavefront over logits of type DT. Every member
+// function is called by all 64 lanes of the wavefront together; fill, thr
+// and thr_f are the same in every lane.
+template <int DT>
 struct TopM {
   uint64_t* keys;              // cap entries of LDS
   uint32_t* bins;              // 256 words of LDS
@@ -168,7 +214,7 @@ struct TopM {
   uint32_t cap, want;          // list size (>= want + 64); m
   uint32_t fill;
   uint64_t thr;                // keys below it cannot be among the m largest
-  float thr_f;                 // key_floor of thr's bf16 key
+  float thr_f;                 // order_floor of thr's logit key
 
   __device__ void init(uint64_t* k, uint32_t* b, unsigned long long* s, uint32_t c, uint32_t w) {
     keys = k;
@@ -186,7 +232,7 @@ struct TopM {
     const int lane = threadIdx.x & (kWave - 1);
     uint64_t t = thr;
     if (fill > want) {
-      const uint64_t kth = wave_kth_largest(keys, int(fill), want, bins);
+      const uint64_t kth = wave_kth_largest(keys, int(fill), want, bins, key_top_shift<DT>());
       t = kth > t ? kth : t;
       if (lane == 0) atomicMax(shared, (unsigned long long)t);
     }
@@ -204,12 +250,12 @@ struct TopM {
     wave_sync();
     fill = out;
     thr = t;
-    thr_f = key_floor(uint32_t(t >> 32));
+    thr_f = order_floor<DT>(uint32_t(t >> 32));
   }
 
-  // Offer the values of one bf16 chunk whose bits in `pend` are set (value e
-  // has index idx0 + e, bits bits_of(e)); one value per lane and round, as
-  // many rounds as the busiest lane needs.
+  // Offer the values of one chunk whose bits in `pend` are set (value e has
+  // index idx0 + e and logit bits bits_of(e)); one value per lane and round,
+  // as many rounds as the busiest lane needs.
   template <class BitsOf>
   __device__ void offer(uint32_t pend, BitsOf bits_of, long long idx0) {
     while (__ballot(pend != 0u) != 0ull) {
@@ -218,7 +264,7 @@ struct TopM {
       const int e = act ? __builtin_ctz(pend) : 0;
       pend &= pend - 1u;
       const uint64_t k =
-          (uint64_t(bf16_key(bits_of(e))) << 32) | uint64_t(~uint32_t(idx0 + e));
+          (uint64_t(order_key<DT>(bits_of(e))) << 32) | uint64_t(~uint32_t(idx0 + e));
       const bool put = act && k >= thr;
       const uint64_t mask = __ballot(put);
       if (put) keys[fill + lanes_below(mask)] = k;
@@ -226,8 +272,9 @@ struct TopM {
     }
   }
 
-  // Offer a lane's N bf16 chunks of 8: chunk u holds the values of indexes
-  // 8 c_u .. 8 c_u + 7 with c_u = c0 + u * stride, and is skipped unless bit
+  // Offer a lane's N 16-byte chunks: chunk u holds the values of indexes
+  // E c_u .. E c_u + E - 1 (E values per chunk) with c_u = c0 + u * stride,
+  // and is skipped unless bit
   // u of `valid` is set. Each round takes one chunk per lane among those
   // whose largest value reaches the threshold, so a lane with one candidate
   // chunk costs one round.
@@ -237,7 +284,7 @@ struct TopM {
     uint32_t cand = 0;
 #pragma unroll
     for (int u = 0; u < N; ++u)
-      cand |= ((valid >> u) & 1u) != 0u && chunk8_max(raw[u]) >= thr_f ? 1u << u : 0u;
+      cand |= ((valid >> u) & 1u) != 0u && chunk_max<DT>(raw[u]) >= thr_f ? 1u << u : 0u;
     while (__ballot(cand != 0u) != 0ull) {
       const bool act = cand != 0u;
       const int u = act ? __builtin_ctz(cand) : 0;
@@ -257,8 +304,9 @@ struct TopM {
         }
         ch[w] = x;
       }
-      const uint32_t pend = act ? chunk8_pend(ch, thr_f) : 0u;
-      offer(pend, [&](int e) { return chunk8_bits(ch, e); }, (c0 + (long long)u * stride) * 8);
+      const uint32_t pend = act ? chunk_pend<DT>(ch, thr_f) : 0u;
+      offer(pend, [&](int e) { return ChunkVals<DT>::bits(ch, e); },
+            (c0 + (long long)u * stride) * ChunkVals<DT>::N);
     }
   }
 };
@@ -268,6 +316,7 @@ struct TopM {
 // by key, and at rank r the token and
 //   (x_t(v)/T - LSE_S(x_t/T)) - (x_d(v)/T - LSE_S(x_d/T))
 // are written; slots mm..m-1 get -1 and NaN. One whole wavefront; mm <= 64.
+template <int DT>
 __device__ inline void support_residual(const uint64_t* keys, uint32_t mm, const void* drow,
                                         const void* trow, double invT, int m,
                                         int32_t* __restrict__ out_support,
@@ -281,8 +330,8 @@ __device__ inline void support_residual(const uint64_t* keys, uint32_t mm, const
     rank += (has && ko > key) ? 1 : 0;
   }
   const int v = has ? int(~uint32_t(key)) : -1;
-  const double ad = has ? double(load_logit<DT_BF16>(drow, v)) * invT : -__builtin_inf();
-  const double at = has ? double(load_logit<DT_BF16>(trow, v)) * invT : -__builtin_inf();
+  const double ad = has ? double(load_logit<DT>(drow, v)) * invT : -__builtin_inf();
+  const double at = has ? double(load_logit<DT>(trow, v)) * invT : -__builtin_inf();
   double mt = at, md = ad;
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) {

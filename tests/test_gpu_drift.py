@@ -105,8 +105,7 @@ def test_set_residual_arguments(sv):
     v32 = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32)
     buf = torch.zeros(cfg.B * cfg.K * 64, dtype=torch.int32, device=DEV)
     dbl = torch.zeros(cfg.B * cfg.K * 64, dtype=torch.float64, device=DEV)
-    assert v32.lib.spec_verify_set_residual(v32._h, 32, sv._ptr(buf), sv._ptr(dbl)) == \
-        sv.SV_EUNSUPPORTED
+    assert v32.lib.spec_verify_set_residual(v32._h, 32, sv._ptr(buf), sv._ptr(dbl)) == sv.SV_OK
     v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.bfloat16)
     for m in (0, 65, -1):
         assert v.lib.spec_verify_set_residual(v._h, m, sv._ptr(buf), sv._ptr(dbl)) == sv.SV_EINVAL
@@ -186,3 +185,59 @@ def test_residual_c3_sampled(sv):
         assert np.max(np.abs(r_np[b, i] - r)) <= TOL, (b, i)
     print(f"residual/c3: {cfg.B * cfg.K} positions against topk, {len(picks)} against the oracle",
           flush=True)
+
+
+@pytest.mark.parametrize("route", ["streaming", "streaming-3seg", "own-scalar", "own-one-kernel"])
+def test_residual_fp32_routes(sv, monkeypatch, route):
+    """fp32 logits (64-bit token keys) on every route: the streaming pass's
+    lists with one and three segments, the row-reading kernel on rows not in
+    16-byte chunks and after the one-kernel path; ties and -inf included."""
+    monkeypatch.setenv("SPEC_VERIFY_NSEG", "3" if route == "streaming-3seg" else "0")
+    monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "1" if route == "own-one-kernel" else "0")
+    V = {"own-scalar": 4001, "streaming-3seg": 20000}.get(route, 8000)   # 3 segments: V/4 >= 3072
+    cfg = CONFIGS["c1"].scaled(B=24, V=V)
+    x = make_inputs(cfg, 15, DEV)
+    x["draft"][1] = torch.round(x["draft"][1] * 2) / 2                  # ties
+    x["draft"][2, 0, ::3] = float("-inf")
+    x["draft"][3, 1, 7] = -0.0
+    x["draft"][3, 1, 9] = 0.0
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    sup, res = v.set_residual(24)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+    torch.cuda.synchronize()
+    _check(x, cfg, 24, sup.cpu().numpy(), res.cpu().numpy(), alen.cpu().numpy(),
+           label=f"residual/fp32 {route}")
+
+
+def test_residual_c5_sampled(sv):
+    """The full c5 batch (fp32, B = 1024, K = 4, its p = q and zero-mass
+    sequences) with m = 32: supports against torch's topk at every drafted
+    position of a valid sequence, sampled positions against the oracle."""
+    cfg = CONFIGS["c5"]
+    x = make_inputs(cfg, 16, DEV)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    sup, res = v.set_residual(32)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+    torch.cuda.synchronize()
+    valid = (alen >= 0).cpu().numpy()
+    top = torch.topk(x["draft"], 32, dim=-1).values
+    got = torch.gather(x["draft"], 2, sup.clamp(min=0).long())
+    same = (got == top).all(dim=-1).all(dim=-1).cpu().numpy()
+    assert np.all(same[valid])
+    assert np.all(sup.cpu().numpy()[~valid] == -1)
+    rng = np.random.default_rng(17)
+    T32 = float(np.float32(x["T"]))
+    s_np, r_np = sup.cpu().numpy(), res.cpu().numpy()
+    checked = 0
+    for p in rng.choice(cfg.B * cfg.K, 40, replace=False):
+        b, i = divmod(int(p), cfg.K)
+        if not valid[b]:
+            continue
+        S, r = O.drift_residual(to_host_f64(x["target"][b, i]), to_host_f64(x["draft"][b, i]),
+                                T32, 32)
+        assert np.array_equal(s_np[b, i], S), (b, i)
+        ok = np.isclose(r_np[b, i], r, rtol=0, atol=TOL) | (np.isinf(r) & (r_np[b, i] == r))
+        assert np.all(ok), (b, i)
+        checked += 1
+    print(f"residual/c5: {int(valid.sum()) * cfg.K} positions against topk, {checked} against "
+          f"the oracle", flush=True)
