@@ -30,7 +30,7 @@ namespace sv {
 constexpr int kDriftMaxM = 64;
 constexpr int kDriftBlock = 256;
 constexpr int kDriftWaves = kDriftBlock / kWave;
-constexpr int kDriftCap = 1024;      // keys per wavefront list (drift_residual)
+constexpr int kDriftCap = 448;       // keys per wavefront list (drift_residual)
 constexpr int kDriftUnroll = 4;      // chunks per thread per group (two groups in flight)
 constexpr int kTopmMaxSeg = 16;      // streaming-pass segments per row, at most
 constexpr int kTopmListSlots = kDriftMaxM;            // stored keys per wavefront list
@@ -55,6 +55,8 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   constexpr bool kVector = VEC > 1;         // 16-byte chunks (8 bf16 or 4 fp32)
   __shared__ uint64_t s_keys[kDriftWaves][kDriftCap];
   __shared__ uint32_t s_bins[kDriftWaves][256];
+  __shared__ u32x4 s_stage[kDriftWaves][kVector ? kTopmStage : 1];
+  __shared__ uint32_t s_stage_at[kDriftWaves][kVector ? kTopmStage : 1];
   __shared__ uint32_t s_count[kDriftWaves];
   __shared__ unsigned long long s_thr;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   if (tid == 0) s_thr = 0ull;
   __syncthreads();
   TopM<DT> tm;
-  tm.init(s_keys[wid], s_bins[wid], &s_thr, kDriftCap, mm);
+  tm.init(s_keys[wid], s_bins[wid], &s_thr, kDriftCap, mm, s_stage[wid], s_stage_at[wid]);
 
   // ---- one read of the draft row; one group's loads are in flight while
   // the other is filtered (indexes past the row are clamped to its last
@@ -86,11 +88,19 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   auto filter_group = [&](long long it, const raw_t (&raw)[kDriftUnroll]) {
     if constexpr (kVector) {
       const long long c0 = it * kDriftUnroll * kDriftBlock + tid;
-      uint32_t valid = 0;
+      float cm[kDriftUnroll];
+      uint32_t ok = 0;
 #pragma unroll
-      for (int u = 0; u < kDriftUnroll; ++u)
-        valid |= c0 + (long long)u * kDriftBlock < nchunks ? 1u << u : 0u;
-      tm.template offer_group<kDriftUnroll>(raw, c0, kDriftBlock, valid);
+      for (int u = 0; u < kDriftUnroll; ++u) {
+        cm[u] = chunk_max<DT>(raw[u]);
+        ok |= c0 + (long long)u * kDriftBlock < nchunks ? 1u << u : 0u;
+      }
+      if (it == 0) tm.template seed<kDriftUnroll>(cm, ok);   // start the threshold
+#pragma unroll
+      for (int u = 0; u < kDriftUnroll; ++u) {
+        const long long cu = c0 + (long long)u * kDriftBlock;
+        tm.stage_chunk(((ok >> u) & 1u) != 0u && cm[u] >= tm.thr_f, raw[u], uint32_t(cu));
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < kDriftUnroll; ++u) {
@@ -116,6 +126,7 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
       filter_group(it + 1, gb);
     }
   }
+  if constexpr (kVector) tm.flush();
   tm.compact();                                 // at most mm keys per wavefront
   if (lane == 0) s_count[wid] = tm.fill;
   __syncthreads();

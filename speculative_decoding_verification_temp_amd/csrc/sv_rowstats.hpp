@@ -77,14 +77,17 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
   [[maybe_unused]] TopM<DT> tm;
   [[maybe_unused]] const bool topm_row = TOPM && r > K;   // uniform
   [[maybe_unused]] long long topm_next = c0 + tid;        // first chunk not yet fed
+  [[maybe_unused]] bool topm_seeded = false;              // uniform
   if constexpr (TOPM) {
     __shared__ uint64_t s_tk[kWavesPerBlock][kTopmCapFused];
     __shared__ uint32_t s_tb[kWavesPerBlock][256];
+    __shared__ u32x4 s_ts[kWavesPerBlock][kTopmStage];
+    __shared__ uint32_t s_ta[kWavesPerBlock][kTopmStage];
     __shared__ unsigned long long s_tt;
     if (tid == 0) s_tt = 0ull;
     __syncthreads();
     tm.init(s_tk[tid / kWave], s_tb[tid / kWave], &s_tt, kTopmCapFused,
-            uint32_t(min(topm_m, V)));
+            uint32_t(min(topm_m, V)), s_ts[tid / kWave], s_ta[tid / kWave]);
   }
 
   float R = kRefInit;
@@ -99,10 +102,21 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
 #pragma unroll
     for (int u = 0; u < U; ++u) C::unpack(raw[u], x[u]);
     float gm = x[0][0];
+    [[maybe_unused]] float cm[U];
+    if constexpr (TOPM) {   // chunk maxima first (the same maximum)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        cm[u] = x[u][0];
 #pragma unroll
-      for (int k = 0; k < C::N; ++k) gm = fmaxf(gm, x[u][k]);
+        for (int k = 1; k < C::N; ++k) cm[u] = fmaxf(cm[u], x[u][k]);
+        gm = fmaxf(gm, cm[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < C::N; ++k) gm = fmaxf(gm, x[u][k]);
+    }
     const float Rn = fmaxf(R, ceilf(gm * c));
     S = rescale(S, R, Rn);
     R = Rn;
@@ -118,7 +132,15 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
     S += (double)t[0];
     if constexpr (TOPM) {
       if (topm_row && __builtin_amdgcn_read_exec() == ~0ull) {   // all 64 lanes here
-        if (__ballot(gm >= tm.thr_f) != 0ull) tm.template offer_group<U>(raw, ci, kBlock, (1u << U) - 1u);
+        if (!topm_seeded) {   // the first group's chunk maxima start the threshold
+          tm.template seed<U>(cm, (1u << U) - 1u);
+          topm_seeded = true;
+        }
+        if (__ballot(gm >= tm.thr_f) != 0ull) {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            tm.stage_chunk(cm[u] >= tm.thr_f, raw[u], uint32_t(ci + (long long)u * kBlock));
+        }
         topm_next = ci + (long long)U * kBlock;
       }
     }
@@ -147,14 +169,17 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
   if constexpr (TOPM) {
     if (topm_row) {   // the lanes are together again: feed the chunks read apart
       typename C::raw_t raw[2 * U - 1];
-      uint32_t valid = 0;
 #pragma unroll
       for (int j = 0; j < 2 * U - 1; ++j) {
         const long long cc = topm_next + (long long)j * kBlock;
         raw[j] = C::load(row, cc < c1 ? cc : c0);
-        valid |= cc < c1 ? 1u << j : 0u;
       }
-      tm.template offer_group<2 * U - 1>(raw, topm_next, kBlock, valid);
+#pragma unroll
+      for (int j = 0; j < 2 * U - 1; ++j) {
+        const long long cc = topm_next + (long long)j * kBlock;
+        tm.stage_chunk(cc < c1 && chunk_max<DT>(raw[j]) >= tm.thr_f, raw[j], uint32_t(cc));
+      }
+      tm.flush();
       tm.compact();
       const int lane = tid & (kWave - 1);
       uint64_t* out = topm_lists +

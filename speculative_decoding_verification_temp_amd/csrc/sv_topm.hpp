@@ -203,9 +203,14 @@ __device__ inline float chunk_max(const u32x4& r) {
   return mx;
 }
 
+constexpr int kTopmStage = 128;   // staged chunks per wavefront
+
 // The candidate list of one wavefront over logits of type DT. Every member
-// function is called by all 64 lanes of the wavefront together; fill, thr
-// and thr_f are the same in every lane.
+// function is called by all 64 lanes of the wavefront together; fill, thr,
+// thr_f and nstage are the same in every lane. Chunks whose largest value
+// reaches the threshold are first staged in LDS (kTopmStage per wavefront)
+// and filtered 64 at a time, one per lane, so that the insert rounds run
+// with every lane busy whichever lanes found the candidates.
 template <int DT>
 struct TopM {
   uint64_t* keys;              // cap entries of LDS
@@ -215,8 +220,12 @@ struct TopM {
   uint32_t fill;
   uint64_t thr;                // keys below it cannot be among the m largest
   float thr_f;                 // order_floor of thr's logit key
+  u32x4* stage;                // kTopmStage staged chunks (LDS)
+  uint32_t* stage_at;          // their chunk indexes in the row
+  uint32_t nstage;
 
-  __device__ void init(uint64_t* k, uint32_t* b, unsigned long long* s, uint32_t c, uint32_t w) {
+  __device__ void init(uint64_t* k, uint32_t* b, unsigned long long* s, uint32_t c, uint32_t w,
+                       u32x4* st = nullptr, uint32_t* st_at = nullptr) {
     keys = k;
     bins = b;
     shared = s;
@@ -225,6 +234,9 @@ struct TopM {
     fill = 0;
     thr = 0;
     thr_f = -__builtin_inff();
+    stage = st;
+    stage_at = st_at;
+    nstage = 0;
   }
 
   // keep the keys at or above max(the want-th largest key, the shared threshold)
@@ -272,42 +284,70 @@ struct TopM {
     }
   }
 
-  // Offer a lane's N 16-byte chunks: chunk u holds the values of indexes
-  // E c_u .. E c_u + E - 1 (E values per chunk) with c_u = c0 + u * stride,
-  // and is skipped unless bit
-  // u of `valid` is set. Each round takes one chunk per lane among those
-  // whose largest value reaches the threshold, so a lane with one candidate
-  // chunk costs one round.
+  // Start the threshold from values already at hand: the want-th largest of
+  // v[q] over the lanes (slots q with bit q of `ok` set), each taken with the
+  // lowest key its value can have, is at most the row's want-th largest
+  // token key. Needs an empty list; chunk maxima are the usual v.
   template <int N>
-  __device__ void offer_group(const u32x4 (&raw)[N], long long c0, long long stride,
-                              uint32_t valid) {
-    uint32_t cand = 0;
+  __device__ void seed(const float (&v)[N], uint32_t ok) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t n = 0;
 #pragma unroll
-    for (int u = 0; u < N; ++u)
-      cand |= ((valid >> u) & 1u) != 0u && chunk_max<DT>(raw[u]) >= thr_f ? 1u << u : 0u;
-    while (__ballot(cand != 0u) != 0ull) {
-      const bool act = cand != 0u;
-      const int u = act ? __builtin_ctz(cand) : 0;
-      cand &= cand - 1u;
-      // the chunk of this lane's round, by selects on register copies (the
-      // empty asm keeps the compiler from indexing the array in memory)
-      u32x4 ch;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t x = raw[0][w];
-        asm volatile("" : "+v"(x));
-#pragma unroll
-        for (int j = 1; j < N; ++j) {
-          uint32_t y = raw[j][w];
-          asm volatile("" : "+v"(y));
-          x = u == j ? y : x;
-        }
-        ch[w] = x;
-      }
-      const uint32_t pend = act ? chunk_pend<DT>(ch, thr_f) : 0u;
-      offer(pend, [&](int e) { return ChunkVals<DT>::bits(ch, e); },
-            (c0 + (long long)u * stride) * ChunkVals<DT>::N);
+    for (int q = 0; q < N; ++q) {
+      const bool put = ((ok >> q) & 1u) != 0u && v[q] == v[q];
+      const uint32_t bits =
+          DT == DT_BF16 ? __float_as_uint(v[q]) >> 16 : __float_as_uint(v[q]);
+      const uint64_t mask = __ballot(put);
+      if (put) keys[n + lanes_below(mask)] = uint64_t(order_key<DT>(bits)) << 32;
+      n += uint32_t(__popcll(mask));
     }
+    wave_sync();
+    if (n >= want) {
+      const uint64_t t = wave_kth_largest(keys, int(n), want, bins, key_top_shift<DT>());
+      if (t > thr) {
+        thr = t;
+        thr_f = order_floor<DT>(uint32_t(t >> 32));
+        if (lane == 0) atomicMax(shared, (unsigned long long)t);
+      }
+    }
+    wave_sync();
+  }
+
+  // Stage this lane's 16-byte chunk number `at` of the row (values of
+  // indexes E at .. E at + E - 1) when `cand`; filter the staged chunks once
+  // fewer than 64 slots are free.
+  __device__ void stage_chunk(bool cand, const u32x4& ch, uint32_t at) {
+    const uint64_t mask = __ballot(cand);
+    if (mask == 0ull) return;
+    if (cand) {
+      const uint32_t slot = nstage + lanes_below(mask);
+      stage[slot] = ch;
+      stage_at[slot] = at;
+    }
+    nstage += uint32_t(__popcll(mask));
+    if (nstage > uint32_t(kTopmStage - kWave)) flush();
+  }
+
+  // Filter every staged chunk against the current threshold, one per lane.
+  __device__ void flush() {
+    const int lane = threadIdx.x & (kWave - 1);
+    wave_sync();
+    for (uint32_t base = 0; base < nstage; base += kWave) {
+      const uint32_t e = base + uint32_t(lane);
+      const bool has = e < nstage;
+      u32x4 ch = {0u, 0u, 0u, 0u};
+      uint32_t at = 0;
+      if (has) {
+        ch = stage[e];
+        at = stage_at[e];
+      }
+      const uint32_t pend = has ? chunk_pend<DT>(ch, thr_f) : 0u;
+      offer(pend, [&](int q) { return ChunkVals<DT>::bits(ch, q); },
+            (long long)at * ChunkVals<DT>::N);
+    }
+    nstage = 0;
+    wave_sync();
+    if (fill > 2 * want) compact();   // a tighter threshold early stages fewer chunks
   }
 };
 
