@@ -140,6 +140,9 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
 #pragma unroll
           for (int u = 0; u < U; ++u)
             tm.stage_chunk(cm[u] >= tm.thr_f, raw[u], uint32_t(ci + (long long)u * kBlock));
+          // a tighter threshold early stages fewer chunks (measured a small
+          // gain here; the row-reading kernel is faster without it)
+          if (tm.fill > 2 * tm.want) tm.compact();
         }
         topm_next = ci + (long long)U * kBlock;
       }

@@ -347,7 +347,6 @@ struct TopM {
     }
     nstage = 0;
     wave_sync();
-    if (fill > 2 * want) compact();   // a tighter threshold early stages fewer chunks
   }
 };
 
