@@ -216,7 +216,7 @@ struct TopM {
   uint64_t* keys;              // cap entries of LDS
   uint32_t* bins;              // 256 words of LDS
   unsigned long long* shared;  // the workgroup's threshold (LDS)
-  uint32_t cap, want;          // list size (>= want + 64); m
+  uint32_t cap, want;          // list size (>= want + 64, and >= 64 N for seed<N>); m
   uint32_t fill;
   uint64_t thr;                // keys below it cannot be among the m largest
   float thr_f;                 // order_floor of thr's logit key
