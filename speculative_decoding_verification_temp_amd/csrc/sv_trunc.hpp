@@ -419,6 +419,8 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
 // ---------------------------------------------------------------------------
 constexpr int kTwBlock = 512;
 constexpr int kTwWaves = kTwBlock / kWave;
+using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+
 constexpr int kWinBins = 8192;
 constexpr int kBinsPerThread = kWinBins / kTwBlock;      // 16
 constexpr int kWinELo = 127 - 24;                        // smallest window exponent field
@@ -493,18 +495,27 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
     // formula; any other chunk classifies each value
     auto count_chunk = [&](const raw_t& raw) {
       if constexpr (VEC == 8) {
-        uint32_t o2[8], worst = 0;
+        // both values of a word at once in packed 16-bit lanes (low half
+        // first): o = |x| pattern - (window base - 2), which wraps far above
+        // the window for values below it
+        u16x2 o[4], worst2 = {0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (e & 1) ? raw[e >> 1] >> 16 : raw[e >> 1] & 0xffffu;
-          o2[e] = (bits & 0x7fffu) - uint32_t((kWinELo << 7) - 2);
-          worst = max(worst, o2[e] - 2u);
+        for (int q = 0; q < 4; ++q) {
+          // bit-cast a scalar copy: the cast of a vector element reads element 0
+          const uint32_t w = raw[q];
+          const u16x2 v = __builtin_bit_cast(u16x2, w);
+          o[q] = (v & (u16x2)(0x7fff)) - (u16x2)(uint16_t((kWinELo << 7) - 2));
+          worst2 = __builtin_elementwise_max(worst2, o[q] - (u16x2)(2));
         }
-        if (worst < uint32_t(kWinHalf)) {
+        if (max(uint32_t(worst2.x), uint32_t(worst2.y)) < uint32_t(kWinHalf)) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t neg = uint32_t(int(raw[e >> 1] << ((e & 1) ? 0 : 16)) >> 31);
-            atomicAdd(&H[uint32_t(kWinZero) + ((o2[e] ^ neg) - neg)], 1u);
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = raw[q];
+            const u16x2 v = __builtin_bit_cast(u16x2, w);
+            const u16x2 neg = (u16x2)(0) - (v >> (u16x2)(15));   // 0xffff where negative
+            const u16x2 bin = (u16x2)(uint16_t(kWinZero)) + ((o[q] ^ neg) - neg);
+            atomicAdd(&H[bin.x], 1u);
+            atomicAdd(&H[bin.y], 1u);
           }
         } else {
 #pragma unroll
