@@ -201,9 +201,14 @@ int spec_verify_set_stops(spec_verify_handle *h, int eos_token, const int32_t *d
  *          > 0 (or NaN): the sequence is invalid; NULL: off
  *
  * Kept tokens are renormalised, dropped ones have probability exactly 0.
- * Greedy and margin calls ignore the settings. Only bf16 logits are
- * supported (SV_EUNSUPPORTED for a float32 handle) with V up to 524288
- * (larger V: spec_verify returns SV_EUNSUPPORTED). The arrays are read by
+ * Greedy and margin calls ignore the settings. bf16 and float32 logits are
+ * supported, with V up to 524288 (bf16) or 262144 (float32) when V is a
+ * multiple of 8 (bf16) or 4 (float32) and the logit tensors are 16-byte
+ * aligned, else 65536 (larger V: spec_verify returns SV_EUNSUPPORTED). A
+ * float32 call reads each needed row two to six times (the k-th largest
+ * value and the top-p level are narrowed 12, 10 and 10 bits of the value's
+ * order key at a time); its normalisers carry a relative error below 1e-8
+ * beyond the terms' own. The arrays are read by
  * the device during later calls and stay owned by the caller; they must
  * outlive those calls. spec_verify_set_truncation(h, NULL, NULL) turns
  * truncation off. Returns SV_EINVAL for a NULL handle or a misaligned array.

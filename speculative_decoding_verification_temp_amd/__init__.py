@@ -188,7 +188,8 @@ class SpecVerifier:
     def set_truncation(self, top_k=None, top_p=None):
         """Per-sequence top-k [max_batch] (int32) and top-p [max_batch]
         (float32) device tensors, or None, for later stochastic calls (bf16
-        logits). The tensors are kept referenced here while they are in use."""
+        or float32 logits). The tensors are kept referenced here while they
+        are in use."""
         for t, dt, name in ((top_k, torch.int32, "top_k"), (top_p, torch.float32, "top_p")):
             if t is not None and (t.dtype != dt or t.device != self.device or not t.is_contiguous()
                                   or t.numel() < self.max_batch):

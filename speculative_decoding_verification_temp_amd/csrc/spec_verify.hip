@@ -13,6 +13,7 @@
 
 #include "sv_drift.hpp"
 #include "sv_trunc.hpp"
+#include "sv_trunc32.hpp"
 
 #ifndef SV_U_BF16
 #define SV_U_BF16 4
@@ -226,6 +227,35 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
   return check_launch(h, "finish_seq (truncated)");
 }
 
+// Stochastic mode with top-k / top-p truncation (fp32 rows): the digit-wise
+// truncation pass over every needed row, then the per-sequence finish, whose
+// draw compares each value's order key with its row's threshold.
+template <int VEC>
+int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* draft,
+                const int32_t* tokens, const float* uniforms, float c, double c64,
+                int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
+  const int K = h->K, V = h->V;
+  const int rows = 2 * K + 1;
+  const int ntiles = div_up(V / VEC, sv::kTileChunks);
+  if (ntiles > sv::kFMaxTiles || rows > sv::kFMaxRows)
+    return fail(h, SV_EUNSUPPORTED, "truncation needs V <= %d (fp32)",
+                sv::kFMaxTiles * sv::kTileChunks * VEC);
+  int lg = 0;                        // ceil(log2 V): fixed-point masses keep 61 - lg bits
+  while ((1ll << lg) < (long long)V) ++lg;
+  prof_mark(h, 0, s);
+  hipLaunchKernelGGL((sv::rowstats_trunc32<VEC>), dim3(unsigned(B * rows)), dim3(sv::kT32Block),
+                     0, s, target, draft, K, V, c, c64, 61 - lg, h->trunc, h->rules.k, h->parts,
+                     hist);
+  int rc = check_launch(h, "rowstats_trunc32");
+  prof_mark(h, 1, s);
+  if (rc) return rc;
+  hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
+                     dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
+                     uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
+                     h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z);
+  return check_launch(h, "finish_seq (truncated)");
+}
+
 // Stochastic mode, one workgroup per sequence (large batches).
 template <int DT, int VEC, int U>
 int run_fused(spec_verify_handle* h, int B, const void* target, const void* draft,
@@ -418,8 +448,6 @@ int spec_verify_set_stops(spec_verify_handle* h, int eos_token, const int32_t* d
 
 int spec_verify_set_truncation(spec_verify_handle* h, const int32_t* top_k, const float* top_p) {
   if (h == nullptr) return SV_EINVAL;
-  if ((top_k != nullptr || top_p != nullptr) && h->dtype != SV_DTYPE_BF16)
-    return fail(h, SV_EUNSUPPORTED, "truncation is implemented for bf16 logits");
   if (top_k != nullptr && !aligned(top_k, 4)) return fail(h, SV_EINVAL, "misaligned top_k");
   if (top_p != nullptr && !aligned(top_p, 4)) return fail(h, SV_EINVAL, "misaligned top_p");
   h->trunc.k = top_k;
@@ -500,7 +528,14 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   const double c64 = kLog2e / double(temperature);
   const float c = float(c64);
   const bool trunc = h->trunc.k != nullptr || h->trunc.p != nullptr;
-  if (mode == SV_MODE_STOCHASTIC && trunc) {
+  if (mode == SV_MODE_STOCHASTIC && trunc && h->dtype == SV_DTYPE_F32) {
+    if (vec)
+      rc = run_trunc32<4>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens, out_len,
+                          out_hist, stream);
+    else
+      rc = run_trunc32<1>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens, out_len,
+                          out_hist, stream);
+  } else if (mode == SV_MODE_STOCHASTIC && trunc) {
     if (vec)
       rc = run_trunc<8>(h, B, target, draft, tokens, uniforms, c, c64, out_tokens, out_len,
                         out_hist, stream);

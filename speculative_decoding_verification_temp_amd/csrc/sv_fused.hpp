@@ -253,7 +253,9 @@ __device__ __forceinline__ uint32_t word_at(const u32x4 (&a)[kUnitChunks], int k
 // one lane's sums over one unit (chunks c0 + k * kWave; RAGGED: chunks at or
 // past nchunks are skipped). Tt, Td: the target and draft rows' tables (one
 // table unless the rows are truncated), thr_t, thr_d their threshold keys.
-template <int DT, bool RESID, bool RAGGED>
+// MASK (truncated fp32 rows): a value whose order key is below its row's
+// threshold contributes 0.
+template <int DT, bool RESID, bool RAGGED, bool MASK = false>
 __device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, uint32_t thr_t,
                                           uint32_t thr_d, const UnitBuf& u, long long c0,
                                           long long nchunks, double rho2, double c, double& E,
@@ -265,9 +267,11 @@ __device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, ui
       if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const double et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, Tt);
+        double et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, Tt);
+        if (MASK && order_key<DT_F32>(u.a[k][q]) < thr_t) et = 0.0;
         if constexpr (RESID) {
-          const double ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, Tt);
+          double ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, Tt);
+          if (MASK && order_key<DT_F32>(u.d[k][q]) < thr_d) ed = 0.0;
           accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
         } else {
           E += et;
@@ -321,7 +325,7 @@ __device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, ui
 // keeps kUnits - 1 units of loads outstanding while it computes. Chunks past
 // the row end are clamped to the last chunk for loading and skipped in the
 // sums.
-template <int DT, int VEC, bool RESID, int NW>
+template <int DT, int VEC, bool RESID, int NW, bool MASK = false>
 __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* Td,
                                                const void* trow, const void* drow,
                                                const DrawRow& dr, double c, int ntiles,
@@ -371,8 +375,8 @@ __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* T
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       double e, ed, a, bd;
-      unit_sums<DT, RESID, false>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u), nchunks,
-                                  rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, false, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u),
+                                        nchunks, rho2, c, e, ed, a, bd);
       load_unit(ti + 1, u, b[u]);
       E += e;
       Ed += ed;
@@ -387,11 +391,11 @@ __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* T
   for (int u = 0; u < kUnits; ++u) {
     double e, ed, a, bd;
     if (whole)
-      unit_sums<DT, RESID, false>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u), nchunks,
-                                  rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, false, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u),
+                                        nchunks, rho2, c, e, ed, a, bd);
     else
-      unit_sums<DT, RESID, true>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u), nchunks,
-                                 rho2, c, e, ed, a, bd);
+      unit_sums<DT, RESID, true, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u),
+                                       nchunks, rho2, c, e, ed, a, bd);
     E += e;
     Ed += ed;
     A += a;
@@ -480,9 +484,13 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
         et = term_unscaled(Tt, (e & 1) ? wt[e >> 1] >> 16 : wt[e >> 1] & 0xffffu, c, dr.thr_t);
         if (which)
           ed = term_unscaled(Td, (e & 1) ? wd[e >> 1] >> 16 : wd[e >> 1] & 0xffffu, c, dr.thr_d);
-      } else {
-        et = exp2_tab(double(__uint_as_float(wt[e])) * c, Tt);
-        if (which) ed = exp2_tab(double(__uint_as_float(wd[e])) * c, Tt);
+      } else {        // fp32: threshold 0 (untruncated rows) keeps every value
+        et = order_key<DT_F32>(wt[e]) >= dr.thr_t ? exp2_tab(double(__uint_as_float(wt[e])) * c, Tt)
+                                                  : 0.0;
+        if (which)
+          ed = order_key<DT_F32>(wd[e]) >= dr.thr_d
+                   ? exp2_tab(double(__uint_as_float(wd[e])) * c, Tt)
+                   : 0.0;
       }
       wv[e] = which ? fmax(__builtin_fma(-rho2, ed, et), 0.0) : et;
       if (!valid) wv[e] = 0.0;
@@ -537,13 +545,14 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
 // Phases 2-4 for one sequence, given its row statistics in LDS (fR, fS):
 // the acceptance scan on wavefront 0, the draw's float64 tile sums of row
 // pair j over all wavefronts of the workgroup, then the pick.
-// TRUNC (bf16 rows): fK holds each row's truncation threshold key and fS its
-// truncated normaliser, a sum of level_term values; p(d) and q(d) are formed
-// with level_term too and are 0 for dropped values, and once j is
-// known T is filled with two tables, the target row's and the draft row's,
-// each 0 at the values its row drops (without TRUNC, T is one table built by
-// the caller, or, with TABLE_IN_SCAN, by wavefronts 1.. while wavefront 0
-// runs the scan).
+// TRUNC: fK holds each row's truncation threshold key and fS its truncated
+// normaliser, a sum of level_term (bf16) or value_term (fp32) values; p(d)
+// and q(d) are formed with the same terms and are 0 for dropped values. For
+// bf16 rows, once j is known T is filled with two tables, the target row's
+// and the draft row's, each 0 at the values its row drops; fp32 rows keep the
+// one table and the draw compares each value's order key with its row's
+// threshold (without TRUNC, T is one table built by the caller, or, with
+// TABLE_IN_SCAN, by wavefronts 1.. while wavefront 0 runs the scan).
 template <int DT, int VEC, int NT, bool TRUNC, bool TABLE_IN_SCAN>
 __device__ __forceinline__ void finish_sequence(
     int b, int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
@@ -586,12 +595,16 @@ __device__ __forceinline__ void finish_sequence(
       if (!lane_bad) {
         const float xt = load_logit<DT>(row_base(lane), d);
         const float xd = load_logit<DT>(row_base(K + 1 + lane), d);
-        if constexpr (TRUNC) {
+        if constexpr (TRUNC && DT == DT_BF16) {
           // the same level terms as the truncated normalisers; 0 when dropped
           const uint32_t at = bf16_key(__float_as_uint(xt) >> 16);
           const uint32_t ad = bf16_key(__float_as_uint(xd) >> 16);
           P = (at >= kt && key_finite(at)) ? level_term(at, c64, Rt) / St : 0.0;
           Q = (ad >= kd && key_finite(ad)) ? level_term(ad, c64, Rd) / Sd : 0.0;
+        } else if constexpr (TRUNC) {
+          // fp32: the terms the truncation pass summed (0 for -inf); 0 when dropped
+          P = order_key<DT_F32>(__float_as_uint(xt)) >= kt ? value_term(xt, c64, Rt) / St : 0.0;
+          Q = order_key<DT_F32>(__float_as_uint(xd)) >= kd ? value_term(xd, c64, Rd) / Sd : 0.0;
         } else {
           P = double(term(xt, c, Rt)) / St;
           Q = double(term(xd, c, Rd)) / Sd;
@@ -665,12 +678,13 @@ __device__ __forceinline__ void finish_sequence(
     unscaled = fabsf(dr.R_t) <= kUnscaledMaxR && (!W.residual || fabsf(dr.R_d) <= kUnscaledMaxR);
   if (unscaled) {
     if constexpr (kFast) {
+      constexpr bool kMask = TRUNC && DT == DT_F32;
       if (W.residual)
-        tiles_unscaled<DT, VEC, true, kW>(Tt, Td, W.trow, W.drow, dr, c64, ntiles, nchunks,
-                                          tiles, wid, lane);
+        tiles_unscaled<DT, VEC, true, kW, kMask>(Tt, Td, W.trow, W.drow, dr, c64, ntiles,
+                                                 nchunks, tiles, wid, lane);
       else
-        tiles_unscaled<DT, VEC, false, kW>(Tt, Td, W.trow, W.drow, dr, c64, ntiles, nchunks,
-                                           tiles, wid, lane);
+        tiles_unscaled<DT, VEC, false, kW, kMask>(Tt, Td, W.trow, W.drow, dr, c64, ntiles,
+                                                  nchunks, tiles, wid, lane);
     }
   } else {
     for (int t = wid; t < ntiles; t += kW) {
@@ -870,8 +884,8 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
 
 // After the multi-workgroup streaming pass: one workgroup per sequence
 // combines the row partials (fixed order) and runs phases 2-4. TRUNC: after
-// the truncation pass instead, with one partial per row whose idx holds the
-// row's threshold key.
+// a truncation pass instead (sv_trunc.hpp for bf16 rows, sv_trunc32.hpp for
+// fp32), with one partial per row whose idx holds the row's threshold key.
 template <int DT, int VEC, int NT, bool TRUNC>
 __global__ __launch_bounds__(NT) void finish_seq(
     int K, int V, int nseg, const RowPart* __restrict__ parts, const void* __restrict__ target,
@@ -882,7 +896,6 @@ __global__ __launch_bounds__(NT) void finish_seq(
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
   constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
-  static_assert(!TRUNC || DT == DT_BF16, "truncation is implemented for bf16 rows");
   __shared__ double T[kTab ? (TRUNC ? 2 * kTabMax : kTabMax) : kTab2F ? kTab2 : 1];
   __shared__ float fR[kFMaxRows];
   __shared__ double fS[kFMaxRows];
@@ -902,7 +915,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
     if constexpr (TRUNC) fK[r] = uint32_t(pr->idx);
   }
   __syncthreads();
-  finish_sequence<DT, VEC, NT, TRUNC, !TRUNC>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
+  // the fp32 table does not depend on the truncation: built during the scan
+  finish_sequence<DT, VEC, NT, TRUNC, !TRUNC || DT == DT_F32>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
                                       n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
                                       out_len, hist, ema,
                                     steps,

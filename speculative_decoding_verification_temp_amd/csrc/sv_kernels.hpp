@@ -223,6 +223,13 @@ __device__ inline double level_term(uint32_t key, double c64, float R) {
   return __builtin_ldexp(double(__builtin_amdgcn_exp2f(float(a - n))), int(n));
 }
 
+// The same term of an fp32 logit (the truncated fp32 path); -inf gives 0.
+__device__ inline double value_term(float x, double c64, float R) {
+  const double a = fmax(__builtin_fma(double(x), c64, -double(R)), -2000.0);
+  const double n = __builtin_rint(a);
+  return __builtin_ldexp(double(__builtin_amdgcn_exp2f(float(a - n))), int(n));
+}
+
 // --------------------------------------------------------------------------
 // Stochastic scan: lane i tests position i.
 // --------------------------------------------------------------------------
@@ -391,10 +398,10 @@ template <int DT, int VEC> struct DrawRows {
     thr_t = dr.thr_t;
     thr_d = dr.thr_d;
   }
-  // whether a value survives its row's truncation (bf16 rows only)
+  // whether a value survives its row's truncation (threshold 0 keeps all)
   __device__ static inline bool kept(float x, uint32_t thr) {
     if constexpr (DT == DT_BF16) return bf16_key(__float_as_uint(x) >> 16) >= thr;
-    return true;
+    return order_key<DT_F32>(__float_as_uint(x)) >= thr;
   }
   __device__ inline void load(long long ci, typename C::raw_t& rt, typename C::raw_t& rd) const {
     rt = C::load(trow, ci);

@@ -1,0 +1,361 @@
+// Top-k / top-p truncation pass over fp32 logit rows (gfx950).
+//
+// The rules are those of the bf16 passes in sv_trunc.hpp ([RNR] s.1 and s.2):
+// top-k keeps the values at or above the k-th largest, counted with
+// multiplicity; top-p then keeps, from the top, whole value levels up to and
+// including the first level at which the kept mass reaches top_p of the
+// top-k mass. A bf16 row has at most 65536 distinct values, so one bin per
+// value is possible there; an fp32 row may hold V distinct values. This pass
+// narrows the 32-bit order key of sv_topm.hpp instead, one digit at a time
+// (bits 31..20, then 19..10, then 9..0), with one read of the row per digit:
+//   read A    the row maximum (and so R = ceil(max * c)), non-finite values,
+//             and (top-k) counts by the first digit;
+//   reads B-C (top-k) counts by the second digit inside the first digit's
+//             cut bin, then by the third inside the second's, which gives the
+//             k-th largest key exactly; the same reads sum the masses of the
+//             values above the cut bins and inside them;
+//   read D    (no top-k) masses by the first digit;
+//   reads E-F (top-p) masses by the second and third digit inside the bins
+//             where the mass from the top crosses top_p of the top-k mass,
+//             skipped when the top-k reads already hold them.
+// A bin of the third digit is one value level, so the last walk gives the
+// exact threshold key. All reads use cached loads: a row read again is
+// usually still in the last-level cache.
+//
+// Masses are softmax terms 2^(x c - R), each rounded once to unsigned 64-bit
+// fixed point with FX = 61 - ceil(log2 V) fraction bits (a term is at most
+// about 1, so no sum reaches 2^62), and summed with integer LDS atomics. The
+// sums are exact: they do not depend on the order in which lanes add, a
+// digit's bin sums add up to the coarser digit's bin, and so a finer walk
+// always finds the cut the coarser walk located. The rounding costs at most
+// V 2^-(FX+1) against a normaliser of at least 1/2, below 1e-8 relative.
+//
+// Output: one RowPart per needed row, as the bf16 passes write it: S = the
+// truncated normaliser relative to 2^R, R, idx = the threshold key (0 keeps
+// every value). A row holding NaN or +inf or no finite value, or a sequence
+// whose top_p is not > 0, gets S = NaN (the scan then marks the sequence
+// invalid). So does a row whose reads disagree (a walk that finds no cut,
+// which only a row changed during the call can cause): no bin index is ever
+// used unchecked. Rows past a sequence's draft count are not read.
+#pragma once
+
+#include "sv_trunc.hpp"
+
+namespace sv {
+
+constexpr int kT32Block = 512;
+constexpr int kT32Waves = kT32Block / kWave;
+constexpr int kT32Bins1 = 4096;     // first digit: key bits 31..20
+constexpr int kT32Bins = 1024;      // second and third digits: bits 19..10 and 9..0
+constexpr uint32_t kKey32NegInf = 0x80000000u - 0x7f800000u;
+constexpr uint32_t kKey32PosInf = 0x80000000u + 0x7f800000u;
+
+typedef unsigned long long u64;
+
+// A term 2^(x c - R) in fixed point with `scale` = 2^FX.
+__device__ inline u64 fixed_term(float x, double c64, float R, double scale) {
+  return u64(__builtin_rint(value_term(x, c64, R) * scale));
+}
+
+// What one read of the row gathers; every field is uniform over the workgroup.
+struct T32Sel {
+  bool count;                  // counts of the keys with (key & cmask) == cval,
+  uint32_t cmask, cval;        //   by bin (key >> cshift) & (kT32Bins - 1)
+  int cshift;
+  bool m1;                     // first-digit masses of the keys >= m1_floor
+  uint32_t m1_floor;
+  bool m2;                     // second-digit masses of the keys in first-digit
+  uint32_t m2_bin, m2_floor;   //   bin m2_bin that are >= m2_floor
+  bool m3;                     // third-digit masses of the keys with key >> 10
+  uint32_t m3_sel, m3_floor;   //   == m3_sel that are >= m3_floor
+};
+
+__device__ inline T32Sel t32_none() {
+  T32Sel s;
+  s.count = s.m1 = s.m2 = s.m3 = false;
+  s.cmask = s.cval = 0u;
+  s.cshift = 0;
+  s.m1_floor = s.m2_bin = s.m2_floor = s.m3_sel = s.m3_floor = 0u;
+  return s;
+}
+
+// the VEC-value chunk ci of an fp32 row with a cached load
+template <int VEC>
+__device__ inline void t32_load(const void* row, long long ci, uint32_t (&v)[VEC]) {
+  if constexpr (VEC == 4) {
+    const u32x4 r = reinterpret_cast<const u32x4*>(row)[ci];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = r[q];
+  } else {
+    v[0] = reinterpret_cast<const uint32_t*>(row)[ci];
+  }
+}
+
+// One read of the row, f(bits) per value. Four chunks per thread are in
+// flight (indexes past the row are clamped for the load and skipped).
+template <int VEC, typename F>
+__device__ inline void t32_stream(const void* row, long long nchunks, F&& f) {
+  constexpr int U = 4;
+  for (long long c0 = threadIdx.x; c0 < nchunks; c0 += (long long)U * kT32Block) {
+    uint32_t v[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      t32_load<VEC>(row, min(c0 + (long long)u * kT32Block, nchunks - 1), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + (long long)u * kT32Block >= nchunks) break;
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) f(v[u][q]);
+    }
+  }
+  __syncthreads();
+}
+
+template <int VEC>
+__device__ inline void t32_read(const void* row, long long nchunks, const T32Sel& s, double c64,
+                                float R, double scale, uint32_t* cnt, u64* m1, u64* m2, u64* m3) {
+  t32_stream<VEC>(row, nchunks, [&](uint32_t bits) {
+    const uint32_t key = order_key<DT_F32>(bits);
+    if (s.count && (key & s.cmask) == s.cval)
+      atomicAdd(&cnt[(key >> s.cshift) & uint32_t(kT32Bins - 1)], 1u);
+    const bool in1 = s.m1 && key >= s.m1_floor;
+    const bool in2 = s.m2 && (key >> 20) == s.m2_bin && key >= s.m2_floor;
+    const bool in3 = s.m3 && (key >> 10) == s.m3_sel && key >= s.m3_floor;
+    if (in1 || in2 || in3) {
+      const u64 t = fixed_term(__uint_as_float(bits), c64, R, scale);
+      if (in1) atomicAdd(&m1[key >> 20], t);
+      if (in2) atomicAdd(&m2[(key >> 10) & uint32_t(kT32Bins - 1)], t);
+      if (in3) atomicAdd(&m3[key & uint32_t(kT32Bins - 1)], t);
+    }
+  });
+}
+
+__device__ inline uint32_t t32_max(uint32_t v, uint32_t* s) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), o, kWave)));
+  if (lane == 0) s[wid] = v;
+  __syncthreads();
+  uint32_t t = s[0];
+#pragma unroll
+  for (int w = 1; w < kT32Waves; ++w) t = max(t, s[w]);
+  __syncthreads();
+  return t;
+}
+
+// Per-walk LDS: reduction slots and the cut thread's answer.
+struct T32Walk {
+  u64 red[kT32Waves];
+  uint32_t red32[kT32Waves];
+  int ired[kT32Waves];
+  u64 above;
+  int bin;
+};
+
+// The bin at which the sum from the top first reaches goal (> 0): the highest
+// bin b whose inclusive sum from the top, over bins >= b, is >= goal. Returns
+// b, or -1 when the total stays below goal, and in `above` the sum over the
+// bins above b (the total when -1). Thread t holds bins NB/512 * t onwards.
+// T: uint32_t (counts) or u64 (fixed-point masses).
+template <typename T, int NB>
+__device__ inline int t32_walk(const T* v, T goal, T& above, T32Walk& w) {
+  constexpr int BPT = NB / kT32Block;
+  const int tid = threadIdx.x;
+  T own = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) own += v[tid * BPT + i];
+  T total;
+  T abv;
+  if constexpr (sizeof(T) == 8)
+    abv = tr_above<T, kT32Waves>(own, w.red, total);
+  else
+    abv = tr_above<T, kT32Waves>(own, w.red32, total);
+  const int cut = tr_max<kT32Waves>(abv + own >= goal ? tid : -1, w.ired);
+  if (tid == cut) {
+    T acc = abv;
+    for (int i = BPT - 1; i >= 0; --i) {
+      const T x = v[tid * BPT + i];
+      if (acc + x >= goal) {
+        w.bin = tid * BPT + i;
+        w.above = u64(acc);
+        break;
+      }
+      acc += x;
+    }
+  }
+  __syncthreads();
+  const int bin = cut >= 0 ? w.bin : -1;
+  above = cut >= 0 ? T(w.above) : total;
+  __syncthreads();
+  return bin;
+}
+
+template <int NB>
+__device__ inline u64 t32_sum(const u64* v, T32Walk& w) {
+  constexpr int BPT = NB / kT32Block;
+  u64 own = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) own += v[threadIdx.x * BPT + i];
+  return tr_sum<u64, kT32Waves>(own, w.red);
+}
+
+template <typename T_, int NB>
+__device__ inline void t32_clear(T_* a) {
+  for (int i = threadIdx.x; i < NB; i += kT32Block) a[i] = T_(0);
+}
+
+// One workgroup per (sequence, row): blockIdx.x = b (2K + 1) + r.
+template <int VEC>
+__global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
+    double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t cnt[kT32Bins1];
+  __shared__ u64 m1[kT32Bins1];
+  __shared__ u64 m2[kT32Bins], m3[kT32Bins];
+  __shared__ uint32_t s_u[kT32Waves];
+  __shared__ T32Walk w;
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  const int rows = 2 * K + 1;
+  const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
+  if (kdraft != nullptr) {           // rows past the draft count are not needed
+    const int kb = kdraft[b];
+    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  }
+  const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
+  const long long nchunks = V / VEC;
+  const double scale = __builtin_ldexp(1.0, fx);
+  const int kk = tr.k != nullptr ? tr.k[b] : 0;
+  const bool kon = kk >= 1 && kk < V;
+  const float pp = tr.p != nullptr ? tr.p[b] : 1.0f;
+  const bool pon = pp < 1.0f;
+  auto put = [&](double S, float R, uint32_t thr) {
+    if (tid == 0) {
+      RowPart p;
+      p.S = S;
+      p.R = R;
+      p.m = 0.0f;
+      p.idx = int(thr);
+      p.flags = 0;
+      parts[blockIdx.x] = p;
+    }
+  };
+
+  // ---- read A: maximum, non-finite values, first-digit counts ----
+  t32_clear<uint32_t, kT32Bins1>(cnt);
+  t32_clear<u64, kT32Bins1>(m1);
+  t32_clear<u64, kT32Bins>(m2);
+  t32_clear<u64, kT32Bins>(m3);
+  __syncthreads();
+  uint32_t top = 0u, nonfin = 0u;
+  t32_stream<VEC>(row, nchunks, [&](uint32_t bits) {
+    const uint32_t key = order_key<DT_F32>(bits);
+    const bool fin = key > kKey32NegInf && key < kKey32PosInf;
+    top = max(top, fin ? key : 0u);
+    nonfin |= (key < kKey32NegInf || key >= kKey32PosInf) ? 1u : 0u;
+    if (kon) atomicAdd(&cnt[key >> 20], 1u);
+  });
+  top = t32_max(top, s_u);
+  const bool bad = t32_max(nonfin, s_u) != 0u || top == 0u || !(pp > 0.0f);
+  if (bad) return put(__builtin_nan(""), 0.0f, 0u);
+  const float R = ceilf(order_floor<DT_F32>(top) * c);
+
+  // ---- top-k: the k-th largest key, digit by digit ----
+  uint32_t tk = 0u, b1 = 0u, b2 = 0u;
+  if (kon) {
+    uint32_t rem = uint32_t(kk), abv;
+    const int c1 = t32_walk<uint32_t, kT32Bins1>(cnt, rem, abv, w);   // the total is V >= k
+    if (c1 < 0) return put(__builtin_nan(""), 0.0f, 0u);
+    b1 = uint32_t(c1);
+    rem -= abv;
+    t32_clear<uint32_t, kT32Bins>(cnt);
+    __syncthreads();
+    T32Sel s = t32_none();           // read B
+    s.count = true;
+    s.cmask = 0xfff00000u;
+    s.cval = b1 << 20;
+    s.cshift = 10;
+    s.m1 = b1 + 1u < uint32_t(kT32Bins1);
+    s.m1_floor = (b1 + 1u) << 20;
+    s.m2 = true;
+    s.m2_bin = b1;
+    t32_read<VEC>(row, nchunks, s, c64, R, scale, cnt, m1, m2, m3);
+    const int c2 = t32_walk<uint32_t, kT32Bins>(cnt, rem, abv, w);
+    if (c2 < 0) return put(__builtin_nan(""), 0.0f, 0u);
+    b2 = uint32_t(c2);
+    rem -= abv;
+    t32_clear<uint32_t, kT32Bins>(cnt);
+    __syncthreads();
+    s = t32_none();                  // read C
+    s.count = true;
+    s.cmask = 0xfffffc00u;
+    s.cval = (b1 << 20) | (b2 << 10);
+    s.cshift = 0;
+    s.m3 = true;
+    s.m3_sel = (b1 << 10) | b2;
+    t32_read<VEC>(row, nchunks, s, c64, R, scale, cnt, m1, m2, m3);
+    const int c3 = t32_walk<uint32_t, kT32Bins>(cnt, rem, abv, w);
+    if (c3 < 0) return put(__builtin_nan(""), 0.0f, 0u);
+    const uint32_t b3 = uint32_t(c3);
+    tk = (b1 << 20) | (b2 << 10) | b3;
+    // kept masses: drop what lies below the cut at each digit and fold each
+    // cut bin into the coarser digit
+    for (int i = tid; i < kT32Bins; i += kT32Block)
+      if (uint32_t(i) < b3) m3[i] = 0ull;
+    __syncthreads();
+    const u64 mk2 = t32_sum<kT32Bins>(m3, w);
+    for (int i = tid; i < kT32Bins; i += kT32Block)
+      if (uint32_t(i) < b2) m2[i] = 0ull;
+    if (tid == 0) m2[b2] = mk2;
+    __syncthreads();
+    const u64 mk1 = t32_sum<kT32Bins>(m2, w);
+    if (tid == 0) m1[b1] = mk1;
+    __syncthreads();
+  } else {
+    T32Sel s = t32_none();           // read D
+    s.m1 = true;
+    t32_read<VEC>(row, nchunks, s, c64, R, scale, cnt, m1, m2, m3);
+  }
+  const u64 S_k = t32_sum<kT32Bins1>(m1, w);
+  if (!pon) return put(__builtin_ldexp(double(S_k), -fx), R, tk);
+
+  // ---- top-p: the level where the mass from the top reaches top_p S_k ----
+  u64 goal = u64(__builtin_ceil(double(pp) * double(S_k)));
+  goal = min(max(goal, 1ull), S_k);
+  u64 a1, a2, a3;
+  const int q1 = t32_walk<u64, kT32Bins1>(m1, goal, a1, w);
+  if (q1 < 0) return put(__builtin_nan(""), 0.0f, 0u);
+  const uint32_t p1 = uint32_t(q1);
+  goal -= a1;
+  const bool same1 = kon && p1 == b1;      // m2 already holds p1's kept masses
+  if (!same1) {
+    t32_clear<u64, kT32Bins>(m2);
+    __syncthreads();
+    T32Sel s = t32_none();           // read E
+    s.m2 = true;
+    s.m2_bin = p1;
+    s.m2_floor = tk;
+    t32_read<VEC>(row, nchunks, s, c64, R, scale, cnt, m1, m2, m3);
+  }
+  const int q2 = t32_walk<u64, kT32Bins>(m2, goal, a2, w);
+  if (q2 < 0) return put(__builtin_nan(""), 0.0f, 0u);
+  const uint32_t p2 = uint32_t(q2);
+  goal -= a2;
+  if (!(same1 && p2 == b2)) {
+    t32_clear<u64, kT32Bins>(m3);
+    __syncthreads();
+    T32Sel s = t32_none();           // read F
+    s.m3 = true;
+    s.m3_sel = (p1 << 10) | p2;
+    s.m3_floor = tk;
+    t32_read<VEC>(row, nchunks, s, c64, R, scale, cnt, m1, m2, m3);
+  }
+  const int q3 = t32_walk<u64, kT32Bins>(m3, goal, a3, w);
+  if (q3 < 0) return put(__builtin_nan(""), 0.0f, 0u);
+  const uint32_t p3 = uint32_t(q3);
+  const u64 S_p = a1 + a2 + a3 + m3[p3];
+  put(__builtin_ldexp(double(S_p), -fx), R, (p1 << 20) | (p2 << 10) | p3);
+}
+
+}  // namespace sv

@@ -1,0 +1,226 @@
+"""GPU parity of top-k / top-p truncation over fp32 rows against the oracle.
+
+fp32 rows go through their own truncation pass (the k-th largest order key
+and the top-p level found digit by digit, 12 + 10 + 10 bits, with fixed-point
+masses) and then the per-sequence finish, whose draw compares each value's
+order key with its row's threshold. The tests cover: per-sequence mixes of
+settings (off, on, invalid), each rule alone, drafts from the untruncated
+draft (q(d) = 0 accepted), values that share their upper key digits, ties,
+-inf, zeros of both signs, huge magnitudes, rows with NaN or +inf, low
+temperatures (the draw's per-term scaled path), the stopping rules, the
+residual side output, top_k = 1 against the greedy mode, vocabularies that
+are not a multiple of 4 (scalar loads), and the c5 shape (B = 1024, K = 4,
+V = 128256) on sampled sequences.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import spec_oracle as O
+from tests.parity import compare, oracle_for
+from tests.test_gpu_trunc import _check, _resample_drafts, _settings
+from workloads import CONFIGS, make_inputs, to_host_f64, window_edge_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+SMALL = CONFIGS["c5"].scaled(B=48, V=20000)
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import speculative_decoding_verification_temp_amd as pkg
+    pkg.load_library()
+    torch.cuda.set_device(DEV)
+    return pkg
+
+
+def test_trunc32_per_sequence_settings(sv):
+    cfg = SMALL
+    x = make_inputs(cfg, 1, DEV)
+    assert x["target"].dtype == torch.float32
+    tk, tp = _settings(cfg.B, cfg.V, 21, invalid=True)
+    _resample_drafts(x, cfg.T, tk, tp, 22)
+    tok, alen, ref = _check(sv, x, cfg, tk, tp, "trunc32/mixed")
+    a = alen.cpu().numpy()
+    assert a[1] == -1 and a[2] == -1          # top_p = 0 and NaN
+    assert (a >= 0).sum() == cfg.B - 2
+
+
+@pytest.mark.parametrize("which", ["top_k", "top_p"])
+def test_trunc32_one_rule(sv, which):
+    cfg = SMALL.scaled(B=32)
+    x = make_inputs(cfg, 2, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 23)
+    if which == "top_k":
+        tp = None
+    else:
+        tk = None
+    _resample_drafts(x, cfg.T, tk if tk is not None else np.zeros(cfg.B, np.int32),
+                     tp if tp is not None else np.ones(cfg.B, np.float32), 24)
+    _check(sv, x, cfg, tk, tp, f"trunc32/{which}")
+
+
+def test_trunc32_untruncated_drafts(sv):
+    cfg = SMALL.scaled(B=32)
+    x = make_inputs(cfg, 3, DEV)
+    tk = np.full(cfg.B, 30, np.int32)
+    tp = np.full(cfg.B, 0.9, np.float32)
+    _check(sv, x, cfg, tk, tp, "trunc32/raw drafts")
+
+
+def test_trunc32_special_values(sv):
+    """Per sequence (mod 8): 0 values that share their upper 22 key bits
+    (1 + n 2^-23), 1 integer ties, 2 -inf in a third of the entries with
+    +-0, 3 magnitudes near 3e6 (a bin's values span far more than the
+    float64 range of the softmax), 4 one value of +40 dominating, 5 all but
+    one value -inf, 6 one NaN (invalid), 7 one +inf (invalid)."""
+    cfg = SMALL.scaled(B=32, V=4096)
+    x = make_inputs(cfg, 4, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    V = cfg.V
+    for key in ("target", "draft"):
+        t = x[key]
+        for b in range(cfg.B):
+            for i in range(t.shape[1]):
+                kind = b % 8
+                r = torch.rand(V, generator=g, device=DEV)
+                if kind == 0:
+                    t[b, i] = 1.0 + torch.randint(0, 50, (V,), generator=g, device=DEV) * 2.0 ** -23
+                elif kind == 1:
+                    t[b, i] = torch.randint(-3, 3, (V,), generator=g, device=DEV).float()
+                elif kind == 2:
+                    t[b, i] = torch.where(r < 0.3, float("-inf"), t[b, i])
+                    t[b, i] = torch.where((r >= 0.3) & (r < 0.4), 0.0, t[b, i])
+                    t[b, i] = torch.where((r >= 0.4) & (r < 0.5), -0.0, t[b, i])
+                elif kind == 3:
+                    t[b, i] = t[b, i] * 1e6 - 3e6
+                elif kind == 4:
+                    t[b, i, int(r[0] * V)] = 40.0
+                elif kind == 5:
+                    t[b, i] = float("-inf")
+                    t[b, i, int(r[0] * V)] = -5.0
+                elif kind == 6 and key == "target" and i == 0:
+                    t[b, i, int(r[0] * V)] = float("nan")
+                elif kind == 7 and key == "draft" and i == 0:
+                    t[b, i, int(r[0] * V)] = float("inf")
+    rng = np.random.default_rng(32)
+    tk = rng.choice([0, 1, 5, 100, 2000, V - 1], cfg.B).astype(np.int32)
+    tp = rng.choice([1.0, 0.3, 0.9, 0.99], cfg.B).astype(np.float32)
+    # drafts from the truncated law where it is defined (valid rows)
+    d = to_host_f64(x["draft"])
+    toks = np.zeros((cfg.B, cfg.K), dtype=np.int32)
+    for b in range(cfg.B):
+        for i in range(cfg.K):
+            row = d[b, i]
+            if np.isnan(row).any() or np.isposinf(row).any():
+                toks[b, i] = 0
+                continue
+            q, _ = O.truncated_softmax(row, cfg.T, int(tk[b]), float(tp[b]))
+            toks[b, i] = rng.choice(q.size, p=q)
+    x["tokens"] = torch.as_tensor(toks, device=DEV).contiguous()
+    tok, alen, ref = _check(sv, x, cfg, tk, tp, "trunc32/special values")
+    a = alen.cpu().numpy()
+    assert np.all(a[6::8] == -1) and np.all(a[7::8] == -1)
+
+
+def test_trunc32_window_edges(sv):
+    cfg = SMALL.scaled(B=32)
+    x = window_edge_inputs(cfg, 5, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 25)
+    _resample_drafts(x, cfg.T, tk, tp, 26)
+    _check(sv, x, cfg, tk, tp, "trunc32/window edges")
+
+
+def test_trunc32_low_temperature_scaled_path(sv):
+    cfg = SMALL.scaled(B=24)
+    x = make_inputs(cfg, 6, DEV)
+    T = 0.02
+    tk, tp = _settings(cfg.B, cfg.V, 27)
+    _resample_drafts(x, T, tk, tp, 28)
+    _check(sv, x, cfg, tk, tp, "trunc32/low temperature", T=T)
+
+
+def test_trunc32_with_stops(sv):
+    cfg = SMALL
+    x = make_inputs(cfg, 7, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 29)
+    _resample_drafts(x, cfg.T, tk, tp, 30)
+    rng = np.random.default_rng(33)
+    toks = x["tokens"].cpu().numpy()
+    eos = int(np.bincount(toks.ravel()).argmax())
+    kb = rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    mx = rng.integers(1, cfg.K + 3, cfg.B).astype(np.int32)
+    _check(sv, x, cfg, tk, tp, "trunc32/stops", stops=(eos, kb, mx))
+
+
+def test_trunc32_top_k_one_is_greedy(sv):
+    cfg = SMALL.scaled(B=64)
+    x = make_inputs(cfg, 8, DEV, "greedy")
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    g_tok, g_len, _ = [t.clone() for t in v.verify(x["target"], x["draft"], x["tokens"],
+                                                   x["uniforms"], cfg.T, "greedy")]
+    v.set_truncation(torch.ones(cfg.B, dtype=torch.int32, device=DEV), None)
+    s_tok, s_len, _ = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T,
+                               "stochastic")
+    torch.cuda.synchronize()
+    t, d = x["target"], x["draft"]
+    uniq = ((t == t.max(-1, keepdim=True).values).sum(-1) == 1).all(-1) & \
+           ((d == d.max(-1, keepdim=True).values).sum(-1) == 1).all(-1)
+    u = uniq.cpu().numpy()
+    assert u.sum() > cfg.B // 2
+    assert np.array_equal(s_tok.cpu().numpy()[u], g_tok.cpu().numpy()[u])
+    assert np.array_equal(s_len.cpu().numpy()[u], g_len.cpu().numpy()[u])
+
+
+def test_trunc32_with_residual(sv):
+    """Truncation and the residual side output in one call: the residual's
+    support is the untruncated draft's top m, from the own-read route."""
+    cfg = SMALL.scaled(B=16)
+    x = make_inputs(cfg, 9, DEV)
+    tk, tp = _settings(cfg.B, cfg.V, 34)
+    _resample_drafts(x, cfg.T, tk, tp, 35)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.float32)
+    aux = v.enable_aux()
+    v.set_truncation(torch.as_tensor(tk, device=DEV), torch.as_tensor(tp, device=DEV))
+    sup, res = v.set_residual(16)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T)
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.B)
+    ref = oracle_for(x, rows, "stochastic", trunc=(tk, tp))
+    compare(rows, ref, tok, alen, "stochastic", aux, "trunc32/residual")
+    T32 = float(np.float32(cfg.T))
+    r_sup, r_res = O.drift_batch(to_host_f64(x["target"]), to_host_f64(x["draft"]), T32, 16,
+                                 alen.cpu().numpy(), None)
+    g_res = res.cpu().numpy()
+    assert np.array_equal(sup.cpu().numpy(), r_sup)
+    both = np.isnan(g_res) & np.isnan(r_res)
+    assert np.all(both | (np.abs(g_res - r_res) <= 1e-9))
+
+
+@pytest.mark.parametrize("V,K,B", [(1001, 3, 8), (3, 1, 4), (16, 2, 1), (8191, 1, 5)])
+def test_trunc32_scalar_and_small_shapes(sv, V, K, B):
+    cfg = SMALL.scaled(B=B, K=K, V=V)
+    x = make_inputs(cfg, 12, DEV)
+    for b in range(0, B, 2):
+        x["target"][b, 0, (7 * b) % V] = 2.0 ** -30
+        x["draft"][b, 0, (3 * b + 1) % V] = -200.0
+    rng = np.random.default_rng(36)
+    tk = rng.integers(0, V + 1, B).astype(np.int32)
+    tp = rng.choice([1.0, 0.3, 0.7, 0.95], B).astype(np.float32)
+    _resample_drafts(x, cfg.T, tk, tp, 37)
+    _check(sv, x, cfg, tk, tp, f"trunc32/V={V} K={K} B={B}")
+
+
+def test_trunc32_c5_sampled(sv):
+    """The c5 shape (B = 1024, K = 4, V = 128256, fp32, its p = q and
+    zero-mass sequences included) with top_k = 50 and top_p = 0.9 on every
+    sequence; the oracle checks 24 sampled sequences."""
+    cfg = CONFIGS["c5"]
+    x = make_inputs(cfg, 0, DEV)
+    tk = np.full(cfg.B, 50, np.int32)
+    tp = np.full(cfg.B, 0.9, np.float32)
+    rows = np.random.default_rng(38).choice(cfg.B, 24, replace=False)
+    _check(sv, x, cfg, tk, tp, "trunc32/c5 sampled", rows=np.sort(rows))
