@@ -41,6 +41,8 @@ STREAM_SOURCES = {
     "rowstats_max": ("sv_device.hpp", "sv_topm.hpp", "sv_rowstats.hpp"),
     "rowstats_trunc_win": ("sv_device.hpp", "sv_topm.hpp", "sv_rowstats.hpp", "sv_kernels.hpp",
                            "sv_fused.hpp", "sv_trunc.hpp"),
+    "rowstats_trunc32": ("sv_device.hpp", "sv_topm.hpp", "sv_rowstats.hpp", "sv_kernels.hpp",
+                         "sv_fused.hpp", "sv_trunc.hpp", "sv_trunc32.hpp"),
 }
 
 
@@ -309,7 +311,8 @@ def main():
     pass_bytes = rows_total * V * s
     io_bytes = B * (K * 4 + (K + 1) * 4 + (K + 1) * 4 + 4) + 2 * B * K * s
     call_bytes = pass_bytes + sum(draw_bytes) / len(draw_bytes) + io_bytes
-    kernel = ("rowstats_trunc_win" if trunc else "rowstats_sum") if mode == "stochastic" \
+    trunc_kernel = "rowstats_trunc32" if cfg.dtype == "f32" else "rowstats_trunc_win"
+    kernel = (trunc_kernel if trunc else "rowstats_sum") if mode == "stochastic" \
         else "rowstats_max"
     achieved = pass_bytes / (pass_avg * 1e-3) / 1e9
     workload = f"{cfg.name}/{mode}" + (f"/top-k{args.top_k}-top-p{args.top_p}" if trunc else "") \

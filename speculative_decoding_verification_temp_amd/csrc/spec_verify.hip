@@ -75,6 +75,7 @@ struct spec_verify_handle {
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int n_cu = 256;          // compute units of the device
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
+  int trunc32_buf = 1;     // fp32 truncation: sort the few candidate values in LDS (0 = digit reads only)
   char err[256] = {0};
 };
 
@@ -244,8 +245,8 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
   while ((1ll << lg) < (long long)V) ++lg;
   prof_mark(h, 0, s);
   hipLaunchKernelGGL((sv::rowstats_trunc32<VEC>), dim3(unsigned(B * rows)), dim3(sv::kT32Block),
-                     0, s, target, draft, K, V, c, c64, 61 - lg, h->trunc, h->rules.k, h->parts,
-                     hist);
+                     0, s, target, draft, K, V, c, c64, 61 - lg, h->trunc32_buf, h->trunc,
+                     h->rules.k, h->parts, hist);
   int rc = check_launch(h, "rowstats_trunc32");
   prof_mark(h, 1, s);
   if (rc) return rc;
@@ -373,6 +374,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   h->decay = ema_decay;
   h->target_wgs = env_int("SPEC_VERIFY_TARGET_WGS", 2048);
   h->nseg_force = env_int("SPEC_VERIFY_NSEG", 0);
+  h->trunc32_buf = env_int("SPEC_VERIFY_TRUNC32_BUF", 1);
   h->tiles_per_group = env_int("SPEC_VERIFY_TILES_PER_GROUP", 16);
   if (h->tiles_per_group < 1) h->tiles_per_group = 1;
   h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);

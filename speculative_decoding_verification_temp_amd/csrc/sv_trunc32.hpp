@@ -22,6 +22,13 @@
 // exact threshold key. All reads use cached loads: a row read again is
 // usually still in the last-level cache.
 //
+// Most rows need fewer reads: when the values from the first digit's cut bin
+// upwards number at most kT32Buf (top-k: every value the truncation can keep;
+// top-p alone: the values of the bin where the mass crosses), the second read
+// copies their keys into LDS instead, a bitonic sort orders them, and the
+// k-th largest key, the prefix masses and the top-p level come from the
+// sorted keys: two reads of the row with top-k, three with top-p alone.
+//
 // Masses are softmax terms 2^(x c - R), each rounded once to unsigned 64-bit
 // fixed point with FX = 61 - ceil(log2 V) fraction bits (a term is at most
 // about 1, so no sum reaches 2^62), and summed with integer LDS atomics. The
@@ -47,6 +54,7 @@ constexpr int kT32Block = 512;
 constexpr int kT32Waves = kT32Block / kWave;
 constexpr int kT32Bins1 = 4096;     // first digit: key bits 31..20
 constexpr int kT32Bins = 1024;      // second and third digits: bits 19..10 and 9..0
+constexpr int kT32Buf = kT32Bins1;  // keys copied into LDS (in the first digit's count array)
 constexpr uint32_t kKey32NegInf = 0x80000000u - 0x7f800000u;
 constexpr uint32_t kKey32PosInf = 0x80000000u + 0x7f800000u;
 
@@ -204,16 +212,107 @@ __device__ inline void t32_clear(T_* a) {
   for (int i = threadIdx.x; i < NB; i += kT32Block) a[i] = T_(0);
 }
 
+// ---- the buffered route: up to kT32Buf keys in LDS ----
+// Thread t holds entries (kT32Block - 1 - t) E .. + E - 1, so that the
+// threads above t (tr_above) hold the entries before its own.
+constexpr int kT32E = kT32Buf / kT32Block;
+
+// Sort buf[0..n) descending: bitonic over the next power of two, padded
+// with key 0 (below the key of every value of a valid row).
+__device__ inline void t32_sort_desc(uint32_t* buf, int n) {
+  const int tid = threadIdx.x;
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + tid; i < n2; i += kT32Block) buf[i] = 0u;
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += kT32Block) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t a = buf[i], b = buf[l];
+          if ((i & k) == 0 ? a < b : a > b) {
+            buf[i] = b;
+            buf[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// P[i] = the fixed-point mass of the sorted keys buf[0..i] that are >= floor;
+// returns the total.
+__device__ inline u64 t32_prefix(const uint32_t* buf, int n, uint32_t floor, double c64, float R,
+                                 double scale, u64* P, T32Walk& w) {
+  const int base = (kT32Block - 1 - int(threadIdx.x)) * kT32E;
+  u64 loc[kT32E], own = 0;
+#pragma unroll
+  for (int e = 0; e < kT32E; ++e) {
+    const int i = base + e;
+    const uint32_t key = i < n ? buf[i] : 0u;
+    if (i < n && key >= floor) own += fixed_term(order_floor<DT_F32>(key), c64, R, scale);
+    loc[e] = own;
+  }
+  u64 total;
+  const u64 before = tr_above<u64, kT32Waves>(own, w.red, total);
+#pragma unroll
+  for (int e = 0; e < kT32E; ++e)
+    if (base + e < n) P[base + e] = before + loc[e];
+  __syncthreads();
+  return total;
+}
+
+// the smallest i < n with P[i] >= goal (P non-decreasing), -1 if none
+__device__ inline int t32_first_reach(const u64* P, int n, u64 goal, T32Walk& w) {
+  const int base = (kT32Block - 1 - int(threadIdx.x)) * kT32E;
+  int first = -1;
+#pragma unroll
+  for (int e = kT32E - 1; e >= 0; --e)
+    if (base + e < n && P[base + e] >= goal) first = base + e;
+  const int best = tr_max<kT32Waves>(first >= 0 ? kT32Buf - first : -1, w.ired);
+  return best >= 0 ? kT32Buf - best : -1;
+}
+
+// the number of keys >= key among buf[0..n)
+__device__ inline uint32_t t32_count_ge(const uint32_t* buf, int n, uint32_t key, T32Walk& w) {
+  uint32_t c = 0;
+  for (int i = threadIdx.x; i < n; i += kT32Block) c += buf[i] >= key ? 1u : 0u;
+  return tr_sum<uint32_t, kT32Waves>(c, w.red32);
+}
+
+// Copy the keys of the row with (key >> 20) in [lo, hi] into buf; returns
+// how many there were (more than kT32Buf: only the first kT32Buf stored).
+template <int VEC>
+__device__ inline uint32_t t32_gather(const void* row, long long nchunks, uint32_t lo, uint32_t hi,
+                                      uint32_t* buf, uint32_t* s_n) {
+  if (threadIdx.x == 0) *s_n = 0u;
+  __syncthreads();
+  t32_stream<VEC>(row, nchunks, [&](uint32_t bits) {
+    const uint32_t key = order_key<DT_F32>(bits);
+    const uint32_t d = key >> 20;
+    if (d >= lo && d <= hi) {
+      const uint32_t pos = atomicAdd(s_n, 1u);
+      if (pos < uint32_t(kT32Buf)) buf[pos] = key;
+    }
+  });
+  const uint32_t n = *s_n;
+  __syncthreads();
+  return n;
+}
+
 // One workgroup per (sequence, row): blockIdx.x = b (2K + 1) + r.
 template <int VEC>
 __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
-    double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
+    double c64, int fx, int use_buf, Trunc tr, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
   __shared__ uint32_t cnt[kT32Bins1];
   __shared__ u64 m1[kT32Bins1];
   __shared__ u64 m2[kT32Bins], m3[kT32Bins];
   __shared__ uint32_t s_u[kT32Waves];
+  __shared__ uint32_t s_n;
   __shared__ T32Walk w;
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
@@ -249,12 +348,13 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   t32_clear<u64, kT32Bins>(m3);
   __syncthreads();
   uint32_t top = 0u, nonfin = 0u;
+  const bool count1 = kon || (pon && use_buf);
   t32_stream<VEC>(row, nchunks, [&](uint32_t bits) {
     const uint32_t key = order_key<DT_F32>(bits);
     const bool fin = key > kKey32NegInf && key < kKey32PosInf;
     top = max(top, fin ? key : 0u);
     nonfin |= (key < kKey32NegInf || key >= kKey32PosInf) ? 1u : 0u;
-    if (kon) atomicAdd(&cnt[key >> 20], 1u);
+    if (count1) atomicAdd(&cnt[key >> 20], 1u);
   });
   top = t32_max(top, s_u);
   const bool bad = t32_max(nonfin, s_u) != 0u || top == 0u || !(pp > 0.0f);
@@ -268,6 +368,24 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
     const int c1 = t32_walk<uint32_t, kT32Bins1>(cnt, rem, abv, w);   // the total is V >= k
     if (c1 < 0) return put(__builtin_nan(""), 0.0f, 0u);
     b1 = uint32_t(c1);
+    const uint32_t n_hi = abv + cnt[b1];   // values in bins b1 and above
+    if (use_buf && n_hi <= uint32_t(kT32Buf)) {
+      // ---- buffered: every value top-k can keep, sorted in LDS ----
+      __syncthreads();                 // cnt[b1] read before cnt holds keys
+      const uint32_t n = t32_gather<VEC>(row, nchunks, b1, uint32_t(kT32Bins1 - 1), cnt, &s_n);
+      if (n != n_hi) return put(__builtin_nan(""), 0.0f, 0u);
+      t32_sort_desc(cnt, int(n));
+      tk = cnt[kk - 1];
+      const u64 Sb = t32_prefix(cnt, int(n), tk, c64, R, scale, m1, w);
+      if (!pon) return put(__builtin_ldexp(double(Sb), -fx), R, tk);
+      u64 goal = u64(__builtin_ceil(double(pp) * double(Sb)));
+      goal = min(max(goal, 1ull), Sb);
+      const int i = t32_first_reach(m1, int(n), goal, w);
+      if (i < 0) return put(__builtin_nan(""), 0.0f, 0u);
+      const uint32_t thr = cnt[i];
+      const uint32_t n_thr = t32_count_ge(cnt, int(n), thr, w);
+      return put(__builtin_ldexp(double(m1[n_thr - 1]), -fx), R, thr);
+    }
     rem -= abv;
     t32_clear<uint32_t, kT32Bins>(cnt);
     __syncthreads();
@@ -328,6 +446,20 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   if (q1 < 0) return put(__builtin_nan(""), 0.0f, 0u);
   const uint32_t p1 = uint32_t(q1);
   goal -= a1;
+  if (!kon && use_buf && cnt[p1] <= uint32_t(kT32Buf)) {
+    // ---- buffered: the crossing bin's values, sorted in LDS ----
+    const uint32_t n_p = cnt[p1];
+    __syncthreads();                   // cnt[p1] read before cnt holds keys
+    const uint32_t n = t32_gather<VEC>(row, nchunks, p1, p1, cnt, &s_n);
+    if (n != n_p) return put(__builtin_nan(""), 0.0f, 0u);
+    t32_sort_desc(cnt, int(n));
+    t32_prefix(cnt, int(n), 0u, c64, R, scale, m1, w);
+    const int i = t32_first_reach(m1, int(n), goal, w);
+    if (i < 0) return put(__builtin_nan(""), 0.0f, 0u);
+    const uint32_t thr = cnt[i];
+    const uint32_t n_thr = t32_count_ge(cnt, int(n), thr, w);
+    return put(__builtin_ldexp(double(a1 + m1[n_thr - 1]), -fx), R, thr);
+  }
   const bool same1 = kon && p1 == b1;      // m2 already holds p1's kept masses
   if (!same1) {
     t32_clear<u64, kT32Bins>(m2);

@@ -2,15 +2,18 @@
 
 fp32 rows go through their own truncation pass (the k-th largest order key
 and the top-p level found digit by digit, 12 + 10 + 10 bits, with fixed-point
-masses) and then the per-sequence finish, whose draw compares each value's
-order key with its row's threshold. The tests cover: per-sequence mixes of
-settings (off, on, invalid), each rule alone, drafts from the untruncated
-draft (q(d) = 0 accepted), values that share their upper key digits, ties,
--inf, zeros of both signs, huge magnitudes, rows with NaN or +inf, low
-temperatures (the draw's per-term scaled path), the stopping rules, the
-residual side output, top_k = 1 against the greedy mode, vocabularies that
-are not a multiple of 4 (scalar loads), and the c5 shape (B = 1024, K = 4,
-V = 128256) on sampled sequences.
+masses, or from the few candidate values sorted in LDS) and then the
+per-sequence finish, whose draw compares each value's order key with its
+row's threshold. The main cases run on both routes of the pass (the `route`
+fixture; SPEC_VERIFY_TRUNC32_BUF=0 keeps to the digit reads), and rows whose
+candidates do not fit the buffer fall back by themselves. The tests cover:
+per-sequence mixes of settings (off, on, invalid), each rule alone, drafts
+from the untruncated draft (q(d) = 0 accepted), values that share their
+upper key digits, ties, -inf, zeros of both signs, huge magnitudes, rows with
+NaN or +inf, low temperatures (the draw's per-term scaled path), the stopping
+rules, the residual side output, top_k = 1 against the greedy mode,
+vocabularies that are not a multiple of 4 (scalar loads), and the c5 shape
+(B = 1024, K = 4, V = 128256) on sampled sequences.
 """
 
 import numpy as np
@@ -28,6 +31,13 @@ DEV = torch.device("cuda", 0)
 SMALL = CONFIGS["c5"].scaled(B=48, V=20000)
 
 
+@pytest.fixture(params=["buffered", "digits"])
+def route(request, monkeypatch):
+    """The truncation pass's route, read when a verifier is created."""
+    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_BUF", "1" if request.param == "buffered" else "0")
+    return request.param
+
+
 @pytest.fixture(scope="module")
 def sv():
     import speculative_decoding_verification_temp_amd as pkg
@@ -36,20 +46,20 @@ def sv():
     return pkg
 
 
-def test_trunc32_per_sequence_settings(sv):
+def test_trunc32_per_sequence_settings(sv, route):
     cfg = SMALL
     x = make_inputs(cfg, 1, DEV)
     assert x["target"].dtype == torch.float32
     tk, tp = _settings(cfg.B, cfg.V, 21, invalid=True)
     _resample_drafts(x, cfg.T, tk, tp, 22)
-    tok, alen, ref = _check(sv, x, cfg, tk, tp, "trunc32/mixed")
+    tok, alen, ref = _check(sv, x, cfg, tk, tp, f"trunc32/mixed/{route}")
     a = alen.cpu().numpy()
     assert a[1] == -1 and a[2] == -1          # top_p = 0 and NaN
     assert (a >= 0).sum() == cfg.B - 2
 
 
 @pytest.mark.parametrize("which", ["top_k", "top_p"])
-def test_trunc32_one_rule(sv, which):
+def test_trunc32_one_rule(sv, which, route):
     cfg = SMALL.scaled(B=32)
     x = make_inputs(cfg, 2, DEV)
     tk, tp = _settings(cfg.B, cfg.V, 23)
@@ -59,7 +69,7 @@ def test_trunc32_one_rule(sv, which):
         tk = None
     _resample_drafts(x, cfg.T, tk if tk is not None else np.zeros(cfg.B, np.int32),
                      tp if tp is not None else np.ones(cfg.B, np.float32), 24)
-    _check(sv, x, cfg, tk, tp, f"trunc32/{which}")
+    _check(sv, x, cfg, tk, tp, f"trunc32/{which}/{route}")
 
 
 def test_trunc32_untruncated_drafts(sv):
@@ -70,7 +80,7 @@ def test_trunc32_untruncated_drafts(sv):
     _check(sv, x, cfg, tk, tp, "trunc32/raw drafts")
 
 
-def test_trunc32_special_values(sv):
+def test_trunc32_special_values(sv, route):
     """Per sequence (mod 8): 0 values that share their upper 22 key bits
     (1 + n 2^-23), 1 integer ties, 2 -inf in a third of the entries with
     +-0, 3 magnitudes near 3e6 (a bin's values span far more than the
@@ -121,7 +131,7 @@ def test_trunc32_special_values(sv):
             q, _ = O.truncated_softmax(row, cfg.T, int(tk[b]), float(tp[b]))
             toks[b, i] = rng.choice(q.size, p=q)
     x["tokens"] = torch.as_tensor(toks, device=DEV).contiguous()
-    tok, alen, ref = _check(sv, x, cfg, tk, tp, "trunc32/special values")
+    tok, alen, ref = _check(sv, x, cfg, tk, tp, f"trunc32/special values/{route}")
     a = alen.cpu().numpy()
     assert np.all(a[6::8] == -1) and np.all(a[7::8] == -1)
 
@@ -201,7 +211,7 @@ def test_trunc32_with_residual(sv):
 
 
 @pytest.mark.parametrize("V,K,B", [(1001, 3, 8), (3, 1, 4), (16, 2, 1), (8191, 1, 5)])
-def test_trunc32_scalar_and_small_shapes(sv, V, K, B):
+def test_trunc32_scalar_and_small_shapes(sv, V, K, B, route):
     cfg = SMALL.scaled(B=B, K=K, V=V)
     x = make_inputs(cfg, 12, DEV)
     for b in range(0, B, 2):
@@ -211,10 +221,10 @@ def test_trunc32_scalar_and_small_shapes(sv, V, K, B):
     tk = rng.integers(0, V + 1, B).astype(np.int32)
     tp = rng.choice([1.0, 0.3, 0.7, 0.95], B).astype(np.float32)
     _resample_drafts(x, cfg.T, tk, tp, 37)
-    _check(sv, x, cfg, tk, tp, f"trunc32/V={V} K={K} B={B}")
+    _check(sv, x, cfg, tk, tp, f"trunc32/V={V} K={K} B={B}/{route}")
 
 
-def test_trunc32_c5_sampled(sv):
+def test_trunc32_c5_sampled(sv, route):
     """The c5 shape (B = 1024, K = 4, V = 128256, fp32, its p = q and
     zero-mass sequences included) with top_k = 50 and top_p = 0.9 on every
     sequence; the oracle checks 24 sampled sequences."""
@@ -223,4 +233,27 @@ def test_trunc32_c5_sampled(sv):
     tk = np.full(cfg.B, 50, np.int32)
     tp = np.full(cfg.B, 0.9, np.float32)
     rows = np.random.default_rng(38).choice(cfg.B, 24, replace=False)
-    _check(sv, x, cfg, tk, tp, "trunc32/c5 sampled", rows=np.sort(rows))
+    _check(sv, x, cfg, tk, tp, f"trunc32/c5 sampled/{route}", rows=np.sort(rows))
+
+
+def test_trunc32_candidates_beyond_buffer(sv):
+    """Rows whose candidate values do not fit the LDS buffer take the digit
+    reads under the default setting. Sequences b % 4 < 3 hold rows of
+    1 + 0.1 u (all values in one first-digit bin, [1, 1.125)) at T = 0.05:
+    top-k at half the vocabulary, top-p = 0.5 alone, and top-k 40 with
+    top-p 0.9 (the cut bin holds every value of the row); sequences
+    b % 4 == 3 keep their plain rows with top-k 40 and top-p 0.9, which fit."""
+    cfg = SMALL.scaled(B=32, T=0.05)
+    x = make_inputs(cfg, 13, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(41)
+    for key in ("target", "draft"):
+        t = x[key]
+        for b in range(cfg.B):
+            if b % 4 < 3:
+                t[b] = 1.0 + 0.1 * torch.rand(t.shape[1:], generator=g, device=DEV)
+    m = np.arange(cfg.B) % 4
+    tk = np.select([m == 0, m == 1], [cfg.V // 2, 0], 40).astype(np.int32)
+    tp = np.select([m == 0, m == 1], [1.0, 0.5], 0.9).astype(np.float32)
+    _resample_drafts(x, cfg.T, tk, tp, 39)
+    _check(sv, x, cfg, tk, tp, "trunc32/beyond buffer")
