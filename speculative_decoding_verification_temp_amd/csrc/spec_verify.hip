@@ -76,6 +76,7 @@ struct spec_verify_handle {
   int n_cu = 256;          // compute units of the device
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
   int trunc32_buf = 1;     // fp32 truncation: sort the few candidate values in LDS (0 = digit reads only)
+  int trunc32_list = 1;    // fp32 truncation: settle rows from one read's top-k list first (0 = off)
   char err[256] = {0};
 };
 
@@ -228,9 +229,11 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
   return check_launch(h, "finish_seq (truncated)");
 }
 
-// Stochastic mode with top-k / top-p truncation (fp32 rows): the digit-wise
-// truncation pass over every needed row, then the per-sequence finish, whose
-// draw compares each value's order key with its row's threshold.
+// Stochastic mode with top-k / top-p truncation (fp32 rows): the list pass
+// (16-byte chunks) settles most rows in one read, the multi-read pass takes
+// the rows it hands over (every needed row for other chunks), then the
+// per-sequence finish, whose draw compares each value's order key with its
+// row's threshold.
 template <int VEC>
 int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* draft,
                 const int32_t* tokens, const float* uniforms, float c, double c64,
@@ -244,11 +247,22 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
   int lg = 0;                        // ceil(log2 V): fixed-point masses keep 61 - lg bits
   while ((1ll << lg) < (long long)V) ++lg;
   prof_mark(h, 0, s);
+  const bool list = VEC == 4 && h->trunc32_list;
+  int rc = SV_OK;
+  if constexpr (VEC == 4) {
+    if (list) {
+      hipLaunchKernelGGL((sv::rowstats_trunc32_list<VEC>), dim3(unsigned(B * rows)),
+                         dim3(sv::kT1Block), 0, s, target, draft, K, V, c, c64, 61 - lg,
+                         h->trunc, h->rules.k, h->parts, hist);
+      rc = check_launch(h, "rowstats_trunc32_list");
+    }
+  }
+  if (rc) return rc;
   hipLaunchKernelGGL((sv::rowstats_trunc32<VEC>), dim3(unsigned(B * rows)), dim3(sv::kT32Block),
-                     0, s, target, draft, K, V, c, c64, 61 - lg, h->trunc32_buf, h->trunc,
-                     h->rules.k, h->parts, hist);
-  int rc = check_launch(h, "rowstats_trunc32");
-  prof_mark(h, 1, s);
+                     0, s, target, draft, K, V, c, c64, 61 - lg, h->trunc32_buf, list ? 1 : 0,
+                     h->trunc, h->rules.k, h->parts, list ? nullptr : hist);
+  rc = check_launch(h, "rowstats_trunc32");
+  prof_mark(h, 1, s);                // both truncation passes
   if (rc) return rc;
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
@@ -375,6 +389,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   h->target_wgs = env_int("SPEC_VERIFY_TARGET_WGS", 2048);
   h->nseg_force = env_int("SPEC_VERIFY_NSEG", 0);
   h->trunc32_buf = env_int("SPEC_VERIFY_TRUNC32_BUF", 1);
+  h->trunc32_list = env_int("SPEC_VERIFY_TRUNC32_LIST", 1);
   h->tiles_per_group = env_int("SPEC_VERIFY_TILES_PER_GROUP", 16);
   if (h->tiles_per_group < 1) h->tiles_per_group = 1;
   h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);

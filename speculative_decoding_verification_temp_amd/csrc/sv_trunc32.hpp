@@ -302,11 +302,12 @@ __device__ inline uint32_t t32_gather(const void* row, long long nchunks, uint32
   return n;
 }
 
-// One workgroup per (sequence, row): blockIdx.x = b (2K + 1) + r.
+// One workgroup per (sequence, row): blockIdx.x = b (2K + 1) + r. only_redo:
+// skip the rows the list pass below has settled (flags != kTruncRedo).
 template <int VEC>
 __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
-    double c64, int fx, int use_buf, Trunc tr, const int32_t* __restrict__ kdraft,
+    double c64, int fx, int use_buf, int only_redo, Trunc tr, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
   __shared__ uint32_t cnt[kT32Bins1];
   __shared__ u64 m1[kT32Bins1];
@@ -322,6 +323,8 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
     const int kb = kdraft[b];
     if (r <= K ? r > kb : r - K - 1 >= kb) return;
   }
+  // after the list pass: only the rows it handed over
+  if (only_redo && parts[blockIdx.x].flags != kTruncRedo) return;
   const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
   const long long nchunks = V / VEC;
   const double scale = __builtin_ldexp(1.0, fx);
@@ -488,6 +491,321 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   const uint32_t p3 = uint32_t(q3);
   const u64 S_p = a1 + a2 + a3 + m3[p3];
   put(__builtin_ldexp(double(S_p), -fx), R, (p1 << 20) | (p2 << 10) | p3);
+}
+
+// ---------------------------------------------------------------------------
+// List pass (16-byte chunks): one read of the row settles most rows. A
+// 256-thread workgroup keeps the row's top k + 1 token keys in the top-m
+// candidate lists of sv_topm.hpp while it forms, in the same read, the row's
+// maximum and checks for NaN and +inf. The merged list, sorted, gives the
+// k-th largest value and, when the next token's value differs from it, every
+// value top-k keeps; the top-k mass and the top-p level then follow from
+// fixed-point prefix masses as in the buffered route. A row with neither
+// rule gets its normaliser from the same read instead (value_term terms, the
+// ones p(d) and q(d) are formed with, over a running reference as in the
+// streaming pass). A row the list cannot settle (k + 1 > kT1MaxWant, a tie
+// across the top-k cut) is marked kTruncRedo for the pass above, and so is
+// every row with top-p alone: its kept set is not bounded in advance (several
+// hundred tokens at the c5 shape), so the multi-read pass takes it from the
+// start.
+// ---------------------------------------------------------------------------
+constexpr int kT1Block = 256;
+constexpr int kT1Waves = kT1Block / kWave;
+constexpr int kT1Cap = 448;                        // keys per wavefront list
+constexpr uint32_t kT1MaxWant = kT1Cap - kWave;    // 384
+constexpr int kT1Unroll = 4;                       // chunks per thread per group
+constexpr int kT1Merge = kT1Waves * kT1MaxWant;    // merged lists
+constexpr int kT1Per = (kT1MaxWant + kWave - 1) / kWave;   // list entries per lane (6)
+
+// inclusive prefix over the lanes of a wavefront (u64)
+__device__ inline u64 wave_incl_scan_u64(u64 v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const u64 u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
+    double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+  static_assert(VEC == 4, "the list pass reads 16-byte chunks");
+  __shared__ uint64_t s_keys[kT1Waves][kT1Cap];
+  __shared__ uint32_t s_bins[kT1Waves][256];
+  __shared__ u32x4 s_stage[kT1Waves][kTopmStage];
+  __shared__ uint32_t s_stage_at[kT1Waves][kTopmStage];
+  __shared__ uint64_t s_merge[kT1Merge];
+  __shared__ u64 s_P[kT1MaxWant];
+  __shared__ uint32_t s_count[kT1Waves], s_flag[kT1Waves];
+  __shared__ float s_R[kT1Waves], s_M[kT1Waves];
+  __shared__ double s_S[kT1Waves];
+  __shared__ unsigned long long s_thr;
+  __shared__ uint32_t s_n;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  const int rows = 2 * K + 1;
+  const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
+  if (kdraft != nullptr) {
+    const int kb = kdraft[b];
+    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  }
+  const int kk = tr.k != nullptr ? tr.k[b] : 0;
+  const bool kon = kk >= 1 && kk < V;
+  const float pp = tr.p != nullptr ? tr.p[b] : 1.0f;
+  const bool pon = pp < 1.0f;
+  auto put = [&](double S, float R, uint32_t thr, int flags) {
+    if (tid == 0) {
+      RowPart p;
+      p.S = S;
+      p.R = R;
+      p.m = 0.0f;
+      p.idx = int(thr);
+      p.flags = flags;
+      parts[blockIdx.x] = p;
+    }
+  };
+  if (!(pp > 0.0f)) return put(__builtin_nan(""), 0.0f, 0u, 0);
+  if ((kon && uint32_t(kk) + 1u > kT1MaxWant) || (pon && !kon))
+    return put(0.0, 0.0f, 0u, kTruncRedo);
+  const uint32_t want = kon ? uint32_t(kk) + 1u : 1u;
+  const bool complete = want >= uint32_t(V);         // the list holds every token
+  const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
+  if (tid == 0) s_thr = 0ull;
+  __syncthreads();
+  TopM<DT_F32> tm;
+  tm.init(s_keys[wid], s_bins[wid], &s_thr, kT1Cap, want, s_stage[wid], s_stage_at[wid]);
+
+  // ---- the one read: candidate lists, running-reference normaliser, checks ----
+  const long long nchunks = V / VEC;
+  constexpr long long kPerIt = (long long)kT1Block * kT1Unroll;
+  const long long nit = (nchunks + kPerIt - 1) / kPerIt;
+  const bool need_all = !kon;          // no truncation: the whole row's mass is needed
+  float Ra = kRefInit, gmax = -__builtin_inff();
+  double Sa = 0.0;
+  uint32_t nonfin = 0u;
+  auto load_group = [&](long long it, u32x4 (&raw)[kT1Unroll]) {
+#pragma unroll
+    for (int u = 0; u < kT1Unroll; ++u) {
+      const long long ci = (it * kT1Unroll + u) * kT1Block + tid;
+      raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) +
+                                          (ci < nchunks ? ci : nchunks - 1));
+    }
+  };
+  auto filter_group = [&](long long it, const u32x4 (&raw)[kT1Unroll]) {
+    const long long c0 = it * kT1Unroll * kT1Block + tid;
+    float cm[kT1Unroll];
+    uint32_t ok = 0;
+    float gm = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < kT1Unroll; ++u) {
+      const bool in = c0 + (long long)u * kT1Block < nchunks;
+      ok |= in ? 1u << u : 0u;
+      cm[u] = chunk_max<DT_F32>(raw[u]);
+      gm = in ? fmaxf(gm, cm[u]) : gm;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t m = raw[u][q] & 0x7fffffffu;
+        nonfin |= (in && (m > 0x7f800000u || raw[u][q] == 0x7f800000u)) ? 1u : 0u;
+      }
+    }
+    gmax = fmaxf(gmax, gm);
+    if (need_all) {
+      const float Rn = fmaxf(Ra, ceilf(gm * c));
+      Sa = rescale(Sa, Ra, Rn);
+      Ra = Rn;
+      double t = 0.0;
+#pragma unroll
+      for (int u = 0; u < kT1Unroll; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          t += ((ok >> u) & 1u) ? value_term(__uint_as_float(raw[u][q]), c64, Rn) : 0.0;
+      Sa += t;
+    }
+    if (it == 0) tm.template seed<kT1Unroll>(cm, ok);
+#pragma unroll
+    for (int u = 0; u < kT1Unroll; ++u)
+      tm.stage_chunk(((ok >> u) & 1u) != 0u && cm[u] >= tm.thr_f, raw[u],
+                     uint32_t(c0 + (long long)u * kT1Block));
+  };
+  {
+    u32x4 ga[kT1Unroll], gb[kT1Unroll];
+    load_group(0, ga);
+#pragma unroll 1
+    for (long long it = 0; it < nit; it += 2) {
+      load_group(it + 1, gb);
+      filter_group(it, ga);
+      load_group(it + 2, ga);
+      if (it + 1 < nit) filter_group(it + 1, gb);
+    }
+  }
+  tm.flush();
+  tm.compact();                                 // at most want keys per wavefront
+  // the normaliser over the workgroup, in a fixed order
+  {
+    const float Rw = wave_max(Ra);
+    const double Sw = wave_sum(rescale(Sa, Ra, Rw));
+    const uint32_t fw = wave_or(nonfin);
+    const float Mw = wave_max(gmax);
+    if (lane == 0) {
+      s_M[wid] = Mw;
+      s_R[wid] = Rw;
+      s_S[wid] = Sw;
+      s_flag[wid] = fw;
+      s_count[wid] = tm.fill;
+    }
+  }
+  __syncthreads();
+  float M = s_M[0];
+  uint32_t bad = s_flag[0];
+#pragma unroll
+  for (int w = 1; w < kT1Waves; ++w) {
+    M = fmaxf(M, s_M[w]);
+    bad |= s_flag[w];
+  }
+  if (bad != 0u || !(M > -__builtin_inff())) return put(__builtin_nan(""), 0.0f, 0u, 0);
+  const float R = ceilf(M * c);                  // the largest running reference, too
+  double S_all = 0.0;
+  if (need_all)
+#pragma unroll
+    for (int w = 0; w < kT1Waves; ++w) S_all += rescale(s_S[w], s_R[w], R);
+
+  // ---- merge the lists, keep the want largest keys, sort them ----
+  if (wid == 0) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int w = 0; w < kT1Waves; ++w) {
+      const uint32_t cw = s_count[w];
+      for (uint32_t e = uint32_t(lane); e < cw; e += kWave) s_merge[n + e] = s_keys[w][e];
+      n += cw;
+    }
+    wave_sync();
+    TopM<DT_F32> mg;
+    mg.init(s_merge, s_bins[0], &s_thr, kT1Merge, want);
+    mg.fill = n;
+    mg.compact();
+    if (lane == 0) s_n = mg.fill;
+  }
+  __syncthreads();
+  const int n = int(s_n);
+  {
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int i = n + tid; i < n2; i += kT1Block) s_merge[i] = 0ull;
+    __syncthreads();
+    for (int k2 = 2; k2 <= n2; k2 <<= 1) {
+      for (int j = k2 >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kT1Block) {
+          const int l = i ^ j;
+          if (l > i) {
+            const uint64_t a = s_merge[i], bb = s_merge[l];
+            if ((i & k2) == 0 ? a < bb : a > bb) {
+              s_merge[i] = bb;
+              s_merge[l] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (n < int(want) || n < 1) return put(0.0, 0.0f, 0u, kTruncRedo);   // (not expected)
+  if (wid != 0) return;
+
+  // ---- wavefront 0: the cut, the masses, the top-p level ----
+  auto key32 = [&](int i) -> uint32_t { return uint32_t(s_merge[i] >> 32); };
+  if (!kon && !pon) {                            // no truncation: the whole row
+    if (lane == 0) {
+      RowPart p;
+      p.S = S_all;
+      p.R = R;
+      p.m = 0.0f;
+      p.idx = 0;
+      p.flags = 0;
+      parts[blockIdx.x] = p;
+    }
+    return;
+  }
+  const double scale = __builtin_ldexp(1.0, fx);
+  uint32_t tk = 0u;
+  int n_k = n;                                   // list entries in the top-k set
+  if (kon) {
+    tk = key32(kk - 1);
+    if (!complete && key32(kk) == tk) {          // the tie may go on past the list
+      if (lane == 0) {
+        RowPart p;
+        p.S = 0.0;
+        p.R = 0.0f;
+        p.m = 0.0f;
+        p.idx = 0;
+        p.flags = kTruncRedo;
+        parts[blockIdx.x] = p;
+      }
+      return;
+    }
+    n_k = kk;
+    if (complete)
+      while (n_k < n && key32(n_k) == tk) ++n_k;
+  }
+  // prefix masses over the list's first n_k entries: lane l holds kT1Per of them
+  const int base = lane * kT1Per;
+  u64 loc[kT1Per], own = 0;
+#pragma unroll
+  for (int e = 0; e < kT1Per; ++e) {
+    const int i = base + e;
+    if (i < n_k) own += fixed_term(order_floor<DT_F32>(key32(i)), c64, R, scale);
+    loc[e] = own;
+  }
+  const u64 incl = wave_incl_scan_u64(own, lane);
+  const u64 before = incl - own;
+  const u64 total = __shfl(incl, kWave - 1, kWave);
+#pragma unroll
+  for (int e = 0; e < kT1Per; ++e)
+    if (base + e < n_k) s_P[base + e] = before + loc[e];
+  wave_sync();
+  if (!pon) {
+    if (lane == 0) {
+      RowPart p;
+      p.S = __builtin_ldexp(double(total), -fx);
+      p.R = R;
+      p.m = 0.0f;
+      p.idx = int(tk);
+      p.flags = 0;
+      parts[blockIdx.x] = p;
+    }
+    return;
+  }
+  // top-p inside the top-k set (rows with top-p alone took the pass above)
+  u64 goal = u64(__builtin_ceil(double(pp) * double(total)));
+  goal = min(max(goal, 1ull), total);
+  int first = -1;
+#pragma unroll
+  for (int e = kT1Per - 1; e >= 0; --e)
+    if (base + e < n_k && s_P[base + e] >= goal) first = base + e;
+  const unsigned long long hit = __ballot(first >= 0);
+  const int i0 = hit ? __shfl(first, __ffsll((long long)hit) - 1, kWave) : -1;
+  int flags = 0;
+  uint32_t thr = 0u;
+  u64 S_p = 0;
+  if (i0 < 0) {
+    flags = kTruncRedo;                          // (not expected: P[n_k - 1] = total)
+  } else {
+    thr = key32(i0);
+    int end = i0;                                // last entry of the level
+    while (end + 1 < n_k && key32(end + 1) == thr) ++end;
+    S_p = s_P[end];
+  }
+  if (lane == 0) {
+    RowPart p;
+    p.S = flags ? 0.0 : __builtin_ldexp(double(S_p), -fx);
+    p.R = R;
+    p.m = 0.0f;
+    p.idx = int(thr);
+    p.flags = flags;
+    parts[blockIdx.x] = p;
+  }
 }
 
 }  // namespace sv

@@ -1,12 +1,13 @@
 """GPU parity of top-k / top-p truncation over fp32 rows against the oracle.
 
-fp32 rows go through their own truncation pass (the k-th largest order key
-and the top-p level found digit by digit, 12 + 10 + 10 bits, with fixed-point
-masses, or from the few candidate values sorted in LDS) and then the
-per-sequence finish, whose draw compares each value's order key with its
-row's threshold. The main cases run on both routes of the pass (the `route`
-fixture; SPEC_VERIFY_TRUNC32_BUF=0 keeps to the digit reads), and rows whose
-candidates do not fit the buffer fall back by themselves. The tests cover:
+fp32 rows go through their own truncation passes (the row's top-k list from
+one read; else the k-th largest order key and the top-p level found digit by
+digit, 12 + 10 + 10 bits, with fixed-point masses, or from the few candidate
+values sorted in LDS) and then the per-sequence finish, whose draw compares
+each value's order key with its row's threshold. The main cases run on each
+route (the `route` fixture; SPEC_VERIFY_TRUNC32_LIST=0 skips the list pass,
+SPEC_VERIFY_TRUNC32_BUF=0 keeps to the digit reads), and rows a route cannot
+settle fall back by themselves. The tests cover:
 per-sequence mixes of settings (off, on, invalid), each rule alone, drafts
 from the untruncated draft (q(d) = 0 accepted), values that share their
 upper key digits, ties, -inf, zeros of both signs, huge magnitudes, rows with
@@ -31,10 +32,13 @@ DEV = torch.device("cuda", 0)
 SMALL = CONFIGS["c5"].scaled(B=48, V=20000)
 
 
-@pytest.fixture(params=["buffered", "digits"])
+@pytest.fixture(params=["list", "buffered", "digits"])
 def route(request, monkeypatch):
-    """The truncation pass's route, read when a verifier is created."""
-    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_BUF", "1" if request.param == "buffered" else "0")
+    """The truncation passes' route, read when a verifier is created: the
+    one-read list pass first (rows it cannot settle then take the buffered
+    route), the buffered route alone, or the digit reads alone."""
+    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_LIST", "1" if request.param == "list" else "0")
+    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_BUF", "0" if request.param == "digits" else "1")
     return request.param
 
 
