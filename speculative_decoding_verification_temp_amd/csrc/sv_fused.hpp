@@ -262,6 +262,21 @@ __device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, ui
                                           double& Ed, double& A, double& Bd) {
   E = Ed = A = Bd = 0.0;
   if constexpr (DT == DT_F32) {      // 4 fp32 values per chunk, terms from exp2_tab
+    if constexpr (MASK) {
+      // a unit in which no lane holds a kept value adds nothing: skip its
+      // terms (most units, when the truncation keeps few values)
+      bool kept = false;
+#pragma unroll
+      for (int k = 0; k < kUnitChunks; ++k) {
+        if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          kept |= order_key<DT_F32>(u.a[k][q]) >= thr_t;
+          if constexpr (RESID) kept |= order_key<DT_F32>(u.d[k][q]) >= thr_d;
+        }
+      }
+      if (!__any(kept)) return;
+    }
 #pragma unroll
     for (int k = 0; k < kUnitChunks; ++k) {
       if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
