@@ -22,12 +22,15 @@
 // exact threshold key. All reads use cached loads: a row read again is
 // usually still in the last-level cache.
 //
-// Most rows need fewer reads: when the values from the first digit's cut bin
-// upwards number at most kT32Buf (top-k: every value the truncation can keep;
-// top-p alone: the values of the bin where the mass crosses), the second read
-// copies their keys into LDS instead, a bitonic sort orders them, and the
-// k-th largest key, the prefix masses and the top-p level come from the
-// sorted keys: two reads of the row with top-k, three with top-p alone.
+// Most rows need fewer reads: when the values that can matter number at most
+// kT32Buf, one more read copies their keys into LDS and the same digit walks
+// run over the copy instead of the row. With top-k they are the values from
+// the first digit's cut bin upwards (two reads in all). With top-p alone,
+// read A also counts the values by first digit and estimates the row's
+// normaliser; a bound on each bin's mass then places the crossing, and the
+// values from a bin at or below it upwards are copied (two reads), or, when
+// they do not fit, the mass read finds the crossing bin and its values are
+// copied (three reads).
 //
 // Masses are softmax terms 2^(x c - R), each rounded once to unsigned 64-bit
 // fixed point with FX = 61 - ceil(log2 V) fraction bits (a term is at most
@@ -138,6 +141,25 @@ __device__ inline void t32_read(const void* row, long long nchunks, const T32Sel
   });
 }
 
+// The same gathering over n keys held in LDS (each passed on as the bits of
+// its value; -0 comes back as +0, which has the same key).
+__device__ inline void t32_read_buf(const uint32_t* buf, int n, const T32Sel& s, double c64,
+                                    float R, double scale, u64* m1, u64* m2, u64* m3) {
+  for (int i = threadIdx.x; i < n; i += kT32Block) {
+    const uint32_t key = buf[i];
+    const bool in1 = s.m1 && key >= s.m1_floor;
+    const bool in2 = s.m2 && (key >> 20) == s.m2_bin && key >= s.m2_floor;
+    const bool in3 = s.m3 && (key >> 10) == s.m3_sel && key >= s.m3_floor;
+    if (in1 || in2 || in3) {
+      const u64 t = fixed_term(order_floor<DT_F32>(key), c64, R, scale);
+      if (in1) atomicAdd(&m1[key >> 20], t);
+      if (in2) atomicAdd(&m2[(key >> 10) & uint32_t(kT32Bins - 1)], t);
+      if (in3) atomicAdd(&m3[key & uint32_t(kT32Bins - 1)], t);
+    }
+  }
+  __syncthreads();
+}
+
 __device__ inline uint32_t t32_max(uint32_t v, uint32_t* s) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
 #pragma unroll
@@ -155,8 +177,10 @@ __device__ inline uint32_t t32_max(uint32_t v, uint32_t* s) {
 struct T32Walk {
   u64 red[kT32Waves];
   uint32_t red32[kT32Waves];
+  double redd[kT32Waves];
   int ired[kT32Waves];
   u64 above;
+  double above_d;
   int bin;
 };
 
@@ -164,7 +188,7 @@ struct T32Walk {
 // bin b whose inclusive sum from the top, over bins >= b, is >= goal. Returns
 // b, or -1 when the total stays below goal, and in `above` the sum over the
 // bins above b (the total when -1). Thread t holds bins NB/512 * t onwards.
-// T: uint32_t (counts) or u64 (fixed-point masses).
+// T: uint32_t (counts), u64 (fixed-point masses) or double (mass bounds).
 template <typename T, int NB>
 __device__ inline int t32_walk(const T* v, T goal, T& above, T32Walk& w) {
   constexpr int BPT = NB / kT32Block;
@@ -174,7 +198,9 @@ __device__ inline int t32_walk(const T* v, T goal, T& above, T32Walk& w) {
   for (int i = 0; i < BPT; ++i) own += v[tid * BPT + i];
   T total;
   T abv;
-  if constexpr (sizeof(T) == 8)
+  if constexpr (__is_same(T, double))
+    abv = tr_above<T, kT32Waves>(own, w.redd, total);
+  else if constexpr (sizeof(T) == 8)
     abv = tr_above<T, kT32Waves>(own, w.red, total);
   else
     abv = tr_above<T, kT32Waves>(own, w.red32, total);
@@ -185,7 +211,10 @@ __device__ inline int t32_walk(const T* v, T goal, T& above, T32Walk& w) {
       const T x = v[tid * BPT + i];
       if (acc + x >= goal) {
         w.bin = tid * BPT + i;
-        w.above = u64(acc);
+        if constexpr (__is_same(T, double))
+          w.above_d = acc;
+        else
+          w.above = u64(acc);
         break;
       }
       acc += x;
@@ -193,7 +222,10 @@ __device__ inline int t32_walk(const T* v, T goal, T& above, T32Walk& w) {
   }
   __syncthreads();
   const int bin = cut >= 0 ? w.bin : -1;
-  above = cut >= 0 ? T(w.above) : total;
+  if constexpr (__is_same(T, double))
+    above = cut >= 0 ? w.above_d : total;
+  else
+    above = cut >= 0 ? T(w.above) : total;
   __syncthreads();
   return bin;
 }
@@ -212,74 +244,90 @@ __device__ inline void t32_clear(T_* a) {
   for (int i = threadIdx.x; i < NB; i += kT32Block) a[i] = T_(0);
 }
 
-// ---- the buffered route: up to kT32Buf keys in LDS ----
-// Thread t holds entries (kT32Block - 1 - t) E .. + E - 1, so that the
-// threads above t (tr_above) hold the entries before its own.
-constexpr int kT32E = kT32Buf / kT32Block;
+// ---- the buffered routes: up to kT32Buf keys in LDS ----
 
-// Sort buf[0..n) descending: bitonic over the next power of two, padded
-// with key 0 (below the key of every value of a valid row).
-__device__ inline void t32_sort_desc(uint32_t* buf, int n) {
+// The k-th largest of n keys in LDS (1 <= k <= n), digit by digit with
+// counts in the mass arrays; ok = false if a walk finds no cut (not expected).
+__device__ inline uint32_t t32_buf_kth(const uint32_t* buf, int n, uint32_t k, u64* m1, u64* m2,
+                                       u64* m3, T32Walk& w, bool& ok) {
   const int tid = threadIdx.x;
-  int n2 = 1;
-  while (n2 < n) n2 <<= 1;
-  for (int i = n + tid; i < n2; i += kT32Block) buf[i] = 0u;
+  t32_clear<u64, kT32Bins1>(m1);
+  t32_clear<u64, kT32Bins>(m2);
+  t32_clear<u64, kT32Bins>(m3);
   __syncthreads();
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += kT32Block) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint32_t a = buf[i], b = buf[l];
-          if ((i & k) == 0 ? a < b : a > b) {
-            buf[i] = b;
-            buf[l] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// P[i] = the fixed-point mass of the sorted keys buf[0..i] that are >= floor;
-// returns the total.
-__device__ inline u64 t32_prefix(const uint32_t* buf, int n, uint32_t floor, double c64, float R,
-                                 double scale, u64* P, T32Walk& w) {
-  const int base = (kT32Block - 1 - int(threadIdx.x)) * kT32E;
-  u64 loc[kT32E], own = 0;
-#pragma unroll
-  for (int e = 0; e < kT32E; ++e) {
-    const int i = base + e;
-    const uint32_t key = i < n ? buf[i] : 0u;
-    if (i < n && key >= floor) own += fixed_term(order_floor<DT_F32>(key), c64, R, scale);
-    loc[e] = own;
-  }
-  u64 total;
-  const u64 before = tr_above<u64, kT32Waves>(own, w.red, total);
-#pragma unroll
-  for (int e = 0; e < kT32E; ++e)
-    if (base + e < n) P[base + e] = before + loc[e];
+  for (int i = tid; i < n; i += kT32Block) atomicAdd(&m1[buf[i] >> 20], 1ull);
   __syncthreads();
-  return total;
+  u64 rem = k, abv;
+  const int q1 = t32_walk<u64, kT32Bins1>(m1, rem, abv, w);
+  ok = q1 >= 0;
+  if (!ok) return 0u;
+  rem -= abv;
+  for (int i = tid; i < n; i += kT32Block) {
+    const uint32_t key = buf[i];
+    if ((key >> 20) == uint32_t(q1)) atomicAdd(&m2[(key >> 10) & uint32_t(kT32Bins - 1)], 1ull);
+  }
+  __syncthreads();
+  const int q2 = t32_walk<u64, kT32Bins>(m2, rem, abv, w);
+  ok = q2 >= 0;
+  if (!ok) return 0u;
+  rem -= abv;
+  const uint32_t sel = (uint32_t(q1) << 10) | uint32_t(q2);
+  for (int i = tid; i < n; i += kT32Block) {
+    const uint32_t key = buf[i];
+    if ((key >> 10) == sel) atomicAdd(&m3[key & uint32_t(kT32Bins - 1)], 1ull);
+  }
+  __syncthreads();
+  const int q3 = t32_walk<u64, kT32Bins>(m3, rem, abv, w);
+  ok = q3 >= 0;
+  return (sel << 10) | uint32_t(q3 >= 0 ? q3 : 0);
 }
 
-// the smallest i < n with P[i] >= goal (P non-decreasing), -1 if none
-__device__ inline int t32_first_reach(const u64* P, int n, u64 goal, T32Walk& w) {
-  const int base = (kT32Block - 1 - int(threadIdx.x)) * kT32E;
-  int first = -1;
-#pragma unroll
-  for (int e = kT32E - 1; e >= 0; --e)
-    if (base + e < n && P[base + e] >= goal) first = base + e;
-  const int best = tr_max<kT32Waves>(first >= 0 ? kT32Buf - first : -1, w.ired);
-  return best >= 0 ? kT32Buf - best : -1;
+// The fixed-point mass of the keys >= floor among n keys in LDS.
+__device__ inline u64 t32_buf_mass(const uint32_t* buf, int n, uint32_t floor, double c64, float R,
+                                   double scale, T32Walk& w) {
+  u64 own = 0;
+  for (int i = threadIdx.x; i < n; i += kT32Block) {
+    const uint32_t key = buf[i];
+    if (key >= floor) own += fixed_term(order_floor<DT_F32>(key), c64, R, scale);
+  }
+  return tr_sum<u64, kT32Waves>(own, w.red);
 }
 
-// the number of keys >= key among buf[0..n)
-__device__ inline uint32_t t32_count_ge(const uint32_t* buf, int n, uint32_t key, T32Walk& w) {
-  uint32_t c = 0;
-  for (int i = threadIdx.x; i < n; i += kT32Block) c += buf[i] >= key ? 1u : 0u;
-  return tr_sum<uint32_t, kT32Waves>(c, w.red32);
+// The top-p level among n keys in LDS that form a top part of the row (or
+// the part of it below a mass already counted): the three digit walks over
+// the masses of the keys >= floor. Returns false when their mass stays below
+// goal; else thr = the level's key and mass = the mass at or above it.
+__device__ inline bool t32_buf_level(const uint32_t* buf, int n, uint32_t floor, u64 goal,
+                                     double c64, float R, double scale, u64* m1, u64* m2,
+                                     u64* m3, T32Walk& w, uint32_t& thr, u64& mass) {
+  t32_clear<u64, kT32Bins1>(m1);
+  t32_clear<u64, kT32Bins>(m2);
+  t32_clear<u64, kT32Bins>(m3);
+  __syncthreads();
+  T32Sel sb = t32_none();
+  sb.m1 = true;
+  sb.m1_floor = floor;
+  t32_read_buf(buf, n, sb, c64, R, scale, m1, m2, m3);
+  u64 a1, a2, a3;
+  const int q1 = t32_walk<u64, kT32Bins1>(m1, goal, a1, w);
+  if (q1 < 0) return false;
+  sb = t32_none();
+  sb.m2 = true;
+  sb.m2_bin = uint32_t(q1);
+  sb.m2_floor = floor;
+  t32_read_buf(buf, n, sb, c64, R, scale, m1, m2, m3);
+  const int q2 = t32_walk<u64, kT32Bins>(m2, goal - a1, a2, w);
+  if (q2 < 0) return false;
+  sb = t32_none();
+  sb.m3 = true;
+  sb.m3_sel = (uint32_t(q1) << 10) | uint32_t(q2);
+  sb.m3_floor = floor;
+  t32_read_buf(buf, n, sb, c64, R, scale, m1, m2, m3);
+  const int q3 = t32_walk<u64, kT32Bins>(m3, goal - a1 - a2, a3, w);
+  if (q3 < 0) return false;
+  thr = (uint32_t(q1) << 20) | (uint32_t(q2) << 10) | uint32_t(q3);
+  mass = a1 + a2 + a3 + m3[q3];
+  return true;
 }
 
 // Copy the keys of the row with (key >> 20) in [lo, hi] into buf; returns
@@ -314,8 +362,10 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   __shared__ u64 m2[kT32Bins], m3[kT32Bins];
   __shared__ uint32_t s_u[kT32Waves];
   __shared__ uint32_t s_n;
+  __shared__ float s_rf[kT32Waves];
+  __shared__ double s_sd[kT32Waves];
   __shared__ T32Walk w;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
   const int rows = 2 * K + 1;
   const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
@@ -352,17 +402,89 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   __syncthreads();
   uint32_t top = 0u, nonfin = 0u;
   const bool count1 = kon || (pon && use_buf);
+  // top-p alone: the row's normaliser too, from float terms whose exponent
+  // x c - R carries c as two floats (about 1e-7 relative), over a running
+  // reference in registers; it places the top-p goal for the route below
+  const bool est = pon && !kon && use_buf;
+  const float c_lo = float(c64 - double(c));
+  float Ra = kRefInit;
+  double Sa = 0.0;
   t32_stream<VEC>(row, nchunks, [&](uint32_t bits) {
     const uint32_t key = order_key<DT_F32>(bits);
     const bool fin = key > kKey32NegInf && key < kKey32PosInf;
     top = max(top, fin ? key : 0u);
     nonfin |= (key < kKey32NegInf || key >= kKey32PosInf) ? 1u : 0u;
     if (count1) atomicAdd(&cnt[key >> 20], 1u);
+    if (est && fin) {                // (-inf adds 0; its product with c_lo may be NaN)
+      const float x = __uint_as_float(bits);
+      const float xc = x * c;
+      if (xc > Ra) {                 // a new reference (rare after the first values)
+        const float Rn = ceilf(xc);
+        Sa = rescale(Sa, Ra, Rn);
+        Ra = Rn;
+      }
+      Sa += double(__builtin_amdgcn_exp2f(__builtin_fmaf(x, c_lo, __builtin_fmaf(x, c, -Ra))));
+    }
   });
   top = t32_max(top, s_u);
   const bool bad = t32_max(nonfin, s_u) != 0u || top == 0u || !(pp > 0.0f);
   if (bad) return put(__builtin_nan(""), 0.0f, 0u);
   const float R = ceilf(order_floor<DT_F32>(top) * c);
+
+  // ---- top-p alone: the candidates from the counts and a mass bound ----
+  // Bin b of the first digit holds cnt[b] values of at most its largest
+  // value v_b, so cnt[b] term(v_b) bounds its mass from above, and the
+  // crossing lies at or below the highest bin whose bound from the top
+  // reaches the goal. The values of that bin and of as many bins below it as
+  // fit in LDS are copied by one more read (a top part of the row), and the
+  // three digit walks run over them in LDS with exact masses; when their mass
+  // reaches the goal the row is settled, else it takes the mass reads below.
+  bool counts_ok = true;             // cnt holds the first-digit counts
+  if (est) {
+    const float Rw = wave_max(Ra);
+    const double Sw = wave_sum(rescale(Sa, Ra, Rw));
+    if (lane == 0) {
+      s_rf[wid] = Rw;
+      s_sd[wid] = Sw;
+    }
+    __syncthreads();
+    double S_all = 0.0;
+#pragma unroll
+    for (int q = 0; q < kT32Waves; ++q) S_all += rescale(s_sd[q], s_rf[q], R);
+    const u64 goal = max(u64(__builtin_ceil(double(pp) * S_all * scale)), 1ull);
+    double* ubd = reinterpret_cast<double*>(m1);       // the bounds, in m1's space
+    for (int i = tid; i < kT32Bins1; i += kT32Block) {
+      const uint32_t n_i = cnt[i];
+      double ub = 0.0;
+      if (n_i != 0u) {
+        const double t = value_term(order_floor<DT_F32>((uint32_t(i) << 20) | 0xfffffu), c64, R);
+        ub = double(n_i) * (t * (1.0 + 1e-6) * scale + 1.0);
+      }
+      ubd[i] = ub;
+    }
+    __syncthreads();
+    double abd;
+    const int bu = t32_walk<double, kT32Bins1>(ubd, double(goal), abd, w);   // crossing <= bu
+    uint32_t ca;
+    const int bf = t32_walk<uint32_t, kT32Bins1>(cnt, uint32_t(kT32Buf) + 1u, ca, w);
+    const int bl = bf + 1;           // bins bl.. hold at most kT32Buf values
+    if (bu >= 0 && bl <= bu) {
+      uint32_t own = 0u;
+      for (int i = tid; i < kT32Bins1; i += kT32Block) own += i >= bl ? cnt[i] : 0u;
+      const uint32_t n_hi = tr_sum<uint32_t, kT32Waves>(own, w.red32);
+      const uint32_t n =
+          t32_gather<VEC>(row, nchunks, uint32_t(bl), uint32_t(kT32Bins1 - 1), cnt, &s_n);
+      counts_ok = false;
+      uint32_t thr;
+      u64 mass;
+      if (n == n_hi &&
+          t32_buf_level(cnt, int(n), 0u, goal, c64, R, scale, m1, m2, m3, w, thr, mass))
+        return put(__builtin_ldexp(double(mass), -fx), R, thr);
+    }
+    // not settled: the mass reads below (m1 is cleared for them)
+    t32_clear<u64, kT32Bins1>(m1);
+    __syncthreads();
+  }
 
   // ---- top-k: the k-th largest key, digit by digit ----
   uint32_t tk = 0u, b1 = 0u, b2 = 0u;
@@ -377,17 +499,18 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
       __syncthreads();                 // cnt[b1] read before cnt holds keys
       const uint32_t n = t32_gather<VEC>(row, nchunks, b1, uint32_t(kT32Bins1 - 1), cnt, &s_n);
       if (n != n_hi) return put(__builtin_nan(""), 0.0f, 0u);
-      t32_sort_desc(cnt, int(n));
-      tk = cnt[kk - 1];
-      const u64 Sb = t32_prefix(cnt, int(n), tk, c64, R, scale, m1, w);
+      bool ok;
+      tk = t32_buf_kth(cnt, int(n), uint32_t(kk), m1, m2, m3, w, ok);
+      if (!ok) return put(__builtin_nan(""), 0.0f, 0u);
+      const u64 Sb = t32_buf_mass(cnt, int(n), tk, c64, R, scale, w);
       if (!pon) return put(__builtin_ldexp(double(Sb), -fx), R, tk);
       u64 goal = u64(__builtin_ceil(double(pp) * double(Sb)));
       goal = min(max(goal, 1ull), Sb);
-      const int i = t32_first_reach(m1, int(n), goal, w);
-      if (i < 0) return put(__builtin_nan(""), 0.0f, 0u);
-      const uint32_t thr = cnt[i];
-      const uint32_t n_thr = t32_count_ge(cnt, int(n), thr, w);
-      return put(__builtin_ldexp(double(m1[n_thr - 1]), -fx), R, thr);
+      uint32_t thr;
+      u64 mass;
+      if (!t32_buf_level(cnt, int(n), tk, goal, c64, R, scale, m1, m2, m3, w, thr, mass))
+        return put(__builtin_nan(""), 0.0f, 0u);
+      return put(__builtin_ldexp(double(mass), -fx), R, thr);
     }
     rem -= abv;
     t32_clear<uint32_t, kT32Bins>(cnt);
@@ -449,19 +572,17 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   if (q1 < 0) return put(__builtin_nan(""), 0.0f, 0u);
   const uint32_t p1 = uint32_t(q1);
   goal -= a1;
-  if (!kon && use_buf && cnt[p1] <= uint32_t(kT32Buf)) {
+  if (!kon && use_buf && counts_ok && cnt[p1] <= uint32_t(kT32Buf)) {
     // ---- buffered: the crossing bin's values, sorted in LDS ----
     const uint32_t n_p = cnt[p1];
     __syncthreads();                   // cnt[p1] read before cnt holds keys
     const uint32_t n = t32_gather<VEC>(row, nchunks, p1, p1, cnt, &s_n);
     if (n != n_p) return put(__builtin_nan(""), 0.0f, 0u);
-    t32_sort_desc(cnt, int(n));
-    t32_prefix(cnt, int(n), 0u, c64, R, scale, m1, w);
-    const int i = t32_first_reach(m1, int(n), goal, w);
-    if (i < 0) return put(__builtin_nan(""), 0.0f, 0u);
-    const uint32_t thr = cnt[i];
-    const uint32_t n_thr = t32_count_ge(cnt, int(n), thr, w);
-    return put(__builtin_ldexp(double(a1 + m1[n_thr - 1]), -fx), R, thr);
+    uint32_t thr;
+    u64 mass;
+    if (!t32_buf_level(cnt, int(n), 0u, goal, c64, R, scale, m1, m2, m3, w, thr, mass))
+      return put(__builtin_nan(""), 0.0f, 0u);
+    return put(__builtin_ldexp(double(a1 + mass), -fx), R, thr);
   }
   const bool same1 = kon && p1 == b1;      // m2 already holds p1's kept masses
   if (!same1) {
