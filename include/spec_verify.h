@@ -205,10 +205,11 @@ int spec_verify_set_stops(spec_verify_handle *h, int eos_token, const int32_t *d
  * supported, with V up to 524288 (bf16) or 262144 (float32) when V is a
  * multiple of 8 (bf16) or 4 (float32) and the logit tensors are 16-byte
  * aligned, else 65536 (larger V: spec_verify returns SV_EUNSUPPORTED). A
- * float32 call reads each needed row two to six times (the k-th largest
- * value and the top-p level are narrowed 12, 10 and 10 bits of the value's
- * order key at a time); its normalisers carry a relative error below 1e-8
- * beyond the terms' own. The arrays are read by
+ * float32 call reads a needed row once when its top k + 1 values (k <= 383)
+ * settle it, else two to six times (the k-th largest value and the top-p
+ * level are narrowed 12, 10 and 10 bits of the value's order key at a time);
+ * its normalisers carry a relative error below 1e-8 beyond the terms' own.
+ * The arrays are read by
  * the device during later calls and stay owned by the caller; they must
  * outlive those calls. spec_verify_set_truncation(h, NULL, NULL) turns
  * truncation off. Returns SV_EINVAL for a NULL handle or a misaligned array.
