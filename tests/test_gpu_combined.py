@@ -1,6 +1,7 @@
 """GPU parity with every optional extension on at once.
 
-One c2-shaped batch (bf16) with per-sequence top-k / top-p truncation (drafts
+One c2-shaped batch (bf16), and one c5-shaped batch (fp32, B = 48,
+V = 20000), with per-sequence top-k / top-p truncation (drafts
 sampled from each sequence's truncated draft law), stopping rules (an EOS id,
 per-sequence draft counts and emission budgets), the tree-shape policy
 epilogue on a seeded EMA, and the draft residual side output, over three
@@ -48,15 +49,16 @@ def _drafts_from_truncated(x, T, tk, tp, seed):
     x["tokens"] = torch.as_tensor(toks, device=DEV).contiguous()
 
 
-def test_all_extensions_three_calls(sv):
-    cfg = CONFIGS["c2"].scaled(B=48)
+@pytest.mark.parametrize("case", ["c2 bf16", "c5 fp32"])
+def test_all_extensions_three_calls(sv, case):
+    cfg = CONFIGS["c2"].scaled(B=48) if case == "c2 bf16" else CONFIGS["c5"].scaled(B=48, V=20000)
     rng = np.random.default_rng(40)
     tk = rng.choice([0, 1, 20, 50, 1000, cfg.V], cfg.B).astype(np.int32)
     tp = rng.choice([1.0, 0.8, 0.9, 0.95], cfg.B).astype(np.float32)
     kb = rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32)
     mx = rng.integers(1, cfg.K + 3, cfg.B).astype(np.int32)
 
-    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.bfloat16, ema_decay=DECAY)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, cfg.torch_dtype, ema_decay=DECAY)
     aux = v.enable_aux()
     v.set_truncation(torch.as_tensor(tk, device=DEV), torch.as_tensor(tp, device=DEV))
     conf_d = torch.zeros(cfg.B, dtype=torch.float32, device=DEV)
@@ -91,7 +93,7 @@ def test_all_extensions_three_calls(sv):
         sub = O.BatchResult(**{f: getattr(ref, f)[rows] if isinstance(getattr(ref, f), np.ndarray)
                                and getattr(ref, f).shape[:1] == (cfg.B,) else getattr(ref, f)
                                for f in ref.__dataclass_fields__})
-        rep = compare(rows, sub, tok, alen, "stochastic", aux, f"combined/step{step}")
+        rep = compare(rows, sub, tok, alen, "stochastic", aux, f"combined/{case}/step{step}")
         strict = ref.min_dist >= 1e-6
         g_len = alen.cpu().numpy()
         # excused sequences leave the tracked set (their EMA and streak may differ now)
@@ -115,4 +117,4 @@ def test_all_extensions_three_calls(sv):
         both = np.isnan(g_res) & np.isnan(r_res)
         same_inf = np.isinf(r_res) & (g_res == r_res)
         assert np.all(both | same_inf | (np.abs(g_res - r_res) <= 1e-9))
-        print(f"combined/step{step}: {rep}, tracked {int(tracked.sum())}", flush=True)
+        print(f"combined/{case}/step{step}: {rep}, tracked {int(tracked.sum())}", flush=True)
