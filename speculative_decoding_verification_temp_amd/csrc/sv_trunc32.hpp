@@ -621,21 +621,18 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
 // maximum and checks for NaN and +inf. The merged list, sorted, gives the
 // k-th largest value and, when the next token's value differs from it, every
 // value top-k keeps; the top-k mass and the top-p level then follow from
-// fixed-point prefix masses as in the buffered route. A row with neither
-// rule gets its normaliser from the same read instead (value_term terms, the
-// ones p(d) and q(d) are formed with, over a running reference as in the
-// streaming pass). A row the list cannot settle (k + 1 > kT1MaxWant, a tie
-// across the top-k cut) is marked kTruncRedo for the pass above, and so is
-// every row with top-p alone: its kept set is not bounded in advance (several
-// hundred tokens at the c5 shape), so the multi-read pass takes it from the
-// start.
+// fixed-point prefix masses. A row the list cannot settle (k + 1 >
+// kT1MaxWant, a tie across the top-k cut) is marked kTruncRedo for the pass
+// above, and so is every row without top-k: with top-p alone the kept set is
+// not bounded in advance (a thousand tokens and more at the c5 shape), and a
+// row with neither rule needs its whole mass. Keeping the pass to top-k rows
+// keeps it at 4 workgroups per compute unit (registers and LDS).
 // ---------------------------------------------------------------------------
 constexpr int kT1Block = 256;
 constexpr int kT1Waves = kT1Block / kWave;
 constexpr int kT1Cap = 448;                        // keys per wavefront list
 constexpr uint32_t kT1MaxWant = kT1Cap - kWave;    // 384
 constexpr int kT1Unroll = 4;                       // chunks per thread per group
-constexpr int kT1Merge = kT1Waves * kT1MaxWant;    // merged lists
 constexpr int kT1Per = (kT1MaxWant + kWave - 1) / kWave;   // list entries per lane (6)
 
 // inclusive prefix over the lanes of a wavefront (u64)
@@ -654,15 +651,13 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
     double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
   static_assert(VEC == 4, "the list pass reads 16-byte chunks");
-  __shared__ uint64_t s_keys[kT1Waves][kT1Cap];
+  __shared__ uint64_t s_keys[kT1Waves * kT1Cap];    // the lists, then merged in place
   __shared__ uint32_t s_bins[kT1Waves][256];
   __shared__ u32x4 s_stage[kT1Waves][kTopmStage];
   __shared__ uint32_t s_stage_at[kT1Waves][kTopmStage];
-  __shared__ uint64_t s_merge[kT1Merge];
   __shared__ u64 s_P[kT1MaxWant];
   __shared__ uint32_t s_count[kT1Waves], s_flag[kT1Waves];
-  __shared__ float s_R[kT1Waves], s_M[kT1Waves];
-  __shared__ double s_S[kT1Waves];
+  __shared__ float s_M[kT1Waves];
   __shared__ unsigned long long s_thr;
   __shared__ uint32_t s_n;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -689,23 +684,21 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
     }
   };
   if (!(pp > 0.0f)) return put(__builtin_nan(""), 0.0f, 0u, 0);
-  if ((kon && uint32_t(kk) + 1u > kT1MaxWant) || (pon && !kon))
-    return put(0.0, 0.0f, 0u, kTruncRedo);
-  const uint32_t want = kon ? uint32_t(kk) + 1u : 1u;
+  if (!kon || uint32_t(kk) + 1u > kT1MaxWant) return put(0.0, 0.0f, 0u, kTruncRedo);
+  const uint32_t want = uint32_t(kk) + 1u;
   const bool complete = want >= uint32_t(V);         // the list holds every token
   const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
   if (tid == 0) s_thr = 0ull;
   __syncthreads();
   TopM<DT_F32> tm;
-  tm.init(s_keys[wid], s_bins[wid], &s_thr, kT1Cap, want, s_stage[wid], s_stage_at[wid]);
+  tm.init(s_keys + wid * kT1Cap, s_bins[wid], &s_thr, kT1Cap, want, s_stage[wid],
+          s_stage_at[wid]);
 
   // ---- the one read: candidate lists, running-reference normaliser, checks ----
   const long long nchunks = V / VEC;
   constexpr long long kPerIt = (long long)kT1Block * kT1Unroll;
   const long long nit = (nchunks + kPerIt - 1) / kPerIt;
-  const bool need_all = !kon;          // no truncation: the whole row's mass is needed
-  float Ra = kRefInit, gmax = -__builtin_inff();
-  double Sa = 0.0;
+  float gmax = -__builtin_inff();
   uint32_t nonfin = 0u;
   auto load_group = [&](long long it, u32x4 (&raw)[kT1Unroll]) {
 #pragma unroll
@@ -733,18 +726,6 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
       }
     }
     gmax = fmaxf(gmax, gm);
-    if (need_all) {
-      const float Rn = fmaxf(Ra, ceilf(gm * c));
-      Sa = rescale(Sa, Ra, Rn);
-      Ra = Rn;
-      double t = 0.0;
-#pragma unroll
-      for (int u = 0; u < kT1Unroll; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          t += ((ok >> u) & 1u) ? value_term(__uint_as_float(raw[u][q]), c64, Rn) : 0.0;
-      Sa += t;
-    }
     if (it == 0) tm.template seed<kT1Unroll>(cm, ok);
 #pragma unroll
     for (int u = 0; u < kT1Unroll; ++u)
@@ -764,16 +745,11 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
   }
   tm.flush();
   tm.compact();                                 // at most want keys per wavefront
-  // the normaliser over the workgroup, in a fixed order
   {
-    const float Rw = wave_max(Ra);
-    const double Sw = wave_sum(rescale(Sa, Ra, Rw));
     const uint32_t fw = wave_or(nonfin);
     const float Mw = wave_max(gmax);
     if (lane == 0) {
       s_M[wid] = Mw;
-      s_R[wid] = Rw;
-      s_S[wid] = Sw;
       s_flag[wid] = fw;
       s_count[wid] = tm.fill;
     }
@@ -787,24 +763,28 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
     bad |= s_flag[w];
   }
   if (bad != 0u || !(M > -__builtin_inff())) return put(__builtin_nan(""), 0.0f, 0u, 0);
-  const float R = ceilf(M * c);                  // the largest running reference, too
-  double S_all = 0.0;
-  if (need_all)
-#pragma unroll
-    for (int w = 0; w < kT1Waves; ++w) S_all += rescale(s_S[w], s_R[w], R);
+  const float R = ceilf(M * c);
 
-  // ---- merge the lists, keep the want largest keys, sort them ----
+  // ---- merge the lists in place, keep the want largest keys, sort them ----
+  // List w (at most want <= kT1MaxWant keys at w kT1Cap) moves down to the
+  // end of the lists before it: the target lies below the source, and each
+  // 64-key step reads its keys before any later step's writes reach them.
   if (wid == 0) {
-    uint32_t n = 0;
+    uint32_t n = s_count[0];
 #pragma unroll
-    for (int w = 0; w < kT1Waves; ++w) {
+    for (int w = 1; w < kT1Waves; ++w) {
       const uint32_t cw = s_count[w];
-      for (uint32_t e = uint32_t(lane); e < cw; e += kWave) s_merge[n + e] = s_keys[w][e];
+      for (uint32_t e0 = 0; e0 < cw; e0 += kWave) {
+        const uint32_t e = e0 + uint32_t(lane);
+        const uint64_t k = e < cw ? s_keys[w * kT1Cap + e] : 0ull;
+        wave_sync();
+        if (e < cw) s_keys[n + e] = k;
+        wave_sync();
+      }
       n += cw;
     }
-    wave_sync();
     TopM<DT_F32> mg;
-    mg.init(s_merge, s_bins[0], &s_thr, kT1Merge, want);
+    mg.init(s_keys, s_bins[0], &s_thr, kT1Waves * kT1Cap, want);
     mg.fill = n;
     mg.compact();
     if (lane == 0) s_n = mg.fill;
@@ -814,17 +794,17 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
   {
     int n2 = 1;
     while (n2 < n) n2 <<= 1;
-    for (int i = n + tid; i < n2; i += kT1Block) s_merge[i] = 0ull;
+    for (int i = n + tid; i < n2; i += kT1Block) s_keys[i] = 0ull;
     __syncthreads();
     for (int k2 = 2; k2 <= n2; k2 <<= 1) {
       for (int j = k2 >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < n2; i += kT1Block) {
           const int l = i ^ j;
           if (l > i) {
-            const uint64_t a = s_merge[i], bb = s_merge[l];
+            const uint64_t a = s_keys[i], bb = s_keys[l];
             if ((i & k2) == 0 ? a < bb : a > bb) {
-              s_merge[i] = bb;
-              s_merge[l] = a;
+              s_keys[i] = bb;
+              s_keys[l] = a;
             }
           }
         }
@@ -836,23 +816,11 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
   if (wid != 0) return;
 
   // ---- wavefront 0: the cut, the masses, the top-p level ----
-  auto key32 = [&](int i) -> uint32_t { return uint32_t(s_merge[i] >> 32); };
-  if (!kon && !pon) {                            // no truncation: the whole row
-    if (lane == 0) {
-      RowPart p;
-      p.S = S_all;
-      p.R = R;
-      p.m = 0.0f;
-      p.idx = 0;
-      p.flags = 0;
-      parts[blockIdx.x] = p;
-    }
-    return;
-  }
+  auto key32 = [&](int i) -> uint32_t { return uint32_t(s_keys[i] >> 32); };
   const double scale = __builtin_ldexp(1.0, fx);
   uint32_t tk = 0u;
   int n_k = n;                                   // list entries in the top-k set
-  if (kon) {
+  {
     tk = key32(kk - 1);
     if (!complete && key32(kk) == tk) {          // the tie may go on past the list
       if (lane == 0) {
