@@ -1,4 +1,8 @@
-// Top-k / top-p truncation pass over fp32 logit rows (gfx950).
+// Top-k / top-p truncation passes over fp32 logit rows (gfx950).
+//
+// Two passes: the list pass at the end of this file settles most rows with
+// top-k in one read from the row's top k + 1 token keys; the multi-read pass
+// described here takes every other row (and every row not in 16-byte chunks).
 //
 // The rules are those of the bf16 passes in sv_trunc.hpp ([RNR] s.1 and s.2):
 // top-k keeps the values at or above the k-th largest, counted with
