@@ -261,3 +261,33 @@ def test_trunc32_candidates_beyond_buffer(sv):
     tp = np.select([m == 0, m == 1], [1.0, 0.5], 0.9).astype(np.float32)
     _resample_drafts(x, cfg.T, tk, tp, 39)
     _check(sv, x, cfg, tk, tp, "trunc32/beyond buffer")
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 524296), (torch.bfloat16, 65537),
+                                     (torch.float32, 262148), (torch.float32, 65537)])
+def test_trunc_vocabulary_limits(sv, dtype, V):
+    """Past the finish's tile limit (524288 bf16 / 262144 fp32 values in
+    16-byte chunks, 65536 on the scalar path) a truncated call is refused with
+    SV_EUNSUPPORTED before anything is enqueued; without truncation the same
+    shape verifies."""
+    B, K = 1, 1
+    g = torch.Generator(device=DEV)
+    g.manual_seed(43)
+    target = torch.randn((B, K + 1, V), generator=g, device=DEV).to(dtype)
+    draft = torch.randn((B, K, V), generator=g, device=DEV).to(dtype)
+    tokens = torch.zeros((B, K), dtype=torch.int32, device=DEV)
+    uniforms = torch.full((B, K + 1), 0.5, dtype=torch.float32, device=DEV)
+    v = sv.SpecVerifier(B, K, V, dtype)
+    out = (torch.full((B, K + 1), -7, dtype=torch.int32, device=DEV),
+           torch.full((B,), -7, dtype=torch.int32, device=DEV),
+           torch.full((K + 1,), 7, dtype=torch.int32, device=DEV))
+    v.set_truncation(torch.full((B,), 5, dtype=torch.int32, device=DEV), None)
+    with pytest.raises(sv.SpecVerifyError) as e:
+        v.verify(target, draft, tokens, uniforms, 1.0, out=out)
+    assert e.value.code == sv.SV_EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert int(out[0].min()) == -7 and int(out[1][0]) == -7 and int(out[2].max()) == 7
+    v.clear_truncation()
+    tok, alen, _ = v.verify(target, draft, tokens, uniforms, 1.0)
+    torch.cuda.synchronize()
+    assert int(alen[0]) in (0, 1)
