@@ -105,6 +105,10 @@ typedef struct spec_verify_stats {
  *   SPEC_VERIFY_TILES_PER_GROUP  draw tiles per workgroup on that path (16)
  *   SPEC_VERIFY_FUSED_MIN_B      smallest batch that streams and finishes each
  *                                sequence in one kernel (0 = never)
+ *   SPEC_VERIFY_TRUNC32_LIST     0: float32 truncation without the one-read
+ *                                top-k list pass (1)
+ *   SPEC_VERIFY_TRUNC32_BUF      0: float32 truncation narrows every row by
+ *                                digit reads, never through an LDS copy (1)
  */
 int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
                      int logits_dtype, double ema_decay);
