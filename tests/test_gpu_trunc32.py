@@ -291,3 +291,20 @@ def test_trunc_vocabulary_limits(sv, dtype, V):
     tok, alen, _ = v.verify(target, draft, tokens, uniforms, 1.0)
     torch.cuda.synchronize()
     assert int(alen[0]) in (0, 1)
+
+
+def test_trunc32_list_holds_every_token(sv, route):
+    """V = 256 (16-byte chunks), so top_k = V - 1 makes the list pass keep
+    every token (its `complete` case, where ties at the cut are counted in
+    the list itself); half the rows hold integer ties."""
+    cfg = SMALL.scaled(B=8, K=2, V=256)
+    x = make_inputs(cfg, 14, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(47)
+    for key in ("target", "draft"):
+        for b in range(0, cfg.B, 2):
+            x[key][b] = torch.randint(-2, 3, x[key][b].shape, generator=g, device=DEV).float()
+    tk = np.array([255, 255, 254, 128, 5, 1, 200, 255], np.int32)
+    tp = np.array([1.0, 0.9, 0.5, 0.95, 1.0, 1.0, 0.3, 0.99], np.float32)
+    _resample_drafts(x, cfg.T, tk, tp, 48)
+    _check(sv, x, cfg, tk, tp, f"trunc32/list holds every token/{route}")
