@@ -75,7 +75,7 @@ struct spec_verify_handle {
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int n_cu = 256;          // compute units of the device
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
-  int trunc32_buf = 1;     // fp32 truncation: sort the few candidate values in LDS (0 = digit reads only)
+  int trunc32_buf = 1;     // fp32 truncation: walk the digits over an LDS copy of the few candidates (0 = digit reads only)
   int trunc32_list = 1;    // fp32 truncation: settle rows from one read's top-k list first (0 = off)
   char err[256] = {0};
 };
