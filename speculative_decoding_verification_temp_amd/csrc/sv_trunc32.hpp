@@ -34,7 +34,9 @@
 // normaliser; a bound on each bin's mass then places the crossing, and the
 // values from a bin at or below it upwards are copied (two reads), or, when
 // they do not fit, the mass read finds the crossing bin and its values are
-// copied (three reads).
+// copied (three reads). A row with neither rule (a sequence without
+// truncation in a truncated batch) takes one read: read A also sums its
+// terms over a running reference.
 //
 // Masses are softmax terms 2^(x c - R), each rounded once to unsigned 64-bit
 // fixed point with FX = 61 - ceil(log2 V) fraction bits (a term is at most
@@ -410,6 +412,9 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   // x c - R carries c as two floats (about 1e-7 relative), over a running
   // reference in registers; it places the top-p goal for the route below
   const bool est = pon && !kon && use_buf;
+  // neither rule: the whole row's normaliser from this read, with the terms
+  // p(d) and q(d) are formed with (value_term), over a running reference
+  const bool plain = !pon && !kon;
   const float c_lo = float(c64 - double(c));
   float Ra = kRefInit;
   double Sa = 0.0;
@@ -429,11 +434,34 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
       }
       Sa += double(__builtin_amdgcn_exp2f(__builtin_fmaf(x, c_lo, __builtin_fmaf(x, c, -Ra))));
     }
+    if (plain && fin) {
+      const float x = __uint_as_float(bits);
+      const float xc = x * c;
+      if (xc > Ra) {
+        const float Rn = ceilf(xc);
+        Sa = rescale(Sa, Ra, Rn);
+        Ra = Rn;
+      }
+      Sa += value_term(x, c64, Ra);
+    }
   });
   top = t32_max(top, s_u);
   const bool bad = t32_max(nonfin, s_u) != 0u || top == 0u || !(pp > 0.0f);
   if (bad) return put(__builtin_nan(""), 0.0f, 0u);
   const float R = ceilf(order_floor<DT_F32>(top) * c);
+  if (plain) {
+    const float Rw = wave_max(Ra);
+    const double Sw = wave_sum(rescale(Sa, Ra, Rw));
+    if (lane == 0) {
+      s_rf[wid] = Rw;
+      s_sd[wid] = Sw;
+    }
+    __syncthreads();
+    double S_all = 0.0;
+#pragma unroll
+    for (int q = 0; q < kT32Waves; ++q) S_all += rescale(s_sd[q], s_rf[q], R);
+    return put(S_all, R, 0u);
+  }
 
   // ---- top-p alone: the candidates from the counts and a mass bound ----
   // Bin b of the first digit holds cnt[b] values of at most its largest
