@@ -256,3 +256,20 @@ def test_batch_passes_per_sequence_truncation():
                                 top_k=int(tk[b]), top_p=float(tp[b]))
         assert np.array_equal(res.tokens[b], one.tokens)
         assert res.accept_len[b] == one.accept_len
+
+
+def test_signed_zeros_are_one_level():
+    """-0 and +0 compare equal, so they are one value level: top_k = 1 on a
+    row whose maximum is zero keeps both zeros (counted with multiplicity),
+    and top-p keeps or drops them together (fp32 rows hold both)."""
+    x = np.array([-1.0, 0.0, -3.0, -0.0, -2.0])
+    keep, _ = O.truncation_keep(x, 1.0, 1, 1.0)
+    assert keep.tolist() == [False, True, False, True, False]
+    # mass of the zero level is 2 / (2 + e^-1 + e^-2 + e^-3) ~ 0.783: a top_p
+    # below that keeps exactly the two zeros, above it the next level too
+    keep, _ = O.truncation_keep(x, 1.0, 0, 0.5)
+    assert keep.tolist() == [False, True, False, True, False]
+    keep, _ = O.truncation_keep(x, 1.0, 0, 0.8)
+    assert keep.tolist() == [True, True, False, True, False]
+    p, _ = O.truncated_softmax(x, 1.0, 1, 1.0)
+    assert p[1] == p[3] == 0.5 and p.sum() == 1.0
