@@ -529,6 +529,7 @@ class BatchResult:
     invalid: int
     shape: np.ndarray = None  # [B, 3] next tree shape (policy only)
     dcs: np.ndarray = None    # [B] draft confidence score (policy only)
+    n_decisions: int = 0      # decisions with a boundary distance (tests, draws, cuts)
 
 
 def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
@@ -582,6 +583,7 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
         out.min_dist[k] = res.min_dist
         out.zero_q_accepts += res.zero_q_accepts
         out.z0_fallbacks += res.z0_fallback
+        out.n_decisions += len(res.dists)
         if res.valid:
             out.hist[res.accept_len] += 1
             if ema is not None and res.draft_len > 0:
