@@ -3,11 +3,25 @@
 The rule: emitted tokens, accept lengths and argmaxes must be identical for
 every sequence whose decisions all lie at least 1e-6 (in uniform units) from a
 decision boundary, as measured by the fp64 oracle; sequences closer than that
-are counted and excused, and must be rare. p(d), q(d), margin ratios and Z
-must agree within 1e-5 absolute.
+are counted and excused. Two ceilings keep the excuse honest:
+
+  * sequences that do differ (all of them inside the band) must be under
+    1e-4 of the decisions compared (acceptance tests, draws, margin tests,
+    top-p cuts), so none at all below 10^4 decisions;
+  * the excused sequences must stay under 10% of the compared rows, plus a
+    three-sigma binomial allowance and 3 for small samples. At V = 128256 about 5%
+    of draws land within 1e-6 of an interval edge whatever the implementation
+    (a token's share of [0, 1) averages ~8e-6), so the band itself is not
+    rare; a distance computed too small would push the share far above this.
+
+p(d), q(d), margin ratios and Z must agree within 1e-5 absolute. Every
+comparison is recorded in REPORTS; the test session prints a summary of them.
 """
 
 from __future__ import annotations
+
+import math
+import os
 
 import numpy as np
 import torch
@@ -17,6 +31,15 @@ from workloads import to_host_f64
 
 BOUNDARY = 1e-6
 PROB_TOL = 1e-5
+MISMATCH_RATE = 1e-4
+EXCUSED_FRACTION = 0.10
+
+REPORTS: list = []          # one dict per compare() call, in call order
+
+
+def excused_ceiling(rows: int) -> float:
+    mean = EXCUSED_FRACTION * rows
+    return mean + 3.0 * math.sqrt(mean) + 3.0
 
 
 def _merge(parts):
@@ -28,6 +51,7 @@ def _merge(parts):
         out.zero_q_accepts += p.zero_q_accepts
         out.z0_fallbacks += p.z0_fallbacks
         out.invalid += p.invalid
+        out.n_decisions += p.n_decisions
     return out
 
 
@@ -85,8 +109,17 @@ def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
         f"oracle {ref.tokens[bad_tok[:2]] if len(bad_tok) else ref.accept_len[bad_len[:5]]}")
     # near-boundary sequences are excused; count how many actually differ
     diff = (g_len != ref.accept_len) | np.any(g_tok != ref.tokens, axis=1)
-    report = dict(rows=len(rows), near_boundary=int((~strict).sum()),
-                  mismatches=int(diff.sum()))
+    report = dict(rows=len(rows), decisions=int(ref.n_decisions),
+                  near_boundary=int((~strict).sum()), mismatches=int(diff.sum()))
+    REPORTS.append(dict(report, label=label,
+                        test=os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]))
+    assert report["mismatches"] == 0 or \
+        report["mismatches"] < MISMATCH_RATE * report["decisions"], (
+        f"{label}: {report['mismatches']} excused mismatches in {report['decisions']} "
+        f"decisions (must be under {MISMATCH_RATE:g} of them)")
+    assert report["near_boundary"] <= excused_ceiling(len(rows)), (
+        f"{label}: {report['near_boundary']} of {len(rows)} rows within {BOUNDARY:g} of a "
+        f"boundary (ceiling {excused_ceiling(len(rows)):.1f})")
     if aux is not None:
         valid = ref.accept_len >= 0
         if mode in ("stochastic", "margin"):
@@ -107,6 +140,7 @@ def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
         if mode in ("greedy", "margin"):
             ga = aux["argmax"].cpu().numpy()[rows]
             assert np.array_equal(ga[valid], ref.argmax[valid]), f"{label}: argmax mismatch"
+        REPORTS[-1].update({k: report[k] for k in ("p_err", "q_err", "z_err") if k in report})
     return report
 
 

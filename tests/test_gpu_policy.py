@@ -16,6 +16,7 @@ import pytest
 import torch
 
 from oracle import spec_oracle as O
+from tests.parity import compare
 from workloads import CONFIGS, make_inputs, to_host_f64
 
 pytestmark = pytest.mark.gpu
@@ -110,8 +111,8 @@ def test_policy_stochastic_paths(sv, monkeypatch, path):
     ref = O.verify_batch(to_host_f64(x["target"]), to_host_f64(x["draft"]),
                          x["tokens"].cpu().numpy(), x["uniforms"].cpu().double().numpy(), cfg.T,
                          O.MODE_STOCHASTIC, ema=ema, policy=pol, conf=conf, **(trunc or {}))
+    compare(np.arange(cfg.B), ref, tok, alen, "stochastic", None, f"policy/{path}")
     strict = ref.min_dist >= 1e-6
-    assert np.array_equal(alen.cpu().numpy()[strict], ref.accept_len[strict])
     _compare(shape, dcs, ref, np.flatnonzero(strict))
     g = shape.cpu().numpy()
     assert np.all(g[[1, 2, 3]] == -1)      # confidences outside [0, 1]
