@@ -1,8 +1,8 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
-Small configurations are compared on the full batch; the large ones on seeded
-samples of sequences at full size, in the same launch configuration the
-benchmark times, plus size-independent invariants on every sequence.
+Small configurations and special cases are compared on the full batch here;
+the full-size configurations are compared on whole batches in
+test_gpu_full_batch.py.
 """
 
 import math
@@ -77,8 +77,9 @@ def test_c2_full_batch(sv):
     ref = oracle_for(x, rows, "stochastic")
     rep = compare(rows, ref, tok, alen, "stochastic", aux, "c2")
     check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-    if rep["mismatches"] == 0:
-        assert np.array_equal(hist.cpu().numpy(), ref.hist)
+    # an excused mismatch moves at most one count between two bins
+    h = hist.cpu().numpy().astype(np.int64)
+    assert np.abs(h - ref.hist).sum() <= 2 * rep["mismatches"]
     _log(f"c2: {rep} alpha~{np.mean(ref.accept_len) / cfg.K:.3f}")
 
 
@@ -130,79 +131,6 @@ def test_fused_and_pipeline_paths_agree(sv, monkeypatch, name):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
         assert torch.allclose(a[3]["p_d"], b[3]["p_d"], rtol=1e-6, atol=0)
         assert torch.allclose(a[3]["z"], b[3]["z"], rtol=1e-9, atol=1e-15)
-
-
-def test_c3_pipeline_path_sampled(sv, monkeypatch):
-    """The multi-kernel path (separate scan, tile-sum and pick kernels) at the
-    full c3 shape; the default there is one workgroup per sequence after the
-    streaming pass."""
-    monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "0")
-    monkeypatch.setenv("SPEC_VERIFY_FINISH_SEQ", "0")
-    cfg = CONFIGS["c3"]
-    x = make_inputs(cfg, 1, DEV, "stochastic")
-    v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
-    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-    rows = _sample(cfg.B, 16, 37)
-    rep = compare(rows, oracle_for(x, rows, "stochastic"), tok, alen, "stochastic", aux,
-                  "c3/pipeline")
-    _log(f"c3/pipeline: {rep}")
-
-
-# --------------------------------------------------------------------------
-# full-size configurations, sampled sequences
-# --------------------------------------------------------------------------
-
-def test_c3_stochastic_sampled(sv):
-    cfg = CONFIGS["c3"]
-    x = make_inputs(cfg, 0, DEV, "stochastic")
-    v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
-    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-    rows = _sample(cfg.B, 24, 33)
-    ref = oracle_for(x, rows, "stochastic")
-    rep = compare(rows, ref, tok, alen, "stochastic", aux, "c3/stochastic")
-    _log(f"c3/stochastic: {rep} mean accept {alen.float().mean().item():.3f}")
-
-
-def test_c3_greedy_sampled(sv):
-    cfg = CONFIGS["c3"]
-    x = make_inputs(cfg, 0, DEV, "greedy")
-    v, aux, tok, alen, hist = _verify(sv, x, cfg, "greedy")
-    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-    rows = _sample(cfg.B, 96, 34)
-    ref = oracle_for(x, rows, "greedy")
-    rep = compare(rows, ref, tok, alen, "greedy", aux, "c3/greedy")
-    _log(f"c3/greedy: {rep} hist {hist.cpu().tolist()}")
-
-
-@pytest.mark.parametrize("mode", ["margin", "greedy"])
-def test_c4_sampled(sv, mode):
-    cfg = CONFIGS["c4"]
-    x = make_inputs(cfg, 0, DEV, mode)
-    v, aux, tok, alen, hist = _verify(sv, x, cfg, mode)
-    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-    rows = _sample(cfg.B, 48, 35)
-    ref = oracle_for(x, rows, mode, tau=cfg.tau)
-    rep = compare(rows, ref, tok, alen, mode, aux, f"c4/{mode}")
-    _log(f"c4/{mode}: {rep} hist {hist.cpu().tolist()}")
-
-
-def test_c5_sampled_with_special_sequences(sv):
-    cfg = CONFIGS["c5"]
-    x = make_inputs(cfg, 0, DEV)
-    v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
-    check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-    pq, zz = x["pq_idx"], x["z_idx"]
-    # every p = q sequence keeps all drafts, and no residual is evaluated
-    a = alen.cpu().numpy()
-    assert np.all(a[pq] == cfg.K)
-    assert np.all(aux["z"].cpu().numpy()[pq] == -1.0)
-    pd, qd = aux["p_d"].cpu().numpy(), aux["q_d"].cpu().numpy()
-    assert np.array_equal(pd[pq], qd[pq])
-    rows = np.unique(np.concatenate([pq[:6], zz[:6], _sample(cfg.B, 12, 36)]))
-    ref = oracle_for(x, rows, "stochastic")
-    rep = compare(rows, ref, tok, alen, "stochastic", aux, "c5")
-    assert v.stats()["z0_fallbacks"] == 0
-    _log(f"c5: {rep}")
 
 
 # --------------------------------------------------------------------------
@@ -424,37 +352,6 @@ def test_ema_tracks_oracle_and_accessors(sv):
     e, s = v.ema()
     torch.cuda.synchronize()
     assert torch.all(e == 0) and torch.all(s == 0)
-
-
-def test_c3_ema_600_steps(sv):
-    """The 600-step run at the full c3 shape with fresh logits each step and
-    EMA decay 0.99: four seeded slots are verified by the oracle at every
-    step (tokens, accept lengths) and their EMA compared at the end; every
-    step's outputs satisfy the invariants on the whole batch."""
-    cfg = CONFIGS["c3"]
-    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, cfg.torch_dtype, ema_decay=cfg.ema_decay)
-    ema = O.EmaState(cfg.B, cfg.ema_decay)
-    rows = _sample(cfg.B, 4, 38)
-    near = 0
-    for step in range(cfg.steps):
-        x = make_inputs(cfg, step, DEV, "stochastic")
-        tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T)
-        torch.cuda.synchronize()
-        ref = oracle_for(x, rows, "stochastic", ema=ema)
-        rep = compare(rows, ref, tok, alen, "stochastic", None, f"ema step {step}")
-        assert rep["mismatches"] == 0, rep
-        near += rep["near_boundary"]
-        check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
-        if step % 100 == 0:
-            _log(f"ema step {step}: mean accept {alen.float().mean().item():.3f}")
-    e, s = v.ema()
-    torch.cuda.synchronize()
-    e = e.cpu().numpy()
-    assert np.all(s.cpu().numpy()[: cfg.B] == cfg.steps)
-    err = np.abs(e[rows] - ema.ema[rows]).max()
-    _log(f"ema 600 steps: slots {rows.tolist()} gpu {np.round(e[rows], 6).tolist()} "
-         f"oracle {np.round(ema.ema[rows], 6).tolist()} max err {err:.2e} near-boundary {near}")
-    assert err <= 1e-5
 
 
 def test_profiling_events(sv):
