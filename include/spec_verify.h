@@ -31,6 +31,17 @@
  *     acceptance EMA are maintained ("... not resampling from the target",
  *     section 7; "Margins, Not Windows", section 3, dynamic tree shaping).
  *
+ * Short names used for these pages further down:
+ *   [DVC]   "Speculative Decoding: Draft, Verify, and Correct"
+ *   [SMB]   "Speculative Decoding: How a Small Model Speeds Up a Big One
+ *            Without Changing Its Output"
+ *   [RNR]   "Speculative decoding: why correcting a rejection is not
+ *            resampling from the target"
+ *   [MNW]   "Margins, Not Windows: Training-Free Per-Step Lossy Speculative
+ *            Decoding"
+ *   [DRIFT] "Speculative Decoding Under Distribution Shift: DRIFT
+ *            Recalibration"
+ *
  * Conventions fixed by this library where the pages leave a choice:
  *   - u[b][i] decides position i (keep iff p >= q or u < p/q, strict);
  *     u[b][K] drives the one correction/bonus draw (inverse CDF in index
@@ -129,6 +140,8 @@ int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
  *   out_tokens      [B][K+1]    int32: kept drafts, then the correction/bonus, then -1
  *   out_accept_len  [B]         int32: kept drafts j in 0..K (emitted = j+1); -1 if invalid
  *   out_accept_hist [K+1]       uint32: zeroed, then hist[j] counts this call's valid sequences
+ *                               (the Python binding hands it out as an int32 tensor holding
+ *                               these bits; counts stay below 2^31 for any B it accepts)
  *   stream          HIP stream the work is ordered on
  *
  * EMA slot b is updated with x = accept_len/K for every valid sequence b

@@ -91,6 +91,49 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_out(out, B: int, K: int, device):
+    """The caller's output tensors: int32, contiguous, on `device`, shaped
+    [B, K+1], [B] and [K+1] (the kernels write exactly these)."""
+    if not isinstance(out, (tuple, list)) or len(out) != 3:
+        raise SpecVerifyError(SV_EINVAL, "out: expected (tokens, accept_len, hist)")
+    for t, shape, name in zip(out, ((B, K + 1), (B,), (K + 1,)),
+                              ("tokens", "accept_len", "hist")):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.device != device
+                or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise SpecVerifyError(SV_EINVAL, f"out {name}: expected a contiguous int32 tensor "
+                                             f"of shape {list(shape)} on {device}")
+
+
+def _check_inputs(target, draft, tokens, uniforms, mode, K, V, dtype, device):
+    """Shapes, dtypes, devices and contiguity of one call's inputs; returns B
+    and the (draft, uniforms) the mode reads (None for greedy and margin)."""
+    if mode not in MODES:
+        raise SpecVerifyError(SV_EINVAL, f"unknown mode {mode!r}")
+    B = int(target.shape[0])
+
+    def logits(t, rows, name):
+        if t.device != device or t.dtype != dtype:
+            raise SpecVerifyError(SV_EINVAL, f"{name}: expected {dtype} on {device}")
+        if tuple(t.shape) != (B, rows, V) or not t.is_contiguous():
+            raise SpecVerifyError(SV_EINVAL, f"{name}: expected contiguous [B, {rows}, {V}]")
+
+    logits(target, K + 1, "target")
+    if mode == "stochastic":
+        if draft is None or uniforms is None:
+            raise SpecVerifyError(SV_EINVAL, "stochastic mode needs draft and uniforms")
+        logits(draft, K, "draft")
+        if (uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1)
+                or not uniforms.is_contiguous() or uniforms.device != device):
+            raise SpecVerifyError(SV_EINVAL, "uniforms: expected contiguous float32 [B, K+1]")
+    else:
+        draft = None
+        uniforms = None
+    if (tokens.dtype != torch.int32 or tuple(tokens.shape) != (B, K)
+            or not tokens.is_contiguous() or tokens.device != device):
+        raise SpecVerifyError(SV_EINVAL, "tokens: expected contiguous int32 [B, K]")
+    return B, draft, uniforms
+
+
 def read_probe(buf: "torch.Tensor", sink: "torch.Tensor") -> None:
     """One plain streaming read of `buf` (a contiguous device tensor, 16-byte
     aligned, size a multiple of 16 bytes) on the current stream: the
@@ -245,41 +288,20 @@ class SpecVerifier:
         return shape, dcs
 
     # -- verification --
-    def _check_logits(self, t, rows, name):
-        B = t.shape[0]
-        if t.device != self.device or t.dtype != self.dtype:
-            raise SpecVerifyError(SV_EINVAL, f"{name}: expected {self.dtype} on {self.device}")
-        if tuple(t.shape) != (B, rows, self.V) or not t.is_contiguous():
-            raise SpecVerifyError(SV_EINVAL, f"{name}: expected contiguous [B, {rows}, {self.V}]")
-
     def verify(self, target, draft, tokens, uniforms=None, temperature: float = 1.0,
                mode: str = "stochastic", tau: float = 0.0, out=None):
         """Verify a batch. Returns (tokens [B, K+1] int32, accept_len [B] int32,
-        hist [K+1] int32 holding uint32 counts), ordered on the current stream."""
-        if mode not in MODES:
-            raise SpecVerifyError(SV_EINVAL, f"unknown mode {mode!r}")
+        hist [K+1] int32 holding uint32 counts), ordered on the current stream.
+        out, when given, is the (tokens, accept_len, hist) tensors to write."""
         K = self.K
-        B = int(target.shape[0])
-        self._check_logits(target, K + 1, "target")
-        if mode == "stochastic":
-            if draft is None or uniforms is None:
-                raise SpecVerifyError(SV_EINVAL, "stochastic mode needs draft and uniforms")
-            self._check_logits(draft, K, "draft")
-            if draft.shape[0] != B:
-                raise SpecVerifyError(SV_EINVAL, "draft batch differs from target")
-            if (uniforms.dtype != torch.float32 or tuple(uniforms.shape) != (B, K + 1)
-                    or not uniforms.is_contiguous() or uniforms.device != self.device):
-                raise SpecVerifyError(SV_EINVAL, "uniforms: expected contiguous float32 [B, K+1]")
-        else:
-            draft = None
-            uniforms = None
-        if (tokens.dtype != torch.int32 or tuple(tokens.shape) != (B, K)
-                or not tokens.is_contiguous() or tokens.device != self.device):
-            raise SpecVerifyError(SV_EINVAL, "tokens: expected contiguous int32 [B, K]")
+        B, draft, uniforms = _check_inputs(target, draft, tokens, uniforms, mode, K, self.V,
+                                           self.dtype, self.device)
         if out is None:
             out = (torch.empty((B, K + 1), dtype=torch.int32, device=self.device),
                    torch.empty((B,), dtype=torch.int32, device=self.device),
                    torch.empty((K + 1,), dtype=torch.int32, device=self.device))
+        else:
+            _check_out(out, B, K, self.device)
         ot, ol, oh = out
         with torch.cuda.device(self.device):
             rc = self.lib.spec_verify(self._h, B, _ptr(target), _ptr(draft), _ptr(tokens),
