@@ -325,8 +325,47 @@ int spec_verify_profile(spec_verify_handle *h, int enable);
 int spec_verify_profile_read(spec_verify_handle *h, double *stream_pass_ms, double *call_ms,
                              int *n_calls);
 
-/* Text of the last error on this handle ("" if none). Valid until the next call. */
+/*
+ * Text of the last error on this handle ("" if none). Valid until the next
+ * call. With h = NULL: the text of this thread's last failed
+ * spec_verify_noalloc call, or "null handle" if there was none.
+ */
 const char *spec_verify_last_error(const spec_verify_handle *h);
+
+/*
+ * One verification without a handle and without any allocation, for callers
+ * that cannot allocate device memory: code being captured into a HIP graph,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments and
+ * outputs as spec_verify, with the handle's fixed sizes given per call
+ * (K in 1..63, V >= 1, V * (K+1) < 2^31, B >= 1, logits_dtype SV_DTYPE_*),
+ * on the current HIP device.
+ *
+ * The workspace (row partials, counters, the per-call EMA) lies in a 1 MiB
+ * device array inside this library, one copy per GPU, held until the process
+ * ends; its device address is looked up once per device on the first call
+ * there. Nothing else is kept between calls: the EMA and the counters are not
+ * maintained, and the optional side outputs, stopping rules, truncation,
+ * policy and residual of a handle do not exist here. Every call on one GPU
+ * uses the same array, so calls that overlap on one GPU (concurrent streams,
+ * threads) race and must be ordered by the caller.
+ *
+ * Routes: the streaming pass then one workgroup per sequence (stochastic,
+ * V <= 524288 for bf16 / 262144 for fp32 logit arrays in 16-byte chunks,
+ * V <= 65536 otherwise), the argmax pass then the scan (greedy, margin).
+ * Returns SV_OK once enqueued; SV_EINVAL, with nothing enqueued, for the
+ * argument errors of spec_verify or when B * rows * segments of row partials
+ * would not fit in the array (about B * (2K+1) * 24 bytes for large batches:
+ * B = 1024 at K = 4 fits, B = 4096 at K = 7 does not); SV_EUNSUPPORTED for
+ * V beyond the stochastic route's limit or an unknown dtype; SV_EHIP when the
+ * array's address cannot be found or a launch fails. The message is read
+ * with spec_verify_last_error(NULL).
+ */
+int spec_verify_noalloc(int B, int K, int V, int logits_dtype,
+                        const void *target_logits, const void *draft_logits,
+                        const int32_t *draft_tokens, const float *uniforms,
+                        float temperature, int mode, float tau,
+                        int32_t *out_tokens, int32_t *out_accept_len,
+                        uint32_t *out_accept_hist, hipStream_t stream);
 
 /* Library version string. */
 const char *spec_verify_version(void);

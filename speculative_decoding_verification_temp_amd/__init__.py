@@ -28,6 +28,7 @@ EXPORTED = (
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
     "spec_verify_last_error", "spec_verify_version", "spec_verify_read_probe",
+    "spec_verify_noalloc",
 )
 
 
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify_last_error.restype = ctypes.c_char_p
     L.spec_verify_version.restype = ctypes.c_char_p
     L.spec_verify_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    L.spec_verify_noalloc.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, f32, i32, f32,
+                                      vp, vp, vp, vp]
     for name in EXPORTED:
         if name not in ("spec_verify_last_error", "spec_verify_version"):
             getattr(L, name).restype = i32
@@ -132,6 +135,33 @@ def _check_inputs(target, draft, tokens, uniforms, mode, K, V, dtype, device):
             or not tokens.is_contiguous() or tokens.device != device):
         raise SpecVerifyError(SV_EINVAL, "tokens: expected contiguous int32 [B, K]")
     return B, draft, uniforms
+
+
+def verify_noalloc(target, draft, tokens, uniforms, temperature: float, mode: str, tau: float,
+                   out) -> None:
+    """One verification through spec_verify_noalloc: no handle, no device
+    allocation by the library, its workspace in the library's fixed per-GPU
+    scratch array. The caller passes the inputs and the outputs out =
+    (tokens [B, K+1], accept_len [B], hist [K+1]), all int32 device tensors;
+    work is ordered on the current stream of the inputs' device. No EMA and
+    no side outputs are kept. Calls that overlap on one GPU race."""
+    L = load_library()
+    device = target.device
+    B, K, V = int(target.shape[0]), int(target.shape[1]) - 1, int(target.shape[2])
+    if target.dtype not in (torch.float32, torch.bfloat16):
+        raise SpecVerifyError(SV_EUNSUPPORTED, f"logit dtype {target.dtype}")
+    B, draft, uniforms = _check_inputs(target, draft, tokens, uniforms, mode, K, V,
+                                       target.dtype, device)
+    _check_out(out, B, K, device)
+    ot, ol, oh = out
+    code = SV_DTYPE_F32 if target.dtype == torch.float32 else SV_DTYPE_BF16
+    with torch.cuda.device(device):
+        rc = L.spec_verify_noalloc(B, K, V, code, _ptr(target), _ptr(draft), _ptr(tokens),
+                                   _ptr(uniforms), float(temperature), MODES[mode], float(tau),
+                                   _ptr(ot), _ptr(ol), _ptr(oh), _stream(device))
+    if rc != SV_OK:
+        msg = L.spec_verify_last_error(None)
+        raise SpecVerifyError(rc, f"spec_verify_noalloc: {msg.decode() if msg else ''}")
 
 
 def read_probe(buf: "torch.Tensor", sink: "torch.Tensor") -> None:
@@ -357,4 +387,5 @@ def version() -> str:
     return load_library().spec_verify_version().decode()
 
 
-__all__ = ["SpecVerifier", "SpecVerifyError", "load_library", "version", "MODES", "EXPORTED"]
+__all__ = ["SpecVerifier", "SpecVerifyError", "load_library", "version", "verify_noalloc",
+           "MODES", "EXPORTED"]

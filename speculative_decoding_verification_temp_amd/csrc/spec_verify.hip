@@ -10,6 +10,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
+#include <mutex>
 
 #include "sv_drift.hpp"
 #include "sv_trunc.hpp"
@@ -31,6 +33,9 @@ constexpr int kMaxSeg = 16;
 static_assert(kMaxSeg <= sv::kTopmMaxSeg, "top-m lists are laid out for kTopmMaxSeg segments");
 constexpr int kProfCalls = 4096;
 constexpr double kLog2e = 1.4426950408889634073599246810018921;
+
+// last error of spec_verify_noalloc on this thread (it has no handle to hold it)
+thread_local char g_noalloc_err[256] = {0};
 
 struct Launch {
   int vec;          // elements per chunk: 8 (bf16) / 4 (fp32) vector path, 1 scalar path
@@ -347,6 +352,19 @@ void launch_residual(spec_verify_handle* h, int B, bool vec, const void* target,
                        h->drift_res);
 }
 
+// whether a call reads 16-byte chunks (the 128-bit load path)
+bool use_vec(const spec_verify_handle* h, const void* target, const void* draft, int mode) {
+  const int full_vec = h->dtype == SV_DTYPE_BF16 ? 8 : 4;
+  bool vec = (h->V % full_vec) == 0 && aligned(target, 16);
+  if (mode == SV_MODE_STOCHASTIC) vec = vec && aligned(draft, 16);
+  return vec;
+}
+
+int verify_call(spec_verify_handle* h, int B, const void* target, const void* draft,
+                const int32_t* tokens, const float* uniforms, float temperature, int mode,
+                float tau, int32_t* out_tokens, int32_t* out_len, uint32_t* out_hist,
+                hipStream_t stream);
+
 void free_all(spec_verify_handle* h) {
   void* ptrs[] = {h->parts, h->draw,  h->tsum,  h->table,     h->ema,
                   h->steps, h->streak, h->stats, h->topm_lists};
@@ -514,6 +532,20 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   h->err[0] = 0;
   h->topm_nseg = 0;
   if (B < 1 || B > h->max_batch) return fail(h, SV_EINVAL, "B=%d outside [1, %d]", B, h->max_batch);
+  return verify_call(h, B, target, draft, tokens, uniforms, temperature, mode, tau, out_tokens,
+                     out_len, out_hist, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The checks and launches of one verification on a handle whose workspace is
+// in place (the library's own, or the static scratch array).
+int verify_call(spec_verify_handle* h, int B, const void* target, const void* draft,
+                const int32_t* tokens, const float* uniforms, float temperature, int mode,
+                float tau, int32_t* out_tokens, int32_t* out_len, uint32_t* out_hist,
+                hipStream_t stream) {
   if (target == nullptr || tokens == nullptr || out_tokens == nullptr || out_len == nullptr ||
       out_hist == nullptr)
     return fail(h, SV_EINVAL, "required pointer is NULL");
@@ -537,9 +569,7 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
       !aligned(out_len, 4) || !aligned(out_hist, 4))
     return fail(h, SV_EINVAL, "misaligned pointer");
 
-  const int full_vec = h->dtype == SV_DTYPE_BF16 ? 8 : 4;
-  bool vec = (h->V % full_vec) == 0 && aligned(target, 16);
-  if (mode == SV_MODE_STOCHASTIC) vec = vec && aligned(draft, 16);
+  const bool vec = use_vec(h, target, draft, mode);
 
   int rc = SV_OK;
   const double c64 = kLog2e / double(temperature);
@@ -622,6 +652,10 @@ int spec_verify(spec_verify_handle* h, int B, const void* target, const void* dr
   }
   return rc;
 }
+
+}  // namespace
+
+extern "C" {
 
 int spec_verify_profile(spec_verify_handle* h, int enable) {
   if (h == nullptr) return SV_EINVAL;
@@ -750,7 +784,131 @@ int spec_verify_get_stats(spec_verify_handle* h, spec_verify_stats* out, int res
 }
 
 const char* spec_verify_last_error(const spec_verify_handle* h) {
-  return h == nullptr ? "null handle" : h->err;
+  if (h == nullptr) return g_noalloc_err[0] != 0 ? g_noalloc_err : "null handle";
+  return h->err;
+}
+
+}  // extern "C"
+
+// --------------------------------------------------------------------------
+// Allocation-free entry point: one verification with no handle, its
+// workspace in a fixed device array of this library (one copy per GPU).
+// --------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(1) << 20;    // per GPU, held until the process ends
+constexpr size_t kScratchAlign = 256;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+struct ScratchDev {
+  std::once_flag once;
+  void* ptr = nullptr;            // device address of `scratch` on this GPU
+  hipError_t err = hipSuccess;
+  int n_cu = 256;
+};
+ScratchDev g_scratch[kMaxDevices];
+
+// Once per device, with that device current: the device address of this
+// GPU's copy of the array (the host-side name is only a stand-in for it).
+void scratch_setup(ScratchDev& d, int dev) {
+  void* p = nullptr;
+  d.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  d.ptr = d.err == hipSuccess ? p : nullptr;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    d.n_cu = n;
+}
+
+int noalloc_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_noalloc_err, sizeof(g_noalloc_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+size_t align_up(size_t x) { return (x + kScratchAlign - 1) / kScratchAlign * kScratchAlign; }
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_noalloc(int B, int K, int V, int logits_dtype, const void* target,
+                        const void* draft, const int32_t* tokens, const float* uniforms,
+                        float temperature, int mode, float tau, int32_t* out_tokens,
+                        int32_t* out_len, uint32_t* out_hist, hipStream_t stream) {
+  g_noalloc_err[0] = 0;
+  if (logits_dtype != SV_DTYPE_F32 && logits_dtype != SV_DTYPE_BF16)
+    return noalloc_fail(SV_EUNSUPPORTED, "unknown logit dtype %d", logits_dtype);
+  if (B < 1 || K < 1 || K > 63 || V < 1 || (long long)V * (K + 1) >= (1ll << 31))
+    return noalloc_fail(SV_EINVAL, "sizes B=%d K=%d V=%d outside the supported range", B, K, V);
+  if (mode != SV_MODE_STOCHASTIC && mode != SV_MODE_GREEDY && mode != SV_MODE_MARGIN)
+    return noalloc_fail(SV_EINVAL, "unknown mode %d", mode);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return noalloc_fail(SV_EHIP, "no usable current device");
+  ScratchDev& sd = g_scratch[dev];
+  std::call_once(sd.once, scratch_setup, std::ref(sd), dev);
+  if (sd.ptr == nullptr)
+    return noalloc_fail(SV_EHIP, "scratch address: %s", hipGetErrorString(sd.err));
+
+  // a handle on the stack (host memory) whose workspace pointers lie in the
+  // scratch array; the routes that need more workspace are refused
+  spec_verify_handle h;
+  h.device = dev;
+  h.max_batch = B;
+  h.K = K;
+  h.V = V;
+  h.dtype = logits_dtype;
+  h.n_cu = sd.n_cu;
+  const bool vec = use_vec(&h, target, draft, mode);
+  const bool stoch = mode == SV_MODE_STOCHASTIC;
+  const int rows = stoch ? 2 * K + 1 : K + 1;
+  const int v = vec ? (logits_dtype == SV_DTYPE_BF16 ? 8 : 4) : 1;
+  int U = 8;
+  if (vec) U = !stoch ? SV_U_MAX : logits_dtype == SV_DTYPE_BF16 ? SV_U_BF16 : SV_U_F32;
+  const Launch L = plan(&h, B, rows, v, U);
+  if (stoch && (L.ntiles > sv::kFMaxTiles || rows > sv::kFMaxRows))
+    return noalloc_fail(SV_EUNSUPPORTED,
+                        "stochastic calls without allocation need V <= %d for this layout",
+                        sv::kFMaxTiles * sv::kTileChunks * v);
+  const size_t off_ema = align_up(sizeof(sv::DevStats));
+  const size_t off_steps = align_up(off_ema + (size_t)B * sizeof(double));
+  const size_t off_parts = align_up(off_steps + (size_t)B * sizeof(int32_t));
+  const size_t need = off_parts + (size_t)B * rows * L.nseg * sizeof(sv::RowPart);
+  if (need > kScratchBytes)
+    return noalloc_fail(SV_EINVAL,
+                        "B=%d K=%d V=%d needs %zu bytes of scratch; the limit is %zu", B, K, V,
+                        need, kScratchBytes);
+  unsigned char* base = static_cast<unsigned char*>(sd.ptr);
+  h.stats = reinterpret_cast<sv::DevStats*>(base);
+  h.ema = reinterpret_cast<double*>(base + off_ema);
+  h.steps = reinterpret_cast<int32_t*>(base + off_steps);
+  h.parts = reinterpret_cast<sv::RowPart*>(base + off_parts);
+  // counters and the per-call EMA start from zero (fill kernels: no memset
+  // nodes when the call is captured into a graph)
+  hipLaunchKernelGGL(sv::fill_u64, dim3(1), dim3(64), 0, stream,
+                     reinterpret_cast<unsigned long long*>(h.stats),
+                     int(sizeof(sv::DevStats) / 8));
+  hipLaunchKernelGGL(sv::fill_f64_i32, dim3(div_up(B, 256)), dim3(256), 0, stream, h.ema,
+                     h.steps, B, 0.0, 0);
+  int rc = check_launch(&h, "scratch clear");
+  if (rc == SV_OK)
+    rc = verify_call(&h, B, target, draft, tokens, uniforms, temperature, mode, tau, out_tokens,
+                     out_len, out_hist, stream);
+  if (rc != SV_OK) {
+    snprintf(g_noalloc_err, sizeof(g_noalloc_err), "%s", h.err);
+    return rc;
+  }
+  return SV_OK;
 }
 
 }  // extern "C"

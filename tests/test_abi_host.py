@@ -70,3 +70,32 @@ def test_host_side_argument_errors():
     assert L.spec_verify_get_ema(None, None, None, None) == sv.SV_EINVAL
     assert L.spec_verify_reset_ema(None, None) == sv.SV_EINVAL
     assert L.spec_verify_last_error(None) == b"null handle"
+
+
+def test_noalloc_rejects_bad_arguments_before_the_device():
+    """spec_verify_noalloc checks dtype, sizes and mode before it looks for a
+    device, and leaves its message for spec_verify_last_error(NULL) on the
+    calling thread only."""
+    import threading
+    sv, L = _lib()
+    args = [None] * 4 + [1.0]
+    outs = [None] * 4
+    res = {}
+
+    def run():
+        res["dtype"] = L.spec_verify_noalloc(4, 4, 16, 7, *args, 0, 0.0, *outs)
+        res["dtype_msg"] = L.spec_verify_last_error(None)
+        res["B"] = L.spec_verify_noalloc(0, 4, 16, 1, *args, 0, 0.0, *outs)
+        res["K"] = L.spec_verify_noalloc(4, 64, 16, 1, *args, 0, 0.0, *outs)
+        res["V"] = L.spec_verify_noalloc(4, 4, 0, 1, *args, 0, 0.0, *outs)
+        res["big"] = L.spec_verify_noalloc(4, 7, 1 << 28, 1, *args, 0, 0.0, *outs)
+        res["mode"] = L.spec_verify_noalloc(4, 4, 16, 1, *args, 9, 0.0, *outs)
+        res["mode_msg"] = L.spec_verify_last_error(None)
+
+    t = threading.Thread(target=run)
+    t.start()
+    t.join()
+    assert res["dtype"] == sv.SV_EUNSUPPORTED and b"dtype" in res["dtype_msg"]
+    assert res["B"] == res["K"] == res["V"] == res["big"] == sv.SV_EINVAL
+    assert res["mode"] == sv.SV_EINVAL and b"mode" in res["mode_msg"]
+    assert L.spec_verify_last_error(None) == b"null handle"    # another thread's errors
