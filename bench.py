@@ -7,7 +7,9 @@ draft configuration). A step is one spec_verify call over one batch: the
 streaming softmax-statistics pass over all 2K+1 logit rows per sequence, the
 acceptance scan with emit/histogram/EMA, and the residual or bonus draw.
 Inputs are synthetic, seeded and resident in HBM before the timed region;
-two input sets are rotated.
+input sets are rotated, as many as make them span at least twice the 256 MB
+last-level cache (two for the large configurations). With --graph the timed
+calls are replayed from a HIP graph (the launch-bound small configurations).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -27,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "verified seqs/sec + achieved HBM GB/s (% of MI355X peak), V=128256 B=256 K=7"
 PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20       # MI355X last-level (Infinity) cache
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "speculative_decoding_verification_temp_amd", "csrc")
 
@@ -113,10 +116,22 @@ def _worker_task(k):
     return q, int(r.accept_len[0]), r.tokens[0].tolist(), float(r.min_dist[0])
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1.0)):
     """Time the fp64 CPU oracle on a bounded sample of the same workload, one
     sequence per task: first in this process on one core, then on a pool of
-    worker processes (one per usable core, at most 16), about seconds/2 each,
+    worker processes (one per core of this process's CPU set, at most 16: the
+    host share of one GPU), about seconds/2 each,
     cycling over up to 64 sequences of the timed input sets. Every verified
     sequence is compared with the GPU's output for it (gpu_outs[i] holds the
     GPU's tokens and accept lengths for set i)."""
@@ -160,9 +175,10 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1
 
     # all usable cores (at most 16), worker processes over shared memory
     try:
-        nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        nproc = max(1, min(16, os.cpu_count() or 1))
+        avail = os.cpu_count() or 1
+    nproc = max(1, min(16, avail))
     shms, specs = [], {}
     try:
         for name, a in arrays.items():
@@ -190,6 +206,7 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1
             shm.close()
             shm.unlink()
     return dict(value=nn / tn, unit="seqs/s", cores=nproc, kind="oracle",
+                cores_available=avail, cpu_model=cpu_model(),
                 single_core_value=n1 / t1,
                 sample=f"{n1} sequence verifications on one core ({t1:.1f} s), then {nn} on "
                        f"{nproc} worker processes ({tn:.1f} s), cycling over {n} sequences of "
@@ -204,7 +221,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3")
     ap.add_argument("--mode", default="stochastic", choices=["stochastic", "greedy", "margin"])
-    ap.add_argument("--sets", type=int, default=2, help="input sets rotated across steps")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated across steps (0: enough to span twice the 256 MB "
+                         "last-level cache, between 2 and 64)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the calls as replays of a HIP graph that holds one call per "
+                         "input set (the streaming-pass time then comes from the same calls "
+                         "run eagerly right after)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stops", default="none", choices=["none", "varlen"],
@@ -246,8 +269,11 @@ def main():
     B, K, V = cfg.B, cfg.K, cfg.V
     s = cfg.elem_bytes
     gen_mode = "stochastic" if mode == "stochastic" else "greedy" if cfg.name != "c4" else mode
-    log(f"generating {args.sets} input set(s) for {cfg.name} {mode} B={B} K={K} V={V} {cfg.dtype}")
-    sets = [make_inputs(cfg, step, dev, gen_mode) for step in range(args.sets)]
+    read_rows = 2 * K + 1 if mode == "stochastic" else K + 1
+    set_bytes = B * read_rows * V * s
+    nsets = args.sets or max(2, min(64, -(-2 * MALL_BYTES // set_bytes)))
+    log(f"generating {nsets} input set(s) for {cfg.name} {mode} B={B} K={K} V={V} {cfg.dtype}")
+    sets = [make_inputs(cfg, step, dev, gen_mode) for step in range(nsets)]
     torch.cuda.synchronize()
 
     v = sv.SpecVerifier(B, K, V, cfg.torch_dtype, ema_decay=cfg.ema_decay)
@@ -291,20 +317,53 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    v.profile(True)
-    log(f"timing {args.steps} steps")
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    pass_ms, call_ms, ncalls = v.profile_read()
-    v.profile(False)
-    ms_step = ms_total / args.steps
+    if args.graph:
+        # one graph holding one call per input set, replayed; the library's
+        # own timing events stay out of the graph
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            for i in range(len(sets)):
+                step(i)
+        torch.cuda.current_stream(dev).wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(len(sets)):
+                step(i)
+        reps = max(1, -(-args.steps // len(sets)))
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        log(f"timing {reps} graph replays of {len(sets)} calls")
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_step = t0.elapsed_time(t1) / (reps * len(sets))
+        v.profile(True)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        pass_ms, call_ms, ncalls = v.profile_read()
+        v.profile(False)
+        args.steps = reps * len(sets)
+    else:
+        v.profile(True)
+        log(f"timing {args.steps} steps")
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        ms_total = t0.elapsed_time(t1)
+        pass_ms, call_ms, ncalls = v.profile_read()
+        v.profile(False)
+        ms_step = ms_total / args.steps
     pass_avg = pass_ms / max(1, ncalls)
 
     rows_total = int((2 * kb + 1).sum()) if mode == "stochastic" else int((kb + 1).sum())
@@ -339,7 +398,9 @@ def main():
                                + (", tree-shape policy" if args.policy else "")
                                + (f", draft residual m={args.residual}"
                                   if args.residual and mode == "stochastic" else ""),
-                   "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU"},
+                   "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU",
+                   "input_sets": len(sets), "input_bytes_rotated": int(set_bytes * len(sets)),
+                   "timing": "hip graph replays" if args.graph else "eager calls"},
         "achieved_hbm_gbs": round(call_bytes / (ms_step * 1e-3) / 1e9, 1),
         "frac_of_peak": round(call_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "algorithmic_bytes_per_step": int(call_bytes),
