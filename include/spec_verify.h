@@ -108,6 +108,8 @@ typedef struct spec_verify_stats {
  * Path selection and tuning are read from the environment here (for tests and
  * measurement; the defaults are the tuned ones):
  *   SPEC_VERIFY_TARGET_WGS       streaming-pass workgroups to aim for (2048)
+ *   SPEC_VERIFY_TARGET_WGS_MAX   the same for the argmax pass of greedy and
+ *                                margin calls (6144)
  *   SPEC_VERIFY_NSEG             fixed segments per row (0 = from the target)
  *   SPEC_VERIFY_FINISH_SEQ       0: stochastic draw as separate scan, tile-sum
  *                                and pick kernels instead of one workgroup per

@@ -78,6 +78,7 @@ struct spec_verify_handle {
   int topm_nseg = 0;                       // segments per row of this call's lists, 0 = none
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
+  int target_wgs_max = 6144;  // the same for the argmax pass (greedy, margin)
   int n_cu = 256;          // compute units of the device
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
   int trunc32_buf = 1;     // fp32 truncation: walk the digits over an LDS copy of the few candidates (0 = digit reads only)
@@ -110,7 +111,10 @@ int env_int(const char* name, int dflt) {
   return (s != nullptr && *s) ? atoi(s) : dflt;
 }
 
-Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
+// argmax: the max pass, which does less arithmetic per byte and finishes its
+// segments sooner; it is planned for more workgroups (about three rounds of
+// the resident ones) so that the last round's tail stays short
+Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U, bool argmax = false) {
   Launch L;
   L.vec = vec;
   const long long nchunks = h->V / vec;
@@ -120,7 +124,9 @@ Launch plan(const spec_verify_handle* h, int B, int rows, int vec, int U) {
   if (max_nseg > kMaxSeg) max_nseg = kMaxSeg;
   // with per-sequence draft counts some (row, segment) workgroups exit at
   // once; four times as many, shorter ones keep the other rows evenly spread
-  const long long target = (long long)h->target_wgs * (h->rules.k != nullptr ? 4 : 1);
+  const long long base = argmax ? h->target_wgs_max : h->target_wgs;
+  const long long target =
+      h->rules.k != nullptr ? std::max(base, 4ll * h->target_wgs) : base;
   int nseg = h->nseg_force > 0 ? h->nseg_force : div_up(target, (long long)B * rows);
   if (nseg > max_nseg) nseg = max_nseg;
   if (nseg < 1) nseg = 1;
@@ -405,6 +411,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   h->dtype = logits_dtype;
   h->decay = ema_decay;
   h->target_wgs = env_int("SPEC_VERIFY_TARGET_WGS", 2048);
+  h->target_wgs_max = env_int("SPEC_VERIFY_TARGET_WGS_MAX", 6144);
   h->nseg_force = env_int("SPEC_VERIFY_NSEG", 0);
   h->trunc32_buf = env_int("SPEC_VERIFY_TRUNC32_BUF", 1);
   h->trunc32_list = env_int("SPEC_VERIFY_TRUNC32_LIST", 1);
@@ -617,20 +624,20 @@ int verify_call(spec_verify_handle* h, int B, const void* target, const void* dr
     const int rows = h->K + 1;
     if (h->dtype == SV_DTYPE_BF16) {
       if (vec)
-        rc = run_argmax<sv::DT_BF16, 8, SV_U_MAX>(h, plan(h, B, rows, 8, SV_U_MAX), B, target,
+        rc = run_argmax<sv::DT_BF16, 8, SV_U_MAX>(h, plan(h, B, rows, 8, SV_U_MAX, true), B, target,
                                                   tokens, margin, invT, double(tau), out_tokens,
                                                   out_len, out_hist, stream);
       else
-        rc = run_argmax<sv::DT_BF16, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, tokens, margin,
+        rc = run_argmax<sv::DT_BF16, 1, 8>(h, plan(h, B, rows, 1, 8, true), B, target, tokens, margin,
                                            invT, double(tau), out_tokens, out_len, out_hist,
                                            stream);
     } else {
       if (vec)
-        rc = run_argmax<sv::DT_F32, 4, SV_U_MAX>(h, plan(h, B, rows, 4, SV_U_MAX), B, target,
+        rc = run_argmax<sv::DT_F32, 4, SV_U_MAX>(h, plan(h, B, rows, 4, SV_U_MAX, true), B, target,
                                                  tokens, margin, invT, double(tau), out_tokens,
                                                  out_len, out_hist, stream);
       else
-        rc = run_argmax<sv::DT_F32, 1, 8>(h, plan(h, B, rows, 1, 8), B, target, tokens, margin,
+        rc = run_argmax<sv::DT_F32, 1, 8>(h, plan(h, B, rows, 1, 8, true), B, target, tokens, margin,
                                           invT, double(tau), out_tokens, out_len, out_hist,
                                           stream);
     }
@@ -875,7 +882,7 @@ int spec_verify_noalloc(int B, int K, int V, int logits_dtype, const void* targe
   const int v = vec ? (logits_dtype == SV_DTYPE_BF16 ? 8 : 4) : 1;
   int U = 8;
   if (vec) U = !stoch ? SV_U_MAX : logits_dtype == SV_DTYPE_BF16 ? SV_U_BF16 : SV_U_F32;
-  const Launch L = plan(&h, B, rows, v, U);
+  const Launch L = plan(&h, B, rows, v, U, !stoch);
   if (stoch && (L.ntiles > sv::kFMaxTiles || rows > sv::kFMaxRows))
     return noalloc_fail(SV_EUNSUPPORTED,
                         "stochastic calls without allocation need V <= %d for this layout",
