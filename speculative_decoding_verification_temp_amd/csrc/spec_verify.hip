@@ -83,6 +83,7 @@ struct spec_verify_handle {
   int nseg_force = 0;      // fixed segment count (tuning), 0 = automatic
   int trunc32_buf = 1;     // fp32 truncation: walk the digits over an LDS copy of the few candidates (0 = digit reads only)
   int trunc32_list = 1;    // fp32 truncation: settle rows from one read's top-k list first (0 = off)
+  int trunc32_one = 1;     // fp32 truncation: rows with top-p alone in one read after the list pass (0 = off)
   char err[256] = {0};
 };
 
@@ -266,6 +267,13 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
                          dim3(sv::kT1Block), 0, s, target, draft, K, V, c, c64, 61 - lg,
                          h->trunc, h->rules.k, h->parts, hist);
       rc = check_launch(h, "rowstats_trunc32_list");
+      // rows with top-p alone (the list pass handed them over): one read each
+      if (rc == SV_OK && h->trunc32_one && h->trunc.p != nullptr) {
+        hipLaunchKernelGGL((sv::rowstats_trunc32_topp<VEC>), dim3(unsigned(B * rows)),
+                           dim3(sv::kTPBlock), 0, s, target, draft, K, V, c, c64, 61 - lg,
+                           h->trunc, h->rules.k, h->parts);
+        rc = check_launch(h, "rowstats_trunc32_topp");
+      }
     }
   }
   if (rc) return rc;
@@ -415,6 +423,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   h->nseg_force = env_int("SPEC_VERIFY_NSEG", 0);
   h->trunc32_buf = env_int("SPEC_VERIFY_TRUNC32_BUF", 1);
   h->trunc32_list = env_int("SPEC_VERIFY_TRUNC32_LIST", 1);
+  h->trunc32_one = env_int("SPEC_VERIFY_TRUNC32_ONE", 1);
   h->tiles_per_group = env_int("SPEC_VERIFY_TILES_PER_GROUP", 16);
   if (h->tiles_per_group < 1) h->tiles_per_group = 1;
   h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);

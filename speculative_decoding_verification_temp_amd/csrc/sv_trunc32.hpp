@@ -647,6 +647,301 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
 }
 
 // ---------------------------------------------------------------------------
+// Top-p alone in one read (16-byte chunks). With top-p alone the kept set is
+// not bounded in advance, but at the shapes this library serves it is a few
+// thousand tokens: a sample of the row (one slice of kT32Block chunks in
+// kT32SampleEvery, up to kT32SampleMax slices, held in registers) counted by
+// the first digit sets a cut such that the bins from the cut up should hold
+// about kT32SampleTarget values, and the row then streams once: its maximum,
+// non-finite values, the normaliser estimate (float terms whose exponent
+// carries c as two floats, summed in single precision over a lane's 16 values
+// and in float64 across groups, over a running reference: about 2e-7
+// relative), and every key at or above the cut copied into LDS (each copied
+// key's place from the wavefront's ballot of its value slot; one counter
+// update per wavefront and group). When no key was lost and the copy's exact
+// fixed-point masses reach top_p of the normaliser, the copy (a top part of
+// the row) holds the crossing and the three digit walks over it give the
+// level; the first digit is counted relative to the cut (kTPBins1 bins).
+// Otherwise the row stays marked kTruncRedo for the multi-read pass.
+// Small LDS arrays (about 48 KB) leave room for three workgroups per compute
+// unit; the multi-read pass holds two.
+// ---------------------------------------------------------------------------
+constexpr int kTPBlock = 512;
+constexpr int kTPWaves = kTPBlock / kWave;
+constexpr int kTPBins1 = 512;                    // first digit, from the cut up
+constexpr int kT32BufOne = 7168;                 // keys the copy holds
+constexpr int kT32SampleEvery = 16;
+constexpr int kT32SampleMax = 4;
+constexpr int kT32SampleTarget = 5000;
+
+struct TPWalk {
+  u64 red[kTPWaves];
+  uint32_t red32[kTPWaves];
+  int ired[kTPWaves];
+  u64 above;
+  int bin;
+};
+
+// The bin (of NB, NB = kTPBlock or a multiple) at which the sum from the top
+// first reaches goal, as t32_walk, over this kernel's workgroup.
+template <typename T, int NB>
+__device__ inline int tp_walk(const T* v, T goal, T& above, TPWalk& w) {
+  constexpr int BPT = NB / kTPBlock;
+  static_assert(BPT >= 1 && NB % kTPBlock == 0, "at least one bin per thread");
+  const int tid = threadIdx.x;
+  T own = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) own += v[tid * BPT + i];
+  T total;
+  T abv;
+  if constexpr (sizeof(T) == 8)
+    abv = tr_above<T, kTPWaves>(own, w.red, total);
+  else
+    abv = tr_above<T, kTPWaves>(own, w.red32, total);
+  const int cut = tr_max<kTPWaves>(abv + own >= goal ? tid : -1, w.ired);
+  if (tid == cut) {
+    T acc = abv;
+    for (int i = BPT - 1; i >= 0; --i) {
+      const T x = v[tid * BPT + i];
+      if (acc + x >= goal) {
+        w.bin = tid * BPT + i;
+        w.above = u64(acc);
+        break;
+      }
+      acc += x;
+    }
+  }
+  __syncthreads();
+  const int bin = cut >= 0 ? w.bin : -1;
+  above = cut >= 0 ? T(w.above) : total;
+  __syncthreads();
+  return bin;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
+    double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts) {
+  static_assert(VEC == 4, "the one-read route reads 16-byte chunks");
+  __shared__ uint32_t buf[kT32BufOne];   // sample counts by first digit, then the copy
+  __shared__ u64 m1[kTPBins1], m2[kT32Bins], m3[kT32Bins];
+  __shared__ uint32_t s_u[kTPWaves];
+  __shared__ uint32_t s_n;
+  __shared__ float s_rf[kTPWaves];
+  __shared__ double s_sd[kTPWaves];
+  __shared__ TPWalk w;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int rows = 2 * K + 1;
+  const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
+  if (kdraft != nullptr) {           // rows past the draft count are not needed
+    const int kb = kdraft[b];
+    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  }
+  const int kk = tr.k != nullptr ? tr.k[b] : 0;
+  const float pp = tr.p != nullptr ? tr.p[b] : 1.0f;
+  // top-p alone, valid: every other row is the other passes' (the list pass
+  // marked this one kTruncRedo)
+  if ((kk >= 1 && kk < V) || !(pp < 1.0f && pp > 0.0f)) return;
+  const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
+  const long long nchunks = V / VEC;
+  const double scale = __builtin_ldexp(1.0, fx);
+  const float c_lo = float(c64 - double(c));
+
+  for (int i = tid; i < kT32Bins1; i += kTPBlock) buf[i] = 0u;
+  if (tid == 0) s_n = 0u;
+  __syncthreads();
+
+  // A lane's group is 16 values (four chunks); values outside the row are
+  // -inf, whose key is below every cut and whose term is 0. kmax and kmin are
+  // the lane's largest and smallest keys: +inf and NaN lie outside
+  // [key(-inf), key(+inf)), so they show there.
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  float Ra = kRefInit;
+  double Sa = 0.0;
+  constexpr uint32_t kNegInfBits = 0xff800000u;
+  auto group = [&](const uint32_t (&v)[4][VEC], uint32_t (&key)[4][VEC]) {
+    uint32_t gmax = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        key[u][e] = order_key<DT_F32>(v[u][e]);
+        gmax = max(gmax, key[u][e]);
+        kmin = min(kmin, key[u][e]);
+      }
+    kmax = max(kmax, gmax);
+    // the reference follows the group's largest finite value (terms <= 1)
+    if (gmax > kKey32NegInf && gmax < kKey32PosInf) {
+      const float mx = order_floor<DT_F32>(gmax) * c;
+      if (mx > Ra) {
+        const float Rn = ceilf(mx);
+        Sa = rescale(Sa, Ra, Rn);
+        Ra = Rn;
+      }
+    }
+    // terms 2^(x c - R) with x c carried as two floats; the exponent is
+    // clamped at -126 (an -inf value, or one 2^126 below the reference, adds
+    // at most 2^-126: nothing at this precision)
+    float g = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float x = __uint_as_float(v[u][e]);
+        const float y = __builtin_fmaf(x, c_lo, __builtin_fmaf(x, c, -Ra));
+        g += __builtin_amdgcn_exp2f(fmaxf(y, -126.0f));
+      }
+    Sa += double(g);
+  };
+  // copy the keys of a group at or above the cut: each value slot's ballot
+  // gives its keys' places; one counter update per wavefront
+  auto copy = [&](const uint32_t (&key)[4][VEC], uint32_t cut_key) {
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) tot += uint32_t(__popcll(__ballot(key[u][e] >= cut_key)));
+    if (tot == 0u) return;
+    uint32_t base = 0u;
+    if (lane == 0) base = atomicAdd(&s_n, tot);
+    base = uint32_t(__shfl(int(base), 0, kWave));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const bool take = key[u][e] >= cut_key;
+        const unsigned long long m = __ballot(take);
+        if (take) {
+          const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(
+              uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+          if (pos < uint32_t(kT32BufOne)) buf[pos] = key[u][e];
+        }
+        base += uint32_t(__popcll(m));
+      }
+  };
+
+  // ---- the sample: slices 0, 16, 32, 48 of kTPBlock chunks ----
+  uint32_t sv[kT32SampleMax][VEC], sk[kT32SampleMax][VEC];
+  long long n_sampled = 0;
+#pragma unroll
+  for (int q = 0; q < kT32SampleMax; ++q) {
+    const long long s0 = (long long)kTPBlock * kT32SampleEvery * q;
+    const long long ci = s0 + tid;
+    n_sampled += max(0ll, min((long long)kTPBlock, nchunks - s0));
+    if (ci < nchunks) {
+      t32_load<VEC>(row, ci, sv[q]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sv[q][e] = kNegInfBits;
+    }
+  }
+  static_assert(kT32SampleMax == 4, "the sample is one group of four chunks");
+  group(sv, sk);
+#pragma unroll
+  for (int q = 0; q < kT32SampleMax; ++q) {
+    const bool in = (long long)kTPBlock * kT32SampleEvery * q + tid < nchunks;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (in) atomicAdd(&buf[sk[q][e] >> 20], 1u);
+  }
+  __syncthreads();
+  const uint32_t want = uint32_t((long long)kT32SampleTarget * n_sampled / nchunks) + 1u;
+  uint32_t abv1;
+  const int bx = tp_walk<uint32_t, kT32Bins1>(buf, want, abv1, w);
+  const uint32_t cut = bx >= 0 ? uint32_t(bx + 1) : 0u;   // (tp_walk ends with a barrier)
+  // keys of bins >= cut (a cut of 4096 keeps nothing), never -inf or padding
+  const uint32_t cut_key =
+      cut >= uint32_t(kT32Bins1) ? 0xffffffffu : max(cut << 20, kKey32NegInf + 1u);
+  copy(sk, cut_key);
+
+  // ---- the rest of the row, once: slices 4j + u, the sampled ones skipped;
+  // the loop runs while the wavefront's first chunk is in the row, so every
+  // lane takes part in the ballots ----
+  static_assert(kT32SampleEvery == 16, "a sampled slice opens every fourth group");
+  long long j = 0;
+  for (long long c0 = tid; c0 - lane < nchunks; c0 += 4ll * kTPBlock, ++j) {
+    const bool samp0 = (j % 4 == 0) && (j / 4 < kT32SampleMax);
+    uint32_t v[4][VEC], key[4][VEC];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long long ci = c0 + (long long)u * kTPBlock;
+      if (ci < nchunks && !(u == 0 && samp0)) {
+        t32_load<VEC>(row, ci, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[u][e] = kNegInfBits;
+      }
+    }
+    group(v, key);
+    copy(key, cut_key);
+  }
+  __syncthreads();
+
+  const uint32_t top = t32_max(kmax, s_u);
+  const uint32_t low = ~t32_max(~kmin, s_u);
+  const bool bad = top >= kKey32PosInf || top <= kKey32NegInf || low < kKey32NegInf;
+  if (bad) return;                   // the multi-read pass reports the row
+  const float R = ceilf(order_floor<DT_F32>(top) * c);
+  const float Rw = wave_max(Ra);
+  const double Sw = wave_sum(rescale(Sa, Ra, Rw));
+  if (lane == 0) {
+    s_rf[wid] = Rw;
+    s_sd[wid] = Sw;
+  }
+  __syncthreads();
+  double S_all = 0.0;
+#pragma unroll
+  for (int q = 0; q < kTPWaves; ++q) S_all += rescale(s_sd[q], s_rf[q], R);
+  const u64 goal = max(u64(__builtin_ceil(double(pp) * S_all * scale)), 1ull);
+  const int n = int(s_n);
+  const uint32_t topb = top >> 20;
+  if (n > kT32BufOne || topb < cut || topb - cut >= uint32_t(kTPBins1)) return;
+
+  // ---- the three digit walks over the copy ----
+  for (int i = tid; i < kTPBins1; i += kTPBlock) m1[i] = 0ull;
+  for (int i = tid; i < kT32Bins; i += kTPBlock) m2[i] = m3[i] = 0ull;
+  __syncthreads();
+  for (int i = tid; i < n; i += kTPBlock) {
+    const uint32_t key = buf[i];
+    atomicAdd(&m1[(key >> 20) - cut], fixed_term(order_floor<DT_F32>(key), c64, R, scale));
+  }
+  __syncthreads();
+  u64 a1, a2, a3;
+  const int q1 = tp_walk<u64, kTPBins1>(m1, goal, a1, w);
+  if (q1 < 0) return;                // the copy's mass stays below the goal
+  const uint32_t d1 = uint32_t(q1) + cut;
+  for (int i = tid; i < n; i += kTPBlock) {
+    const uint32_t key = buf[i];
+    if ((key >> 20) == d1)
+      atomicAdd(&m2[(key >> 10) & uint32_t(kT32Bins - 1)],
+                fixed_term(order_floor<DT_F32>(key), c64, R, scale));
+  }
+  __syncthreads();
+  const int q2 = tp_walk<u64, kT32Bins>(m2, goal - a1, a2, w);
+  if (q2 < 0) return;
+  const uint32_t sel = (d1 << 10) | uint32_t(q2);
+  for (int i = tid; i < n; i += kTPBlock) {
+    const uint32_t key = buf[i];
+    if ((key >> 10) == sel)
+      atomicAdd(&m3[key & uint32_t(kT32Bins - 1)],
+                fixed_term(order_floor<DT_F32>(key), c64, R, scale));
+  }
+  __syncthreads();
+  const int q3 = tp_walk<u64, kT32Bins>(m3, goal - a1 - a2, a3, w);
+  if (q3 < 0) return;
+  if (tid == 0) {
+    RowPart p;
+    p.S = __builtin_ldexp(double(a1 + a2 + a3 + m3[q3]), -fx);
+    p.R = R;
+    p.m = 0.0f;
+    p.idx = int((sel << 10) | uint32_t(q3));
+    p.flags = 0;
+    parts[blockIdx.x] = p;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // List pass (16-byte chunks): one read of the row settles most rows. A
 // 256-thread workgroup keeps the row's top k + 1 token keys in the top-m
 // candidate lists of sv_topm.hpp while it forms, in the same read, the row's

@@ -37,8 +37,8 @@ EXCUSED_FRACTION = 0.10
 REPORTS: list = []          # one dict per compare() call, in call order
 
 
-def excused_ceiling(rows: int) -> float:
-    mean = EXCUSED_FRACTION * rows
+def excused_ceiling(rows: int, fraction: float = EXCUSED_FRACTION) -> float:
+    mean = fraction * rows
     return mean + 3.0 * math.sqrt(mean) + 3.0
 
 
@@ -93,9 +93,13 @@ def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int 
     return _merge(parts)
 
 
-def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
+def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label="",
+            excused_fraction: float = EXCUSED_FRACTION):
     """Compare GPU outputs (full-batch tensors) on `rows` against oracle
-    results for the same rows. Returns a small report dict."""
+    results for the same rows. Returns a small report dict. A test whose
+    inputs put many decisions near their boundaries by construction (top_p
+    close to 1, where the masses of the value levels at the cut are about
+    1e-6 apart) passes the share it expects as excused_fraction."""
     rows = np.asarray(rows, dtype=np.int64)
     g_tok = tokens.cpu().numpy()[rows].astype(np.int64)
     g_len = accept_len.cpu().numpy()[rows].astype(np.int64)
@@ -117,9 +121,10 @@ def compare(rows, ref, tokens, accept_len, mode: str, aux=None, label=""):
         report["mismatches"] < MISMATCH_RATE * report["decisions"], (
         f"{label}: {report['mismatches']} excused mismatches in {report['decisions']} "
         f"decisions (must be under {MISMATCH_RATE:g} of them)")
-    assert report["near_boundary"] <= excused_ceiling(len(rows)), (
+    ceiling = excused_ceiling(len(rows), excused_fraction)
+    assert report["near_boundary"] <= ceiling, (
         f"{label}: {report['near_boundary']} of {len(rows)} rows within {BOUNDARY:g} of a "
-        f"boundary (ceiling {excused_ceiling(len(rows)):.1f})")
+        f"boundary (ceiling {ceiling:.1f})")
     if aux is not None:
         valid = ref.accept_len >= 0
         if mode in ("stochastic", "margin"):

@@ -71,7 +71,7 @@ def _run(sv, x, cfg, tk, tp, stops=None, decay=0.9, T=None):
     return v, aux, tok, alen, hist
 
 
-def _check(sv, x, cfg, tk, tp, label, stops=None, T=None, rows=None):
+def _check(sv, x, cfg, tk, tp, label, stops=None, T=None, rows=None, excused_fraction=None):
     v, aux, tok, alen, hist = _run(sv, x, cfg, tk, tp, stops=stops, T=T)
     xT = dict(x)
     if T is not None:
@@ -79,7 +79,8 @@ def _check(sv, x, cfg, tk, tp, label, stops=None, T=None, rows=None):
     rows = np.arange(cfg.B) if rows is None else np.asarray(rows)
     ema = O.EmaState(cfg.B, 0.9)
     ref = oracle_for(xT, rows, "stochastic", ema=ema, stops=stops, trunc=(tk, tp))
-    rep = compare(rows, ref, tok, alen, "stochastic", aux, label)
+    kw = {} if excused_fraction is None else dict(excused_fraction=excused_fraction)
+    rep = compare(rows, ref, tok, alen, "stochastic", aux, label, **kw)
     if len(rows) == cfg.B:
         assert np.array_equal(hist.cpu().numpy(), ref.hist)
         e, s = v.ema()

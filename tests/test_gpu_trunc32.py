@@ -32,12 +32,14 @@ DEV = torch.device("cuda", 0)
 SMALL = CONFIGS["c5"].scaled(B=48, V=20000)
 
 
-@pytest.fixture(params=["list", "buffered", "digits"])
+@pytest.fixture(params=["list", "list-multi", "buffered", "digits"])
 def route(request, monkeypatch):
     """The truncation passes' route, read when a verifier is created: the
-    one-read list pass first (rows it cannot settle then take the buffered
-    route), the buffered route alone, or the digit reads alone."""
-    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_LIST", "1" if request.param == "list" else "0")
+    one-read list pass and the one-read top-p pass first (rows they cannot
+    settle then take the buffered route), the list pass without the top-p
+    pass, the buffered route alone, or the digit reads alone."""
+    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_LIST", "1" if request.param.startswith("list") else "0")
+    monkeypatch.setenv("SPEC_VERIFY_TRUNC32_ONE", "0" if request.param == "list-multi" else "1")
     monkeypatch.setenv("SPEC_VERIFY_TRUNC32_BUF", "0" if request.param == "digits" else "1")
     return request.param
 
@@ -238,6 +240,34 @@ def test_trunc32_c5_sampled(sv, route):
     tp = np.full(cfg.B, 0.9, np.float32)
     rows = np.random.default_rng(38).choice(cfg.B, 24, replace=False)
     _check(sv, x, cfg, tk, tp, f"trunc32/c5 sampled/{route}", rows=np.sort(rows))
+
+
+@pytest.mark.parametrize("route", ["list", "list-multi"], indirect=True)
+def test_trunc32_top_p_alone_one_read_and_fallback(sv, route):
+    """Top-p alone at the c5 vocabulary (V = 128256): the one-read route copies
+    the keys above a sampled cut while the row streams; with top_p = 0.5 and
+    0.9 the crossing lies in the copy, with 0.999 the kept set (tens of
+    thousands of tokens) overflows it and the row falls back to the mass
+    reads. Every sequence against the oracle. At top_p = 0.999 the masses of
+    the value levels at the cut are about 1e-6 apart, so nearly every such
+    row's cut lies within 1e-6 of moving: a third of the rows are expected in
+    the excuse band (mismatches must still be none)."""
+    cfg = CONFIGS["c5"].scaled(B=24, K=2)
+    x = make_inputs(cfg, 9, DEV)
+    tp = np.tile(np.array([0.5, 0.9, 0.999], np.float32), cfg.B // 3)
+    tk = np.zeros(cfg.B, np.int32)
+    _resample_drafts(x, cfg.T, tk, tp, 25)
+    _check(sv, x, cfg, None, tp, f"trunc32/top-p alone/{route}", excused_fraction=0.45)
+
+
+def test_trunc32_c5_top_p_alone_sampled(sv):
+    """The c5 shape with top_p = 0.9 alone on every sequence (the one-read
+    route); the oracle checks 24 sampled sequences."""
+    cfg = CONFIGS["c5"]
+    x = make_inputs(cfg, 0, DEV)
+    tp = np.full(cfg.B, 0.9, np.float32)
+    rows = np.random.default_rng(39).choice(cfg.B, 24, replace=False)
+    _check(sv, x, cfg, None, tp, "trunc32/c5 top-p alone sampled", rows=np.sort(rows))
 
 
 def test_trunc32_candidates_beyond_buffer(sv):
