@@ -282,15 +282,30 @@ __device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, ui
       if (RAGGED && c0 + (long long)k * kWave >= nchunks) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        double et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, Tt);
-        if (MASK && order_key<DT_F32>(u.a[k][q]) < thr_t) et = 0.0;
-        if constexpr (RESID) {
-          double ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, Tt);
-          if (MASK && order_key<DT_F32>(u.d[k][q]) < thr_d) ed = 0.0;
-          accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
+        double et = 0.0, ed = 0.0;
+        if constexpr (MASK) {
+          // a term is formed only in value slots where some lane keeps one
+          // (few with top-p: its kept values lie scattered over the row)
+          const bool kt = order_key<DT_F32>(u.a[k][q]) >= thr_t;
+          if (__any(kt)) {
+            et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, Tt);
+            if (!kt) et = 0.0;
+          }
+          if constexpr (RESID) {
+            const bool kd = order_key<DT_F32>(u.d[k][q]) >= thr_d;
+            if (__any(kd)) {
+              ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, Tt);
+              if (!kd) ed = 0.0;
+            }
+          }
         } else {
-          E += et;
+          et = exp2_tab(double(__uint_as_float(u.a[k][q])) * c, Tt);
+          if constexpr (RESID) ed = exp2_tab(double(__uint_as_float(u.d[k][q])) * c, Tt);
         }
+        if constexpr (RESID)
+          accum_pair_u(et, ed, rho2, E, Ed, A, Bd);
+        else
+          E += et;
       }
     }
     return;

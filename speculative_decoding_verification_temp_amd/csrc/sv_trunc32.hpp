@@ -663,13 +663,14 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
 // the row) holds the crossing and the three digit walks over it give the
 // level; the first digit is counted relative to the cut (kTPBins1 bins).
 // Otherwise the row stays marked kTruncRedo for the multi-read pass.
-// Small LDS arrays (about 48 KB) leave room for three workgroups per compute
-// unit; the multi-read pass holds two.
+// Small LDS arrays (40 KB: the third digit's masses reuse the second's) and
+// at most 80 registers give three workgroups per compute unit; the
+// multi-read pass holds two. (Four, at 64 registers, spill and run slower.)
 // ---------------------------------------------------------------------------
 constexpr int kTPBlock = 512;
 constexpr int kTPWaves = kTPBlock / kWave;
 constexpr int kTPBins1 = 512;                    // first digit, from the cut up
-constexpr int kT32BufOne = 7168;                 // keys the copy holds
+constexpr int kT32BufOne = 7040;                 // keys the copy holds
 constexpr int kT32SampleEvery = 16;
 constexpr int kT32SampleMax = 4;
 constexpr int kT32SampleTarget = 5000;
@@ -725,7 +726,8 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
     RowPart* __restrict__ parts) {
   static_assert(VEC == 4, "the one-read route reads 16-byte chunks");
   __shared__ uint32_t buf[kT32BufOne];   // sample counts by first digit, then the copy
-  __shared__ u64 m1[kTPBins1], m2[kT32Bins], m3[kT32Bins];
+  __shared__ u64 m1[kTPBins1], m2[kT32Bins];    // the third digit reuses m2
+  u64* const m3 = m2;
   __shared__ uint32_t s_u[kTPWaves];
   __shared__ uint32_t s_n;
   __shared__ float s_rf[kTPWaves];
@@ -743,8 +745,16 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   // top-p alone, valid: every other row is the other passes' (the list pass
   // marked this one kTruncRedo)
   if ((kk >= 1 && kk < V) || !(pp < 1.0f && pp > 0.0f)) return;
-  const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
-  const long long nchunks = V / VEC;
+  // the row's base comes from the arguments and the workgroup index (the
+  // same in every lane); chunks are indexed with 32-bit offsets (a row holds
+  // fewer than 2^27 chunks)
+  const u32x4* row4 = static_cast<const u32x4*>(row_ptr<DT_F32>(target, draft, b, r, K, V));
+  auto load4 = [&](int ci, uint32_t (&v)[VEC]) {
+    const u32x4 q = row4[ci];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = q[e];
+  };
+  const int nchunks = V / VEC;        // (a row holds fewer than 2^31 chunks)
   const double scale = __builtin_ldexp(1.0, fx);
   const float c_lo = float(c64 - double(c));
 
@@ -760,25 +770,21 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   float Ra = kRefInit;
   double Sa = 0.0;
   constexpr uint32_t kNegInfBits = 0xff800000u;
-  auto group = [&](const uint32_t (&v)[4][VEC], uint32_t (&key)[4][VEC]) {
-    uint32_t gmax = 0u;
+  // the group's values v become their keys
+  auto group = [&](uint32_t (&v)[4][VEC]) {
+    // the reference follows the group's largest value (terms <= 1); NaN is
+    // passed over here and +inf makes a reference no term uses: both mark
+    // the row bad through the keys below
+    float fmx = -__builtin_inff();
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        key[u][e] = order_key<DT_F32>(v[u][e]);
-        gmax = max(gmax, key[u][e]);
-        kmin = min(kmin, key[u][e]);
-      }
-    kmax = max(kmax, gmax);
-    // the reference follows the group's largest finite value (terms <= 1)
-    if (gmax > kKey32NegInf && gmax < kKey32PosInf) {
-      const float mx = order_floor<DT_F32>(gmax) * c;
-      if (mx > Ra) {
-        const float Rn = ceilf(mx);
-        Sa = rescale(Sa, Ra, Rn);
-        Ra = Rn;
-      }
+      for (int e = 0; e < VEC; ++e) fmx = fmaxf(fmx, __uint_as_float(v[u][e]));
+    const float mx = fmx * c;
+    if (mx > Ra) {
+      const float Rn = ceilf(mx);
+      Sa = rescale(Sa, Ra, Rn);
+      Ra = Rn;
     }
     // terms 2^(x c - R) with x c carried as two floats; the exponent is
     // clamped at -126 (an -inf value, or one 2^126 below the reference, adds
@@ -793,6 +799,14 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
         g += __builtin_amdgcn_exp2f(fmaxf(y, -126.0f));
       }
     Sa += double(g);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        v[u][e] = order_key<DT_F32>(v[u][e]);
+        kmax = max(kmax, v[u][e]);
+        kmin = min(kmin, v[u][e]);
+      }
   };
   // copy the keys of a group at or above the cut: each value slot's ballot
   // gives its keys' places; one counter update per wavefront
@@ -822,25 +836,25 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   };
 
   // ---- the sample: slices 0, 16, 32, 48 of kTPBlock chunks ----
-  uint32_t sv[kT32SampleMax][VEC], sk[kT32SampleMax][VEC];
-  long long n_sampled = 0;
+  uint32_t sk[kT32SampleMax][VEC];     // the sample's values, then their keys
+  int n_sampled = 0;
 #pragma unroll
   for (int q = 0; q < kT32SampleMax; ++q) {
-    const long long s0 = (long long)kTPBlock * kT32SampleEvery * q;
-    const long long ci = s0 + tid;
-    n_sampled += max(0ll, min((long long)kTPBlock, nchunks - s0));
+    const int s0 = kTPBlock * kT32SampleEvery * q;
+    const int ci = s0 + tid;
+    n_sampled += max(0, min(kTPBlock, nchunks - s0));
     if (ci < nchunks) {
-      t32_load<VEC>(row, ci, sv[q]);
+      load4(ci, sk[q]);
     } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) sv[q][e] = kNegInfBits;
+      for (int e = 0; e < VEC; ++e) sk[q][e] = kNegInfBits;
     }
   }
   static_assert(kT32SampleMax == 4, "the sample is one group of four chunks");
-  group(sv, sk);
+  group(sk);
 #pragma unroll
   for (int q = 0; q < kT32SampleMax; ++q) {
-    const bool in = (long long)kTPBlock * kT32SampleEvery * q + tid < nchunks;
+    const bool in = kTPBlock * kT32SampleEvery * q + tid < nchunks;
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
       if (in) atomicAdd(&buf[sk[q][e] >> 20], 1u);
@@ -859,22 +873,22 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   // the loop runs while the wavefront's first chunk is in the row, so every
   // lane takes part in the ballots ----
   static_assert(kT32SampleEvery == 16, "a sampled slice opens every fourth group");
-  long long j = 0;
-  for (long long c0 = tid; c0 - lane < nchunks; c0 += 4ll * kTPBlock, ++j) {
+  int j = 0;
+  for (int c0 = tid; c0 - lane < nchunks; c0 += 4 * kTPBlock, ++j) {
     const bool samp0 = (j % 4 == 0) && (j / 4 < kT32SampleMax);
-    uint32_t v[4][VEC], key[4][VEC];
+    uint32_t v[4][VEC];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const long long ci = c0 + (long long)u * kTPBlock;
+      const int ci = c0 + u * kTPBlock;
       if (ci < nchunks && !(u == 0 && samp0)) {
-        t32_load<VEC>(row, ci, v[u]);
+        load4(ci, v[u]);
       } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[u][e] = kNegInfBits;
       }
     }
-    group(v, key);
-    copy(key, cut_key);
+    group(v);
+    copy(v, cut_key);
   }
   __syncthreads();
 
@@ -900,7 +914,7 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
 
   // ---- the three digit walks over the copy ----
   for (int i = tid; i < kTPBins1; i += kTPBlock) m1[i] = 0ull;
-  for (int i = tid; i < kT32Bins; i += kTPBlock) m2[i] = m3[i] = 0ull;
+  for (int i = tid; i < kT32Bins; i += kTPBlock) m2[i] = 0ull;
   __syncthreads();
   for (int i = tid; i < n; i += kTPBlock) {
     const uint32_t key = buf[i];
@@ -921,6 +935,8 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   const int q2 = tp_walk<u64, kT32Bins>(m2, goal - a1, a2, w);
   if (q2 < 0) return;
   const uint32_t sel = (d1 << 10) | uint32_t(q2);
+  for (int i = tid; i < kT32Bins; i += kTPBlock) m3[i] = 0ull;   // (tp_walk ended with a barrier)
+  __syncthreads();
   for (int i = tid; i < n; i += kTPBlock) {
     const uint32_t key = buf[i];
     if ((key >> 10) == sel)
