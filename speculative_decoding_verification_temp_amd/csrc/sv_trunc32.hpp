@@ -649,31 +649,35 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
 // ---------------------------------------------------------------------------
 // Top-p alone in one read (16-byte chunks). With top-p alone the kept set is
 // not bounded in advance, but at the shapes this library serves it is a few
-// thousand tokens: a sample of the row (one slice of kT32Block chunks in
-// kT32SampleEvery, up to kT32SampleMax slices, held in registers) counted by
-// the first digit sets a cut such that the bins from the cut up should hold
-// about kT32SampleTarget values, and the row then streams once: its maximum,
-// non-finite values, the normaliser estimate (float terms whose exponent
-// carries c as two floats, summed in single precision over a lane's 16 values
-// and in float64 across groups, over a running reference: about 2e-7
-// relative), and every key at or above the cut copied into LDS (each copied
-// key's place from the wavefront's ballot of its value slot; one counter
-// update per wavefront and group). When no key was lost and the copy's exact
-// fixed-point masses reach top_p of the normaliser, the copy (a top part of
-// the row) holds the crossing and the three digit walks over it give the
-// level; the first digit is counted relative to the cut (kTPBins1 bins).
-// Otherwise the row stays marked kTruncRedo for the multi-read pass.
-// Small LDS arrays (40 KB: the third digit's masses reuse the second's) and
-// at most 80 registers give three workgroups per compute unit; the
-// multi-read pass holds two. (Four, at 64 registers, spill and run slower.)
+// thousand tokens: a sample of the row (one slice of kTPBlock chunks in
+// kT32SampleEvery, up to kT32SampleMax slices) counted by the first digit of
+// the order key sets a cut, the lower edge of the bin in which the count from
+// the top reaches about kT32SampleTarget values of the whole row, and the rest
+// of the row then streams once (the sampled slices are not read again). The
+// stream forms the row's largest value, the normaliser estimate (float terms
+// whose exponent carries c as two floats, c_hi <= c and c_lo = c - c_hi > 0,
+// summed in single precision over a lane's 16 values and in float64 across
+// groups, over a running reference: about 2e-7 relative) and copies into LDS
+// every value at or above the cut: a float compare against the least value of
+// the cut's bin (exact for a normal cut value; a cut at zero or a subnormal
+// value leaves the row to the multi-read pass), each copied value placed by
+// its value slot's ballot, one counter update per wavefront and group. A NaN
+// makes the sum NaN and +inf the maximum infinite (and the sum NaN): either
+// hands the row over. When no value was lost and the copy's exact fixed-point
+// masses reach top_p of the normaliser, the copy (a top part of the row) holds
+// the crossing and three digit walks over its keys give the level; the first
+// digit is counted relative to the cut (kTPBins1 bins). Otherwise the row
+// stays marked kTruncRedo for the multi-read pass.
+// 53 KB of LDS (the third digit's masses reuse the second's) and at most 80
+// registers give three workgroups per compute unit.
 // ---------------------------------------------------------------------------
 constexpr int kTPBlock = 512;
 constexpr int kTPWaves = kTPBlock / kWave;
 constexpr int kTPBins1 = 512;                    // first digit, from the cut up
-constexpr int kT32BufOne = 7040;                 // keys the copy holds
+constexpr int kT32BufOne = 10112;                // values the copy holds
 constexpr int kT32SampleEvery = 16;
 constexpr int kT32SampleMax = 4;
-constexpr int kT32SampleTarget = 5000;
+constexpr int kT32SampleTarget = 6000;
 
 struct TPWalk {
   u64 red[kTPWaves];
@@ -725,6 +729,7 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
     double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts) {
   static_assert(VEC == 4, "the one-read route reads 16-byte chunks");
+  static_assert(kT32SampleMax == 4, "the sample is one group of four slices");
   __shared__ uint32_t buf[kT32BufOne];   // sample counts by first digit, then the copy
   __shared__ u64 m1[kTPBins1], m2[kT32Bins];    // the third digit reuses m2
   u64* const m3 = m2;
@@ -749,154 +754,191 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   // same in every lane); chunks are indexed with 32-bit offsets (a row holds
   // fewer than 2^27 chunks)
   const u32x4* row4 = static_cast<const u32x4*>(row_ptr<DT_F32>(target, draft, b, r, K, V));
-  auto load4 = [&](int ci, uint32_t (&v)[VEC]) {
-    const u32x4 q = row4[ci];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) v[e] = q[e];
-  };
-  const int nchunks = V / VEC;        // (a row holds fewer than 2^31 chunks)
+  const int nchunks = V / VEC;
   const double scale = __builtin_ldexp(1.0, fx);
-  const float c_lo = float(c64 - double(c));
+  // c = c_hi + c_lo with c_hi rounded toward zero, so c_lo >= 0; c_lo is kept
+  // at least 2^-126 so that -inf times it stays -inf (never NaN), which adds
+  // at most x 2^-126 to a finite exponent x c: nothing at this precision
+  float c_hi = float(c64);
+  if (double(c_hi) > c64) c_hi = __uint_as_float(__float_as_uint(c_hi) - 1u);
+  const float c_lo = fmaxf(float(c64 - double(c_hi)), 0x1p-126f);
 
   for (int i = tid; i < kT32Bins1; i += kTPBlock) buf[i] = 0u;
   if (tid == 0) s_n = 0u;
   __syncthreads();
 
   // A lane's group is 16 values (four chunks); values outside the row are
-  // -inf, whose key is below every cut and whose term is 0. kmax and kmin are
-  // the lane's largest and smallest keys: +inf and NaN lie outside
-  // [key(-inf), key(+inf)), so they show there.
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  // -inf, whose term is 0 and which no cut keeps.
+  float fmax_l = -__builtin_inff();     // the lane's largest value (NaN passed over)
   float Ra = kRefInit;
   double Sa = 0.0;
   constexpr uint32_t kNegInfBits = 0xff800000u;
-  // the group's values v become their keys
-  auto group = [&](uint32_t (&v)[4][VEC]) {
-    // the reference follows the group's largest value (terms <= 1); NaN is
-    // passed over here and +inf makes a reference no term uses: both mark
-    // the row bad through the keys below
-    float fmx = -__builtin_inff();
+  auto sums = [&](const uint32_t (&v)[4][VEC]) {
+    // the reference follows the group's largest value (terms <= 1)
+    float fmx = __uint_as_float(v[0][0]);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) fmx = fmaxf(fmx, __uint_as_float(v[u][e]));
-    const float mx = fmx * c;
+      for (int e = (u == 0 ? 1 : 0); e < VEC; ++e) fmx = fmaxf(fmx, __uint_as_float(v[u][e]));
+    fmax_l = fmaxf(fmax_l, fmx);
+    const float mx = fmx * c_hi;
     if (mx > Ra) {
       const float Rn = ceilf(mx);
       Sa = rescale(Sa, Ra, Rn);
       Ra = Rn;
     }
-    // terms 2^(x c - R) with x c carried as two floats; the exponent is
-    // clamped at -126 (an -inf value, or one 2^126 below the reference, adds
-    // at most 2^-126: nothing at this precision)
+    // terms 2^(x c - R) with x c carried as two floats; -inf adds 0, NaN
+    // makes the sum NaN
     float g = 0.0f;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float x = __uint_as_float(v[u][e]);
-        const float y = __builtin_fmaf(x, c_lo, __builtin_fmaf(x, c, -Ra));
-        g += __builtin_amdgcn_exp2f(fmaxf(y, -126.0f));
+        g += __builtin_amdgcn_exp2f(__builtin_fmaf(x, c_lo, __builtin_fmaf(x, c_hi, -Ra)));
       }
     Sa += double(g);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        v[u][e] = order_key<DT_F32>(v[u][e]);
-        kmax = max(kmax, v[u][e]);
-        kmin = min(kmin, v[u][e]);
-      }
   };
-  // copy the keys of a group at or above the cut: each value slot's ballot
-  // gives its keys' places; one counter update per wavefront
-  auto copy = [&](const uint32_t (&key)[4][VEC], uint32_t cut_key) {
+  // copy the values of a group at or above cut_f: each value slot's ballot
+  // gives its values' places; one counter update per wavefront. A group that
+  // would pass the end of the copy is not written (the count still grows, and
+  // the row is handed over).
+  auto copy = [&](const uint32_t (&v)[4][VEC], float cut_f) {
+    unsigned long long mk[4][VEC];     // each slot's ballot, taken once
     uint32_t tot = 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) tot += uint32_t(__popcll(__ballot(key[u][e] >= cut_key)));
+      for (int e = 0; e < VEC; ++e) {
+        mk[u][e] = __ballot(__uint_as_float(v[u][e]) >= cut_f);
+        tot += uint32_t(__popcll(mk[u][e]));
+      }
     if (tot == 0u) return;
     uint32_t base = 0u;
     if (lane == 0) base = atomicAdd(&s_n, tot);
-    base = uint32_t(__shfl(int(base), 0, kWave));
+    base = uint32_t(__builtin_amdgcn_readfirstlane(int(base)));
+    if (base + tot > uint32_t(kT32BufOne)) return;
+    uint32_t base4 = base * 4u;        // byte offsets: one shift-add per slot
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const bool take = key[u][e] >= cut_key;
-        const unsigned long long m = __ballot(take);
-        if (take) {
-          const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(
+        const unsigned long long m = mk[u][e];
+        if (__uint_as_float(v[u][e]) >= cut_f) {
+          const uint32_t at = __builtin_amdgcn_mbcnt_hi(
               uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
-          if (pos < uint32_t(kT32BufOne)) buf[pos] = key[u][e];
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(buf) + (base4 + (at << 2))) =
+              v[u][e];
         }
-        base += uint32_t(__popcll(m));
+        base4 += uint32_t(__popcll(m)) * 4u;
       }
   };
 
+  // The slices in order, the sampled ones skipped (non-sampled slice vs is
+  // slice vs + 1 + min(3, vs / 15)), four to a group: whole groups of whole
+  // slices first, then the remainder (at most three whole slices and the
+  // partial last one) as one group.
+  const int nsl = (nchunks + kTPBlock - 1) / kTPBlock;
+  const int nfull = nchunks / kTPBlock;
+  const int nsamp = min(kT32SampleMax, (nsl + kT32SampleEvery - 1) / kT32SampleEvery);
+  const int nv = nsl - nsamp;
+  auto slice_of = [](int vs) {
+    return vs + 1 + min(kT32SampleMax - 1, vs / (kT32SampleEvery - 1));
+  };
+  auto whole = [&](int g) { return g + 3 < nv && slice_of(g + 3) < nfull; };
+  // chunk indexes past the row are clamped to its last chunk (loaded, not used)
+  auto load_group = [&](int g, uint32_t (&v)[4][VEC]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 x = row4[min(slice_of(g + u) * kTPBlock + tid, nchunks - 1)];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[u][e] = x[e];
+    }
+  };
+
   // ---- the sample: slices 0, 16, 32, 48 of kTPBlock chunks ----
-  uint32_t sk[kT32SampleMax][VEC];     // the sample's values, then their keys
+  uint32_t sk[kT32SampleMax][VEC];
   int n_sampled = 0;
 #pragma unroll
   for (int q = 0; q < kT32SampleMax; ++q) {
     const int s0 = kTPBlock * kT32SampleEvery * q;
-    const int ci = s0 + tid;
     n_sampled += max(0, min(kTPBlock, nchunks - s0));
-    if (ci < nchunks) {
-      load4(ci, sk[q]);
-    } else {
+    const u32x4 x = row4[min(s0 + tid, nchunks - 1)];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) sk[q][e] = x[e];
+  }
+#pragma unroll
+  for (int q = 0; q < kT32SampleMax; ++q)
+    if (kTPBlock * kT32SampleEvery * q + tid >= nchunks) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) sk[q][e] = kNegInfBits;
     }
-  }
-  static_assert(kT32SampleMax == 4, "the sample is one group of four chunks");
-  group(sk);
+  sums(sk);
 #pragma unroll
   for (int q = 0; q < kT32SampleMax; ++q) {
     const bool in = kTPBlock * kT32SampleEvery * q + tid < nchunks;
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
-      if (in) atomicAdd(&buf[sk[q][e] >> 20], 1u);
+      if (in) atomicAdd(&buf[order_key<DT_F32>(sk[q][e]) >> 20], 1u);
   }
   __syncthreads();
   const uint32_t want = uint32_t((long long)kT32SampleTarget * n_sampled / nchunks) + 1u;
   uint32_t abv1;
   const int bx = tp_walk<uint32_t, kT32Bins1>(buf, want, abv1, w);
-  const uint32_t cut = bx >= 0 ? uint32_t(bx + 1) : 0u;   // (tp_walk ends with a barrier)
-  // keys of bins >= cut (a cut of 4096 keeps nothing), never -inf or padding
-  const uint32_t cut_key =
-      cut >= uint32_t(kT32Bins1) ? 0xffffffffu : max(cut << 20, kKey32NegInf + 1u);
-  copy(sk, cut_key);
+  // the copy starts at the bin in which the sample's count reaches want (at
+  // bin 0 when it never does); never at -inf or below
+  const uint32_t cut = bx >= 0 ? uint32_t(bx) : 0u;   // (tp_walk ends with a barrier)
+  const uint32_t cut_key = max(cut << 20, kKey32NegInf + 1u);
+  const float cut_f = order_floor<DT_F32>(cut_key);
+  // a cut at zero or at a subnormal value: the float compare and the key
+  // order could part there, so the multi-read pass takes the row
+  if (!(fabsf(cut_f) >= 0x1p-126f)) return;
+  copy(sk, cut_f);
 
-  // ---- the rest of the row, once: slices 4j + u, the sampled ones skipped;
-  // the loop runs while the wavefront's first chunk is in the row, so every
-  // lane takes part in the ballots ----
-  static_assert(kT32SampleEvery == 16, "a sampled slice opens every fourth group");
-  int j = 0;
-  for (int c0 = tid; c0 - lane < nchunks; c0 += 4 * kTPBlock, ++j) {
-    const bool samp0 = (j % 4 == 0) && (j / 4 < kT32SampleMax);
+  // ---- the rest of the row, once ----
+  int vs = 0;
+  // whole groups two at a time, the next group's loads issued before this
+  // group's arithmetic (after the last whole group, this group's again: the
+  // loads are unconditional, so every wait count stays exact)
+  if (whole(0)) {
+    uint32_t va[4][VEC], vb[4][VEC];
+    load_group(0, va);
+    for (;;) {
+      const bool nb = whole(vs + 4);
+      load_group(nb ? vs + 4 : vs, vb);
+      sums(va);
+      copy(va, cut_f);
+      vs += 4;
+      if (!nb) break;
+      const bool na = whole(vs + 4);
+      load_group(na ? vs + 4 : vs, va);
+      sums(vb);
+      copy(vb, cut_f);
+      vs += 4;
+      if (!na) break;
+    }
+  }
+  if (vs < nv) {
     uint32_t v[4][VEC];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int ci = c0 + u * kTPBlock;
-      if (ci < nchunks && !(u == 0 && samp0)) {
-        load4(ci, v[u]);
+      const int ci = vs + u < nv ? slice_of(vs + u) * kTPBlock + tid : nchunks;
+      if (ci < nchunks) {
+        const u32x4 x = row4[ci];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[u][e] = x[e];
       } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[u][e] = kNegInfBits;
       }
     }
-    group(v);
-    copy(v, cut_key);
+    sums(v);
+    copy(v, cut_f);
   }
   __syncthreads();
 
-  const uint32_t top = t32_max(kmax, s_u);
-  const uint32_t low = ~t32_max(~kmin, s_u);
-  const bool bad = top >= kKey32PosInf || top <= kKey32NegInf || low < kKey32NegInf;
-  if (bad) return;                   // the multi-read pass reports the row
-  const float R = ceilf(order_floor<DT_F32>(top) * c);
+  // the row's largest value (as its order key) and the normaliser estimate
+  const uint32_t top = t32_max(order_key<DT_F32>(__float_as_uint(fmax_l)), s_u);
   const float Rw = wave_max(Ra);
   const double Sw = wave_sum(rescale(Sa, Ra, Rw));
   if (lane == 0) {
@@ -904,21 +946,29 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
     s_sd[wid] = Sw;
   }
   __syncthreads();
+  // +inf, no finite value, or a NaN anywhere (the sum): the multi-read pass
+  // reports the row
+  if (top >= kKey32PosInf || top <= kKey32NegInf) return;
+  const float R = ceilf(order_floor<DT_F32>(top) * c);
   double S_all = 0.0;
 #pragma unroll
   for (int q = 0; q < kTPWaves; ++q) S_all += rescale(s_sd[q], s_rf[q], R);
+  if (!(S_all > 0.0 && S_all < __builtin_inf())) return;
   const u64 goal = max(u64(__builtin_ceil(double(pp) * S_all * scale)), 1ull);
   const int n = int(s_n);
   const uint32_t topb = top >> 20;
   if (n > kT32BufOne || topb < cut || topb - cut >= uint32_t(kTPBins1)) return;
 
-  // ---- the three digit walks over the copy ----
+  // ---- the three digit walks over the copy's keys ----
+  for (int i = tid; i < n; i += kTPBlock) buf[i] = order_key<DT_F32>(buf[i]);
   for (int i = tid; i < kTPBins1; i += kTPBlock) m1[i] = 0ull;
   for (int i = tid; i < kT32Bins; i += kTPBlock) m2[i] = 0ull;
   __syncthreads();
   for (int i = tid; i < n; i += kTPBlock) {
     const uint32_t key = buf[i];
-    atomicAdd(&m1[(key >> 20) - cut], fixed_term(order_floor<DT_F32>(key), c64, R, scale));
+    const uint32_t bin = (key >> 20) - cut;      // every copied key is >= cut_key
+    if (bin < uint32_t(kTPBins1))
+      atomicAdd(&m1[bin], fixed_term(order_floor<DT_F32>(key), c64, R, scale));
   }
   __syncthreads();
   u64 a1, a2, a3;
