@@ -122,8 +122,9 @@ typedef struct spec_verify_stats {
  *                                top-k list pass (1)
  *   SPEC_VERIFY_TRUNC32_BUF      0: float32 truncation narrows every row by
  *                                digit reads, never through an LDS copy (1)
- *   SPEC_VERIFY_TRUNC32_ONE      0: float32 rows with top-p alone skip the
- *                                one-read pass that follows the list pass (1)
+ *   SPEC_VERIFY_TRUNC32_ONE      0: float32 rows the list pass hands over
+ *                                (top-p alone, top-k past its lists or tied)
+ *                                skip the one-read pass that follows it (1)
  */
 int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
                      int logits_dtype, double ema_decay);

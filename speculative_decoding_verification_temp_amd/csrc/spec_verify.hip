@@ -267,8 +267,9 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
                          dim3(sv::kT1Block), 0, s, target, draft, K, V, c, c64, 61 - lg,
                          h->trunc, h->rules.k, h->parts, hist);
       rc = check_launch(h, "rowstats_trunc32_list");
-      // rows with top-p alone (the list pass handed them over): one read each
-      if (rc == SV_OK && h->trunc32_one && h->trunc.p != nullptr) {
+      // the rows the list pass handed over (top-p alone, top-k past its lists
+      // or tied at the k-th value): one read each where the copy suffices
+      if (rc == SV_OK && h->trunc32_one) {
         hipLaunchKernelGGL((sv::rowstats_trunc32_topp<VEC>), dim3(unsigned(B * rows)),
                            dim3(sv::kTPBlock), 0, s, target, draft, K, V, c, c64, 61 - lg,
                            h->trunc, h->rules.k, h->parts);

@@ -747,9 +747,13 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   }
   const int kk = tr.k != nullptr ? tr.k[b] : 0;
   const float pp = tr.p != nullptr ? tr.p[b] : 1.0f;
-  // top-p alone, valid: every other row is the other passes' (the list pass
-  // marked this one kTruncRedo)
-  if ((kk >= 1 && kk < V) || !(pp < 1.0f && pp > 0.0f)) return;
+  const bool kon = kk >= 1 && kk < V;
+  const bool pon = pp < 1.0f && pp > 0.0f;
+  // the rows the list pass handed over (kTruncRedo) that have a rule: top-p
+  // alone, or top-k (with or without top-p) beyond the list's size or tied at
+  // the k-th value; a row with neither rule or an invalid top_p is the
+  // multi-read pass's
+  if (!(kon || pon) || !(pp > 0.0f) || parts[blockIdx.x].flags != kTruncRedo) return;
   // the row's base comes from the arguments and the workgroup index (the
   // same in every lane); chunks are indexed with 32-bit offsets (a row holds
   // fewer than 2^27 chunks)
@@ -882,7 +886,9 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
       if (in) atomicAdd(&buf[order_key<DT_F32>(sk[q][e]) >> 20], 1u);
   }
   __syncthreads();
-  const uint32_t want = uint32_t((long long)kT32SampleTarget * n_sampled / nchunks) + 1u;
+  // with top-k the copy should hold the top k values and a margin
+  const long long target_n = kon ? max(kT32SampleTarget, kk + kk / 4 + 64) : kT32SampleTarget;
+  const uint32_t want = uint32_t(min(target_n * n_sampled / nchunks + 1, (long long)V));
   uint32_t abv1;
   const int bx = tp_walk<uint32_t, kT32Bins1>(buf, want, abv1, w);
   // the copy starts at the bin in which the sample's count reaches want (at
@@ -954,57 +960,92 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
 #pragma unroll
   for (int q = 0; q < kTPWaves; ++q) S_all += rescale(s_sd[q], s_rf[q], R);
   if (!(S_all > 0.0 && S_all < __builtin_inf())) return;
-  const u64 goal = max(u64(__builtin_ceil(double(pp) * S_all * scale)), 1ull);
   const int n = int(s_n);
   const uint32_t topb = top >> 20;
   if (n > kT32BufOne || topb < cut || topb - cut >= uint32_t(kTPBins1)) return;
+  if (kon && n < kk) return;         // the copy must hold the top k values
 
-  // ---- the three digit walks over the copy's keys ----
+  // ---- digit walks over the copy's keys ----
   for (int i = tid; i < n; i += kTPBlock) buf[i] = order_key<DT_F32>(buf[i]);
-  for (int i = tid; i < kTPBins1; i += kTPBlock) m1[i] = 0ull;
-  for (int i = tid; i < kT32Bins; i += kTPBlock) m2[i] = 0ull;
-  __syncthreads();
+  // The key at which the sum from the top over the copy's keys >= floor first
+  // reaches goal (counts: each key adds 1; masses: its fixed-point term),
+  // digit by digit (the first digit relative to the cut); false when the sum
+  // stays below goal. mass = the sum over the keys at or above the level.
+  auto walk3 = [&](bool counts, uint32_t floor, u64 goal, uint32_t& thr, u64& mass) -> bool {
+    auto add = [&](uint32_t key) -> u64 {
+      return counts ? 1ull : fixed_term(order_floor<DT_F32>(key), c64, R, scale);
+    };
+    for (int i = tid; i < kTPBins1; i += kTPBlock) m1[i] = 0ull;
+    for (int i = tid; i < kT32Bins; i += kTPBlock) m2[i] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < n; i += kTPBlock) {
+      const uint32_t key = buf[i];
+      const uint32_t bin = (key >> 20) - cut;    // every copied key is >= cut_key
+      if (key >= floor && bin < uint32_t(kTPBins1)) atomicAdd(&m1[bin], add(key));
+    }
+    __syncthreads();
+    u64 a1, a2, a3;
+    const int q1 = tp_walk<u64, kTPBins1>(m1, goal, a1, w);
+    if (q1 < 0) return false;
+    const uint32_t d1 = uint32_t(q1) + cut;
+    for (int i = tid; i < n; i += kTPBlock) {
+      const uint32_t key = buf[i];
+      if ((key >> 20) == d1 && key >= floor)
+        atomicAdd(&m2[(key >> 10) & uint32_t(kT32Bins - 1)], add(key));
+    }
+    __syncthreads();
+    const int q2 = tp_walk<u64, kT32Bins>(m2, goal - a1, a2, w);
+    if (q2 < 0) return false;
+    const uint32_t sel = (d1 << 10) | uint32_t(q2);
+    for (int i = tid; i < kT32Bins; i += kTPBlock) m3[i] = 0ull;   // (tp_walk ended with a barrier)
+    __syncthreads();
+    for (int i = tid; i < n; i += kTPBlock) {
+      const uint32_t key = buf[i];
+      if ((key >> 10) == sel && key >= floor) atomicAdd(&m3[key & uint32_t(kT32Bins - 1)], add(key));
+    }
+    __syncthreads();
+    const int q3 = tp_walk<u64, kT32Bins>(m3, goal - a1 - a2, a3, w);
+    if (q3 < 0) return false;
+    thr = (sel << 10) | uint32_t(q3);
+    mass = a1 + a2 + a3 + m3[q3];
+    __syncthreads();                   // m3 read before the next walk clears it
+    return true;
+  };
+  auto put = [&](u64 mass, uint32_t thr) {
+    if (tid == 0) {
+      RowPart p;
+      p.S = __builtin_ldexp(double(mass), -fx);
+      p.R = R;
+      p.m = 0.0f;
+      p.idx = int(thr);
+      p.flags = 0;
+      parts[blockIdx.x] = p;
+    }
+  };
+  uint32_t thr;
+  u64 mass;
+  if (!kon) {
+    // top-p alone: the level where the mass from the top reaches top_p of
+    // the normaliser estimate
+    const u64 goal = max(u64(__builtin_ceil(double(pp) * S_all * scale)), 1ull);
+    if (walk3(false, 0u, goal, thr, mass)) put(mass, thr);
+    return;
+  }
+  // top-k: the k-th largest key (every value equal to it is kept), the exact
+  // mass at or above it, then with top-p the level where the mass from the
+  // top reaches top_p of that mass
+  uint32_t tk;
+  if (!walk3(true, 0u, u64(kk), tk, mass)) return;
+  u64 own = 0;
   for (int i = tid; i < n; i += kTPBlock) {
     const uint32_t key = buf[i];
-    const uint32_t bin = (key >> 20) - cut;      // every copied key is >= cut_key
-    if (bin < uint32_t(kTPBins1))
-      atomicAdd(&m1[bin], fixed_term(order_floor<DT_F32>(key), c64, R, scale));
+    if (key >= tk) own += fixed_term(order_floor<DT_F32>(key), c64, R, scale);
   }
-  __syncthreads();
-  u64 a1, a2, a3;
-  const int q1 = tp_walk<u64, kTPBins1>(m1, goal, a1, w);
-  if (q1 < 0) return;                // the copy's mass stays below the goal
-  const uint32_t d1 = uint32_t(q1) + cut;
-  for (int i = tid; i < n; i += kTPBlock) {
-    const uint32_t key = buf[i];
-    if ((key >> 20) == d1)
-      atomicAdd(&m2[(key >> 10) & uint32_t(kT32Bins - 1)],
-                fixed_term(order_floor<DT_F32>(key), c64, R, scale));
-  }
-  __syncthreads();
-  const int q2 = tp_walk<u64, kT32Bins>(m2, goal - a1, a2, w);
-  if (q2 < 0) return;
-  const uint32_t sel = (d1 << 10) | uint32_t(q2);
-  for (int i = tid; i < kT32Bins; i += kTPBlock) m3[i] = 0ull;   // (tp_walk ended with a barrier)
-  __syncthreads();
-  for (int i = tid; i < n; i += kTPBlock) {
-    const uint32_t key = buf[i];
-    if ((key >> 10) == sel)
-      atomicAdd(&m3[key & uint32_t(kT32Bins - 1)],
-                fixed_term(order_floor<DT_F32>(key), c64, R, scale));
-  }
-  __syncthreads();
-  const int q3 = tp_walk<u64, kT32Bins>(m3, goal - a1 - a2, a3, w);
-  if (q3 < 0) return;
-  if (tid == 0) {
-    RowPart p;
-    p.S = __builtin_ldexp(double(a1 + a2 + a3 + m3[q3]), -fx);
-    p.R = R;
-    p.m = 0.0f;
-    p.idx = int((sel << 10) | uint32_t(q3));
-    p.flags = 0;
-    parts[blockIdx.x] = p;
-  }
+  const u64 S_k = tr_sum<u64, kTPWaves>(own, w.red);
+  if (!pon) return put(S_k, tk);
+  u64 goal = u64(__builtin_ceil(double(pp) * double(S_k)));
+  goal = min(max(goal, 1ull), S_k);
+  if (walk3(false, tk, goal, thr, mass)) put(mass, thr);
 }
 
 // ---------------------------------------------------------------------------

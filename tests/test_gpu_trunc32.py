@@ -260,6 +260,21 @@ def test_trunc32_top_p_alone_one_read_and_fallback(sv, route):
     _check(sv, x, cfg, None, tp, f"trunc32/top-p alone/{route}", excused_fraction=0.45)
 
 
+@pytest.mark.parametrize("route", ["list", "list-multi"], indirect=True)
+def test_trunc32_large_top_k_one_read(sv, route):
+    """Top-k beyond the list pass's lists (500, 1000, 3000 at the c5
+    vocabulary), alone or with top_p = 0.95 or 0.5: the list pass hands these
+    rows over, and the one-read route finds the k-th largest value and the
+    level in its copy of the row's top part (or, on the other route, the
+    multi-read pass does). Every sequence against the oracle."""
+    cfg = CONFIGS["c5"].scaled(B=24, K=2)
+    x = make_inputs(cfg, 10, DEV)
+    tk = np.tile(np.array([500, 1000, 3000, 1000, 500, 3000], np.int32), cfg.B // 6)
+    tp = np.tile(np.array([1.0, 0.95, 0.5, 1.0, 0.95, 0.95], np.float32), cfg.B // 6)
+    _resample_drafts(x, cfg.T, tk, tp, 26)
+    _check(sv, x, cfg, tk, tp, f"trunc32/large top-k/{route}")
+
+
 def test_trunc32_c5_top_p_alone_sampled(sv):
     """The c5 shape with top_p = 0.9 alone on every sequence (the one-read
     route); the oracle checks 24 sampled sequences."""
