@@ -434,6 +434,107 @@ __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* T
   finish_tile(ti, E, Ed, A, Bd);
 }
 
+// Tile sums of truncated fp32 draw rows. Such rows keep few of their values
+// (the others' terms are 0), so a wavefront first gathers, per value slot of
+// a unit, the pairs that either row keeps into its LDS buffer (a dropped
+// value as -inf, whose term is 0): a float compare of each value against its
+// row's threshold value, which is the key compare (order_floor gives the
+// least float of the key, and compares keep subnormals), and the slot's
+// ballot places the pair. The terms are then formed for the gathered pairs
+// only, one per lane in gather order (so every sum is the same from run to
+// run), when the buffer could not take another unit and at each tile's end.
+// Loads run as in tiles_unscaled: the units of the next tile are issued as
+// the units of this one are gathered (after the last tile, the last tile's
+// again, so that the loads are unconditional).
+constexpr int kSparseCap = 512;    // gathered pairs per wavefront
+
+template <int VEC, bool RESID, int NW>
+__device__ __forceinline__ void tiles_sparse32(const double* T2, const void* trow,
+                                               const void* drow, const DrawRow& dr, double c,
+                                               int ntiles, long long nchunks, TileSums* tiles,
+                                               int wid, int lane, float2* buf) {
+  using C = Chunk<DT_F32, VEC>;
+  static_assert(VEC == 4 && kUnitChunks == 1, "units of one 16-byte chunk per lane and row");
+  const double rho2 = RESID ? __builtin_ldexp(dr.rho, int(dr.R_t) - int(dr.R_d)) : 0.0;
+  const int st = -int(dr.R_t), sd = -int(dr.R_d);
+  const float ft = order_floor<DT_F32>(dr.thr_t);
+  const float fd = RESID ? order_floor<DT_F32>(dr.thr_d) : __builtin_inff();
+  constexpr float kNegInf = -__builtin_inff();
+  const int my_tiles = wid < ntiles ? (ntiles - 1 - wid) / NW + 1 : 0;
+  if (my_tiles == 0) return;
+  auto unit_c0 = [&](int ti, int u) -> long long {
+    return (long long)(wid + ti * NW) * kTileChunks + (long long)u * kWave + lane;
+  };
+  auto load_unit = [&](int ti, int u, UnitBuf& b) {
+    const long long ci = min(unit_c0(ti, u), nchunks - 1);
+    b.a[0] = C::load(trow, ci);
+    if constexpr (RESID) b.d[0] = C::load(drow, ci);
+  };
+  uint32_t n = 0;                      // pairs in the buffer (the same in every lane)
+  double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
+  auto drain = [&]() {
+    wave_sync();
+    for (uint32_t e = uint32_t(lane); e < n; e += kWave) {
+      const float2 v = buf[e];
+      const double et = exp2_tab(double(v.x) * c, T2);
+      if constexpr (RESID)
+        accum_pair_u(et, exp2_tab(double(v.y) * c, T2), rho2, E, Ed, A, Bd);
+      else
+        E += et;
+    }
+    n = 0;
+    wave_sync();
+  };
+  UnitBuf b[kUnits];
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) load_unit(0, u, b[u]);
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const int tn = ti + 1 < my_tiles ? ti + 1 : ti;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      if (n > uint32_t(kSparseCap - 4 * kWave)) drain();
+      const bool in = unit_c0(ti, u) < nchunks;
+      bool kt[4], kd[4], any = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kt[q] = in && __uint_as_float(b[u].a[0][q]) >= ft;
+        kd[q] = RESID && in && __uint_as_float(b[u].d[0][q]) >= fd;
+        any |= kt[q] || kd[q];
+      }
+      if (__any(any)) {                // (a unit without a kept value is common with top-k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool take = kt[q] || kd[q];
+          const unsigned long long m = __ballot(take);
+          if (take)
+            buf[n + lanes_below(m)] =
+                make_float2(kt[q] ? __uint_as_float(b[u].a[0][q]) : kNegInf,
+                            kd[q] ? __uint_as_float(b[u].d[0][q]) : kNegInf);
+          n += uint32_t(__popcll(m));
+        }
+      }
+      load_unit(tn, u, b[u]);
+    }
+    drain();
+    double Et = wave_sum(E);
+    double Edt = 0.0, At = 0.0, Bdt = 0.0;
+    if constexpr (RESID) {
+      Edt = wave_sum(Ed);
+      At = wave_sum(A);
+      Bdt = wave_sum(Bd);
+    }
+    if (lane == 0) {
+      TileSums ts;
+      ts.E = __builtin_ldexp(Et, st);
+      ts.Ed = RESID ? __builtin_ldexp(Edt, sd) : 0.0;
+      ts.A = RESID ? __builtin_ldexp(At, st) : 0.0;
+      ts.Bd = RESID ? __builtin_ldexp(Bdt, sd) : 0.0;
+      tiles[wid + ti * NW] = ts;
+    }
+    E = Ed = A = Bd = 0.0;
+  }
+}
+
 // Phase 4 when the tile sums came from tiles_unscaled. Wavefronts 0-3 each
 // find the crossing tile from the tile sums (the same arithmetic in each, so
 // the same tile); thread t < kTileChunks then re-reads chunk t of that tile,
@@ -592,7 +693,8 @@ __device__ __forceinline__ void finish_sequence(
     DrawRow& s_dr, PickShared& psh, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
-    double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
+    double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
+    float2* sparse = nullptr) {
   using C = Chunk<DT, VEC>;
   constexpr int kW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -707,14 +809,30 @@ __device__ __forceinline__ void finish_sequence(
   if constexpr (kFast)
     unscaled = fabsf(dr.R_t) <= kUnscaledMaxR && (!W.residual || fabsf(dr.R_d) <= kUnscaledMaxR);
   if (unscaled) {
+    // truncated fp32 rows: gather the kept values first (a pair of rows
+    // without truncation keeps every value: the dense loop)
+    bool gathered = false;
+    if constexpr (TRUNC && DT == DT_F32 && VEC == 4) {
+      if (sparse != nullptr && (dr.thr_t != 0u || (W.residual && dr.thr_d != 0u))) {
+        if (W.residual)
+          tiles_sparse32<VEC, true, kW>(Tt, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
+                                        lane, sparse + wid * kSparseCap);
+        else
+          tiles_sparse32<VEC, false, kW>(Tt, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles,
+                                         wid, lane, sparse + wid * kSparseCap);
+        gathered = true;
+      }
+    }
     if constexpr (kFast) {
       constexpr bool kMask = TRUNC && DT == DT_F32;
-      if (W.residual)
+      if (gathered) {
+      } else if (W.residual) {
         tiles_unscaled<DT, VEC, true, kW, kMask>(Tt, Td, W.trow, W.drow, dr, c64, ntiles,
                                                  nchunks, tiles, wid, lane);
-      else
+      } else {
         tiles_unscaled<DT, VEC, false, kW, kMask>(Tt, Td, W.trow, W.drow, dr, c64, ntiles,
                                                   nchunks, tiles, wid, lane);
+      }
     }
   } else {
     for (int t = wid; t < ntiles; t += kW) {
@@ -933,6 +1051,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
   __shared__ TileSums tiles[kFMaxTiles];
   __shared__ DrawRow s_dr;
   __shared__ PickShared psh;
+  // truncated fp32 rows: the gathered value pairs, kSparseCap per wavefront
+  __shared__ float2 sparse[TRUNC && kTab2F ? (NT / kWave) * kSparseCap : 1];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
   for (int r = tid; r < rows; r += NT) {
@@ -948,9 +1068,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
   // the fp32 table does not depend on the truncation: built during the scan
   finish_sequence<DT, VEC, NT, TRUNC, !TRUNC || DT == DT_F32>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
                                       n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
-                                      out_len, hist, ema,
-                                    steps,
-                                    decay, st, aux_p, aux_q, aux_z);
+                                      out_len, hist, ema, steps, decay, st, aux_p, aux_q, aux_z,
+                                      TRUNC && kTab2F ? sparse : nullptr);
 }
 
 __global__ void zero_hist(uint32_t* hist, int n) {
