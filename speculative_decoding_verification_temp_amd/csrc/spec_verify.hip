@@ -175,7 +175,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
     if (h->drift_sup != nullptr && h->topm_lists != nullptr) {
       hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U, true>), dim3(unsigned(B * rows * L.nseg)),
                          dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                         h->rules.k, h->parts, hist, h->drift_m, h->topm_lists);
+                         h->rules.k, h->parts, hist, h->drift_m, h->topm_lists, tokens);
       h->topm_nseg = L.nseg;
       topm = true;
     }
@@ -183,7 +183,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   if (!topm)
     hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
                        dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                       h->rules.k, h->parts, hist, 0, nullptr);
+                       h->rules.k, h->parts, hist, 0, nullptr, tokens);
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;

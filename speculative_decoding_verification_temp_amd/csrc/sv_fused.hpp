@@ -694,7 +694,8 @@ __device__ __forceinline__ void finish_sequence(
     int32_t* __restrict__ out_len,
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
-    float2* sparse = nullptr) {
+    float2* sparse = nullptr, const float* fX = nullptr, const int32_t* pre_tok = nullptr,
+    const float* pre_u = nullptr) {
   using C = Chunk<DT, VEC>;
   constexpr int kW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -722,11 +723,13 @@ __device__ __forceinline__ void finish_sequence(
       Sd = fS[K + 1 + lane];
       if constexpr (TRUNC) kd = fK[K + 1 + lane];
       lane_bad |= !finite_pos(Sd);
-      d = tokens[(long long)b * K + lane];
+      d = pre_tok != nullptr ? pre_tok[lane] : tokens[(long long)b * K + lane];
       lane_bad |= !(d >= 0 && d < V);   // checked before the gather below
       if (!lane_bad) {
-        const float xt = load_logit<DT>(row_base(lane), d);
-        const float xd = load_logit<DT>(row_base(K + 1 + lane), d);
+        // the logits at d: from the streaming pass's partials when it kept
+        // them (fX), else gathered here
+        const float xt = fX != nullptr ? fX[lane] : load_logit<DT>(row_base(lane), d);
+        const float xd = fX != nullptr ? fX[K + 1 + lane] : load_logit<DT>(row_base(K + 1 + lane), d);
         if constexpr (TRUNC && DT == DT_BF16) {
           // the same level terms as the truncated normalisers; 0 when dropped
           const uint32_t at = bf16_key(__float_as_uint(xt) >> 16);
@@ -741,7 +744,7 @@ __device__ __forceinline__ void finish_sequence(
           P = double(term(xt, c, Rt)) / St;
           Q = double(term(xd, c, Rd)) / Sd;
         }
-        const double u = uniforms[(long long)b * (K + 1) + lane];
+        const double u = pre_u != nullptr ? pre_u[lane] : uniforms[(long long)b * (K + 1) + lane];
         keep = (P >= Q) || (u < P / Q);
         zq = keep && Q == 0.0;
       }
@@ -1053,8 +1056,18 @@ __global__ __launch_bounds__(NT) void finish_seq(
   __shared__ PickShared psh;
   // truncated fp32 rows: the gathered value pairs, kSparseCap per wavefront
   __shared__ float2 sparse[TRUNC && kTab2F ? (NT / kWave) * kSparseCap : 1];
+  // after the streaming pass: each row's logit at its drafted token (RowPart
+  // m), and the sequence's tokens and uniforms, loaded with the partials
+  __shared__ float fX[TRUNC ? 1 : kFMaxRows];
+  __shared__ int32_t s_tok[kWave];
+  __shared__ float s_u[kWave];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
+  if (tid >= NT - kWave) {             // the last wavefront: tokens and uniforms
+    const int l = tid - (NT - kWave);
+    if (l < K) s_tok[l] = tokens[(long long)b * K + l];
+    if (l <= K) s_u[l] = uniforms[(long long)b * (K + 1) + l];
+  }
   for (int r = tid; r < rows; r += NT) {
     float R;
     double S;
@@ -1063,13 +1076,15 @@ __global__ __launch_bounds__(NT) void finish_seq(
     fR[r] = R;
     fS[r] = S;
     if constexpr (TRUNC) fK[r] = uint32_t(pr->idx);
+    else fX[r] = pr->m;
   }
   __syncthreads();
   // the fp32 table does not depend on the truncation: built during the scan
   finish_sequence<DT, VEC, NT, TRUNC, !TRUNC || DT == DT_F32>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
                                       n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
                                       out_len, hist, ema, steps, decay, st, aux_p, aux_q, aux_z,
-                                      TRUNC && kTab2F ? sparse : nullptr);
+                                      TRUNC && kTab2F ? sparse : nullptr, TRUNC ? nullptr : fX,
+                                      s_tok, s_u);
 }
 
 __global__ void zero_hist(uint32_t* hist, int n) {

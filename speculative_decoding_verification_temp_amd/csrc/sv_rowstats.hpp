@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
     const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
     int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
-    uint64_t* __restrict__ topm_lists) {
+    uint64_t* __restrict__ topm_lists, const int32_t* __restrict__ tokens) {
   static_assert(!TOPM || (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4),
                 "top-m lists need 16-byte chunks");
   using C = Chunk<DT, VEC>;
@@ -73,6 +73,16 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
   const long long nchunks = V / VEC;
   const long long c0 = (long long)seg * seg_chunks;
   const long long c1 = min(c0 + (long long)seg_chunks, nchunks);
+  // the logit at this row's drafted token (target row i < K and draft row i
+  // hold position i's), loaded now and stored with the row's partial, so the
+  // scan that follows need not gather it; NaN when there is none or it is
+  // out of range (the scan checks the token itself)
+  float x_drafted = __builtin_nanf("");
+  if (tokens != nullptr && tid == 0 && r != K) {
+    const int i = r < K ? r : r - K - 1;
+    const int d = tokens[(long long)b * K + i];
+    if (d >= 0 && d < V) x_drafted = load_logit<DT>(row, d);
+  }
 
   [[maybe_unused]] TopM<DT> tm;
   [[maybe_unused]] const bool topm_row = TOPM && r > K;   // uniform
@@ -214,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
     RowPart p;
     p.S = Sb;
     p.R = Rb;
-    p.m = 0.0f;
+    p.m = x_drafted;
     p.idx = -1;
     p.flags = 0;
     parts[wg] = p;
