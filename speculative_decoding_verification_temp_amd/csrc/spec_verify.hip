@@ -192,7 +192,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
                        dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
                        h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
                        out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p,
-                       h->aux_q, h->aux_z);
+                       h->aux_q, h->aux_z, nullptr);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
@@ -237,7 +237,7 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                      uniforms, c, c64, tab_half(c64), h->rules, out_tokens, out_len, hist, h->ema,
-                     h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z);
+                     h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, h->trunc.k);
   return check_launch(h, "finish_seq (truncated)");
 }
 
@@ -287,7 +287,7 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                      uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
-                     h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z);
+                     h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr);
   return check_launch(h, "finish_seq (truncated)");
 }
 

@@ -535,6 +535,108 @@ __device__ __forceinline__ void tiles_sparse32(const double* T2, const void* tro
   }
 }
 
+// The same for truncated bf16 draw rows: a gathered pair is the two 16-bit
+// values in one word (target low, draft high), and its terms come from the
+// rows' masked tables (term_unscaled: 0 for a value its row drops), so a
+// pair gathered for one row's sake adds nothing for the other. A value is
+// gathered when, as a float, it is at least its row's threshold value (the
+// key compare). 16 wavefronts x kSparseCap16 words of LDS beside the two
+// tables.
+constexpr int kSparseCap16 = 256;   // gathered pairs per wavefront
+
+template <bool RESID, int NW>
+__device__ __forceinline__ void tiles_sparse16(const double* Tt, const double* Td,
+                                               const void* trow, const void* drow,
+                                               const DrawRow& dr, double c, int ntiles,
+                                               long long nchunks, TileSums* tiles, int wid,
+                                               int lane, uint32_t* buf) {
+  using C = Chunk<DT_BF16, 8>;
+  static_assert(kUnitChunks == 1, "units of one 16-byte chunk per lane and row");
+  const double rho2 = RESID ? __builtin_ldexp(dr.rho, int(dr.R_t) - int(dr.R_d)) : 0.0;
+  const int st = -int(dr.R_t), sd = -int(dr.R_d);
+  const float ft = key_floor(dr.thr_t);
+  const float fd = RESID ? key_floor(dr.thr_d) : __builtin_inff();
+  const int my_tiles = wid < ntiles ? (ntiles - 1 - wid) / NW + 1 : 0;
+  if (my_tiles == 0) return;
+  auto unit_c0 = [&](int ti, int u) -> long long {
+    return (long long)(wid + ti * NW) * kTileChunks + (long long)u * kWave + lane;
+  };
+  auto load_unit = [&](int ti, int u, UnitBuf& b) {
+    const long long ci = min(unit_c0(ti, u), nchunks - 1);
+    b.a[0] = C::load(trow, ci);
+    if constexpr (RESID) b.d[0] = C::load(drow, ci);
+  };
+  uint32_t n = 0;                      // pairs in the buffer (the same in every lane)
+  double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
+  auto drain = [&]() {
+    wave_sync();
+    for (uint32_t e = uint32_t(lane); e < n; e += kWave) {
+      const uint32_t w = buf[e];
+      const double et = term_unscaled(Tt, w & 0xffffu, c, dr.thr_t);
+      if constexpr (RESID)
+        accum_pair_u(et, term_unscaled(Td, w >> 16, c, dr.thr_d), rho2, E, Ed, A, Bd);
+      else
+        E += et;
+    }
+    n = 0;
+    wave_sync();
+  };
+  UnitBuf b[kUnits];
+#pragma unroll
+  for (int u = 0; u < kUnits; ++u) load_unit(0, u, b[u]);
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const int tn = ti + 1 < my_tiles ? ti + 1 : ti;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const bool in = unit_c0(ti, u) < nchunks;
+      // value v of the chunk: word v / 2, low half for even v
+      auto val = [](const u32x4& r, int v) {
+        return __uint_as_float((v & 1) ? r[v >> 1] & 0xffff0000u : r[v >> 1] << 16);
+      };
+      bool kt[8], kd[8], any = false;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        kt[v] = in && val(b[u].a[0], v) >= ft;
+        kd[v] = RESID && in && val(b[u].d[0], v) >= fd;
+        any |= kt[v] || kd[v];
+      }
+      if (__any(any)) {                // (a unit without a kept value is common with top-k)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          if (n > uint32_t(kSparseCap16 - kWave)) drain();
+          const bool take = kt[v] || kd[v];
+          const unsigned long long m = __ballot(take);
+          if (take) {
+            const uint32_t wt = b[u].a[0][v >> 1], wd = RESID ? b[u].d[0][v >> 1] : 0u;
+            const uint32_t lo = (v & 1) ? wt >> 16 : wt & 0xffffu;
+            const uint32_t hi = (v & 1) ? wd >> 16 : wd & 0xffffu;
+            buf[n + lanes_below(m)] = lo | (hi << 16);
+          }
+          n += uint32_t(__popcll(m));
+        }
+      }
+      load_unit(tn, u, b[u]);
+    }
+    drain();
+    double Et = wave_sum(E);
+    double Edt = 0.0, At = 0.0, Bdt = 0.0;
+    if constexpr (RESID) {
+      Edt = wave_sum(Ed);
+      At = wave_sum(A);
+      Bdt = wave_sum(Bd);
+    }
+    if (lane == 0) {
+      TileSums ts;
+      ts.E = __builtin_ldexp(Et, st);
+      ts.Ed = RESID ? __builtin_ldexp(Edt, sd) : 0.0;
+      ts.A = RESID ? __builtin_ldexp(At, st) : 0.0;
+      ts.Bd = RESID ? __builtin_ldexp(Bdt, sd) : 0.0;
+      tiles[wid + ti * NW] = ts;
+    }
+    E = Ed = A = Bd = 0.0;
+  }
+}
+
 // Phase 4 when the tile sums came from tiles_unscaled. Wavefronts 0-3 each
 // find the crossing tile from the tile sums (the same arithmetic in each, so
 // the same tile); thread t < kTileChunks then re-reads chunk t of that tile,
@@ -695,7 +797,7 @@ __device__ __forceinline__ void finish_sequence(
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
     float2* sparse = nullptr, const float* fX = nullptr, const int32_t* pre_tok = nullptr,
-    const float* pre_u = nullptr) {
+    const float* pre_u = nullptr, uint32_t* sparse16 = nullptr, int trunc_k = 0) {
   using C = Chunk<DT, VEC>;
   constexpr int kW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -823,6 +925,22 @@ __device__ __forceinline__ void finish_sequence(
         else
           tiles_sparse32<VEC, false, kW>(Tt, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles,
                                          wid, lane, sparse + wid * kSparseCap);
+        gathered = true;
+      }
+    }
+    if constexpr (TRUNC && DT == DT_BF16 && VEC == 8) {
+      // bf16 table lookups are cheap: gathering pays only when the rows keep
+      // few values, as a small top-k bounds them (measured at c3: 4-5 us
+      // faster with top-k 20 or 50, 3.6 us slower with top-p 0.95 alone,
+      // which keeps about 13% of V over both rows)
+      if (sparse16 != nullptr && (dr.thr_t != 0u || (W.residual && dr.thr_d != 0u)) &&
+          trunc_k >= 1 && trunc_k <= V / 32) {
+        if (W.residual)
+          tiles_sparse16<true, kW>(Tt, Td, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
+                                   lane, sparse16 + wid * kSparseCap16);
+        else
+          tiles_sparse16<false, kW>(Tt, Td, W.trow, W.drow, dr, c64, ntiles, nchunks, tiles, wid,
+                                    lane, sparse16 + wid * kSparseCap16);
         gathered = true;
       }
     }
@@ -1044,7 +1162,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
     const float* __restrict__ uniforms, float c, double c64, int n_half, Rules sp,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len, uint32_t* __restrict__ hist,
     double* __restrict__ ema, int32_t* __restrict__ steps, double decay,
-    DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z) {
+    DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
+    const int32_t* __restrict__ trunc_k) {
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
   constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
   __shared__ double T[kTab ? (TRUNC ? 2 * kTabMax : kTabMax) : kTab2F ? kTab2 : 1];
@@ -1056,6 +1175,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
   __shared__ PickShared psh;
   // truncated fp32 rows: the gathered value pairs, kSparseCap per wavefront
   __shared__ float2 sparse[TRUNC && kTab2F ? (NT / kWave) * kSparseCap : 1];
+  __shared__ uint32_t sparse16[TRUNC && kTab ? (NT / kWave) * kSparseCap16 : 1];
   // after the streaming pass: each row's logit at its drafted token (RowPart
   // m), and the sequence's tokens and uniforms, loaded with the partials
   __shared__ float fX[TRUNC ? 1 : kFMaxRows];
@@ -1084,7 +1204,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
                                       n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
                                       out_len, hist, ema, steps, decay, st, aux_p, aux_q, aux_z,
                                       TRUNC && kTab2F ? sparse : nullptr, TRUNC ? nullptr : fX,
-                                      s_tok, s_u);
+                                      s_tok, s_u, TRUNC && kTab ? sparse16 : nullptr,
+                                      trunc_k != nullptr ? trunc_k[b] : 0);
 }
 
 __global__ void zero_hist(uint32_t* hist, int n) {
