@@ -205,23 +205,24 @@ __device__ __forceinline__ double term_unscaled(const double* T, uint32_t bits, 
   return bf16_key(bits) >= thr ? exp2_acc(double(__uint_as_float(bits << 16)) * c) : 0.0;
 }
 
-// fp32 rows: 2^y = 2^floor(y) * 2^(i/256) * 2^r in float64, with i the
-// nearest integer to 256 (y - floor(y)) (all steps exact), |r| <= 1/512, a
-// 257-entry LDS table T2[i] = 2^(i/256) and a degree-4 polynomial for 2^r
-// (truncation error below 4e-17 relative). y <= -1100 (including -inf) gives 0.
-constexpr int kTab2 = 257;
-__device__ inline double exp2_frac_entry(int i) { return exp2_acc_hi(double(i) * (1.0 / 256.0)); }
+// fp32 rows: 2^y = 2^n * 2^(i/4096) * 2^r in float64, with 4096 n + i the
+// nearest integer to 4096 y (read from the low bits of y + 1.5 * 2^40, whose
+// unit in the last place is 2^-12; every step exact), |r| <= 2^-13, a
+// 4096-entry LDS table T2[i] = 2^(i/4096) and the degree-2 Taylor polynomial
+// of 2^r (truncation error below 1.1e-13 relative, far inside what the draw's
+// comparisons resolve). y <= -1100 (including -inf) gives 0.
+constexpr int kTab2 = 4096;
+__device__ inline double exp2_frac_entry(int i) { return exp2_acc_hi(double(i) * (1.0 / 4096.0)); }
 __device__ __forceinline__ double exp2_tab(double y, const double* T2) {
   constexpr double L = 0.6931471805599453094172321214581766;   // ln 2
-  constexpr double a1 = L, a2 = a1 * L / 2, a3 = a2 * L / 3, a4 = a3 * L / 4;
+  constexpr double a2 = L * L / 2;
+  constexpr double kShift = 0x1.8p40;
   y = fmax(y, -1100.0);
-  const double n = __builtin_floor(y);
-  const double t = (y - n) * 256.0;
-  const double ti = __builtin_rint(t);
-  const double r = (t - ti) * (1.0 / 256.0);
-  const double p =
-      __builtin_fma(__builtin_fma(__builtin_fma(__builtin_fma(a4, r, a3), r, a2), r, a1), r, 1.0);
-  return __builtin_ldexp(T2[int(ti)] * p, int(n));
+  const double ys = y + kShift;
+  const int k = int(uint32_t(__double_as_longlong(ys)));      // 4096 n + i (two's complement)
+  const double r = y - (ys - kShift);
+  const double p = __builtin_fma(__builtin_fma(a2, r, L), r, 1.0);
+  return __builtin_ldexp(T2[k & (kTab2 - 1)] * p, k >> 12);
 }
 
 __device__ __forceinline__ void accum_pair_u(double et, double ed, double rho2, double& E,
