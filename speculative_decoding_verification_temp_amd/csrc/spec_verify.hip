@@ -188,11 +188,22 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   prof_mark(h, 1, s);
   if (rc) return rc;
   if (h->finish_seq && L.ntiles <= sv::kFMaxTiles && rows <= sv::kFMaxRows) {
-    hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock, false>), dim3(B),
-                       dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
-                       h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
-                       out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats, h->aux_p,
-                       h->aux_q, h->aux_z, nullptr);
+    // with at least two sequences per compute unit, 512-thread workgroups
+    // let two sequences share a unit, so one's scan and pick overlap the
+    // other's loads (c5: 918 -> 899 us per call); below that, 1024 threads
+    // keep every unit's waves on its one sequence
+    if (B >= 2 * h->n_cu)
+      hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlockHalf, false>), dim3(B),
+                         dim3(sv::kFinishBlockHalf), 0, s, K, V, L.nseg,
+                         h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
+                         out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats,
+                         h->aux_p, h->aux_q, h->aux_z, nullptr);
+    else
+      hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock, false>), dim3(B),
+                         dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
+                         h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
+                         out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats,
+                         h->aux_p, h->aux_q, h->aux_z, nullptr);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
@@ -284,10 +295,16 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
   rc = check_launch(h, "rowstats_trunc32");
   prof_mark(h, 1, s);                // both truncation passes
   if (rc) return rc;
-  hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
-                     dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
-                     uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
-                     h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr);
+  if (B >= 2 * h->n_cu)                // as in run_stochastic
+    hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlockHalf, true>), dim3(B),
+                       dim3(sv::kFinishBlockHalf), 0, s, K, V, 1, h->parts, target, draft,
+                       tokens, uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema,
+                       h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr);
+  else
+    hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
+                       dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
+                       uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
+                       h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr);
   return check_launch(h, "finish_seq (truncated)");
 }
 

@@ -28,6 +28,7 @@ constexpr int kFWaves = kFBlock / kWave;
 constexpr int kFMaxRows = 127;      // 2K + 1 for K <= 63
 constexpr int kFMaxTiles = 256;     // draw tiles per row held in LDS
 constexpr int kFinishBlock = 1024;   // threads per sequence after the multi-workgroup pass
+constexpr int kFinishBlockHalf = 512;   // the same with two sequences per compute unit
 
 // Shared state of the workgroup-wide pick.
 struct PickShared {
