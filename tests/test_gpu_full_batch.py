@@ -5,7 +5,8 @@ processes) and compared with the HIP library's output, in the launch
 configuration the benchmark times: c3 stochastic and greedy (B = 256, K = 7,
 V = 128256, bf16), c4 margin and greedy (B = 128, K = 8, V = 151936, bf16),
 c5 (B = 1024, K = 4, V = 128256, fp32, with its p = q and zeroed-mass
-sequences), and the 600-step c3 run with EMA decay 0.99: 32 seeded slots
+sequences), the c3 rows at B = 512 (the finish in 512-thread workgroups),
+and the 600-step c3 run with EMA decay 0.99: 32 seeded slots
 checked at every step (tokens, accept lengths) and their EMA at the end, the
 whole batch at steps 0, 299 and 599.
 """
@@ -144,6 +145,15 @@ def test_c5_full_batch(sv):
     assert ref.z0_fallbacks == 0 and ref.zero_q_accepts == 0
     _log(f"c5 full batch: {rep} (p = q rows {len(pq)}, zeroed rows {len(zz)}) "
          f"hist {hist.cpu().tolist()}")
+
+
+def test_bf16_half_block_finish_full_batch(sv):
+    """The c3 rows with B = 512: a batch of at least two sequences per
+    compute unit runs the finish in 512-thread workgroups (two sequences per
+    unit, bf16 table lookups); every sequence against the oracle."""
+    cfg = CONFIGS["c3"].scaled(B=512)
+    x, v, aux, tok, alen, hist, ref, rep = _full(sv, cfg, "stochastic", step=5)
+    _log(f"c3 rows, B=512 (512-thread finish): {rep}")
 
 
 def test_c3_ema_600_steps(sv):
