@@ -37,6 +37,63 @@ __device__ inline const void* row_ptr(const void* target, const void* draft, int
 // --------------------------------------------------------------------------
 //
 // With TOPM (16-byte chunks only), the workgroups of draft rows also keep a
+// Where the sum from the top over bins[0..256) (thread t holds bin t) first
+// reaches goal: the highest t whose sum over the bins >= t is >= goal, and in
+// above the sum over the bins > t. Needs all kBlock threads; sw: 8 words of
+// LDS. (The first sum, over all bins, must reach goal.)
+__device__ inline void wg_suffix_cut(const uint32_t* bins, uint32_t goal, uint32_t* sw,
+                                     uint32_t& cut, uint32_t& above) {
+  static_assert(kBlock == 256 && kWavesPerBlock == 4, "one bin per thread");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const uint32_t c = bins[tid];
+  uint32_t v = c;                      // sum over this wavefront's lanes >= lane
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t u = __shfl_down(v, o, kWave);
+    if (lane + o < kWave) v += u;
+  }
+  if (lane == 0) sw[wid] = v;
+  __syncthreads();
+  uint32_t add = 0u;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) add += w > wid ? sw[w] : 0u;
+  const uint32_t suf = v + add;        // non-increasing in tid
+  const uint32_t n = uint32_t(__popcll(__ballot(suf >= goal)));
+  __syncthreads();                     // sw read before it is written again
+  if (lane == 0) sw[wid] = n;
+  __syncthreads();
+  uint32_t t = 0u;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) t += sw[w];
+  cut = t - 1u;
+  if (uint32_t(tid) == cut) sw[4] = suf - c;
+  __syncthreads();
+  above = sw[4];
+  __syncthreads();
+}
+
+// A lower bound of the m-th largest (1 <= m <= 256) of the kBits-bit keys
+// held one per thread of the workgroup: that key's top 16 bits, lower bits 0,
+// from two rounds of 256 bins (the top byte, then the next byte among the
+// keys in the chosen top-byte bin). Needs all kBlock threads; bins: 512
+// words of LDS, sw: 8.
+template <int kBits>
+__device__ inline uint32_t wg_kth_top16(uint32_t key, uint32_t m, uint32_t* bins, uint32_t* sw) {
+  constexpr int s1 = kBits - 8, s2 = kBits - 16;
+  const int tid = threadIdx.x;
+  bins[tid] = 0u;
+  bins[kBlock + tid] = 0u;
+  __syncthreads();
+  atomicAdd(&bins[key >> s1], 1u);
+  __syncthreads();
+  uint32_t b1, above1, b2, above2;
+  wg_suffix_cut(bins, m, sw, b1, above1);
+  if ((key >> s1) == b1) atomicAdd(&bins[kBlock + ((key >> s2) & 255u)], 1u);
+  __syncthreads();
+  wg_suffix_cut(bins + kBlock, m - above1, sw, b2, above2);
+  return (b1 << s1) | (b2 << s2);
+}
+
 // top-m candidate list per wavefront (sv_topm.hpp) for the draft residual
 // side output and store it, as at most m keys followed by zeros, at
 //   topm_lists[((b K + i) nseg + seg) 4 + wavefront][0..m)
@@ -47,7 +104,7 @@ __device__ inline const void* row_ptr(const void* target, const void* draft, int
 constexpr int kTopmCapFused = 448;   // keys per wavefront list in the streaming pass
 
 template <int DT, int VEC, int U, bool TOPM = false>
-__global__ __launch_bounds__(kBlock) void rowstats_sum(
+__global__ __launch_bounds__(kBlock, TOPM ? 4 : 1) void rowstats_sum(
     const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
     int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
@@ -99,6 +156,13 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
     tm.init(s_tk[tid / kWave], s_tb[tid / kWave], &s_tt, kTopmCapFused,
             uint32_t(min(topm_m, V)), s_ts[tid / kWave], s_ta[tid / kWave]);
   }
+  // With a whole group for every thread, the first group starts every
+  // wavefront's threshold from the workgroup's 256 lane maxima (their m-th
+  // largest is at most the row's m-th largest value): a quarter as many
+  // candidates as one wavefront's chunk maxima give, and no compaction is
+  // needed along the way.
+  [[maybe_unused]] const bool wg_seed = topm_row && (c1 - c0) >= (long long)U * kBlock;
+  [[maybe_unused]] __shared__ uint32_t s_wg[TOPM ? 8 : 1];
 
   float R = kRefInit;
   double S = 0.0;
@@ -141,6 +205,17 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
       for (int k = 0; k + w < U * C::N; k += 2 * w) t[k] += t[k + w];
     S += (double)t[0];
     if constexpr (TOPM) {
+      if (wg_seed && !topm_seeded) {   // every thread is in this first group
+        const uint32_t gbits = __float_as_uint(gm);
+        uint32_t key = DT == DT_BF16 ? bf16_key(gbits >> 16) : order_key<DT_F32>(gbits);
+        if (!(gm == gm)) key = 0u;    // (a NaN counts as nothing)
+        const uint32_t t = wg_kth_top16<DT == DT_BF16 ? 16 : 32>(
+            key, tm.want, tm.bins - (tid / kWave) * 256, s_wg);
+        tm.thr = uint64_t(t) << 32;
+        tm.thr_f = order_floor<DT>(t);
+        if (tid == 0) atomicMax(tm.shared, (unsigned long long)tm.thr);
+        topm_seeded = true;
+      }
       if (topm_row && __builtin_amdgcn_read_exec() == ~0ull) {   // all 64 lanes here
         if (!topm_seeded) {   // the first group's chunk maxima start the threshold
           tm.template seed<U>(cm, (1u << U) - 1u);
@@ -151,8 +226,8 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum(
           for (int u = 0; u < U; ++u)
             tm.stage_chunk(cm[u] >= tm.thr_f, raw[u], uint32_t(ci + (long long)u * kBlock));
           // a tighter threshold early stages fewer chunks (measured a small
-          // gain here; the row-reading kernel is faster without it)
-          if (tm.fill > 2 * tm.want) tm.compact();
+          // gain with the wavefront seed)
+          if (!wg_seed && tm.fill > 2 * tm.want) tm.compact();
         }
         topm_next = ci + (long long)U * kBlock;
       }
