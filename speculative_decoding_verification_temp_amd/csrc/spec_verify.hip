@@ -76,6 +76,10 @@ struct spec_verify_handle {
   double* drift_res = nullptr;             //   [max_batch][K][m] residuals
   uint64_t* topm_lists = nullptr;          // streaming-pass top-m lists (allocated by set_residual)
   int topm_nseg = 0;                       // segments per row of this call's lists, 0 = none
+  bool topm_merged = false;                // this call's finish also merged the lists
+  double res_invT = 1.0;                   // this call's 1 / temperature
+  int merge_in_finish = 1;     // lists merged inside the finish when they fit (0: own kernel)
+  int lds_cu = 160 * 1024;                 // LDS bytes per compute unit
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
   int target_wgs_max = 6144;  // the same for the argmax pass (greedy, margin)
@@ -148,6 +152,15 @@ int tab_half(double c) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// static LDS bytes of a kernel (SIZE_MAX when the runtime cannot say)
+template <class F>
+size_t static_lds(F* kernel) {
+  hipFuncAttributes fa;
+  return hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel)) == hipSuccess
+             ? fa.sharedSizeBytes
+             : SIZE_MAX / 4;
+}
+
 // Event k (0: before the streaming pass, 1: after it, 2: after the call) of
 // the current recorded call.
 void prof_mark(spec_verify_handle* h, int k, hipStream_t s) {
@@ -187,23 +200,42 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
+  h->topm_merged = false;
   if (h->finish_seq && L.ntiles <= sv::kFMaxTiles && rows <= sv::kFMaxRows) {
     // with at least two sequences per compute unit, 512-thread workgroups
     // let two sequences share a unit, so one's scan and pick overlap the
     // other's loads (c5: 918 -> 899 us per call); below that, 1024 threads
     // keep every unit's waves on its one sequence
-    if (B >= 2 * h->n_cu)
-      hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlockHalf, false>), dim3(B),
-                         dim3(sv::kFinishBlockHalf), 0, s, K, V, L.nseg,
-                         h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
-                         out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats,
-                         h->aux_p, h->aux_q, h->aux_z, nullptr);
-    else
-      hipLaunchKernelGGL((sv::finish_seq<DT, VEC, sv::kFinishBlock, false>), dim3(B),
-                         dim3(sv::kFinishBlock), 0, s, K, V, L.nseg,
-                         h->parts, target, draft, tokens, uniforms, c, c64, n_half, h->rules,
-                         out_tokens, out_len, hist, h->ema, h->steps, h->decay, h->stats,
-                         h->aux_p, h->aux_q, h->aux_z, nullptr);
+    const bool half = B >= 2 * h->n_cu;
+    const int NT = half ? sv::kFinishBlockHalf : sv::kFinishBlock;
+    auto kern = half ? sv::finish_seq<DT, VEC, sv::kFinishBlockHalf, false>
+                     : sv::finish_seq<DT, VEC, sv::kFinishBlock, false>;
+    // the lists' merge inside the finish, one wavefront per drafted position
+    // beside the scan, when its keys fit in the LDS the finish leaves (one
+    // or two workgroups per compute unit as above); else drift_merge after it
+    sv::MergeJob mj;
+    size_t dyn = 0;
+    if (topm && h->merge_in_finish && K < NT / sv::kWave) {
+      const size_t need = size_t(K) * sv::merge_lds_words(L.nseg, h->drift_m, V) * 8;
+      static const size_t lds_static[2] = {static_lds(sv::finish_seq<DT, VEC, sv::kFinishBlock,
+                                                                    false>),
+                                           static_lds(sv::finish_seq<DT, VEC,
+                                                                    sv::kFinishBlockHalf, false>)};
+      if ((lds_static[half ? 1 : 0] + need) * (half ? 2 : 1) <= size_t(h->lds_cu)) {
+        mj.lists = h->topm_lists;
+        mj.nseg = L.nseg;
+        mj.m = h->drift_m;
+        mj.invT = h->res_invT;
+        mj.sup = h->drift_sup;
+        mj.res = h->drift_res;
+        dyn = need;
+        h->topm_merged = true;
+      }
+    }
+    hipLaunchKernelGGL(kern, dim3(B), dim3(NT), dyn, s, K, V, L.nseg, h->parts, target, draft,
+                       tokens, uniforms, c, c64, n_half, h->rules, out_tokens, out_len, hist,
+                       h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
+                       nullptr, mj);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
@@ -248,7 +280,8 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                      uniforms, c, c64, tab_half(c64), h->rules, out_tokens, out_len, hist, h->ema,
-                     h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, h->trunc.k);
+                     h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, h->trunc.k,
+                     sv::MergeJob{});
   return check_launch(h, "finish_seq (truncated)");
 }
 
@@ -299,12 +332,13 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
     hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlockHalf, true>), dim3(B),
                        dim3(sv::kFinishBlockHalf), 0, s, K, V, 1, h->parts, target, draft,
                        tokens, uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema,
-                       h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr);
+                       h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr,
+                       sv::MergeJob{});
   else
     hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                        uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
-                       h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr);
+                       h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr, sv::MergeJob{});
   return check_launch(h, "finish_seq (truncated)");
 }
 
@@ -369,6 +403,7 @@ template <int DT, int VEC>
 void launch_residual(spec_verify_handle* h, int B, bool vec, const void* target,
                      const void* draft, double invT, const int32_t* out_len, hipStream_t s) {
   const dim3 grid(unsigned(B * h->K));
+  if (h->topm_merged) return;          // done inside the finish
   if (h->topm_nseg > 0)
     hipLaunchKernelGGL(sv::drift_merge<DT>, grid, dim3(sv::kWave),
                        size_t(h->topm_nseg) * sv::kWavesPerBlock * std::min(h->drift_m, h->V) * 8,
@@ -446,6 +481,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   if (h->tiles_per_group < 1) h->tiles_per_group = 1;
   h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);
   h->finish_seq = env_int("SPEC_VERIFY_FINISH_SEQ", 1);
+  h->merge_in_finish = env_int("SPEC_VERIFY_MERGE_IN_FINISH", 1);
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return SV_EHIP;
@@ -454,6 +490,10 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device) ==
           hipSuccess && n_cu > 0)
     h->n_cu = n_cu;
+  int lds = 0;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                            h->device) == hipSuccess && lds > 0)
+    h->lds_cu = lds;
   h->ntiles_max = div_up(V, sv::kTileChunks);   // scalar path has the most tiles
   const size_t n_parts = (size_t)max_batch * (2 * K + 1) * kMaxSeg;
   const size_t n_tiles = (size_t)max_batch * h->ntiles_max;
@@ -608,6 +648,8 @@ int verify_call(spec_verify_handle* h, int B, const void* target, const void* dr
   int rc = SV_OK;
   const double c64 = kLog2e / double(temperature);
   const float c = float(c64);
+  h->topm_merged = false;
+  h->res_invT = 1.0 / double(temperature);
   const bool trunc = h->trunc.k != nullptr || h->trunc.p != nullptr;
   if (mode == SV_MODE_STOCHASTIC && trunc && h->dtype == SV_DTYPE_F32) {
     if (vec)

@@ -146,24 +146,20 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   support_residual<DT>(s_keys[0], mm, drow, trow, invT, m, out_support + o0, out_res + o0);
 }
 
-// Per drafted position: the m largest keys of the lists the streaming pass
-// stored for its draft row (nseg segments x 4 wavefronts, mm slots each,
-// empty slots 0), then the residuals. One wavefront per drafted position;
-// dynamic LDS of nseg * 4 * min(m, V) keys.
+// One wavefront: drafted position (b, i)'s support and residuals from the
+// lists the streaming pass stored for its draft row (nseg segments x 4
+// wavefronts, mm = min(m, V) slots each, empty slots 0): the m largest keys,
+// ranked, then the two log-sum-exps. keys: LDS for nseg * 4 * mm keys;
+// bins: 256 words of LDS; thr: one LDS word (all this wavefront's).
 template <int DT>
-__global__ __launch_bounds__(kWave) void drift_merge(
-    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, double invT,
-    int m, int nseg, const uint64_t* __restrict__ lists, const int32_t* __restrict__ kdraft,
-    const int32_t* __restrict__ accept_len, int32_t* __restrict__ out_support,
-    double* __restrict__ out_res) {
-  extern __shared__ uint64_t s_keys[];
-  __shared__ uint32_t s_bins[256];
-  __shared__ unsigned long long s_thr;
-  const int lane = threadIdx.x;
-  const int b = int(blockIdx.x) / K, i = int(blockIdx.x) % K;
+__device__ __forceinline__ void merge_position(const void* __restrict__ target,
+                                      const void* __restrict__ draft, int K, int V, double invT,
+                                      int m, int nseg, const uint64_t* __restrict__ lists, int b,
+                                      int i, uint64_t* keys, uint32_t* bins,
+                                      unsigned long long* thr, int32_t* __restrict__ out_support,
+                                      double* __restrict__ out_res) {
+  const int lane = threadIdx.x & (kWave - 1);
   const long long o0 = ((long long)b * K + i) * m;
-  const int kb = kdraft != nullptr ? kdraft[b] : K;
-  if (accept_len[b] < 0 || i >= kb) return no_support(m, out_support + o0, out_res + o0);
   const uint32_t mm = uint32_t(min(m, V));
   const uint64_t* L = lists + ((long long)b * K + i) * nseg * kTopmRowSlots;
   // slot e of the nseg * 4 lists of mm slots: list e / mm, slot e % mm; eight
@@ -181,19 +177,90 @@ __global__ __launch_bounds__(kWave) void drift_merge(
     for (int q = 0; q < 8; ++q) {
       const bool put = k[q] != 0ull;                   // keys are never 0
       const uint64_t mask = __ballot(put);
-      if (put) s_keys[fill + lanes_below(mask)] = k[q];
+      if (put) keys[fill + lanes_below(mask)] = k[q];
       fill += uint32_t(__popcll(mask));
     }
   }
-  if (lane == 0) s_thr = 0ull;
+  if (lane == 0) *thr = 0ull;
   wave_sync();
   TopM<DT> tm;
-  tm.init(s_keys, s_bins, &s_thr, n_slots, mm);
+  tm.init(keys, bins, thr, n_slots, mm);
   tm.fill = fill;
   tm.compact();                                 // exactly mm keys remain
-  support_residual<DT>(s_keys, mm, row_ptr<DT>(target, draft, b, K + 1 + i, K, V),
+  support_residual<DT>(keys, mm, row_ptr<DT>(target, draft, b, K + 1 + i, K, V),
                        row_ptr<DT>(target, draft, b, i, K, V), invT, m, out_support + o0,
                        out_res + o0);
+}
+
+// The residual merge run inside the per-sequence finish: its wavefront 1 + i
+// takes drafted position i (needs K < waves per workgroup) while wavefront 0
+// runs the acceptance scan. lds: per position, nseg * 4 * min(m, V) keys,
+// then 256 bin words (128 u64) and the threshold word, from lds.
+struct MergeJob {
+  const uint64_t* lists = nullptr;     // null: no merge in the finish
+  int nseg = 0, m = 0;
+  double invT = 1.0;
+  int32_t* sup = nullptr;
+  double* res = nullptr;
+};
+
+__host__ __device__ inline int merge_lds_words(int nseg, int m, int V) {
+  return nseg * kWavesPerBlock * (m < V ? m : V) + 128 + 1;
+}
+
+// Position i of sequence b after the finish's partials are combined: the
+// call's validity taken as the scan takes it (stopping rules, finite
+// normalisers of rows 0..k_b and K+1..K+k_b, drafted tokens in [0, V)), then
+// no support (invalid call, or i >= k_b) or merge_position.
+template <int DT>
+__device__ __forceinline__ void merge_in_finish(const MergeJob& mj, uint64_t* lds,
+                                                const Rules& sp, int b, int i, int K, int V,
+                                                const void* __restrict__ target,
+                                                const void* __restrict__ draft, const double* fS,
+                                                const int32_t* tok) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int kb, me;
+  bool lane_bad;
+  stops_of(sp, b, K, kb, me, lane_bad);
+  if (lane <= kb) lane_bad |= !finite_pos(fS[lane]);
+  if (lane < kb) {
+    lane_bad |= !finite_pos(fS[K + 1 + lane]);
+    const int d = tok[lane];
+    lane_bad |= !(d >= 0 && d < V);
+  }
+  const long long o0 = ((long long)b * K + i) * mj.m;
+  if (__any(lane_bad) || i >= kb) {
+    if (lane < mj.m) {
+      mj.sup[o0 + lane] = -1;
+      mj.res[o0 + lane] = __builtin_nan("");
+    }
+    return;
+  }
+  uint64_t* keys = lds + (long long)i * merge_lds_words(mj.nseg, mj.m, V);
+  const int nk = mj.nseg * kWavesPerBlock * min(mj.m, V);
+  merge_position<DT>(target, draft, K, V, mj.invT, mj.m, mj.nseg, mj.lists, b, i, keys,
+                     reinterpret_cast<uint32_t*>(keys + nk),
+                     reinterpret_cast<unsigned long long*>(keys + nk + 128), mj.sup, mj.res);
+}
+
+// Per drafted position: merge_position on one wavefront after the call's
+// outcome (accept_len < 0, or a position past k_b: no support); dynamic LDS
+// of nseg * 4 * min(m, V) keys.
+template <int DT>
+__global__ __launch_bounds__(kWave) void drift_merge(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, double invT,
+    int m, int nseg, const uint64_t* __restrict__ lists, const int32_t* __restrict__ kdraft,
+    const int32_t* __restrict__ accept_len, int32_t* __restrict__ out_support,
+    double* __restrict__ out_res) {
+  extern __shared__ uint64_t s_keys[];
+  __shared__ uint32_t s_bins[256];
+  __shared__ unsigned long long s_thr;
+  const int b = int(blockIdx.x) / K, i = int(blockIdx.x) % K;
+  const long long o0 = ((long long)b * K + i) * m;
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (accept_len[b] < 0 || i >= kb) return no_support(m, out_support + o0, out_res + o0);
+  merge_position<DT>(target, draft, K, V, invT, m, nseg, lists, b, i, s_keys, s_bins, &s_thr,
+                     out_support, out_res);
 }
 
 }  // namespace sv

@@ -18,7 +18,7 @@
 // finish gains no overlap.
 #pragma once
 
-#include "sv_kernels.hpp"
+#include "sv_drift.hpp"
 
 namespace sv {
 
@@ -799,7 +799,8 @@ __device__ __forceinline__ void finish_sequence(
     uint32_t* __restrict__ hist, double* __restrict__ ema, int32_t* __restrict__ steps,
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
     float2* sparse = nullptr, const float* fX = nullptr, const int32_t* pre_tok = nullptr,
-    const float* pre_u = nullptr, uint32_t* sparse16 = nullptr, int trunc_k = 0) {
+    const float* pre_u = nullptr, uint32_t* sparse16 = nullptr, int trunc_k = 0,
+    MergeJob mj = MergeJob{}, uint64_t* merge_lds = nullptr) {
   using C = Chunk<DT, VEC>;
   constexpr int kW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -881,6 +882,9 @@ __device__ __forceinline__ void finish_sequence(
     emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
                     decay, st, d, sp.pol);
   } else {
+    // the residual merge of position wid - 1, beside the scan
+    if (mj.lists != nullptr && wid <= K)
+      merge_in_finish<DT>(mj, merge_lds, sp, b, wid - 1, K, V, target, draft, fS, pre_tok);
     if constexpr (TABLE_IN_SCAN && DT == DT_BF16 && VEC == 8) {
       for (int i = tid - kWave; i < kTabMax; i += NT - kWave) T[i] = exp_table_entry(i, c64);
     }
@@ -1165,7 +1169,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len, uint32_t* __restrict__ hist,
     double* __restrict__ ema, int32_t* __restrict__ steps, double decay,
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
-    const int32_t* __restrict__ trunc_k) {
+    const int32_t* __restrict__ trunc_k, MergeJob mj) {
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
   constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
   __shared__ double T[kTab ? (TRUNC ? 2 * kTabMax : kTabMax) : kTab2F ? kTab2 : 1];
@@ -1183,6 +1187,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
   __shared__ float fX[TRUNC ? 1 : kFMaxRows];
   __shared__ int32_t s_tok[kWave];
   __shared__ float s_u[kWave];
+  extern __shared__ uint64_t s_merge[];     // the residual merge's keys (dynamic)
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
   if (tid >= NT - kWave) {             // the last wavefront: tokens and uniforms
@@ -1207,7 +1212,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
                                       out_len, hist, ema, steps, decay, st, aux_p, aux_q, aux_z,
                                       TRUNC && kTab2F ? sparse : nullptr, TRUNC ? nullptr : fX,
                                       s_tok, s_u, TRUNC && kTab ? sparse16 : nullptr,
-                                      trunc_k != nullptr ? trunc_k[b] : 0);
+                                      trunc_k != nullptr ? trunc_k[b] : 0,
+                                      TRUNC ? MergeJob{} : mj, s_merge);
 }
 
 __global__ void zero_hist(uint32_t* hist, int n) {

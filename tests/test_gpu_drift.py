@@ -5,7 +5,8 @@ Supports must match exactly (token ids in order); residuals within 1e-9
 Cases: a full c2 batch with per-sequence draft counts and invalid sequences,
 rows with many ties, V below m, -inf logits inside the support, draft rows
 with 70000 equal values, every route to the support (the streaming pass's
-candidate lists with one and three segments per row, the kernel that reads
+candidate lists with one and three segments per row, merged inside the
+finish or by their own kernel, the kernel that reads
 the rows itself after truncation, on rows not in 16-byte chunks and after the
 one-kernel path), verification outputs unchanged by the side output, and
 argument errors.
@@ -57,14 +58,26 @@ def _check(x, cfg, m, sup, res, alen, kb=None, label=""):
     print(f"{label}: {int((sup >= 0).sum())} support entries checked", flush=True)
 
 
-def test_residual_c2_with_draft_counts(sv):
+@pytest.mark.parametrize("merge", ["in-finish", "own-kernel"])
+def test_residual_c2_with_draft_counts(sv, monkeypatch, merge):
+    """Per-sequence draft counts and each way a sequence is invalid (a token
+    out of range, a draft count above K, a NaN in a target row and in a draft
+    row): the merge inside the finish decides validity as the scan does, and
+    its own kernel reads the scan's accept lengths."""
+    monkeypatch.setenv("SPEC_VERIFY_MERGE_IN_FINISH", "1" if merge == "in-finish" else "0")
     cfg = CONFIGS["c2"].scaled(B=32)
     x = make_inputs(cfg, 3, DEV)
-    x["tokens"][5, 0] = cfg.V + 3              # an invalid sequence
     kb = np.random.default_rng(4).integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    x["tokens"][5, 0] = cfg.V + 3              # invalid sequences
+    kb[5] = cfg.K
+    kb[7] = cfg.K + 2
+    x["target"][9, 0, 100] = float("nan")
+    x["draft"][11, 1, 50] = float("nan")
+    kb[11] = cfg.K
     sup, res, alen = _run(sv, x, cfg, 32, kb)
-    assert alen[5] == -1
-    _check(x, cfg, 32, sup, res, alen, kb, "residual/c2")
+    assert alen[5] == -1 and alen[7] == -1 and alen[9] == -1 and alen[11] == -1
+    assert (alen >= 0).sum() == cfg.B - 4
+    _check(x, cfg, 32, sup, res, alen, kb, f"residual/c2 {merge}")
 
 
 def test_residual_many_ties_and_small_m(sv):
@@ -114,13 +127,16 @@ def test_set_residual_arguments(sv):
     assert v.lib.spec_verify_set_residual(None, 8, None, None) == sv.SV_EINVAL
 
 
-@pytest.mark.parametrize("route", ["streaming", "streaming-3seg", "own-truncated", "own-scalar",
-                                   "own-one-kernel"])
+@pytest.mark.parametrize("route", ["streaming", "streaming-3seg", "streaming-merge-kernel",
+                                   "own-truncated", "own-scalar", "own-one-kernel"])
 def test_residual_routes(sv, monkeypatch, route):
     """Every route to the support: the streaming pass's lists (one and three
-    segments per row) and the kernel that reads the draft rows itself (with
-    truncation, on rows not in 16-byte chunks, after the one-kernel path)."""
+    segments per row, merged inside the finish or by their own kernel) and
+    the kernel that reads the draft rows itself (with truncation, on rows not
+    in 16-byte chunks, after the one-kernel path)."""
     monkeypatch.setenv("SPEC_VERIFY_NSEG", "3" if route == "streaming-3seg" else "0")
+    monkeypatch.setenv("SPEC_VERIFY_MERGE_IN_FINISH",
+                       "0" if route == "streaming-merge-kernel" else "1")
     monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "1" if route == "own-one-kernel" else "0")
     V = {"own-scalar": 4001, "streaming-3seg": 40000}.get(route, 8000)   # 3 segments need V/8 >= 3072
     cfg = CONFIGS["c2"].scaled(B=24, V=V)
@@ -187,12 +203,16 @@ def test_residual_c3_sampled(sv):
           flush=True)
 
 
-@pytest.mark.parametrize("route", ["streaming", "streaming-3seg", "own-scalar", "own-one-kernel"])
+@pytest.mark.parametrize("route", ["streaming", "streaming-3seg", "streaming-merge-kernel",
+                                   "own-scalar", "own-one-kernel"])
 def test_residual_fp32_routes(sv, monkeypatch, route):
     """fp32 logits (64-bit token keys) on every route: the streaming pass's
-    lists with one and three segments, the row-reading kernel on rows not in
-    16-byte chunks and after the one-kernel path; ties and -inf included."""
+    lists with one and three segments (merged inside the finish or by their
+    own kernel), the row-reading kernel on rows not in 16-byte chunks and
+    after the one-kernel path; ties and -inf included."""
     monkeypatch.setenv("SPEC_VERIFY_NSEG", "3" if route == "streaming-3seg" else "0")
+    monkeypatch.setenv("SPEC_VERIFY_MERGE_IN_FINISH",
+                       "0" if route == "streaming-merge-kernel" else "1")
     monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", "1" if route == "own-one-kernel" else "0")
     V = {"own-scalar": 4001, "streaming-3seg": 20000}.get(route, 8000)   # 3 segments: V/4 >= 3072
     cfg = CONFIGS["c1"].scaled(B=24, V=V)
