@@ -211,12 +211,14 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
     auto kern = half ? sv::finish_seq<DT, VEC, sv::kFinishBlockHalf, false>
                      : sv::finish_seq<DT, VEC, sv::kFinishBlock, false>;
     // the lists' merge inside the finish, one wavefront per drafted position
-    // beside the scan, when its keys fit in the LDS the finish leaves (one
-    // or two workgroups per compute unit as above); else drift_merge after it
+    // after its draw tiles, when a position's lists hold at most 256 slots and
+    // their keys fit in the LDS the finish leaves (one or two workgroups per
+    // compute unit as above); else drift_merge after it
     sv::MergeJob mj;
     size_t dyn = 0;
-    if (topm && h->merge_in_finish && K < NT / sv::kWave) {
-      const size_t need = size_t(K) * sv::merge_lds_words(L.nseg, h->drift_m, V) * 8;
+    if (topm && h->merge_in_finish && K < NT / sv::kWave &&
+        sv::merge_fits(L.nseg, h->drift_m, V)) {
+      const size_t need = size_t(K) * sv::merge_lds_words() * 8;
       static const size_t lds_static[2] = {static_lds(sv::finish_seq<DT, VEC, sv::kFinishBlock,
                                                                     false>),
                                            static_lds(sv::finish_seq<DT, VEC,
@@ -338,7 +340,8 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
     hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                        uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
-                       h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr, sv::MergeJob{});
+                       h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr,
+                       sv::MergeJob{});
   return check_launch(h, "finish_seq (truncated)");
 }
 

@@ -193,9 +193,13 @@ __device__ __forceinline__ void merge_position(const void* __restrict__ target,
 }
 
 // The residual merge run inside the per-sequence finish: its wavefront 1 + i
-// takes drafted position i (needs K < waves per workgroup) while wavefront 0
-// runs the acceptance scan. lds: per position, nseg * 4 * min(m, V) keys,
-// then 256 bin words (128 u64) and the threshold word, from lds.
+// takes drafted position i (needs K < waves per workgroup) once its share of
+// the draw's tiles is read, with at most 64 kMergeHeld keys per position
+// (nseg * 4 * min(m, V) list slots), so that every key stays in a register
+// of one lane: load the lists (merge_load), rank every key by counting the
+// larger ones, gather the target logits at the m selected tokens only, and
+// write the residuals (merge_in_finish).
+constexpr int kMergeHeld = 4;
 struct MergeJob {
   const uint64_t* lists = nullptr;     // null: no merge in the finish
   int nseg = 0, m = 0;
@@ -204,20 +208,65 @@ struct MergeJob {
   double* res = nullptr;
 };
 
-__host__ __device__ inline int merge_lds_words(int nseg, int m, int V) {
-  return nseg * kWavesPerBlock * (m < V ? m : V) + 128 + 1;
+// LDS words per merged position (one slot per list slot, rounded up to a
+// whole number of wavefront rows)
+__host__ __device__ inline int merge_lds_words() { return kWave * kMergeHeld; }
+__host__ __device__ inline bool merge_fits(int nseg, int m, int V) {
+  return nseg * kWavesPerBlock * (m < V ? m : V) <= kWave * kMergeHeld;
 }
 
-// Position i of sequence b after the finish's partials are combined: the
-// call's validity taken as the scan takes it (stopping rules, finite
-// normalisers of rows 0..k_b and K+1..K+k_b, drafted tokens in [0, V)), then
-// no support (invalid call, or i >= k_b) or merge_position.
+// A lane's list slots p * 64 + lane (key 0: empty).
+struct MergeHeld {
+  uint64_t key[kMergeHeld];
+};
+
+// Slot e of the nseg * 4 lists of mm slots (list e / mm, slot e % mm) into
+// keys[e] (LDS, read by the whole wavefront next) and this lane's slots into
+// h. The lists of positions this call's streaming pass skipped (past k_b, or
+// an invalid k_b) hold earlier calls' keys, or nothing written yet; they are
+// loaded all the same and never used.
 template <int DT>
-__device__ __forceinline__ void merge_in_finish(const MergeJob& mj, uint64_t* lds,
-                                                const Rules& sp, int b, int i, int K, int V,
+__device__ __forceinline__ void merge_load(const MergeJob& mj, uint64_t* keys, int b, int i,
+                                           int K, int V, MergeHeld& h) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t mm = uint32_t(min(mj.m, V));
+  const uint32_t n_slots = uint32_t(mj.nseg * kWavesPerBlock) * mm;
+  const uint64_t* L = mj.lists + ((long long)b * K + i) * mj.nseg * kTopmRowSlots;
+#pragma unroll
+  for (int p = 0; p < kMergeHeld; ++p) {
+    const uint32_t e = uint32_t(p * kWave + lane);
+    h.key[p] = e < n_slots ? L[(e / mm) * kTopmListSlots + e % mm] : 0ull;
+  }
+#pragma unroll
+  for (int p = 0; p < kMergeHeld; ++p) keys[p * kWave + lane] = h.key[p];
+}
+
+// ranks of the held keys among keys[0..n) (the number of larger keys; keys
+// are distinct, 0 is never counted)
+template <int Q>
+__device__ __forceinline__ void merge_count(const uint64_t* keys, uint32_t n, const MergeHeld& h,
+                                            uint32_t (&rank)[kMergeHeld]) {
+#pragma unroll 8
+  for (uint32_t e = 0; e < n; ++e) {
+    const uint64_t k = keys[e];
+#pragma unroll
+    for (int p = 0; p < Q; ++p) rank[p] += k > h.key[p] ? 1u : 0u;
+  }
+}
+
+// After merge_load and a wavefront sync, with the finish's partials
+// combined: the call's validity taken as the scan takes it (stopping rules, finite normalisers of
+// rows 0..k_b and K+1..K+k_b, drafted tokens in [0, V)); then no support
+// (invalid call, or i >= k_b), or the min(m, V) largest held keys, each
+// written at its rank with
+//   (x_t(v)/T - LSE_S(x_t/T)) - (x_d(v)/T - LSE_S(x_d/T)),
+// slots min(m, V)..m-1 -1 and NaN.
+template <int DT>
+__device__ __forceinline__ void merge_in_finish(const MergeJob& mj, const uint64_t* keys,
+                                                const MergeHeld& h, const Rules& sp, int b,
+                                                int i, int K, int V,
                                                 const void* __restrict__ target,
-                                                const void* __restrict__ draft, const double* fS,
-                                                const int32_t* tok) {
+                                                const double* fS, const int32_t* tok) {
   const int lane = threadIdx.x & (kWave - 1);
   int kb, me;
   bool lane_bad;
@@ -229,6 +278,7 @@ __device__ __forceinline__ void merge_in_finish(const MergeJob& mj, uint64_t* ld
     lane_bad |= !(d >= 0 && d < V);
   }
   const long long o0 = ((long long)b * K + i) * mj.m;
+  const uint32_t mm = uint32_t(min(mj.m, V));
   if (__any(lane_bad) || i >= kb) {
     if (lane < mj.m) {
       mj.sup[o0 + lane] = -1;
@@ -236,11 +286,55 @@ __device__ __forceinline__ void merge_in_finish(const MergeJob& mj, uint64_t* ld
     }
     return;
   }
-  uint64_t* keys = lds + (long long)i * merge_lds_words(mj.nseg, mj.m, V);
-  const int nk = mj.nseg * kWavesPerBlock * min(mj.m, V);
-  merge_position<DT>(target, draft, K, V, mj.invT, mj.m, mj.nseg, mj.lists, b, i, keys,
-                     reinterpret_cast<uint32_t*>(keys + nk),
-                     reinterpret_cast<unsigned long long*>(keys + nk + 128), mj.sup, mj.res);
+  const uint32_t n_slots = uint32_t(mj.nseg * kWavesPerBlock) * mm;
+  uint32_t rank[kMergeHeld] = {};
+  if (n_slots <= 2u * kWave) merge_count<2>(keys, n_slots, h, rank);
+  else merge_count<kMergeHeld>(keys, n_slots, h, rank);
+  // the target logit gathered at the selected tokens only (each read takes
+  // a whole cache line); the draft logit is the value its key encodes (the
+  // keys of -0 and +0 agree, and the residual does not tell them apart)
+  const void* trow = row_ptr<DT>(target, nullptr, b, i, K, V);
+  bool sel[kMergeHeld];
+  float xt[kMergeHeld];
+#pragma unroll
+  for (int p = 0; p < kMergeHeld; ++p) {
+    sel[p] = h.key[p] != 0ull && rank[p] < mm;
+    xt[p] = sel[p] ? load_logit<DT>(trow, int(~uint32_t(h.key[p]))) : 0.0f;
+  }
+  double at[kMergeHeld], ad[kMergeHeld];
+  double mt = -__builtin_inf(), md = -__builtin_inf();
+#pragma unroll
+  for (int p = 0; p < kMergeHeld; ++p) {
+    const float xd = order_floor<DT>(uint32_t(h.key[p] >> 32));
+    at[p] = sel[p] ? double(xt[p]) * mj.invT : -__builtin_inf();
+    ad[p] = sel[p] ? double(xd) * mj.invT : -__builtin_inf();
+    mt = fmax(mt, at[p]);
+    md = fmax(md, ad[p]);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    mt = fmax(mt, __shfl_xor(mt, o, kWave));
+    md = fmax(md, __shfl_xor(md, o, kWave));
+  }
+  double et = 0.0, ed = 0.0;
+#pragma unroll
+  for (int p = 0; p < kMergeHeld; ++p) {
+    et += sel[p] ? exp(at[p] - mt) : 0.0;
+    ed += sel[p] ? exp(ad[p] - md) : 0.0;
+  }
+  const double lse_t = mt + log(wave_sum(et));
+  const double lse_d = md + log(wave_sum(ed));
+#pragma unroll
+  for (int p = 0; p < kMergeHeld; ++p) {
+    if (sel[p]) {
+      mj.sup[o0 + rank[p]] = int32_t(~uint32_t(h.key[p]));
+      mj.res[o0 + rank[p]] = (at[p] - lse_t) - (ad[p] - lse_d);
+    }
+  }
+  if (uint32_t(lane) >= mm && lane < mj.m) {
+    mj.sup[o0 + lane] = -1;
+    mj.res[o0 + lane] = __builtin_nan("");
+  }
 }
 
 // Per drafted position: merge_position on one wavefront after the call's

@@ -788,7 +788,11 @@ __device__ __forceinline__ void pick_unscaled(int b, int K, int ntiles, long lon
 // one table and the draw compares each value's order key with its row's
 // threshold (without TRUNC, T is one table built by the caller, or, with
 // TABLE_IN_SCAN, by wavefronts 1.. while wavefront 0 runs the scan).
-template <int DT, int VEC, int NT, bool TRUNC, bool TABLE_IN_SCAN>
+struct NoSideWork {
+  __device__ void operator()() const {}
+};
+
+template <int DT, int VEC, int NT, bool TRUNC, bool TABLE_IN_SCAN, class SideWork = NoSideWork>
 __device__ __forceinline__ void finish_sequence(
     int b, int K, int V, const void* __restrict__ target, const void* __restrict__ draft,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, float c, double c64,
@@ -800,7 +804,7 @@ __device__ __forceinline__ void finish_sequence(
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
     float2* sparse = nullptr, const float* fX = nullptr, const int32_t* pre_tok = nullptr,
     const float* pre_u = nullptr, uint32_t* sparse16 = nullptr, int trunc_k = 0,
-    MergeJob mj = MergeJob{}, uint64_t* merge_lds = nullptr) {
+    SideWork side = SideWork{}) {
   using C = Chunk<DT, VEC>;
   constexpr int kW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -882,9 +886,6 @@ __device__ __forceinline__ void finish_sequence(
     emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
                     decay, st, d, sp.pol);
   } else {
-    // the residual merge of position wid - 1, beside the scan
-    if (mj.lists != nullptr && wid <= K)
-      merge_in_finish<DT>(mj, merge_lds, sp, b, wid - 1, K, V, target, draft, fS, pre_tok);
     if constexpr (TABLE_IN_SCAN && DT == DT_BF16 && VEC == 8) {
       for (int i = tid - kWave; i < kTabMax; i += NT - kWave) T[i] = exp_table_entry(i, c64);
     }
@@ -894,7 +895,10 @@ __device__ __forceinline__ void finish_sequence(
   }
   __syncthreads();
   const DrawRow dr = s_dr;
-  if (dr.j < 0) return;
+  if (dr.j < 0) {
+    side();
+    return;
+  }
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
   if constexpr (TRUNC && kTab) {
     for (int i = tid; i < kTabMax; i += NT) {
@@ -989,6 +993,7 @@ __device__ __forceinline__ void finish_sequence(
       }
     }
   }
+  side();
   __syncthreads();
 
   // ---- 4. pick ----
@@ -1206,14 +1211,27 @@ __global__ __launch_bounds__(NT) void finish_seq(
     else fX[r] = pr->m;
   }
   __syncthreads();
+  // the residual merge of drafted position wid - 1 on wavefront wid, once
+  // its share of the draw tiles is done (the lower wavefronts finish their
+  // tiles first) or when the call draws nothing
+  const int wid = tid / kWave;
+  const bool mwave = !TRUNC && mj.lists != nullptr && wid >= 1 && wid <= K;
+  auto merge = [&]() {
+    if (mwave) {
+      uint64_t* mkeys = s_merge + (wid - 1) * merge_lds_words();
+      MergeHeld held;
+      merge_load<DT>(mj, mkeys, b, wid - 1, K, V, held);
+      wave_sync();
+      merge_in_finish<DT>(mj, mkeys, held, sp, b, wid - 1, K, V, target, fS, s_tok);
+    }
+  };
   // the fp32 table does not depend on the truncation: built during the scan
   finish_sequence<DT, VEC, NT, TRUNC, !TRUNC || DT == DT_F32>(b, K, V, target, draft, tokens, uniforms, c, c64, sp,
                                       n_half, T, fR, fS, fK, tiles, s_dr, psh, out_tokens,
                                       out_len, hist, ema, steps, decay, st, aux_p, aux_q, aux_z,
                                       TRUNC && kTab2F ? sparse : nullptr, TRUNC ? nullptr : fX,
                                       s_tok, s_u, TRUNC && kTab ? sparse16 : nullptr,
-                                      trunc_k != nullptr ? trunc_k[b] : 0,
-                                      TRUNC ? MergeJob{} : mj, s_merge);
+                                      trunc_k != nullptr ? trunc_k[b] : 0, merge);
 }
 
 __global__ void zero_hist(uint32_t* hist, int n) {
