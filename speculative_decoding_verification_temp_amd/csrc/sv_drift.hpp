@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   __shared__ uint32_t s_stage_at[kDriftWaves][kVector ? kTopmStage : 1];
   __shared__ uint32_t s_count[kDriftWaves];
   __shared__ unsigned long long s_thr;
+  __shared__ uint32_t s_wg[8];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int b = int(blockIdx.x) / K, i = int(blockIdx.x) % K;
   const long long o0 = ((long long)b * K + i) * m;
@@ -78,6 +79,11 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
   const long long nchunks = V / VEC;
   constexpr long long kPerIt = (long long)kDriftBlock * kDriftUnroll;
   const long long nit = (nchunks + kPerIt - 1) / kPerIt;
+  // with a whole first group, every wavefront's threshold starts from the
+  // workgroup's 256 thread maxima of that group (their m-th largest is at
+  // most the row's m-th largest value): far fewer candidates than from one
+  // wavefront's chunk maxima
+  const bool wg_seed = kVector && nchunks >= kPerIt;
   auto load_group = [&](long long it, raw_t (&raw)[kDriftUnroll]) {
 #pragma unroll
     for (int u = 0; u < kDriftUnroll; ++u) {
@@ -95,7 +101,21 @@ __global__ __launch_bounds__(kDriftBlock) void drift_residual(
         cm[u] = chunk_max<DT>(raw[u]);
         ok |= c0 + (long long)u * kDriftBlock < nchunks ? 1u << u : 0u;
       }
-      if (it == 0) tm.template seed<kDriftUnroll>(cm, ok);   // start the threshold
+      if (it == 0 && wg_seed) {        // uniform: every thread is here
+        float gm = cm[0];
+#pragma unroll
+        for (int u = 1; u < kDriftUnroll; ++u) gm = fmaxf(gm, cm[u]);
+        const uint32_t gbits = __float_as_uint(gm);
+        uint32_t key = DT == DT_BF16 ? bf16_key(gbits >> 16) : order_key<DT_F32>(gbits);
+        if (!(gm == gm)) key = 0u;    // (a NaN counts as nothing)
+        const uint32_t t =
+            wg_kth_top16<DT == DT_BF16 ? 16 : 32>(key, tm.want, &s_bins[0][0], s_wg);
+        tm.thr = uint64_t(t) << 32;
+        tm.thr_f = order_floor<DT>(t);
+        if (tid == 0) atomicMax(&s_thr, (unsigned long long)tm.thr);
+      } else if (it == 0) {
+        tm.template seed<kDriftUnroll>(cm, ok);   // start the threshold
+      }
 #pragma unroll
       for (int u = 0; u < kDriftUnroll; ++u) {
         const long long cu = c0 + (long long)u * kDriftBlock;
