@@ -125,6 +125,10 @@ typedef struct spec_verify_stats {
  *   SPEC_VERIFY_TRUNC32_ONE      0: float32 rows the list pass hands over
  *                                (top-p alone, top-k past its lists or tied)
  *                                skip the one-read pass that follows it (1)
+ *   SPEC_VERIFY_MERGE_IN_FINISH  0: the residual side output's candidate
+ *                                lists are merged by a kernel of their own
+ *                                after the call instead of inside the
+ *                                per-sequence finish (1)
  */
 int spec_verify_init(spec_verify_handle **h, int max_batch, int K, int V,
                      int logits_dtype, double ema_decay);
@@ -289,11 +293,13 @@ int spec_verify_set_policy(spec_verify_handle *h, const float *draft_conf, doubl
  * "Shared top m" is read as the draft's top m. Positions i >= k_b, invalid
  * sequences and slots s >= V hold -1 and NaN. Arrays are device pointers of
  * [max_batch][K][m] entries (int32 and float64), caller-owned, written by
- * later calls on their stream after the verification itself. Where the
- * call's streaming pass reads 16-byte chunks of bf16 rows, that pass also
- * keeps the draft rows' top-m candidates and one small kernel per call
- * finishes the output; otherwise (truncation, one kernel per sequence, rows
- * not in 16-byte chunks) one extra kernel reads each draft row once more.
+ * later calls on their stream, by the call's own kernels or one kernel after
+ * them. Where the call's streaming pass reads 16-byte chunks (bf16 or fp32
+ * rows), that pass also keeps the draft rows' top-m candidates, and the
+ * per-sequence finish merges them (or, when they do not fit beside it, one
+ * small kernel after the call); otherwise (truncation, one kernel per
+ * sequence, rows not in 16-byte chunks) one extra kernel reads each draft
+ * row once more.
  * The first call with out_support set allocates the candidate lists,
  * max_batch * K * 32 KiB on the handle's device, kept until
  * spec_verify_destroy (SV_ENOMEM if that fails); spec_verify itself still
