@@ -2,7 +2,8 @@
 
 Supports must match exactly (token ids in order); residuals within 1e-9
 (both sides sum the same 32 float64 exponentials in different orders).
-Cases: a full c2 batch with per-sequence draft counts and invalid sequences,
+Cases: a full c2 batch with per-sequence draft counts and invalid sequences
+(also as the second call on a verifier whose first call read every row),
 rows with many ties, V below m, -inf logits inside the support, draft rows
 with 70000 equal values, every route to the support (the streaming pass's
 candidate lists with one and three segments per row, merged inside the
@@ -152,6 +153,33 @@ def test_residual_routes(sv, monkeypatch, route):
     torch.cuda.synchronize()
     _check(x, cfg, 16, sup.cpu().numpy(), res.cpu().numpy(), alen.cpu().numpy(),
            label=f"residual/{route}")
+
+
+@pytest.mark.parametrize("merge", ["in-finish", "own-kernel"])
+def test_residual_second_call_with_draft_counts(sv, monkeypatch, merge):
+    """Two calls on one verifier: the first reads every row and leaves its
+    candidate lists behind; the second has per-sequence draft counts (and a
+    draft count above K), so its streaming pass skips rows whose lists still
+    hold the first call's keys. Every output of the second call matches the
+    oracle: the skipped positions get -1 and NaN, the others their own rows'
+    support."""
+    monkeypatch.setenv("SPEC_VERIFY_MERGE_IN_FINISH", "1" if merge == "in-finish" else "0")
+    cfg = CONFIGS["c2"].scaled(B=32)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, torch.bfloat16)
+    sup, res = v.set_residual(32)
+    x1 = make_inputs(cfg, 21, DEV)
+    v.verify(x1["target"], x1["draft"], x1["tokens"], x1["uniforms"], x1["T"])
+    torch.cuda.synchronize()
+    x2 = make_inputs(cfg, 22, DEV)
+    kb = np.random.default_rng(23).integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    kb[3] = cfg.K + 1
+    v.set_stops(-1, torch.as_tensor(kb, device=DEV).contiguous(), None)
+    tok, alen, hist = v.verify(x2["target"], x2["draft"], x2["tokens"], x2["uniforms"], x2["T"])
+    torch.cuda.synchronize()
+    a = alen.cpu().numpy()
+    assert a[3] == -1 and (a >= 0).sum() == cfg.B - 1
+    _check(x2, cfg, 32, sup.cpu().numpy(), res.cpu().numpy(), a, kb,
+           f"residual/second call {merge}")
 
 
 def test_residual_leaves_verification_unchanged(sv):
