@@ -9,7 +9,8 @@ with 70000 equal values, every route to the support (the streaming pass's
 candidate lists with one and three segments per row, merged inside the
 finish or by their own kernel, the kernel that reads
 the rows itself after truncation, on rows not in 16-byte chunks and after the
-one-kernel path), verification outputs unchanged by the side output, and
+one-kernel path, also on full-length truncated rows with a row handed to the
+full-histogram pass), verification outputs unchanged by the side output, and
 argument errors.
 """
 
@@ -180,6 +181,38 @@ def test_residual_second_call_with_draft_counts(sv, monkeypatch, merge):
     assert a[3] == -1 and (a >= 0).sum() == cfg.B - 1
     _check(x2, cfg, 32, sup.cpu().numpy(), res.cpu().numpy(), a, kb,
            f"residual/second call {merge}")
+
+
+def test_residual_truncated_full_rows(sv):
+    """Truncation and the residual side output on full-length c3 rows (the
+    row-reading kernel, its wavefronts' thresholds seeded from the
+    workgroup's first group): a draft row with a value outside the window
+    pass's bins (its row goes on to the full-histogram pass), a draft row
+    with a 70000-way tie at the top, -inf values in the support, 40 tied
+    values at a row's start and per-sequence draft counts; every position
+    against the oracle."""
+    cfg = CONFIGS["c3"].scaled(B=6)
+    x = make_inputs(cfg, 31, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(32)
+    x["draft"][0, 1, 777] = 200.0                     # outside the window (|x| >= 2^7)
+    perm = torch.randperm(cfg.V, generator=g, device=DEV)
+    x["draft"][1, 2, perm[:70000]] = 9.0              # a 70000-way tie above every other value
+    x["draft"][2, 0, ::2] = float("-inf")
+    x["draft"][3, 3, :40] = 30.0                      # the top 40 tied at the row start
+    kb = np.array([7, 7, 7, 5, 7, 2], dtype=np.int32)
+    v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype)
+    v.set_truncation(torch.tensor([50, 20, 0, 1000, 50, 3], dtype=torch.int32, device=DEV),
+                     torch.tensor([0.9, 1.0, 0.95, 0.5, 1.0, 0.9], dtype=torch.float32,
+                                  device=DEV))
+    v.set_stops(-1, torch.as_tensor(kb, device=DEV).contiguous(), None)
+    sup, res = v.set_residual(32)
+    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"])
+    torch.cuda.synchronize()
+    a = alen.cpu().numpy()
+    assert np.all(a >= 0)
+    _check(x, cfg, 32, sup.cpu().numpy(), res.cpu().numpy(), a, kb,
+           "residual/truncated full rows")
 
 
 def test_residual_leaves_verification_unchanged(sv):
