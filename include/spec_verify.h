@@ -116,6 +116,10 @@ typedef struct spec_verify_stats {
  *                                sequence (that path is always used when a row
  *                                has more than 256 draw tiles)
  *   SPEC_VERIFY_TILES_PER_GROUP  draw tiles per workgroup on that path (16)
+ *   SPEC_VERIFY_CLAIM_TILES      0: the per-sequence finish gives wavefront w
+ *                                the draw tiles w, w + 16, ... instead of
+ *                                each wavefront claiming the next tile from a
+ *                                counter in LDS (1)
  *   SPEC_VERIFY_FUSED_MIN_B      smallest batch that streams and finishes each
  *                                sequence in one kernel (0 = never)
  *   SPEC_VERIFY_TRUNC32_LIST     0: float32 truncation without the one-read

@@ -57,6 +57,7 @@ struct spec_verify_handle {
   int tiles_per_group = 16;           // draw tiles per workgroup (tuning)
   int fused_min_batch = 0;            // smallest batch for one workgroup per sequence, 0 = off
   int finish_seq = 1;                 // scan + draw + pick in one kernel after the streaming pass
+  int claim_tiles = 1;                // finish_seq's wavefronts claim draw tiles from a counter
   double* ema = nullptr;
   int32_t* steps = nullptr;
   int32_t* streak = nullptr;          // tree-shape policy state, per slot
@@ -237,7 +238,7 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
     hipLaunchKernelGGL(kern, dim3(B), dim3(NT), dyn, s, K, V, L.nseg, h->parts, target, draft,
                        tokens, uniforms, c, c64, n_half, h->rules, out_tokens, out_len, hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
-                       nullptr, mj);
+                       nullptr, mj, h->claim_tiles);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
@@ -283,7 +284,7 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                      uniforms, c, c64, tab_half(c64), h->rules, out_tokens, out_len, hist, h->ema,
                      h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, h->trunc.k,
-                     sv::MergeJob{});
+                     sv::MergeJob{}, h->claim_tiles);
   return check_launch(h, "finish_seq (truncated)");
 }
 
@@ -335,13 +336,13 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
                        dim3(sv::kFinishBlockHalf), 0, s, K, V, 1, h->parts, target, draft,
                        tokens, uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema,
                        h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr,
-                       sv::MergeJob{});
+                       sv::MergeJob{}, h->claim_tiles);
   else
     hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
                        uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
                        h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr,
-                       sv::MergeJob{});
+                       sv::MergeJob{}, h->claim_tiles);
   return check_launch(h, "finish_seq (truncated)");
 }
 
@@ -484,6 +485,7 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
   if (h->tiles_per_group < 1) h->tiles_per_group = 1;
   h->fused_min_batch = env_int("SPEC_VERIFY_FUSED_MIN_B", 0);
   h->finish_seq = env_int("SPEC_VERIFY_FINISH_SEQ", 1);
+  h->claim_tiles = env_int("SPEC_VERIFY_CLAIM_TILES", 1);
   h->merge_in_finish = env_int("SPEC_VERIFY_MERGE_IN_FINISH", 1);
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;

@@ -351,27 +351,32 @@ __device__ __forceinline__ void unit_sums(const double* Tt, const double* Td, ui
   }
 }
 
-// Tile sums of the draw rows. Wavefront w takes tiles w, w + NW, ... as a
-// stream of units, with the units of one tile in flight: the loads of unit
-// i + kUnits are issued right after unit i has been summed, so a wavefront
-// keeps kUnits - 1 units of loads outstanding while it computes. Chunks past
-// the row end are clamped to the last chunk for loading and skipped in the
-// sums.
+// Tile sums of the draw rows. A wavefront takes its tiles as a stream of
+// units, with the units of one tile in flight: the loads of unit i + kUnits
+// are issued right after unit i has been summed, so a wavefront keeps
+// kUnits - 1 units of loads outstanding while it computes. Wavefront w takes
+// tiles w, w + NW, w + 2 NW, ... or, with a claim counter in LDS (next, set
+// to 0 before the phase), each time the lowest tile no wavefront has claimed
+// yet: the wavefronts of a SIMD do not progress at one rate, and claiming
+// lets the faster ones take more tiles (and a wavefront with other work
+// joins when it is done). Either way a wavefront's tiles come in increasing
+// order and every tile but the row's last is whole, so only the last tile a
+// wavefront takes can be ragged. Chunks past the row end are clamped to the
+// last chunk for loading and skipped in the sums.
 template <int DT, int VEC, bool RESID, int NW, bool MASK = false>
 __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* Td,
                                                const void* trow, const void* drow,
                                                const DrawRow& dr, double c, int ntiles,
                                                long long nchunks, TileSums* tiles, int wid,
-                                               int lane) {
+                                               int lane, int* next = nullptr) {
   using C = Chunk<DT, VEC>;
   const double rho2 = RESID ? __builtin_ldexp(dr.rho, int(dr.R_t) - int(dr.R_d)) : 0.0;
   const int st = -int(dr.R_t), sd = -int(dr.R_d);
-  const int my_tiles = wid < ntiles ? (ntiles - 1 - wid) / NW + 1 : 0;
-  auto unit_c0 = [&](int ti, int u) -> long long {
-    return (long long)(wid + ti * NW) * kTileChunks + (long long)u * kUnitChunks * kWave + lane;
+  auto unit_c0 = [&](int t, int u) -> long long {
+    return (long long)t * kTileChunks + (long long)u * kUnitChunks * kWave + lane;
   };
-  auto load_unit = [&](int ti, int u, UnitBuf& b) {
-    const long long c0 = unit_c0(ti, u);
+  auto load_unit = [&](int t, int u, UnitBuf& b) {
+    const long long c0 = unit_c0(t, u);
 #pragma unroll
     for (int k = 0; k < kUnitChunks; ++k) {
       const long long ci = min(c0 + (long long)k * kWave, nchunks - 1);
@@ -379,7 +384,7 @@ __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* T
       if constexpr (RESID) b.d[k] = C::load(drow, ci);
     }
   };
-  auto finish_tile = [&](int ti, double E, double Ed, double A, double Bd) {
+  auto finish_tile = [&](int t, double E, double Ed, double A, double Bd) {
     E = wave_sum(E);
     if constexpr (RESID) {
       Ed = wave_sum(Ed);
@@ -392,48 +397,58 @@ __device__ __forceinline__ void tiles_unscaled(const double* Tt, const double* T
       ts.Ed = RESID ? __builtin_ldexp(Ed, sd) : 0.0;
       ts.A = RESID ? __builtin_ldexp(A, st) : 0.0;
       ts.Bd = RESID ? __builtin_ldexp(Bd, sd) : 0.0;
-      tiles[wid + ti * NW] = ts;
+      tiles[t] = ts;
     }
   };
-  if (my_tiles == 0) return;
+  // this wavefront's tile after t (its first for t < 0)
+  auto claim = [&](int t) -> int {
+    if (next == nullptr) return t < 0 ? wid : t + NW;
+    int v = 0;
+    if (lane == 0) v = atomicAdd(next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int t = claim(-1);
+  if (t >= ntiles) return;
   UnitBuf b[kUnits];
 #pragma unroll
-  for (int u = 0; u < kUnits; ++u) load_unit(0, u, b[u]);
-  // every tile but this wavefront's last is whole (only the row's last tile
-  // can be ragged), and its loop body issues its loads unconditionally
-  int ti = 0;
-  for (; ti + 1 < my_tiles; ++ti) {
+  for (int u = 0; u < kUnits; ++u) load_unit(t, u, b[u]);
+  // a tile with a successor is whole, and its loop body issues the
+  // successor's loads unconditionally
+  int tn = claim(t);
+  while (tn < ntiles) {
     double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       double e, ed, a, bd;
-      unit_sums<DT, RESID, false, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u),
+      unit_sums<DT, RESID, false, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(t, u),
                                         nchunks, rho2, c, e, ed, a, bd);
-      load_unit(ti + 1, u, b[u]);
+      load_unit(tn, u, b[u]);
       E += e;
       Ed += ed;
       A += a;
       Bd += bd;
     }
-    finish_tile(ti, E, Ed, A, Bd);
+    finish_tile(t, E, Ed, A, Bd);
+    t = tn;
+    tn = claim(t);
   }
   double E = 0.0, Ed = 0.0, A = 0.0, Bd = 0.0;
-  const bool whole = (long long)(wid + ti * NW + 1) * kTileChunks <= nchunks;
+  const bool whole = (long long)(t + 1) * kTileChunks <= nchunks;
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
     double e, ed, a, bd;
     if (whole)
-      unit_sums<DT, RESID, false, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u),
+      unit_sums<DT, RESID, false, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(t, u),
                                         nchunks, rho2, c, e, ed, a, bd);
     else
-      unit_sums<DT, RESID, true, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(ti, u),
+      unit_sums<DT, RESID, true, MASK>(Tt, Td, dr.thr_t, dr.thr_d, b[u], unit_c0(t, u),
                                        nchunks, rho2, c, e, ed, a, bd);
     E += e;
     Ed += ed;
     A += a;
     Bd += bd;
   }
-  finish_tile(ti, E, Ed, A, Bd);
+  finish_tile(t, E, Ed, A, Bd);
 }
 
 // Tile sums of truncated fp32 draw rows. Such rows keep few of their values
@@ -804,13 +819,17 @@ __device__ __forceinline__ void finish_sequence(
     double decay, DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
     float2* sparse = nullptr, const float* fX = nullptr, const int32_t* pre_tok = nullptr,
     const float* pre_u = nullptr, uint32_t* sparse16 = nullptr, int trunc_k = 0,
-    SideWork side = SideWork{}) {
+    SideWork side = SideWork{}, int* tile_ctr = nullptr) {
   using C = Chunk<DT, VEC>;
   constexpr int kW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const long long nchunks = V / VEC;
   auto row_base = [&](int r) -> const void* { return row_ptr<DT>(target, draft, b, r, K, V); };
   // ---- 2. acceptance scan on wavefront 0 ----
+  // (its emission, histogram and EMA update follow the barrier, off the path
+  // to the draw: the EMA update waits on a global load)
+  int e_kb = 0, e_n = 0, e_cpos = -1, e_d = 0;
+  bool e_bad = true;
   if (wid == 0) {
     int kb, m;
     bool lane_bad;
@@ -878,13 +897,17 @@ __device__ __forceinline__ void finish_sequence(
       dr.thr_t = ktj;
       dr.thr_d = kdj;
       s_dr = dr;
+      if (tile_ctr != nullptr) *tile_ctr = 0;   // the draw's first unclaimed tile
       if (dr.j < 0 && aux_z != nullptr) aux_z[b] = -1.0;
     }
     const unsigned long long zqm = __ballot(zq && lane < j);
     if (lane == 0 && !bad && zqm)
       atomicAdd(&st->zero_q_accepts, (unsigned long long)__popcll(zqm));
-    emit_and_update(lane, b, K, kb, w.n, w.cpos, -1, bad, out_tokens, out_len, hist, ema, steps,
-                    decay, st, d, sp.pol);
+    e_kb = kb;
+    e_n = w.n;
+    e_cpos = w.cpos;
+    e_d = d;
+    e_bad = bad;
   } else {
     if constexpr (TABLE_IN_SCAN && DT == DT_BF16 && VEC == 8) {
       for (int i = tid - kWave; i < kTabMax; i += NT - kWave) T[i] = exp_table_entry(i, c64);
@@ -894,6 +917,9 @@ __device__ __forceinline__ void finish_sequence(
     }
   }
   __syncthreads();
+  if (wid == 0)
+    emit_and_update(lane, b, K, e_kb, e_n, e_cpos, -1, e_bad, out_tokens, out_len, hist, ema,
+                    steps, decay, st, e_d, sp.pol);
   const DrawRow dr = s_dr;
   if (dr.j < 0) {
     side();
@@ -913,7 +939,6 @@ __device__ __forceinline__ void finish_sequence(
   const double* Td = (TRUNC && kTab) ? T + kTabMax : T;
 
   // ---- 3. draw tile sums of row pair j (or target row K) ----
-  // wavefront w takes tiles w, w + kW, ...
   DrawRows<DT, VEC> W;
   W.init(target, draft, dr, b, K, V, c64);
   const int ntiles = int((nchunks + kTileChunks - 1) / kTileChunks);
@@ -923,6 +948,11 @@ __device__ __forceinline__ void finish_sequence(
   constexpr bool kFast = (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4);
   if constexpr (kFast)
     unscaled = fabsf(dr.R_t) <= kUnscaledMaxR && (!W.residual || fabsf(dr.R_d) <= kUnscaledMaxR);
+  // with claimed tiles a wavefront with side work does it first and then
+  // joins the draw; with fixed tiles the lower wavefronts, which finish their
+  // tiles first, do it afterwards
+  const bool side_first = tile_ctr != nullptr && unscaled;
+  if (side_first) side();
   if (unscaled) {
     // truncated fp32 rows: gather the kept values first (a pair of rows
     // without truncation keeps every value: the dense loop)
@@ -959,10 +989,10 @@ __device__ __forceinline__ void finish_sequence(
       if (gathered) {
       } else if (W.residual) {
         tiles_unscaled<DT, VEC, true, kW, kMask>(Tt, Td, W.trow, W.drow, dr, c64, ntiles,
-                                                 nchunks, tiles, wid, lane);
+                                                 nchunks, tiles, wid, lane, tile_ctr);
       } else {
         tiles_unscaled<DT, VEC, false, kW, kMask>(Tt, Td, W.trow, W.drow, dr, c64, ntiles,
-                                                  nchunks, tiles, wid, lane);
+                                                  nchunks, tiles, wid, lane, tile_ctr);
       }
     }
   } else {
@@ -993,7 +1023,7 @@ __device__ __forceinline__ void finish_sequence(
       }
     }
   }
-  side();
+  if (!side_first) side();
   __syncthreads();
 
   // ---- 4. pick ----
@@ -1174,7 +1204,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_len, uint32_t* __restrict__ hist,
     double* __restrict__ ema, int32_t* __restrict__ steps, double decay,
     DevStats* __restrict__ st, double* aux_p, double* aux_q, double* aux_z,
-    const int32_t* __restrict__ trunc_k, MergeJob mj) {
+    const int32_t* __restrict__ trunc_k, MergeJob mj, int claim) {
   constexpr bool kTab = (DT == DT_BF16 && VEC == 8);
   constexpr bool kTab2F = (DT == DT_F32 && VEC == 4);
   __shared__ double T[kTab ? (TRUNC ? 2 * kTabMax : kTabMax) : kTab2F ? kTab2 : 1];
@@ -1184,6 +1214,7 @@ __global__ __launch_bounds__(NT) void finish_seq(
   __shared__ TileSums tiles[kFMaxTiles];
   __shared__ DrawRow s_dr;
   __shared__ PickShared psh;
+  __shared__ int s_claim;              // the draw's tile claim counter
   // truncated fp32 rows: the gathered value pairs, kSparseCap per wavefront
   __shared__ float2 sparse[TRUNC && kTab2F ? (NT / kWave) * kSparseCap : 1];
   __shared__ uint32_t sparse16[TRUNC && kTab ? (NT / kWave) * kSparseCap16 : 1];
@@ -1231,7 +1262,8 @@ __global__ __launch_bounds__(NT) void finish_seq(
                                       out_len, hist, ema, steps, decay, st, aux_p, aux_q, aux_z,
                                       TRUNC && kTab2F ? sparse : nullptr, TRUNC ? nullptr : fX,
                                       s_tok, s_u, TRUNC && kTab ? sparse16 : nullptr,
-                                      trunc_k != nullptr ? trunc_k[b] : 0, merge);
+                                      trunc_k != nullptr ? trunc_k[b] : 0, merge,
+                                      claim ? &s_claim : nullptr);
 }
 
 __global__ void zero_hist(uint32_t* hist, int n) {

@@ -105,16 +105,18 @@ def test_c2_forced_segments_agree(sv, monkeypatch):
 @pytest.mark.parametrize("name", ["c1", "c2"])
 def test_fused_and_pipeline_paths_agree(sv, monkeypatch, name):
     """The three stochastic paths match the oracle and each other: the
-    streaming pass then one workgroup per sequence (default), the streaming
+    streaming pass then one workgroup per sequence (default; its wavefronts
+    claim the draw tiles from a counter, or take fixed tiles), the streaming
     pass then separate scan, tile-sum and pick kernels (the path for V >
     524288), and one workgroup per sequence for everything (forced on)."""
     cfg = CONFIGS[name]
     x = make_inputs(cfg, 5, DEV)
     outs = {}
-    for path, min_b, fin in (("pipeline", "0", "1"), ("multikernel", "0", "0"),
-                             ("fused", "1", "1")):
+    for path, min_b, fin, claim in (("pipeline", "0", "1", "1"), ("fixed-tiles", "0", "1", "0"),
+                                    ("multikernel", "0", "0", "1"), ("fused", "1", "1", "1")):
         monkeypatch.setenv("SPEC_VERIFY_FUSED_MIN_B", min_b)
         monkeypatch.setenv("SPEC_VERIFY_FINISH_SEQ", fin)
+        monkeypatch.setenv("SPEC_VERIFY_CLAIM_TILES", claim)
         v, aux, tok, alen, hist = _verify(sv, x, cfg, "stochastic")
         outs[path] = (tok.clone(), alen.clone(), hist.clone(),
                       {k: t.clone() for k, t in aux.items()})
@@ -126,7 +128,7 @@ def test_fused_and_pipeline_paths_agree(sv, monkeypatch, name):
         check_invariants(tok, alen, hist, x["tokens"], cfg.V, cfg.K)
         _log(f"{name}/{path}: {rep}")
     a = outs["pipeline"]
-    for other in ("multikernel", "fused"):
+    for other in ("fixed-tiles", "multikernel", "fused"):
         b = outs[other]
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
         assert torch.allclose(a[3]["p_d"], b[3]["p_d"], rtol=1e-6, atol=0)
