@@ -1226,6 +1226,13 @@ __global__ __launch_bounds__(NT) void finish_seq(
   extern __shared__ uint64_t s_merge[];     // the residual merge's keys (dynamic)
   const int b = blockIdx.x, tid = threadIdx.x;
   const int rows = 2 * K + 1;
+  // the residual merge of drafted position wid - 1 on wavefront wid: its
+  // lists are loaded now, beside the partials, and merged after the scan
+  const int wid = tid / kWave;
+  const bool mwave = !TRUNC && mj.lists != nullptr && wid >= 1 && wid <= K;
+  MergeHeld held;
+  uint64_t* mkeys = mwave ? s_merge + (wid - 1) * merge_lds_words() : s_merge;
+  if (mwave) merge_load<DT>(mj, mkeys, b, wid - 1, K, V, held);
   if (tid >= NT - kWave) {             // the last wavefront: tokens and uniforms
     const int l = tid - (NT - kWave);
     if (l < K) s_tok[l] = tokens[(long long)b * K + l];
@@ -1242,16 +1249,11 @@ __global__ __launch_bounds__(NT) void finish_seq(
     else fX[r] = pr->m;
   }
   __syncthreads();
-  // the residual merge of drafted position wid - 1 on wavefront wid, once
-  // its share of the draw tiles is done (the lower wavefronts finish their
-  // tiles first) or when the call draws nothing
-  const int wid = tid / kWave;
-  const bool mwave = !TRUNC && mj.lists != nullptr && wid >= 1 && wid <= K;
+  // the merge itself: before the wavefront's share of the draw tiles when it
+  // claims them (the others take more), after it with fixed tiles, or when
+  // the call draws nothing
   auto merge = [&]() {
     if (mwave) {
-      uint64_t* mkeys = s_merge + (wid - 1) * merge_lds_words();
-      MergeHeld held;
-      merge_load<DT>(mj, mkeys, b, wid - 1, K, V, held);
       wave_sync();
       merge_in_finish<DT>(mj, mkeys, held, sp, b, wid - 1, K, V, target, fS, s_tok);
     }
