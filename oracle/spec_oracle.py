@@ -47,6 +47,19 @@ listed with its reason in the design notes):
     marked invalid: accept_len -1, tokens all -1, not counted in the histogram,
     EMA untouched. Needed rows: all K+1 target rows, plus all K draft rows in
     stochastic mode.
+  * Walk-order reading (optional, stochastic mode without truncation; [DVC]
+    "Verify several proposed tokens in one target pass": at the first
+    rejection the correction is drawn and later proposals are discarded;
+    [SMB] "Seeing It in Code": the walk over the drafts stops at the first
+    disagreement). The rows of position i are read only when the walk
+    reaches it, i.e. once every earlier position has been kept. The sequence
+    is then invalid only when something the walk reads is unusable: the
+    drafted token or the target or draft row of a position up to the first
+    rejection, or target row k_b when every position is kept; rows past the
+    first rejection are never looked at. End-of-sequence and budget stops
+    cut the emission, not the reading. p(d) and q(d) are NaN past the first
+    rejection. With every row and token usable the result equals that of the
+    full reading.
   * EMA: per call and slot, x = accept_len / K; the first observation of a slot
     sets it, later ones do ema = decay * ema + (1 - decay) * x.
   * Stopping rules ([DVC] "Verify several proposed tokens in one target pass"
@@ -285,14 +298,15 @@ class SequenceResult:
 def verify_sequence(target, draft, tokens, u, T: float, mode: int,
                     tau: float = 0.0, eos: int = -1, draft_len: int | None = None,
                     max_emit: int | None = None, top_k: int = 0,
-                    top_p: float = 1.0) -> SequenceResult:
+                    top_p: float = 1.0, walk_order: bool = False) -> SequenceResult:
     """Verify one sequence.
 
     target: [K+1, V] logits, draft: [K, V] logits (stochastic only),
     tokens: [K] drafted tokens, u: [K+1] uniforms (stochastic only).
     eos, draft_len (k_b) and max_emit (m_b) are the optional stopping rules,
-    top_k and top_p the optional truncation of the module docstring; the
-    defaults give the plain cycle.
+    top_k and top_p the optional truncation, walk_order the optional reading
+    of the rows in walk order, all as in the module docstring; the defaults
+    give the plain cycle.
     """
     target = np.asarray(target, dtype=np.float64)
     K = target.shape[0] - 1
@@ -302,14 +316,18 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     toks = np.asarray(tokens, dtype=np.int64).reshape(K)
     nan_k = np.full(K, np.nan)
     out = np.full(K + 1, -1, dtype=np.int64)
+    truncated = (0 < int(top_k) < V) or not (float(top_p) >= 1.0)
+    walk_order = bool(walk_order) and mode == MODE_STOCHASTIC and not truncated
 
     valid = 0 <= kb <= K and m >= 1
-    valid = valid and bool(np.all((toks[:kb] >= 0) & (toks[:kb] < V)))
-    valid = valid and all(row_is_valid(target[i]) for i in range(kb + 1))
     if mode == MODE_STOCHASTIC:
         draft = np.asarray(draft, dtype=np.float64)
-        valid = valid and all(row_is_valid(draft[i]) for i in range(kb))
-        valid = valid and float(top_p) > 0.0      # NaN compares false
+    if not walk_order:       # (walk order: rows and tokens are checked as the walk reads them)
+        valid = valid and bool(np.all((toks[:kb] >= 0) & (toks[:kb] < V)))
+        valid = valid and all(row_is_valid(target[i]) for i in range(kb + 1))
+        if mode == MODE_STOCHASTIC:
+            valid = valid and all(row_is_valid(draft[i]) for i in range(kb))
+            valid = valid and float(top_p) > 0.0      # NaN compares false
     # per-row argmax side output: rows 0..k_b (rows past k_b are not read)
     argmax = np.array([argmax_lowest(target[i]) if i <= kb and row_is_valid(target[i]) else -1
                        for i in range(K + 1)], dtype=np.int64)
@@ -325,31 +343,59 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     # 1. the ordered walk over positions 0..kb-1: j = first rejection, else kb
     if mode == MODE_STOCHASTIC:
         u = np.asarray(u, dtype=np.float64).reshape(K + 1)
-        tp = [truncated_softmax(target[i], T, top_k, top_p) for i in range(kb + 1)]
-        tq = [truncated_softmax(draft[i], T, top_k, top_p) for i in range(kb)]
-        p_rows = [p for p, _ in tp]
-        q_rows = [q for q, _ in tq]
-        # a top-p cut close to moving is a decision too (every needed row)
-        acc_dists += [(-1, d) for _, d in tp + tq if d < math.inf]
-        for i in range(kb):
-            p_d[i] = p_rows[i][toks[i]]
-            q_d[i] = q_rows[i][toks[i]]
-        j = kb
-        for i in range(kb):
+
+        def kept(i):
+            """The acceptance test of position i (counts q(d) = 0 accepts and
+            records the decision's distance to its boundary)."""
+            nonlocal zero_q
             P, Q = p_d[i], q_d[i]
             if P >= Q:
-                keep = True
                 if Q == 0.0:
                     zero_q += 1
                 if Q > 0.0:
                     acc_dists.append((i, abs(u[i] - P / Q)))
-            else:
-                ratio = P / Q
-                keep = bool(u[i] < ratio)
-                acc_dists.append((i, abs(u[i] - ratio)))
-            if not keep:
-                j = i
-                break
+                return True
+            ratio = P / Q
+            acc_dists.append((i, abs(u[i] - ratio)))
+            return bool(u[i] < ratio)
+
+        j = kb
+        if walk_order:
+            # read position i's rows only once the walk reaches it; a row or
+            # token the walk reads that is not usable makes the sequence
+            # invalid, later ones are never looked at
+            p_rows, q_rows = [], []
+            for i in range(kb):
+                if not (0 <= toks[i] < V and row_is_valid(target[i])
+                        and row_is_valid(draft[i])):
+                    return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
+                                          math.inf, valid=False)
+                p_rows.append(truncated_softmax(target[i], T)[0])
+                q_rows.append(truncated_softmax(draft[i], T)[0])
+                p_d[i] = p_rows[i][toks[i]]
+                q_d[i] = q_rows[i][toks[i]]
+                if not kept(i):
+                    j = i
+                    break
+            if j == kb:
+                if not row_is_valid(target[kb]):
+                    return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
+                                          math.inf, valid=False)
+                p_rows.append(truncated_softmax(target[kb], T)[0])
+        else:
+            tp = [truncated_softmax(target[i], T, top_k, top_p) for i in range(kb + 1)]
+            tq = [truncated_softmax(draft[i], T, top_k, top_p) for i in range(kb)]
+            p_rows = [p for p, _ in tp]
+            q_rows = [q for q, _ in tq]
+            # a top-p cut close to moving is a decision too (every needed row)
+            acc_dists += [(-1, d) for _, d in tp + tq if d < math.inf]
+            for i in range(kb):
+                p_d[i] = p_rows[i][toks[i]]
+                q_d[i] = q_rows[i][toks[i]]
+            for i in range(kb):
+                if not kept(i):
+                    j = i
+                    break
     elif mode == MODE_GREEDY:
         j = kb
         for i in range(kb):
@@ -536,7 +582,7 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
                  tau: float = 0.0, ema: EmaState | None = None,
                  rows=None, eos: int = -1, draft_len=None, max_emit=None,
                  top_k=None, top_p=None, policy: TreePolicy | None = None,
-                 conf=None) -> BatchResult:
+                 conf=None, walk_order: bool = False) -> BatchResult:
     """Verify every sequence b (or only those listed in `rows`).
 
     target [B, K+1, V], draft [B, K, V] (stochastic), tokens [B, K],
@@ -546,7 +592,8 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
     max_emit [B] (indexed by b) are the optional stopping rules, top_k [B]
     and top_p [B] the optional truncation. With `policy` (which needs `ema`)
     and conf [B] (the draft's top-1 probabilities), each sequence's next
-    tree shape is computed after its EMA update.
+    tree shape is computed after its EMA update. walk_order: the rows are
+    read in walk order (module docstring).
     """
     B = target.shape[0]
     K = target.shape[1] - 1
@@ -573,7 +620,7 @@ def verify_batch(target, draft, tokens, uniforms, T: float, mode: int,
             draft_len=None if draft_len is None else int(draft_len[b]),
             max_emit=None if max_emit is None else int(max_emit[b]),
             top_k=0 if top_k is None else int(top_k[b]),
-            top_p=1.0 if top_p is None else float(top_p[b]))
+            top_p=1.0 if top_p is None else float(top_p[b]), walk_order=walk_order)
         out.tokens[k] = res.tokens
         out.accept_len[k] = res.accept_len
         out.p_d[k] = res.p_d

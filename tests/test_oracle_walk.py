@@ -1,0 +1,202 @@
+"""Pins for the oracle's walk-order reading (stochastic mode without
+truncation): a position's rows are read only once the walk reaches it, and
+the walk reads nothing past its first rejection ([DVC] "Verify several
+proposed tokens in one target pass": at the first rejection the correction is
+drawn and later proposals are discarded; [SMB] "Seeing It in Code": the walk
+stops at the first disagreement).
+
+Pinned against things other than the walk-order code itself:
+
+  * with every row and token usable, the result is the full reading's, field
+    by field (the full reading is pinned elsewhere);
+  * the boundary of what is read, by construction: the first rejection j is
+    forced with the uniforms, then an unusable row or token is planted at
+    position j + 1 (must not matter), at j (must invalidate) and below j (must
+    invalidate); with every position kept, target row k_b must be usable and
+    target rows past k_b are never read;
+  * planted-mistake control: a walk that read one position further than its
+    first rejection would invalidate the j + 1 case, and one that stopped a
+    position early would keep the j case valid; both are caught above.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import spec_oracle as O
+
+S = O.MODE_STOCHASTIC
+
+
+def _case(rng, V, K):
+    target = rng.normal(0, 2.0, (K + 1, V))
+    draft = 0.5 * target[:K] + rng.normal(0, 2.0, (K, V))
+    q = [O.softmax_t(draft[i], 1.0) for i in range(K)]
+    toks = np.array([rng.choice(V, p=q[i]) for i in range(K)])
+    return target, draft, toks
+
+
+def _forced(rng, V, K, j):
+    """A case whose walk keeps positions < j and rejects j (j = K: keeps all):
+    positions < j get u = 0 (kept whatever the ratio, since p(d) > 0), and
+    position j gets a draft token with p < q and u just below 1."""
+    while True:
+        target, draft, toks = _case(rng, V, K)
+        u = np.zeros(K + 1)
+        u[K] = rng.random()
+        if j == K:
+            return target, draft, toks, u
+        p = O.softmax_t(target[j], 1.0)
+        q = O.softmax_t(draft[j], 1.0)
+        cand = np.flatnonzero(p < 0.5 * q)
+        if len(cand):
+            toks[j] = cand[0]
+            u[j] = 0.999999
+            return target, draft, toks, u
+
+
+def _same(a, b):
+    assert a.valid == b.valid
+    assert np.array_equal(a.tokens, b.tokens)
+    assert a.accept_len == b.accept_len
+    assert (a.z == b.z) or (math.isnan(a.z) and math.isnan(b.z))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_walk_order_equals_full_reading_on_usable_rows(seed):
+    rng = np.random.default_rng(400 + seed)
+    V, K = 16, 5
+    for _ in range(40):
+        target, draft, toks = _case(rng, V, K)
+        u = rng.random(K + 1)
+        full = O.verify_sequence(target, draft, toks, u, 1.0, S)
+        walk = O.verify_sequence(target, draft, toks, u, 1.0, S, walk_order=True)
+        _same(full, walk)
+        j = full.accept_len
+        # p(d), q(d): the same where the walk read, NaN past the rejection
+        last = j if j < K else K - 1
+        assert np.array_equal(full.p_d[:last + 1], walk.p_d[:last + 1])
+        assert np.array_equal(full.q_d[:last + 1], walk.q_d[:last + 1])
+        assert np.all(np.isnan(walk.p_d[last + 1:])) and np.all(np.isnan(walk.q_d[last + 1:]))
+
+
+BAD = {
+    "nan": lambda row: row.__setitem__(3, np.nan),
+    "+inf": lambda row: row.__setitem__(5, np.inf),
+    "all -inf": lambda row: row.__setitem__(slice(None), -np.inf),
+}
+
+
+@pytest.mark.parametrize("kind", list(BAD))
+@pytest.mark.parametrize("j", [0, 1, 3])
+def test_read_boundary_is_the_first_rejection(kind, j):
+    rng = np.random.default_rng(17 + j)
+    V, K = 12, 5
+    target, draft, toks, u = _forced(rng, V, K, j)
+    ref = O.verify_sequence(target, draft, toks, u, 1.0, S, walk_order=True)
+    assert ref.valid and ref.accept_len == j
+    for which in ("target", "draft"):
+        # past the rejection: not read
+        t2, d2 = target.copy(), draft.copy()
+        BAD[kind]((t2 if which == "target" else d2)[j + 1])
+        r = O.verify_sequence(t2, d2, toks, u, 1.0, S, walk_order=True)
+        _same(r, ref)
+        assert not O.verify_sequence(t2, d2, toks, u, 1.0, S).valid   # the full reading reads it
+        # at the rejection, and below it: read
+        for i in range(j + 1):
+            t3, d3 = target.copy(), draft.copy()
+            BAD[kind]((t3 if which == "target" else d3)[i])
+            r = O.verify_sequence(t3, d3, toks, u, 1.0, S, walk_order=True)
+            assert not r.valid and r.accept_len == -1 and np.all(r.tokens == -1)
+
+
+@pytest.mark.parametrize("j", [0, 2])
+def test_token_out_of_range_counts_only_where_read(j):
+    rng = np.random.default_rng(90 + j)
+    V, K = 10, 4
+    target, draft, toks, u = _forced(rng, V, K, j)
+    ref = O.verify_sequence(target, draft, toks, u, 1.0, S, walk_order=True)
+    t2 = toks.copy()
+    t2[j + 1] = V            # past the rejection
+    _same(O.verify_sequence(target, draft, t2, u, 1.0, S, walk_order=True), ref)
+    t3 = toks.copy()
+    t3[j] = -1               # at the rejection
+    assert not O.verify_sequence(target, draft, t3, u, 1.0, S, walk_order=True).valid
+
+
+def test_all_kept_reads_the_bonus_row_and_nothing_past_k_b():
+    rng = np.random.default_rng(5)
+    V, K = 12, 5
+    target, draft, toks, u = _forced(rng, V, K, K)
+    ref = O.verify_sequence(target, draft, toks, u, 1.0, S, walk_order=True)
+    assert ref.valid and ref.accept_len == K and ref.tokens[K] >= 0
+    t2 = target.copy()
+    t2[K, 2] = np.nan
+    assert not O.verify_sequence(t2, draft, toks, u, 1.0, S, walk_order=True).valid
+    # k_b = 3: bonus from target row 3; rows 4.. of either kind are never read
+    kb = 3
+    r = O.verify_sequence(target, draft, toks, u, 1.0, S, draft_len=kb, walk_order=True)
+    t3, d3, tk3 = target.copy(), draft.copy(), toks.copy()
+    t3[kb + 1:] = np.nan
+    d3[kb:] = np.nan
+    tk3[kb:] = -5
+    r3 = O.verify_sequence(t3, d3, tk3, u, 1.0, S, draft_len=kb, walk_order=True)
+    _same(r3, r)
+    assert r3.valid and r3.accept_len == kb
+
+
+def test_stops_cut_the_emission_not_the_reading():
+    """An end-of-sequence draft before the first rejection ends the emission
+    there, yet the walk still reads up to the rejection: a bad row at the
+    rejection invalidates the sequence, one past it does not."""
+    rng = np.random.default_rng(71)
+    V, K, j = 12, 5, 3
+    target, draft, toks, u = _forced(rng, V, K, j)
+    eos = int(toks[1])
+    if eos in toks[:1]:
+        pytest.skip("needs a first eos at position 1")
+    r = O.verify_sequence(target, draft, toks, u, 1.0, S, eos=eos, walk_order=True)
+    assert r.valid and r.accept_len == 2 and r.tokens[2] == -1
+    d2 = draft.copy()
+    d2[j] = np.nan
+    assert not O.verify_sequence(target, d2, toks, u, 1.0, S, eos=eos, walk_order=True).valid
+    d3 = draft.copy()
+    d3[j + 1] = np.nan
+    _same(O.verify_sequence(target, d3, toks, u, 1.0, S, eos=eos, walk_order=True), r)
+
+
+def test_walk_order_leaves_other_modes_and_truncation_alone():
+    rng = np.random.default_rng(8)
+    V, K = 12, 4
+    target, draft, toks = _case(rng, V, K)
+    u = rng.random(K + 1)
+    t2 = target.copy()
+    t2[K, 0] = np.nan
+    for mode in (O.MODE_GREEDY, O.MODE_MARGIN):
+        a = O.verify_sequence(t2, None, toks, None, 1.0, mode, tau=0.3)
+        b = O.verify_sequence(t2, None, toks, None, 1.0, mode, tau=0.3, walk_order=True)
+        _same(a, b)
+        assert not b.valid
+    d2 = draft.copy()
+    d2[K - 1, 0] = np.nan
+    for tk, tp in ((5, 1.0), (0, 0.9)):
+        a = O.verify_sequence(target, d2, toks, u, 1.0, S, top_k=tk, top_p=tp)
+        b = O.verify_sequence(target, d2, toks, u, 1.0, S, top_k=tk, top_p=tp, walk_order=True)
+        _same(a, b)
+        assert not b.valid
+
+
+def test_batch_threads_the_reading():
+    rng = np.random.default_rng(12)
+    B, V, K = 6, 10, 4
+    cases = [_forced(rng, V, K, 0) for _ in range(B)]
+    tg = np.stack([c[0] for c in cases])
+    dr = np.stack([c[1] for c in cases])
+    tk = np.stack([c[2] for c in cases])
+    uu = np.stack([c[3] for c in cases])
+    dr[:, 2, :] = np.nan              # past every sequence's rejection at 0
+    full = O.verify_batch(tg, dr, tk, uu, 1.0, S)
+    walk = O.verify_batch(tg, dr, tk, uu, 1.0, S, walk_order=True)
+    assert full.invalid == B and walk.invalid == 0
+    assert np.all(walk.accept_len == 0) and walk.hist[0] == B
