@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "verified seqs/sec + achieved HBM GB/s (% of MI355X peak), V=128256 B=256 K=7"
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20       # MI355X last-level (Infinity) cache
+WALK_SINGLES = 3             # walk-order reading: the library streams positions 0..2 one stage each
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "speculative_decoding_verification_temp_amd", "csrc")
 
@@ -85,7 +86,7 @@ def traffic_for(workload: str, kernel: str):
 _W = {}
 
 
-def _worker_init(specs, T, mode, tau, trunc=(0, 1.0)):
+def _worker_init(specs, T, mode, tau, trunc=(0, 1.0), walk=False):
     from multiprocessing import shared_memory
     import numpy as np
     from oracle import spec_oracle as O
@@ -99,6 +100,7 @@ def _worker_init(specs, T, mode, tau, trunc=(0, 1.0)):
         _W[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
     _W["args"] = (T, mode, tau)
     _W["trunc"] = trunc
+    _W["walk"] = walk
     _W["O"] = O
 
 
@@ -112,7 +114,7 @@ def _worker_task(k):
     r = O.verify_batch(_W["tgt"][q:q + 1], None if _W["drf"] is None else _W["drf"][q:q + 1],
                        _W["tok"][q:q + 1], _W["uni"][q:q + 1], T, mode, tau,
                        draft_len=None if kb is None else kb[q:q + 1],
-                       top_k=[tk], top_p=[tp])
+                       top_k=[tk], top_p=[tp], walk_order=_W["walk"])
     return q, int(r.accept_len[0]), r.tokens[0].tolist(), float(r.min_dist[0])
 
 
@@ -127,7 +129,8 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1.0)):
+def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1.0),
+                 walk=False):
     """Time the fp64 CPU oracle on a bounded sample of the same workload, one
     sequence per task: first in this process on one core, then on a pool of
     worker processes (one per core of this process's CPU set, at most 16: the
@@ -168,7 +171,7 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1
                            None if arrays["drf"] is None else arrays["drf"][q:q + 1],
                            arrays["tok"][q:q + 1], arrays["uni"][q:q + 1], cfg.T, m, cfg.tau,
                            draft_len=None if kb is None else arrays["kb"][q:q + 1],
-                           top_k=[trunc[0]], top_p=[trunc[1]])
+                           top_k=[trunc[0]], top_p=[trunc[1]], walk_order=walk)
         mism += check(q, int(r.accept_len[0]), r.tokens[0], float(r.min_dist[0]))
         n1 += 1
     t1 = time.perf_counter() - t0
@@ -191,7 +194,7 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1
             specs[name] = (shm.name, a.shape, a.dtype.str)
         ctx = mp.get_context("spawn")
         with cf.ProcessPoolExecutor(nproc, mp_context=ctx, initializer=_worker_init,
-                                    initargs=(specs, cfg.T, m, cfg.tau, trunc)) as ex:
+                                    initargs=(specs, cfg.T, m, cfg.tau, trunc, walk)) as ex:
             list(ex.map(_worker_task, range(nproc)))          # start-up, not timed
             nn, k = 0, 0
             t0 = time.perf_counter()
@@ -210,7 +213,8 @@ def cpu_baseline(sets, gpu_outs, cfg, mode, seconds: float, kb=None, trunc=(0, 1
                 single_core_value=n1 / t1,
                 sample=f"{n1} sequence verifications on one core ({t1:.1f} s), then {nn} on "
                        f"{nproc} worker processes ({tn:.1f} s), cycling over {n} sequences of "
-                       f"the timed input sets; fp64 numpy",
+                       f"the timed input sets; fp64 numpy"
+                       + ("; rows read in walk order" if walk else ""),
                 parity_mismatches=mism)
 
 
@@ -241,6 +245,10 @@ def main():
     ap.add_argument("--residual", type=int, default=0,
                     help="stochastic mode: draft residual side output on the draft's top-m "
                          "support (m = this value, 0 = off)")
+    ap.add_argument("--walk", action="store_true",
+                    help="stochastic mode: walk-order reading (the rows of a position are read "
+                         "only when the walk reaches it; nothing past the first rejection); "
+                         "no effect with truncation or the residual side output")
     ap.add_argument("--policy", action="store_true",
                     help="run the tree-shape policy epilogue (seeded draft confidences, d = 0.5)")
     ap.add_argument("--read-probe", action="store_true",
@@ -288,6 +296,9 @@ def main():
                          torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
     if args.residual and mode == "stochastic":
         v.set_residual(args.residual)
+    walk = args.walk and mode == "stochastic" and not trunc and not args.residual
+    if walk:
+        v.set_walk_order(True)
     if args.policy:
         conf = np.random.default_rng([20260923, cfg.index, 8]).uniform(0.0, 1.0, B)
         v.set_policy(torch.as_tensor(conf.astype(np.float32), device=dev), 0.5)
@@ -302,6 +313,7 @@ def main():
 
     # draw rows re-read per set (data dependent): 2 rows per rejection, 1 per bonus
     draw_bytes = []
+    walk_rows = []      # walk-order reading: rows the staged streaming pass reads per set
     for i in range(len(sets)):
         step(i)
         torch.cuda.synchronize()
@@ -313,6 +325,20 @@ def main():
         else:
             rows = 0
         draw_bytes.append(rows * V * s)
+        if walk:
+            # stages 0..S-1 read position st's rows when the walk reaches st
+            # (st <= j, the first rejection, or k_b when all are kept); the last
+            # stage reads target rows S..k_b and draft rows S..k_b-1 once the
+            # walk reaches S (no invalid sequences in these workloads)
+            S = min(K, WALK_SINGLES)
+            jj = a.numpy().astype(np.int64)
+            kk = kbt.numpy().astype(np.int64)
+            n = 0
+            for jb, kbb in zip(jj[valid.numpy()], kk[valid.numpy()]):
+                n += sum(int(st <= kbb) + int(st < kbb) for st in range(min(S, jb + 1)))
+                if jb >= S:
+                    n += max(kbb - S + 1, 0) + max(kbb - S, 0)
+            walk_rows.append(n)
     log(f"warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
@@ -367,7 +393,9 @@ def main():
     pass_avg = pass_ms / max(1, ncalls)
 
     rows_total = int((2 * kb + 1).sum()) if mode == "stochastic" else int((kb + 1).sum())
-    pass_bytes = rows_total * V * s
+    if walk:
+        rows_total = sum(walk_rows) / len(walk_rows)
+    pass_bytes = int(rows_total * V * s)
     io_bytes = B * (K * 4 + (K + 1) * 4 + (K + 1) * 4 + 4) + 2 * B * K * s
     call_bytes = pass_bytes + sum(draw_bytes) / len(draw_bytes) + io_bytes
     trunc_kernel = "rowstats_trunc32" if cfg.dtype == "f32" else "rowstats_trunc_win"
@@ -375,7 +403,8 @@ def main():
         else "rowstats_max"
     achieved = pass_bytes / (pass_avg * 1e-3) / 1e9
     workload = f"{cfg.name}/{mode}" + (f"/top-k{args.top_k}-top-p{args.top_p}" if trunc else "") \
-        + (f"/residual{args.residual}" if args.residual and mode == "stochastic" else "")
+        + (f"/residual{args.residual}" if args.residual and mode == "stochastic" else "") \
+        + ("/walk" if walk else "")
     traffic = traffic_for(workload, kernel) if args.stops == "none" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -397,7 +426,8 @@ def main():
                                + (f", top-k {args.top_k}, top-p {args.top_p}" if trunc else "")
                                + (", tree-shape policy" if args.policy else "")
                                + (f", draft residual m={args.residual}"
-                                  if args.residual and mode == "stochastic" else ""),
+                                  if args.residual and mode == "stochastic" else "")
+                               + (", walk-order reading" if walk else ""),
                    "B": B, "K": K, "V": V, "mode": mode, "parallelism": "single GPU",
                    "input_sets": len(sets), "input_bytes_rotated": int(set_bytes * len(sets)),
                    "timing": "hip graph replays" if args.graph else "eager calls"},
@@ -450,7 +480,7 @@ def main():
             gpu_outs.append((out[0].cpu().numpy(), out[1].cpu().numpy()))
         res["cpu_baseline"] = cpu_baseline(
             sets, gpu_outs, cfg, mode, args.cpu_seconds, kb if args.stops == "varlen" else None,
-            (args.top_k, float(np.float32(args.top_p))) if trunc else (0, 1.0))
+            (args.top_k, float(np.float32(args.top_p))) if trunc else (0, 1.0), walk)
     print(json.dumps(res), flush=True)
 
 

@@ -24,7 +24,7 @@ _ERRNAMES = {-1: "SV_EINVAL", -2: "SV_EUNSUPPORTED", -3: "SV_ENOMEM", -4: "SV_EH
 EXPORTED = (
     "spec_verify_init", "spec_verify", "spec_verify_destroy", "spec_verify_set_aux",
     "spec_verify_set_stops", "spec_verify_set_truncation", "spec_verify_set_policy",
-    "spec_verify_set_residual",
+    "spec_verify_set_residual", "spec_verify_set_walk_order",
     "spec_verify_get_ema", "spec_verify_set_ema", "spec_verify_reset_ema",
     "spec_verify_get_stats", "spec_verify_profile", "spec_verify_profile_read",
     "spec_verify_last_error", "spec_verify_version", "spec_verify_read_probe",
@@ -66,6 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.spec_verify_set_truncation.argtypes = [vp, vp, vp]
     L.spec_verify_set_policy.argtypes = [vp, vp, ctypes.c_double, vp, vp]
     L.spec_verify_set_residual.argtypes = [vp, i32, vp, vp]
+    L.spec_verify_set_walk_order.argtypes = [vp, i32]
     L.spec_verify_get_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_set_ema.argtypes = [vp, vp, vp, vp]
     L.spec_verify_reset_ema.argtypes = [vp, vp]
@@ -292,6 +293,13 @@ class SpecVerifier:
                     "set_residual")
         self._residual = (sup, res)
         return sup, res
+
+    def set_walk_order(self, on: bool = True):
+        """Walk-order reading for later stochastic calls without truncation:
+        rows past each sequence's first rejection are not read (and so not
+        checked); p(d), q(d) past it are NaN."""
+        self._check(self.lib.spec_verify_set_walk_order(self._h, 1 if on else 0),
+                    "set_walk_order")
 
     def set_policy(self, draft_conf, d: float = 0.5, want_dcs: bool = False):
         """Tree-shape policy for later calls: draft_conf is a float32 device

@@ -30,6 +30,7 @@
 namespace {
 
 constexpr int kMaxSeg = 16;
+constexpr int kWalkSingles = 3;   // walk-order reading: positions streamed one stage each
 static_assert(kMaxSeg <= sv::kTopmMaxSeg, "top-m lists are laid out for kTopmMaxSeg segments");
 constexpr int kProfCalls = 4096;
 constexpr double kLog2e = 1.4426950408889634073599246810018921;
@@ -80,6 +81,7 @@ struct spec_verify_handle {
   bool topm_merged = false;                // this call's finish also merged the lists
   double res_invT = 1.0;                   // this call's 1 / temperature
   int merge_in_finish = 1;     // lists merged inside the finish when they fit (0: own kernel)
+  int walk = 0;                // stochastic calls read rows in walk order (spec_verify_set_walk_order)
   int lds_cu = 160 * 1024;                 // LDS bytes per compute unit
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
@@ -177,27 +179,51 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
                    int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
   const int K = h->K, V = h->V;
   const int rows = 2 * K + 1;
-  const Launch L = plan(h, B, rows, VEC, U);
+  bool topm = false;
+  if constexpr ((DT == sv::DT_BF16 && VEC == 8) || (DT == sv::DT_F32 && VEC == 4))
+    topm = h->drift_sup != nullptr && h->topm_lists != nullptr;
+  // walk-order reading (not with the residual side output, which needs every
+  // draft row): the streaming pass runs in stages of positions, each planned
+  // as if every sequence were still being walked
+  const bool walk = h->walk && !topm;
+  sv::Rules rules = h->rules;
+  rules.walk = walk ? 1 : 0;
+  const Launch L = plan(h, B, walk ? 2 : rows, VEC, U);
   const bool tab = (DT == sv::DT_BF16 && VEC == 8);
   const int n_half = tab_half(c64);
   const int groups = div_up(L.ntiles, h->tiles_per_group);
   const int grid_seq = div_up(B, sv::kWavesPerBlock);
+  const sv::StageRows all_rows{0, K + 1, 0, K, 0};
   prof_mark(h, 0, s);
-  bool topm = false;
   if constexpr ((DT == sv::DT_BF16 && VEC == 8) || (DT == sv::DT_F32 && VEC == 4)) {
     // the residual side output takes its draft-row candidates from this pass
-    if (h->drift_sup != nullptr && h->topm_lists != nullptr) {
+    if (topm) {
       hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U, true>), dim3(unsigned(B * rows * L.nseg)),
                          dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                         h->rules.k, h->parts, hist, h->drift_m, h->topm_lists, tokens);
+                         h->rules.k, h->parts, hist, h->drift_m, h->topm_lists, tokens, all_rows,
+                         uniforms);
       h->topm_nseg = L.nseg;
-      topm = true;
     }
   }
-  if (!topm)
+  if (walk) {
+    // positions 0, 1, .., S-1 one at a time, then S..K-1 with the bonus rows
+    // (target rows S..K); a stage's workgroups read their rows only when the
+    // walk of their sequence reaches the stage's first position
+    const int S = std::min(K, kWalkSingles);
+    for (int st = 0; st <= S; ++st) {
+      const sv::StageRows sr =
+          st < S ? sv::StageRows{st, st + 1, st, st + 1, st} : sv::StageRows{S, K + 1, S, K, S};
+      const int nr = (sr.t1 - sr.t0) + (sr.d1 - sr.d0);
+      hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * nr * L.nseg)),
+                         dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks,
+                         c, h->rules.k, h->parts, st == 0 ? hist : nullptr, 0, nullptr, tokens,
+                         sr, uniforms);
+    }
+  } else if (!topm) {
     hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
                        dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
-                       h->rules.k, h->parts, hist, 0, nullptr, tokens);
+                       h->rules.k, h->parts, hist, 0, nullptr, tokens, all_rows, uniforms);
+  }
   int rc = check_launch(h, "rowstats_sum");
   prof_mark(h, 1, s);
   if (rc) return rc;
@@ -236,13 +262,13 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
       }
     }
     hipLaunchKernelGGL(kern, dim3(B), dim3(NT), dyn, s, K, V, L.nseg, h->parts, target, draft,
-                       tokens, uniforms, c, c64, n_half, h->rules, out_tokens, out_len, hist,
+                       tokens, uniforms, c, c64, n_half, rules, out_tokens, out_len, hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        nullptr, mj, h->claim_tiles);
     return check_launch(h, "finish_seq");
   }
   hipLaunchKernelGGL((sv::scan_stochastic<DT>), dim3(grid_seq), dim3(sv::kBlock), 0, s, 0, B, K,
-                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, h->rules, out_tokens,
+                     V, L.nseg, h->parts, target, draft, tokens, uniforms, c, rules, out_tokens,
                      out_len, hist, h->ema, h->steps, h->decay, h->stats, h->draw, h->aux_p, h->aux_q,
                      h->aux_z, tab ? h->table : nullptr, n_half, c64);
   if ((rc = check_launch(h, "scan_stochastic"))) return rc;
@@ -367,7 +393,7 @@ int run_fused(spec_verify_handle* h, int B, const void* target, const void* draf
 
 // whether the one-workgroup-per-sequence kernel serves this call
 bool use_fused(const spec_verify_handle* h, int B, int vec) {
-  if (h->fused_min_batch <= 0 || B < h->fused_min_batch || vec == 1) return false;
+  if (h->fused_min_batch <= 0 || B < h->fused_min_batch || vec == 1 || h->walk) return false;
   const long long ntiles = ((long long)h->V / vec + sv::kTileChunks - 1) / sv::kTileChunks;
   return ntiles <= sv::kFMaxTiles && 2 * h->K + 1 <= sv::kFMaxRows;
 }
@@ -600,6 +626,12 @@ int spec_verify_set_residual(spec_verify_handle* h, int m, int32_t* out_support,
   h->drift_m = m;
   h->drift_sup = out_support;
   h->drift_res = out_residual;
+  return SV_OK;
+}
+
+int spec_verify_set_walk_order(spec_verify_handle* h, int on) {
+  if (h == nullptr || (on != 0 && on != 1)) return SV_EINVAL;
+  h->walk = on;
   return SV_OK;
 }
 

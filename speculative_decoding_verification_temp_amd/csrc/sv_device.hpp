@@ -195,6 +195,30 @@ struct RowPart {
   int flags;     // bit 0: NaN seen (greedy/margin rows)
 };
 
+// A row's normaliser from its segments' partials: common reference, exact
+// rescale, fixed order.
+__device__ inline void combine_sum_parts(const RowPart* p, int nseg, float& R, double& S) {
+  R = p[0].R;
+  for (int s = 1; s < nseg; ++s) R = fmaxf(R, p[s].R);
+  S = 0.0;
+  for (int s = 0; s < nseg; ++s) S += rescale(p[s].S, p[s].R, R);
+}
+
+__device__ inline bool finite_pos(double S) { return S > 0.0 && S < __builtin_inf(); }
+
+// The acceptance test of one drafted position ([SMB] "The Guarantee Behind
+// Rejection Sampling"; [RNR] s.2): from the logits of its drafted token in
+// the target and draft rows and the rows' normalisers, P = p(d), Q = q(d);
+// the draft is kept iff P >= Q or u < P / Q. Every place that takes this
+// decision (the scans and the walk-order gate of the streaming pass) calls
+// this one function, so they agree bit for bit.
+__device__ inline bool accept_position(float xt, float xd, float Rt, double St, float Rd,
+                                       double Sd, double u, float c, double& P, double& Q) {
+  P = double(term(xt, c, Rt)) / St;
+  Q = double(term(xd, c, Rd)) / Sd;
+  return (P >= Q) || (u < P / Q);
+}
+
 // Final statistics of the row a sequence draws from, left by the scan for the
 // draw kernels.
 struct DrawRow {

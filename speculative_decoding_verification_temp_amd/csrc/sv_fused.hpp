@@ -868,22 +868,22 @@ __device__ __forceinline__ void finish_sequence(
           // fp32: the terms the truncation pass summed (0 for -inf); 0 when dropped
           P = order_key<DT_F32>(__float_as_uint(xt)) >= kt ? value_term(xt, c64, Rt) / St : 0.0;
           Q = order_key<DT_F32>(__float_as_uint(xd)) >= kd ? value_term(xd, c64, Rd) / Sd : 0.0;
-        } else {
-          P = double(term(xt, c, Rt)) / St;
-          Q = double(term(xd, c, Rd)) / Sd;
         }
         const double u = pre_u != nullptr ? pre_u[lane] : uniforms[(long long)b * (K + 1) + lane];
-        keep = (P >= Q) || (u < P / Q);
+        if constexpr (TRUNC)
+          keep = (P >= Q) || (u < P / Q);
+        else
+          keep = accept_position(xt, xd, Rt, St, Rd, Sd, u, c, P, Q);
         zq = keep && Q == 0.0;
       }
     }
-    const bool bad = __any(lane_bad);
+    const bool bad = sequence_bad(lane, kb, !TRUNC && sp.walk != 0, lane_bad, keep);
     const Walk w = walk_outcome(lane, kb, m, sp.eos, keep, d);
     const int j = w.j;
-    if (aux_p != nullptr && lane < K)
-      aux_p[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : P;
-    if (aux_q != nullptr && lane < K)
-      aux_q[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : Q;
+    // (walk-order reading: nothing past the first rejection was read)
+    const bool no_pq = bad || lane >= kb || (!TRUNC && sp.walk && lane > j);
+    if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = no_pq ? __builtin_nan("") : P;
+    if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = no_pq ? __builtin_nan("") : Q;
     const float Rtj = __shfl(Rt, j, kWave), Rdj = __shfl(Rd, j, kWave);
     const double Stj = __shfl(St, j, kWave), Sdj = __shfl(Sd, j, kWave);
     const uint32_t ktj = __shfl(kt, j, kWave), kdj = __shfl(kd, j, kWave);

@@ -24,12 +24,6 @@ namespace sv {
 // --------------------------------------------------------------------------
 // Scan helpers
 // --------------------------------------------------------------------------
-__device__ inline void combine_sum_parts(const RowPart* p, int nseg, float& R, double& S) {
-  R = p[0].R;
-  for (int s = 1; s < nseg; ++s) R = fmaxf(R, p[s].R);
-  S = 0.0;
-  for (int s = 0; s < nseg; ++s) S += rescale(p[s].S, p[s].R, R);
-}
 
 __device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, int& idx,
                                          int& nan) {
@@ -42,7 +36,6 @@ __device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, i
   }
 }
 
-__device__ inline bool finite_pos(double S) { return S > 0.0 && S < __builtin_inf(); }
 
 // Tree-shape policy epilogue ([MNW] s.3, dynamic draft tree-shaping), run
 // after each sequence's EMA update when conf is set: the draft confidence
@@ -71,6 +64,7 @@ struct Rules {
   const int32_t* m = nullptr;
   int eos = -1;
   Policy pol{nullptr, nullptr, nullptr, nullptr, 1.0};
+  int walk = 0;      // walk-order reading (stochastic calls without truncation)
 };
 
 __device__ inline void stops_of(const Rules& sp, int b, int K, int& kb, int& m, bool& bad) {
@@ -88,6 +82,23 @@ __device__ inline void stops_of(const Rules& sp, int b, int K, int& kb, int& m, 
 struct Walk {
   int j, n, cpos;
 };
+
+// Whether a sequence is invalid, on one wavefront (lane i holds position i,
+// lane kb the bonus row): with the full reading any unusable token or row
+// among the needed ones; with walk-order reading ([DVC] "Verify several
+// proposed tokens in one target pass": later proposals are discarded at the
+// first rejection) only one the walk reads, i.e. at the first position that
+// is rejected or unusable, or the bonus row when every position is kept.
+// Lanes past that position may hold the partials of rows that were never
+// read. keep is cleared where the lane is unusable, so that the walk stops
+// there.
+__device__ inline bool sequence_bad(int lane, int kb, bool walk, bool lane_bad, bool& keep) {
+  if (!walk) return __any(lane_bad);
+  const unsigned long long stop = __ballot(lane < kb && (lane_bad || !keep));
+  const int t = stop ? __ffsll((long long)stop) - 1 : kb;
+  keep = keep && !lane_bad;
+  return __shfl(lane_bad ? 1 : 0, t, kWave) != 0;
+}
 __device__ inline Walk walk_outcome(int lane, int kb, int m, int eos, bool keep, int d) {
   Walk w;
   const unsigned long long rej = __ballot(lane < kb && !keep);
@@ -273,20 +284,18 @@ __global__ __launch_bounds__(kBlock) void scan_stochastic(
     if (!lane_bad) {
       const float xt = load_logit<DT>(row_ptr<DT>(target, draft, b, lane, K, V), d);
       const float xd = load_logit<DT>(row_ptr<DT>(target, draft, b, K + 1 + lane, K, V), d);
-      P = double(term(xt, c, Rt)) / St;
-      Q = double(term(xd, c, Rd)) / Sd;
       const double u = uniforms[(long long)b * (K + 1) + lane];
-      keep = (P >= Q) || (u < P / Q);
+      keep = accept_position(xt, xd, Rt, St, Rd, Sd, u, c, P, Q);
       zq = keep && Q == 0.0;
     }
   }
-  const bool bad = __any(lane_bad);
+  const bool bad = sequence_bad(lane, kb, sp.walk != 0, lane_bad, keep);
   const Walk w = walk_outcome(lane, kb, m, sp.eos, keep, d);
 
-  if (aux_p != nullptr && lane < K)
-    aux_p[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : P;
-  if (aux_q != nullptr && lane < K)
-    aux_q[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : Q;
+  // (walk-order reading: nothing past the first rejection was read)
+  const bool no_pq = bad || lane >= kb || (sp.walk && lane > w.j);
+  if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = no_pq ? __builtin_nan("") : P;
+  if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = no_pq ? __builtin_nan("") : Q;
 
   // statistics of row j for the draw (j = kb: the bonus from target row kb)
   const int j = w.j;

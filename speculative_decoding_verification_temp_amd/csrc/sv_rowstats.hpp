@@ -94,6 +94,43 @@ __device__ inline uint32_t wg_kth_top16(uint32_t key, uint32_t m, uint32_t* bins
   return (b1 << s1) | (b2 << s2);
 }
 
+// The rows one launch of the stochastic streaming pass covers in every
+// sequence: target rows t0..t1-1 and draft rows d0..d1-1 (all of them:
+// 0..K+1, 0..K). gate > 0 (walk-order reading): a workgroup streams its row
+// only when the walk reaches position gate, i.e. positions 0..gate-1, whose
+// rows earlier launches streamed, are all kept (acceptance tested exactly as
+// the scans test it, from the same partials).
+struct StageRows {
+  int t0, t1, d0, d1, gate;
+};
+
+// Whether the walk of sequence b keeps every position below p (p <= K),
+// given the partials of their rows (one wavefront; lane i tests position i;
+// a position with an unusable token or row stops the walk).
+__device__ inline bool walk_reaches(const RowPart* __restrict__ parts, int b, int K, int V,
+                                    int nseg, int p, int kb, const int32_t* __restrict__ tokens,
+                                    const float* __restrict__ uniforms, float c) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rows = 2 * K + 1;
+  bool stop = false;
+  if (lane < p && lane < kb) {
+    const RowPart* pt = parts + ((long long)b * rows + lane) * nseg;
+    const RowPart* pd = parts + ((long long)b * rows + K + 1 + lane) * nseg;
+    float Rt, Rd;
+    double St, Sd;
+    combine_sum_parts(pt, nseg, Rt, St);
+    combine_sum_parts(pd, nseg, Rd, Sd);
+    const int d = tokens[(long long)b * K + lane];
+    stop = !(d >= 0 && d < V) || !finite_pos(St) || !finite_pos(Sd);
+    if (!stop) {
+      double P, Q;
+      stop = !accept_position(pt->m, pd->m, Rt, St, Rd, Sd,
+                              double(uniforms[(long long)b * (K + 1) + lane]), c, P, Q);
+    }
+  }
+  return __ballot(stop) == 0ull;
+}
+
 // top-m candidate list per wavefront (sv_topm.hpp) for the draft residual
 // side output and store it, as at most m keys followed by zeros, at
 //   topm_lists[((b K + i) nseg + seg) 4 + wavefront][0..m)
@@ -108,22 +145,35 @@ __global__ __launch_bounds__(kBlock, TOPM ? 4 : 1) void rowstats_sum(
     const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
     int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
     RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
-    uint64_t* __restrict__ topm_lists, const int32_t* __restrict__ tokens) {
+    uint64_t* __restrict__ topm_lists, const int32_t* __restrict__ tokens, StageRows sr,
+    const float* __restrict__ uniforms) {
   static_assert(!TOPM || (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4),
                 "top-m lists need 16-byte chunks");
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
-  const long long wg = (long long)b0 * rows * nseg + blockIdx.x;   // global (row, segment)
-  const int seg = int(wg % nseg);
-  const long long grow = wg / nseg;
-  const int b = int(grow / rows), r = int(grow % rows);
+  const int nt = sr.t1 - sr.t0, nr = nt + (sr.d1 - sr.d0);   // rows per sequence here
+  const long long lw = (long long)b0 * nr * nseg + blockIdx.x;
+  const int seg = int(lw % nseg);
+  const long long lrow = lw / nseg;
+  const int b = int(lrow / nr), lr = int(lrow % nr);
+  const int r = lr < nt ? sr.t0 + lr : K + 1 + sr.d0 + (lr - nt);
+  const long long wg = ((long long)b * rows + r) * nseg + seg;   // global (row, segment)
   if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
   // with per-sequence draft counts k_b, target rows past k_b and draft rows
   // k_b.. are never read again: skip them (uniform over the workgroup)
-  if (kdraft != nullptr) {
-    const int kb = kdraft[b];
-    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (kdraft != nullptr && (r <= K ? r > kb : r - K - 1 >= kb)) return;
+  // walk-order reading: rows of positions the walk does not reach are never
+  // read (wavefront 0 decides for the workgroup)
+  if (sr.gate > 0) {
+    __shared__ int s_reach;
+    if (tid < kWave) {
+      const bool reach = walk_reaches(parts, b, K, V, nseg, sr.gate, kb, tokens, uniforms, c);
+      if (tid == 0) s_reach = reach ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_reach) return;
   }
 
   const void* row = row_ptr<DT>(target, draft, b, r, K, V);

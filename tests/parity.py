@@ -56,11 +56,12 @@ def _merge(parts):
 
 
 def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int = 256,
-               stops=None, trunc=None):
+               stops=None, trunc=None, walk: bool = False):
     """Run the oracle on the listed sequences of a generated input dict
     (host copies are made a chunk of sequences at a time). stops: optional
     (eos, draft_len [B] or None, max_emit [B] or None) with host arrays indexed
-    by batch row; trunc: optional (top_k [B] or None, top_p [B] or None)."""
+    by batch row; trunc: optional (top_k [B] or None, top_p [B] or None);
+    walk: the walk-order reading."""
     rows = np.asarray(rows, dtype=np.int64)
     m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
     parts = []
@@ -71,10 +72,10 @@ def oracle_for(x: dict, rows, mode: str, tau: float = 0.0, ema=None, chunk: int 
         drf = to_host_f64(x["draft"].index_select(0, idx)) if mode == "stochastic" else None
         tok = x["tokens"].index_select(0, idx).cpu().numpy()
         uni = x["uniforms"].index_select(0, idx).cpu().double().numpy()
-        kw = {}
+        kw = {"walk_order": True} if walk else {}
         if stops is not None:
             eos, kb, mx = stops
-            kw = dict(eos=eos, draft_len=None if kb is None else np.asarray(kb)[sub_rows],
+            kw.update(eos=eos, draft_len=None if kb is None else np.asarray(kb)[sub_rows],
                       max_emit=None if mx is None else np.asarray(mx)[sub_rows])
         if trunc is not None:
             tk, tp = trunc
