@@ -30,7 +30,6 @@ if ROOT not in sys.path:
 METRIC = "verified seqs/sec + achieved HBM GB/s (% of MI355X peak), V=128256 B=256 K=7"
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20       # MI355X last-level (Infinity) cache
-WALK_SINGLES = 3             # walk-order reading: the library streams positions 0..2 one stage each
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "speculative_decoding_verification_temp_amd", "csrc")
 
@@ -326,18 +325,17 @@ def main():
             rows = 0
         draw_bytes.append(rows * V * s)
         if walk:
-            # stages 0..S-1 read position st's rows when the walk reaches st
-            # (st <= j, the first rejection, or k_b when all are kept); the last
-            # stage reads target rows S..k_b and draft rows S..k_b-1 once the
-            # walk reaches S (no invalid sequences in these workloads)
-            S = min(K, WALK_SINGLES)
+            # the library reads position 0's rows (target row 0, draft row 0
+            # when k_b > 0) of every sequence, then every other needed row
+            # (target rows 1..k_b, draft rows 1..k_b-1) of the sequences whose
+            # walk keeps position 0 (no invalid sequences in these workloads)
             jj = a.numpy().astype(np.int64)
             kk = kbt.numpy().astype(np.int64)
             n = 0
             for jb, kbb in zip(jj[valid.numpy()], kk[valid.numpy()]):
-                n += sum(int(st <= kbb) + int(st < kbb) for st in range(min(S, jb + 1)))
-                if jb >= S:
-                    n += max(kbb - S + 1, 0) + max(kbb - S, 0)
+                n += 1 + int(kbb > 0)
+                if jb >= 1:
+                    n += kbb + max(kbb - 1, 0)
             walk_rows.append(n)
     log(f"warmup {args.warmup}")
     for i in range(args.warmup):

@@ -322,10 +322,12 @@ int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
  * draft row i) are read only when the walk reaches position i, i.e. once
  * positions 0..i-1 are kept, and nothing past the first rejection is read
  * (target row k_b, the bonus row, only when every position is kept). The
- * streaming pass then runs in stages: positions 0, 1 and 2 one at a time,
- * then the rest; a stage's workgroups first test the earlier positions from
- * the partials the earlier stages left (the same acceptance test as the
- * scan) and return at once when the walk stopped before them.
+ * streaming pass then reads position 0's rows of every sequence, lists the
+ * sequences whose walk keeps position 0 (the same acceptance test as the
+ * scan, from the partials), and reads their remaining rows with a fixed
+ * grid; the finish reads no further than the walk. Rows of positions past the
+ * first rejection after position 0 may still be read (not checked, and
+ * never used).
  * What changes for the caller, and only this: a sequence is invalid only when
  * a drafted token or a row that the walk reads is unusable (NaN, +inf or no
  * finite maximum), not when one past its first rejection is; p(d) and q(d)

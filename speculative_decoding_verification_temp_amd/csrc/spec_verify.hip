@@ -30,7 +30,7 @@
 namespace {
 
 constexpr int kMaxSeg = 16;
-constexpr int kWalkSingles = 3;   // walk-order reading: positions streamed one stage each
+constexpr long long kWalkGrid = 2048;   // walk-order reading: workgroups after position 0
 static_assert(kMaxSeg <= sv::kTopmMaxSeg, "top-m lists are laid out for kTopmMaxSeg segments");
 constexpr int kProfCalls = 4096;
 constexpr double kLog2e = 1.4426950408889634073599246810018921;
@@ -82,6 +82,8 @@ struct spec_verify_handle {
   double res_invT = 1.0;                   // this call's 1 / temperature
   int merge_in_finish = 1;     // lists merged inside the finish when they fit (0: own kernel)
   int walk = 0;                // stochastic calls read rows in walk order (spec_verify_set_walk_order)
+  int32_t* walk_seq = nullptr;  // walk-order reading: sequences whose walk keeps position 0
+  uint32_t* walk_cnt = nullptr; //   and their count
   int lds_cu = 160 * 1024;                 // LDS bytes per compute unit
   int prof_cap = 0, prof_n = 0;
   int target_wgs = 2048;   // streaming-pass workgroups to aim for (tuning)
@@ -188,12 +190,15 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
   const bool walk = h->walk && !topm;
   sv::Rules rules = h->rules;
   rules.walk = walk ? 1 : 0;
-  const Launch L = plan(h, B, walk ? 2 : rows, VEC, U);
+  // (walk-order reading: position 0's two rows are planned for half the usual
+  // workgroups, i.e. segments twice as long, which measured a little faster:
+  // c3 87.0 against 91.9 us per call)
+  const Launch L = plan(h, B, walk ? 4 : rows, VEC, U);
   const bool tab = (DT == sv::DT_BF16 && VEC == 8);
   const int n_half = tab_half(c64);
   const int groups = div_up(L.ntiles, h->tiles_per_group);
   const int grid_seq = div_up(B, sv::kWavesPerBlock);
-  const sv::StageRows all_rows{0, K + 1, 0, K, 0};
+  const sv::StageRows all_rows{0, K + 1, 0, K, 0, nullptr};
   prof_mark(h, 0, s);
   if constexpr ((DT == sv::DT_BF16 && VEC == 8) || (DT == sv::DT_F32 && VEC == 4)) {
     // the residual side output takes its draft-row candidates from this pass
@@ -206,19 +211,21 @@ int run_stochastic(spec_verify_handle* h, int B, const void* target, const void*
     }
   }
   if (walk) {
-    // positions 0, 1, .., S-1 one at a time, then S..K-1 with the bonus rows
-    // (target rows S..K); a stage's workgroups read their rows only when the
-    // walk of their sequence reaches the stage's first position
-    const int S = std::min(K, kWalkSingles);
-    for (int st = 0; st <= S; ++st) {
-      const sv::StageRows sr =
-          st < S ? sv::StageRows{st, st + 1, st, st + 1, st} : sv::StageRows{S, K + 1, S, K, S};
-      const int nr = (sr.t1 - sr.t0) + (sr.d1 - sr.d0);
-      hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * nr * L.nseg)),
-                         dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks,
-                         c, h->rules.k, h->parts, st == 0 ? hist : nullptr, 0, nullptr, tokens,
-                         sr, uniforms);
-    }
+    // position 0's rows of every sequence; then the sequences whose walk
+    // keeps position 0 are listed, and their rows of positions 1..K (target
+    // rows 1..k_b, draft rows 1..k_b-1) are streamed by a fixed grid
+    const sv::StageRows first{0, 1, 0, 1, 0, h->walk_cnt};
+    hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * 2 * L.nseg)),
+                       dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
+                       h->rules.k, h->parts, hist, 0, nullptr, tokens, first, uniforms);
+    hipLaunchKernelGGL(sv::walk_gate, dim3(unsigned(grid_seq)), dim3(sv::kBlock), 0, s, B, K, V,
+                       L.nseg, h->parts, h->rules.k, tokens, uniforms, c, 1, h->walk_seq,
+                       h->walk_cnt);
+    const long long rest = (long long)B * (2 * K - 1) * L.nseg;
+    hipLaunchKernelGGL((sv::rowstats_sum_list<DT, VEC, U>),
+                       dim3(unsigned(std::min<long long>(rest, kWalkGrid))), dim3(sv::kBlock), 0,
+                       s, target, draft, K, V, L.nseg, L.seg_chunks, c, h->rules.k, h->parts,
+                       tokens, h->walk_seq, h->walk_cnt, 1);
   } else if (!topm) {
     hipLaunchKernelGGL((sv::rowstats_sum<DT, VEC, U>), dim3(unsigned(B * rows * L.nseg)),
                        dim3(sv::kBlock), 0, s, target, draft, 0, K, V, L.nseg, L.seg_chunks, c,
@@ -463,8 +470,8 @@ int verify_call(spec_verify_handle* h, int B, const void* target, const void* dr
                 hipStream_t stream);
 
 void free_all(spec_verify_handle* h) {
-  void* ptrs[] = {h->parts, h->draw,  h->tsum,  h->table,     h->ema,
-                  h->steps, h->streak, h->stats, h->topm_lists};
+  void* ptrs[] = {h->parts, h->draw,  h->tsum,  h->table,      h->ema,     h->steps,
+                  h->streak, h->stats, h->topm_lists, h->walk_seq, h->walk_cnt};
   for (void* p : ptrs)
     if (p != nullptr) (void)hipFree(p);
 }
@@ -535,7 +542,9 @@ int spec_verify_init(spec_verify_handle** out, int max_batch, int K, int V, int 
             hipMalloc(&h->ema, (size_t)max_batch * sizeof(double)) == hipSuccess &&
             hipMalloc(&h->steps, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
             hipMalloc(&h->streak, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
-            hipMalloc(&h->stats, sizeof(sv::DevStats)) == hipSuccess;
+            hipMalloc(&h->stats, sizeof(sv::DevStats)) == hipSuccess &&
+            hipMalloc(&h->walk_seq, (size_t)max_batch * sizeof(int32_t)) == hipSuccess &&
+            hipMalloc(&h->walk_cnt, 64) == hipSuccess;
   if (!ok) {
     free_all(h);
     delete h;

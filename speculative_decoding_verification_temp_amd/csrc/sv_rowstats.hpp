@@ -99,9 +99,12 @@ __device__ inline uint32_t wg_kth_top16(uint32_t key, uint32_t m, uint32_t* bins
 // 0..K+1, 0..K). gate > 0 (walk-order reading): a workgroup streams its row
 // only when the walk reaches position gate, i.e. positions 0..gate-1, whose
 // rows earlier launches streamed, are all kept (acceptance tested exactly as
-// the scans test it, from the same partials).
+// the scans test it, from the same partials). The library's walk-order
+// reading streams position 0 this way and the rest through a list of the
+// sequences whose walk goes on (walk_gate, rowstats_sum_list).
 struct StageRows {
   int t0, t1, d0, d1, gate;
+  uint32_t* clear;   // set to 0 by workgroup 0 (the next stage's list count), or null
 };
 
 // Whether the walk of sequence b keeps every position below p (p <= K),
@@ -140,42 +143,21 @@ __device__ inline bool walk_reaches(const RowPart* __restrict__ parts, int b, in
 // at the end. The normaliser is computed exactly as without TOPM.
 constexpr int kTopmCapFused = 448;   // keys per wavefront list in the streaming pass
 
-template <int DT, int VEC, int U, bool TOPM = false>
-__global__ __launch_bounds__(kBlock, TOPM ? 4 : 1) void rowstats_sum(
-    const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
-    int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
-    RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
-    uint64_t* __restrict__ topm_lists, const int32_t* __restrict__ tokens, StageRows sr,
-    const float* __restrict__ uniforms) {
-  static_assert(!TOPM || (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4),
-                "top-m lists need 16-byte chunks");
+// One (row, segment) of the stochastic streaming pass: the segment's softmax
+// normaliser relative to an integer reference, the logit at the row's
+// drafted token, and with TOPM the draft row's top-m candidate lists; the
+// workgroup's partial goes to parts[(b (2K+1) + r) nseg + seg]. Called once
+// per workgroup (rowstats_sum) or for each listed row segment in turn
+// (rowstats_sum_list); every thread of the workgroup calls it.
+template <int DT, int VEC, int U, bool TOPM>
+__device__ __forceinline__ void stream_segment(
+    const void* __restrict__ target, const void* __restrict__ draft, int b, int r, int seg,
+    int K, int V, int nseg, int seg_chunks, float c, RowPart* __restrict__ parts, int topm_m,
+    uint64_t* __restrict__ topm_lists, const int32_t* __restrict__ tokens) {
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
-  const int nt = sr.t1 - sr.t0, nr = nt + (sr.d1 - sr.d0);   // rows per sequence here
-  const long long lw = (long long)b0 * nr * nseg + blockIdx.x;
-  const int seg = int(lw % nseg);
-  const long long lrow = lw / nseg;
-  const int b = int(lrow / nr), lr = int(lrow % nr);
-  const int r = lr < nt ? sr.t0 + lr : K + 1 + sr.d0 + (lr - nt);
   const long long wg = ((long long)b * rows + r) * nseg + seg;   // global (row, segment)
-  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
-  // with per-sequence draft counts k_b, target rows past k_b and draft rows
-  // k_b.. are never read again: skip them (uniform over the workgroup)
-  const int kb = kdraft != nullptr ? kdraft[b] : K;
-  if (kdraft != nullptr && (r <= K ? r > kb : r - K - 1 >= kb)) return;
-  // walk-order reading: rows of positions the walk does not reach are never
-  // read (wavefront 0 decides for the workgroup)
-  if (sr.gate > 0) {
-    __shared__ int s_reach;
-    if (tid < kWave) {
-      const bool reach = walk_reaches(parts, b, K, V, nseg, sr.gate, kb, tokens, uniforms, c);
-      if (tid == 0) s_reach = reach ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_reach) return;
-  }
-
   const void* row = row_ptr<DT>(target, draft, b, r, K, V);
   const long long nchunks = V / VEC;
   const long long c0 = (long long)seg * seg_chunks;
@@ -353,6 +335,88 @@ __global__ __launch_bounds__(kBlock, TOPM ? 4 : 1) void rowstats_sum(
     p.idx = -1;
     p.flags = 0;
     parts[wg] = p;
+  }
+}
+
+template <int DT, int VEC, int U, bool TOPM = false>
+__global__ __launch_bounds__(kBlock, TOPM ? 4 : 1) void rowstats_sum(
+    const void* __restrict__ target, const void* __restrict__ draft, int b0, int K, int V,
+    int nseg, int seg_chunks, float c, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int topm_m,
+    uint64_t* __restrict__ topm_lists, const int32_t* __restrict__ tokens, StageRows sr,
+    const float* __restrict__ uniforms) {
+  static_assert(!TOPM || (DT == DT_BF16 && VEC == 8) || (DT == DT_F32 && VEC == 4),
+                "top-m lists need 16-byte chunks");
+  const int tid = threadIdx.x;
+  const int nt = sr.t1 - sr.t0, nr = nt + (sr.d1 - sr.d0);   // rows per sequence here
+  const long long lw = (long long)b0 * nr * nseg + blockIdx.x;
+  const int seg = int(lw % nseg);
+  const long long lrow = lw / nseg;
+  const int b = int(lrow / nr), lr = int(lrow % nr);
+  const int r = lr < nt ? sr.t0 + lr : K + 1 + sr.d0 + (lr - nt);
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (blockIdx.x == 0 && sr.clear != nullptr && tid == 0) *sr.clear = 0u;
+  // with per-sequence draft counts k_b, target rows past k_b and draft rows
+  // k_b.. are never read again: skip them (uniform over the workgroup)
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (kdraft != nullptr && (r <= K ? r > kb : r - K - 1 >= kb)) return;
+  // walk-order reading: rows of positions the walk does not reach are never
+  // read (wavefront 0 decides for the workgroup)
+  if (sr.gate > 0) {
+    __shared__ int s_reach;
+    if (tid < kWave) {
+      const bool reach = walk_reaches(parts, b, K, V, nseg, sr.gate, kb, tokens, uniforms, c);
+      if (tid == 0) s_reach = reach ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_reach) return;
+  }
+
+  stream_segment<DT, VEC, U, TOPM>(target, draft, b, r, seg, K, V, nseg, seg_chunks, c, parts,
+                                   topm_m, topm_lists, tokens);
+}
+
+// Walk-order reading, after the streaming pass over position 0: one
+// wavefront per sequence tests positions below p0 from their partials (as
+// walk_reaches does for a gated workgroup) and lists the sequences whose walk
+// reaches p0 and that have rows there (k_b >= p0) in seqs[0 .. *count) (in
+// no particular order; count starts at 0).
+__global__ __launch_bounds__(kBlock) void walk_gate(
+    int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
+    const int32_t* __restrict__ kdraft, const int32_t* __restrict__ tokens,
+    const float* __restrict__ uniforms, float c, int p0, int32_t* __restrict__ seqs,
+    uint32_t* __restrict__ count) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (b >= B) return;                              // (the whole wavefront)
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (!(kb >= p0 && kb <= K)) return;              // nothing there to read
+  if (walk_reaches(parts, b, K, V, nseg, p0, kb, tokens, uniforms, c) && lane == 0)
+    seqs[atomicAdd(count, 1u)] = b;
+}
+
+// Walk-order reading: the row segments of positions p0..K (target rows
+// p0..K, draft rows p0..K-1) of the listed sequences, spread over a fixed
+// grid that loops over them, so that sequences whose walk ended cost no
+// workgroup. Each segment's partial is the one rowstats_sum would write.
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_sum_list(
+    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, int nseg,
+    int seg_chunks, float c, const int32_t* __restrict__ kdraft, RowPart* __restrict__ parts,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ seqs,
+    const uint32_t* __restrict__ count, int p0) {
+  const int nt = K + 1 - p0, nr = nt + (K - p0);
+  const long long items = (long long)(*count) * nr * nseg;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int seg = int(it % nseg);
+    const long long lrow = it / nseg;
+    const int b = seqs[lrow / nr], lr = int(lrow % nr);
+    const int r = lr < nt ? p0 + lr : K + 1 + p0 + (lr - nt);
+    const int kb = kdraft != nullptr ? kdraft[b] : K;
+    if (kdraft != nullptr && (r <= K ? r > kb : r - K - 1 >= kb)) continue;   // (uniform)
+    stream_segment<DT, VEC, U, false>(target, draft, b, r, seg, K, V, nseg, seg_chunks, c,
+                                      parts, 0, nullptr, tokens);
+    __syncthreads();                 // the combine's LDS is reused by the next segment
   }
 }
 
