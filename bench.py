@@ -248,6 +248,9 @@ def main():
                     help="stochastic mode: walk-order reading (the rows of a position are read "
                          "only when the walk reaches it; nothing past the first rejection); "
                          "no effect with truncation or the residual side output")
+    ap.add_argument("--no-walk-report", action="store_true",
+                    help="leave out the walk-order timing reported beside a plain stochastic "
+                         "line (counter and trace runs that should see the line's calls only)")
     ap.add_argument("--policy", action="store_true",
                     help="run the tree-shape policy epilogue (seeded draft confidences, d = 0.5)")
     ap.add_argument("--read-probe", action="store_true",
@@ -434,6 +437,48 @@ def main():
         "algorithmic_bytes_per_step": int(call_bytes),
         "roofline": roofline,
     }
+    if (mode == "stochastic" and not walk and not trunc and not args.residual
+            and not args.graph and not args.policy and not args.no_walk_report):
+        # the same calls with walk-order reading, reported beside the line:
+        # rows past each sequence's first rejection are not read
+        vw = sv.SpecVerifier(B, K, V, cfg.torch_dtype, ema_decay=cfg.ema_decay)
+        if args.stops == "varlen":
+            vw.set_stops(-1, kb_dev, None)
+        vw.set_walk_order(True)
+        outw = tuple(torch.empty_like(t) for t in out)
+        same, rows_w = True, []
+        for i in range(len(sets)):
+            step(i)
+            x = sets[i]
+            vw.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T, mode,
+                      cfg.tau, out=outw)
+            torch.cuda.synchronize()
+            same = same and torch.equal(out[0], outw[0]) and torch.equal(out[1], outw[1])
+            a = outw[1].cpu().numpy().astype(np.int64)
+            rows_w.append(int(sum(1 + int(k > 0) + (k + max(k - 1, 0) if j >= 1 else 0)
+                                  for j, k in zip(a, kb) if j >= 0)))
+        for i in range(args.warmup):
+            x = sets[i % len(sets)]
+            vw.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T, mode,
+                      cfg.tau, out=outw)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            x = sets[i % len(sets)]
+            vw.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T, mode,
+                      cfg.tau, out=outw)
+        t1.record()
+        torch.cuda.synchronize()
+        ms_w = t0.elapsed_time(t1) / args.steps
+        res["walk_order_reading"] = {
+            "value": round(B / (ms_w * 1e-3), 1), "unit": "verified seqs/s",
+            "ms_per_step": round(ms_w, 5),
+            "logit_rows_read_per_call": round(sum(rows_w) / len(rows_w), 1),
+            "logit_rows_per_call": int(rows_total),
+            "outputs_equal_full_reading": bool(same),
+            "note": "spec_verify_set_walk_order(1): a position's rows are read only once the "
+                    "walk reaches it; same calls and inputs as the line"}
+        vw.close()
     if args.read_probe:
         buf = torch.zeros(2 << 30, dtype=torch.uint8, device=dev)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)

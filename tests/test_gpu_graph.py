@@ -8,7 +8,7 @@ outputs), then for several steps copies fresh inputs into the captured
 buffers, replays, and compares everything the call writes with an eager
 verifier set up the same way on the same inputs, and the tokens with the
 oracle. Eager work and synchronisation sit between the replays. A second
-case captures plain greedy and margin calls.
+case captures plain greedy and margin calls, a third a walk-order call.
 """
 
 import numpy as np
@@ -145,3 +145,67 @@ def test_graph_replay_argmax_modes(sv, mode):
                              1.0, O.MODE_GREEDY if mode == "greedy" else O.MODE_MARGIN, 0.3)
         compare(np.arange(cfg.B), ref, out[0], out[1], mode, None, f"graph/{mode}/step {step}")
         assert np.array_equal(out[2].cpu().numpy().astype(np.int64), ref.hist)
+
+
+@pytest.mark.parametrize("cfg_name", ["c2", "c1"])
+def test_graph_replay_walk_order(sv, cfg_name):
+    """A walk-order call (its list count is cleared by its first kernel, not
+    by a memset) captured once and replayed on fresh inputs with stopping
+    rules on: every output equals an eager twin's, the tokens the oracle's
+    walk-order reading."""
+    cfg = CONFIGS[cfg_name]
+    rng = np.random.default_rng(62)
+    kb = torch.as_tensor(rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32), device=DEV)
+
+    def setup():
+        v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, cfg.torch_dtype, ema_decay=0.9)
+        aux = v.enable_aux()
+        v.set_stops(-1, kb, None)
+        v.set_walk_order(True)
+        out = (torch.full((cfg.B, cfg.K + 1), -7, dtype=torch.int32, device=DEV),
+               torch.full((cfg.B,), -7, dtype=torch.int32, device=DEV),
+               torch.full((cfg.K + 1,), -7, dtype=torch.int32, device=DEV))
+        return v, aux, out
+
+    vg, aux_g, out_g = setup()
+    ve, aux_e, out_e = setup()
+    x0 = make_inputs(cfg, 90, DEV)
+    buf = {k: x0[k].clone() for k in ("target", "draft", "tokens", "uniforms")}
+
+    def call(v, out, inp):
+        v.verify(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"], cfg.T,
+                 "stochastic", out=out)
+
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        call(vg, out_g, buf)
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    call(ve, out_e, buf)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(vg, out_g, buf)
+    for step in range(4):
+        x = make_inputs(cfg, 91 + step, DEV)
+        for k in buf:
+            buf[k].copy_(x[k])
+        for t in out_g:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in out_g] + [aux_g[k].clone() for k in ("p_d", "q_d", "z")]
+        call(ve, out_e, x)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in out_e] + [aux_e[k].clone() for k in ("p_d", "q_d", "z")]
+        for a, b in zip(got, ref):
+            if a.is_floating_point():
+                a, b = torch.nan_to_num(a, nan=-123.0), torch.nan_to_num(b, nan=-123.0)
+            assert torch.equal(a, b), f"walk graph {cfg_name} step {step}"
+        o = O.verify_batch(to_host_f64(x["target"]), to_host_f64(x["draft"]),
+                           x["tokens"].cpu().numpy(), x["uniforms"].cpu().double().numpy(),
+                           cfg.T, O.MODE_STOCHASTIC, draft_len=kb.cpu().numpy(),
+                           walk_order=True)
+        compare(np.arange(cfg.B), o, out_g[0], out_g[1], "stochastic", None,
+                f"graph/walk/{cfg_name}/step {step}")
