@@ -47,7 +47,8 @@ listed with its reason in the design notes):
     marked invalid: accept_len -1, tokens all -1, not counted in the histogram,
     EMA untouched. Needed rows: all K+1 target rows, plus all K draft rows in
     stochastic mode.
-  * Walk-order reading (optional, stochastic mode without truncation; [DVC]
+  * Walk-order reading (optional; stochastic mode without truncation, and the
+    greedy and margin modes; [DVC]
     "Verify several proposed tokens in one target pass": at the first
     rejection the correction is drawn and later proposals are discarded;
     [SMB] "Seeing It in Code": the walk over the drafts stops at the first
@@ -58,8 +59,11 @@ listed with its reason in the design notes):
     rejection, or target row k_b when every position is kept; rows past the
     first rejection are never looked at. End-of-sequence and budget stops
     cut the emission, not the reading. p(d) and q(d) are NaN past the first
-    rejection. With every row and token usable the result equals that of the
-    full reading.
+    rejection. In the greedy and margin modes the walk reads target rows
+    only, stops at the first position that fails its rule, and the argmax
+    side output is -1 for the rows it does not read (the margin ratio NaN).
+    With every row and token usable the result equals that of the full
+    reading (the argmax side output aside).
   * EMA: per call and slot, x = accept_len / K; the first observation of a slot
     sets it, later ones do ema = decay * ema + (1 - decay) * x.
   * Stopping rules ([DVC] "Verify several proposed tokens in one target pass"
@@ -317,7 +321,7 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     nan_k = np.full(K, np.nan)
     out = np.full(K + 1, -1, dtype=np.int64)
     truncated = (0 < int(top_k) < V) or not (float(top_p) >= 1.0)
-    walk_order = bool(walk_order) and mode == MODE_STOCHASTIC and not truncated
+    walk_order = bool(walk_order) and not (mode == MODE_STOCHASTIC and truncated)
 
     valid = 0 <= kb <= K and m >= 1
     if mode == MODE_STOCHASTIC:
@@ -334,6 +338,29 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     if not valid:
         return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
                               math.inf, valid=False)
+    if walk_order and mode != MODE_STOCHASTIC:
+        # greedy and margin walks in walk order: position i's target row is
+        # read once every earlier position is kept; the walk stops at the
+        # first position that fails its rule or whose row or token is not
+        # usable, and reads target row k_b when every position is kept
+        t = kb
+        for i in range(kb):
+            if not (0 <= toks[i] < V and row_is_valid(target[i])):
+                t = i
+                break
+            if toks[i] == argmax[i]:
+                continue
+            if mode == MODE_MARGIN:
+                p = softmax_t(target[i], T)
+                if p[toks[i]] / p[argmax[i]] > tau:
+                    continue
+            t = i
+            break
+        argmax[t + 1:] = -1        # rows the walk does not read
+        usable = row_is_valid(target[t]) and (t == kb or 0 <= toks[t] < V)
+        if not usable:
+            return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
+                                  math.inf, valid=False)
 
     acc_dists = []       # (position, distance of that position's decision)
     zero_q = 0
@@ -404,8 +431,9 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
                 break
     elif mode == MODE_MARGIN:
         for i in range(kb):
-            p = softmax_t(target[i], T)
-            p_d[i] = p[toks[i]] / p[argmax[i]]
+            if argmax[i] >= 0:       # (walk order: rows past the walk are not read)
+                p = softmax_t(target[i], T)
+                p_d[i] = p[toks[i]] / p[argmax[i]]
         j = kb
         for i in range(kb):
             if toks[i] == argmax[i]:

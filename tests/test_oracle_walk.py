@@ -16,7 +16,10 @@ Pinned against things other than the walk-order code itself:
     target rows past k_b are never read;
   * planted-mistake control: a walk that read one position further than its
     first rejection would invalidate the j + 1 case, and one that stopped a
-    position early would keep the j case valid; both are caught above.
+    position early would keep the j case valid; both are caught above;
+  * the greedy and margin walks the same way over target rows, with the
+    argmax side output -1 past the stop, and a margin mismatch that clears
+    tau keeping the walk going.
 """
 
 import math
@@ -166,18 +169,11 @@ def test_stops_cut_the_emission_not_the_reading():
     _same(O.verify_sequence(target, d3, toks, u, 1.0, S, eos=eos, walk_order=True), r)
 
 
-def test_walk_order_leaves_other_modes_and_truncation_alone():
+def test_walk_order_leaves_truncation_alone():
     rng = np.random.default_rng(8)
     V, K = 12, 4
     target, draft, toks = _case(rng, V, K)
     u = rng.random(K + 1)
-    t2 = target.copy()
-    t2[K, 0] = np.nan
-    for mode in (O.MODE_GREEDY, O.MODE_MARGIN):
-        a = O.verify_sequence(t2, None, toks, None, 1.0, mode, tau=0.3)
-        b = O.verify_sequence(t2, None, toks, None, 1.0, mode, tau=0.3, walk_order=True)
-        _same(a, b)
-        assert not b.valid
     d2 = draft.copy()
     d2[K - 1, 0] = np.nan
     for tk, tp in ((5, 1.0), (0, 0.9)):
@@ -185,6 +181,89 @@ def test_walk_order_leaves_other_modes_and_truncation_alone():
         b = O.verify_sequence(target, d2, toks, u, 1.0, S, top_k=tk, top_p=tp, walk_order=True)
         _same(a, b)
         assert not b.valid
+
+
+# greedy and margin walks: target rows only, the walk stops at the first
+# position that fails its rule
+
+def _argmax_case(rng, V, K, t, mode, tau=0.3):
+    """Tokens that keep positions < t and fail position t (t = K: keep all):
+    the row argmax below t, at t a token whose margin ratio is below tau."""
+    target = rng.normal(0, 2.0, (K + 1, V))
+    toks = np.argmax(target[:K], axis=1).astype(np.int64)
+    if t < K:
+        p = O.softmax_t(target[t], 1.0)
+        r = p / p.max()
+        cand = np.flatnonzero(r < 0.5 * tau)
+        toks[t] = cand[0]
+    return target, toks
+
+
+@pytest.mark.parametrize("mode", [O.MODE_GREEDY, O.MODE_MARGIN])
+@pytest.mark.parametrize("t", [0, 2, 4])
+def test_argmax_walk_read_boundary(mode, t):
+    rng = np.random.default_rng(300 + t + 10 * mode)
+    V, K = 12, 4
+    target, toks = _argmax_case(rng, V, K, t, mode)
+    full = O.verify_sequence(target, None, toks, None, 1.0, mode, tau=0.3)
+    ref = O.verify_sequence(target, None, toks, None, 1.0, mode, tau=0.3, walk_order=True)
+    _same(full, ref)
+    assert ref.valid and ref.accept_len == t
+    # the argmax side output: rows the walk reads (0..t), -1 past them
+    assert np.array_equal(ref.argmax[:t + 1], full.argmax[:t + 1])
+    assert np.all(ref.argmax[t + 1:] == -1)
+    if t + 1 <= K:
+        t2 = target.copy()
+        t2[t + 1, 1] = np.nan                    # past the stop: not read
+        _same(O.verify_sequence(t2, None, toks, None, 1.0, mode, tau=0.3, walk_order=True),
+              ref)
+        assert not O.verify_sequence(t2, None, toks, None, 1.0, mode, tau=0.3).valid
+        tk2 = toks.copy()
+        if t + 1 < K:
+            tk2[t + 1] = V + 1                   # a token past the stop: not read
+            _same(O.verify_sequence(target, None, tk2, None, 1.0, mode, tau=0.3,
+                                    walk_order=True), ref)
+    for i in range(t + 1):                       # at and below the stop: read
+        t3 = target.copy()
+        t3[i, :] = -np.inf
+        assert not O.verify_sequence(t3, None, toks, None, 1.0, mode, tau=0.3,
+                                     walk_order=True).valid
+
+
+def test_margin_walk_goes_on_past_a_kept_mismatch():
+    """A drafted token that is not the argmax but clears the margin keeps the
+    walk going: the next row is read (a bad row there invalidates)."""
+    rng = np.random.default_rng(41)
+    V, K = 12, 4
+    target = rng.normal(0, 0.3, (K + 1, V))    # flat rows: every ratio near 1
+    toks = np.argmax(target[:K], axis=1).astype(np.int64)
+    toks[0] = int(np.argsort(target[0])[-2])  # second largest: ratio > 0.3
+    r = O.verify_sequence(target, None, toks, None, 1.0, O.MODE_MARGIN, tau=0.3,
+                          walk_order=True)
+    assert r.valid and r.accept_len == K
+    t2 = target.copy()
+    t2[1, 3] = np.inf
+    assert not O.verify_sequence(t2, None, toks, None, 1.0, O.MODE_MARGIN, tau=0.3,
+                                 walk_order=True).valid
+    assert O.verify_sequence(t2, None, toks, None, 1.0, O.MODE_GREEDY,
+                             walk_order=True).valid   # greedy stops at position 0
+
+
+@pytest.mark.parametrize("mode", [O.MODE_GREEDY, O.MODE_MARGIN])
+def test_argmax_walk_equals_full_reading_on_usable_rows(mode):
+    rng = np.random.default_rng(500 + mode)
+    V, K = 16, 5
+    for _ in range(60):
+        target = rng.normal(0, 2.0, (K + 1, V))
+        toks = np.argmax(target[:K] + rng.normal(0, 1.5, (K, V)), axis=1)
+        kb = int(rng.integers(0, K + 1))
+        a = O.verify_sequence(target, None, toks, None, 1.0, mode, tau=0.3, draft_len=kb)
+        b = O.verify_sequence(target, None, toks, None, 1.0, mode, tau=0.3, draft_len=kb,
+                              walk_order=True)
+        _same(a, b)
+        stop = a.accept_len if a.accept_len < kb else kb
+        assert np.array_equal(a.argmax[:stop + 1], b.argmax[:stop + 1])
+        assert np.all(b.argmax[stop + 1:] == -1)
 
 
 def test_batch_threads_the_reading():
