@@ -85,6 +85,24 @@ def traffic_for(workload: str, kernel: str):
 _W = {}
 
 
+def walk_rows_read(accept_len, kb, mode: str) -> int:
+    """Logit rows one walk-order call reads: position 0's rows (target row 0,
+    and draft row 0 when k_b > 0 for stochastic calls) of every sequence, then
+    every other needed row (target rows 1..k_b, and draft rows 1..k_b-1 for
+    stochastic calls) of the sequences whose walk keeps position 0, i.e. those
+    with j >= 1 (no invalid sequences in these workloads)."""
+    import numpy as np
+    n = 0
+    for j, k in zip(np.asarray(accept_len, dtype=np.int64), np.asarray(kb, dtype=np.int64)):
+        if j < 0:
+            continue
+        if mode == "stochastic":
+            n += 1 + int(k > 0) + ((k + max(k - 1, 0)) if j >= 1 else 0)
+        else:
+            n += 1 + (k if j >= 1 else 0)
+    return int(n)
+
+
 def _worker_init(specs, T, mode, tau, trunc=(0, 1.0), walk=False):
     from multiprocessing import shared_memory
     import numpy as np
@@ -245,12 +263,12 @@ def main():
                     help="stochastic mode: draft residual side output on the draft's top-m "
                          "support (m = this value, 0 = off)")
     ap.add_argument("--walk", action="store_true",
-                    help="stochastic mode: walk-order reading (the rows of a position are read "
-                         "only when the walk reaches it; nothing past the first rejection); "
-                         "no effect with truncation or the residual side output")
+                    help="walk-order reading (the rows of a position are read only when the "
+                         "walk reaches it; nothing past the first rejection); no effect on "
+                         "stochastic calls with truncation or the residual side output")
     ap.add_argument("--no-walk-report", action="store_true",
-                    help="leave out the walk-order timing reported beside a plain stochastic "
-                         "line (counter and trace runs that should see the line's calls only)")
+                    help="leave out the walk-order timing reported beside a plain line "
+                         "(counter and trace runs that should see the line's calls only)")
     ap.add_argument("--policy", action="store_true",
                     help="run the tree-shape policy epilogue (seeded draft confidences, d = 0.5)")
     ap.add_argument("--read-probe", action="store_true",
@@ -298,7 +316,7 @@ def main():
                          torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
     if args.residual and mode == "stochastic":
         v.set_residual(args.residual)
-    walk = args.walk and mode == "stochastic" and not trunc and not args.residual
+    walk = args.walk and not (mode == "stochastic" and (trunc or args.residual))
     if walk:
         v.set_walk_order(True)
     if args.policy:
@@ -328,18 +346,7 @@ def main():
             rows = 0
         draw_bytes.append(rows * V * s)
         if walk:
-            # the library reads position 0's rows (target row 0, draft row 0
-            # when k_b > 0) of every sequence, then every other needed row
-            # (target rows 1..k_b, draft rows 1..k_b-1) of the sequences whose
-            # walk keeps position 0 (no invalid sequences in these workloads)
-            jj = a.numpy().astype(np.int64)
-            kk = kbt.numpy().astype(np.int64)
-            n = 0
-            for jb, kbb in zip(jj[valid.numpy()], kk[valid.numpy()]):
-                n += 1 + int(kbb > 0)
-                if jb >= 1:
-                    n += kbb + max(kbb - 1, 0)
-            walk_rows.append(n)
+            walk_rows.append(walk_rows_read(a.numpy(), kb, mode))
     log(f"warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
@@ -437,7 +444,7 @@ def main():
         "algorithmic_bytes_per_step": int(call_bytes),
         "roofline": roofline,
     }
-    if (mode == "stochastic" and not walk and not trunc and not args.residual
+    if (not walk and not trunc and not args.residual
             and not args.graph and not args.policy and not args.no_walk_report):
         # the same calls with walk-order reading, reported beside the line:
         # rows past each sequence's first rejection are not read
@@ -454,9 +461,7 @@ def main():
                       cfg.tau, out=outw)
             torch.cuda.synchronize()
             same = same and torch.equal(out[0], outw[0]) and torch.equal(out[1], outw[1])
-            a = outw[1].cpu().numpy().astype(np.int64)
-            rows_w.append(int(sum(1 + int(k > 0) + (k + max(k - 1, 0) if j >= 1 else 0)
-                                  for j, k in zip(a, kb) if j >= 0)))
+            rows_w.append(walk_rows_read(outw[1].cpu().numpy(), kb, mode))
         for i in range(args.warmup):
             x = sets[i % len(sets)]
             vw.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], cfg.T, mode,

@@ -295,9 +295,10 @@ class SpecVerifier:
         return sup, res
 
     def set_walk_order(self, on: bool = True):
-        """Walk-order reading for later stochastic calls without truncation:
-        rows past each sequence's first rejection are not read (and so not
-        checked); p(d), q(d) past it are NaN."""
+        """Walk-order reading for later greedy and margin calls and stochastic
+        calls without truncation or the residual side output: rows past each
+        sequence's first rejection are not read (and so not checked); p(d),
+        q(d) or the margin ratio past it are NaN, the per-row argmax -1."""
         self._check(self.lib.spec_verify_set_walk_order(self._h, 1 if on else 0),
                     "set_walk_order")
 

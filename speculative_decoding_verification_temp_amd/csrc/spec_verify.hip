@@ -411,23 +411,47 @@ int run_argmax(spec_verify_handle* h, const Launch& L, int B, const void* target
                int32_t* out_tokens, int32_t* out_len, uint32_t* hist, hipStream_t s) {
   const int K = h->K, V = h->V;
   const int rows = K + 1;
-  const long long grid1 = (long long)B * rows * L.nseg;
+  const int grid2 = div_up(B, sv::kWavesPerBlock);
+  sv::Rules rules = h->rules;
+  rules.walk = h->walk ? 1 : 0;
   prof_mark(h, 0, s);
-  hipLaunchKernelGGL((sv::rowstats_max<DT, VEC, U>), dim3(unsigned(grid1)), dim3(sv::kBlock), 0,
-                     s, target, K, V, L.nseg, L.seg_chunks, h->rules.k, h->parts, hist);
+  if (h->walk) {
+    // walk-order reading: target row 0 of every sequence, then the rows
+    // 1..k_b of the sequences whose walk keeps position 0 (as for stochastic
+    // calls)
+    hipLaunchKernelGGL((sv::rowstats_max<DT, VEC, U>), dim3(unsigned((long long)B * L.nseg)),
+                       dim3(sv::kBlock), 0, s, target, K, V, L.nseg, L.seg_chunks, h->rules.k,
+                       h->parts, hist, 0, 1, h->walk_cnt);
+    if (margin)
+      hipLaunchKernelGGL((sv::walk_gate_argmax<DT, true>), dim3(grid2), dim3(sv::kBlock), 0, s, B,
+                         K, V, L.nseg, h->parts, target, h->rules.k, tokens, invT, tau, 1,
+                         h->walk_seq, h->walk_cnt);
+    else
+      hipLaunchKernelGGL((sv::walk_gate_argmax<DT, false>), dim3(grid2), dim3(sv::kBlock), 0, s,
+                         B, K, V, L.nseg, h->parts, target, h->rules.k, tokens, invT, tau, 1,
+                         h->walk_seq, h->walk_cnt);
+    const long long rest = (long long)B * K * L.nseg;
+    hipLaunchKernelGGL((sv::rowstats_max_list<DT, VEC, U>),
+                       dim3(unsigned(std::max(1ll, std::min<long long>(rest, kWalkGrid)))),
+                       dim3(sv::kBlock), 0, s, target, K, V, L.nseg, L.seg_chunks, h->rules.k,
+                       h->parts, h->walk_seq, h->walk_cnt, 1);
+  } else {
+    hipLaunchKernelGGL((sv::rowstats_max<DT, VEC, U>), dim3(unsigned((long long)B * rows * L.nseg)),
+                       dim3(sv::kBlock), 0, s, target, K, V, L.nseg, L.seg_chunks, h->rules.k,
+                       h->parts, hist, 0, rows, nullptr);
+  }
   int rc = check_launch(h, "rowstats_max");
   prof_mark(h, 1, s);
   if (rc) return rc;
-  const int grid2 = div_up(B, sv::kWavesPerBlock);
   if (margin)
     hipLaunchKernelGGL((sv::scan_argmax<DT, true>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K, V,
-                       L.nseg, h->parts, target, tokens, invT, tau, h->rules, out_tokens, out_len,
+                       L.nseg, h->parts, target, tokens, invT, tau, rules, out_tokens, out_len,
                        hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);
   else
     hipLaunchKernelGGL((sv::scan_argmax<DT, false>), dim3(grid2), dim3(sv::kBlock), 0, s, B, K,
-                       V, L.nseg, h->parts, target, tokens, invT, tau, h->rules, out_tokens, out_len,
+                       V, L.nseg, h->parts, target, tokens, invT, tau, rules, out_tokens, out_len,
                        hist,
                        h->ema, h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z,
                        h->aux_argmax);

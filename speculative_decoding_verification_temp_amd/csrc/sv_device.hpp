@@ -206,6 +206,18 @@ __device__ inline void combine_sum_parts(const RowPart* p, int nseg, float& R, d
 
 __device__ inline bool finite_pos(double S) { return S > 0.0 && S < __builtin_inf(); }
 
+// A row's maximum, lowest argmax and NaN flag from its segments' partials.
+__device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, int& idx,
+                                         int& nan) {
+  m = p[0].m;
+  idx = p[0].idx;
+  nan = p[0].flags;
+  for (int s = 1; s < nseg; ++s) {
+    argmax_combine(m, idx, p[s].m, p[s].idx);
+    nan |= p[s].flags;
+  }
+}
+
 // The acceptance test of one drafted position ([SMB] "The Guarantee Behind
 // Rejection Sampling"; [RNR] s.2): from the logits of its drafted token in
 // the target and draft rows and the rows' normalisers, P = p(d), Q = q(d);

@@ -25,16 +25,6 @@ namespace sv {
 // Scan helpers
 // --------------------------------------------------------------------------
 
-__device__ inline void combine_max_parts(const RowPart* p, int nseg, float& m, int& idx,
-                                         int& nan) {
-  m = p[0].m;
-  idx = p[0].idx;
-  nan = p[0].flags;
-  for (int s = 1; s < nseg; ++s) {
-    argmax_combine(m, idx, p[s].m, p[s].idx);
-    nan |= p[s].flags;
-  }
-}
 
 
 // Tree-shape policy epilogue ([MNW] s.3, dynamic draft tree-shaping), run
@@ -348,26 +338,21 @@ __global__ __launch_bounds__(kBlock) void scan_argmax(
   if (lane < kb) {
     d = tokens[(long long)b * K + lane];
     lane_bad |= !(d >= 0 && d < V);
-    if (!lane_bad) {
-      if constexpr (MARGIN) {
-        const float xd = load_logit<DT>(row_ptr<DT>(target, nullptr, b, lane, K, V), d);
-        ratio = exp((double(xd) - double(m)) * invT);
-        keep = (d == A) || (ratio > tau);
-      } else {
-        keep = (d == A);
-      }
-    }
+    if (!lane_bad) keep = argmax_kept<DT, MARGIN>(target, b, lane, K, V, d, A, m, invT, tau, ratio);
   }
-  const bool bad = __any(lane_bad);
+  const bool bad = sequence_bad(lane, kb, sp.walk != 0, lane_bad, keep);
   const Walk w = walk_outcome(lane, kb, mm, sp.eos, keep, d);
   const int Aj = __shfl(A, w.j, kWave);
 
+  // rows past k_b are not read, nor with walk-order reading rows past the
+  // position the walk stops at
+  const int last = sp.walk ? w.j : kb;
   if (aux_p != nullptr && lane < K)
-    aux_p[(long long)b * K + lane] = (bad || lane >= kb) ? __builtin_nan("") : ratio;
+    aux_p[(long long)b * K + lane] = (bad || lane >= kb || lane > last) ? __builtin_nan("") : ratio;
   if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = __builtin_nan("");
   if (aux_z != nullptr && lane == 0) aux_z[b] = -1.0;
   if (aux_argmax != nullptr && lane <= K)
-    aux_argmax[(long long)b * (K + 1) + lane] = lane <= kb ? A : -1;   // rows past k_b unread
+    aux_argmax[(long long)b * (K + 1) + lane] = lane <= last ? A : -1;
   emit_and_update(lane, b, K, kb, w.n, w.cpos, Aj, bad, out_tokens, out_len, hist, ema, steps,
                   decay, st, d, sp.pol);
 }

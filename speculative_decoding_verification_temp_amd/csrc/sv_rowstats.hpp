@@ -425,22 +425,17 @@ __global__ __launch_bounds__(kBlock) void rowstats_sum_list(
 // A lane remembers the first chunk in which its running maximum was reached
 // and finds the lowest matching element in it at the end.
 // --------------------------------------------------------------------------
+// One (target row, segment) of the argmax pass: the segment's maximum, its
+// lowest index and a NaN flag, written to parts[(b (K+1) + r) nseg + seg].
+// Called once per workgroup (rowstats_max) or for each listed row segment in
+// turn (rowstats_max_list); every thread of the workgroup calls it.
 template <int DT, int VEC, int U>
-__global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ target, int K,
-                                                       int V, int nseg, int seg_chunks,
-                                                       const int32_t* __restrict__ kdraft,
-                                                       RowPart* __restrict__ parts,
-                                                       uint32_t* __restrict__ hist) {
+__device__ __forceinline__ void max_segment(const void* __restrict__ target, int b, int r,
+                                            int seg, int K, int V, int nseg, int seg_chunks,
+                                            RowPart* __restrict__ parts) {
   using C = Chunk<DT, VEC>;
   const int tid = threadIdx.x;
-  const long long wg = blockIdx.x;
-  const int rows = K + 1;
-  const int seg = int(wg % nseg);
-  const long long grow = wg / nseg;
-  const int b = int(grow / rows), r = int(grow % rows);
-  if (wg == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
-  if (kdraft != nullptr && r > kdraft[b]) return;   // target row past k_b: not needed
-
+  const long long wg = ((long long)b * (K + 1) + r) * nseg + seg;
   const void* row = row_ptr<DT>(target, nullptr, b, r, K, V);
   const long long nchunks = V / VEC;
   const long long c0 = (long long)seg * seg_chunks;
@@ -520,6 +515,110 @@ __global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ 
     p.idx = i;
     p.flags = f ? 1 : 0;
     parts[wg] = p;
+  }
+}
+
+// Every (target row, segment) of target rows r0 .. r0 + nr - 1 of every
+// sequence (all of them: r0 = 0, nr = K + 1); workgroup 0 clears the
+// histogram and, when set, the walk-order list count.
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_max(const void* __restrict__ target, int K,
+                                                       int V, int nseg, int seg_chunks,
+                                                       const int32_t* __restrict__ kdraft,
+                                                       RowPart* __restrict__ parts,
+                                                       uint32_t* __restrict__ hist, int r0,
+                                                       int nr, uint32_t* __restrict__ clear) {
+  const int tid = threadIdx.x;
+  const long long lw = blockIdx.x;
+  const int seg = int(lw % nseg);
+  const long long lrow = lw / nseg;
+  const int b = int(lrow / nr), r = r0 + int(lrow % nr);
+  if (lw == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (lw == 0 && clear != nullptr && tid == 0) *clear = 0u;
+  if (kdraft != nullptr && r > kdraft[b]) return;   // target row past k_b: not needed
+  max_segment<DT, VEC, U>(target, b, r, seg, K, V, nseg, seg_chunks, parts);
+}
+
+// The greedy or margin test of one drafted position from its target row's
+// combined maximum m and lowest argmax A ([SMB] "The Guarantee Behind
+// Rejection Sampling": greedy keeps a draft that is the target's argmax;
+// [MNW] the margin rule also keeps one whose probability ratio to the top-1
+// token exceeds tau). Every place that takes this decision (the argmax scan
+// and the walk-order gate) calls this one function. ratio: the margin ratio.
+template <int DT, bool MARGIN>
+__device__ inline bool argmax_kept(const void* __restrict__ target, int b, int i, int K, int V,
+                                   int d, int A, float m, double invT, double tau,
+                                   double& ratio) {
+  if constexpr (MARGIN) {
+    const float xd = load_logit<DT>(row_ptr<DT>(target, nullptr, b, i, K, V), d);
+    ratio = exp((double(xd) - double(m)) * invT);
+    return (d == A) || (ratio > tau);
+  } else {
+    return d == A;
+  }
+}
+
+// The greedy or margin walk of sequence b keeps every position below p
+// (one wavefront; lane i tests position i from its row's partials; an
+// unusable row or token stops the walk).
+template <int DT, bool MARGIN>
+__device__ inline bool argmax_walk_reaches(const RowPart* __restrict__ parts,
+                                           const void* __restrict__ target, int b, int K, int V,
+                                           int nseg, int p, int kb,
+                                           const int32_t* __restrict__ tokens, double invT,
+                                           double tau) {
+  const int lane = threadIdx.x & (kWave - 1);
+  bool stop = false;
+  if (lane < p && lane < kb) {
+    float m;
+    int A, nan;
+    combine_max_parts(parts + ((long long)b * (K + 1) + lane) * nseg, nseg, m, A, nan);
+    const int d = tokens[(long long)b * K + lane];
+    stop = nan != 0 || !(m > -__builtin_inff() && m < __builtin_inff()) || A < 0 ||
+           !(d >= 0 && d < V);
+    if (!stop) {
+      double ratio;
+      stop = !argmax_kept<DT, MARGIN>(target, b, lane, K, V, d, A, m, invT, tau, ratio);
+    }
+  }
+  return __ballot(stop) == 0ull;
+}
+
+// Walk-order reading of greedy and margin calls, after the argmax pass over
+// target row 0: lists the sequences whose walk keeps position 0 and that
+// have rows past it (k_b >= 1), as walk_gate does for stochastic calls.
+template <int DT, bool MARGIN>
+__global__ __launch_bounds__(kBlock) void walk_gate_argmax(
+    int B, int K, int V, int nseg, const RowPart* __restrict__ parts,
+    const void* __restrict__ target, const int32_t* __restrict__ kdraft,
+    const int32_t* __restrict__ tokens, double invT, double tau, int p0,
+    int32_t* __restrict__ seqs, uint32_t* __restrict__ count) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (b >= B) return;                              // (the whole wavefront)
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (!(kb >= p0 && kb <= K)) return;
+  if (argmax_walk_reaches<DT, MARGIN>(parts, target, b, K, V, nseg, p0, kb, tokens, invT, tau) &&
+      lane == 0)
+    seqs[atomicAdd(count, 1u)] = b;
+}
+
+// Walk-order reading: the (target row, segment)s of rows p0..K of the listed
+// sequences over a fixed grid, as rowstats_sum_list does for stochastic calls.
+template <int DT, int VEC, int U>
+__global__ __launch_bounds__(kBlock) void rowstats_max_list(
+    const void* __restrict__ target, int K, int V, int nseg, int seg_chunks,
+    const int32_t* __restrict__ kdraft, RowPart* __restrict__ parts,
+    const int32_t* __restrict__ seqs, const uint32_t* __restrict__ count, int p0) {
+  const int nr = K + 1 - p0;
+  const long long items = (long long)(*count) * nr * nseg;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int seg = int(it % nseg);
+    const long long lrow = it / nseg;
+    const int b = seqs[lrow / nr], r = p0 + int(lrow % nr);
+    if (kdraft != nullptr && r > kdraft[b]) continue;   // (uniform)
+    max_segment<DT, VEC, U>(target, b, r, seg, K, V, nseg, seg_chunks, parts);
+    __syncthreads();                 // the combine's LDS is reused by the next segment
   }
 }
 

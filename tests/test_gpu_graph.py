@@ -147,8 +147,9 @@ def test_graph_replay_argmax_modes(sv, mode):
         assert np.array_equal(out[2].cpu().numpy().astype(np.int64), ref.hist)
 
 
-@pytest.mark.parametrize("cfg_name", ["c2", "c1"])
-def test_graph_replay_walk_order(sv, cfg_name):
+@pytest.mark.parametrize("cfg_name,mode", [("c2", "stochastic"), ("c1", "stochastic"),
+                                           ("c2", "greedy"), ("c1", "margin")])
+def test_graph_replay_walk_order(sv, cfg_name, mode):
     """A walk-order call (its list count is cleared by its first kernel, not
     by a memset) captured once and replayed on fresh inputs with stopping
     rules on: every output equals an eager twin's, the tokens the oracle's
@@ -169,12 +170,19 @@ def test_graph_replay_walk_order(sv, cfg_name):
 
     vg, aux_g, out_g = setup()
     ve, aux_e, out_e = setup()
-    x0 = make_inputs(cfg, 90, DEV)
-    buf = {k: x0[k].clone() for k in ("target", "draft", "tokens", "uniforms")}
+    stoch = mode == "stochastic"
+    gen_mode = "stochastic" if stoch else "greedy"
+    x0 = make_inputs(cfg, 90, DEV, gen_mode)
+    names = ("target", "draft", "tokens", "uniforms") if stoch else ("target", "tokens")
+    buf = {k: x0[k].clone() for k in names}
+    aux_keys = ("p_d", "q_d", "z") if stoch else ("p_d", "argmax")
 
     def call(v, out, inp):
-        v.verify(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"], cfg.T,
-                 "stochastic", out=out)
+        if stoch:
+            v.verify(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"], cfg.T,
+                     "stochastic", out=out)
+        else:
+            v.verify(inp["target"], None, inp["tokens"], None, cfg.T, mode, tau=0.3, out=out)
 
     side = torch.cuda.Stream(DEV)
     side.wait_stream(torch.cuda.current_stream(DEV))
@@ -187,7 +195,7 @@ def test_graph_replay_walk_order(sv, cfg_name):
     with torch.cuda.graph(g):
         call(vg, out_g, buf)
     for step in range(4):
-        x = make_inputs(cfg, 91 + step, DEV)
+        x = make_inputs(cfg, 91 + step, DEV, gen_mode)
         for k in buf:
             buf[k].copy_(x[k])
         for t in out_g:
@@ -195,17 +203,19 @@ def test_graph_replay_walk_order(sv, cfg_name):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in out_g] + [aux_g[k].clone() for k in ("p_d", "q_d", "z")]
+        got = [t.clone() for t in out_g] + [aux_g[k].clone() for k in aux_keys]
         call(ve, out_e, x)
         torch.cuda.synchronize()
-        ref = [t.clone() for t in out_e] + [aux_e[k].clone() for k in ("p_d", "q_d", "z")]
+        ref = [t.clone() for t in out_e] + [aux_e[k].clone() for k in aux_keys]
         for a, b in zip(got, ref):
             if a.is_floating_point():
                 a, b = torch.nan_to_num(a, nan=-123.0), torch.nan_to_num(b, nan=-123.0)
-            assert torch.equal(a, b), f"walk graph {cfg_name} step {step}"
-        o = O.verify_batch(to_host_f64(x["target"]), to_host_f64(x["draft"]),
+            assert torch.equal(a, b), f"walk graph {cfg_name} {mode} step {step}"
+        m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY,
+             "margin": O.MODE_MARGIN}[mode]
+        o = O.verify_batch(to_host_f64(x["target"]),
+                           to_host_f64(x["draft"]) if stoch else None,
                            x["tokens"].cpu().numpy(), x["uniforms"].cpu().double().numpy(),
-                           cfg.T, O.MODE_STOCHASTIC, draft_len=kb.cpu().numpy(),
-                           walk_order=True)
-        compare(np.arange(cfg.B), o, out_g[0], out_g[1], "stochastic", None,
-                f"graph/walk/{cfg_name}/step {step}")
+                           cfg.T, m, 0.3, draft_len=kb.cpu().numpy(), walk_order=True)
+        compare(np.arange(cfg.B), o, out_g[0], out_g[1], mode, None,
+                f"graph/walk/{cfg_name}/{mode}/step {step}")

@@ -8,7 +8,10 @@ scan / tile / pick kernels), bf16 and fp32 rows, whole batches (c1, c2, c3),
 against the full reading of the same inputs (every output equal, p(d) and
 q(d) NaN past the first rejection), with unusable rows and tokens planted
 past, at and below each sequence's first rejection and in the bonus row, and
-with the stopping rules.
+with the stopping rules. The greedy and margin walks (target rows only: the
+argmax pass over row 0, then the rows of the sequences that keep position 0)
+are checked the same way, with the per-row argmax side output -1 and the
+margin ratio NaN past the row the walk stops at.
 """
 
 import numpy as np
@@ -31,7 +34,7 @@ def sv():
     return pkg
 
 
-def _run(sv, x, cfg, walk, stops=None):
+def _run(sv, x, cfg, walk, stops=None, mode="stochastic", tau=0.3):
     v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype, ema_decay=0.9)
     aux = v.enable_aux()
     if stops is not None:
@@ -39,8 +42,11 @@ def _run(sv, x, cfg, walk, stops=None):
         v.set_stops(eos, None if kb is None else torch.as_tensor(kb, device=DEV).contiguous(),
                     None if mx is None else torch.as_tensor(mx, device=DEV).contiguous())
     v.set_walk_order(walk)
-    tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"],
-                               "stochastic")
+    if mode == "stochastic":
+        tok, alen, hist = v.verify(x["target"], x["draft"], x["tokens"], x["uniforms"], x["T"],
+                                   "stochastic")
+    else:
+        tok, alen, hist = v.verify(x["target"], None, x["tokens"], None, x["T"], mode, tau=tau)
     torch.cuda.synchronize()
     out = (tok.clone(), alen.clone(), hist.clone(), {k: t.clone() for k, t in aux.items()})
     v.close()
@@ -172,3 +178,146 @@ def test_walk_with_stopping_rules(sv):
     compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c2/walk/stops")
     _pq_pattern(walk[3], ref, rows, "c2/stops")
     _same_outputs(walk, full)
+
+
+# --------------------------------------------------------------------------
+# greedy and margin
+# --------------------------------------------------------------------------
+
+TAU = 0.3
+
+
+def _argmax_checks(res, ref, rows, mode, label):
+    """Side outputs of the greedy and margin walks: the argmax -1 exactly
+    where the oracle's is on valid sequences (rows past the stop are not
+    read), the margin ratio NaN exactly where the oracle's is."""
+    valid = ref.accept_len >= 0
+    ga = res[3]["argmax"].cpu().numpy()[rows]
+    assert np.array_equal(ga[valid], ref.argmax[valid]), f"{label}: argmax"
+    if mode == "margin":
+        gp = res[3]["p_d"].cpu().numpy()[rows]
+        assert np.array_equal(np.isnan(gp), np.isnan(ref.p_d)), f"{label}: ratio NaN pattern"
+
+
+def _same_argmax_outputs(walk, full, mode):
+    """Tokens, lengths and histogram equal; where the walk read a row, its
+    argmax and margin ratio are those of the full reading (the same maxima:
+    no rounding is involved)."""
+    for a, b in zip(walk[:3], full[:3]):
+        assert torch.equal(a, b)
+    ok = walk[1].cpu().numpy() >= 0
+    ga, fa = walk[3]["argmax"].cpu().numpy()[ok], full[3]["argmax"].cpu().numpy()[ok]
+    read = ga >= 0
+    assert np.array_equal(ga[read], fa[read])
+    if mode == "margin":
+        g, f = walk[3]["p_d"].cpu().numpy(), full[3]["p_d"].cpu().numpy()
+        read = ~np.isnan(g)
+        assert np.array_equal(g[read], f[read])
+
+
+@pytest.mark.parametrize("mode", ["greedy", "margin"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c2odd"])
+def test_walk_argmax_matches_oracle_and_full_reading(sv, name, mode):
+    # c2odd: V not a multiple of the vector width (the one-element load path)
+    cfg = CONFIGS["c2"].scaled(V=32003) if name == "c2odd" else CONFIGS[name]
+    x = make_inputs(cfg, 4, DEV, "greedy")
+    rows = np.arange(cfg.B)
+    full = _run(sv, x, cfg, False, mode=mode, tau=TAU)
+    walk = _run(sv, x, cfg, True, mode=mode, tau=TAU)
+    ref = oracle_for(x, rows, mode, tau=TAU, walk=True)
+    compare(rows, ref, walk[0], walk[1], mode, walk[3], f"{name}/{mode}/walk")
+    check_invariants(walk[0], walk[1], walk[2], x["tokens"], cfg.V, cfg.K)
+    _argmax_checks(walk, ref, rows, mode, f"{name}/{mode}")
+    _same_argmax_outputs(walk, full, mode)
+    # the walk stops at position 0 in some sequences and goes past it in others
+    a = walk[1].cpu().numpy()
+    if cfg.B >= 16:
+        assert (a == 0).any() and (a >= 1).any()
+
+
+@pytest.mark.parametrize("name,mode", [("c3", "greedy"), ("c4", "margin"), ("c4", "greedy")])
+def test_walk_argmax_whole_batch(sv, name, mode):
+    cfg = CONFIGS[name]
+    x = make_inputs(cfg, 0, DEV, "greedy")
+    rows = np.arange(cfg.B)
+    full = _run(sv, x, cfg, False, mode=mode, tau=cfg.tau or TAU)
+    walk = _run(sv, x, cfg, True, mode=mode, tau=cfg.tau or TAU)
+    ref = oracle_for(x, rows, mode, tau=cfg.tau or TAU, walk=True)
+    compare(rows, ref, walk[0], walk[1], mode, walk[3], f"{name}/{mode}/walk")
+    _argmax_checks(walk, ref, rows, mode, f"{name}/{mode}")
+    _same_argmax_outputs(walk, full, mode)
+
+
+def _plant_target(x, cfg, j, seed):
+    """Unusable target rows and tokens placed by each sequence's stop j
+    (from the full reading): past it (never read by the walk), at it and below
+    it (read), and in the last row of sequences that keep every draft."""
+    rng = np.random.default_rng(seed)
+    K, V = cfg.K, cfg.V
+    tg, tk = x["target"].clone(), x["tokens"].clone()
+
+    def spoil(row):
+        k = int(rng.integers(0, 3))
+        if k == 0:
+            row[int(rng.integers(0, V))] = float("nan")
+        elif k == 1:
+            row[int(rng.integers(0, V))] = float("inf")
+        else:
+            row.fill_(float("-inf"))
+
+    for b in range(cfg.B):
+        jb = int(j[b])
+        case = b % 4
+        if case == 0 and jb < K:                 # past the stop: the next row
+            spoil(tg[b, jb + 1])
+        elif case == 1 and jb < K:               # at the stop
+            spoil(tg[b, jb])
+        elif case == 2 and jb > 0:               # below it
+            spoil(tg[b, jb - 1])
+        elif case == 3 and jb + 1 < K:           # a drafted token out of range past it
+            tk[b, jb + 1] = -2
+        if jb == K:                              # every draft kept: the last row
+            spoil(tg[b, K])
+    return dict(x, target=tg, tokens=tk)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "margin"])
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_walk_argmax_unusable_rows_count_only_where_read(sv, name, mode):
+    cfg = CONFIGS[name].scaled(B=CONFIGS[name].B * 8) if name == "c1" else CONFIGS[name]
+    x = make_inputs(cfg, 9, DEV, "greedy")
+    j = _run(sv, x, cfg, False, mode=mode)[1].cpu().numpy()
+    assert np.all(j >= 0)
+    y = _plant_target(x, cfg, j, 23)
+    rows = np.arange(cfg.B)
+    walk = _run(sv, y, cfg, True, mode=mode)
+    full = _run(sv, y, cfg, False, mode=mode)
+    ref = oracle_for(y, rows, mode, tau=TAU, walk=True)
+    ref_full = oracle_for(y, rows, mode, tau=TAU)
+    compare(rows, ref, walk[0], walk[1], mode, walk[3], f"{name}/{mode}/walk/planted")
+    compare(rows, ref_full, full[0], full[1], mode, full[3], f"{name}/{mode}/full/planted")
+    _argmax_checks(walk, ref, rows, mode, f"{name}/{mode}/planted")
+    a_walk, a_full = walk[1].cpu().numpy(), full[1].cpu().numpy()
+    assert (a_walk < 0).sum() < (a_full < 0).sum()
+    assert np.array_equal(a_walk < 0, ref.accept_len < 0)
+    assert np.array_equal(a_full < 0, ref_full.accept_len < 0)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "margin"])
+def test_walk_argmax_with_stopping_rules(sv, mode):
+    cfg = CONFIGS["c2"]
+    x = make_inputs(cfg, 12, DEV, "greedy")
+    rng = np.random.default_rng(6)
+    toks = x["tokens"].cpu().numpy()
+    eos = int(np.bincount(toks.ravel()).argmax())
+    kb = rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    mx = rng.integers(1, cfg.K + 3, cfg.B).astype(np.int32)
+    kb[1], kb[2], mx[3] = -1, cfg.K + 1, 0
+    stops = (eos, kb, mx)
+    rows = np.arange(cfg.B)
+    walk = _run(sv, x, cfg, True, stops, mode=mode)
+    full = _run(sv, x, cfg, False, stops, mode=mode)
+    ref = oracle_for(x, rows, mode, tau=TAU, stops=stops, walk=True)
+    compare(rows, ref, walk[0], walk[1], mode, walk[3], f"c2/{mode}/walk/stops")
+    _argmax_checks(walk, ref, rows, mode, f"c2/{mode}/stops")
+    _same_argmax_outputs(walk, full, mode)
