@@ -1196,8 +1196,9 @@ __global__ __launch_bounds__(kFBlock) void verify_fused(
 // combines the row partials (fixed order) and runs phases 2-4. TRUNC: after
 // a truncation pass instead (sv_trunc.hpp for bf16 rows, sv_trunc32.hpp for
 // fp32), with one partial per row whose idx holds the row's threshold key.
+// (four wavefronts per SIMD: two 512-thread workgroups share a compute unit)
 template <int DT, int VEC, int NT, bool TRUNC>
-__global__ __launch_bounds__(NT) void finish_seq(
+__global__ __launch_bounds__(NT, 4) void finish_seq(
     int K, int V, int nseg, const RowPart* __restrict__ parts, const void* __restrict__ target,
     const void* __restrict__ draft, const int32_t* __restrict__ tokens,
     const float* __restrict__ uniforms, float c, double c64, int n_half, Rules sp,
