@@ -47,8 +47,8 @@ listed with its reason in the design notes):
     marked invalid: accept_len -1, tokens all -1, not counted in the histogram,
     EMA untouched. Needed rows: all K+1 target rows, plus all K draft rows in
     stochastic mode.
-  * Walk-order reading (optional; stochastic mode without truncation, and the
-    greedy and margin modes; [DVC]
+  * Walk-order reading (optional; stochastic mode, with or without
+    truncation, and the greedy and margin modes; [DVC]
     "Verify several proposed tokens in one target pass": at the first
     rejection the correction is drawn and later proposals are discarded;
     [SMB] "Seeing It in Code": the walk over the drafts stops at the first
@@ -62,8 +62,11 @@ listed with its reason in the design notes):
     rejection. In the greedy and margin modes the walk reads target rows
     only, stops at the first position that fails its rule, and the argmax
     side output is -1 for the rows it does not read (the margin ratio NaN).
-    With every row and token usable the result equals that of the full
-    reading (the argmax side output aside).
+    With truncation every row the walk reads is truncated as in the full
+    reading (top_p <= 0 or NaN still makes the sequence invalid), and only
+    those rows' top-p cuts count among the decisions. With every row and
+    token usable the result equals that of the full reading (the argmax side
+    output aside).
   * EMA: per call and slot, x = accept_len / K; the first observation of a slot
     sets it, later ones do ema = decay * ema + (1 - decay) * x.
   * Stopping rules ([DVC] "Verify several proposed tokens in one target pass"
@@ -320,8 +323,7 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
     toks = np.asarray(tokens, dtype=np.int64).reshape(K)
     nan_k = np.full(K, np.nan)
     out = np.full(K + 1, -1, dtype=np.int64)
-    truncated = (0 < int(top_k) < V) or not (float(top_p) >= 1.0)
-    walk_order = bool(walk_order) and not (mode == MODE_STOCHASTIC and truncated)
+    walk_order = bool(walk_order)
 
     valid = 0 <= kb <= K and m >= 1
     if mode == MODE_STOCHASTIC:
@@ -332,6 +334,8 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
         if mode == MODE_STOCHASTIC:
             valid = valid and all(row_is_valid(draft[i]) for i in range(kb))
             valid = valid and float(top_p) > 0.0      # NaN compares false
+    elif mode == MODE_STOCHASTIC:
+        valid = valid and float(top_p) > 0.0          # (a parameter, not a row)
     # per-row argmax side output: rows 0..k_b (rows past k_b are not read)
     argmax = np.array([argmax_lowest(target[i]) if i <= kb and row_is_valid(target[i]) else -1
                        for i in range(K + 1)], dtype=np.int64)
@@ -390,15 +394,19 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
         if walk_order:
             # read position i's rows only once the walk reaches it; a row or
             # token the walk reads that is not usable makes the sequence
-            # invalid, later ones are never looked at
+            # invalid, later ones are never looked at; each row read is
+            # truncated, and its top-p cut is a decision too
             p_rows, q_rows = [], []
             for i in range(kb):
                 if not (0 <= toks[i] < V and row_is_valid(target[i])
                         and row_is_valid(draft[i])):
                     return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
                                           math.inf, valid=False)
-                p_rows.append(truncated_softmax(target[i], T)[0])
-                q_rows.append(truncated_softmax(draft[i], T)[0])
+                pi, dt = truncated_softmax(target[i], T, top_k, top_p)
+                qi, dq = truncated_softmax(draft[i], T, top_k, top_p)
+                acc_dists += [(-1, d) for d in (dt, dq) if d < math.inf]
+                p_rows.append(pi)
+                q_rows.append(qi)
                 p_d[i] = p_rows[i][toks[i]]
                 q_d[i] = q_rows[i][toks[i]]
                 if not kept(i):
@@ -408,7 +416,9 @@ def verify_sequence(target, draft, tokens, u, T: float, mode: int,
                 if not row_is_valid(target[kb]):
                     return SequenceResult(out, -1, nan_k.copy(), nan_k.copy(), -1.0, argmax,
                                           math.inf, valid=False)
-                p_rows.append(truncated_softmax(target[kb], T)[0])
+                pb, db = truncated_softmax(target[kb], T, top_k, top_p)
+                acc_dists += [(-1, db)] if db < math.inf else []
+                p_rows.append(pb)
         else:
             tp = [truncated_softmax(target[i], T, top_k, top_p) for i in range(kb + 1)]
             tq = [truncated_softmax(draft[i], T, top_k, top_p) for i in range(kb)]

@@ -1,5 +1,5 @@
-"""Pins for the oracle's walk-order reading (stochastic mode without
-truncation): a position's rows are read only once the walk reaches it, and
+"""Pins for the oracle's walk-order reading: a position's rows are read only
+once the walk reaches it, and
 the walk reads nothing past its first rejection ([DVC] "Verify several
 proposed tokens in one target pass": at the first rejection the correction is
 drawn and later proposals are discarded; [SMB] "Seeing It in Code": the walk
@@ -19,7 +19,11 @@ Pinned against things other than the walk-order code itself:
     position early would keep the j case valid; both are caught above;
   * the greedy and margin walks the same way over target rows, with the
     argmax side output -1 past the stop, and a margin mismatch that clears
-    tau keeping the walk going.
+    tau keeping the walk going;
+  * with truncation: the full reading's result on usable rows (each row read
+    truncated as there), the same read boundary, the top-p parameter still
+    checked, and only the rows read contributing top-p cut decisions (so the
+    smallest decision distance is never below the full reading's).
 """
 
 import math
@@ -169,18 +173,113 @@ def test_stops_cut_the_emission_not_the_reading():
     _same(O.verify_sequence(target, d3, toks, u, 1.0, S, eos=eos, walk_order=True), r)
 
 
-def test_walk_order_leaves_truncation_alone():
+TRUNCS = ((5, 1.0), (0, 0.9), (3, 0.8), (1, 1.0), (0, 0.5))
+
+
+def _forced_trunc(rng, V, K, j, tk, tp):
+    """As _forced, under truncation (top_k tk, top_p tp): positions < j draft
+    their target row's argmax (inside any truncation, so p > 0 and u = 0
+    keeps them); position j drafts a token the truncated draft row keeps
+    with truncated p below half its truncated q, and u just below 1."""
+    while True:
+        target, draft, toks = _case(rng, V, K)
+        u = np.zeros(K + 1)
+        u[K] = rng.random()
+        toks[:j] = np.argmax(target[:j], axis=1)
+        if j == K:
+            return target, draft, toks, u
+        p = O.truncated_softmax(target[j], 1.0, tk, tp)[0]
+        q = O.truncated_softmax(draft[j], 1.0, tk, tp)[0]
+        cand = np.flatnonzero((q > 0) & (p < 0.5 * q))
+        if len(cand):
+            toks[j] = cand[0]
+            u[j] = 0.999999
+            return target, draft, toks, u
+
+
+@pytest.mark.parametrize("tk,tp", TRUNCS)
+def test_truncated_walk_equals_full_reading_on_usable_rows(tk, tp):
+    rng = np.random.default_rng(800 + tk + int(10 * tp))
+    V, K = 14, 5
+    for _ in range(30):
+        target, draft, toks = _case(rng, V, K)
+        u = rng.random(K + 1)
+        full = O.verify_sequence(target, draft, toks, u, 1.0, S, top_k=tk, top_p=tp)
+        walk = O.verify_sequence(target, draft, toks, u, 1.0, S, top_k=tk, top_p=tp,
+                                 walk_order=True)
+        _same(full, walk)
+        j = full.accept_len
+        last = j if j < K else K - 1
+        assert np.array_equal(full.p_d[:last + 1], walk.p_d[:last + 1])
+        assert np.array_equal(full.q_d[:last + 1], walk.q_d[:last + 1])
+        assert np.all(np.isnan(walk.p_d[last + 1:])) and np.all(np.isnan(walk.q_d[last + 1:]))
+        # the walk's decisions are a subset of the full reading's
+        assert walk.min_dist >= full.min_dist
+
+
+@pytest.mark.parametrize("tk,tp", ((5, 1.0), (0, 0.9)))
+@pytest.mark.parametrize("j", [0, 2])
+def test_truncated_read_boundary(tk, tp, j):
+    rng = np.random.default_rng(60 + j + tk)
+    V, K = 12, 5
+    target, draft, toks, u = _forced_trunc(rng, V, K, j, tk, tp)
+    ref = O.verify_sequence(target, draft, toks, u, 1.0, S, top_k=tk, top_p=tp, walk_order=True)
+    assert ref.valid and ref.accept_len == j
+    for which in ("target", "draft"):
+        t2, d2 = target.copy(), draft.copy()
+        (t2 if which == "target" else d2)[j + 1, 1] = np.nan      # past it: not read
+        _same(O.verify_sequence(t2, d2, toks, u, 1.0, S, top_k=tk, top_p=tp, walk_order=True),
+              ref)
+        assert not O.verify_sequence(t2, d2, toks, u, 1.0, S, top_k=tk, top_p=tp).valid
+        t3, d3 = target.copy(), draft.copy()
+        (t3 if which == "target" else d3)[j, 1] = np.inf          # at it: read
+        assert not O.verify_sequence(t3, d3, toks, u, 1.0, S, top_k=tk, top_p=tp,
+                                     walk_order=True).valid
+
+
+def test_truncated_walk_still_checks_top_p():
     rng = np.random.default_rng(8)
     V, K = 12, 4
     target, draft, toks = _case(rng, V, K)
     u = rng.random(K + 1)
-    d2 = draft.copy()
-    d2[K - 1, 0] = np.nan
-    for tk, tp in ((5, 1.0), (0, 0.9)):
-        a = O.verify_sequence(target, d2, toks, u, 1.0, S, top_k=tk, top_p=tp)
-        b = O.verify_sequence(target, d2, toks, u, 1.0, S, top_k=tk, top_p=tp, walk_order=True)
-        _same(a, b)
-        assert not b.valid
+    for tp in (0.0, -1.0, float("nan")):
+        r = O.verify_sequence(target, draft, toks, u, 1.0, S, top_p=tp, walk_order=True)
+        assert not r.valid and r.accept_len == -1
+    # greedy ignores the truncation parameters, as in the full reading
+    g = O.verify_sequence(target, None, toks, None, 1.0, O.MODE_GREEDY, top_p=0.0,
+                          walk_order=True)
+    assert g.valid
+
+
+def test_truncated_walk_cut_decisions_only_from_rows_read():
+    """A top-p cut close to moving in a row past the first rejection is not a
+    decision of the walk-order reading (it is one of the full reading)."""
+    rng = np.random.default_rng(23)
+    V, K, j = 12, 4, 0
+    tp = 0.9
+    target, draft, toks, u = _forced_trunc(rng, V, K, j, 0, tp)
+    # put target row j + 1's top-p cut exactly on a level boundary: two
+    # levels whose masses after renormalisation are tp and 1 - tp
+    t2 = target.copy()
+    row = np.full(V, -1e9)
+    row[0] = math.log(tp)
+    row[1] = math.log(1.0 - tp)
+    t2[j + 1] = row
+    full = O.verify_sequence(t2, draft, toks, u, 1.0, S, top_p=tp)
+    walk = O.verify_sequence(t2, draft, toks, u, 1.0, S, top_p=tp, walk_order=True)
+    assert walk.valid and walk.accept_len == j and full.valid and full.accept_len == j
+    assert full.min_dist < 1e-9
+    assert walk.min_dist > 1e-9
+    # the same cut in a row the walk reads (position 0, kept, before a
+    # rejection at 1) is a decision of both readings
+    target, draft, toks, u = _forced_trunc(rng, V, K, 1, 0, tp)
+    t3 = target.copy()
+    t3[0] = row
+    toks[0] = 0
+    full = O.verify_sequence(t3, draft, toks, u, 1.0, S, top_p=tp)
+    walk = O.verify_sequence(t3, draft, toks, u, 1.0, S, top_p=tp, walk_order=True)
+    assert walk.valid and walk.accept_len == 1 and full.accept_len == 1
+    assert walk.min_dist < 1e-9 and full.min_dist < 1e-9
 
 
 # greedy and margin walks: target rows only, the walk stops at the first
