@@ -265,7 +265,7 @@ def main():
     ap.add_argument("--walk", action="store_true",
                     help="walk-order reading (the rows of a position are read only when the "
                          "walk reaches it; nothing past the first rejection); no effect on "
-                         "stochastic calls with truncation or the residual side output")
+                         "stochastic calls with the residual side output or fp32 truncation")
     ap.add_argument("--no-walk-report", action="store_true",
                     help="leave out the walk-order timing reported beside a plain line "
                          "(counter and trace runs that should see the line's calls only)")
@@ -311,12 +311,16 @@ def main():
         kb_dev = torch.as_tensor(kb.astype(np.int32), device=dev).contiguous()
         v.set_stops(-1, kb_dev, None)
     trunc = mode == "stochastic" and (0 < args.top_k < V or args.top_p < 1.0)
+    trunc_args = (torch.full((B,), args.top_k, dtype=torch.int32, device=dev),
+                  torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
     if trunc:
-        v.set_truncation(torch.full((B,), args.top_k, dtype=torch.int32, device=dev),
-                         torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
+        v.set_truncation(*trunc_args)
+    # (the library reads truncated fp32 calls and calls with the residual
+    # side output in full whatever the setting)
+    walk_ok = not (mode == "stochastic" and (args.residual or (trunc and cfg.dtype == "f32")))
     if args.residual and mode == "stochastic":
         v.set_residual(args.residual)
-    walk = args.walk and not (mode == "stochastic" and (trunc or args.residual))
+    walk = args.walk and walk_ok
     if walk:
         v.set_walk_order(True)
     if args.policy:
@@ -444,13 +448,15 @@ def main():
         "algorithmic_bytes_per_step": int(call_bytes),
         "roofline": roofline,
     }
-    if (not walk and not trunc and not args.residual
-            and not args.graph and not args.policy and not args.no_walk_report):
+    if (not walk and walk_ok and not args.graph and not args.policy
+            and not args.no_walk_report):
         # the same calls with walk-order reading, reported beside the line:
         # rows past each sequence's first rejection are not read
         vw = sv.SpecVerifier(B, K, V, cfg.torch_dtype, ema_decay=cfg.ema_decay)
         if args.stops == "varlen":
             vw.set_stops(-1, kb_dev, None)
+        if trunc:
+            vw.set_truncation(*trunc_args)
         vw.set_walk_order(True)
         outw = tuple(torch.empty_like(t) for t in out)
         same, rows_w = True, []

@@ -314,8 +314,8 @@ int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
                              double *out_residual);
 
 /*
- * Walk-order reading for later spec_verify calls: stochastic calls without
- * truncation or the draft residual side output, and greedy and margin calls
+ * Walk-order reading for later spec_verify calls: stochastic calls (also
+ * with top-k / top-p truncation of bf16 logits) and greedy and margin calls
  * ([DVC] "Verify several proposed tokens in one target pass": at the first
  * rejection the correction is drawn and later proposals are discarded;
  * [SMB] "Seeing It in Code": the walk over the drafts stops at the first
@@ -323,21 +323,21 @@ int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
  * draft row i for stochastic calls) are read only when the walk reaches
  * position i, i.e. once positions 0..i-1 are kept, and nothing past the
  * first rejection is read (target row k_b, the bonus row, only when every
- * position is kept). The streaming (stochastic) or argmax (greedy, margin)
- * pass then reads position 0's rows of every sequence, lists the sequences
- * whose walk keeps position 0 (the same test as the scan, from the
- * partials), and reads their remaining rows with a fixed grid; the finish
- * reads no further than the walk. Rows of positions past the first
- * rejection after position 0 may still be read (not checked, and never
- * used).
+ * position is kept). The streaming, truncation (both passes) or argmax pass
+ * then reads position 0's rows of every sequence, lists the sequences whose
+ * walk keeps position 0 (the same test as the scan, from the partials), and
+ * reads their remaining rows; the finish reads no further than the walk.
+ * Rows of positions past the first rejection after position 0 may still be
+ * read (not checked, and never used).
  * What changes for the caller, and only this: a sequence is invalid only when
  * a drafted token or a row that the walk reads is unusable (NaN, +inf or no
  * finite maximum), not when one past its first rejection is; p(d) and q(d),
  * or the margin ratio (spec_verify_set_aux), are NaN past the first
  * rejection, and the per-row argmax is -1 past it. End-of-sequence and
- * budget stops cut the emission, not the reading. Every other output equals
- * that of the full reading on the same inputs. Stochastic calls with
- * truncation or the draft residual side output read every row as usual.
+ * budget stops cut the emission, not the reading; top_p <= 0 or NaN still
+ * makes a sequence invalid. Every other output equals that of the full
+ * reading on the same inputs. Stochastic calls with the draft residual side
+ * output, and truncated calls with fp32 logits, read every row as usual.
  * on = 0 (the default) reads every needed row.
  * Returns SV_EINVAL for a NULL handle or on outside {0, 1}.
  */

@@ -295,10 +295,11 @@ class SpecVerifier:
         return sup, res
 
     def set_walk_order(self, on: bool = True):
-        """Walk-order reading for later greedy and margin calls and stochastic
-        calls without truncation or the residual side output: rows past each
-        sequence's first rejection are not read (and so not checked); p(d),
-        q(d) or the margin ratio past it are NaN, the per-row argmax -1."""
+        """Walk-order reading for later greedy, margin and stochastic calls
+        (not with the residual side output, nor truncated fp32 calls): rows
+        past each sequence's first rejection are not read (and so not
+        checked); p(d), q(d) or the margin ratio past it are NaN, the per-row
+        argmax -1."""
         self._check(self.lib.spec_verify_set_walk_order(self._h, 1 if on else 0),
                     "set_walk_order")
 

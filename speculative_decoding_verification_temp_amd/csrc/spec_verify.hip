@@ -303,19 +303,52 @@ int run_trunc(spec_verify_handle* h, int B, const void* target, const void* draf
   if (ntiles > sv::kFMaxTiles || rows > sv::kFMaxRows)
     return fail(h, SV_EUNSUPPORTED, "truncation needs V <= %d (bf16)",
                 sv::kFMaxTiles * sv::kTileChunks * VEC);
+  // walk-order reading (not with the residual side output, which reads every
+  // draft row): both truncation passes over position 0's rows of every
+  // sequence, the sequences whose walk keeps position 0 listed, then both
+  // passes over their other rows
+  const bool walk = h->walk && h->drift_sup == nullptr;
+  sv::Rules rules = h->rules;
+  rules.walk = walk ? 1 : 0;
+  int rc;
   prof_mark(h, 0, s);
-  hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>), dim3(unsigned(B * rows)), dim3(sv::kTwBlock),
-                     0, s, target, draft, K, V, c, c64, h->trunc, h->rules.k, h->parts, hist);
-  int rc = check_launch(h, "rowstats_trunc_win");
-  prof_mark(h, 1, s);
-  if (rc) return rc;
-  hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(std::min(B * rows, h->n_cu))),
-                     dim3(sv::kTrBlock), 0, s, target, draft, K, V, c, c64, h->trunc, h->rules.k,
-                     h->parts, (long long)B * rows);
-  if ((rc = check_launch(h, "rowstats_trunc"))) return rc;
+  if (walk) {
+    const sv::RowSel first{0, 1, 0, 1, nullptr, nullptr};
+    const sv::RowSel rest{1, K + 1, 1, K, h->walk_seq, h->walk_cnt};
+    hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>), dim3(unsigned(B * 2)), dim3(sv::kTwBlock), 0,
+                       s, target, draft, B, K, V, c, c64, h->trunc, h->rules.k, h->parts, hist,
+                       first, h->walk_cnt);
+    hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(std::min(B * 2, h->n_cu))),
+                       dim3(sv::kTrBlock), 0, s, target, draft, B, K, V, c, c64, h->trunc,
+                       h->rules.k, h->parts, first);
+    hipLaunchKernelGGL(sv::walk_gate_trunc, dim3(unsigned(div_up(B, sv::kBlock))),
+                       dim3(sv::kBlock), 0, s, B, K, V, h->parts, target, draft, h->rules.k,
+                       tokens, uniforms, c64, h->walk_seq, h->walk_cnt);
+    hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>),
+                       dim3(unsigned(std::max(1, B * (2 * K - 1)))), dim3(sv::kTwBlock), 0, s,
+                       target, draft, B, K, V, c, c64, h->trunc, h->rules.k, h->parts, nullptr,
+                       rest, nullptr);
+    hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(h->n_cu)), dim3(sv::kTrBlock), 0,
+                       s, target, draft, B, K, V, c, c64, h->trunc, h->rules.k, h->parts, rest);
+    rc = check_launch(h, "truncation passes (walk order)");
+    prof_mark(h, 1, s);
+    if (rc) return rc;
+  } else {
+    const sv::RowSel all{0, K + 1, 0, K, nullptr, nullptr};
+    hipLaunchKernelGGL((sv::rowstats_trunc_win<VEC>), dim3(unsigned(B * rows)),
+                       dim3(sv::kTwBlock), 0, s, target, draft, B, K, V, c, c64, h->trunc,
+                       h->rules.k, h->parts, hist, all, nullptr);
+    rc = check_launch(h, "rowstats_trunc_win");
+    prof_mark(h, 1, s);
+    if (rc) return rc;
+    hipLaunchKernelGGL((sv::rowstats_trunc<VEC>), dim3(unsigned(std::min(B * rows, h->n_cu))),
+                       dim3(sv::kTrBlock), 0, s, target, draft, B, K, V, c, c64, h->trunc,
+                       h->rules.k, h->parts, all);
+    if ((rc = check_launch(h, "rowstats_trunc"))) return rc;
+  }
   hipLaunchKernelGGL((sv::finish_seq<sv::DT_BF16, VEC, sv::kFinishBlock, true>), dim3(B),
                      dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
-                     uniforms, c, c64, tab_half(c64), h->rules, out_tokens, out_len, hist, h->ema,
+                     uniforms, c, c64, tab_half(c64), rules, out_tokens, out_len, hist, h->ema,
                      h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, h->trunc.k,
                      sv::MergeJob{}, h->claim_tiles);
   return check_launch(h, "finish_seq (truncated)");

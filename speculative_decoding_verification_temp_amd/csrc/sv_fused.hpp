@@ -858,30 +858,26 @@ __device__ __forceinline__ void finish_sequence(
         // them (fX), else gathered here
         const float xt = fX != nullptr ? fX[lane] : load_logit<DT>(row_base(lane), d);
         const float xd = fX != nullptr ? fX[K + 1 + lane] : load_logit<DT>(row_base(K + 1 + lane), d);
+        const double u = pre_u != nullptr ? pre_u[lane] : uniforms[(long long)b * (K + 1) + lane];
         if constexpr (TRUNC && DT == DT_BF16) {
           // the same level terms as the truncated normalisers; 0 when dropped
-          const uint32_t at = bf16_key(__float_as_uint(xt) >> 16);
-          const uint32_t ad = bf16_key(__float_as_uint(xd) >> 16);
-          P = (at >= kt && key_finite(at)) ? level_term(at, c64, Rt) / St : 0.0;
-          Q = (ad >= kd && key_finite(ad)) ? level_term(ad, c64, Rd) / Sd : 0.0;
+          keep = trunc_accept_bf16(xt, xd, Rt, St, kt, Rd, Sd, kd, u, c64, P, Q);
         } else if constexpr (TRUNC) {
           // fp32: the terms the truncation pass summed (0 for -inf); 0 when dropped
           P = order_key<DT_F32>(__float_as_uint(xt)) >= kt ? value_term(xt, c64, Rt) / St : 0.0;
           Q = order_key<DT_F32>(__float_as_uint(xd)) >= kd ? value_term(xd, c64, Rd) / Sd : 0.0;
-        }
-        const double u = pre_u != nullptr ? pre_u[lane] : uniforms[(long long)b * (K + 1) + lane];
-        if constexpr (TRUNC)
           keep = (P >= Q) || (u < P / Q);
-        else
+        } else {
           keep = accept_position(xt, xd, Rt, St, Rd, Sd, u, c, P, Q);
+        }
         zq = keep && Q == 0.0;
       }
     }
-    const bool bad = sequence_bad(lane, kb, !TRUNC && sp.walk != 0, lane_bad, keep);
+    const bool bad = sequence_bad(lane, kb, sp.walk != 0, lane_bad, keep);
     const Walk w = walk_outcome(lane, kb, m, sp.eos, keep, d);
     const int j = w.j;
     // (walk-order reading: nothing past the first rejection was read)
-    const bool no_pq = bad || lane >= kb || (!TRUNC && sp.walk && lane > j);
+    const bool no_pq = bad || lane >= kb || (sp.walk && lane > j);
     if (aux_p != nullptr && lane < K) aux_p[(long long)b * K + lane] = no_pq ? __builtin_nan("") : P;
     if (aux_q != nullptr && lane < K) aux_q[(long long)b * K + lane] = no_pq ? __builtin_nan("") : Q;
     const float Rtj = __shfl(Rt, j, kWave), Rdj = __shfl(Rd, j, kWave);

@@ -231,6 +231,23 @@ __device__ inline double value_term(float x, double c64, float R) {
   return __builtin_ldexp(double(__builtin_amdgcn_exp2f(float(a - n))), int(n));
 }
 
+// The acceptance test of one drafted position of a truncated bf16 sequence
+// ([RNR] s.1-2: p and q after truncation; [SMB] "The Guarantee Behind
+// Rejection Sampling"): from the logits at the drafted token, the rows'
+// references, truncated normalisers and threshold keys, P = p(d) and Q = q(d)
+// are the level terms over the normalisers (0 for a dropped value), and the
+// draft is kept iff P >= Q or u < P / Q. The per-sequence finish and the
+// walk-order gate both call it, so the two take the same decision.
+__device__ inline bool trunc_accept_bf16(float xt, float xd, float Rt, double St, uint32_t kt,
+                                         float Rd, double Sd, uint32_t kd, double u, double c64,
+                                         double& P, double& Q) {
+  const uint32_t at = bf16_key(__float_as_uint(xt) >> 16);
+  const uint32_t ad = bf16_key(__float_as_uint(xd) >> 16);
+  P = (at >= kt && key_finite(at)) ? level_term(at, c64, Rt) / St : 0.0;
+  Q = (ad >= kd && key_finite(ad)) ? level_term(ad, c64, Rd) / Sd : 0.0;
+  return (P >= Q) || (u < P / Q);
+}
+
 // --------------------------------------------------------------------------
 // Stochastic scan: lane i tests position i.
 // --------------------------------------------------------------------------

@@ -107,6 +107,27 @@ struct StageRows {
   uint32_t* clear;   // set to 0 by workgroup 0 (the next stage's list count), or null
 };
 
+// Rows of a pass that takes them one after another (the truncation passes):
+// target rows t0..t1-1 and draft rows d0..d1-1 of every sequence, or of the
+// listed sequences seqs[0 .. *count) when seqs is set. Candidate it in
+// 0 .. total(B) - 1 is row at(it) of sequence it / per_seq().
+struct RowSel {
+  int t0, t1, d0, d1;
+  const int32_t* seqs;
+  const uint32_t* count;
+  __device__ int per_seq() const { return (t1 - t0) + (d1 - d0); }
+  __device__ long long total(int B) const {
+    return (long long)(seqs != nullptr ? int(*count) : B) * per_seq();
+  }
+  __device__ void at(long long it, int K, int& b, int& r) const {
+    const int nr = per_seq(), nt = t1 - t0;
+    const long long s = it / nr;
+    const int lr = int(it % nr);
+    b = seqs != nullptr ? seqs[s] : int(s);
+    r = lr < nt ? t0 + lr : K + 1 + d0 + (lr - nt);
+  }
+};
+
 // Whether the walk of sequence b keeps every position below p (p <= K),
 // given the partials of their rows (one wavefront; lane i tests position i;
 // a position with an unusable token or row stops the walk).

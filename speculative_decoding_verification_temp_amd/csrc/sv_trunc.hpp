@@ -199,14 +199,14 @@ __device__ inline T_ tr_above(T_ v, T_* s, T_& total) {
 }
 
 template <int VEC>
-// One workgroup per compute unit takes rows blockIdx.x, blockIdx.x +
-// gridDim.x, ... (nrows = B (2K + 1)): its threads first check up to 1024 of
-// them at once and list the ones the window pass handed over, then the
-// workgroup counts the listed rows one after another.
+// One workgroup per compute unit takes the rows sel selects (candidates
+// blockIdx.x, blockIdx.x + gridDim.x, ...): its threads first check up to
+// 1024 of them at once and list the ones the window pass handed over, then
+// the workgroup counts the listed rows one after another.
 __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
-    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
-    double c64, Trunc tr, const int32_t* __restrict__ kdraft, RowPart* __restrict__ parts,
-    long long nrows) {
+    const void* __restrict__ target, const void* __restrict__ draft, int B, int K, int V,
+    float c, double c64, Trunc tr, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts, RowSel sel) {
   __shared__ uint32_t H[kHistWords];
   __shared__ uint32_t s_wraps[kMaxWraps];
   __shared__ uint32_t s_nwrap;
@@ -219,19 +219,22 @@ __global__ __launch_bounds__(kTrBlock) void rowstats_trunc(
   __shared__ int s_nrows;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
+  const long long nrows = sel.total(B);
   for (long long g0 = blockIdx.x; g0 < nrows; g0 += (long long)gridDim.x * kTrBlock) {
   if (tid == 0) s_nrows = 0;
   __syncthreads();
   {
     const long long cand = g0 + (long long)tid * gridDim.x;
     if (cand < nrows) {
-      const int cb = int(cand / rows), cr = int(cand % rows);
+      int cb, cr;
+      sel.at(cand, K, cb, cr);
       bool need = true;              // rows past the draft count are not needed
       if (kdraft != nullptr) {
         const int kb = kdraft[cb];
         need = !(cr <= K ? cr > kb : cr - K - 1 >= kb);
       }
-      if (need && parts[cand].flags == kTruncRedo) s_rows[atomicAdd(&s_nrows, 1)] = cand;
+      const long long grow = (long long)cb * rows + cr;
+      if (need && parts[grow].flags == kTruncRedo) s_rows[atomicAdd(&s_nrows, 1)] = grow;
     }
   }
   __syncthreads();
@@ -452,11 +455,14 @@ __device__ __forceinline__ uint32_t win_bin(uint32_t bits) {
   return off2 - 2u < uint32_t(kWinHalf) ? wb : sp;
 }
 
+// One row (b, r) of the window pass, by the whole workgroup; its partial goes
+// to parts[b (2K + 1) + r]. The workgroup's LDS is free again after a
+// barrier.
 template <int VEC>
-__global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
-    const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
-    double c64, Trunc tr, const int32_t* __restrict__ kdraft, RowPart* __restrict__ parts,
-    uint32_t* __restrict__ hist) {
+__device__ __forceinline__ void trunc_win_row(const void* __restrict__ target,
+                                              const void* __restrict__ draft, int b, int r,
+                                              int K, int V, float c, double c64, const Trunc& tr,
+                                              RowPart* __restrict__ parts) {
   using C = Chunk<DT_BF16, VEC>;
   __shared__ uint32_t H[kWinBins];
   __shared__ uint32_t s_u[kTwWaves];
@@ -466,13 +472,7 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
   __shared__ double s_S;
   const int tid = threadIdx.x;
   const int rows = 2 * K + 1;
-  const long long grow = blockIdx.x;
-  const int b = int(grow / rows), r = int(grow % rows);
-  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
-  if (kdraft != nullptr) {           // rows past the draft count are not needed
-    const int kb = kdraft[b];
-    if (r <= K ? r > kb : r - K - 1 >= kb) return;
-  }
+  const long long grow = (long long)b * rows + r;
   const void* row = row_ptr<DT_BF16>(target, draft, b, r, K, V);
 
   // ---- 1. count: groups of U chunks per thread, the next group's loads
@@ -726,6 +726,56 @@ __global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
     p.flags = 0;
     parts[grow] = p;
   }
+}
+
+// The window pass, one workgroup per row that sel selects: every needed row
+// of every sequence, or with walk-order reading position 0's rows of every
+// sequence and then the other rows of the listed sequences (a grid sized for
+// every sequence: the workgroups past the listed rows return at once).
+// Workgroup 0 clears the histogram and, when set, the list count.
+template <int VEC>
+__global__ __launch_bounds__(kTwBlock) void rowstats_trunc_win(
+    const void* __restrict__ target, const void* __restrict__ draft, int B, int K, int V,
+    float c, double c64, Trunc tr, const int32_t* __restrict__ kdraft,
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist, RowSel sel,
+    uint32_t* __restrict__ clear) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (blockIdx.x == 0 && clear != nullptr && tid == 0) *clear = 0u;
+  if ((long long)blockIdx.x >= sel.total(B)) return;
+  int b, r;
+  sel.at(blockIdx.x, K, b, r);
+  if (kdraft != nullptr) {           // rows past the draft count are not needed
+    const int kb = kdraft[b];
+    if (r <= K ? r > kb : r - K - 1 >= kb) return;
+  }
+  trunc_win_row<VEC>(target, draft, b, r, K, V, c, c64, tr, parts);
+}
+
+// Walk-order reading of truncated bf16 calls, after both truncation passes
+// over position 0's rows: lists the sequences whose walk keeps position 0
+// and that have rows past it (k_b >= 1), one thread per sequence, with the
+// scan's own truncated acceptance test (trunc_accept_bf16).
+__global__ __launch_bounds__(kBlock) void walk_gate_trunc(
+    int B, int K, int V, const RowPart* __restrict__ parts, const void* __restrict__ target,
+    const void* __restrict__ draft, const int32_t* __restrict__ kdraft,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, double c64,
+    int32_t* __restrict__ seqs, uint32_t* __restrict__ count) {
+  const int b = int(blockIdx.x) * kBlock + int(threadIdx.x);
+  if (b >= B) return;
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (!(kb >= 1 && kb <= K)) return;
+  const int rows = 2 * K + 1;
+  const RowPart pt = parts[(long long)b * rows];
+  const RowPart pd = parts[(long long)b * rows + K + 1];
+  const int d = tokens[(long long)b * K];
+  if (!(finite_pos(pt.S) && finite_pos(pd.S) && d >= 0 && d < V)) return;
+  const float xt = load_logit<DT_BF16>(row_ptr<DT_BF16>(target, draft, b, 0, K, V), d);
+  const float xd = load_logit<DT_BF16>(row_ptr<DT_BF16>(target, draft, b, K + 1, K, V), d);
+  double P, Q;
+  if (trunc_accept_bf16(xt, xd, pt.R, pt.S, uint32_t(pt.idx), pd.R, pd.S, uint32_t(pd.idx),
+                        double(uniforms[(long long)b * (K + 1)]), c64, P, Q))
+    seqs[atomicAdd(count, 1u)] = b;
 }
 
 }  // namespace sv

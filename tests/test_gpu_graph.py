@@ -148,7 +148,8 @@ def test_graph_replay_argmax_modes(sv, mode):
 
 
 @pytest.mark.parametrize("cfg_name,mode", [("c2", "stochastic"), ("c1", "stochastic"),
-                                           ("c2", "greedy"), ("c1", "margin")])
+                                           ("c2", "greedy"), ("c1", "margin"),
+                                           ("c2", "truncated")])
 def test_graph_replay_walk_order(sv, cfg_name, mode):
     """A walk-order call (its list count is cleared by its first kernel, not
     by a memset) captured once and replayed on fresh inputs with stopping
@@ -157,11 +158,15 @@ def test_graph_replay_walk_order(sv, cfg_name, mode):
     cfg = CONFIGS[cfg_name]
     rng = np.random.default_rng(62)
     kb = torch.as_tensor(rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32), device=DEV)
+    tk = torch.as_tensor(rng.choice([0, 20, 200], cfg.B).astype(np.int32), device=DEV)
+    tp = torch.as_tensor(rng.choice([1.0, 0.9, 0.6], cfg.B).astype(np.float32), device=DEV)
 
     def setup():
         v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, cfg.torch_dtype, ema_decay=0.9)
         aux = v.enable_aux()
         v.set_stops(-1, kb, None)
+        if mode == "truncated":
+            v.set_truncation(tk, tp)
         v.set_walk_order(True)
         out = (torch.full((cfg.B, cfg.K + 1), -7, dtype=torch.int32, device=DEV),
                torch.full((cfg.B,), -7, dtype=torch.int32, device=DEV),
@@ -170,7 +175,7 @@ def test_graph_replay_walk_order(sv, cfg_name, mode):
 
     vg, aux_g, out_g = setup()
     ve, aux_e, out_e = setup()
-    stoch = mode == "stochastic"
+    stoch = mode in ("stochastic", "truncated")
     gen_mode = "stochastic" if stoch else "greedy"
     x0 = make_inputs(cfg, 90, DEV, gen_mode)
     names = ("target", "draft", "tokens", "uniforms") if stoch else ("target", "tokens")
@@ -211,11 +216,12 @@ def test_graph_replay_walk_order(sv, cfg_name, mode):
             if a.is_floating_point():
                 a, b = torch.nan_to_num(a, nan=-123.0), torch.nan_to_num(b, nan=-123.0)
             assert torch.equal(a, b), f"walk graph {cfg_name} {mode} step {step}"
-        m = {"stochastic": O.MODE_STOCHASTIC, "greedy": O.MODE_GREEDY,
-             "margin": O.MODE_MARGIN}[mode]
+        m = {"stochastic": O.MODE_STOCHASTIC, "truncated": O.MODE_STOCHASTIC,
+             "greedy": O.MODE_GREEDY, "margin": O.MODE_MARGIN}[mode]
+        kw = dict(top_k=tk.cpu().numpy(), top_p=tp.cpu().numpy()) if mode == "truncated" else {}
         o = O.verify_batch(to_host_f64(x["target"]),
                            to_host_f64(x["draft"]) if stoch else None,
                            x["tokens"].cpu().numpy(), x["uniforms"].cpu().double().numpy(),
-                           cfg.T, m, 0.3, draft_len=kb.cpu().numpy(), walk_order=True)
-        compare(np.arange(cfg.B), o, out_g[0], out_g[1], mode, None,
+                           cfg.T, m, 0.3, draft_len=kb.cpu().numpy(), walk_order=True, **kw)
+        compare(np.arange(cfg.B), o, out_g[0], out_g[1], "stochastic" if stoch else mode, None,
                 f"graph/walk/{cfg_name}/{mode}/step {step}")

@@ -11,15 +11,19 @@ past, at and below each sequence's first rejection and in the bonus row, and
 with the stopping rules. The greedy and margin walks (target rows only: the
 argmax pass over row 0, then the rows of the sequences that keep position 0)
 are checked the same way, with the per-row argmax side output -1 and the
-margin ratio NaN past the row the walk stops at.
+margin ratio NaN past the row the walk stops at. Truncated bf16 calls read
+in walk order through both truncation passes (mixed per-sequence top-k /
+top-p, rows handed to the full-histogram pass, planted rows, stopping rules,
+the c3 shape); truncated fp32 calls read every row as before.
 """
 
 import numpy as np
 import pytest
 import torch
 
+from oracle import spec_oracle as O
 from tests.parity import check_invariants, compare, oracle_for
-from workloads import CONFIGS, make_inputs
+from workloads import CONFIGS, make_inputs, to_host_f64, window_edge_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +38,13 @@ def sv():
     return pkg
 
 
-def _run(sv, x, cfg, walk, stops=None, mode="stochastic", tau=0.3):
+def _run(sv, x, cfg, walk, stops=None, mode="stochastic", tau=0.3, trunc=None):
     v = sv.SpecVerifier(cfg.B, cfg.K, cfg.V, x["target"].dtype, ema_decay=0.9)
     aux = v.enable_aux()
+    if trunc is not None:
+        tk, tp = trunc
+        v.set_truncation(torch.as_tensor(tk, device=DEV).contiguous(),
+                         torch.as_tensor(tp, device=DEV).contiguous())
     if stops is not None:
         eos, kb, mx = stops
         v.set_stops(eos, None if kb is None else torch.as_tensor(kb, device=DEV).contiguous(),
@@ -321,3 +329,133 @@ def test_walk_argmax_with_stopping_rules(sv, mode):
     compare(rows, ref, walk[0], walk[1], mode, walk[3], f"c2/{mode}/walk/stops")
     _argmax_checks(walk, ref, rows, mode, f"c2/{mode}/stops")
     _same_argmax_outputs(walk, full, mode)
+
+
+# --------------------------------------------------------------------------
+# truncated calls
+# --------------------------------------------------------------------------
+
+def _trunc_settings(B, V, seed, invalid=False):
+    rng = np.random.default_rng(seed)
+    tk = rng.choice([0, 1, 2, 20, 50, 1000, V, V + 7, -3], B).astype(np.int32)
+    tp = rng.choice([1.0, 0.5, 0.8, 0.9, 0.95, 0.99, 1.5], B).astype(np.float32)
+    if invalid:
+        tp[1], tp[2] = 0.0, np.nan
+    return tk, tp
+
+
+def _trunc_drafts(x, T, tk, tp, seed):
+    """Drafted tokens from each sequence's truncated draft distribution."""
+    rng = np.random.default_rng(seed)
+    d = to_host_f64(x["draft"])
+    B, K, _ = d.shape
+    toks = np.zeros((B, K), dtype=np.int32)
+    for b in range(B):
+        p = float(tp[b]) if np.isfinite(tp[b]) and tp[b] > 0 else 1.0
+        for i in range(K):
+            q, _ = O.truncated_softmax(d[b, i], T, int(tk[b]), p)
+            toks[b, i] = rng.choice(q.size, p=q)
+    return dict(x, tokens=torch.as_tensor(toks, device=DEV).contiguous())
+
+
+def _same_exact(a, b):
+    """Tokens, lengths, histogram and Z equal (the truncation passes give
+    each row the same partial whichever launch reads it)."""
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    za, zb = a[3]["z"], b[3]["z"]
+    assert torch.equal(torch.nan_to_num(za, nan=-9.0), torch.nan_to_num(zb, nan=-9.0))
+
+
+def _trunc_case(sv, x, cfg, trunc, label, stops=None):
+    rows = np.arange(cfg.B)
+    walk = _run(sv, x, cfg, True, stops, trunc=trunc)
+    full = _run(sv, x, cfg, False, stops, trunc=trunc)
+    ref = oracle_for(x, rows, "stochastic", stops=stops, trunc=trunc, walk=True)
+    compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], f"{label}/walk")
+    _pq_pattern(walk[3], ref, rows, label)
+    _same_exact(walk, full)
+    return walk, full, ref
+
+
+def test_walk_truncated_mixed_settings(sv):
+    cfg = CONFIGS["c2"]
+    x = make_inputs(cfg, 13, DEV)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 14, invalid=True)
+    x = _trunc_drafts(x, cfg.T, tk, tp, 15)
+    walk, full, ref = _trunc_case(sv, x, cfg, (tk, tp), "c2/trunc")
+    a = walk[1].cpu().numpy()
+    assert a[1] == -1 and a[2] == -1          # top_p = 0 and NaN
+    assert (a == 0).any() and (a >= 1).any()
+
+
+def test_walk_truncated_rows_handed_over(sv):
+    """Rows with values outside the window pass's bins go through the
+    full-histogram pass, in both stages of the walk."""
+    cfg = CONFIGS["c2"].scaled(B=32)
+    x = window_edge_inputs(cfg, 4, DEV)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 5)
+    x = _trunc_drafts(x, cfg.T, tk, tp, 6)
+    _trunc_case(sv, x, cfg, (tk, tp), "c2/trunc/window edges")
+
+
+def test_walk_truncated_unusable_rows_count_only_where_read(sv):
+    cfg = CONFIGS["c2"]
+    x = make_inputs(cfg, 16, DEV)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 17)
+    x = _trunc_drafts(x, cfg.T, tk, tp, 18)
+    trunc = (tk, tp)
+    j = _run(sv, x, cfg, False, trunc=trunc)[1].cpu().numpy()
+    assert np.all(j >= 0)
+    y = _plant(x, cfg, j, 22)
+    rows = np.arange(cfg.B)
+    walk = _run(sv, y, cfg, True, trunc=trunc)
+    full = _run(sv, y, cfg, False, trunc=trunc)
+    ref = oracle_for(y, rows, "stochastic", trunc=trunc, walk=True)
+    ref_full = oracle_for(y, rows, "stochastic", trunc=trunc)
+    compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c2/trunc/walk/planted")
+    compare(rows, ref_full, full[0], full[1], "stochastic", full[3], "c2/trunc/full/planted")
+    _pq_pattern(walk[3], ref, rows, "c2/trunc/planted")
+    a_walk, a_full = walk[1].cpu().numpy(), full[1].cpu().numpy()
+    assert (a_walk < 0).sum() < (a_full < 0).sum()
+    assert np.array_equal(a_walk < 0, ref.accept_len < 0)
+    assert np.array_equal(a_full < 0, ref_full.accept_len < 0)
+
+
+def test_walk_truncated_with_stopping_rules(sv):
+    cfg = CONFIGS["c2"]
+    x = make_inputs(cfg, 19, DEV)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 20)
+    x = _trunc_drafts(x, cfg.T, tk, tp, 21)
+    rng = np.random.default_rng(7)
+    toks = x["tokens"].cpu().numpy()
+    eos = int(np.bincount(toks.ravel()).argmax())
+    kb = rng.integers(0, cfg.K + 1, cfg.B).astype(np.int32)
+    mx = rng.integers(1, cfg.K + 3, cfg.B).astype(np.int32)
+    kb[3], kb[4], mx[5] = -1, cfg.K + 1, 0
+    _trunc_case(sv, x, cfg, (tk, tp), "c2/trunc/stops", stops=(eos, kb, mx))
+
+
+def test_walk_truncated_c3_whole_batch(sv):
+    cfg = CONFIGS["c3"]
+    x = make_inputs(cfg, 0, DEV)
+    tk = np.full(cfg.B, 50, np.int32)
+    tp = np.full(cfg.B, 0.9, np.float32)
+    _trunc_case(sv, x, cfg, (tk, tp), "c3/trunc")
+
+
+def test_walk_fp32_truncated_reads_every_row(sv):
+    """Truncated fp32 calls ignore the walk-order setting: every needed row is
+    read and checked, as without it (the oracle's full reading)."""
+    cfg = CONFIGS["c1"].scaled(B=16)
+    x = make_inputs(cfg, 23, DEV)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 24)
+    x = _trunc_drafts(x, cfg.T, tk, tp, 25)
+    rows = np.arange(cfg.B)
+    walk = _run(sv, x, cfg, True, trunc=(tk, tp))
+    full = _run(sv, x, cfg, False, trunc=(tk, tp))
+    _same_exact(walk, full)
+    ref = oracle_for(x, rows, "stochastic", trunc=(tk, tp))
+    compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c1/fp32 trunc/walk setting")
+    for key in ("p_d", "q_d"):
+        assert torch.equal(torch.nan_to_num(walk[3][key], nan=-9.0),
+                           torch.nan_to_num(full[3][key], nan=-9.0))
