@@ -265,7 +265,7 @@ def main():
     ap.add_argument("--walk", action="store_true",
                     help="walk-order reading (the rows of a position are read only when the "
                          "walk reaches it; nothing past the first rejection); no effect on "
-                         "stochastic calls with the residual side output or fp32 truncation")
+                         "stochastic calls with the residual side output")
     ap.add_argument("--no-walk-report", action="store_true",
                     help="leave out the walk-order timing reported beside a plain line "
                          "(counter and trace runs that should see the line's calls only)")
@@ -315,9 +315,9 @@ def main():
                   torch.full((B,), args.top_p, dtype=torch.float32, device=dev))
     if trunc:
         v.set_truncation(*trunc_args)
-    # (the library reads truncated fp32 calls and calls with the residual
-    # side output in full whatever the setting)
-    walk_ok = not (mode == "stochastic" and (args.residual or (trunc and cfg.dtype == "f32")))
+    # (the library reads calls with the residual side output in full
+    # whatever the setting)
+    walk_ok = not (mode == "stochastic" and args.residual)
     if args.residual and mode == "stochastic":
         v.set_residual(args.residual)
     walk = args.walk and walk_ok

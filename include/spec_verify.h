@@ -315,7 +315,7 @@ int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
 
 /*
  * Walk-order reading for later spec_verify calls: stochastic calls (also
- * with top-k / top-p truncation of bf16 logits) and greedy and margin calls
+ * with top-k / top-p truncation) and greedy and margin calls
  * ([DVC] "Verify several proposed tokens in one target pass": at the first
  * rejection the correction is drawn and later proposals are discarded;
  * [SMB] "Seeing It in Code": the walk over the drafts stops at the first
@@ -337,7 +337,7 @@ int spec_verify_set_residual(spec_verify_handle *h, int m, int32_t *out_support,
  * budget stops cut the emission, not the reading; top_p <= 0 or NaN still
  * makes a sequence invalid. Every other output equals that of the full
  * reading on the same inputs. Stochastic calls with the draft residual side
- * output, and truncated calls with fp32 logits, read every row as usual.
+ * output read every row as usual.
  * on = 0 (the default) reads every needed row.
  * Returns SV_EINVAL for a NULL handle or on outside {0, 1}.
  */

@@ -296,7 +296,7 @@ class SpecVerifier:
 
     def set_walk_order(self, on: bool = True):
         """Walk-order reading for later greedy, margin and stochastic calls
-        (not with the residual side output, nor truncated fp32 calls): rows
+        (not with the residual side output): rows
         past each sequence's first rejection are not read (and so not
         checked); p(d), q(d) or the margin ratio past it are NaN, the per-row
         argmax -1."""

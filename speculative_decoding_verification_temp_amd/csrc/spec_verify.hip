@@ -371,42 +371,70 @@ int run_trunc32(spec_verify_handle* h, int B, const void* target, const void* dr
                 sv::kFMaxTiles * sv::kTileChunks * VEC);
   int lg = 0;                        // ceil(log2 V): fixed-point masses keep 61 - lg bits
   while ((1ll << lg) < (long long)V) ++lg;
-  prof_mark(h, 0, s);
   const bool list = VEC == 4 && h->trunc32_list;
-  int rc = SV_OK;
-  if constexpr (VEC == 4) {
-    if (list) {
-      hipLaunchKernelGGL((sv::rowstats_trunc32_list<VEC>), dim3(unsigned(B * rows)),
-                         dim3(sv::kT1Block), 0, s, target, draft, K, V, c, c64, 61 - lg,
-                         h->trunc, h->rules.k, h->parts, hist);
-      rc = check_launch(h, "rowstats_trunc32_list");
-      // the rows the list pass handed over (top-p alone, top-k past its lists
-      // or tied at the k-th value): one read each where the copy suffices
-      if (rc == SV_OK && h->trunc32_one) {
-        hipLaunchKernelGGL((sv::rowstats_trunc32_topp<VEC>), dim3(unsigned(B * rows)),
-                           dim3(sv::kTPBlock), 0, s, target, draft, K, V, c, c64, 61 - lg,
-                           h->trunc, h->rules.k, h->parts);
-        rc = check_launch(h, "rowstats_trunc32_topp");
+  // the truncation passes over the rows sel selects (grid: one workgroup per
+  // candidate row); the first launch clears the histogram and `clear`
+  auto passes = [&](const sv::RowSel& sel, int grid, uint32_t* hist_, uint32_t* clear) -> int {
+    int rc_ = SV_OK;
+    if constexpr (VEC == 4) {
+      if (list) {
+        hipLaunchKernelGGL((sv::rowstats_trunc32_list<VEC>), dim3(unsigned(grid)),
+                           dim3(sv::kT1Block), 0, s, target, draft, K, V, c, c64, 61 - lg,
+                           h->trunc, h->rules.k, h->parts, hist_, B, sel, clear);
+        rc_ = check_launch(h, "rowstats_trunc32_list");
+        // the rows the list pass handed over (top-p alone, top-k past its
+        // lists or tied at the k-th value): one read each where the copy
+        // suffices
+        if (rc_ == SV_OK && h->trunc32_one) {
+          hipLaunchKernelGGL((sv::rowstats_trunc32_topp<VEC>), dim3(unsigned(grid)),
+                             dim3(sv::kTPBlock), 0, s, target, draft, K, V, c, c64, 61 - lg,
+                             h->trunc, h->rules.k, h->parts, B, sel);
+          rc_ = check_launch(h, "rowstats_trunc32_topp");
+        }
       }
     }
+    if (rc_) return rc_;
+    hipLaunchKernelGGL((sv::rowstats_trunc32<VEC>), dim3(unsigned(grid)), dim3(sv::kT32Block), 0,
+                       s, target, draft, K, V, c, c64, 61 - lg, h->trunc32_buf, list ? 1 : 0,
+                       h->trunc, h->rules.k, h->parts, list ? nullptr : hist_, B, sel,
+                       list ? nullptr : clear);
+    return check_launch(h, "rowstats_trunc32");
+  };
+  // walk-order reading (not with the residual side output, which reads every
+  // draft row): the passes over position 0's rows of every sequence, the
+  // sequences whose walk keeps position 0 listed, then the passes over their
+  // other rows (a grid for every possible row; the rest return at once)
+  const bool walk = h->walk && h->drift_sup == nullptr;
+  sv::Rules rules = h->rules;
+  rules.walk = walk ? 1 : 0;
+  int rc;
+  prof_mark(h, 0, s);
+  if (walk) {
+    const sv::RowSel first{0, 1, 0, 1, nullptr, nullptr};
+    const sv::RowSel rest{1, K + 1, 1, K, h->walk_seq, h->walk_cnt};
+    rc = passes(first, B * 2, hist, h->walk_cnt);
+    if (rc) return rc;
+    hipLaunchKernelGGL(sv::walk_gate_trunc32, dim3(unsigned(div_up(B, sv::kBlock))),
+                       dim3(sv::kBlock), 0, s, B, K, V, h->parts, target, draft, h->rules.k,
+                       tokens, uniforms, c64, h->walk_seq, h->walk_cnt);
+    if ((rc = check_launch(h, "walk_gate_trunc32"))) return rc;
+    rc = passes(rest, std::max(1, B * (2 * K - 1)), nullptr, nullptr);
+  } else {
+    const sv::RowSel all{0, K + 1, 0, K, nullptr, nullptr};
+    rc = passes(all, B * rows, hist, nullptr);
   }
-  if (rc) return rc;
-  hipLaunchKernelGGL((sv::rowstats_trunc32<VEC>), dim3(unsigned(B * rows)), dim3(sv::kT32Block),
-                     0, s, target, draft, K, V, c, c64, 61 - lg, h->trunc32_buf, list ? 1 : 0,
-                     h->trunc, h->rules.k, h->parts, list ? nullptr : hist);
-  rc = check_launch(h, "rowstats_trunc32");
-  prof_mark(h, 1, s);                // both truncation passes
+  prof_mark(h, 1, s);                // the truncation passes
   if (rc) return rc;
   if (B >= 2 * h->n_cu)                // as in run_stochastic
     hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlockHalf, true>), dim3(B),
                        dim3(sv::kFinishBlockHalf), 0, s, K, V, 1, h->parts, target, draft,
-                       tokens, uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema,
+                       tokens, uniforms, c, c64, 0, rules, out_tokens, out_len, hist, h->ema,
                        h->steps, h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr,
                        sv::MergeJob{}, h->claim_tiles);
   else
     hipLaunchKernelGGL((sv::finish_seq<sv::DT_F32, VEC, sv::kFinishBlock, true>), dim3(B),
                        dim3(sv::kFinishBlock), 0, s, K, V, 1, h->parts, target, draft, tokens,
-                       uniforms, c, c64, 0, h->rules, out_tokens, out_len, hist, h->ema, h->steps,
+                       uniforms, c, c64, 0, rules, out_tokens, out_len, hist, h->ema, h->steps,
                        h->decay, h->stats, h->aux_p, h->aux_q, h->aux_z, nullptr,
                        sv::MergeJob{}, h->claim_tiles);
   return check_launch(h, "finish_seq (truncated)");

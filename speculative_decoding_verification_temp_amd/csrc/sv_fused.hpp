@@ -864,9 +864,7 @@ __device__ __forceinline__ void finish_sequence(
           keep = trunc_accept_bf16(xt, xd, Rt, St, kt, Rd, Sd, kd, u, c64, P, Q);
         } else if constexpr (TRUNC) {
           // fp32: the terms the truncation pass summed (0 for -inf); 0 when dropped
-          P = order_key<DT_F32>(__float_as_uint(xt)) >= kt ? value_term(xt, c64, Rt) / St : 0.0;
-          Q = order_key<DT_F32>(__float_as_uint(xd)) >= kd ? value_term(xd, c64, Rd) / Sd : 0.0;
-          keep = (P >= Q) || (u < P / Q);
+          keep = trunc_accept_f32(xt, xd, Rt, St, kt, Rd, Sd, kd, u, c64, P, Q);
         } else {
           keep = accept_position(xt, xd, Rt, St, Rd, Sd, u, c, P, Q);
         }

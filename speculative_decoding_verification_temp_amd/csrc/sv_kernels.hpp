@@ -248,6 +248,16 @@ __device__ inline bool trunc_accept_bf16(float xt, float xd, float Rt, double St
   return (P >= Q) || (u < P / Q);
 }
 
+// The same test for a truncated fp32 sequence: P and Q from the value terms
+// over the truncated normalisers, 0 for a value below its row's threshold key.
+__device__ inline bool trunc_accept_f32(float xt, float xd, float Rt, double St, uint32_t kt,
+                                        float Rd, double Sd, uint32_t kd, double u, double c64,
+                                        double& P, double& Q) {
+  P = order_key<DT_F32>(__float_as_uint(xt)) >= kt ? value_term(xt, c64, Rt) / St : 0.0;
+  Q = order_key<DT_F32>(__float_as_uint(xd)) >= kd ? value_term(xd, c64, Rd) / Sd : 0.0;
+  return (P >= Q) || (u < P / Q);
+}
+
 // --------------------------------------------------------------------------
 // Stochastic scan: lane i tests position i.
 // --------------------------------------------------------------------------

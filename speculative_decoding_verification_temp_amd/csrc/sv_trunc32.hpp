@@ -362,7 +362,8 @@ template <int VEC>
 __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
     double c64, int fx, int use_buf, int only_redo, Trunc tr, const int32_t* __restrict__ kdraft,
-    RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int B, RowSel sel,
+    uint32_t* __restrict__ clear) {
   __shared__ uint32_t cnt[kT32Bins1];
   __shared__ u64 m1[kT32Bins1];
   __shared__ u64 m2[kT32Bins], m3[kT32Bins];
@@ -373,14 +374,18 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
   __shared__ T32Walk w;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (blockIdx.x == 0 && clear != nullptr && tid == 0) *clear = 0u;
   const int rows = 2 * K + 1;
-  const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
+  if ((long long)blockIdx.x >= sel.total(B)) return;   // (walk-order list stage)
+  int b, r;
+  sel.at(blockIdx.x, K, b, r);
+  const long long grow = (long long)b * rows + r;
   if (kdraft != nullptr) {           // rows past the draft count are not needed
     const int kb = kdraft[b];
     if (r <= K ? r > kb : r - K - 1 >= kb) return;
   }
   // after the list pass: only the rows it handed over
-  if (only_redo && parts[blockIdx.x].flags != kTruncRedo) return;
+  if (only_redo && parts[grow].flags != kTruncRedo) return;
   const void* row = row_ptr<DT_F32>(target, draft, b, r, K, V);
   const long long nchunks = V / VEC;
   const double scale = __builtin_ldexp(1.0, fx);
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
       p.m = 0.0f;
       p.idx = int(thr);
       p.flags = 0;
-      parts[blockIdx.x] = p;
+      parts[grow] = p;
     }
   };
 
@@ -727,7 +732,7 @@ template <int VEC>
 __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
     double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
-    RowPart* __restrict__ parts) {
+    RowPart* __restrict__ parts, int B, RowSel sel) {
   static_assert(VEC == 4, "the one-read route reads 16-byte chunks");
   static_assert(kT32SampleMax == 4, "the sample is one group of four slices");
   __shared__ uint32_t buf[kT32BufOne];   // sample counts by first digit, then the copy
@@ -740,7 +745,10 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   __shared__ TPWalk w;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int rows = 2 * K + 1;
-  const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
+  if ((long long)blockIdx.x >= sel.total(B)) return;   // (walk-order list stage)
+  int b, r;
+  sel.at(blockIdx.x, K, b, r);
+  const long long grow = (long long)b * rows + r;
   if (kdraft != nullptr) {           // rows past the draft count are not needed
     const int kb = kdraft[b];
     if (r <= K ? r > kb : r - K - 1 >= kb) return;
@@ -753,7 +761,7 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
   // alone, or top-k (with or without top-p) beyond the list's size or tied at
   // the k-th value; a row with neither rule or an invalid top_p is the
   // multi-read pass's
-  if (!(kon || pon) || !(pp > 0.0f) || parts[blockIdx.x].flags != kTruncRedo) return;
+  if (!(kon || pon) || !(pp > 0.0f) || parts[grow].flags != kTruncRedo) return;
   // the row's base comes from the arguments and the workgroup index (the
   // same in every lane); chunks are indexed with 32-bit offsets (a row holds
   // fewer than 2^27 chunks)
@@ -1019,7 +1027,7 @@ __global__ __launch_bounds__(kTPBlock, 6) void rowstats_trunc32_topp(
       p.m = 0.0f;
       p.idx = int(thr);
       p.flags = 0;
-      parts[blockIdx.x] = p;
+      parts[grow] = p;
     }
   };
   uint32_t thr;
@@ -1083,7 +1091,8 @@ template <int VEC>
 __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
     double c64, int fx, Trunc tr, const int32_t* __restrict__ kdraft,
-    RowPart* __restrict__ parts, uint32_t* __restrict__ hist) {
+    RowPart* __restrict__ parts, uint32_t* __restrict__ hist, int B, RowSel sel,
+    uint32_t* __restrict__ clear) {
   static_assert(VEC == 4, "the list pass reads 16-byte chunks");
   __shared__ uint64_t s_keys[kT1Waves * kT1Cap];    // the lists, then merged in place
   __shared__ uint32_t s_bins[kT1Waves][256];
@@ -1096,8 +1105,12 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
   __shared__ uint32_t s_n;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   if (blockIdx.x == 0 && hist != nullptr && tid <= K) hist[tid] = 0u;
+  if (blockIdx.x == 0 && clear != nullptr && tid == 0) *clear = 0u;
   const int rows = 2 * K + 1;
-  const int b = int(blockIdx.x) / rows, r = int(blockIdx.x) % rows;
+  if ((long long)blockIdx.x >= sel.total(B)) return;   // (walk-order list stage)
+  int b, r;
+  sel.at(blockIdx.x, K, b, r);
+  const long long grow = (long long)b * rows + r;
   if (kdraft != nullptr) {
     const int kb = kdraft[b];
     if (r <= K ? r > kb : r - K - 1 >= kb) return;
@@ -1114,7 +1127,7 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
       p.m = 0.0f;
       p.idx = int(thr);
       p.flags = flags;
-      parts[blockIdx.x] = p;
+      parts[grow] = p;
     }
   };
   if (!(pp > 0.0f)) return put(__builtin_nan(""), 0.0f, 0u, 0);
@@ -1264,7 +1277,7 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
         p.m = 0.0f;
         p.idx = 0;
         p.flags = kTruncRedo;
-        parts[blockIdx.x] = p;
+        parts[grow] = p;
       }
       return;
     }
@@ -1296,7 +1309,7 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
       p.m = 0.0f;
       p.idx = int(tk);
       p.flags = 0;
-      parts[blockIdx.x] = p;
+      parts[grow] = p;
     }
     return;
   }
@@ -1327,8 +1340,34 @@ __global__ __launch_bounds__(kT1Block) void rowstats_trunc32_list(
     p.m = 0.0f;
     p.idx = int(thr);
     p.flags = flags;
-    parts[blockIdx.x] = p;
+    parts[grow] = p;
   }
+}
+
+// Walk-order reading of truncated fp32 calls, after the truncation passes over
+// position 0's rows: lists the sequences whose walk keeps position 0 and that
+// have rows past it (k_b >= 1), one thread per sequence, with the scan's own
+// truncated fp32 acceptance test (trunc_accept_f32).
+__global__ __launch_bounds__(kBlock) void walk_gate_trunc32(
+    int B, int K, int V, const RowPart* __restrict__ parts, const void* __restrict__ target,
+    const void* __restrict__ draft, const int32_t* __restrict__ kdraft,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, double c64,
+    int32_t* __restrict__ seqs, uint32_t* __restrict__ count) {
+  const int b = int(blockIdx.x) * kBlock + int(threadIdx.x);
+  if (b >= B) return;
+  const int kb = kdraft != nullptr ? kdraft[b] : K;
+  if (!(kb >= 1 && kb <= K)) return;
+  const int rows = 2 * K + 1;
+  const RowPart pt = parts[(long long)b * rows];
+  const RowPart pd = parts[(long long)b * rows + K + 1];
+  const int d = tokens[(long long)b * K];
+  if (!(finite_pos(pt.S) && finite_pos(pd.S) && d >= 0 && d < V)) return;
+  const float xt = load_logit<DT_F32>(row_ptr<DT_F32>(target, draft, b, 0, K, V), d);
+  const float xd = load_logit<DT_F32>(row_ptr<DT_F32>(target, draft, b, K + 1, K, V), d);
+  double P, Q;
+  if (trunc_accept_f32(xt, xd, pt.R, pt.S, uint32_t(pt.idx), pd.R, pd.S, uint32_t(pd.idx),
+                       double(uniforms[(long long)b * (K + 1)]), c64, P, Q))
+    seqs[atomicAdd(count, 1u)] = b;
 }
 
 }  // namespace sv

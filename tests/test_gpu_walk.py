@@ -14,7 +14,8 @@ are checked the same way, with the per-row argmax side output -1 and the
 margin ratio NaN past the row the walk stops at. Truncated bf16 calls read
 in walk order through both truncation passes (mixed per-sequence top-k /
 top-p, rows handed to the full-histogram pass, planted rows, stopping rules,
-the c3 shape); truncated fp32 calls read every row as before.
+the c3 shape), and truncated fp32 calls through their three passes (c1, fp32
+rows of the c2 shape, planted rows, a c5 sample).
 """
 
 import numpy as np
@@ -443,19 +444,54 @@ def test_walk_truncated_c3_whole_batch(sv):
     _trunc_case(sv, x, cfg, (tk, tp), "c3/trunc")
 
 
-def test_walk_fp32_truncated_reads_every_row(sv):
-    """Truncated fp32 calls ignore the walk-order setting: every needed row is
-    read and checked, as without it (the oracle's full reading)."""
-    cfg = CONFIGS["c1"].scaled(B=16)
+@pytest.mark.parametrize("name", ["c1", "c2f32"])
+def test_walk_fp32_truncated(sv, name):
+    """Truncated fp32 rows through the list, one-read and multi-read passes
+    (mixed per-sequence top-k / top-p, invalid top_p included)."""
+    cfg = (CONFIGS["c1"].scaled(B=32) if name == "c1"
+           else CONFIGS["c2"].scaled(B=32, dtype="f32"))
     x = make_inputs(cfg, 23, DEV)
-    tk, tp = _trunc_settings(cfg.B, cfg.V, 24)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 24, invalid=True)
     x = _trunc_drafts(x, cfg.T, tk, tp, 25)
+    walk, full, ref = _trunc_case(sv, x, cfg, (tk, tp), f"{name}/fp32 trunc")
+    a = walk[1].cpu().numpy()
+    assert a[1] == -1 and a[2] == -1
+
+
+def test_walk_fp32_truncated_unusable_rows_count_only_where_read(sv):
+    cfg = CONFIGS["c1"].scaled(B=40)
+    x = make_inputs(cfg, 26, DEV)
+    tk, tp = _trunc_settings(cfg.B, cfg.V, 27)
+    x = _trunc_drafts(x, cfg.T, tk, tp, 28)
+    trunc = (tk, tp)
+    j = _run(sv, x, cfg, False, trunc=trunc)[1].cpu().numpy()
+    assert np.all(j >= 0)
+    y = _plant(x, cfg, j, 29)
     rows = np.arange(cfg.B)
+    walk = _run(sv, y, cfg, True, trunc=trunc)
+    full = _run(sv, y, cfg, False, trunc=trunc)
+    ref = oracle_for(y, rows, "stochastic", trunc=trunc, walk=True)
+    ref_full = oracle_for(y, rows, "stochastic", trunc=trunc)
+    compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c1/fp32 trunc/walk/planted")
+    compare(rows, ref_full, full[0], full[1], "stochastic", full[3],
+            "c1/fp32 trunc/full/planted")
+    _pq_pattern(walk[3], ref, rows, "c1/fp32 trunc/planted")
+    a_walk, a_full = walk[1].cpu().numpy(), full[1].cpu().numpy()
+    assert (a_walk < 0).sum() < (a_full < 0).sum()
+    assert np.array_equal(a_walk < 0, ref.accept_len < 0)
+
+
+def test_walk_fp32_truncated_c5_sample(sv):
+    """The c5 shape (B = 1024, fp32, p = q and zeroed-mass sequences), top-k
+    50 + top-p 0.9: every sequence equal to the full reading, a sample of
+    256 against the oracle."""
+    cfg = CONFIGS["c5"]
+    x = make_inputs(cfg, 0, DEV)
+    tk = np.full(cfg.B, 50, np.int32)
+    tp = np.full(cfg.B, 0.9, np.float32)
     walk = _run(sv, x, cfg, True, trunc=(tk, tp))
     full = _run(sv, x, cfg, False, trunc=(tk, tp))
     _same_exact(walk, full)
-    ref = oracle_for(x, rows, "stochastic", trunc=(tk, tp))
-    compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c1/fp32 trunc/walk setting")
-    for key in ("p_d", "q_d"):
-        assert torch.equal(torch.nan_to_num(walk[3][key], nan=-9.0),
-                           torch.nan_to_num(full[3][key], nan=-9.0))
+    rows = np.sort(np.random.default_rng(31).choice(cfg.B, 256, replace=False))
+    ref = oracle_for(x, rows, "stochastic", trunc=(tk, tp), walk=True)
+    compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c5/fp32 trunc/walk")
