@@ -495,3 +495,34 @@ def test_walk_fp32_truncated_c5_sample(sv):
     rows = np.sort(np.random.default_rng(31).choice(cfg.B, 256, replace=False))
     ref = oracle_for(x, rows, "stochastic", trunc=(tk, tp), walk=True)
     compare(rows, ref, walk[0], walk[1], "stochastic", walk[3], "c5/fp32 trunc/walk")
+
+
+# --------------------------------------------------------------------------
+# small shapes: one drafted position, one sequence
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("route", ["plain", "trunc-bf16", "trunc-fp32", "greedy", "margin"])
+@pytest.mark.parametrize("B,K", [(1, 1), (1, 4), (9, 1)])
+def test_walk_small_shapes(sv, route, B, K):
+    """Grids of one or two workgroups per stage, a list stage holding only
+    the bonus row (K = 1), and a single sequence: every route of the
+    walk-order reading against the oracle's and the full reading."""
+    dtype = "f32" if route == "trunc-fp32" else "bf16"
+    cfg = CONFIGS["c2"].scaled(B=B, K=K, dtype=dtype)
+    argmax = route in ("greedy", "margin")
+    for step in range(6):
+        x = make_inputs(cfg, 40 + step, DEV, "greedy" if argmax else "stochastic")
+        trunc = None
+        if route.startswith("trunc"):
+            tk = np.full(B, 20, np.int32)
+            tp = np.full(B, 0.9, np.float32)
+            trunc = (tk, tp)
+            x = _trunc_drafts(x, cfg.T, tk, tp, 50 + step)
+        mode = route if argmax else "stochastic"
+        rows = np.arange(B)
+        walk = _run(sv, x, cfg, True, mode=mode, trunc=trunc)
+        full = _run(sv, x, cfg, False, mode=mode, trunc=trunc)
+        ref = oracle_for(x, rows, mode, tau=TAU, trunc=trunc, walk=True)
+        compare(rows, ref, walk[0], walk[1], mode, walk[3], f"small/{route}/B{B}K{K}/{step}")
+        for a, b in zip(walk[:3], full[:3]):
+            assert torch.equal(a, b)
