@@ -356,8 +356,12 @@ __device__ inline uint32_t t32_gather(const void* row, long long nchunks, uint32
   return n;
 }
 
-// One workgroup per (sequence, row): blockIdx.x = b (2K + 1) + r. only_redo:
-// skip the rows the list pass below has settled (flags != kTruncRedo).
+// One workgroup per row that sel selects (workgroup i takes candidate i:
+// every needed row, or with walk-order reading position 0's rows and then
+// the listed sequences' other rows; workgroups past the candidates return at
+// once). only_redo: skip the rows the list pass below has settled (flags !=
+// kTruncRedo). The list and one-read passes below take their rows the same
+// way.
 template <int VEC>
 __global__ __launch_bounds__(kT32Block) void rowstats_trunc32(
     const void* __restrict__ target, const void* __restrict__ draft, int K, int V, float c,
