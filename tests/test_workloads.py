@@ -62,3 +62,19 @@ def test_mc_and_const_alpha_inputs():
     assert abs(f[1] - 0.5) < 0.06
     y = const_alpha_inputs(0.7, 5, 10, 3)
     assert torch.isinf(y["draft"][:, :, 1]).all()
+
+
+def test_walk_rows_read_accounting():
+    """bench.py's count of the logit rows a walk-order call reads: position
+    0's rows of every valid sequence (target row 0, and draft row 0 when
+    k_b > 0 in stochastic mode), plus the other needed rows (target rows
+    1..k_b, draft rows 1..k_b-1) of the sequences whose walk keeps position
+    0 (j >= 1); invalid sequences (j = -1) are not counted."""
+    import bench
+    j = np.array([0, 1, 7, -1, 0, 3])
+    kb = np.array([7, 7, 7, 7, 0, 3])
+    # stochastic: 2 + (2 + 7 + 6) + (2 + 7 + 6) + 0 + 1 + (2 + 3 + 2)
+    assert bench.walk_rows_read(j, kb, "stochastic") == 2 + 15 + 15 + 0 + 1 + 7
+    # greedy / margin: target rows only
+    assert bench.walk_rows_read(j, kb, "greedy") == 1 + 8 + 8 + 0 + 1 + 4
+    assert bench.walk_rows_read(j, kb, "margin") == bench.walk_rows_read(j, kb, "greedy")
